@@ -1,0 +1,154 @@
+/*
+ * disco_oracle.c — plain fp64 CPU oracle of the DISCO CSR contraction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  The HIP product path never calls it
+ * and shares no code with it.
+ *
+ * What it computes (torch-harmonics "disco-kernel-dev" page, section
+ * "Architecture snapshot": forward = CSR sparse contraction from the input grid
+ * to the K-expanded (B,C,K,H,W) tensor; backward = the transpose contraction
+ * back to the input grid; fused = contraction followed by the channel/basis
+ * einsum).  The page gives the directions and the CSR layout but no formula;
+ * the formula used is the plain one:
+ *
+ *   fwd:   out[p,k,ho,wo] = sum_{e in row(k,ho)} val_e * x[p, hi_e, (wi_e + s*wo) mod Wi]
+ *   bwd:   gx = F^T gout, computed in the scatter form (each (e, wo) adds
+ *          val_e * gout[p,k,ho,wo] to gx[p, hi_e, (wi_e + s*wo) mod Wi])
+ *   fused: y[b,o,ho,wo] = sum_{c,k} W[o,c,k] * out[b,c,k,ho,wo]
+ *
+ * with s = Wi / Wo (the longitude subsampling factor) and p a flattened
+ * (batch, channel) plane.  All inputs arrive as fp32 (bf16 data is widened to
+ * fp32 exactly before the call) and are widened to double here; every sum is a
+ * serial double accumulation in the order written.  With abs_mode = 1 every
+ * operand is replaced by its absolute value, which yields the normaliser
+ * sum |val * x| used to scale the parity error.
+ *
+ * Parity status: fwd, bwd and fused are each pinned by independent checks in
+ * the CPU test suite (dense brute force, constant field, equivariance, adjoint,
+ * FFT correlation, strided-subsample matmul, hand-worked fixture).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static inline double opnd(double v, int abs_mode) { return abs_mode ? fabs(v) : v; }
+
+/* Forward contraction over P planes.
+ * x:   [P, Hi, Wi] fp32;  out: [P, K, Ho, Wo] double (overwritten). */
+void oracle_fwd(int64_t P, int K, int Ho, int Wo, int Hi, int Wi,
+                const int64_t *row_ptr, const int32_t *col_hi, const int32_t *col_wi,
+                const float *val, const float *x, double *out, int abs_mode)
+{
+    const int s = Wi / Wo;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < P; ++p) {
+        const float *xp = x + p * (int64_t)Hi * Wi;
+        for (int k = 0; k < K; ++k) {
+            for (int ho = 0; ho < Ho; ++ho) {
+                const int64_t r = (int64_t)k * Ho + ho;
+                double *o = out + ((p * K + k) * (int64_t)Ho + ho) * Wo;
+                for (int wo = 0; wo < Wo; ++wo) o[wo] = 0.0;
+                for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+                    const double v = opnd((double)val[e], abs_mode);
+                    const float *xrow = xp + (int64_t)col_hi[e] * Wi;
+                    for (int wo = 0; wo < Wo; ++wo) {
+                        const int wi = (int)(((int64_t)col_wi[e] + (int64_t)s * wo) % Wi);
+                        o[wo] += v * opnd((double)xrow[wi], abs_mode);
+                    }
+                }
+            }
+        }
+    }
+}
+
+/* Transpose contraction (scatter form) over P planes.
+ * gout: [P, K, Ho, Wo] fp32;  gx: [P, Hi, Wi] double (overwritten). */
+void oracle_bwd(int64_t P, int K, int Ho, int Wo, int Hi, int Wi,
+                const int64_t *row_ptr, const int32_t *col_hi, const int32_t *col_wi,
+                const float *val, const float *gout, double *gx, int abs_mode)
+{
+    const int s = Wi / Wo;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < P; ++p) {
+        double *g = gx + p * (int64_t)Hi * Wi;
+        for (int64_t i = 0; i < (int64_t)Hi * Wi; ++i) g[i] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            for (int ho = 0; ho < Ho; ++ho) {
+                const int64_t r = (int64_t)k * Ho + ho;
+                const float *go = gout + ((p * K + k) * (int64_t)Ho + ho) * Wo;
+                for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+                    const double v = opnd((double)val[e], abs_mode);
+                    double *grow = g + (int64_t)col_hi[e] * Wi;
+                    for (int wo = 0; wo < Wo; ++wo) {
+                        const int wi = (int)(((int64_t)col_wi[e] + (int64_t)s * wo) % Wi);
+                        grow[wi] += v * opnd((double)go[wo], abs_mode);
+                    }
+                }
+            }
+        }
+    }
+}
+
+/* Fused convolution for a list of output latitudes.
+ * x: [B, C, Hi, Wi] fp32;  W: [Co, C, K] fp32;  ho_list: [nho];
+ * y: [B, Co, nho, Wo] double (overwritten).
+ * The contraction result for one (b, ho) is kept in double (no rounding)
+ * before the einsum over (c, k). */
+void oracle_fused(int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
+                  const int64_t *row_ptr, const int32_t *col_hi, const int32_t *col_wi,
+                  const float *val, const float *x, const float *W,
+                  int nho, const int32_t *ho_list, double *y, int abs_mode)
+{
+    const int s = Wi / Wo;
+    double *t = (double *)malloc(sizeof(double) * (size_t)C * K * Wo);
+    if (!t) abort();
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < nho; ++h) {
+            const int ho = ho_list[h];
+            /* t[c, k, wo] = contraction at (b, c, k, ho, wo) */
+            #pragma omp parallel for schedule(dynamic, 1)
+            for (int c = 0; c < C; ++c) {
+                const float *xp = x + ((int64_t)b * C + c) * (int64_t)Hi * Wi;
+                for (int k = 0; k < K; ++k) {
+                    const int64_t r = (int64_t)k * Ho + ho;
+                    double *o = t + ((int64_t)c * K + k) * Wo;
+                    for (int wo = 0; wo < Wo; ++wo) o[wo] = 0.0;
+                    for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+                        const double v = opnd((double)val[e], abs_mode);
+                        const float *xrow = xp + (int64_t)col_hi[e] * Wi;
+                        for (int wo = 0; wo < Wo; ++wo) {
+                            const int wi = (int)(((int64_t)col_wi[e] + (int64_t)s * wo) % Wi);
+                            o[wo] += v * opnd((double)xrow[wi], abs_mode);
+                        }
+                    }
+                }
+            }
+            /* y[b, o, h, wo] = sum_{c,k} W[o,c,k] * t[c,k,wo] */
+            #pragma omp parallel for schedule(dynamic, 1)
+            for (int o = 0; o < Co; ++o) {
+                double *yo = y + (((int64_t)b * Co + o) * nho + h) * Wo;
+                for (int wo = 0; wo < Wo; ++wo) yo[wo] = 0.0;
+                for (int c = 0; c < C; ++c) {
+                    for (int k = 0; k < K; ++k) {
+                        const double wv = opnd((double)W[((int64_t)o * C + c) * K + k], abs_mode);
+                        const double *tk = t + ((int64_t)c * K + k) * Wo;
+                        for (int wo = 0; wo < Wo; ++wo) yo[wo] += wv * tk[wo];
+                    }
+                }
+            }
+        }
+    }
+    free(t);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
