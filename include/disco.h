@@ -1,0 +1,122 @@
+/*
+ * disco.h — C ABI of the gfx950 DISCO sparse-contraction library (libdisco.so).
+ *
+ * The operations are the three named on the torch-harmonics "disco-kernel-dev"
+ * page, section "Architecture snapshot":
+ *   - the CSR sparse contraction from the input grid to the K-expanded output
+ *     (B, C, K, Ho, Wo)                                        -> disco_fwd
+ *   - the CSR transpose contraction from (B, C, K, Ho, Wo) back to the input
+ *     grid, computed as an atomic-free gather (section "Backward direction —
+ *     gather vs scatter": each input pixel accumulates from its neighbourhood)
+ *                                                              -> disco_bwd
+ *   - contraction followed by the dense channel/basis einsum    -> disco_fused_conv
+ *
+ * With s = Wi / Wo (an integer >= 1) and psi rows r = k*Ho + ho:
+ *   out[b,c,k,ho,wo] = sum_{e in row r} val_e * x[b,c,hi_e,(wi_e + s*wo) mod Wi]
+ *   gx = F^T gout      (exact transpose of the map above)
+ *   y[b,o,ho,wo]     = sum_{c,k} W[o,c,k] * out[b,c,k,ho,wo]
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, contiguous, row-major, last index fastest; `data` is a
+ *     device pointer on the device the psi handle was created on.  The caller
+ *     owns every tensor buffer.
+ *   - Supported dtypes: DISCO_F32 and DISCO_BF16.  All tensors of one call
+ *     share one dtype.  Accumulation is always fp32; a bf16 output is rounded
+ *     once (round-to-nearest-even) from the fp32 accumulator.  psi values are
+ *     fp32 (kpacked section of the page: values stored as fp32).
+ *   - Outputs are fully overwritten (no accumulate flag); rows with no psi
+ *     entries are written as exact zeros.
+ *   - `stream` is a hipStream_t (0 = the null stream).  Work is enqueued
+ *     asynchronously; the calls never synchronise the host with the device.
+ *   - Every argument is validated on the host before anything is enqueued; on
+ *     any error nothing is written and a status is returned.  The text of the
+ *     last error of the calling thread is available from disco_last_error().
+ *   - Only gfx950 devices are accepted (the page's kernels check the device
+ *     architecture on the host and refuse others; section "Adding a new kernel
+ *     variant", step 1).
+ */
+#ifndef DISCO_H
+#define DISCO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum disco_status {
+    DISCO_OK = 0,
+    DISCO_ERR_INVALID_ARGUMENT = 1,   /* null handle / tensor / data pointer, wrong device */
+    DISCO_ERR_SHAPE = 2,              /* Wi % Wo != 0, or shapes disagree with psi / each other */
+    DISCO_ERR_DTYPE = 3,              /* dtype not F32/BF16, or dtypes of one call differ */
+    DISCO_ERR_PSI = 4,                /* malformed CSR (row_ptr, column range, nnz >= 2^31) */
+    DISCO_ERR_UNSUPPORTED_DEVICE = 5, /* device is not gfx950 */
+    DISCO_ERR_OOM = 6,                /* device or host allocation failed */
+    DISCO_ERR_HIP = 7                 /* a HIP runtime call or kernel launch failed */
+} disco_status;
+
+typedef enum disco_dtype {
+    DISCO_F32 = 0,
+    DISCO_BF16 = 1
+} disco_dtype;
+
+/* Host-side CSR filter ("psi").  Rows r = k*Ho + ho, K*Ho rows in all.
+ * Column of an entry = input pixel (col_hi[e], col_wi[e]): the input latitude
+ * and the longitude offset from output longitude 0.  Entries of one row may be
+ * in any order; a (hi, wi) pair may appear at most once per row.
+ * All arrays are host memory, read during disco_psi_create only. */
+typedef struct disco_csr_desc {
+    int32_t K, Ho, Wo, Hi, Wi;
+    int64_t nnz;              /* must equal row_ptr[K*Ho] and be < 2^31 */
+    const int64_t *row_ptr;   /* [K*Ho + 1], row_ptr[0] == 0, non-decreasing */
+    const int32_t *col_hi;    /* [nnz], in [0, Hi) */
+    const int32_t *col_wi;    /* [nnz], in [0, Wi) */
+    const float *val;         /* [nnz] */
+} disco_csr_desc;
+
+/* Device tensor view.  shape[0..ndim-1] are used; the rest are ignored. */
+typedef struct disco_tensor {
+    void *data;               /* device pointer */
+    int32_t dtype;            /* disco_dtype */
+    int32_t ndim;
+    int64_t shape[5];
+} disco_tensor;
+
+typedef struct disco_psi_s *disco_psi;
+
+/* Validate the CSR, derive the device plans (longitude-run segments of the
+ * forward rows grouped by shared support, and the row-inverted psi used by the
+ * backward gather), and upload them to `device` (a HIP device ordinal).
+ * Host arrays are copied; the caller may free them on return.  May block the
+ * host until the uploads finish.  On success *out_handle owns all device
+ * memory of the plan; release it with disco_psi_destroy.  A handle is
+ * read-only after creation and may be used from several streams at once. */
+disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *out_handle);
+
+/* Free a handle (NULL is accepted).  The caller must ensure no enqueued call
+ * still uses it. */
+disco_status disco_psi_destroy(disco_psi h);
+
+/* Forward contraction.  x: (B, C, Hi, Wi) -> out: (B, C, K, Ho, Wo). */
+disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, void *stream);
+
+/* Transpose contraction.  gout: (B, C, K, Ho, Wo) -> gx: (B, C, Hi, Wi).
+ * Atomic-free: every gx element is produced by one thread in a fixed order,
+ * so results are bitwise reproducible run to run. */
+disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, void *stream);
+
+/* Fused convolution.  x: (B, C, Hi, Wi), W: (Co, C, K) -> y: (B, Co, Ho, Wo).
+ * The contraction is computed on chip in channel chunks and never written to
+ * device memory; the einsum runs on bf16 MFMA tiles with fp32 accumulation
+ * (contraction chunks are rounded to bf16 before the MFMA).  BF16 only. */
+disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
+                              disco_tensor *y, void *stream);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char *disco_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DISCO_H */

@@ -1,0 +1,27 @@
+// common.hpp — device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace disco {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float load_elem(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const bf16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void store_elem(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(bf16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+}  // namespace disco

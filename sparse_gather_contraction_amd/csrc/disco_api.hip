@@ -1,0 +1,335 @@
+// disco_api.hip — C ABI of libdisco.so: validation, plan upload and launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "disco.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+disco_status fail(disco_status s, const std::string &msg)
+{
+    g_last_error = msg;
+    return s;
+}
+
+struct DevPlan {
+    disco::Item *items = nullptr;
+    int32_t *order = nullptr;
+    disco::Seg *segs = nullptr;
+    float *vals = nullptr;
+    int32_t *block_ptr = nullptr;
+    int32_t n_items = 0;
+    int32_t L = 0, in_stride = 1;
+};
+
+template <typename T>
+hipError_t upload(T **dst, const std::vector<T> &src)
+{
+    const size_t n = src.empty() ? 1 : src.size();
+    hipError_t e = hipMalloc((void **)dst, n * sizeof(T));
+    if (e != hipSuccess) return e;
+    if (!src.empty()) e = hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+    return e;
+}
+
+void free_plan(DevPlan &p)
+{
+    (void)hipFree(p.items);
+    (void)hipFree(p.order);
+    (void)hipFree(p.segs);
+    (void)hipFree(p.vals);
+    (void)hipFree(p.block_ptr);
+    p = DevPlan();
+}
+
+hipError_t upload_plan(DevPlan &d, const disco::GatherPlan &p)
+{
+    hipError_t e;
+    if ((e = upload(&d.items, p.items)) != hipSuccess) return e;
+    if ((e = upload(&d.order, p.order)) != hipSuccess) return e;
+    if ((e = upload(&d.segs, p.segs)) != hipSuccess) return e;
+    if ((e = upload(&d.vals, p.vals)) != hipSuccess) return e;
+    if ((e = upload(&d.block_ptr, p.block_ptr)) != hipSuccess) return e;
+    d.n_items = (int32_t)p.items.size();
+    d.L = p.L;
+    d.in_stride = p.in_stride;
+    return hipSuccess;
+}
+
+disco_status check_device(int device)
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_UNSUPPORTED_DEVICE, "no HIP device is visible");
+    }
+    if (device < 0 || device >= n) return fail(DISCO_ERR_INVALID_ARGUMENT, "device ordinal out of range");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_HIP, "hipGetDeviceProperties failed");
+    }
+    const char *env = getenv("DISCO_REQUIRE_ARCH");  // test knob: the architecture prefix to accept
+    const std::string want = (env && *env) ? env : "gfx950";
+    const std::string arch = prop.gcnArchName;
+    const bool ok = arch.compare(0, want.size(), want) == 0 && (arch.size() == want.size() || arch[want.size()] == ':');
+    if (!ok) return fail(DISCO_ERR_UNSUPPORTED_DEVICE, "device architecture " + arch + " is not " + want);
+    return DISCO_OK;
+}
+
+disco_status check_tensor(const disco_tensor *t, const char *name, int ndim, const int64_t *shape, int device)
+{
+    if (!t) return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
+    if (t->dtype != DISCO_F32 && t->dtype != DISCO_BF16)
+        return fail(DISCO_ERR_DTYPE, std::string(name) + " has an unsupported dtype");
+    if (t->ndim != ndim) return fail(DISCO_ERR_SHAPE, std::string(name) + " has the wrong number of dimensions");
+    int64_t numel = 1;
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] != shape[i]) {
+            char buf[160];
+            snprintf(buf, sizeof buf, "%s dimension %d is %lld, expected %lld", name, i, (long long)t->shape[i],
+                     (long long)shape[i]);
+            return fail(DISCO_ERR_SHAPE, buf);
+        }
+        numel *= shape[i];
+    }
+    if (numel == 0) return DISCO_OK;
+    if (!t->data) return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(name) + "->data is NULL");
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, t->data) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(name) + "->data is not device memory");
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(name) + "->data is not device memory");
+    if (attr.device != device)
+        return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(name) + "->data lives on another device");
+    return DISCO_OK;
+}
+
+bool log_enabled()
+{
+    const char *e = getenv("DISCO_LOG");
+    return e && *e && strcmp(e, "0") != 0;
+}
+
+}  // namespace
+
+struct disco_psi_s {
+    int device;
+    int32_t K, Ho, Wo, Hi, Wi;
+    int64_t nnz;
+    DevPlan fwd, bwd;
+    int32_t *ho_order = nullptr;
+};
+
+namespace {
+
+disco_status check_handle(disco_psi h)
+{
+    if (!h) return fail(DISCO_ERR_INVALID_ARGUMENT, "psi handle is NULL");
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_HIP, "hipGetDevice failed");
+    }
+    if (cur != h->device) return fail(DISCO_ERR_INVALID_ARGUMENT, "the current device is not the psi's device");
+    return DISCO_OK;
+}
+
+// Launch the gather over all planes, in chunks that keep the grid below 2^31 blocks.
+disco_status run_gather(const DevPlan &p, const void *src, void *dst, bool bf16, int64_t BC, int64_t src_plane,
+                        int64_t dst_plane, hipStream_t stream)
+{
+    if (BC == 0) return DISCO_OK;
+    const int64_t max_blocks = ((int64_t)1 << 31) - 1;
+    const int64_t chunk = std::max<int64_t>(1, max_blocks / std::max<int32_t>(1, p.n_items));
+    const size_t esz = bf16 ? 2 : 4;
+    for (int64_t b0 = 0; b0 < BC; b0 += chunk) {
+        disco::GatherLaunch a;
+        a.src = (const char *)src + b0 * src_plane * esz;
+        a.dst = (char *)dst + b0 * dst_plane * esz;
+        a.bf16 = bf16;
+        a.items = p.items;
+        a.order = p.order;
+        a.segs = p.segs;
+        a.vals = p.vals;
+        a.n_items = p.n_items;
+        a.BC = (int32_t)std::min<int64_t>(chunk, BC - b0);
+        a.src_plane = src_plane;
+        a.dst_plane = dst_plane;
+        a.L = p.L;
+        a.in_stride = p.in_stride;
+        hipError_t e = disco::launch_gather(a, stream);
+        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("gather launch failed: ") + hipGetErrorString(e));
+    }
+    return DISCO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *disco_last_error(void) { return g_last_error.c_str(); }
+
+disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *out_handle)
+{
+    if (!csr || !out_handle) return fail(DISCO_ERR_INVALID_ARGUMENT, "csr or out_handle is NULL");
+    *out_handle = nullptr;
+    disco::CSRView v{csr->K, csr->Ho, csr->Wo, csr->Hi, csr->Wi, csr->nnz, csr->row_ptr, csr->col_hi, csr->col_wi, csr->val};
+    int code = 0;
+    std::string msg = disco::validate_csr(v, &code);
+    if (code != 0) return fail((disco_status)code, msg);
+    disco_status st = check_device(device);
+    if (st != DISCO_OK) return st;
+
+    disco::GatherPlan fp, bp;
+    try {
+        disco::build_forward_plan(v, fp);
+        disco::build_backward_plan(v, bp);
+    } catch (const std::bad_alloc &) {
+        return fail(DISCO_ERR_OOM, "host allocation failed while building the plan");
+    }
+    // latitudes ordered by forward work, heaviest first (fused launch order)
+    std::vector<int64_t> work(csr->Ho, 0);
+    for (int32_t ho = 0; ho < csr->Ho; ++ho)
+        for (int32_t i = fp.block_ptr[ho]; i < fp.block_ptr[ho + 1]; ++i)
+            for (int32_t s = fp.items[i].seg_begin; s < fp.items[i].seg_end; ++s) work[ho] += (int64_t)fp.segs[s].m * fp.items[i].G;
+    std::vector<int32_t> ho_order(csr->Ho);
+    for (int32_t i = 0; i < csr->Ho; ++i) ho_order[i] = i;
+    std::stable_sort(ho_order.begin(), ho_order.end(), [&](int32_t a, int32_t b) { return work[a] > work[b]; });
+
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_HIP, "cannot select the device");
+    }
+    disco_psi h = new (std::nothrow) disco_psi_s();
+    if (!h) {
+        (void)hipSetDevice(prev);
+        return fail(DISCO_ERR_OOM, "host allocation failed");
+    }
+    h->device = device;
+    h->K = csr->K; h->Ho = csr->Ho; h->Wo = csr->Wo; h->Hi = csr->Hi; h->Wi = csr->Wi;
+    h->nnz = csr->nnz;
+    hipError_t e = upload_plan(h->fwd, fp);
+    if (e == hipSuccess) e = upload_plan(h->bwd, bp);
+    if (e == hipSuccess) e = upload(&h->ho_order, ho_order);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        free_plan(h->fwd);
+        free_plan(h->bwd);
+        (void)hipFree(h->ho_order);
+        delete h;
+        (void)hipSetDevice(prev);
+        return fail(e == hipErrorOutOfMemory ? DISCO_ERR_OOM : DISCO_ERR_HIP,
+                    std::string("plan upload failed: ") + hipGetErrorString(e));
+    }
+    (void)hipSetDevice(prev);
+    if (log_enabled())
+        fprintf(stderr,
+                "[disco] psi K=%d Ho=%d Wo=%d Hi=%d Wi=%d nnz=%lld | fwd: %zu items %zu segs %zu vals | "
+                "bwd: %zu items %zu segs\n",
+                h->K, h->Ho, h->Wo, h->Hi, h->Wi, (long long)h->nnz, fp.items.size(), fp.segs.size(), fp.vals.size(),
+                bp.items.size(), bp.segs.size());
+    *out_handle = h;
+    return DISCO_OK;
+}
+
+disco_status disco_psi_destroy(disco_psi h)
+{
+    if (!h) return DISCO_OK;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(h->device);
+    free_plan(h->fwd);
+    free_plan(h->bwd);
+    (void)hipFree(h->ho_order);
+    (void)hipSetDevice(prev);
+    delete h;
+    return DISCO_OK;
+}
+
+disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, void *stream)
+{
+    disco_status st = check_handle(h);
+    if (st != DISCO_OK) return st;
+    if (!x || !out) return fail(DISCO_ERR_INVALID_ARGUMENT, "x or out is NULL");
+    if (x->ndim != 4) return fail(DISCO_ERR_SHAPE, "x must be (B, C, Hi, Wi)");
+    const int64_t B = x->shape[0], C = x->shape[1];
+    if (B < 0 || C < 0) return fail(DISCO_ERR_SHAPE, "negative batch or channel count");
+    const int64_t xs[4] = {B, C, h->Hi, h->Wi};
+    const int64_t os[5] = {B, C, h->K, h->Ho, h->Wo};
+    if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(out, "out", 5, os, h->device)) != DISCO_OK) return st;
+    if (x->dtype != out->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
+    return run_gather(h->fwd, x->data, out->data, x->dtype == DISCO_BF16, B * C, (int64_t)h->Hi * h->Wi,
+                      (int64_t)h->K * h->Ho * h->Wo, (hipStream_t)stream);
+}
+
+disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, void *stream)
+{
+    disco_status st = check_handle(h);
+    if (st != DISCO_OK) return st;
+    if (!gout || !gx) return fail(DISCO_ERR_INVALID_ARGUMENT, "gout or gx is NULL");
+    if (gout->ndim != 5) return fail(DISCO_ERR_SHAPE, "gout must be (B, C, K, Ho, Wo)");
+    const int64_t B = gout->shape[0], C = gout->shape[1];
+    if (B < 0 || C < 0) return fail(DISCO_ERR_SHAPE, "negative batch or channel count");
+    const int64_t gs[5] = {B, C, h->K, h->Ho, h->Wo};
+    const int64_t xs[4] = {B, C, h->Hi, h->Wi};
+    if ((st = check_tensor(gout, "gout", 5, gs, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
+    if (gout->dtype != gx->dtype) return fail(DISCO_ERR_DTYPE, "gout and gx dtypes differ");
+    return run_gather(h->bwd, gout->data, gx->data, gout->dtype == DISCO_BF16, B * C, (int64_t)h->K * h->Ho * h->Wo,
+                      (int64_t)h->Hi * h->Wi, (hipStream_t)stream);
+}
+
+disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
+                              void *stream)
+{
+    disco_status st = check_handle(h);
+    if (st != DISCO_OK) return st;
+    if (!x || !W || !y) return fail(DISCO_ERR_INVALID_ARGUMENT, "x, W or y is NULL");
+    if (x->ndim != 4) return fail(DISCO_ERR_SHAPE, "x must be (B, C, Hi, Wi)");
+    if (W->ndim != 3) return fail(DISCO_ERR_SHAPE, "W must be (Co, C, K)");
+    const int64_t B = x->shape[0], C = x->shape[1], Co = W->shape[0];
+    if (B < 0 || C < 0 || Co < 0) return fail(DISCO_ERR_SHAPE, "negative batch or channel count");
+    if (h->K > disco::fused_max_k()) return fail(DISCO_ERR_SHAPE, "the fused kernel supports K <= 64");
+    const int64_t xs[4] = {B, C, h->Hi, h->Wi};
+    const int64_t ws[3] = {Co, C, h->K};
+    const int64_t ys[4] = {B, Co, h->Ho, h->Wo};
+    if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(W, "W", 3, ws, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(y, "y", 4, ys, h->device)) != DISCO_OK) return st;
+    if (x->dtype != W->dtype || x->dtype != y->dtype) return fail(DISCO_ERR_DTYPE, "x, W and y dtypes differ");
+    if (x->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution supports bf16 only");
+    if (B * Co * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
+    if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
+        return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
+    disco::FusedLaunch a;
+    a.x = x->data;
+    a.W = W->data;
+    a.y = y->data;
+    a.items = h->fwd.items;
+    a.block_ptr = h->fwd.block_ptr;
+    a.ho_order = h->ho_order;
+    a.segs = h->fwd.segs;
+    a.vals = h->fwd.vals;
+    a.B = (int32_t)B; a.C = (int32_t)C; a.Co = (int32_t)Co; a.K = h->K;
+    a.Ho = h->Ho; a.Wo = h->Wo; a.Hi = h->Hi; a.Wi = h->Wi;
+    a.in_stride = h->fwd.in_stride;
+    hipError_t e = disco::launch_fused(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));
+    return DISCO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// kernels.hpp — launch descriptors of the gfx950 kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "plan.hpp"
+
+namespace disco {
+
+struct GatherLaunch {
+    const void *src;
+    void *dst;
+    bool bf16;
+    const Item *items;     // device
+    const int32_t *order;  // device, heaviest item first
+    const Seg *segs;       // device
+    const float *vals;     // device
+    int32_t n_items;
+    int32_t BC;            // number of (b, c) planes
+    int64_t src_plane, dst_plane;
+    int32_t L, in_stride;
+};
+
+hipError_t launch_gather(const GatherLaunch &a, hipStream_t stream);
+
+struct FusedLaunch {
+    const void *x;          // (B, C, Hi, Wi) bf16
+    const void *W;          // (Co, C, K) bf16
+    void *y;                // (B, Co, Ho, Wo) bf16
+    const Item *items;      // forward plan items, grouped by ho
+    const int32_t *block_ptr;  // [Ho + 1]
+    const int32_t *ho_order;   // [Ho], heaviest latitude first
+    const Seg *segs;
+    const float *vals;
+    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, in_stride;
+};
+
+hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream);
+int fused_max_k();  // largest K the fused kernel accepts
+
+}  // namespace disco

@@ -1,0 +1,181 @@
+// kernels_fused.hip — fused DISCO convolution for gfx950.
+//
+// y[b,o,ho,wo] = sum_{c,k} W[o,c,k] * out[b,c,k,ho,wo]  ("contraction + einsum",
+// torch-harmonics "disco-kernel-dev" page, "Architecture snapshot").
+//
+// The (B,C,K,Ho,Wo) contraction is never written to device memory.  A block
+// owns one (b, ho) latitude, a tile of kPx output longitudes and a block of
+// kOBlk output channels.  It walks the input channels in chunks whose
+// (c, k) rows fill kR reduction rows: the chunk is contracted on the vector
+// ALUs (fp32, serial per element, the forward plan's segments), rounded to
+// bf16 into LDS as a [pixel][c*K + k] tile, and then multiplied on the matrix
+// cores: v_mfma_f32_16x16x32_bf16 with W as the A operand (16 o x 32 rows)
+// and the LDS tile as the B operand (32 rows x 16 pixels), fp32 accumulation
+// in registers across all chunks.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace disco {
+
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kPx = 64;        // output longitudes per block
+constexpr int kOBlk = 256;     // output channels per block (64 per wave)
+constexpr int kR = 64;         // reduction rows (c*K + k) per chunk: two MFMA k-steps
+constexpr int kLdsStride = kR + 8;  // bf16 elements per pixel row in LDS (16-byte aligned rows)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int G>
+__device__ __forceinline__ void contract_item(const bf16_t *__restrict__ plane, const Item &it,
+                                              const Seg *__restrict__ segs, const float *__restrict__ vals,
+                                              int Wo, int in_stride, int wo, bool valid, float *acc)
+{
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+    for (int q = it.seg_begin; q < it.seg_end; ++q) {
+        const Seg sg = segs[q];
+        const float *v = vals + sg.val_off;
+        const bf16_t *row = plane + sg.in_off;
+        for (int t = 0; t < sg.m; ++t) {
+            int base = sg.j0 + t;
+            if (base >= Wo) base -= Wo;
+            int idx = base + wo;
+            if (idx >= Wo) idx -= Wo;
+            const float xv = valid ? bf16_to_f32(row[(int64_t)in_stride * idx]) : 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = fmaf(v[t * G + g], xv, acc[g]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restrict__ x, const bf16_t *__restrict__ W,
+                                                         bf16_t *__restrict__ y, const Item *__restrict__ items,
+                                                         const int32_t *__restrict__ block_ptr,
+                                                         const int32_t *__restrict__ ho_order,
+                                                         const Seg *__restrict__ segs, const float *__restrict__ vals,
+                                                         int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
+                                                         int in_stride, int n_pt, int n_ob)
+{
+    __shared__ __attribute__((aligned(16))) bf16_t tile[kPx * kLdsStride];
+
+    int bid = blockIdx.x;
+    const int pt = bid % n_pt;
+    bid /= n_pt;
+    const int ob = bid % n_ob;
+    bid /= n_ob;
+    const int b = bid % B;
+    const int ho = ho_order[bid / B];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wo0 = pt * kPx;
+    const int o_base = ob * kOBlk + wave * 64;
+    const int CC = kR / K;  // channels per chunk (host guarantees K <= kR)
+    const int64_t plane_sz = (int64_t)Hi * Wi;
+    const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
+    const int HoWo = Ho * Wo;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int npass = (CC * kPx + kThreads - 1) / kThreads;
+    for (int c0 = 0; c0 < C; c0 += CC) {
+        const int ccn = min(CC, C - c0);
+        __syncthreads();  // the previous chunk's MFMA reads of `tile` are done
+        // ---- contraction of channels [c0, c0+ccn) into tile[px][cl*K + k] ----
+        for (int pass = 0; pass < npass; ++pass) {
+            const int pair = tid + kThreads * pass;
+            const int cl = pair / kPx;
+            const int px = pair - cl * kPx;
+            const int wo = wo0 + px;
+            const bool valid = (cl < ccn) && (wo < Wo);
+            const bf16_t *plane = x + ((int64_t)b * C + (c0 + (cl < ccn ? cl : 0))) * plane_sz;
+            for (int ii = it_begin; ii < it_end; ++ii) {
+                const Item it = items[ii];
+                float a[kMaxGroup];
+                switch (it.G) {
+                case 1: contract_item<1>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 2: contract_item<2>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 3: contract_item<3>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                default: contract_item<4>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                }
+                if (cl < CC) {
+                    for (int g = 0; g < it.G; ++g) {
+                        const int k = it.out_off[g] / HoWo;
+                        tile[px * kLdsStride + cl * K + k] = f32_to_bf16(valid ? a[g] : 0.0f);
+                    }
+                }
+            }
+        }
+        // rows past the chunk's (c, k) range are zero
+        for (int e = tid; e < kPx * kR; e += kThreads) {
+            const int px = e / kR, r = e - px * kR;
+            if (r >= ccn * K) tile[px * kLdsStride + r] = 0;
+        }
+        __syncthreads();
+        // ---- einsum on the matrix cores ----
+        const int rvalid = ccn * K;
+#pragma unroll
+        for (int ks = 0; ks < kR / 32; ++ks) {
+            const int rr0 = ks * 32 + 8 * (lane >> 4);
+            bf16x8 bop[4];
+#pragma unroll
+            for (int p4 = 0; p4 < 4; ++p4) {
+                const int px = p4 * 16 + (lane & 15);
+                bop[p4] = *reinterpret_cast<const bf16x8 *>(&tile[px * kLdsStride + rr0]);
+            }
+#pragma unroll
+            for (int ot = 0; ot < 4; ++ot) {
+                const int o = o_base + ot * 16 + (lane & 15);
+                i16x8 av;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int rr = rr0 + i;
+                    av[i] = (o < Co && rr < rvalid) ? (short)W[((int64_t)o * C + c0) * K + rr] : (short)0;
+                }
+                const bf16x8 aop = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+                for (int p4 = 0; p4 < 4; ++p4)
+                    acc[ot][p4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[p4], acc[ot][p4], 0, 0, 0);
+            }
+        }
+    }
+    // ---- epilogue: D[row = o][col = pixel]; lane holds col lane&15, rows 4*(lane>>4)+a ----
+#pragma unroll
+    for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+        for (int p4 = 0; p4 < 4; ++p4)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int o = o_base + ot * 16 + 4 * (lane >> 4) + a;
+                const int wo = wo0 + p4 * 16 + (lane & 15);
+                if (o < Co && wo < Wo) y[(((int64_t)b * Co + o) * Ho + ho) * Wo + wo] = f32_to_bf16(acc[ot][p4][a]);
+            }
+}
+
+}  // namespace
+
+hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
+{
+    if (a.B == 0 || a.Co == 0) return hipSuccess;
+    const int n_pt = (a.Wo + kPx - 1) / kPx;
+    const int n_ob = (a.Co + kOBlk - 1) / kOBlk;
+    const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pt;
+    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const bf16_t *)a.x,
+                       (const bf16_t *)a.W, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
+                       a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    return hipGetLastError();
+}
+
+int fused_max_k() { return kR; }
+
+}  // namespace disco

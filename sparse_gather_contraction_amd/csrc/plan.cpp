@@ -1,0 +1,277 @@
+// plan.cpp — builds the forward and row-inverted (backward) gather plans.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstdio>
+#include <numeric>
+
+namespace disco {
+
+namespace {
+
+enum { kOk = 0, kInvalid = 1, kShape = 2, kPsi = 4 };
+
+struct Run {
+    int32_t in_off;
+    int32_t j0;
+    int32_t m;
+    int64_t first;  // index of the first entry in the caller's entry list
+};
+
+// Turn a list of (row key, position) entries, sorted by (key, pos) and unique,
+// into runs of consecutive positions on a circle of length L.  A run that
+// ends at L-1 and a run of the same key that starts at 0 are merged (the run
+// then wraps).  Runs are split to at most kMaxSegLen entries.
+// `key[i]` is the source-row offset, `pos[i]` the position in [0, L).
+// `perm` receives entry indices in run order (so values can be gathered).
+void make_runs(const std::vector<int32_t> &key, const std::vector<int32_t> &pos, int32_t L,
+               std::vector<Run> &runs, std::vector<int64_t> &perm)
+{
+    runs.clear();
+    perm.clear();
+    const int64_t n = (int64_t)key.size();
+    int64_t i = 0;
+    while (i < n) {
+        // all entries of one key
+        int64_t kb = i;
+        while (i < n && key[i] == key[kb]) ++i;
+        int64_t ke = i;
+        // maximal runs of consecutive positions within [kb, ke)
+        std::vector<std::pair<int64_t, int64_t>> r;  // [begin, end) in entry index
+        int64_t a = kb;
+        for (int64_t j = kb + 1; j <= ke; ++j) {
+            if (j == ke || pos[j] != pos[j - 1] + 1) {
+                r.push_back({a, j});
+                a = j;
+            }
+        }
+        // wrap merge: last run ends at L-1, first run starts at 0, and they differ
+        bool wrap = r.size() > 1 && pos[r.front().first] == 0 && pos[r.back().second - 1] == L - 1;
+        std::vector<std::vector<int64_t>> merged;
+        for (size_t q = 0; q < r.size(); ++q) {
+            if (wrap && q == 0) continue;  // appended after the last run
+            std::vector<int64_t> idx;
+            for (int64_t j = r[q].first; j < r[q].second; ++j) idx.push_back(j);
+            if (wrap && q + 1 == r.size())
+                for (int64_t j = r.front().first; j < r.front().second; ++j) idx.push_back(j);
+            merged.push_back(std::move(idx));
+        }
+        for (auto &idx : merged) {
+            for (size_t s = 0; s < idx.size(); s += kMaxSegLen) {
+                size_t e = std::min(idx.size(), s + (size_t)kMaxSegLen);
+                Run run;
+                run.in_off = key[idx[s]];
+                run.j0 = pos[idx[s]];
+                run.m = (int32_t)(e - s);
+                run.first = (int64_t)perm.size();
+                for (size_t t = s; t < e; ++t) perm.push_back(idx[t]);
+                runs.push_back(run);
+            }
+        }
+    }
+}
+
+void finish_order(GatherPlan &p)
+{
+    std::vector<int64_t> work(p.items.size());
+    for (size_t i = 0; i < p.items.size(); ++i) {
+        int64_t n = 0;
+        for (int32_t s = p.items[i].seg_begin; s < p.items[i].seg_end; ++s) n += p.segs[s].m;
+        work[i] = n * p.items[i].G + 1;
+    }
+    p.order.resize(p.items.size());
+    std::iota(p.order.begin(), p.order.end(), 0);
+    std::stable_sort(p.order.begin(), p.order.end(), [&](int32_t a, int32_t b) { return work[a] > work[b]; });
+}
+
+}  // namespace
+
+std::string validate_csr(const CSRView &c, int *code)
+{
+    char buf[256];
+    *code = kShape;
+    if (c.K <= 0 || c.Ho <= 0 || c.Wo <= 0 || c.Hi <= 0 || c.Wi <= 0) return "K, Ho, Wo, Hi and Wi must all be positive";
+    if (c.Wi % c.Wo != 0) {
+        snprintf(buf, sizeof buf, "Wi (%d) must be an integer multiple of Wo (%d)", c.Wi, c.Wo);
+        return buf;
+    }
+    if ((int64_t)c.K * c.Ho * c.Wo >= (int64_t)1 << 31 || (int64_t)c.Hi * c.Wi >= (int64_t)1 << 31)
+        return "a (K, Ho, Wo) or (Hi, Wi) plane exceeds 2^31 elements";
+    *code = kInvalid;
+    if (!c.row_ptr) return "row_ptr is NULL";
+    if (c.nnz > 0 && (!c.col_hi || !c.col_wi || !c.val)) return "col_hi, col_wi or val is NULL";
+    *code = kPsi;
+    if (c.nnz < 0 || c.nnz >= ((int64_t)1 << 31)) return "nnz must be in [0, 2^31)";
+    const int64_t R = (int64_t)c.K * c.Ho;
+    if (c.row_ptr[0] != 0) return "row_ptr[0] must be 0";
+    for (int64_t r = 0; r < R; ++r)
+        if (c.row_ptr[r + 1] < c.row_ptr[r]) {
+            snprintf(buf, sizeof buf, "row_ptr decreases at row %lld", (long long)r);
+            return buf;
+        }
+    if (c.row_ptr[R] != c.nnz) return "row_ptr[K*Ho] must equal nnz";
+    for (int64_t e = 0; e < c.nnz; ++e) {
+        if (c.col_hi[e] < 0 || c.col_hi[e] >= c.Hi || c.col_wi[e] < 0 || c.col_wi[e] >= c.Wi) {
+            snprintf(buf, sizeof buf, "entry %lld has column (%d, %d) outside [0,%d)x[0,%d)", (long long)e,
+                     c.col_hi[e], c.col_wi[e], c.Hi, c.Wi);
+            return buf;
+        }
+    }
+    // duplicate (hi, wi) within a row
+    std::vector<int64_t> keys;
+    for (int64_t r = 0; r < R; ++r) {
+        keys.clear();
+        for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e) keys.push_back((int64_t)c.col_hi[e] * c.Wi + c.col_wi[e]);
+        std::sort(keys.begin(), keys.end());
+        if (std::adjacent_find(keys.begin(), keys.end()) != keys.end()) {
+            snprintf(buf, sizeof buf, "row %lld holds a duplicate column", (long long)r);
+            return buf;
+        }
+    }
+    *code = kOk;
+    return "";
+}
+
+void build_forward_plan(const CSRView &c, GatherPlan &p)
+{
+    const int32_t s = c.Wi / c.Wo;
+    p = GatherPlan();
+    p.L = c.Wo;
+    p.in_stride = s;
+    p.block_ptr.push_back(0);
+    std::vector<int64_t> perm;
+    std::vector<Run> runs;
+    for (int32_t ho = 0; ho < c.Ho; ++ho) {
+        // sorted entry lists of the K rows at this latitude
+        std::vector<std::vector<int64_t>> ent(c.K);  // entry indices sorted by column
+        for (int32_t k = 0; k < c.K; ++k) {
+            const int64_t r = (int64_t)k * c.Ho + ho;
+            auto &v = ent[k];
+            for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e) v.push_back(e);
+            std::sort(v.begin(), v.end(), [&](int64_t a, int64_t b) {
+                // order by (hi, rho, jj): source row first, then position
+                int64_t ka = ((int64_t)c.col_hi[a] * s + c.col_wi[a] % s) * c.Wo + c.col_wi[a] / s;
+                int64_t kb = ((int64_t)c.col_hi[b] * s + c.col_wi[b] % s) * c.Wo + c.col_wi[b] / s;
+                return ka < kb;
+            });
+        }
+        auto same_support = [&](int32_t a, int32_t b) {
+            if (ent[a].size() != ent[b].size()) return false;
+            for (size_t i = 0; i < ent[a].size(); ++i)
+                if (c.col_hi[ent[a][i]] != c.col_hi[ent[b][i]] || c.col_wi[ent[a][i]] != c.col_wi[ent[b][i]]) return false;
+            return true;
+        };
+        // groups of rows with identical column sets, in order of first appearance
+        std::vector<std::vector<int32_t>> groups;
+        for (int32_t k = 0; k < c.K; ++k) {
+            bool placed = false;
+            for (auto &g : groups)
+                if (same_support(g[0], k)) { g.push_back(k); placed = true; break; }
+            if (!placed) groups.push_back({k});
+        }
+        for (auto &grp : groups) {
+            for (size_t g0 = 0; g0 < grp.size(); g0 += kMaxGroup) {
+                const int32_t G = (int32_t)std::min<size_t>(kMaxGroup, grp.size() - g0);
+                const auto &base = ent[grp[g0]];
+                std::vector<int32_t> key(base.size()), pos(base.size());
+                for (size_t i = 0; i < base.size(); ++i) {
+                    const int64_t e = base[i];
+                    key[i] = c.col_hi[e] * c.Wi + c.col_wi[e] % s;
+                    pos[i] = c.col_wi[e] / s;
+                }
+                make_runs(key, pos, c.Wo, runs, perm);
+                Item it;
+                it.seg_begin = (int32_t)p.segs.size();
+                for (const Run &rn : runs) {
+                    Seg sg;
+                    sg.in_off = rn.in_off;
+                    sg.j0 = rn.j0;
+                    sg.m = rn.m;
+                    sg.val_off = (int32_t)p.vals.size();
+                    for (int32_t t = 0; t < rn.m; ++t) {
+                        const int64_t i = perm[rn.first + t];
+                        for (int32_t g = 0; g < G; ++g) p.vals.push_back(c.val[ent[grp[g0 + g]][i]]);
+                    }
+                    p.segs.push_back(sg);
+                }
+                it.seg_end = (int32_t)p.segs.size();
+                it.G = G;
+                it.out_stride = 1;
+                for (int32_t g = 0; g < kMaxGroup; ++g)
+                    it.out_off[g] = g < G ? (grp[g0 + g] * c.Ho + ho) * c.Wo : 0;
+                p.nnz_updates_per_col += (int64_t)base.size() * G;
+                p.items.push_back(it);
+            }
+        }
+        p.block_ptr.push_back((int32_t)p.items.size());
+    }
+    finish_order(p);
+}
+
+void build_backward_plan(const CSRView &c, GatherPlan &p)
+{
+    const int32_t s = c.Wi / c.Wo;
+    p = GatherPlan();
+    p.L = c.Wo;
+    p.in_stride = 1;
+    p.block_ptr.push_back(0);
+    // bucket entries by (hi, rho)
+    const int64_t nb = (int64_t)c.Hi * s;
+    std::vector<int64_t> cnt(nb + 1, 0);
+    std::vector<int32_t> kho(c.nnz);
+    {
+        int32_t r = 0;
+        for (int64_t e = 0; e < c.nnz; ++e) {
+            while (c.row_ptr[r + 1] <= e) ++r;
+            kho[e] = r;  // r = k*Ho + ho
+            cnt[(int64_t)c.col_hi[e] * s + c.col_wi[e] % s + 1]++;
+        }
+    }
+    for (int64_t b = 0; b < nb; ++b) cnt[b + 1] += cnt[b];
+    std::vector<int64_t> bucket(c.nnz);
+    {
+        std::vector<int64_t> fill(cnt.begin(), cnt.end() - 1);
+        for (int64_t e = 0; e < c.nnz; ++e) bucket[fill[(int64_t)c.col_hi[e] * s + c.col_wi[e] % s]++] = e;
+    }
+    auto shift = [&](int64_t e) { return (c.Wo - c.col_wi[e] / s) % c.Wo; };  // u = (-jj') mod Wo
+    std::vector<int64_t> perm;
+    std::vector<Run> runs;
+    for (int32_t hi = 0; hi < c.Hi; ++hi) {
+        for (int32_t rho = 0; rho < s; ++rho) {
+            const int64_t b = (int64_t)hi * s + rho;
+            std::vector<int64_t> es(bucket.begin() + cnt[b], bucket.begin() + cnt[b + 1]);
+            std::sort(es.begin(), es.end(), [&](int64_t a, int64_t b2) {
+                if (kho[a] != kho[b2]) return kho[a] < kho[b2];
+                return shift(a) < shift(b2);
+            });
+            std::vector<int32_t> key(es.size()), pos(es.size());
+            for (size_t i = 0; i < es.size(); ++i) {
+                key[i] = kho[es[i]] * c.Wo;
+                pos[i] = (int32_t)shift(es[i]);
+            }
+            make_runs(key, pos, c.Wo, runs, perm);
+            Item it;
+            it.seg_begin = (int32_t)p.segs.size();
+            for (const Run &rn : runs) {
+                Seg sg;
+                sg.in_off = rn.in_off;
+                sg.j0 = rn.j0;
+                sg.m = rn.m;
+                sg.val_off = (int32_t)p.vals.size();
+                for (int32_t t = 0; t < rn.m; ++t) p.vals.push_back(c.val[es[perm[rn.first + t]]]);
+                p.segs.push_back(sg);
+            }
+            it.seg_end = (int32_t)p.segs.size();
+            it.G = 1;
+            it.out_stride = s;
+            it.out_off[0] = hi * c.Wi + rho;
+            for (int32_t g = 1; g < kMaxGroup; ++g) it.out_off[g] = 0;
+            p.nnz_updates_per_col += (int64_t)es.size();
+            p.items.push_back(it);
+        }
+        p.block_ptr.push_back((int32_t)p.items.size());
+    }
+    finish_order(p);
+}
+
+}  // namespace disco

@@ -1,0 +1,315 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Error measure (per output element): |gpu - oracle| / N, with N the same
+contraction taken over absolute values (sum |val * x|, and sum |W| * N_out for
+the fused op).  Elements with N == 0 must be exactly 0.  Bars: 1e-5 for fp32
+data, 2e-2 for bf16 data with fp32 accumulation.
+
+Full-size workloads run on the GPU exactly as the benchmark launches them; the
+oracle then checks whole (b, c) planes (every latitude, poles included) or
+whole output latitudes of the fused op.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gather_contraction_amd as sgc
+from disco_inputs import WORKLOADS, randn, workload_gout, workload_psi, workload_weight, workload_x
+from disco_inputs.psi import PsiCSR, build_psi, random_psi
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = torch.device("cuda", 0)
+
+
+def _log(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def normalised_error(gpu, ref, nrm):
+    g = gpu.detach().double().cpu().numpy() if hasattr(gpu, "detach") else np.asarray(gpu, np.float64)
+    assert g.shape == ref.shape == nrm.shape
+    assert np.all(np.isfinite(g)), "non-finite output (unwritten or NaN)"
+    zero = nrm == 0
+    assert np.all(g[zero] == 0.0), "elements with zero normaliser must be exactly 0"
+    if np.all(zero):
+        return 0.0
+    return float(np.max(np.abs(g[~zero] - ref[~zero]) / nrm[~zero]))
+
+
+_PSI = {}
+
+
+def gpu_psi(psi):
+    key = id(psi)
+    if key not in _PSI:
+        _PSI[key] = (psi, sgc.disco_psi_create(psi, 0))
+    return _PSI[key][1]
+
+
+def nan_like(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device=DEV)
+
+
+def tdtype(s):
+    return torch.float32 if s == "f32" else torch.bfloat16
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ["tiny_fwd_f32_16x32", "fwdbwd_f32_181x360"])
+def test_fwd_full_parity_fp32(name):
+    w = WORKLOADS[name]
+    _log(f"fwd {name}")
+    psi = workload_psi(w)
+    x = workload_x(w)
+    out = nan_like((w.B, w.C, w.K, w.Ho, w.Wo), torch.float32)
+    sgc.disco_fwd(gpu_psi(psi), x.to(DEV), out)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(psi, x)
+    nrm = oracle.fwd(psi, x.abs(), abs_mode=True)
+    assert normalised_error(out, ref, nrm) <= TOL["f32"]
+
+
+def test_bwd_full_parity_fp32():
+    w = WORKLOADS["fwdbwd_f32_181x360"]
+    _log("bwd fwdbwd_f32_181x360")
+    psi = workload_psi(w)
+    g = workload_gout(w)
+    gx = nan_like((w.B, w.C, w.Hi, w.Wi), torch.float32)
+    sgc.disco_bwd(gpu_psi(psi), g.to(DEV), gx)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(psi, g)
+    nrm = oracle.bwd(psi, g.abs(), abs_mode=True)
+    assert normalised_error(gx, ref, nrm) <= TOL["f32"]
+
+
+PLANES_721 = [0, 21, 42, 63]
+
+
+def test_fwd_bf16_721x1440_full_size():
+    w = WORKLOADS["fwd_bf16_721x1440"]
+    _log("fwd_bf16_721x1440 (GPU full, oracle on 4 planes)")
+    psi = workload_psi(w)
+    x = workload_x(w)
+    out = nan_like((w.B, w.C, w.K, w.Ho, w.Wo), torch.bfloat16)
+    sgc.disco_fwd(gpu_psi(psi), x.to(DEV), out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    xs = x[0, PLANES_721]
+    ref = oracle.fwd(psi, xs)
+    nrm = oracle.fwd(psi, xs.abs(), abs_mode=True)
+    assert normalised_error(out[0, PLANES_721], ref, nrm) <= TOL["bf16"]
+
+
+def test_bwd_bf16_721x1440_full_size():
+    w = WORKLOADS["bwd_bf16_721x1440"]
+    _log("bwd_bf16_721x1440 (GPU full, oracle on 4 planes)")
+    psi = workload_psi(w)
+    g = workload_gout(w)
+    gx = nan_like((w.B, w.C, w.Hi, w.Wi), torch.bfloat16)
+    sgc.disco_bwd(gpu_psi(psi), g.to(DEV), gx)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(gx).all())
+    gs = g[0, PLANES_721]
+    ref = oracle.bwd(psi, gs)
+    nrm = oracle.bwd(psi, gs.abs(), abs_mode=True)
+    assert normalised_error(gx[0, PLANES_721], ref, nrm) <= TOL["bf16"]
+
+
+def test_fused_721x1440_full_size():
+    w = WORKLOADS["fused_bf16_721x1440"]
+    _log("fused_bf16_721x1440 (GPU full, oracle on 5 latitudes)")
+    psi = workload_psi(w)
+    x = workload_x(w)
+    W = workload_weight(w)
+    y = nan_like((w.B, w.Co, w.Ho, w.Wo), torch.bfloat16)
+    sgc.disco_fused_conv(gpu_psi(psi), x.to(DEV), W.to(DEV), y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    hos = [0, 3, 360, 601]
+    ref = oracle.fused(psi, x, W, ho_list=hos)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), ho_list=hos, abs_mode=True)
+    assert normalised_error(y[:, :, hos], ref, nrm) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _fwd_bwd_check(psi, BC, dtype, seed):
+    x = randn((1, BC, psi.Hi, psi.Wi), seed, dtype)
+    g = randn((1, BC, psi.K, psi.Ho, psi.Wo), seed + 1, dtype)
+    h = sgc.disco_psi_create(psi, 0)
+    out = nan_like((1, BC, psi.K, psi.Ho, psi.Wo), tdtype(dtype))
+    gx = nan_like((1, BC, psi.Hi, psi.Wi), tdtype(dtype))
+    sgc.disco_fwd(h, x.to(DEV), out)
+    sgc.disco_bwd(h, g.to(DEV), gx)
+    torch.cuda.synchronize()
+    e1 = normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True))
+    e2 = normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True))
+    return e1, e2
+
+
+@pytest.mark.parametrize("BC", [1, 3, 4, 7, 8, 9, 65])
+def test_channel_counts(BC):
+    psi = workload_psi(WORKLOADS["tiny_fwd_f32_16x32"])
+    e1, e2 = _fwd_bwd_check(psi, BC, "f32", 100 + BC)
+    assert e1 <= TOL["f32"] and e2 <= TOL["f32"]
+
+
+@pytest.mark.parametrize("geom", [
+    # Hi, Wi, Ho, Wo, theta_c, n_r, n_a: polar caps spanning whole rings, wrapped runs, pscale 2 and 3
+    (31, 60, 16, 20, 0.5, 2, 2),
+    (31, 60, 31, 20, 1.5, 3, 4),
+    (37, 72, 19, 24, 0.9, 4, 2),
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_generated_psi_geometries(geom, dtype):
+    psi = build_psi(*geom)
+    e1, e2 = _fwd_bwd_check(psi, 6, dtype, 300)
+    assert e1 <= TOL[dtype] and e2 <= TOL[dtype]
+
+
+def test_random_psi_with_empty_rows_and_long_rows():
+    # Wo = 1100 > 1024 exercises the outer position loop; dense rows give runs longer than one segment
+    psi = random_psi(3, 4, 1100, 5, 2200, 0.05, seed=11, empty_rows=(0, 5, 11))
+    psi_dense = random_psi(2, 3, 40, 4, 80, 0.9, seed=12, empty_rows=(1,))
+    for p, seed in ((psi, 400), (psi_dense, 410)):
+        e1, e2 = _fwd_bwd_check(p, 5, "f32", seed)
+        assert e1 <= TOL["f32"] and e2 <= TOL["f32"]
+
+
+def test_empty_rows_write_exact_zero():
+    psi = random_psi(2, 5, 16, 6, 32, 0.2, seed=13, empty_rows=(0, 3, 7))
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((2, 3, 6, 32), 500).to(DEV)
+    out = nan_like((2, 3, 2, 5, 16), torch.float32)
+    sgc.disco_fwd(h, x, out)
+    torch.cuda.synchronize()
+    flat = out.reshape(2, 3, 10, 16)
+    for r in (0, 3, 7):
+        assert bool((flat[:, :, r] == 0).all())
+    # input rows no entry touches come back as exact zeros from the backward
+    gx = nan_like((2, 3, 6, 32), torch.float32)
+    sgc.disco_bwd(h, randn((2, 3, 2, 5, 16), 501).to(DEV), gx)
+    torch.cuda.synchronize()
+    used = np.zeros((6, 32), bool)
+    used[psi.col_hi, :] = True  # every longitude of a touched row can be reached by some wo
+    assert bool(torch.isfinite(gx).all())
+    for hi in range(6):
+        if not used[hi].any():
+            assert bool((gx[:, :, hi] == 0).all())
+
+
+def test_bitwise_deterministic():
+    w = WORKLOADS["fwdbwd_f32_181x360"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = workload_x(w).to(DEV)
+    g = workload_gout(w).to(DEV)
+    o1, o2 = sgc.disco_fwd(h, x), sgc.disco_fwd(h, x)
+    g1, g2 = sgc.disco_bwd(h, g), sgc.disco_bwd(h, g)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(g1, g2)
+
+
+def test_bf16_against_fp32_variant():
+    w = WORKLOADS["fwdbwd_f32_181x360"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    xb = randn((2, 8, w.Hi, w.Wi), 600, "bf16").to(DEV)
+    ob = sgc.disco_fwd(h, xb)
+    of = sgc.disco_fwd(h, xb.float())
+    torch.cuda.synchronize()
+    nrm = oracle.fwd(psi, xb.cpu().abs(), abs_mode=True)
+    assert normalised_error(ob, of.double().cpu().numpy(), nrm) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- fused
+
+@pytest.mark.parametrize("cfg", [
+    # (Hi, Wi, Ho, Wo, theta_c, n_r, n_a, B, C, Co)
+    (31, 60, 31, 60, 0.5, 4, 4, 2, 8, 32),      # K=16, p=1, ragged pixel tile
+    (31, 60, 16, 30, 0.6, 3, 1, 1, 23, 20),     # K=3: chunk of 21 channels, Co not a multiple of 16
+    (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 300),    # K=8, p=2, Co > one block
+    (13, 40, 13, 40, 0.9, 2, 2, 1, 1, 1),       # single channel in and out
+])
+def test_fused_small_ragged(cfg):
+    Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((B, C, Hi, Wi), 700, "bf16")
+    W = randn((Co, C, psi.K), 701, "bf16", std=1.0 / np.sqrt(C * psi.K))
+    y = nan_like((B, Co, Ho, Wo), torch.bfloat16)
+    sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.fused(psi, x, W)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)
+    assert normalised_error(y, ref, nrm) <= TOL["bf16"]
+
+
+def test_fused_equals_einsum_of_forward():
+    psi = build_psi(31, 60, 31, 60, 0.5, 4, 4)
+    h = sgc.disco_psi_create(psi, 0)
+    B, C, Co = 2, 12, 24
+    x = randn((B, C, 31, 60), 710, "bf16").to(DEV)
+    W = randn((Co, C, psi.K), 711, "bf16", std=0.1).to(DEV)
+    y = sgc.disco_fused_conv(h, x, W)
+    out = sgc.disco_fwd(h, x.float())  # fp32 contraction
+    yu = torch.matmul(W.float().reshape(Co, C * psi.K), out.reshape(B, C * psi.K, -1)).reshape(B, Co, 31, 60)
+    torch.cuda.synchronize()
+    nrm = oracle.fused(psi, x.cpu().abs(), W.cpu().abs(), abs_mode=True)
+    assert normalised_error(y, yu.double().cpu().numpy(), nrm) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- error paths on the device
+
+def _raw(fn, *descs):
+    lib = sgc.load_library()
+    st = getattr(lib, fn)(*descs)
+    return sgc.STATUS_NAMES[st], lib.disco_last_error().decode()
+
+
+def test_error_paths_leave_outputs_untouched():
+    psi = workload_psi(WORKLOADS["tiny_fwd_f32_16x32"])
+    h = gpu_psi(psi)
+    x = randn((1, 2, psi.Hi, psi.Wi), 800).to(DEV)
+    sentinel = 7.25
+    out = torch.full((1, 2, psi.K, psi.Ho, psi.Wo + 1), sentinel, device=DEV)  # wrong Wo
+    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(out)), None)
+    assert st == "DISCO_ERR_SHAPE"
+    out_bf = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel, device=DEV, dtype=torch.bfloat16)
+    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(out_bf)), None)
+    assert st == "DISCO_ERR_DTYPE"
+    x16 = x.half()
+    out16 = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel, device=DEV, dtype=torch.float16)
+    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x16)), ctypes.byref(sgc.tensor_desc(out16)), None)
+    assert st == "DISCO_ERR_DTYPE"
+    host = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel)
+    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(host)), None)
+    assert st == "DISCO_ERR_INVALID_ARGUMENT" and "device memory" in msg
+    Wf = torch.zeros((3, 2, psi.K), device=DEV)
+    yf = torch.full((1, 3, psi.Ho, psi.Wo), sentinel, device=DEV)
+    st, msg = _raw("disco_fused_conv", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(Wf)),
+                   ctypes.byref(sgc.tensor_desc(yf)), None)
+    assert st == "DISCO_ERR_DTYPE"
+    torch.cuda.synchronize()
+    for t in (out, out_bf, out16, host, yf):
+        assert bool((t == sentinel).all())
+    # an empty batch is valid and writes nothing
+    x0 = torch.empty((0, 2, psi.Hi, psi.Wi), device=DEV)
+    assert sgc.disco_fwd(h, x0).shape == (0, 2, psi.K, psi.Ho, psi.Wo)
+
+
+def test_architecture_refusal_knob(monkeypatch):
+    psi = workload_psi(WORKLOADS["tiny_fwd_f32_16x32"])
+    monkeypatch.setenv("DISCO_REQUIRE_ARCH", "gfx000")
+    with pytest.raises(sgc.DiscoError) as ei:
+        sgc.disco_psi_create(psi, 0)
+    assert ei.value.status_name == "DISCO_ERR_UNSUPPORTED_DEVICE"
+    monkeypatch.delenv("DISCO_REQUIRE_ARCH")
+    sgc.disco_psi_create(psi, 0).close()
