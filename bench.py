@@ -52,6 +52,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="fwd,bwd,fused", help="subset of ops in the step (profiling runs)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built.",
@@ -99,6 +101,17 @@ def main():
             sgc.disco_bwd(h_fb, tensors["g4"], tensors["gx4"])
         else:
             sgc.disco_fused_conv(h_u, tensors["x5"], tensors["W5"], tensors["y5"])
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     for i in range(args.warmup):
         for op in ops:
