@@ -31,6 +31,22 @@ struct DevPlan {
     int32_t L = 0, in_stride = 1;
 };
 
+constexpr int kStagedLdsBudget = 40 * 1024;  // bytes of LDS per block (four blocks per CU)
+
+struct DevStaged {
+    bool ok = false;
+    disco::Task *tasks = nullptr;
+    disco::Stage *stages = nullptr;
+    int32_t *stage_rows = nullptr;
+    int32_t *stage_segptr = nullptr;
+    disco::Seg *segs = nullptr;
+    float *vals = nullptr;
+    disco::Item *items = nullptr;
+    int32_t n_tasks = 0;
+    int32_t L = 0, row_len = 0, lrow = 0, halo = 0, rows_per_stage = 0, wpp = 4, NP = 1;
+    int32_t NI = 1, G = 1, T = 3, S = 1;
+};
+
 template <typename T>
 hipError_t upload(T **dst, const std::vector<T> &src)
 {
@@ -49,6 +65,37 @@ void free_plan(DevPlan &p)
     (void)hipFree(p.vals);
     (void)hipFree(p.block_ptr);
     p = DevPlan();
+}
+
+void free_staged(DevStaged &d)
+{
+    (void)hipFree(d.tasks);
+    (void)hipFree(d.stages);
+    (void)hipFree(d.stage_rows);
+    (void)hipFree(d.stage_segptr);
+    (void)hipFree(d.segs);
+    (void)hipFree(d.vals);
+    (void)hipFree(d.items);
+    d = DevStaged();
+}
+
+hipError_t upload_staged(DevStaged &d, const disco::StagedPlan &p)
+{
+    d = DevStaged();
+    if (!p.ok || !disco::staged_supported(p.NI, p.G, p.T, p.S)) return hipSuccess;
+    hipError_t e;
+    if ((e = upload(&d.tasks, p.tasks)) != hipSuccess) return e;
+    if ((e = upload(&d.stages, p.stages)) != hipSuccess) return e;
+    if ((e = upload(&d.stage_rows, p.stage_rows)) != hipSuccess) return e;
+    if ((e = upload(&d.stage_segptr, p.stage_segptr)) != hipSuccess) return e;
+    if ((e = upload(&d.segs, p.segs)) != hipSuccess) return e;
+    if ((e = upload(&d.vals, p.vals)) != hipSuccess) return e;
+    if ((e = upload(&d.items, p.items)) != hipSuccess) return e;
+    d.ok = true;
+    d.n_tasks = (int32_t)p.tasks.size();
+    d.L = p.L; d.row_len = p.row_len; d.lrow = p.lrow; d.halo = p.halo; d.rows_per_stage = p.rows_per_stage;
+    d.wpp = p.wpp; d.NP = p.NP; d.NI = p.NI; d.G = p.G; d.T = p.T; d.S = p.S;
+    return hipSuccess;
 }
 
 hipError_t upload_plan(DevPlan &d, const disco::GatherPlan &p)
@@ -129,6 +176,7 @@ struct disco_psi_s {
     int32_t K, Ho, Wo, Hi, Wi;
     int64_t nnz;
     DevPlan fwd, bwd;
+    DevStaged sfwd[2], sbwd[2];  // staged plans by source dtype: [0] fp32, [1] bf16
     int32_t *ho_order = nullptr;
 };
 
@@ -146,14 +194,45 @@ disco_status check_handle(disco_psi h)
     return DISCO_OK;
 }
 
+bool staged_env_off()
+{
+    const char *e = getenv("DISCO_STAGED");  // test knob: "0" forces the plain gather kernel
+    return e && strcmp(e, "0") == 0;
+}
+
 // Launch the gather over all planes, in chunks that keep the grid below 2^31 blocks.
-disco_status run_gather(const DevPlan &p, const void *src, void *dst, bool bf16, int64_t BC, int64_t src_plane,
-                        int64_t dst_plane, hipStream_t stream)
+disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, void *dst, bool bf16, int64_t BC,
+                        int64_t src_plane, int64_t dst_plane, hipStream_t stream)
 {
     if (BC == 0) return DISCO_OK;
+    const size_t esz = bf16 ? 2 : 4;
+    if (sp.ok && !staged_env_off()) {
+        const int align = 16 / (int)esz;
+        const bool vec = ((uintptr_t)src % 16 == 0) && (src_plane % align == 0) && (sp.row_len % align == 0) &&
+                         ((sp.row_len + sp.halo) % align == 0);
+        const int64_t n_pg_max = (((int64_t)1 << 31) - 1) / std::max<int32_t>(1, sp.n_tasks);
+        const int64_t chunk = std::max<int64_t>(1, n_pg_max) * sp.NP;
+        for (int64_t b0 = 0; b0 < BC; b0 += chunk) {
+            disco::StagedLaunch a;
+            a.src = (const char *)src + b0 * src_plane * esz;
+            a.dst = (char *)dst + b0 * dst_plane * esz;
+            a.bf16 = bf16;
+            a.tasks = sp.tasks; a.stages = sp.stages; a.stage_rows = sp.stage_rows; a.stage_segptr = sp.stage_segptr;
+            a.segs = sp.segs; a.vals = sp.vals; a.items = sp.items;
+            a.n_tasks = sp.n_tasks;
+            a.BC = (int32_t)std::min<int64_t>(chunk, BC - b0);
+            a.src_plane = src_plane; a.dst_plane = dst_plane;
+            a.L = sp.L; a.row_len = sp.row_len; a.copy_len = sp.row_len + sp.halo; a.lrow = sp.lrow;
+            a.wpp = sp.wpp; a.NP = sp.NP; a.stage_elems = sp.rows_per_stage * sp.lrow; a.vec = vec ? 1 : 0;
+            a.NI = sp.NI; a.G = sp.G; a.T = sp.T; a.S = sp.S;
+            hipError_t e = disco::launch_staged(a, stream);
+            if (e != hipSuccess)
+                return fail(DISCO_ERR_HIP, std::string("staged gather launch failed: ") + hipGetErrorString(e));
+        }
+        return DISCO_OK;
+    }
     const int64_t max_blocks = ((int64_t)1 << 31) - 1;
     const int64_t chunk = std::max<int64_t>(1, max_blocks / std::max<int32_t>(1, p.n_items));
-    const size_t esz = bf16 ? 2 : 4;
     for (int64_t b0 = 0; b0 < BC; b0 += chunk) {
         disco::GatherLaunch a;
         a.src = (const char *)src + b0 * src_plane * esz;
@@ -199,6 +278,16 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the plan");
     }
+    disco::StagedPlan sfp[2], sbp[2];
+    try {
+        for (int d = 0; d < 2; ++d) {
+            const int esz = d ? 2 : 4;
+            disco::build_staged_plan(v, fp, false, esz, kStagedLdsBudget, sfp[d]);
+            disco::build_staged_plan(v, bp, true, esz, kStagedLdsBudget, sbp[d]);
+        }
+    } catch (const std::bad_alloc &) {
+        return fail(DISCO_ERR_OOM, "host allocation failed while building the staged plan");
+    }
     // latitudes ordered by forward work, heaviest first (fused launch order)
     std::vector<int64_t> work(csr->Ho, 0);
     for (int32_t ho = 0; ho < csr->Ho; ++ho)
@@ -224,10 +313,18 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     hipError_t e = upload_plan(h->fwd, fp);
     if (e == hipSuccess) e = upload_plan(h->bwd, bp);
     if (e == hipSuccess) e = upload(&h->ho_order, ho_order);
+    for (int d = 0; d < 2 && e == hipSuccess; ++d) {
+        e = upload_staged(h->sfwd[d], sfp[d]);
+        if (e == hipSuccess) e = upload_staged(h->sbwd[d], sbp[d]);
+    }
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(h->fwd);
         free_plan(h->bwd);
+        for (int d = 0; d < 2; ++d) {
+            free_staged(h->sfwd[d]);
+            free_staged(h->sbwd[d]);
+        }
         (void)hipFree(h->ho_order);
         delete h;
         (void)hipSetDevice(prev);
@@ -238,9 +335,12 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     if (log_enabled())
         fprintf(stderr,
                 "[disco] psi K=%d Ho=%d Wo=%d Hi=%d Wi=%d nnz=%lld | fwd: %zu items %zu segs %zu vals | "
-                "bwd: %zu items %zu segs\n",
+                "bwd: %zu items %zu segs | staged bf16 fwd %s (%zu tasks, %zu stages, T=%d G=%d) bwd %s (%zu tasks, "
+                "%zu stages)\n",
                 h->K, h->Ho, h->Wo, h->Hi, h->Wi, (long long)h->nnz, fp.items.size(), fp.segs.size(), fp.vals.size(),
-                bp.items.size(), bp.segs.size());
+                bp.items.size(), bp.segs.size(), h->sfwd[1].ok ? "on" : "off", sfp[1].tasks.size(),
+                sfp[1].stages.size(), sfp[1].T, sfp[1].G, h->sbwd[1].ok ? "on" : "off", sbp[1].tasks.size(),
+                sbp[1].stages.size());
     *out_handle = h;
     return DISCO_OK;
 }
@@ -253,6 +353,10 @@ disco_status disco_psi_destroy(disco_psi h)
     (void)hipSetDevice(h->device);
     free_plan(h->fwd);
     free_plan(h->bwd);
+    for (int d = 0; d < 2; ++d) {
+        free_staged(h->sfwd[d]);
+        free_staged(h->sbwd[d]);
+    }
     (void)hipFree(h->ho_order);
     (void)hipSetDevice(prev);
     delete h;
@@ -272,7 +376,8 @@ disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, vo
     if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(out, "out", 5, os, h->device)) != DISCO_OK) return st;
     if (x->dtype != out->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
-    return run_gather(h->fwd, x->data, out->data, x->dtype == DISCO_BF16, B * C, (int64_t)h->Hi * h->Wi,
+    const int d = x->dtype == DISCO_BF16 ? 1 : 0;
+    return run_gather(h->fwd, h->sfwd[d], x->data, out->data, d == 1, B * C, (int64_t)h->Hi * h->Wi,
                       (int64_t)h->K * h->Ho * h->Wo, (hipStream_t)stream);
 }
 
@@ -289,7 +394,8 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
     if ((st = check_tensor(gout, "gout", 5, gs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
     if (gout->dtype != gx->dtype) return fail(DISCO_ERR_DTYPE, "gout and gx dtypes differ");
-    return run_gather(h->bwd, gout->data, gx->data, gout->dtype == DISCO_BF16, B * C, (int64_t)h->K * h->Ho * h->Wo,
+    const int d = gout->dtype == DISCO_BF16 ? 1 : 0;
+    return run_gather(h->bwd, h->sbwd[d], gout->data, gx->data, d == 1, B * C, (int64_t)h->K * h->Ho * h->Wo,
                       (int64_t)h->Hi * h->Wi, (hipStream_t)stream);
 }
 

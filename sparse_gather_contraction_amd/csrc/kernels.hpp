@@ -24,6 +24,27 @@ struct GatherLaunch {
 
 hipError_t launch_gather(const GatherLaunch &a, hipStream_t stream);
 
+struct StagedLaunch {
+    const void *src;
+    void *dst;
+    bool bf16;
+    const Task *tasks;            // device, heaviest first
+    const Stage *stages;
+    const int32_t *stage_rows;
+    const int32_t *stage_segptr;
+    const Seg *segs;
+    const float *vals;
+    const Item *items;
+    int32_t n_tasks, BC;
+    int64_t src_plane, dst_plane;
+    int32_t L, row_len, copy_len, lrow, wpp, NP, stage_elems, vec;
+    int32_t NI, G, T, S;
+};
+
+// true when the staged kernel has an instantiation for these parameters
+bool staged_supported(int NI, int G, int T, int S);
+hipError_t launch_staged(const StagedLaunch &a, hipStream_t stream);
+
 struct FusedLaunch {
     const void *x;          // (B, C, Hi, Wi) bf16
     const void *W;          // (Co, C, K) bf16

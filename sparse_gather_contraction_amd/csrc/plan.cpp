@@ -3,6 +3,8 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <climits>
+#include <cstdint>
 #include <numeric>
 
 namespace disco {
@@ -272,6 +274,126 @@ void build_backward_plan(const CSRView &c, GatherPlan &p)
         p.block_ptr.push_back((int32_t)p.items.size());
     }
     finish_order(p);
+}
+
+void build_staged_plan(const CSRView &c, const GatherPlan &p, bool backward, int elem_bytes, int lds_budget,
+                       StagedPlan &out)
+{
+    out = StagedPlan();
+    const int32_t s = c.Wi / c.Wo;
+    const int32_t L = p.L;
+    out.L = L;
+    out.S = backward ? 1 : s;
+    if (out.S > 2) return;
+    if (L <= 192) { out.T = 3; out.wpp = 1; }
+    else if (L <= 384) { out.T = 3; out.wpp = 2; }
+    else if (L <= 768) { out.T = 3; out.wpp = 4; }
+    else if (L <= 1536) { out.T = 6; out.wpp = 4; }
+    else return;
+    out.NP = 4 / out.wpp;
+    out.row_len = backward ? c.Wo : c.Wi;
+    out.halo = out.S * kStagedHaloPos;
+    int32_t lrow = out.row_len + out.halo;
+    const int32_t align = 16 / elem_bytes;
+    lrow = (lrow + align - 1) / align * align;
+    out.lrow = lrow;
+    out.rows_per_stage = (lds_budget / out.NP) / (lrow * elem_bytes);
+    if (out.rows_per_stage < 1) return;
+
+    // Rows sharing a segment list: keep G when every item agrees, else split to single rows.
+    int32_t G = p.items.empty() ? 1 : p.items[0].G;
+    for (const Item &it : p.items)
+        if (it.G != G) G = -1;
+    const bool split_rows = (G < 0);
+    if (split_rows) G = 1;
+    out.G = G;
+    out.NI = (backward && s <= 2) ? s : 1;
+
+    // expanded items: (source item, row g within it or -1 for all)
+    struct XItem { int32_t src; int32_t g; };
+    std::vector<XItem> xitems;
+    for (int32_t i = 0; i < (int32_t)p.items.size(); ++i) {
+        if (split_rows)
+            for (int32_t g = 0; g < p.items[i].G; ++g) xitems.push_back({i, g});
+        else
+            xitems.push_back({i, -1});
+    }
+    // tasks: NI consecutive expanded items (the backward plan lists the s residues of one input row in order)
+    const int32_t NI = out.NI;
+    if ((int32_t)xitems.size() % NI != 0) { out = StagedPlan(); return; }
+    std::vector<Task> tasks;
+    for (size_t t0 = 0; t0 < xitems.size(); t0 += NI) {
+        Task task;
+        task.item_begin = (int32_t)out.items.size();
+        task.stage_begin = (int32_t)out.stages.size();
+        int64_t work = 0;
+        // items
+        for (int32_t i = 0; i < NI; ++i) {
+            const XItem &xi = xitems[t0 + i];
+            const Item &src = p.items[xi.src];
+            Item it = src;
+            if (xi.g >= 0) {
+                it.G = 1;
+                it.out_off[0] = src.out_off[xi.g];
+                for (int32_t g = 1; g < kMaxGroup; ++g) it.out_off[g] = 0;
+            }
+            out.items.push_back(it);
+        }
+        // distinct source rows of the task
+        std::vector<int32_t> rows;
+        for (int32_t i = 0; i < NI; ++i) {
+            const Item &src = p.items[xitems[t0 + i].src];
+            for (int32_t q = src.seg_begin; q < src.seg_end; ++q)
+                rows.push_back(p.segs[q].in_off / out.row_len);
+        }
+        std::sort(rows.begin(), rows.end());
+        rows.erase(std::unique(rows.begin(), rows.end()), rows.end());
+        for (size_t r0 = 0; r0 < rows.size(); r0 += out.rows_per_stage) {
+            const size_t r1 = std::min(rows.size(), r0 + (size_t)out.rows_per_stage);
+            Stage st;
+            st.row_begin = (int32_t)out.stage_rows.size();
+            for (size_t r = r0; r < r1; ++r) out.stage_rows.push_back(rows[r]);
+            st.row_end = (int32_t)out.stage_rows.size();
+            st.segptr = (int32_t)out.stage_segptr.size();
+            st.pad = 0;
+            for (int32_t i = 0; i < NI; ++i) {
+                out.stage_segptr.push_back((int32_t)out.segs.size());
+                const XItem &xi = xitems[t0 + i];
+                const Item &src = p.items[xi.src];
+                for (int32_t q = src.seg_begin; q < src.seg_end; ++q) {
+                    const Seg &sg = p.segs[q];
+                    const int32_t row = sg.in_off / out.row_len;
+                    if (row < rows[r0] || row > rows[r1 - 1]) continue;
+                    const int32_t slot = (int32_t)(std::lower_bound(rows.begin() + r0, rows.begin() + r1, row) -
+                                                   (rows.begin() + r0));
+                    const int32_t rho = sg.in_off - row * out.row_len;
+                    for (int32_t off = 0; off < sg.m; off += kStagedSegLen) {
+                        Seg ns;
+                        ns.in_off = slot * lrow + rho;
+                        ns.j0 = (sg.j0 + off) % L;
+                        ns.m = std::min(kStagedSegLen, sg.m - off);
+                        ns.val_off = (int32_t)out.vals.size();
+                        for (int32_t t = 0; t < ns.m; ++t) {
+                            if (xi.g >= 0)
+                                out.vals.push_back(p.vals[sg.val_off + (off + t) * src.G + xi.g]);
+                            else
+                                for (int32_t g = 0; g < src.G; ++g) out.vals.push_back(p.vals[sg.val_off + (off + t) * src.G + g]);
+                        }
+                        work += (int64_t)ns.m * G;
+                        out.segs.push_back(ns);
+                    }
+                }
+            }
+            out.stage_segptr.push_back((int32_t)out.segs.size());
+            out.stages.push_back(st);
+        }
+        task.stage_end = (int32_t)out.stages.size();
+        task.work = (int32_t)std::min<int64_t>(work, INT32_MAX);
+        tasks.push_back(task);
+    }
+    std::stable_sort(tasks.begin(), tasks.end(), [](const Task &a, const Task &b) { return a.work > b.work; });
+    out.tasks = std::move(tasks);
+    out.ok = true;
 }
 
 }  // namespace disco

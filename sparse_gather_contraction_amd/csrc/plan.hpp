@@ -63,6 +63,54 @@ struct CSRView {
     const float *val;
 };
 
+// ---------------------------------------------------------------------------
+// Staged plan: the same segments, regrouped for the LDS-staged gather kernel.
+//
+// A task is the work of one block for one group of planes: NI items (the
+// forward: one row group of one latitude; the backward: the s residue items
+// of one input row).  Its source rows are copied to LDS in stages of at most
+// `rows_per_stage` rows; each staged row holds row_len elements followed by a
+// wrap halo (a copy of its first `halo` elements), `lrow` elements in all.
+// Segments are cut to at most kStagedSegLen entries and carry LDS offsets:
+// lds_off = slot * lrow + rho (rho = longitude residue of the forward).
+constexpr int kStagedSegLen = 8;
+constexpr int kStagedHaloPos = 16;   // halo, in positions (covers kStagedSegLen + T - 1 for T <= 9)
+
+struct Task {
+    int32_t stage_begin, stage_end;  // into stages
+    int32_t item_begin;              // items [item_begin, item_begin + NI)
+    int32_t work;                    // entries * G summed over its items (for ordering)
+};
+
+struct Stage {
+    int32_t row_begin, row_end;      // into stage_rows (source row indices within a plane)
+    int32_t segptr;                  // stage_segptr[segptr + i] .. [segptr + i + 1]: segments of item i
+    int32_t pad;
+};
+
+struct StagedPlan {
+    bool ok = false;                 // false: shape not covered, use the plain gather
+    int32_t NI = 1, G = 1, T = 3, S = 1;     // items per task, rows per item, positions per lane, source stride
+    int32_t wpp = 4, NP = 1;         // waves per plane, planes per block (4 waves per block)
+    int32_t L = 0, row_len = 0, lrow = 0, halo = 0, rows_per_stage = 0;
+    std::vector<Seg> segs;
+    std::vector<float> vals;
+    std::vector<Item> items;
+    std::vector<Task> tasks;         // heaviest first
+    std::vector<Stage> stages;
+    std::vector<int32_t> stage_rows;
+    std::vector<int32_t> stage_segptr;
+};
+
+// Regroup `p` (built by build_forward_plan / build_backward_plan) for the
+// staged kernel.  `backward` selects the row-inverted source layout (source
+// rows of length Wo, one task per input row covering all s residues);
+// `elem_bytes` is the source element size; `lds_budget` the bytes of LDS one
+// block may use.  Returns plans with ok = false when the shape is outside
+// what the staged kernel covers.
+void build_staged_plan(const CSRView &c, const GatherPlan &p, bool backward, int elem_bytes, int lds_budget,
+                       StagedPlan &out);
+
 // Returns "" on success, else a message; `code` receives a disco_status value.
 std::string validate_csr(const CSRView &c, int *code);
 

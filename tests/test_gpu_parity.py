@@ -313,3 +313,20 @@ def test_architecture_refusal_knob(monkeypatch):
     assert ei.value.status_name == "DISCO_ERR_UNSUPPORTED_DEVICE"
     monkeypatch.delenv("DISCO_REQUIRE_ARCH")
     sgc.disco_psi_create(psi, 0).close()
+
+
+@pytest.mark.parametrize("staged", ["0", "1"])
+def test_plain_and_staged_gather_agree_with_oracle(staged, monkeypatch):
+    """DISCO_STAGED=0 forces the plain gather kernel on shapes the staged kernel covers."""
+    monkeypatch.setenv("DISCO_STAGED", staged)
+    w = WORKLOADS["fwdbwd_f32_181x360"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    for dtype in ("f32", "bf16"):
+        x = randn((1, 5, w.Hi, w.Wi), 900, dtype)
+        g = randn((1, 5, w.K, w.Ho, w.Wo), 901, dtype)
+        out = sgc.disco_fwd(h, x.to(DEV))
+        gx = sgc.disco_bwd(h, g.to(DEV))
+        torch.cuda.synchronize()
+        assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL[dtype]
+        assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL[dtype]
