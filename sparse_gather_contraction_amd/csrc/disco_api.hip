@@ -47,6 +47,20 @@ struct DevStaged {
     int32_t NI = 1, G = 1, T = 3, S = 1;
 };
 
+constexpr int kFusedNpx = 256;                 // output longitudes per fused workgroup (8 waves)
+constexpr int kLdsPerBlock = 160 * 1024;       // gfx950: a workgroup may allocate the whole 160 KiB
+
+struct DevFused {
+    bool ok = false;
+    disco::FPiece *pieces = nullptr;
+    disco::FRow *rows = nullptr;
+    disco::FBlock *blocks = nullptr;
+    uint16_t *adata = nullptr;
+    int32_t *ho_piece = nullptr;
+    int32_t *ho_order = nullptr;
+    int32_t npx = 0, max_piece_elems = 0;
+};
+
 template <typename T>
 hipError_t upload(T **dst, const std::vector<T> &src)
 {
@@ -95,6 +109,34 @@ hipError_t upload_staged(DevStaged &d, const disco::StagedPlan &p)
     d.n_tasks = (int32_t)p.tasks.size();
     d.L = p.L; d.row_len = p.row_len; d.lrow = p.lrow; d.halo = p.halo; d.rows_per_stage = p.rows_per_stage;
     d.wpp = p.wpp; d.NP = p.NP; d.NI = p.NI; d.G = p.G; d.T = p.T; d.S = p.S;
+    return hipSuccess;
+}
+
+void free_fused(DevFused &d)
+{
+    (void)hipFree(d.pieces);
+    (void)hipFree(d.rows);
+    (void)hipFree(d.blocks);
+    (void)hipFree(d.adata);
+    (void)hipFree(d.ho_piece);
+    (void)hipFree(d.ho_order);
+    d = DevFused();
+}
+
+hipError_t upload_fused(DevFused &d, const disco::FusedPlan &p)
+{
+    d = DevFused();
+    if (!p.ok) return hipSuccess;
+    hipError_t e;
+    if ((e = upload(&d.pieces, p.pieces)) != hipSuccess) return e;
+    if ((e = upload(&d.rows, p.rows)) != hipSuccess) return e;
+    if ((e = upload(&d.blocks, p.blocks)) != hipSuccess) return e;
+    if ((e = upload(&d.adata, p.adata)) != hipSuccess) return e;
+    if ((e = upload(&d.ho_piece, p.ho_piece)) != hipSuccess) return e;
+    if ((e = upload(&d.ho_order, p.ho_order)) != hipSuccess) return e;
+    d.ok = true;
+    d.npx = p.npx;
+    d.max_piece_elems = p.max_piece_elems;
     return hipSuccess;
 }
 
@@ -177,6 +219,7 @@ struct disco_psi_s {
     int64_t nnz;
     DevPlan fwd, bwd;
     DevStaged sfwd[2], sbwd[2];  // staged plans by source dtype: [0] fp32, [1] bf16
+    DevFused fused;
     int32_t *ho_order = nullptr;
 };
 
@@ -288,6 +331,14 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the staged plan");
     }
+    disco::FusedPlan fup;
+    try {
+        const int ch = disco::fused_mfma_channels_per_chunk();
+        const int w_bytes = (int)disco::fused_mfma_lds_bytes(8, 0);
+        disco::build_fused_plan(v, fp, kFusedNpx, ch, kLdsPerBlock - w_bytes - 1024, fup);
+    } catch (const std::bad_alloc &) {
+        return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
+    }
     // latitudes ordered by forward work, heaviest first (fused launch order)
     std::vector<int64_t> work(csr->Ho, 0);
     for (int32_t ho = 0; ho < csr->Ho; ++ho)
@@ -317,10 +368,12 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         e = upload_staged(h->sfwd[d], sfp[d]);
         if (e == hipSuccess) e = upload_staged(h->sbwd[d], sbp[d]);
     }
+    if (e == hipSuccess) e = upload_fused(h->fused, fup);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(h->fwd);
         free_plan(h->bwd);
+        free_fused(h->fused);
         for (int d = 0; d < 2; ++d) {
             free_staged(h->sfwd[d]);
             free_staged(h->sbwd[d]);
@@ -341,6 +394,9 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
                 bp.items.size(), bp.segs.size(), h->sfwd[1].ok ? "on" : "off", sfp[1].tasks.size(),
                 sfp[1].stages.size(), sfp[1].T, sfp[1].G, h->sbwd[1].ok ? "on" : "off", sbp[1].tasks.size(),
                 sbp[1].stages.size());
+    if (log_enabled())
+        fprintf(stderr, "[disco] fused packed plan %s: %zu pieces, %lld blocks, max %d blocks/piece, window %d\n",
+                fup.ok ? "on" : "off", fup.pieces.size(), (long long)fup.mfma_blocks, fup.max_blk, fup.max_xwin);
     *out_handle = h;
     return DISCO_OK;
 }
@@ -357,6 +413,7 @@ disco_status disco_psi_destroy(disco_psi h)
         free_staged(h->sfwd[d]);
         free_staged(h->sbwd[d]);
     }
+    free_fused(h->fused);
     (void)hipFree(h->ho_order);
     (void)hipSetDevice(prev);
     delete h;
@@ -421,6 +478,20 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     if (B * Co * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
     if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
         return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
+    const char *fm = getenv("DISCO_FUSED_MFMA");  // test knob: "0" forces the VALU-contraction fused kernel
+    if (h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
+        disco::FusedMfmaLaunch m;
+        m.x = x->data; m.W = W->data; m.y = y->data;
+        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.blocks = h->fused.blocks; m.adata = h->fused.adata;
+        m.ho_piece = h->fused.ho_piece; m.ho_order = h->fused.ho_order;
+        m.B = (int32_t)B; m.C = (int32_t)C; m.Co = (int32_t)Co; m.K = h->K;
+        m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi; m.s = h->Wi / h->Wo;
+        m.npx = h->fused.npx; m.max_piece_elems = h->fused.max_piece_elems;
+        hipError_t e = disco::launch_fused_mfma(m, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));
+        return DISCO_OK;
+    }
     disco::FusedLaunch a;
     a.x = x->data;
     a.W = W->data;

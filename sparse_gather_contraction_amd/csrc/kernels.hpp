@@ -5,6 +5,7 @@
 #include <cstdint>
 
 #include "plan.hpp"
+#include "plan_fused.hpp"
 
 namespace disco {
 
@@ -58,6 +59,21 @@ struct FusedLaunch {
 };
 
 hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream);
+
+struct FusedMfmaLaunch {
+    const void *x, *W;
+    void *y;
+    const FPiece *pieces;
+    const FRow *rows;
+    const FBlock *blocks;
+    const uint16_t *adata;
+    const int32_t *ho_piece, *ho_order;
+    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, npx, max_piece_elems;
+};
+
+hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
+size_t fused_mfma_lds_bytes(int n_ot, int max_piece_elems);
+int fused_mfma_channels_per_chunk();
 int fused_max_k();  // largest K the fused kernel accepts
 
 }  // namespace disco

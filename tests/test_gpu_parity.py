@@ -233,7 +233,9 @@ def test_bf16_against_fp32_variant():
 
 @pytest.mark.parametrize("cfg", [
     # (Hi, Wi, Ho, Wo, theta_c, n_r, n_a, B, C, Co)
-    (31, 60, 31, 60, 0.5, 4, 4, 2, 8, 32),      # K=16, p=1, ragged pixel tile
+    (31, 60, 31, 60, 0.5, 4, 4, 2, 8, 32),      # K=16, p=1, Wo % 8 != 0 (VALU-contraction kernel)
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 8, 32),      # K=16, p=1, packed matrix-core kernel, ragged longitude tile
+    (31, 64, 31, 64, 1.5, 4, 4, 1, 6, 33),      # caps spanning whole rings: several packed pieces per latitude
     (31, 60, 16, 30, 0.6, 3, 1, 1, 23, 20),     # K=3: chunk of 21 channels, Co not a multiple of 16
     (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 300),    # K=8, p=2, Co > one block
     (13, 40, 13, 40, 0.9, 2, 2, 1, 1, 1),       # single channel in and out
@@ -330,3 +332,18 @@ def test_plain_and_staged_gather_agree_with_oracle(staged, monkeypatch):
         torch.cuda.synchronize()
         assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL[dtype]
         assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mfma", ["0", "1"])
+def test_fused_both_kernels_agree_with_oracle(mfma, monkeypatch):
+    """DISCO_FUSED_MFMA=0 forces the VALU-contraction fused kernel on a shape the packed kernel covers."""
+    monkeypatch.setenv("DISCO_FUSED_MFMA", mfma)
+    psi = build_psi(19, 144, 19, 72, 0.7, 4, 2)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((2, 5, 19, 144), 950, "bf16")
+    W = randn((40, 5, psi.K), 951, "bf16", std=0.2)
+    y = sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.fused(psi, x, W)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)
+    assert normalised_error(y, ref, nrm) <= TOL["bf16"]
