@@ -21,9 +21,13 @@ SOURCES = ["plan.cpp", "plan_fused.cpp", "disco_api.hip", "kernels_gather.hip", 
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed fp32 VALU ops are disabled for all device code.
+# Device code is built with packed fp32 VALU ops disabled, and with unaligned memory access
+# disabled: on gfx950 unaligned LDS reads stall the LDS pipeline (SQ_LDS_UNALIGNED_STALL), so
+# reads at 2-byte alignment are kept as 2-byte reads instead of being merged into wide ones.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xclang", "-target-feature", "-Xclang", "-unaligned-access-mode",
+         "-Wall", "-Wno-unused-function"]
 
 
 def _compile(src: str) -> str:
@@ -31,7 +35,8 @@ def _compile(src: str) -> str:
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                     if "packed-fp32-ops" not in l and "unaligned-access-mode" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{out}")
     if out.strip():

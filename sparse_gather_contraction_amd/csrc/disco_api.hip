@@ -54,11 +54,11 @@ struct DevFused {
     bool ok = false;
     disco::FPiece *pieces = nullptr;
     disco::FRow *rows = nullptr;
-    disco::FBlock *blocks = nullptr;
+    int32_t *block_xoff = nullptr;
     uint16_t *adata = nullptr;
     int32_t *ho_piece = nullptr;
     int32_t *ho_order = nullptr;
-    int32_t npx = 0, max_piece_elems = 0;
+    int32_t npx = 0, max_piece_elems = 0, max_blk = 0;
 };
 
 template <typename T>
@@ -116,7 +116,7 @@ void free_fused(DevFused &d)
 {
     (void)hipFree(d.pieces);
     (void)hipFree(d.rows);
-    (void)hipFree(d.blocks);
+    (void)hipFree(d.block_xoff);
     (void)hipFree(d.adata);
     (void)hipFree(d.ho_piece);
     (void)hipFree(d.ho_order);
@@ -130,13 +130,14 @@ hipError_t upload_fused(DevFused &d, const disco::FusedPlan &p)
     hipError_t e;
     if ((e = upload(&d.pieces, p.pieces)) != hipSuccess) return e;
     if ((e = upload(&d.rows, p.rows)) != hipSuccess) return e;
-    if ((e = upload(&d.blocks, p.blocks)) != hipSuccess) return e;
+    if ((e = upload(&d.block_xoff, p.block_xoff)) != hipSuccess) return e;
     if ((e = upload(&d.adata, p.adata)) != hipSuccess) return e;
     if ((e = upload(&d.ho_piece, p.ho_piece)) != hipSuccess) return e;
     if ((e = upload(&d.ho_order, p.ho_order)) != hipSuccess) return e;
     d.ok = true;
     d.npx = p.npx;
     d.max_piece_elems = p.max_piece_elems;
+    d.max_blk = p.max_blk;
     return hipSuccess;
 }
 
@@ -334,7 +335,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     disco::FusedPlan fup;
     try {
         const int ch = disco::fused_mfma_channels_per_chunk();
-        const int w_bytes = (int)disco::fused_mfma_lds_bytes(8, 0);
+        const int w_bytes = (int)disco::fused_mfma_lds_bytes(8, 0, 0) + 4096;  // W slice + block offsets
         disco::build_fused_plan(v, fp, kFusedNpx, ch, kLdsPerBlock - w_bytes - 1024, fup);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
@@ -482,11 +483,11 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     if (h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
-        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.blocks = h->fused.blocks; m.adata = h->fused.adata;
+        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.block_xoff = h->fused.block_xoff; m.adata = h->fused.adata;
         m.ho_piece = h->fused.ho_piece; m.ho_order = h->fused.ho_order;
         m.B = (int32_t)B; m.C = (int32_t)C; m.Co = (int32_t)Co; m.K = h->K;
         m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi; m.s = h->Wi / h->Wo;
-        m.npx = h->fused.npx; m.max_piece_elems = h->fused.max_piece_elems;
+        m.npx = h->fused.npx; m.max_piece_elems = h->fused.max_piece_elems; m.max_blk = h->fused.max_blk;
         hipError_t e = disco::launch_fused_mfma(m, (hipStream_t)stream);
         if (e != hipSuccess)
             return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));

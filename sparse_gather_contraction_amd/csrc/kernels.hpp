@@ -65,14 +65,14 @@ struct FusedMfmaLaunch {
     void *y;
     const FPiece *pieces;
     const FRow *rows;
-    const FBlock *blocks;
+    const int32_t *block_xoff;
     const uint16_t *adata;
     const int32_t *ho_piece, *ho_order;
-    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, npx, max_piece_elems;
+    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, npx, max_piece_elems, max_blk;
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
-size_t fused_mfma_lds_bytes(int n_ot, int max_piece_elems);
+size_t fused_mfma_lds_bytes(int n_ot, int max_piece_elems, int max_blk);
 int fused_mfma_channels_per_chunk();
 int fused_max_k();  // largest K the fused kernel accepts
 

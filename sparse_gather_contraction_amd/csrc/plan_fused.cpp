@@ -113,6 +113,7 @@ void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int
                     b.row = row_index;
                     b.rel = d0 - sb.astart;
                     out.blocks.push_back(b);
+                    out.block_xoff.push_back(fr.lds_off + b.rel);
                     // A operand in lane order: lane l -> row r = l % 32 (k = r % 16, hi/lo part = r / 16),
                     // offsets 8 * (l / 32) + t, t < 8
                     for (int32_t l = 0; l < 64; ++l) {

@@ -41,6 +41,8 @@ struct FBlock {        // one packed 32x16 A operand
     int32_t row;       // index into the piece's rows (absolute index in rows[])
     int32_t rel;       // offset of the block's first position from the row window start
 };
+// The kernel reads, per block, only xoff = rows[row].lds_off + rel (element offset of
+// the block's first window position within one channel's window area).
 
 struct FPiece {
     int32_t blk_begin, blk_end;   // blocks (also index the packed A data, 512 bf16 each)
@@ -61,6 +63,7 @@ struct FusedPlan {
     std::vector<FPiece> pieces;
     std::vector<FRow> rows;
     std::vector<FBlock> blocks;
+    std::vector<int32_t> block_xoff;    // per block: rows[row].lds_off + rel
     std::vector<uint16_t> adata;        // packed A operands, 512 bf16 per block in lane order
     int64_t mfma_blocks = 0;            // total blocks over all latitudes
 };
