@@ -53,6 +53,10 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
+    undef = subprocess.run(["nm", "-D", "-C", "--undefined-only", tmp], stdout=subprocess.PIPE, text=True).stdout
+    missing = [l.split()[-1] for l in undef.splitlines() if "disco::" in l or " disco_" in l]
+    if missing:
+        raise RuntimeError("libdisco.so has undefined symbols of its own: " + ", ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -10,14 +10,8 @@ typedef uint16_t bf16_t;  // raw bfloat16 bits
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32); NaN stays NaN (quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ float load_elem(const float *p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_elem(const bf16_t *p, int64_t i) { return bf16_to_f32(p[i]); }

@@ -47,7 +47,6 @@ struct DevStaged {
     int32_t NI = 1, G = 1, T = 3, S = 1;
 };
 
-constexpr int kFusedNpx = 256;                 // output longitudes per fused workgroup (8 waves)
 constexpr int kLdsPerBlock = 160 * 1024;       // gfx950: a workgroup may allocate the whole 160 KiB
 
 struct DevFused {
@@ -335,8 +334,8 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     disco::FusedPlan fup;
     try {
         const int ch = disco::fused_mfma_channels_per_chunk();
-        const int w_bytes = (int)disco::fused_mfma_lds_bytes(8, 0, 0) + 4096;  // W slice + block offsets
-        disco::build_fused_plan(v, fp, kFusedNpx, ch, kLdsPerBlock - w_bytes - 1024, fup);
+        const int w_bytes = (int)disco::fused_mfma_reserved_bytes();
+        disco::build_fused_plan(v, fp, disco::fused_mfma_npx(), ch, kLdsPerBlock - w_bytes - 1024, fup);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
     }

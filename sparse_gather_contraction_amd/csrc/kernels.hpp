@@ -74,6 +74,8 @@ struct FusedMfmaLaunch {
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
 size_t fused_mfma_lds_bytes(int n_ot, int max_piece_elems, int max_blk);
 int fused_mfma_channels_per_chunk();
+int fused_mfma_npx();               // output longitudes per fused workgroup
+size_t fused_mfma_reserved_bytes(); // LDS bytes besides the largest piece
 int fused_max_k();  // largest K the fused kernel accepts
 
 }  // namespace disco

@@ -78,7 +78,7 @@ __device__ __forceinline__ void stage_rows(TI *lds, const TI *__restrict__ src, 
                                            int nrows, int NP, int plane0, int BC, int64_t src_plane, int row_len,
                                            int copy_len, int lrow, int stage_elems, bool vec)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     constexpr int CH = 16 / (int)sizeof(TI);
     for (int ps = 0; ps < NP; ++ps) {
         const int plane = plane0 + ps;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void staged_gather_kernel(
     const int ti = blockIdx.x / n_pg;
     const int pg = blockIdx.x - ti * n_pg;
     const Task task = tasks[ti];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int pslot = wave / wpp;
     const int plane = pg * NP + pslot;
     const bool plane_ok = plane < BC;

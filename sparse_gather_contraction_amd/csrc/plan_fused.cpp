@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <cstdint>
 #include <map>
 
 namespace disco {
@@ -32,7 +33,7 @@ int32_t round_up8(int32_t v) { return (v + 7) / 8 * 8; }
 
 }  // namespace
 
-void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int ch, int lds_budget, FusedPlan &out)
+void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int ch, int a_budget, FusedPlan &out)
 {
     out = FusedPlan();
     const int32_t s = c.Wi / c.Wo;
@@ -58,9 +59,33 @@ void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int
             }
         }
         struct SubRow { int32_t sr, astart, len; std::vector<int32_t> dblk; };
-        std::vector<SubRow> subs;
+        // blocks of one sub-row: A operand in lane order, lane l -> row r = l % 32 (k = r % 16,
+        // hi/lo part = r / 16), offsets 8 * (l / 32) + t, t < 8
+        auto append_blocks = [&](int32_t sr, int32_t astart, int32_t lds_off, int32_t row_index,
+                                 const std::vector<int32_t> &dblk) {
+            const auto &m = rowsP[sr];
+            for (int32_t d0 : dblk) {
+                FBlock b;
+                b.row = row_index;
+                b.rel = d0 - astart;
+                out.blocks.push_back(b);
+                out.block_xoff.push_back(lds_off + b.rel);
+                for (int32_t l = 0; l < 64; ++l) {
+                    const int32_t r = l % 32, k = r % 16, part = r / 16, h = l / 32;
+                    for (int32_t t = 0; t < 8; ++t) {
+                        const int32_t d = d0 + 8 * h + t;
+                        float v = 0.0f;
+                        auto it = m.find(d);
+                        if (it != m.end() && k < c.K) v = it->second[k];
+                        const uint16_t hi = bf16_rne(v);
+                        out.adata.push_back(part == 0 ? hi : bf16_rne(v - bf16_val(hi)));
+                    }
+                }
+            }
+        };
         // split each source row into blocks of 16 offsets (skipping empty ones), then into
-        // sub-rows small enough for one piece
+        // sub-rows within both piece limits
+        std::vector<SubRow> subs;
         for (auto &kv : rowsP) {
             const int32_t sr = kv.first;
             const auto &m = kv.second;
@@ -70,36 +95,41 @@ void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int
                 auto it = m.lower_bound(d0);
                 if (it != m.end() && it->first < d0 + kBlkJ) dblk.push_back(d0);
             }
-            // a sub-row must fit the budget with one channel-chunk of windows
+            auto len_of = [&](size_t a, size_t b) {
+                const int32_t astart = floor8(dblk[a]);
+                return round_up8(dblk[b - 1] + kBlkJ - astart + npx);
+            };
             size_t q = 0;
             while (q < dblk.size()) {
                 size_t q1 = q + 1;
-                auto cost = [&](size_t a, size_t b) {
-                    const int32_t astart = floor8(dblk[a]);
-                    const int32_t len = round_up8(dblk[b - 1] + kBlkJ - astart + npx);
-                    return (int64_t)ch * len * 2 + (int64_t)(b - a) * 1024;
-                };
-                while (q1 < dblk.size() && cost(q, q1 + 1) <= lds_budget) ++q1;
+                while (q1 < dblk.size() &&
+                       (int64_t)ch * len_of(q, q1 + 1) * 2 + (int64_t)(q1 + 1 - q) * 1024 <= a_budget)
+                    ++q1;
                 SubRow sub;
                 sub.sr = sr;
                 sub.astart = floor8(dblk[q]);
-                sub.len = round_up8(dblk[q1 - 1] + kBlkJ - sub.astart + npx);
+                sub.len = len_of(q, q1);
                 sub.dblk.assign(dblk.begin() + q, dblk.begin() + q1);
                 subs.push_back(std::move(sub));
                 q = q1;
             }
         }
-        // pack sub-rows into pieces
-        size_t i = 0;
-        while (i < subs.size()) {
+        // One piece with two window buffers when the whole latitude fits; otherwise pieces with one
+        // buffer (a latitude of one such piece keeps its packed blocks resident, windows staged
+        // synchronously; several pieces restage everything per channel chunk).
+        int64_t tot_len = 0, tot_blk = 0;
+        for (const SubRow &sb : subs) {
+            tot_len += sb.len;
+            tot_blk += (int64_t)sb.dblk.size();
+        }
+        const bool one_dbuf = 2 * (int64_t)ch * tot_len * 2 + tot_blk * 1024 <= a_budget;
+        auto emit = [&](size_t s0, size_t s1, int32_t dbuf) {
             FPiece pc;
             pc.blk_begin = (int32_t)out.blocks.size();
             pc.row_begin = (int32_t)out.rows.size();
             int32_t xwin = 0, nblk = 0;
-            while (i < subs.size()) {
-                const SubRow &sb = subs[i];
-                const int64_t cost = (int64_t)ch * (xwin + sb.len) * 2 + (int64_t)(nblk + sb.dblk.size()) * 1024;
-                if (nblk > 0 && cost > lds_budget) break;
+            for (size_t j = s0; j < s1; ++j) {
+                const SubRow &sb = subs[j];
                 FRow fr;
                 fr.sr = sb.sr;
                 fr.start = sb.astart;
@@ -107,40 +137,37 @@ void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int
                 fr.lds_off = xwin;
                 const int32_t row_index = (int32_t)out.rows.size();
                 out.rows.push_back(fr);
-                const auto &m = rowsP[sb.sr];
-                for (int32_t d0 : sb.dblk) {
-                    FBlock b;
-                    b.row = row_index;
-                    b.rel = d0 - sb.astart;
-                    out.blocks.push_back(b);
-                    out.block_xoff.push_back(fr.lds_off + b.rel);
-                    // A operand in lane order: lane l -> row r = l % 32 (k = r % 16, hi/lo part = r / 16),
-                    // offsets 8 * (l / 32) + t, t < 8
-                    for (int32_t l = 0; l < 64; ++l) {
-                        const int32_t r = l % 32, k = r % 16, part = r / 16, h = l / 32;
-                        for (int32_t t = 0; t < 8; ++t) {
-                            const int32_t d = d0 + 8 * h + t;
-                            float v = 0.0f;
-                            auto it = m.find(d);
-                            if (it != m.end() && k < c.K) v = it->second[k];
-                            const uint16_t hi = bf16_rne(v);
-                            out.adata.push_back(part == 0 ? hi : bf16_rne(v - bf16_val(hi)));
-                        }
-                    }
-                }
+                append_blocks(sb.sr, sb.astart, fr.lds_off, row_index, sb.dblk);
                 xwin += sb.len;
                 nblk += (int32_t)sb.dblk.size();
-                ++i;
             }
             pc.blk_end = (int32_t)out.blocks.size();
             pc.row_end = (int32_t)out.rows.size();
             pc.xwin_elems = xwin;
-            pc.pad[0] = pc.pad[1] = pc.pad[2] = 0;
+            pc.dbuf = dbuf;
+            pc.pad[0] = pc.pad[1] = 0;
             out.max_xwin = std::max(out.max_xwin, xwin);
             out.max_blk = std::max(out.max_blk, nblk);
-            out.max_piece_elems = std::max(out.max_piece_elems, nblk * 512 + ch * xwin);
+            out.max_piece_elems = std::max(out.max_piece_elems, nblk * 512 + (1 + dbuf) * ch * xwin);
             work[ho] += nblk;
             out.pieces.push_back(pc);
+        };
+        if (one_dbuf) {
+            emit(0, subs.size(), 1);
+        } else {
+            std::vector<size_t> cuts{0};
+            int64_t xwin = 0, nblk = 0;
+            for (size_t j = 0; j < subs.size(); ++j) {
+                const int64_t cost = (int64_t)ch * (xwin + subs[j].len) * 2 + (nblk + (int64_t)subs[j].dblk.size()) * 1024;
+                if (j > cuts.back() && cost > a_budget) {
+                    cuts.push_back(j);
+                    xwin = nblk = 0;
+                }
+                xwin += subs[j].len;
+                nblk += (int64_t)subs[j].dblk.size();
+            }
+            cuts.push_back(subs.size());
+            for (size_t q = 0; q + 1 < cuts.size(); ++q) emit(cuts[q], cuts[q + 1], 0);
         }
         out.mfma_blocks += work[ho];
         out.ho_piece.push_back((int32_t)out.pieces.size());

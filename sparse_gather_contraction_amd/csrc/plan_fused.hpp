@@ -48,7 +48,9 @@ struct FPiece {
     int32_t blk_begin, blk_end;   // blocks (also index the packed A data, 512 bf16 each)
     int32_t row_begin, row_end;   // rows
     int32_t xwin_elems;           // window elements per channel (sum of row lens)
-    int32_t pad[3];
+    int32_t dbuf;                 // 1: the latitude's only piece, with room for two window buffers
+                                  //    (a latitude of one piece with dbuf = 0 keeps its blocks resident)
+    int32_t pad[2];
 };
 
 struct FusedPlan {
@@ -57,7 +59,7 @@ struct FusedPlan {
     int32_t ch = 4;               // channels per chunk
     int32_t max_xwin = 0;         // max window elements per channel over all pieces
     int32_t max_blk = 0;          // max blocks per piece
-    int32_t max_piece_elems = 0;  // max over pieces of 512 * blocks + ch * window elements (bf16 elements of LDS)
+    int32_t max_piece_elems = 0;  // max over pieces of 512 * blocks + (1 + dbuf) * ch * window elements
     std::vector<int32_t> ho_piece;      // [Ho + 1]: pieces of latitude ho
     std::vector<int32_t> ho_order;      // latitudes, heaviest first
     std::vector<FPiece> pieces;
@@ -68,10 +70,12 @@ struct FusedPlan {
     int64_t mfma_blocks = 0;            // total blocks over all latitudes
 };
 
-// Build from the forward plan.  `npx` output longitudes per workgroup,
-// `ch` channels per chunk, `lds_budget` bytes available for x windows and
-// packed blocks (W is staged separately).  ok = false if the shape is outside
-// the packed kernel (K > 16, s > 2, Wo not a multiple of 8).
-void build_fused_plan(const CSRView &c, const GatherPlan &fwd, int npx, int ch, int lds_budget, FusedPlan &out);
+// Build from the forward plan.  `npx` output longitudes per workgroup, `ch`
+// channels per chunk; a piece's packed blocks plus its windows for `ch`
+// channels take at most `a_budget` bytes of LDS.  A latitude that fits in one
+// piece with two window buffers is one double-buffered piece; otherwise it is
+// split into pieces with one buffer.  ok = false if the shape is
+// outside the packed kernel (K > 16, s > 2, Wo not a multiple of 8).
+void build_fused_plan(const CSRView &c, const GatherPlan &fwd, int npx, int ch, int a_budget, FusedPlan &out);
 
 }  // namespace disco
