@@ -53,11 +53,12 @@ struct DevFused {
     bool ok = false;
     disco::FPiece *pieces = nullptr;
     disco::FRow *rows = nullptr;
-    int32_t *block_xoff = nullptr;
+    int32_t *descs = nullptr;
     uint16_t *adata = nullptr;
     int32_t *ho_piece = nullptr;
     int32_t *ho_order = nullptr;
-    int32_t npx = 0, max_piece_elems = 0, max_blk = 0;
+    int32_t max_piece_bytes = 0;
+    uint32_t desc_bytes = 0, adata_bytes = 0;
 };
 
 template <typename T>
@@ -115,7 +116,7 @@ void free_fused(DevFused &d)
 {
     (void)hipFree(d.pieces);
     (void)hipFree(d.rows);
-    (void)hipFree(d.block_xoff);
+    (void)hipFree(d.descs);
     (void)hipFree(d.adata);
     (void)hipFree(d.ho_piece);
     (void)hipFree(d.ho_order);
@@ -129,14 +130,14 @@ hipError_t upload_fused(DevFused &d, const disco::FusedPlan &p)
     hipError_t e;
     if ((e = upload(&d.pieces, p.pieces)) != hipSuccess) return e;
     if ((e = upload(&d.rows, p.rows)) != hipSuccess) return e;
-    if ((e = upload(&d.block_xoff, p.block_xoff)) != hipSuccess) return e;
+    if ((e = upload(&d.descs, p.descs)) != hipSuccess) return e;
     if ((e = upload(&d.adata, p.adata)) != hipSuccess) return e;
     if ((e = upload(&d.ho_piece, p.ho_piece)) != hipSuccess) return e;
     if ((e = upload(&d.ho_order, p.ho_order)) != hipSuccess) return e;
     d.ok = true;
-    d.npx = p.npx;
-    d.max_piece_elems = p.max_piece_elems;
-    d.max_blk = p.max_blk;
+    d.max_piece_bytes = p.max_piece_bytes;
+    d.desc_bytes = (uint32_t)(p.descs.size() * sizeof(int32_t));
+    d.adata_bytes = (uint32_t)(p.adata.size() * sizeof(uint16_t));
     return hipSuccess;
 }
 
@@ -333,9 +334,10 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     }
     disco::FusedPlan fup;
     try {
+        // two piece stage buffers share what the W slice leaves of the workgroup's LDS
         const int ch = disco::fused_mfma_channels_per_chunk();
-        const int w_bytes = (int)disco::fused_mfma_reserved_bytes();
-        disco::build_fused_plan(v, fp, disco::fused_mfma_npx(), ch, kLdsPerBlock - w_bytes - 1024, fup);
+        const int budget = ((kLdsPerBlock - (int)disco::fused_mfma_reserved_bytes()) / 2) & ~15;
+        disco::build_fused_plan(v, ch, budget, fup);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
     }
@@ -395,8 +397,8 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
                 sfp[1].stages.size(), sfp[1].T, sfp[1].G, h->sbwd[1].ok ? "on" : "off", sbp[1].tasks.size(),
                 sbp[1].stages.size());
     if (log_enabled())
-        fprintf(stderr, "[disco] fused packed plan %s: %zu pieces, %lld blocks, max %d blocks/piece, window %d\n",
-                fup.ok ? "on" : "off", fup.pieces.size(), (long long)fup.mfma_blocks, fup.max_blk, fup.max_xwin);
+        fprintf(stderr, "[disco] fused packed plan %s: %zu pieces, %lld blocks, largest stage %d bytes, window %d\n",
+                fup.ok ? "on" : "off", fup.pieces.size(), (long long)fup.mfma_blocks, fup.max_piece_bytes, fup.max_win);
     *out_handle = h;
     return DISCO_OK;
 }
@@ -482,11 +484,12 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     if (h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
-        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.block_xoff = h->fused.block_xoff; m.adata = h->fused.adata;
+        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs; m.adata = h->fused.adata;
         m.ho_piece = h->fused.ho_piece; m.ho_order = h->fused.ho_order;
         m.B = (int32_t)B; m.C = (int32_t)C; m.Co = (int32_t)Co; m.K = h->K;
         m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi; m.s = h->Wi / h->Wo;
-        m.npx = h->fused.npx; m.max_piece_elems = h->fused.max_piece_elems; m.max_blk = h->fused.max_blk;
+        m.max_piece_bytes = h->fused.max_piece_bytes;
+        m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
         hipError_t e = disco::launch_fused_mfma(m, (hipStream_t)stream);
         if (e != hipSuccess)
             return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));

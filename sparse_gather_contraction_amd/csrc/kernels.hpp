@@ -65,17 +65,17 @@ struct FusedMfmaLaunch {
     void *y;
     const FPiece *pieces;
     const FRow *rows;
-    const int32_t *block_xoff;
+    const int32_t *descs;
     const uint16_t *adata;
     const int32_t *ho_piece, *ho_order;
-    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, npx, max_piece_elems, max_blk;
+    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, max_piece_bytes;
+    uint32_t desc_bytes, adata_bytes;  // sizes of the descriptor and psi arrays
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
-size_t fused_mfma_lds_bytes(int n_ot, int max_piece_elems, int max_blk);
+size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes);
 int fused_mfma_channels_per_chunk();
-int fused_mfma_npx();               // output longitudes per fused workgroup
-size_t fused_mfma_reserved_bytes(); // LDS bytes besides the largest piece
+size_t fused_mfma_reserved_bytes();  // LDS bytes besides the two piece stage buffers
 int fused_max_k();  // largest K the fused kernel accepts
 
 }  // namespace disco

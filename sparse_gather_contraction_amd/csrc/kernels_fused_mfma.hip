@@ -2,29 +2,33 @@
 //
 // y[b,o,ho,wo] = sum_{c,k} W[o,c,k] * out[b,c,k,ho,wo], out = CSR contraction
 // ("contraction + einsum", torch-harmonics "disco-kernel-dev" page,
-// "Architecture snapshot"; the packed-psi idea follows its "kpacked layout"
-// section, re-derived for MFMA).
+// "Architecture snapshot"; its tensor-core forward takes psi in the bf16
+// compute type, "kpacked layout" section — here psi is packed per source row
+// instead, re-derived for MFMA).
 //
-// Workgroup = (b, ho, npx output longitudes, up to 256 output channels);
-// wave w owns the 32 longitudes [px0 + 32w, px0 + 32w + 32) and all output
-// channels.  Input channels are walked in chunks of kCh:
-//  1. stage: the packed A blocks of the latitude's psi piece, the x windows
-//     of the piece's source rows for the kCh channels, and the chunk's W
-//     slice in MFMA A-operand order;
-//  2. contraction: for each block, one v_mfma_f32_32x32x16_bf16 per channel,
-//     A = [bf16(psi) ; bf16 residue] (32 x 16), B = 16 consecutive x values
-//     per longitude (eight aligned 2-byte LDS reads per lane);
-//  3. einsum, chained in registers: lane (h = lane/32) holds out[k] for
-//     k in {4h..4h+3, 8+4h..8+4h+3} (sum of the two psi halves), which is
-//     exactly the B operand of the next v_mfma_f32_32x32x16_bf16 when the
-//     reduction rows of one channel are ordered that way; W is packed to the
-//     same order.  fp32 accumulators for 256 output channels x 32 longitudes
-//     stay in registers across all chunks.
-// A latitude whose packed psi is one piece keeps it resident and
-// double-buffers the x windows: the next chunk's windows stream into LDS by
-// direct global->LDS loads while the current chunk is contracted.  Caps
-// spanning whole rings (several pieces) stage synchronously per piece.
-// No atomics; every output is written once.
+// Workgroup = (b, ho, 256 output longitudes, up to 256 output channels), eight
+// waves.  Waves w and w + 4 share the phase pair q = 2(w % 4) + {0, 1}: the 64
+// longitudes px0 + 8n + q, n < 32.  Input channels are walked in chunks of
+// kCh = 4; within a chunk the latitude's psi pieces are streamed (a "step" is
+// one piece of one chunk):
+//  * contraction (wave half h2 = w / 4 takes channels 2 h2, 2 h2 + 1 of the
+//    chunk): per block (16 offsets d0..d0+15 of one source row) and channel,
+//    one v_mfma_f32_32x32x16_bf16 with
+//      A = psi rows (k, q) for the wave's two phases, P[k, d0 + t - q]
+//          (eight 2-byte LDS reads per lane; one A serves both channels),
+//      B = x[px0 + 8n + d0 + t], which is phase independent and read as one
+//          aligned 16-byte LDS run per lane;
+//  * einsum (wave half h2 takes half of the output-channel tiles): the result
+//    rows are ordered so that a lane holds the reduction slots 8h..8h+7 =
+//    basis k of one longitude for each phase, i.e. exactly the B operand of
+//    v_mfma_f32_32x32x16_bf16 against W (A operand: W[o, c, 8h..8h+7],
+//    contiguous in memory).  The two waves of a pair swap their channels'
+//    operands (bf16) through LDS.  fp32 accumulators for 128 output channels
+//    x 64 longitudes stay in registers across all chunks.
+// Stage buffers are double-buffered: the next step's block descriptors, psi
+// and x windows stream into LDS by direct global->LDS loads while the
+// current step is contracted; the chunk's W slice likewise.  No atomics;
+// every output is written once.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan_fused.hpp"
@@ -35,20 +39,38 @@ namespace {
 
 constexpr int kCh = 4;          // input channels per chunk
 constexpr int kMaxOt = 8;       // 32-row output-channel tiles per workgroup (256 channels)
-constexpr int kNpx = 256;       // output longitudes per workgroup (8 waves)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWBytes = kMaxOt * kCh * 1024;  // W slice of one chunk
+constexpr int kXchBytes = kWaves * 4 * 1024;  // operand exchange (2 channels x 2 phases per wave)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Eight consecutive bf16 at a 2-byte aligned LDS address (element loads keep the alias
-// information of the pointer they are based on).
-__device__ __forceinline__ bf16x8 lds8(const bf16_t *p)
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (reads past the end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct global -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i of the
+// instruction writes LDS base `l` + 16 i.  The buffer form (rather than the global form) keeps
+// the compiler's LDS wait counting exact for the LDS reads that overlap the transfer.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *l)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)l, 16, voff, 0, 0, 0);
+}
+
+// Eight bf16 at p[0], p[16], ..., p[112] (psi column of one basis function).
+__device__ __forceinline__ bf16x8 lds_col8(const bf16_t *p)
 {
     const __bf16 *q = reinterpret_cast<const __bf16 *>(p);
     bf16x8 v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = q[i];
+    for (int i = 0; i < 8; ++i) v[i] = q[16 * i];
     return v;
 }
 
@@ -60,286 +82,332 @@ __device__ __forceinline__ int mod_l(int g, int L)
 
 struct Ctx {
     const bf16_t *x, *W;
+    __amdgpu_buffer_rsrc_t descs_rs, adata_rs, w_rs;
     const FRow *rows;
-    const bf16_t *adata;
-    const int32_t *block_xoff;
-    bf16_t *w_area, *a_area;
-    int32_t *o_area;
-    int B, C, Co, K, L, Wi, s, n_ot, b, px0, o_base, tid, nthreads, wave, nwaves, lane, col, h, pxw;
+    int B, C, Co, K, L, Wi, s, n_ot, b, px0, o_base, tid, wave, lane;
     int64_t plane_sz;
+    bool vec_x, vec_w;
 };
 
-// W slice of the chunk starting at channel c0, in A-operand order: entry (ot, cl, lane).
-__device__ __forceinline__ void stage_w(const Ctx &c, int c0)
+// ---- staging ---------------------------------------------------------------------------------
+
+// Contiguous global -> LDS copy of n16 16-byte units starting at byte voff of buffer r, spread
+// over the workgroup (lane i of a wave's instruction writes base + 16 i).
+__device__ __forceinline__ void copy_units(const Ctx &c, __amdgpu_buffer_rsrc_t r, uint32_t voff, unsigned char *dst,
+                                           int n16)
 {
-    for (int e = c.tid; e < c.n_ot * kCh * 64; e += c.nthreads) {
-        const int ln = e & 63;
-        const int t2 = e >> 6;
-        const int cl = t2 % kCh, ot = t2 / kCh;
-        const int o = c.o_base + ot * 32 + (ln & 31);
-        const int hh = ln >> 5;
-        const int ch = c0 + cl;
-        uint2 lo4 = make_uint2(0u, 0u), hi4 = make_uint2(0u, 0u);
-        if (c.K == 16) {
-            if (o < c.Co && ch < c.C) {
-                const bf16_t *wr = c.W + ((int64_t)o * c.C + ch) * 16;
-                lo4 = *reinterpret_cast<const uint2 *>(wr + 4 * hh);
-                hi4 = *reinterpret_cast<const uint2 *>(wr + 8 + 4 * hh);
-            }
-        } else {
-            i16x8 v;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int k = (i < 4) ? 4 * hh + i : 8 + 4 * hh + (i - 4);
-                v[i] = (o < c.Co && ch < c.C && k < c.K) ? (short)c.W[((int64_t)o * c.C + ch) * c.K + k] : (short)0;
-            }
-            const uint4 u = __builtin_bit_cast(uint4, v);
-            lo4 = make_uint2(u.x, u.y);
-            hi4 = make_uint2(u.z, u.w);
-        }
-        *reinterpret_cast<uint4 *>(c.w_area + (int64_t)e * 8) = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
+    for (int u0 = c.wave * 64; u0 < n16; u0 += kThreads) {
+        const int u = u0 + c.lane;
+        if (u < n16) dma16(r, voff + 16u * (uint32_t)u, dst + 16 * u0);
     }
 }
 
-// Packed A blocks and block offsets of a piece.
-__device__ __forceinline__ void stage_a(const Ctx &c, const FPiece &pc, int nblk)
+// x windows of one piece for the chunk starting at channel c0.
+__device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, int c0, bf16_t *win)
 {
-    const uint4 *src = reinterpret_cast<const uint4 *>(c.adata + (int64_t)pc.blk_begin * 512);
-    uint4 *dst = reinterpret_cast<uint4 *>(c.a_area);
-    for (int e = c.tid; e < nblk * 64; e += c.nthreads) dst[e] = src[e];
-    for (int e = c.tid; e < nblk; e += c.nthreads) c.o_area[e] = c.block_xoff[pc.blk_begin + e];
-}
-
-// x windows of one chunk, synchronous: rows over waves, positions over lanes; channels past C are zeros.
-__device__ __forceinline__ void stage_windows(const Ctx &c, bf16_t *xbuf, const FPiece &pc, int xwin, int c0,
-                                              bool vec)
-{
-    const int ccn = min(kCh, c.C - c0);
     const int nrows = pc.row_end - pc.row_begin;
-    for (int cl = 0; cl < kCh; ++cl) {
-        for (int r = c.wave; r < nrows; r += c.nwaves) {
-            const FRow fr = c.rows[pc.row_begin + r];
-            bf16_t *dst = xbuf + cl * xwin + fr.lds_off;
-            if (cl >= ccn) {
-                for (int e8 = c.lane; e8 < (fr.len >> 3); e8 += 64)
-                    *reinterpret_cast<uint4 *>(dst + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
-                continue;
-            }
-            const int hi = fr.sr / c.s, rho = fr.sr - hi * c.s;
-            const bf16_t *xrow = c.x + ((int64_t)c.b * c.C + (c0 + cl)) * c.plane_sz + (int64_t)hi * c.Wi;
-            const int g0 = mod_l(c.px0 + fr.start, c.L);
-            if (vec) {
-                // s == 1: 8-element chunks never straddle the row end (L and g0 are multiples of 8)
-                for (int e8 = c.lane; e8 < (fr.len >> 3); e8 += 64) {
-                    int pos = g0 + 8 * e8;
-                    while (pos >= c.L) pos -= c.L;
-                    *reinterpret_cast<uint4 *>(dst + 8 * e8) = *reinterpret_cast<const uint4 *>(xrow + pos);
-                }
-            } else {
-                for (int e = c.lane; e < fr.len; e += 64) {
-                    int pos = g0 + e;
-                    while (pos >= c.L) pos -= c.L;
-                    dst[e] = xrow[(int64_t)c.s * pos + rho];
-                }
-            }
+    const int ccn = min(kCh, c.C - c0);
+    for (int q = c.wave; q < kCh * nrows; q += kWaves) {
+        const int cl = q / nrows, r = q - cl * nrows;
+        const FRow fr = c.rows[pc.row_begin + r];
+        bf16_t *dst = win + cl * pc.win_elems + fr.win_off;
+        const int nch = fr.len >> 3;
+        if (cl >= ccn) {
+            for (int e8 = c.lane; e8 < nch; e8 += 64)
+                *reinterpret_cast<uint4 *>(dst + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
+            continue;
         }
-    }
-}
-
-// x windows of one chunk queued as direct global->LDS loads (global_load_lds_dwordx4: lane i of
-// an instruction writes LDS base + 16*i).  s == 1 and 16-byte aligned rows only.  The caller
-// waits (s_waitcnt + barrier) before the windows are read; channels past C get zero stores.
-__device__ __forceinline__ void queue_windows(const Ctx &c, bf16_t *xbuf, const FPiece &pc, int xwin, int c0)
-{
-    const int ccn = min(kCh, c.C - c0);
-    const int nrows = pc.row_end - pc.row_begin;
-    for (int cl = 0; cl < kCh; ++cl) {
-        for (int r = c.wave; r < nrows; r += c.nwaves) {
-            const FRow fr = c.rows[pc.row_begin + r];
-            bf16_t *dst = xbuf + cl * xwin + fr.lds_off;
-            const int nch = fr.len >> 3;
-            if (cl >= ccn) {
-                for (int e8 = c.lane; e8 < nch; e8 += 64)
-                    *reinterpret_cast<uint4 *>(dst + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
-                continue;
-            }
-            const bf16_t *xrow = c.x + ((int64_t)c.b * c.C + (c0 + cl)) * c.plane_sz + (int64_t)fr.sr * c.Wi;
-            const int g0 = mod_l(c.px0 + fr.start, c.L);
+        const int g0 = mod_l(c.px0 + fr.start, c.L);
+        const bf16_t *plane = c.x + ((int64_t)c.b * c.C + (c0 + cl)) * c.plane_sz;
+        if (c.vec_x) {
+            // s == 1, rows 16-byte aligned: 8-position runs never straddle the row end
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(plane, (uint32_t)(2 * c.plane_sz));
+            const uint32_t row0 = 2u * (uint32_t)(fr.sr * c.Wi);
             for (int t = 0; t < nch; t += 64) {
                 const int e8 = t + c.lane;
                 if (e8 < nch) {
                     int pos = g0 + 8 * e8;
                     while (pos >= c.L) pos -= c.L;
-                    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(xrow + pos),
-                                                     (void __attribute__((address_space(3))) *)(dst + 8 * t), 16, 0,
-                                                     0);
+                    dma16(rs, row0 + 2u * (uint32_t)pos, dst + 8 * t);
                 }
             }
-        }
-    }
-}
-
-// Contraction of one piece on the matrix cores.  Operands of block i+1 are read while block
-// i's MFMAs run; the body is straight-line (the last iteration re-reads the last block) so
-// LDS waits stay partial.
-__device__ __forceinline__ void contract(const Ctx &c, const bf16_t *x_area, int xwin, int nblk, f32x16 (&d)[kCh])
-{
-    if (nblk <= 0) return;
-    const int32_t *boff = c.o_area;
-    const int lane_x = c.pxw + c.col + 8 * c.h;
-    const bf16_t *a_lane = c.a_area + c.lane * 8;
-    int off_n = boff[0] + lane_x;
-    int off_nn = boff[nblk > 1 ? 1 : 0];
-    bf16x8 a_n = *reinterpret_cast<const bf16x8 *>(a_lane);
-    bf16x8 bop[kCh];
-#pragma unroll
-    for (int cl = 0; cl < kCh; ++cl) bop[cl] = lds8(x_area + cl * xwin + off_n);
-    for (int i = 0; i < nblk; ++i) {
-        const bf16x8 a_c = a_n;
-        const int ip = min(i + 1, nblk - 1);
-        off_n = off_nn + lane_x;
-        off_nn = boff[min(i + 2, nblk - 1)];
-        a_n = *reinterpret_cast<const bf16x8 *>(a_lane + ip * 512);
-#pragma unroll
-        for (int cl = 0; cl < kCh; ++cl) {
-            d[cl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_c, bop[cl], d[cl], 0, 0, 0);
-            bop[cl] = lds8(x_area + cl * xwin + off_n);
-        }
-    }
-}
-
-// Einsum of a chunk into the y accumulators.
-__device__ __forceinline__ void einsum(const Ctx &c, f32x16 (&d)[kCh], f32x16 (&yacc)[kMaxOt])
-{
-#pragma unroll
-    for (int cl = 0; cl < kCh; ++cl) {
-        bf16x8 bop;
-#pragma unroll
-        for (int a = 0; a < 8; ++a) bop[a] = (__bf16)(d[cl][a] + d[cl][a + 8]);
-#pragma unroll
-        for (int ot = 0; ot < kMaxOt; ++ot) {
-            if (ot < c.n_ot) {
-                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(c.w_area + ((ot * kCh + cl) * 64 + c.lane) * 8);
-                yacc[ot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aw, bop, yacc[ot], 0, 0, 0);
+        } else {
+            const int hi = fr.sr / c.s, rho = fr.sr - hi * c.s;
+            const bf16_t *xrow = plane + (int64_t)hi * c.Wi;
+            for (int e = c.lane; e < fr.len; e += 64) {
+                int pos = g0 + e;
+                while (pos >= c.L) pos -= c.L;
+                dst[e] = xrow[(int64_t)c.s * pos + rho];
             }
         }
     }
 }
 
-__device__ __forceinline__ void zero(f32x16 (&d)[kCh])
+// One step's stage: block descriptors, psi and windows of piece pc for channels c0..c0+kCh-1.
+__device__ __forceinline__ void stage_step(const Ctx &c, const FPiece &pc, int c0, unsigned char *buf)
+{
+    copy_units(c, c.descs_rs, 8u * (uint32_t)pc.desc_begin, buf, pc.desc_words / 4);
+    unsigned char *a_area = buf + 4 * pc.desc_words;
+    copy_units(c, c.adata_rs, 2u * (uint32_t)pc.a_begin, a_area, pc.a_elems / 8);
+    stage_windows(c, pc, c0, reinterpret_cast<bf16_t *>(a_area + 2 * pc.a_elems));
+}
+
+// W slice of the chunk starting at c0 in A-operand order: unit (ot, cl), lane l holds
+// W[o_base + 32 ot + l % 32, c0 + cl, 8 (l / 32) .. + 7].
+__device__ __forceinline__ void stage_w(const Ctx &c, int c0, unsigned char *wb)
+{
+    const int o = c.o_base + (c.lane & 31);
+    const int hh = c.lane >> 5;
+    for (int u = c.wave; u < c.n_ot * kCh; u += kWaves) {
+        const int ot = u / kCh, cl = u - ot * kCh;
+        const int oo = o + 32 * ot, ch = c0 + cl;
+        unsigned char *dst = wb + 1024 * u;
+        const bool ok = oo < c.Co && ch < c.C;
+        if (c.vec_w) {
+            if (ok) dma16(c.w_rs, 2u * (uint32_t)(((int64_t)oo * c.C + ch) * 16 + 8 * hh), dst);
+            else *reinterpret_cast<uint4 *>(dst + 16 * c.lane) = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            i16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = 8 * hh + i;
+                v[i] = (ok && k < c.K) ? (short)c.W[((int64_t)oo * c.C + ch) * c.K + k] : (short)0;
+            }
+            *reinterpret_cast<i16x8 *>(dst + 16 * c.lane) = v;
+        }
+    }
+}
+
+// ---- compute ---------------------------------------------------------------------------------
+
+// Operands of one block: the psi column as eight raw 2-byte reads (packed at the point of use,
+// so that the wait for them falls just before the MFMA) and the two channels' x runs.
+struct Ops {
+    unsigned short a[8];
+    bf16x8 b0, b1;
+};
+
+__device__ __forceinline__ void load_ops(Ops &o, const unsigned char *a_base, const unsigned char *x_base, int wel2,
+                                         int a_off, int x_off)
+{
+    o.b0 = *reinterpret_cast<const bf16x8 *>(x_base + x_off);
+    o.b1 = *reinterpret_cast<const bf16x8 *>(x_base + wel2 + x_off);
+    const unsigned short *p = reinterpret_cast<const unsigned short *>(a_base + a_off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.a[i] = p[16 * i];
+}
+
+__device__ __forceinline__ void mfma_ops(const Ops &o, f32x16 (&d)[2])
+{
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (unsigned)o.a[2 * i] | ((unsigned)o.a[2 * i + 1] << 16);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+    d[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b0, d[0], 0, 0, 0);
+    d[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b1, d[1], 0, 0, 0);
+}
+
+// Contraction of one step for the wave's two channels.  Blocks go in pairs (P, Q): the operands
+// of one block are read while the other block's MFMAs run, and the descriptors of a pair are
+// read two pairs ahead.  Scheduling barriers keep that order (the compiler would otherwise
+// move the reads next to their uses).
+__device__ __forceinline__ void contract(const unsigned char *__restrict__ buf, const FPiece &pc, int a_lane2,
+                                         int x_lane2, int ch0, f32x16 (&d)[2])
+{
+    const int npair = pc.nblk >> 1;
+    if (npair <= 0) return;
+    const int4 *desc = reinterpret_cast<const int4 *>(buf);
+    const unsigned char *a_base = buf + 4 * pc.desc_words + a_lane2;
+    const int wel2 = 2 * pc.win_elems;
+    const unsigned char *x_base = buf + 4 * pc.desc_words + 2 * pc.a_elems + ch0 * wel2 + x_lane2;
+    const int lastp = npair - 1;
+    int4 dA = desc[0];
+    int4 dB = desc[min(1, lastp)];
+    Ops P, Q;
+    load_ops(P, a_base, x_base, wel2, dA.x, dA.y);
+    for (int j = 0; j < npair; ++j) {
+        const int4 dC = desc[min(j + 2, lastp)];
+        load_ops(Q, a_base, x_base, wel2, dA.z, dA.w);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_ops(P, d);
+        __builtin_amdgcn_sched_barrier(0);
+        load_ops(P, a_base, x_base, wel2, dB.x, dB.y);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_ops(Q, d);
+        __builtin_amdgcn_sched_barrier(0);
+        dA = dB;
+        dB = dC;
+    }
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &v, int base)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) r[a] = (__bf16)v[base + a];
+    return r;
+}
+
+// Einsum of a chunk: swap operands with the partner wave through `xch`, then accumulate the
+// wave's NOT/2 output-channel tiles for both phases.  Caller: barrier before (everyone done with
+// `xch` as a stage buffer, W slice visible).
+template <int NOTH>
+__device__ __forceinline__ void einsum(unsigned char *__restrict__ xch, const unsigned char *__restrict__ wb,
+                                       int lane, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
+{
+    bf16x8 own[2][2], oth[2][2];
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph) {
+            own[cl][ph] = to_bf16x8(d[cl], 8 * ph);
+            *reinterpret_cast<bf16x8 *>(xch + 1024 * (((pp * 2 + h2) * 2 + cl) * 2 + ph) + 16 * lane) = own[cl][ph];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph)
+            oth[cl][ph] =
+                *reinterpret_cast<const bf16x8 *>(xch + 1024 * (((pp * 2 + (1 - h2)) * 2 + cl) * 2 + ph) + 16 * lane);
+#pragma unroll
+    for (int j = 0; j < NOTH; ++j) {
+        const int ot = h2 * NOTH + j;
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+            const bf16x8 wo = *reinterpret_cast<const bf16x8 *>(wb + 1024 * (ot * kCh + 2 * h2 + cl) + 16 * lane);
+            const bf16x8 wt = *reinterpret_cast<const bf16x8 *>(wb + 1024 * (ot * kCh + 2 * (1 - h2) + cl) + 16 * lane);
+            yacc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wo, own[cl][0], yacc[0][j], 0, 0, 0);
+            yacc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wo, own[cl][1], yacc[1][j], 0, 0, 0);
+            yacc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wt, oth[cl][0], yacc[0][j], 0, 0, 0);
+            yacc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wt, oth[cl][1], yacc[1][j], 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void zero(f32x16 (&d)[2])
 {
 #pragma unroll
-    for (int cl = 0; cl < kCh; ++cl)
+    for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
         for (int a = 0; a < 16; ++a) d[cl][a] = 0.0f;
 }
 
-// One chunk of a double-buffered latitude: contract from `cur` while the next chunk's windows
-// stream into `nxt`.  The two buffers are restrict parameters so that the compiler knows the
-// queued direct loads do not alias the reads (it then keeps the LDS waits partial).
-__device__ __forceinline__ void dbuf_step(const Ctx &c, const FPiece &pc, int xwin, int nblk, int c0,
-                                          const bf16_t *__restrict__ cur, bf16_t *__restrict__ nxt,
-                                          f32x16 (&yacc)[kMaxOt])
+// One step: wait for its stage, queue the next step's stage (and the chunk's W slice at a
+// chunk start), contract, and run the einsum at the chunk's last piece (the consumed stage
+// buffer then carries the operand exchange).  The buffers are restrict parameters so that the
+// compiler keeps the queued direct loads in flight across the LDS reads of the current stage.
+template <int NOTH>
+__device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
+                                         int nsteps, int st, int t, int p, unsigned char *__restrict__ cur,
+                                         unsigned char *__restrict__ nxt, unsigned char *__restrict__ wb, int a_lane2,
+                                         int x_lane2, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
 {
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` have landed
-    __syncthreads();                // everyone's have; the previous chunk is done with W and `nxt`
-    stage_w(c, c0);
-    __syncthreads();                // W slice visible (a full fence: nothing may be in flight yet)
-    if (c0 + kCh < c.C) queue_windows(c, nxt, pc, xwin, c0 + kCh);  // lands while this chunk computes
-    f32x16 d[kCh];
-    zero(d);
-    contract(c, cur, xwin, nblk, d);
-    einsum(c, d, yacc);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` (and W) have landed
+    __syncthreads();                // everyone's have; the previous step is done with `nxt` and W
+    if (p == 0 && t > 0) stage_w(c, kCh * t, wb);
+    if (st + 1 < nsteps) {
+        const int p1 = (p + 1 == npieces) ? 0 : p + 1;
+        const int t1 = (p + 1 == npieces) ? t + 1 : t;
+        stage_step(c, pieces[p_begin + p1], kCh * t1, nxt);
+    }
+    if (p == 0) zero(d);
+    const FPiece pc = pieces[p_begin + p];
+    contract(cur, pc, a_lane2, x_lane2, 2 * h2, d);
+    if (p + 1 == npieces) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // W slice visible; `cur` free for the exchange
+        einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
+    }
 }
 
-__global__ __launch_bounds__(512) void fused_mfma_kernel(
+template <int NOT>
+__global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ W, bf16_t *__restrict__ y,
-    const FPiece *__restrict__ pieces, const FRow *__restrict__ rows, const int32_t *__restrict__ block_xoff,
+    const FPiece *__restrict__ pieces, const FRow *__restrict__ rows, const int32_t *__restrict__ descs,
     const bf16_t *__restrict__ adata, const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order,
-    int B, int C, int Co, int K, int Ho, int L, int Hi, int Wi, int s, int n_pxb, int n_ob, int n_ot, int max_blk,
-    int vec)
+    int B, int C, int Co, int K, int Ho, int L, int Hi, int Wi, int s, int n_pxb, int n_ob, int buf_bytes,
+    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w)
 {
-    // LDS: [W slice: n_ot*kCh*512 bf16] [block offsets: max_blk int32 (16-B rounded)]
-    //      [piece: blocks*512 bf16 | x windows: kCh*xwin bf16, twice for a double-buffered piece]
+    constexpr int NOTH = NOT / 2;
+    // LDS: [W slice: NOT * kCh KiB] [stage buffer 0] [stage buffer 1]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    Ctx c;
-    c.w_area = reinterpret_cast<bf16_t *>(smem);
-    c.o_area = reinterpret_cast<int32_t *>(c.w_area + n_ot * kCh * 512);
-    c.a_area = reinterpret_cast<bf16_t *>(c.o_area + ((max_blk + 3) & ~3));
+    unsigned char *wb = smem;
+    unsigned char *buf0 = smem + NOT * kCh * 1024;
+    unsigned char *buf1 = buf0 + buf_bytes;
 
     int bid = blockIdx.x;
     const int pxb = bid % n_pxb;
     bid /= n_pxb;
     const int ob = bid % n_ob;
     bid /= n_ob;
+    Ctx c;
     c.b = bid % B;
     const int ho = ho_order[bid / B];
-
-    c.x = x; c.W = W; c.rows = rows; c.adata = adata; c.block_xoff = block_xoff;
-    c.B = B; c.C = C; c.Co = Co; c.K = K; c.L = L; c.Wi = Wi; c.s = s; c.n_ot = n_ot;
-    c.nthreads = blockDim.x;
-    c.nwaves = c.nthreads >> 6;
+    c.x = x; c.W = W; c.rows = rows;
+    c.descs_rs = make_rsrc(descs, desc_bytes);
+    c.adata_rs = make_rsrc(adata, adata_bytes);
+    c.w_rs = make_rsrc(W, vec_w ? (uint32_t)(2 * (int64_t)Co * C * 16) : 0u);
+    c.B = B; c.C = C; c.Co = Co; c.K = K; c.L = L; c.Wi = Wi; c.s = s; c.n_ot = NOT;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
-    c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);  // wave-uniform: row loops run on the scalar unit
-    c.col = c.lane & 31;
-    c.h = c.lane >> 5;
-    c.px0 = pxb * kNpx;
-    c.pxw = c.wave * 32;
+    c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    c.px0 = pxb * kFusedSpan;
     c.o_base = ob * (kMaxOt * 32);
     c.plane_sz = (int64_t)Hi * Wi;
-    const int p_begin = ho_piece[ho], p_end = ho_piece[ho + 1];
+    c.vec_x = vec_x != 0;
+    c.vec_w = vec_w != 0;
 
-    f32x16 yacc[kMaxOt];
-#pragma unroll
-    for (int ot = 0; ot < kMaxOt; ++ot)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) yacc[ot][a] = 0.0f;
+    // lane constants: A row r = lane % 32 is (phase q = 2 pp + r / 16, MFMA row m = r % 16 -> basis k);
+    // the basis order puts k = 8h + a in result register a of lane half h
+    const int pp = c.wave & 3, h2 = c.wave >> 2;
+    const int r = c.lane & 31, hh = c.lane >> 5;
+    const int m = r & 15, q = 2 * pp + (r >> 4);
+    const int kb = (m < 8) ? 8 * (m >> 2) + (m & 3) : 8 * ((m - 8) >> 2) + 4 + (m & 3);
+    const int a_lane2 = 2 * ((8 * hh - q) * 16 + kb);  // bytes
+    const int x_lane2 = 2 * (8 * r + 8 * hh);            // bytes
 
-    const FPiece pc0 = pieces[p_begin];
-    if (vec && pc0.dbuf) {
-        // One piece: packed A resident, x windows double-buffered.
-        const FPiece pc = pc0;
-        const int nblk = pc.blk_end - pc.blk_begin;
-        const int xwin = pc.xwin_elems;
-        bf16_t *xs0 = c.a_area + nblk * 512;
-        bf16_t *xs1 = xs0 + kCh * xwin;
-        stage_a(c, pc, nblk);
-        queue_windows(c, xs0, pc, xwin, 0);
-        for (int c0 = 0; c0 < C; c0 += 2 * kCh) {
-            dbuf_step(c, pc, xwin, nblk, c0, xs0, xs1, yacc);
-            if (c0 + kCh < C) dbuf_step(c, pc, xwin, nblk, c0 + kCh, xs1, xs0, yacc);
-        }
-    } else {
-        for (int c0 = 0; c0 < C; c0 += kCh) {
-            f32x16 d[kCh];
-            zero(d);
-            for (int pi = p_begin; pi < p_end; ++pi) {
-                const FPiece pc = pieces[pi];
-                const int nblk = pc.blk_end - pc.blk_begin;
-                const int xwin = pc.xwin_elems;
-                bf16_t *x_area = c.a_area + nblk * 512;
-                __syncthreads();  // previous piece's LDS (and the previous chunk's W slice) fully consumed
-                if (pi == p_begin) stage_w(c, c0);
-                if (c0 == 0 || p_end - p_begin > 1) stage_a(c, pc, nblk);
-                stage_windows(c, x_area, pc, xwin, c0, vec != 0);
-                __syncthreads();
-                contract(c, x_area, xwin, nblk, d);
+    f32x16 yacc[2][NOTH];
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph)
+#pragma unroll
+        for (int j = 0; j < NOTH; ++j)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) yacc[ph][j][a] = 0.0f;
+    f32x16 d[2];
+    zero(d);
+
+    const int p_begin = ho_piece[ho];
+    const int npieces = ho_piece[ho + 1] - p_begin;
+    const int nchunks = (C + kCh - 1) / kCh;
+    const int nsteps = npieces * nchunks;
+    if (nsteps > 0) {
+        stage_w(c, 0, wb);
+        stage_step(c, pieces[p_begin], 0, buf0);
+        int t = 0, p = 0;
+        for (int st = 0; st < nsteps; st += 2) {
+            run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, pp, h2, d,
+                           yacc);
+            if (++p == npieces) { p = 0; ++t; }
+            if (st + 1 < nsteps) {
+                run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, pp,
+                               h2, d, yacc);
+                if (++p == npieces) { p = 0; ++t; }
             }
-            einsum(c, d, yacc);
         }
     }
 
-    // ---- epilogue: yacc[ot] row = output channel, column = longitude ----
-    const int wo = c.px0 + c.pxw + c.col;
-    if (wo < L) {
+    // ---- epilogue: yacc[ph][j] row = output channel, column n = longitude px0 + 8n + 2 pp + ph ----
 #pragma unroll
-        for (int ot = 0; ot < kMaxOt; ++ot) {
-            if (ot < n_ot) {
+    for (int ph = 0; ph < 2; ++ph) {
+        const int wo = c.px0 + 8 * r + 2 * pp + ph;
+        if (wo < L) {
+#pragma unroll
+            for (int j = 0; j < NOTH; ++j) {
 #pragma unroll
                 for (int a = 0; a < 16; ++a) {
-                    const int o = c.o_base + ot * 32 + 8 * (a >> 2) + 4 * c.h + (a & 3);
-                    if (o < Co) y[(((int64_t)c.b * Co + o) * Ho + ho) * L + wo] = f32_to_bf16(yacc[ot][a]);
+                    const int o = c.o_base + (h2 * NOTH + j) * 32 + 8 * (a >> 2) + 4 * hh + (a & 3);
+                    if (o < Co) y[(((int64_t)c.b * Co + o) * Ho + ho) * L + wo] = f32_to_bf16(yacc[ph][j][a]);
                 }
             }
         }
@@ -348,38 +416,47 @@ __global__ __launch_bounds__(512) void fused_mfma_kernel(
 
 }  // namespace
 
-size_t fused_mfma_lds_bytes(int n_ot, int max_piece_elems, int max_blk)
-{
-    return (size_t)n_ot * kCh * 512 * 2 + (size_t)((max_blk + 3) & ~3) * 4 + (size_t)max_piece_elems * 2;
-}
-
 int fused_mfma_channels_per_chunk() { return kCh; }
 
-int fused_mfma_npx() { return kNpx; }
+size_t fused_mfma_reserved_bytes() { return (size_t)kWBytes; }
 
-size_t fused_mfma_reserved_bytes()
+size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes)
 {
-    // W slice at the largest output-channel tile count, plus the block offsets of a piece
-    // (a piece holds at most 160 KiB / 1 KiB blocks)
-    return (size_t)kMaxOt * kCh * 512 * 2 + 160 * 4 + 16;
+    const size_t buf = std::max<size_t>(((size_t)max_piece_bytes + 15) & ~(size_t)15, (size_t)kXchBytes);
+    return (size_t)n_ot * kCh * 1024 + 2 * buf;
 }
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
 {
     if (a.B == 0 || a.Co == 0) return hipSuccess;
-    const int n_pxb = (a.Wo + kNpx - 1) / kNpx;
+    const int n_pxb = (a.Wo + kFusedSpan - 1) / kFusedSpan;
     const int n_ob = (a.Co + kMaxOt * 32 - 1) / (kMaxOt * 32);
-    const int n_ot = std::min(kMaxOt, (a.Co + 31) / 32);
-    const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_elems, a.max_blk);
-    hipError_t e = hipFuncSetAttribute((const void *)fused_mfma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    const int n_ot1 = std::min(kMaxOt, (a.Co + 31) / 32);
+    const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
+    const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
+    const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_bytes);
+    const void *fn = n_ot == 2 ? (const void *)fused_mfma_kernel<2>
+                   : n_ot == 4 ? (const void *)fused_mfma_kernel<4>
+                               : (const void *)fused_mfma_kernel<8>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pxb;
-    const int vec = (a.s == 1 && a.Wo % 8 == 0 && ((int64_t)a.Hi * a.Wi) % 8 == 0 && ((uintptr_t)a.x % 16) == 0) ? 1 : 0;
-    hipLaunchKernelGGL(fused_mfma_kernel, dim3((unsigned)nblk), dim3(kNpx / 32 * 64), lds, stream,
-                       (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.block_xoff,
-                       (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi,
-                       a.s, n_pxb, n_ob, n_ot, a.max_blk, vec);
+    // direct loads need 16-byte aligned runs and buffer offsets below 2^31
+    const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
+                          (int64_t)a.Hi * a.Wi * 2 < ((int64_t)1 << 31);
+    const int vec_x = (a.s == 1 && a.Wo % 8 == 0 && planes16) ? 1 : 0;
+    const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
+#define DISCO_FUSED_LAUNCH(N)                                                                                  \
+    hipLaunchKernelGGL(fused_mfma_kernel<N>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x, \
+                       (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata,        \
+                       a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_ob,         \
+                       buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w)
+    switch (n_ot) {
+    case 2: DISCO_FUSED_LAUNCH(2); break;
+    case 4: DISCO_FUSED_LAUNCH(4); break;
+    default: DISCO_FUSED_LAUNCH(8); break;
+    }
+#undef DISCO_FUSED_LAUNCH
     return hipGetLastError();
 }
 

@@ -1,10 +1,9 @@
-// plan_fused.cpp — packs psi into dense 16-offset blocks per (latitude, source row).
+// plan_fused.cpp — phase-split psi plan: blocks, sub-rows and pieces per output latitude.
 #include "plan_fused.hpp"
 
 #include <algorithm>
-#include <cmath>
-#include <cstring>
 #include <cstdint>
+#include <cstring>
 #include <map>
 
 namespace disco {
@@ -20,26 +19,29 @@ uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
-float bf16_val(uint16_t b)
-{
-    uint32_t u = (uint32_t)b << 16;
-    float f;
-    std::memcpy(&f, &u, 4);
-    return f;
-}
-
 int32_t floor8(int32_t v) { return (v >= 0) ? (v / 8) * 8 : -(((-v) + 7) / 8) * 8; }
-int32_t round_up8(int32_t v) { return (v + 7) / 8 * 8; }
+
+struct SubRow {
+    int32_t sr;
+    std::vector<int32_t> d0;  // kept block starts, ascending (multiples of 8, step 16)
+    int32_t first() const { return d0.front(); }
+    int32_t ra() const { return d0.back() - d0.front() + 24; }    // psi e-rows
+    int32_t len() const { return d0.back() - d0.front() + 264; }  // window positions
+};
+
+int64_t sub_cost(const SubRow &s, int ch)
+{
+    return fused_piece_bytes(2 * (int64_t)s.d0.size(), 16 * (int64_t)s.ra(), ch, s.len());
+}
 
 }  // namespace
 
-void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int ch, int a_budget, FusedPlan &out)
+void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out)
 {
     out = FusedPlan();
     const int32_t s = c.Wi / c.Wo;
     const int32_t L = c.Wo;
-    if (c.K > kFusedKMax || s > 2 || L % 8 != 0 || npx % 32 != 0) return;
-    out.npx = npx;
+    if (c.K > kFusedKMax || s > 2 || L % 8 != 0) return;
     out.ch = ch;
     out.ho_piece.push_back(0);
     std::vector<int64_t> work(c.Ho, 0);
@@ -58,119 +60,95 @@ void build_fused_plan(const CSRView &c, const GatherPlan & /*fwd*/, int npx, int
                 v[k] = c.val[e];
             }
         }
-        struct SubRow { int32_t sr, astart, len; std::vector<int32_t> dblk; };
-        // blocks of one sub-row: A operand in lane order, lane l -> row r = l % 32 (k = r % 16,
-        // hi/lo part = r / 16), offsets 8 * (l / 32) + t, t < 8
-        auto append_blocks = [&](int32_t sr, int32_t astart, int32_t lds_off, int32_t row_index,
-                                 const std::vector<int32_t> &dblk) {
-            const auto &m = rowsP[sr];
-            for (int32_t d0 : dblk) {
-                FBlock b;
-                b.row = row_index;
-                b.rel = d0 - astart;
-                out.blocks.push_back(b);
-                out.block_xoff.push_back(lds_off + b.rel);
-                for (int32_t l = 0; l < 64; ++l) {
-                    const int32_t r = l % 32, k = r % 16, part = r / 16, h = l / 32;
-                    for (int32_t t = 0; t < 8; ++t) {
-                        const int32_t d = d0 + 8 * h + t;
-                        float v = 0.0f;
-                        auto it = m.find(d);
-                        if (it != m.end() && k < c.K) v = it->second[k];
-                        const uint16_t hi = bf16_rne(v);
-                        out.adata.push_back(part == 0 ? hi : bf16_rne(v - bf16_val(hi)));
-                    }
-                }
-            }
-        };
-        // split each source row into blocks of 16 offsets (skipping empty ones), then into
-        // sub-rows within both piece limits
+        // blocks per source row (skipping blocks that see no entry at any phase), cut into
+        // sub-rows that fit a stage
         std::vector<SubRow> subs;
         for (auto &kv : rowsP) {
-            const int32_t sr = kv.first;
             const auto &m = kv.second;
             const int32_t dmin = m.begin()->first, dmax = m.rbegin()->first;
-            std::vector<int32_t> dblk;
-            for (int32_t d0 = dmin; d0 <= dmax; d0 += kBlkJ) {
-                auto it = m.lower_bound(d0);
-                if (it != m.end() && it->first < d0 + kBlkJ) dblk.push_back(d0);
+            const int32_t D0 = floor8(dmin);
+            std::vector<int32_t> kept;
+            for (int32_t d0 = D0; d0 - 16 + 9 <= dmax || d0 == D0; d0 += kBlkJ) {
+                auto it = m.lower_bound(d0 - 7);
+                if (it != m.end() && it->first <= d0 + kBlkJ - 1) kept.push_back(d0);
             }
-            auto len_of = [&](size_t a, size_t b) {
-                const int32_t astart = floor8(dblk[a]);
-                return round_up8(dblk[b - 1] + kBlkJ - astart + npx);
-            };
-            size_t q = 0;
-            while (q < dblk.size()) {
-                size_t q1 = q + 1;
-                while (q1 < dblk.size() &&
-                       (int64_t)ch * len_of(q, q1 + 1) * 2 + (int64_t)(q1 + 1 - q) * 1024 <= a_budget)
-                    ++q1;
-                SubRow sub;
-                sub.sr = sr;
-                sub.astart = floor8(dblk[q]);
-                sub.len = len_of(q, q1);
-                sub.dblk.assign(dblk.begin() + q, dblk.begin() + q1);
-                subs.push_back(std::move(sub));
-                q = q1;
+            SubRow cur;
+            cur.sr = kv.first;
+            for (int32_t d0 : kept) {
+                SubRow trial = cur;
+                trial.d0.push_back(d0);
+                if (!cur.d0.empty() && sub_cost(trial, ch) > piece_budget) {
+                    subs.push_back(cur);
+                    cur.d0.clear();
+                }
+                cur.d0.push_back(d0);
             }
+            if (!cur.d0.empty()) subs.push_back(cur);
         }
-        // One piece with two window buffers when the whole latitude fits; otherwise pieces with one
-        // buffer (a latitude of one such piece keeps its packed blocks resident, windows staged
-        // synchronously; several pieces restage everything per channel chunk).
-        int64_t tot_len = 0, tot_blk = 0;
-        for (const SubRow &sb : subs) {
-            tot_len += sb.len;
-            tot_blk += (int64_t)sb.dblk.size();
-        }
-        const bool one_dbuf = 2 * (int64_t)ch * tot_len * 2 + tot_blk * 1024 <= a_budget;
-        auto emit = [&](size_t s0, size_t s1, int32_t dbuf) {
+        // group sub-rows into pieces
+        size_t q = 0;
+        while (q < subs.size()) {
+            size_t q1 = q;
+            int64_t nb = 0, ae = 0, we = 0;
+            while (q1 < subs.size()) {
+                const int64_t nb2 = nb + (int64_t)subs[q1].d0.size();
+                const int64_t ae2 = ae + 16 * (int64_t)subs[q1].ra();
+                const int64_t we2 = we + subs[q1].len();
+                if (q1 > q && fused_piece_bytes(2 * (nb2 + 1), ae2 + 24 * 16, ch, we2) > piece_budget) break;
+                nb = nb2; ae = ae2; we = we2;
+                ++q1;
+            }
+            const bool pad = (nb & 1) != 0;  // blocks are contracted in pairs: pad with a zero block
             FPiece pc;
-            pc.blk_begin = (int32_t)out.blocks.size();
+            pc.desc_begin = (int32_t)(out.descs.size() / 2);
+            pc.nblk = (int32_t)(nb + (pad ? 1 : 0));
+            pc.desc_words = 2 * pc.nblk;
+            pc.a_begin = (int32_t)out.adata.size();
+            pc.a_elems = (int32_t)(ae + (pad ? 24 * 16 : 0));
             pc.row_begin = (int32_t)out.rows.size();
-            int32_t xwin = 0, nblk = 0;
-            for (size_t j = s0; j < s1; ++j) {
+            pc.win_elems = (int32_t)we;
+            int32_t a_row_e = 0, win_off = 0;
+            for (size_t j = q; j < q1; ++j) {
                 const SubRow &sb = subs[j];
+                const int32_t first = sb.first(), ra = sb.ra();
+                const auto &m = rowsP[sb.sr];
                 FRow fr;
                 fr.sr = sb.sr;
-                fr.start = sb.astart;
-                fr.len = sb.len;
-                fr.lds_off = xwin;
-                const int32_t row_index = (int32_t)out.rows.size();
+                fr.start = first;
+                fr.len = sb.len();
+                fr.win_off = win_off;
                 out.rows.push_back(fr);
-                append_blocks(sb.sr, sb.astart, fr.lds_off, row_index, sb.dblk);
-                xwin += sb.len;
-                nblk += (int32_t)sb.dblk.size();
-            }
-            pc.blk_end = (int32_t)out.blocks.size();
-            pc.row_end = (int32_t)out.rows.size();
-            pc.xwin_elems = xwin;
-            pc.dbuf = dbuf;
-            pc.pad[0] = pc.pad[1] = 0;
-            out.max_xwin = std::max(out.max_xwin, xwin);
-            out.max_blk = std::max(out.max_blk, nblk);
-            out.max_piece_elems = std::max(out.max_piece_elems, nblk * 512 + (1 + dbuf) * ch * xwin);
-            work[ho] += nblk;
-            out.pieces.push_back(pc);
-        };
-        if (one_dbuf) {
-            emit(0, subs.size(), 1);
-        } else {
-            std::vector<size_t> cuts{0};
-            int64_t xwin = 0, nblk = 0;
-            for (size_t j = 0; j < subs.size(); ++j) {
-                const int64_t cost = (int64_t)ch * (xwin + subs[j].len) * 2 + (nblk + (int64_t)subs[j].dblk.size()) * 1024;
-                if (j > cuts.back() && cost > a_budget) {
-                    cuts.push_back(j);
-                    xwin = nblk = 0;
+                for (int32_t d0 : sb.d0) {
+                    out.descs.push_back(2 * 16 * (a_row_e + (d0 - first) + 8));
+                    out.descs.push_back(2 * (win_off + (d0 - first)));
                 }
-                xwin += subs[j].len;
-                nblk += (int64_t)subs[j].dblk.size();
+                for (int32_t e = 0; e < ra; ++e) {
+                    auto it = m.find(first - 8 + e);
+                    for (int32_t k = 0; k < 16; ++k)
+                        out.adata.push_back((it != m.end() && k < c.K) ? bf16_rne(it->second[k]) : (uint16_t)0);
+                }
+                a_row_e += ra;
+                win_off += sb.len();
             }
-            cuts.push_back(subs.size());
-            for (size_t q = 0; q + 1 < cuts.size(); ++q) emit(cuts[q], cuts[q + 1], 0);
+            if (pad) {  // zero psi rows; the window offset reads the piece's first window
+                out.descs.push_back(2 * 16 * (a_row_e + 8));
+                out.descs.push_back(0);
+                out.adata.insert(out.adata.end(), 24 * 16, (uint16_t)0);
+            }
+            pc.row_end = (int32_t)out.rows.size();
+            out.pieces.push_back(pc);
+            out.max_piece_bytes = std::max<int32_t>(
+                out.max_piece_bytes, (int32_t)fused_piece_bytes(pc.desc_words, pc.a_elems, ch, pc.win_elems));
+            out.max_win = std::max(out.max_win, pc.win_elems);
+            work[ho] += pc.nblk + 8;  // per-piece stage overhead counted as a few blocks
+            out.mfma_blocks += pc.nblk;
+            q = q1;
         }
-        out.mfma_blocks += work[ho];
         out.ho_piece.push_back((int32_t)out.pieces.size());
+    }
+    if (out.adata.size() * 2 >= ((size_t)1 << 31) || out.descs.size() * 4 >= ((size_t)1 << 31)) {
+        out = FusedPlan();  // beyond 32-bit buffer offsets
+        return;
     }
     out.ho_order.resize(c.Ho);
     for (int32_t h = 0; h < c.Ho; ++h) out.ho_order[h] = h;

@@ -1,23 +1,31 @@
-// plan_fused.hpp — packed-psi plan for the matrix-core fused convolution.
+// plan_fused.hpp — phase-split psi plan for the matrix-core fused convolution.
 //
-// The contraction of one output latitude ho is rewritten as dense products:
-// for every source row sr (input latitude hi and longitude residue rho, so
-// row sr holds x[hi, rho + s*j] for j in [0, Wo)) the K psi rows at ho are
-// laid out densely over the union of their column positions, as signed
-// offsets d from output longitude 0, in blocks of 16 consecutive offsets
-// (zeros where a row has no entry):
+// Output longitudes are handled in spans of 256 = 8 phases x 32 columns:
+// column n of phase q is longitude px0 + 8n + q.  For one output latitude ho
+// and one source row sr (input latitude hi and longitude residue rho; row sr
+// holds x[hi, rho + s*j] for j in [0, Wo)), with psi values P[k, d] at signed
+// longitude offsets d,
 //
-//   out[k, wo] = sum_sr sum_blocks sum_{t<16} P[k, d_blk + t] * xrow_sr[(wo + d_blk + t) mod Wo]
+//   out[k, px0 + 8n + q] = sum_d P[k, d] * xrow[px0 + 8n + q + d]
+//                        = sum_blocks sum_{t<16} P[k, d0 + t - q] * xrow[px0 + 8n + d0 + t]
 //
-// One block is the A operand of one v_mfma_f32_32x32x16_bf16: rows 0..15
-// hold bf16(P) for k = 0..15, rows 16..31 the bf16 rounding residue
-// P - bf16(P), so the sum of the two halves of the result carries psi to
-// about 16 significant bits.  The B operand is 16 consecutive source values
-// per output longitude (a Hankel slice of the row), read from an LDS window.
+// where the blocks start at offsets d0 that are multiples of 8 and step by 16
+// (the first at floor8(min d), enough of them that d0 + 16 - 7 passes max d).
+// The x operand of a block, xrow[px0 + 8n + d0 + t], does not depend on the
+// phase and is read as aligned 16-byte runs; the phase only shifts psi.  One
+// v_mfma_f32_32x32x16_bf16 per (block, channel, pair of phases) computes 16
+// basis rows for two phases at once.
 //
-// Blocks are grouped into pieces whose source-row windows and packed blocks
-// fit the LDS budget; a latitude whose rows are whole rings (the caps at the
-// poles) gets several pieces.
+// Per source row the plan stores psi densely as bf16 (round to nearest even)
+// in [e][k] order, e = d - (first block start - 8), 16 values per e; per block
+// a descriptor (byte offsets of its psi rows and of its window run in the
+// piece stage); per row the window of source positions px0 + first + i,
+// i < len = span of its blocks + 264.  Blocks are contracted in pairs: a piece
+// with an odd block count gets a zero block.
+//
+// Rows are cut into sub-rows and grouped into pieces; a piece's descriptors,
+// psi and windows (for one chunk of channels) fit one of two LDS stage
+// buffers.
 #pragma once
 
 #include <cstdint>
@@ -27,55 +35,50 @@
 
 namespace disco {
 
-constexpr int kFusedKMax = 16;   // psi rows per latitude the packed layout holds
+constexpr int kFusedKMax = 16;   // basis functions the packed layout holds
 constexpr int kBlkJ = 16;        // offsets per block (MFMA reduction depth)
+constexpr int kFusedSpan = 256;  // output longitudes per workgroup (8 phases x 32 columns)
 
-struct FRow {          // one source row of a piece
+struct FRow {          // one sub-row of a piece
     int32_t sr;        // source row = hi * s + rho
-    int32_t start;     // signed offset of the first window position (window = px0 + start + e)
+    int32_t start;     // signed offset of the window's first position (window = px0 + start + i)
     int32_t len;       // window length in positions (multiple of 8)
-    int32_t lds_off;   // element offset of this row's window inside one channel's window area
+    int32_t win_off;   // element offset of this window inside one channel's window area
 };
-
-struct FBlock {        // one packed 32x16 A operand
-    int32_t row;       // index into the piece's rows (absolute index in rows[])
-    int32_t rel;       // offset of the block's first position from the row window start
-};
-// The kernel reads, per block, only xoff = rows[row].lds_off + rel (element offset of
-// the block's first window position within one channel's window area).
 
 struct FPiece {
-    int32_t blk_begin, blk_end;   // blocks (also index the packed A data, 512 bf16 each)
-    int32_t row_begin, row_end;   // rows
-    int32_t xwin_elems;           // window elements per channel (sum of row lens)
-    int32_t dbuf;                 // 1: the latitude's only piece, with room for two window buffers
-                                  //    (a latitude of one piece with dbuf = 0 keeps its blocks resident)
-    int32_t pad[2];
+    int32_t desc_begin;  // first block descriptor (pairs of int32)
+    int32_t nblk;        // blocks of the piece (even)
+    int32_t desc_words;  // int32 words staged for the descriptors (2 * nblk, a multiple of 4)
+    int32_t a_begin;     // first bf16 of the piece's psi in adata (multiple of 8)
+    int32_t a_elems;     // bf16 count of the piece's psi (multiple of 8)
+    int32_t row_begin, row_end;
+    int32_t win_elems;   // window elements per channel (multiple of 8)
 };
 
 struct FusedPlan {
     bool ok = false;
-    int32_t npx = 0;              // output longitudes per workgroup
-    int32_t ch = 4;               // channels per chunk
-    int32_t max_xwin = 0;         // max window elements per channel over all pieces
-    int32_t max_blk = 0;          // max blocks per piece
-    int32_t max_piece_elems = 0;  // max over pieces of 512 * blocks + (1 + dbuf) * ch * window elements
+    int32_t ch = 4;                     // channels per chunk
+    int32_t max_piece_bytes = 0;        // largest piece stage (descriptors + psi + ch windows)
+    int32_t max_win = 0;                // largest window area per channel
     std::vector<int32_t> ho_piece;      // [Ho + 1]: pieces of latitude ho
     std::vector<int32_t> ho_order;      // latitudes, heaviest first
     std::vector<FPiece> pieces;
     std::vector<FRow> rows;
-    std::vector<FBlock> blocks;
-    std::vector<int32_t> block_xoff;    // per block: rows[row].lds_off + rel
-    std::vector<uint16_t> adata;        // packed A operands, 512 bf16 per block in lane order
+    std::vector<int32_t> descs;         // per block: byte offsets (psi rows, window run) in the piece stage
+    std::vector<uint16_t> adata;        // bf16 psi, [e][16] per sub-row
     int64_t mfma_blocks = 0;            // total blocks over all latitudes
 };
 
-// Build from the forward plan.  `npx` output longitudes per workgroup, `ch`
-// channels per chunk; a piece's packed blocks plus its windows for `ch`
-// channels take at most `a_budget` bytes of LDS.  A latitude that fits in one
-// piece with two window buffers is one double-buffered piece; otherwise it is
-// split into pieces with one buffer.  ok = false if the shape is
-// outside the packed kernel (K > 16, s > 2, Wo not a multiple of 8).
-void build_fused_plan(const CSRView &c, const GatherPlan &fwd, int npx, int ch, int a_budget, FusedPlan &out);
+// Build the plan; a piece stage takes at most `piece_budget` bytes of LDS for
+// `ch` channels.  ok = false if the shape is outside the packed kernel
+// (K > 16, s > 2, Wo not a multiple of 8).
+void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out);
+
+// Bytes of one piece stage in LDS.
+inline int64_t fused_piece_bytes(int64_t desc_words, int64_t a_elems, int64_t ch, int64_t win_elems)
+{
+    return 4 * desc_words + 2 * a_elems + 2 * ch * win_elems;
+}
 
 }  // namespace disco
