@@ -102,44 +102,47 @@ __device__ __forceinline__ void copy_units(const Ctx &c, __amdgpu_buffer_rsrc_t 
     }
 }
 
-// x windows of one piece for the chunk starting at channel c0.
+// x windows of one piece for the chunk starting at channel c0.  Rows go round the waves; a wave
+// handles all channels of its rows (row data is read once, no integer division).
 __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, int c0, bf16_t *win)
 {
     const int nrows = pc.row_end - pc.row_begin;
     const int ccn = min(kCh, c.C - c0);
-    for (int q = c.wave; q < kCh * nrows; q += kWaves) {
-        const int cl = q / nrows, r = q - cl * nrows;
+    const bf16_t *plane0 = c.x + ((int64_t)c.b * c.C + c0) * c.plane_sz;
+    for (int r = c.wave; r < nrows; r += kWaves) {
         const FRow fr = c.rows[pc.row_begin + r];
-        bf16_t *dst = win + cl * pc.win_elems + fr.win_off;
+        bf16_t *dst = win + fr.win_off;
         const int nch = fr.len >> 3;
-        if (cl >= ccn) {
-            for (int e8 = c.lane; e8 < nch; e8 += 64)
-                *reinterpret_cast<uint4 *>(dst + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
-            continue;
-        }
-        const int g0 = mod_l(c.px0 + fr.start, c.L);
-        const bf16_t *plane = c.x + ((int64_t)c.b * c.C + (c0 + cl)) * c.plane_sz;
+        int g0 = c.px0 + fr.start;  // within a few L of [0, L)
+        while (g0 < 0) g0 += c.L;
+        while (g0 >= c.L) g0 -= c.L;
         if (c.vec_x) {
-            // s == 1, rows 16-byte aligned: 8-position runs never straddle the row end
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(plane, (uint32_t)(2 * c.plane_sz));
+            // s == 1, rows 16-byte aligned: 8-position runs never straddle the row end.  One buffer
+            // resource spans the chunk's channel planes.
+            const uint32_t plane_bytes = 2u * (uint32_t)c.plane_sz;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(plane0, plane_bytes * (uint32_t)ccn);
             const uint32_t row0 = 2u * (uint32_t)(fr.sr * c.Wi);
             for (int t = 0; t < nch; t += 64) {
                 const int e8 = t + c.lane;
+                int pos = g0 + 8 * e8;
+                while (pos >= c.L) pos -= c.L;
+                const uint32_t voff = row0 + 2u * (uint32_t)pos;
                 if (e8 < nch) {
-                    int pos = g0 + 8 * e8;
-                    while (pos >= c.L) pos -= c.L;
-                    dma16(rs, row0 + 2u * (uint32_t)pos, dst + 8 * t);
+                    for (int cl = 0; cl < ccn; ++cl) dma16(rs, voff + plane_bytes * cl, dst + cl * pc.win_elems + 8 * t);
                 }
             }
         } else {
             const int hi = fr.sr / c.s, rho = fr.sr - hi * c.s;
-            const bf16_t *xrow = plane + (int64_t)hi * c.Wi;
             for (int e = c.lane; e < fr.len; e += 64) {
                 int pos = g0 + e;
                 while (pos >= c.L) pos -= c.L;
-                dst[e] = xrow[(int64_t)c.s * pos + rho];
+                const int64_t off = (int64_t)hi * c.Wi + (int64_t)c.s * pos + rho;
+                for (int cl = 0; cl < ccn; ++cl) dst[cl * pc.win_elems + e] = plane0[cl * c.plane_sz + off];
             }
         }
+        for (int cl = ccn; cl < kCh; ++cl)  // channels past C are zeros
+            for (int e8 = c.lane; e8 < nch; e8 += 64)
+                *reinterpret_cast<uint4 *>(dst + cl * pc.win_elems + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
@@ -180,10 +183,11 @@ __device__ __forceinline__ void stage_w(const Ctx &c, int c0, unsigned char *wb)
 
 // ---- compute ---------------------------------------------------------------------------------
 
-// Operands of one block: the psi column as eight raw 2-byte reads (packed at the point of use,
-// so that the wait for them falls just before the MFMA) and the two channels' x runs.
+// Operands of one block: five 4-byte words of psi (pairs of consecutive offsets of one basis
+// function; realigned at the point of use, so that the wait for them falls just before the
+// MFMA) and the two channels' x runs.
 struct Ops {
-    unsigned short a[8];
+    unsigned a[5];
     bf16x8 b0, b1;
 };
 
@@ -192,16 +196,17 @@ __device__ __forceinline__ void load_ops(Ops &o, const unsigned char *a_base, co
 {
     o.b0 = *reinterpret_cast<const bf16x8 *>(x_base + x_off);
     o.b1 = *reinterpret_cast<const bf16x8 *>(x_base + wel2 + x_off);
-    const unsigned short *p = reinterpret_cast<const unsigned short *>(a_base + a_off);
+    const unsigned *p = reinterpret_cast<const unsigned *>(a_base + a_off);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o.a[i] = p[16 * i];
+    for (int i = 0; i < 5; ++i) o.a[i] = p[16 * i];
 }
 
-__device__ __forceinline__ void mfma_ops(const Ops &o, f32x16 (&d)[2])
+// sel: 0x03020100 (even first offset: words as read) or 0x05040302 (odd: shifted by one offset)
+__device__ __forceinline__ void mfma_ops(const Ops &o, unsigned sel, f32x16 (&d)[2])
 {
     unsigned w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (unsigned)o.a[2 * i] | ((unsigned)o.a[2 * i + 1] << 16);
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(o.a[i + 1], o.a[i], sel);
     const bf16x8 a = __builtin_bit_cast(bf16x8, w);
     d[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b0, d[0], 0, 0, 0);
     d[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b1, d[1], 0, 0, 0);
@@ -212,7 +217,7 @@ __device__ __forceinline__ void mfma_ops(const Ops &o, f32x16 (&d)[2])
 // read two pairs ahead.  Scheduling barriers keep that order (the compiler would otherwise
 // move the reads next to their uses).
 __device__ __forceinline__ void contract(const unsigned char *__restrict__ buf, const FPiece &pc, int a_lane2,
-                                         int x_lane2, int ch0, f32x16 (&d)[2])
+                                         int x_lane2, unsigned sel, int ch0, f32x16 (&d)[2])
 {
     const int npair = pc.nblk >> 1;
     if (npair <= 0) return;
@@ -229,11 +234,11 @@ __device__ __forceinline__ void contract(const unsigned char *__restrict__ buf, 
         const int4 dC = desc[min(j + 2, lastp)];
         load_ops(Q, a_base, x_base, wel2, dA.z, dA.w);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_ops(P, d);
+        mfma_ops(P, sel, d);
         __builtin_amdgcn_sched_barrier(0);
         load_ops(P, a_base, x_base, wel2, dB.x, dB.y);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_ops(Q, d);
+        mfma_ops(Q, sel, d);
         __builtin_amdgcn_sched_barrier(0);
         dA = dB;
         dB = dC;
@@ -301,7 +306,7 @@ template <int NOTH>
 __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int nsteps, int st, int t, int p, unsigned char *__restrict__ cur,
                                          unsigned char *__restrict__ nxt, unsigned char *__restrict__ wb, int a_lane2,
-                                         int x_lane2, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
+                                         int x_lane2, unsigned sel, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
 {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` (and W) have landed
     __syncthreads();                // everyone's have; the previous step is done with `nxt` and W
@@ -313,7 +318,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     }
     if (p == 0) zero(d);
     const FPiece pc = pieces[p_begin + p];
-    contract(cur, pc, a_lane2, x_lane2, 2 * h2, d);
+    contract(cur, pc, a_lane2, x_lane2, sel, 2 * h2, d);
     if (p + 1 == npieces) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
@@ -358,13 +363,16 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.vec_x = vec_x != 0;
     c.vec_w = vec_w != 0;
 
-    // lane constants: A row r = lane % 32 is (phase q = 2 pp + r / 16, MFMA row m = r % 16 -> basis k);
+    // lane constants: A row r = lane % 32 is (phase 2 pp + r / 16, MFMA row m = r % 16 -> basis k);
     // the basis order puts k = 8h + a in result register a of lane half h
     const int pp = c.wave & 3, h2 = c.wave >> 2;
     const int r = c.lane & 31, hh = c.lane >> 5;
-    const int m = r & 15, q = 2 * pp + (r >> 4);
+    const int m = r & 15;
     const int kb = (m < 8) ? 8 * (m >> 2) + (m & 3) : 8 * ((m - 8) >> 2) + 4 + (m & 3);
-    const int a_lane2 = 2 * ((8 * hh - q) * 16 + kb);  // bytes
+    // psi words: offset pair (base + 8 hh - q) / 2 rounded down, basis kb; odd q reads one offset early
+    const int ph0 = r >> 4;
+    const int a_lane2 = 64 * (4 * hh - pp - ph0) + 4 * kb;  // bytes
+    const unsigned sel = ph0 ? 0x05040302u : 0x03020100u;
     const int x_lane2 = 2 * (8 * r + 8 * hh);            // bytes
 
     f32x16 yacc[2][NOTH];
@@ -386,11 +394,11 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_step(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
         for (int st = 0; st < nsteps; st += 2) {
-            run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, pp, h2, d,
+            run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, sel, pp, h2, d,
                            yacc);
             if (++p == npieces) { p = 0; ++t; }
             if (st + 1 < nsteps) {
-                run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, pp,
+                run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, sel, pp,
                                h2, d, yacc);
                 if (++p == npieces) { p = 0; ++t; }
             }
@@ -443,7 +451,7 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pxb;
     // direct loads need 16-byte aligned runs and buffer offsets below 2^31
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
-                          (int64_t)a.Hi * a.Wi * 2 < ((int64_t)1 << 31);
+                          (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
     const int vec_x = (a.s == 1 && a.Wo % 8 == 0 && planes16) ? 1 : 0;
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
 #define DISCO_FUSED_LAUNCH(N)                                                                                  \

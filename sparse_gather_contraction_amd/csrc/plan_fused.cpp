@@ -25,7 +25,7 @@ struct SubRow {
     int32_t sr;
     std::vector<int32_t> d0;  // kept block starts, ascending (multiples of 8, step 16)
     int32_t first() const { return d0.front(); }
-    int32_t ra() const { return d0.back() - d0.front() + 24; }    // psi e-rows
+    int32_t ra() const { return d0.back() - d0.front() + 26; }    // psi e-rows (even)
     int32_t len() const { return d0.back() - d0.front() + 264; }  // window positions
 };
 
@@ -94,7 +94,7 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out
                 const int64_t nb2 = nb + (int64_t)subs[q1].d0.size();
                 const int64_t ae2 = ae + 16 * (int64_t)subs[q1].ra();
                 const int64_t we2 = we + subs[q1].len();
-                if (q1 > q && fused_piece_bytes(2 * (nb2 + 1), ae2 + 24 * 16, ch, we2) > piece_budget) break;
+                if (q1 > q && fused_piece_bytes(2 * (nb2 + 1), ae2 + 26 * 16, ch, we2) > piece_budget) break;
                 nb = nb2; ae = ae2; we = we2;
                 ++q1;
             }
@@ -104,7 +104,7 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out
             pc.nblk = (int32_t)(nb + (pad ? 1 : 0));
             pc.desc_words = 2 * pc.nblk;
             pc.a_begin = (int32_t)out.adata.size();
-            pc.a_elems = (int32_t)(ae + (pad ? 24 * 16 : 0));
+            pc.a_elems = (int32_t)(ae + (pad ? 26 * 16 : 0));
             pc.row_begin = (int32_t)out.rows.size();
             pc.win_elems = (int32_t)we;
             int32_t a_row_e = 0, win_off = 0;
@@ -122,10 +122,13 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out
                     out.descs.push_back(2 * 16 * (a_row_e + (d0 - first) + 8));
                     out.descs.push_back(2 * (win_off + (d0 - first)));
                 }
-                for (int32_t e = 0; e < ra; ++e) {
-                    auto it = m.find(first - 8 + e);
-                    for (int32_t k = 0; k < 16; ++k)
-                        out.adata.push_back((it != m.end() && k < c.K) ? bf16_rne(it->second[k]) : (uint16_t)0);
+                // [e pair][k][2]: psi at offset first - 8 + e, basis k, at (e / 2) * 32 + 2 k + e % 2
+                for (int32_t e2 = 0; e2 < ra; e2 += 2) {
+                    auto it0 = m.find(first - 8 + e2), it1 = m.find(first - 8 + e2 + 1);
+                    for (int32_t k = 0; k < 16; ++k) {
+                        out.adata.push_back((it0 != m.end() && k < c.K) ? bf16_rne(it0->second[k]) : (uint16_t)0);
+                        out.adata.push_back((it1 != m.end() && k < c.K) ? bf16_rne(it1->second[k]) : (uint16_t)0);
+                    }
                 }
                 a_row_e += ra;
                 win_off += sb.len();
@@ -133,7 +136,7 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out
             if (pad) {  // zero psi rows; the window offset reads the piece's first window
                 out.descs.push_back(2 * 16 * (a_row_e + 8));
                 out.descs.push_back(0);
-                out.adata.insert(out.adata.end(), 24 * 16, (uint16_t)0);
+                out.adata.insert(out.adata.end(), 26 * 16, (uint16_t)0);
             }
             pc.row_end = (int32_t)out.rows.size();
             out.pieces.push_back(pc);

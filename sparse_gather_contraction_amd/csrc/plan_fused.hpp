@@ -17,7 +17,8 @@
 // basis rows for two phases at once.
 //
 // Per source row the plan stores psi densely as bf16 (round to nearest even)
-// in [e][k] order, e = d - (first block start - 8), 16 values per e; per block
+// by e = d - (first block start - 8) and basis k, pairs of e interleaved
+// ([e/2][k][e%2], so one 4-byte word holds two consecutive offsets); per block
 // a descriptor (byte offsets of its psi rows and of its window run in the
 // piece stage); per row the window of source positions px0 + first + i,
 // i < len = span of its blocks + 264.  Blocks are contracted in pairs: a piece
