@@ -57,7 +57,7 @@ struct DevFused {
     uint16_t *adata = nullptr;
     int32_t *ho_piece = nullptr;
     int32_t *ho_order = nullptr;
-    int32_t max_piece_bytes = 0;
+    int32_t max_piece_bytes = 0, max_resident_bytes = 0;
     uint32_t desc_bytes = 0, adata_bytes = 0;
 };
 
@@ -136,6 +136,7 @@ hipError_t upload_fused(DevFused &d, const disco::FusedPlan &p)
     if ((e = upload(&d.ho_order, p.ho_order)) != hipSuccess) return e;
     d.ok = true;
     d.max_piece_bytes = p.max_piece_bytes;
+    d.max_resident_bytes = p.max_resident_bytes;
     d.desc_bytes = (uint32_t)(p.descs.size() * sizeof(int32_t));
     d.adata_bytes = (uint32_t)(p.adata.size() * sizeof(uint16_t));
     return hipSuccess;
@@ -337,7 +338,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         // two piece stage buffers share what the W slice leaves of the workgroup's LDS
         const int ch = disco::fused_mfma_channels_per_chunk();
         const int budget = ((kLdsPerBlock - (int)disco::fused_mfma_reserved_bytes()) / 2) & ~15;
-        disco::build_fused_plan(v, ch, budget, fup);
+        disco::build_fused_plan(v, ch, budget, disco::fused_mfma_exchange_bytes(), fup);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
     }
@@ -489,6 +490,7 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
         m.B = (int32_t)B; m.C = (int32_t)C; m.Co = (int32_t)Co; m.K = h->K;
         m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi; m.s = h->Wi / h->Wo;
         m.max_piece_bytes = h->fused.max_piece_bytes;
+        m.max_resident_bytes = h->fused.max_resident_bytes;
         m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
         hipError_t e = disco::launch_fused_mfma(m, (hipStream_t)stream);
         if (e != hipSuccess)

@@ -68,13 +68,14 @@ struct FusedMfmaLaunch {
     const int32_t *descs;
     const uint16_t *adata;
     const int32_t *ho_piece, *ho_order;
-    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, max_piece_bytes;
+    int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, max_piece_bytes, max_resident_bytes;
     uint32_t desc_bytes, adata_bytes;  // sizes of the descriptor and psi arrays
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
-size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes);
+size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_bytes);
 int fused_mfma_channels_per_chunk();
+int fused_mfma_exchange_bytes();     // LDS bytes of the einsum operand exchange
 size_t fused_mfma_reserved_bytes();  // LDS bytes besides the two piece stage buffers
 int fused_max_k();  // largest K the fused kernel accepts
 

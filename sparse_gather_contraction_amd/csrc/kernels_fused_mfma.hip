@@ -146,13 +146,18 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
     }
 }
 
+// Block descriptors and psi of piece pc.
+__device__ __forceinline__ void stage_psi(const Ctx &c, const FPiece &pc, unsigned char *buf)
+{
+    copy_units(c, c.descs_rs, 8u * (uint32_t)pc.desc_begin, buf, pc.desc_words / 4);
+    copy_units(c, c.adata_rs, 2u * (uint32_t)pc.a_begin, buf + 4 * pc.desc_words, pc.a_elems / 8);
+}
+
 // One step's stage: block descriptors, psi and windows of piece pc for channels c0..c0+kCh-1.
 __device__ __forceinline__ void stage_step(const Ctx &c, const FPiece &pc, int c0, unsigned char *buf)
 {
-    copy_units(c, c.descs_rs, 8u * (uint32_t)pc.desc_begin, buf, pc.desc_words / 4);
-    unsigned char *a_area = buf + 4 * pc.desc_words;
-    copy_units(c, c.adata_rs, 2u * (uint32_t)pc.a_begin, a_area, pc.a_elems / 8);
-    stage_windows(c, pc, c0, reinterpret_cast<bf16_t *>(a_area + 2 * pc.a_elems));
+    stage_psi(c, pc, buf);
+    stage_windows(c, pc, c0, reinterpret_cast<bf16_t *>(buf + 4 * pc.desc_words + 2 * pc.a_elems));
 }
 
 // W slice of the chunk starting at c0 in A-operand order: unit (ot, cl), lane l holds
@@ -216,15 +221,16 @@ __device__ __forceinline__ void mfma_ops(const Ops &o, unsigned sel, f32x16 (&d)
 // of one block are read while the other block's MFMAs run, and the descriptors of a pair are
 // read two pairs ahead.  Scheduling barriers keep that order (the compiler would otherwise
 // move the reads next to their uses).
-__device__ __forceinline__ void contract(const unsigned char *__restrict__ buf, const FPiece &pc, int a_lane2,
-                                         int x_lane2, unsigned sel, int ch0, f32x16 (&d)[2])
+__device__ __forceinline__ void contract(const unsigned char *__restrict__ stage, const unsigned char *__restrict__ win,
+                                         const FPiece &pc, int a_lane2, int x_lane2, unsigned sel, int ch0,
+                                         f32x16 (&d)[2])
 {
     const int npair = pc.nblk >> 1;
     if (npair <= 0) return;
-    const int4 *desc = reinterpret_cast<const int4 *>(buf);
-    const unsigned char *a_base = buf + 4 * pc.desc_words + a_lane2;
+    const int4 *desc = reinterpret_cast<const int4 *>(stage);
+    const unsigned char *a_base = stage + 4 * pc.desc_words + a_lane2;
     const int wel2 = 2 * pc.win_elems;
-    const unsigned char *x_base = buf + 4 * pc.desc_words + 2 * pc.a_elems + ch0 * wel2 + x_lane2;
+    const unsigned char *x_base = win + ch0 * wel2 + x_lane2;
     const int lastp = npair - 1;
     int4 dA = desc[0];
     int4 dB = desc[min(1, lastp)];
@@ -318,12 +324,32 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     }
     if (p == 0) zero(d);
     const FPiece pc = pieces[p_begin + p];
-    contract(cur, pc, a_lane2, x_lane2, sel, 2 * h2, d);
+    contract(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, sel, 2 * h2, d);
     if (p + 1 == npieces) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
         einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
     }
+}
+
+// One chunk of a latitude whose psi stays resident: only the x windows stream (double-buffered).
+template <int NOTH>
+__device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &pc, int nchunks, int t,
+                                                   const unsigned char *__restrict__ stage,
+                                                   unsigned char *__restrict__ cur, unsigned char *__restrict__ nxt,
+                                                   unsigned char *__restrict__ wb, int a_lane2, int x_lane2,
+                                                   unsigned sel, int pp, int h2, f32x16 (&d)[2],
+                                                   f32x16 (&yacc)[2][NOTH])
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t > 0) stage_w(c, kCh * t, wb);
+    if (t + 1 < nchunks) stage_windows(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
+    zero(d);
+    contract(stage, cur, pc, a_lane2, x_lane2, sel, 2 * h2, d);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // W slice visible; `cur` free for the exchange
+    einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
 }
 
 template <int NOT>
@@ -389,7 +415,24 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const int npieces = ho_piece[ho + 1] - p_begin;
     const int nchunks = (C + kCh - 1) / kCh;
     const int nsteps = npieces * nchunks;
-    if (nsteps > 0) {
+    FPiece pc0;
+    pc0.resident = 0;
+    if (npieces == 1) pc0 = pieces[p_begin];
+    if (npieces == 1 && pc0.resident) {
+        // LDS after W: [descriptors + psi][window buffer 0][window buffer 1]
+        unsigned char *stage = buf0;
+        unsigned char *w0 = stage + 4 * pc0.desc_words + 2 * pc0.a_elems;
+        unsigned char *w1 = w0 + pc0.resident;
+        stage_w(c, 0, wb);
+        stage_psi(c, pc0, stage);
+        stage_windows(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
+        for (int t = 0; t < nchunks; t += 2) {
+            run_chunk_resident<NOTH>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, sel, pp, h2, d, yacc);
+            if (t + 1 < nchunks)
+                run_chunk_resident<NOTH>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, sel, pp, h2, d,
+                                         yacc);
+        }
+    } else if (nsteps > 0) {
         stage_w(c, 0, wb);
         stage_step(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
@@ -426,12 +469,14 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 
 int fused_mfma_channels_per_chunk() { return kCh; }
 
+int fused_mfma_exchange_bytes() { return kXchBytes; }
+
 size_t fused_mfma_reserved_bytes() { return (size_t)kWBytes; }
 
-size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes)
+size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_bytes)
 {
     const size_t buf = std::max<size_t>(((size_t)max_piece_bytes + 15) & ~(size_t)15, (size_t)kXchBytes);
-    return (size_t)n_ot * kCh * 1024 + 2 * buf;
+    return (size_t)n_ot * kCh * 1024 + std::max<size_t>(2 * buf, (size_t)max_resident_bytes);
 }
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
@@ -442,7 +487,7 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const int n_ot1 = std::min(kMaxOt, (a.Co + 31) / 32);
     const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
     const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
-    const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_bytes);
+    const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_bytes, a.max_resident_bytes);
     const void *fn = n_ot == 2 ? (const void *)fused_mfma_kernel<2>
                    : n_ot == 4 ? (const void *)fused_mfma_kernel<4>
                                : (const void *)fused_mfma_kernel<8>;

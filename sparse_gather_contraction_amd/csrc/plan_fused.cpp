@@ -36,7 +36,7 @@ int64_t sub_cost(const SubRow &s, int ch)
 
 }  // namespace
 
-void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out)
+void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes, FusedPlan &out)
 {
     out = FusedPlan();
     const int32_t s = c.Wi / c.Wo;
@@ -139,9 +139,18 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out
                 out.adata.insert(out.adata.end(), 26 * 16, (uint16_t)0);
             }
             pc.row_end = (int32_t)out.rows.size();
+            pc.resident = 0;
+            pc.pad[0] = pc.pad[1] = pc.pad[2] = 0;
+            const int64_t stage_bytes = 4 * (int64_t)pc.desc_words + 2 * (int64_t)pc.a_elems;
+            const int64_t wbuf = std::max<int64_t>(2 * (int64_t)ch * pc.win_elems, xch_bytes);
+            if (q == 0 && q1 == subs.size() && stage_bytes + 2 * wbuf <= 2 * (int64_t)piece_budget) {
+                pc.resident = (int32_t)wbuf;
+                out.max_resident_bytes = std::max<int32_t>(out.max_resident_bytes, (int32_t)(stage_bytes + 2 * wbuf));
+            } else {
+                out.max_piece_bytes = std::max<int32_t>(
+                    out.max_piece_bytes, (int32_t)fused_piece_bytes(pc.desc_words, pc.a_elems, ch, pc.win_elems));
+            }
             out.pieces.push_back(pc);
-            out.max_piece_bytes = std::max<int32_t>(
-                out.max_piece_bytes, (int32_t)fused_piece_bytes(pc.desc_words, pc.a_elems, ch, pc.win_elems));
             out.max_win = std::max(out.max_win, pc.win_elems);
             work[ho] += pc.nblk + 8;  // per-piece stage overhead counted as a few blocks
             out.mfma_blocks += pc.nblk;

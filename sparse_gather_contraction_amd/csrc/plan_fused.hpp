@@ -55,12 +55,17 @@ struct FPiece {
     int32_t a_elems;     // bf16 count of the piece's psi (multiple of 8)
     int32_t row_begin, row_end;
     int32_t win_elems;   // window elements per channel (multiple of 8)
+    int32_t resident;    // > 0: the latitude's only piece, whose descriptors and psi stay in LDS for all
+                         // chunks while the windows are double-buffered; the value is the window buffer
+                         // size in bytes (at least the operand exchange)
+    int32_t pad[3];
 };
 
 struct FusedPlan {
     bool ok = false;
     int32_t ch = 4;                     // channels per chunk
-    int32_t max_piece_bytes = 0;        // largest piece stage (descriptors + psi + ch windows)
+    int32_t max_piece_bytes = 0;        // largest streamed piece stage (descriptors + psi + ch windows)
+    int32_t max_resident_bytes = 0;     // largest resident layout (descriptors + psi + 2 window buffers)
     int32_t max_win = 0;                // largest window area per channel
     std::vector<int32_t> ho_piece;      // [Ho + 1]: pieces of latitude ho
     std::vector<int32_t> ho_order;      // latitudes, heaviest first
@@ -72,9 +77,11 @@ struct FusedPlan {
 };
 
 // Build the plan; a piece stage takes at most `piece_budget` bytes of LDS for
-// `ch` channels.  ok = false if the shape is outside the packed kernel
-// (K > 16, s > 2, Wo not a multiple of 8).
-void build_fused_plan(const CSRView &c, int ch, int piece_budget, FusedPlan &out);
+// `ch` channels; a latitude of one piece is resident when its descriptors,
+// psi and two window buffers of at least `xch_bytes` each fit 2 * piece_budget.
+// ok = false if the shape is outside the packed kernel (K > 16, s > 2, Wo not
+// a multiple of 8).
+void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes, FusedPlan &out);
 
 // Bytes of one piece stage in LDS.
 inline int64_t fused_piece_bytes(int64_t desc_words, int64_t a_elems, int64_t ch, int64_t win_elems)
