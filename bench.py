@@ -168,14 +168,15 @@ def main():
         per[op] = d
 
     dom = max(per, key=lambda o: per[o]["ms"])
+    traffic = counter_traffic(dom)
     dd = per[dom]
     if dd["bound"] == "mfma":
         roofline = {"bound": "mfma", "achieved": dd["mfma_tflops_algorithmic"], "peak": PEAK_BF16_MFMA_TFLOPS,
-                    "unit": "TFLOP/s", "frac": dd["mfma_frac"], "traffic": None, "kernel": dom,
+                    "unit": "TFLOP/s", "frac": dd["mfma_frac"], "traffic": traffic, "kernel": dom,
                     "note": "algorithmic flops: 2 per nnz-update + 2 per einsum MAC; dense bf16 MFMA peak"}
     else:
         roofline = {"bound": "alu", "achieved": dd["valu_tflops"], "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                    "frac": dd["valu_frac"], "traffic": None, "kernel": dom,
+                    "frac": dd["valu_frac"], "traffic": traffic, "kernel": dom,
                     "note": "fp32 vector FMA peak (packed); one nnz-update = 2 flop"}
 
     cpu = None
@@ -203,6 +204,31 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+KERNEL_SOURCES = {"fused": "kernels_fused_mfma.hip"}
+
+
+def counter_traffic(op):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the committed counter summary,
+    or None when that summary was taken from a different kernel source than the one built here."""
+    import hashlib
+    import re
+
+    name = KERNEL_SOURCES.get(op)
+    summary = os.path.join(ROOT, "profiles", "disco_step_721x1440_hbm_counters.md")
+    if name is None or not os.path.exists(summary):
+        return None
+    with open(os.path.join(ROOT, "sparse_gather_contraction_amd", "csrc", name), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    with open(summary) as f:
+        for line in f:
+            m = re.match(r"traffic-record: (\{.*\})", line.strip())
+            if m:
+                rec = json.loads(m.group(1))
+                if rec.get("kernel") == op and rec.get("source_sha256") == digest:
+                    return int(rec["read_bytes"] + rec["write_bytes"])
+    return None
 
 
 def cpu_baseline(wf, wb, wu, psi_fb, psi_u):
