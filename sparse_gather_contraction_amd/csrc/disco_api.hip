@@ -338,7 +338,12 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         // two piece stage buffers share what the W slice leaves of the workgroup's LDS
         const int ch = disco::fused_mfma_channels_per_chunk();
         const int budget = ((kLdsPerBlock - (int)disco::fused_mfma_reserved_bytes()) / 2) & ~15;
-        disco::build_fused_plan(v, ch, budget, disco::fused_mfma_exchange_bytes(), fup);
+        disco::PhasePlanParams prm;
+        prm.kr = 16;
+        prm.ch = ch;
+        prm.piece_budget = budget;
+        prm.xch_bytes = disco::fused_mfma_exchange_bytes();
+        disco::build_phase_plan(v, prm, fup);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
     }

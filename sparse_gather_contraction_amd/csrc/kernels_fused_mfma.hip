@@ -102,7 +102,8 @@ __device__ __forceinline__ void copy_units(const Ctx &c, __amdgpu_buffer_rsrc_t 
     }
 }
 
-// x windows of one piece for the chunk starting at channel c0.  Rows go round the waves; a wave
+// x windows of one piece for the chunk starting at channel c0: window of row r holds input
+// columns s px0 + start + i (mod Wi) of input latitude hi.  Rows go round the waves; a wave
 // handles all channels of its rows (row data is read once, no integer division).
 __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, int c0, bf16_t *win)
 {
@@ -113,11 +114,11 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
         const FRow fr = c.rows[pc.row_begin + r];
         bf16_t *dst = win + fr.win_off;
         const int nch = fr.len >> 3;
-        int g0 = c.px0 + fr.start;  // within a few L of [0, L)
-        while (g0 < 0) g0 += c.L;
-        while (g0 >= c.L) g0 -= c.L;
+        int g0 = c.s * c.px0 + fr.start;  // within a few Wi of [0, Wi)
+        while (g0 < 0) g0 += c.Wi;
+        while (g0 >= c.Wi) g0 -= c.Wi;
         if (c.vec_x) {
-            // s == 1, rows 16-byte aligned: 8-position runs never straddle the row end.  One buffer
+            // Wi and g0 are multiples of 8: 8-column runs never straddle the row end.  One buffer
             // resource spans the chunk's channel planes.
             const uint32_t plane_bytes = 2u * (uint32_t)c.plane_sz;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(plane0, plane_bytes * (uint32_t)ccn);
@@ -125,19 +126,18 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
             for (int t = 0; t < nch; t += 64) {
                 const int e8 = t + c.lane;
                 int pos = g0 + 8 * e8;
-                while (pos >= c.L) pos -= c.L;
+                while (pos >= c.Wi) pos -= c.Wi;
                 const uint32_t voff = row0 + 2u * (uint32_t)pos;
                 if (e8 < nch) {
                     for (int cl = 0; cl < ccn; ++cl) dma16(rs, voff + plane_bytes * cl, dst + cl * pc.win_elems + 8 * t);
                 }
             }
         } else {
-            const int hi = fr.sr / c.s, rho = fr.sr - hi * c.s;
+            const bf16_t *xrow = plane0 + (int64_t)fr.sr * c.Wi;
             for (int e = c.lane; e < fr.len; e += 64) {
                 int pos = g0 + e;
-                while (pos >= c.L) pos -= c.L;
-                const int64_t off = (int64_t)hi * c.Wi + (int64_t)c.s * pos + rho;
-                for (int cl = 0; cl < ccn; ++cl) dst[cl * pc.win_elems + e] = plane0[cl * c.plane_sz + off];
+                while (pos >= c.Wi) pos -= c.Wi;
+                for (int cl = 0; cl < ccn; ++cl) dst[cl * pc.win_elems + e] = xrow[cl * c.plane_sz + pos];
             }
         }
         for (int cl = ccn; cl < kCh; ++cl)  // channels past C are zeros
@@ -395,11 +395,12 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const int r = c.lane & 31, hh = c.lane >> 5;
     const int m = r & 15;
     const int kb = (m < 8) ? 8 * (m >> 2) + (m & 3) : 8 * ((m - 8) >> 2) + 4 + (m & 3);
-    // psi words: offset pair (base + 8 hh - q) / 2 rounded down, basis kb; odd q reads one offset early
-    const int ph0 = r >> 4;
-    const int a_lane2 = 64 * (4 * hh - pp - ph0) + 4 * kb;  // bytes
-    const unsigned sel = ph0 ? 0x05040302u : 0x03020100u;
-    const int x_lane2 = 2 * (8 * r + 8 * hh);            // bytes
+    // psi words: offset pair (base + 8 hh - s q) / 2 rounded down, basis kb; an odd shift reads one
+    // offset early and realigns
+    const int q = 2 * pp + (r >> 4), sq = s * q;
+    const int a_lane2 = 64 * (4 * hh - (sq + 1) / 2) + 4 * kb;  // bytes
+    const unsigned sel = (sq & 1) ? 0x05040302u : 0x03020100u;
+    const int x_lane2 = 2 * (8 * s * r + 8 * hh);                // bytes
 
     f32x16 yacc[2][NOTH];
 #pragma unroll
@@ -497,7 +498,7 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     // direct loads need 16-byte aligned runs and buffer offsets below 2^31
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
                           (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
-    const int vec_x = (a.s == 1 && a.Wo % 8 == 0 && planes16) ? 1 : 0;
+    const int vec_x = planes16 ? 1 : 0;
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
 #define DISCO_FUSED_LAUNCH(N)                                                                                  \
     hipLaunchKernelGGL(fused_mfma_kernel<N>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x, \

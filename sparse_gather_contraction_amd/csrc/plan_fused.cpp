@@ -22,41 +22,42 @@ uint16_t bf16_rne(float f)
 int32_t floor8(int32_t v) { return (v >= 0) ? (v / 8) * 8 : -(((-v) + 7) / 8) * 8; }
 
 struct SubRow {
-    int32_t sr;
-    std::vector<int32_t> d0;  // kept block starts, ascending (multiples of 8, step 16)
-    int32_t first() const { return d0.front(); }
-    int32_t ra() const { return d0.back() - d0.front() + 26; }    // psi e-rows (even)
-    int32_t len() const { return d0.back() - d0.front() + 264; }  // window positions
+    int32_t hi;                // input latitude (the source row)
+    std::vector<int32_t> t0;   // kept block starts, ascending (multiples of 8, step 16)
+    int32_t first() const { return t0.front(); }
 };
-
-int64_t sub_cost(const SubRow &s, int ch)
-{
-    return fused_piece_bytes(2 * (int64_t)s.d0.size(), 16 * (int64_t)s.ra(), ch, s.len());
-}
 
 }  // namespace
 
-void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes, FusedPlan &out)
+void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &out)
 {
     out = FusedPlan();
     const int32_t s = c.Wi / c.Wo;
-    const int32_t L = c.Wo;
-    if (c.K > kFusedKMax || s > 2 || L % 8 != 0) return;
+    const int32_t kr = prm.kr, ch = prm.ch;
+    if (c.K > kr || (kr != 8 && kr != 16) || s < 1 || s > 2 || c.Wo % 8 != 0 || c.Wi % 8 != 0) return;
     out.ch = ch;
+    out.kr = kr;
+    out.s = s;
     out.ho_piece.push_back(0);
     std::vector<int64_t> work(c.Ho, 0);
+    const int32_t smax = 7 * s;                            // largest phase shift of psi
+    auto ra_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 8 * s + 18; };   // psi e-rows (even)
+    auto len_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 256 * s + 8; };  // window positions
+    auto cost_of = [&](int64_t nblk, int64_t a_elems, int64_t win) {
+        return fused_piece_bytes(2 * nblk, a_elems, ch, win);
+    };
+    const int32_t ra_pad = 8 * s + 18;
 
     for (int32_t ho = 0; ho < c.Ho; ++ho) {
-        // dense psi per source row: sr -> (d -> P[k])
+        // dense psi per input latitude: hi -> (t -> P[k]), t = signed input-column offset
         std::map<int32_t, std::map<int32_t, std::vector<float>>> rowsP;
         for (int32_t k = 0; k < c.K; ++k) {
             const int64_t r = (int64_t)k * c.Ho + ho;
             for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e) {
-                const int32_t sr = c.col_hi[e] * s + c.col_wi[e] % s;
-                const int32_t j = c.col_wi[e] / s;
-                const int32_t d = (j <= L / 2) ? j : j - L;
-                auto &v = rowsP[sr][d];
-                if (v.empty()) v.assign(kFusedKMax, 0.0f);
+                const int32_t wi = c.col_wi[e];
+                const int32_t t = (wi <= c.Wi / 2) ? wi : wi - c.Wi;
+                auto &v = rowsP[c.col_hi[e]][t];
+                if (v.empty()) v.assign(kr, 0.0f);
                 v[k] = c.val[e];
             }
         }
@@ -65,25 +66,26 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes,
         std::vector<SubRow> subs;
         for (auto &kv : rowsP) {
             const auto &m = kv.second;
-            const int32_t dmin = m.begin()->first, dmax = m.rbegin()->first;
-            const int32_t D0 = floor8(dmin);
+            const int32_t tmin = m.begin()->first, tmax = m.rbegin()->first;
+            const int32_t T0 = floor8(tmin);
             std::vector<int32_t> kept;
-            for (int32_t d0 = D0; d0 - 16 + 9 <= dmax || d0 == D0; d0 += kBlkJ) {
-                auto it = m.lower_bound(d0 - 7);
-                if (it != m.end() && it->first <= d0 + kBlkJ - 1) kept.push_back(d0);
+            for (int32_t t0 = T0; t0 == T0 || t0 - 1 - smax < tmax; t0 += kBlkJ) {
+                auto it = m.lower_bound(t0 - smax);
+                if (it != m.end() && it->first <= t0 + kBlkJ - 1) kept.push_back(t0);
             }
             SubRow cur;
-            cur.sr = kv.first;
-            for (int32_t d0 : kept) {
+            cur.hi = kv.first;
+            for (int32_t t0 : kept) {
                 SubRow trial = cur;
-                trial.d0.push_back(d0);
-                if (!cur.d0.empty() && sub_cost(trial, ch) > piece_budget) {
+                trial.t0.push_back(t0);
+                if (!cur.t0.empty() &&
+                    cost_of((int64_t)trial.t0.size(), (int64_t)kr * ra_of(trial), len_of(trial)) > prm.piece_budget) {
                     subs.push_back(cur);
-                    cur.d0.clear();
+                    cur.t0.clear();
                 }
-                cur.d0.push_back(d0);
+                cur.t0.push_back(t0);
             }
-            if (!cur.d0.empty()) subs.push_back(cur);
+            if (!cur.t0.empty()) subs.push_back(cur);
         }
         // group sub-rows into pieces
         size_t q = 0;
@@ -91,10 +93,10 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes,
             size_t q1 = q;
             int64_t nb = 0, ae = 0, we = 0;
             while (q1 < subs.size()) {
-                const int64_t nb2 = nb + (int64_t)subs[q1].d0.size();
-                const int64_t ae2 = ae + 16 * (int64_t)subs[q1].ra();
-                const int64_t we2 = we + subs[q1].len();
-                if (q1 > q && fused_piece_bytes(2 * (nb2 + 1), ae2 + 26 * 16, ch, we2) > piece_budget) break;
+                const int64_t nb2 = nb + (int64_t)subs[q1].t0.size();
+                const int64_t ae2 = ae + (int64_t)kr * ra_of(subs[q1]);
+                const int64_t we2 = we + len_of(subs[q1]);
+                if (q1 > q && cost_of(nb2 + 1, ae2 + (int64_t)kr * ra_pad, we2) > prm.piece_budget) break;
                 nb = nb2; ae = ae2; we = we2;
                 ++q1;
             }
@@ -104,46 +106,46 @@ void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes,
             pc.nblk = (int32_t)(nb + (pad ? 1 : 0));
             pc.desc_words = 2 * pc.nblk;
             pc.a_begin = (int32_t)out.adata.size();
-            pc.a_elems = (int32_t)(ae + (pad ? 26 * 16 : 0));
+            pc.a_elems = (int32_t)(ae + (pad ? kr * ra_pad : 0));
             pc.row_begin = (int32_t)out.rows.size();
             pc.win_elems = (int32_t)we;
             int32_t a_row_e = 0, win_off = 0;
             for (size_t j = q; j < q1; ++j) {
                 const SubRow &sb = subs[j];
-                const int32_t first = sb.first(), ra = sb.ra();
-                const auto &m = rowsP[sb.sr];
+                const int32_t first = sb.first(), ra = ra_of(sb);
+                const auto &m = rowsP[sb.hi];
                 FRow fr;
-                fr.sr = sb.sr;
+                fr.sr = sb.hi;
                 fr.start = first;
-                fr.len = sb.len();
+                fr.len = len_of(sb);
                 fr.win_off = win_off;
                 out.rows.push_back(fr);
-                for (int32_t d0 : sb.d0) {
-                    out.descs.push_back(2 * 16 * (a_row_e + (d0 - first) + 8));
-                    out.descs.push_back(2 * (win_off + (d0 - first)));
+                for (int32_t t0 : sb.t0) {
+                    out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));
+                    out.descs.push_back(2 * (win_off + (t0 - first)));
                 }
-                // [e pair][k][2]: psi at offset first - 8 + e, basis k, at (e / 2) * 32 + 2 k + e % 2
+                // [e pair][k][2]: psi at offset first - 8 s + e, basis k, at (e / 2) * 2 kr + 2 k + e % 2
                 for (int32_t e2 = 0; e2 < ra; e2 += 2) {
-                    auto it0 = m.find(first - 8 + e2), it1 = m.find(first - 8 + e2 + 1);
-                    for (int32_t k = 0; k < 16; ++k) {
+                    auto it0 = m.find(first - 8 * s + e2), it1 = m.find(first - 8 * s + e2 + 1);
+                    for (int32_t k = 0; k < kr; ++k) {
                         out.adata.push_back((it0 != m.end() && k < c.K) ? bf16_rne(it0->second[k]) : (uint16_t)0);
                         out.adata.push_back((it1 != m.end() && k < c.K) ? bf16_rne(it1->second[k]) : (uint16_t)0);
                     }
                 }
                 a_row_e += ra;
-                win_off += sb.len();
+                win_off += fr.len;
             }
             if (pad) {  // zero psi rows; the window offset reads the piece's first window
-                out.descs.push_back(2 * 16 * (a_row_e + 8));
+                out.descs.push_back(2 * kr * (a_row_e + 8 * s));
                 out.descs.push_back(0);
-                out.adata.insert(out.adata.end(), 26 * 16, (uint16_t)0);
+                out.adata.insert(out.adata.end(), (size_t)kr * ra_pad, (uint16_t)0);
             }
             pc.row_end = (int32_t)out.rows.size();
             pc.resident = 0;
             pc.pad[0] = pc.pad[1] = pc.pad[2] = 0;
             const int64_t stage_bytes = 4 * (int64_t)pc.desc_words + 2 * (int64_t)pc.a_elems;
-            const int64_t wbuf = std::max<int64_t>(2 * (int64_t)ch * pc.win_elems, xch_bytes);
-            if (q == 0 && q1 == subs.size() && stage_bytes + 2 * wbuf <= 2 * (int64_t)piece_budget) {
+            const int64_t wbuf = std::max<int64_t>(2 * (int64_t)ch * pc.win_elems, prm.xch_bytes);
+            if (prm.allow_resident && q == 0 && q1 == subs.size() && stage_bytes + 2 * wbuf <= 2 * (int64_t)prm.piece_budget) {
                 pc.resident = (int32_t)wbuf;
                 out.max_resident_bytes = std::max<int32_t>(out.max_resident_bytes, (int32_t)(stage_bytes + 2 * wbuf));
             } else {

@@ -1,28 +1,27 @@
-// plan_fused.hpp — phase-split psi plan for the matrix-core fused convolution.
+// plan_fused.hpp — phase-split psi plan for the matrix-core contraction (fused conv and forward).
 //
 // Output longitudes are handled in spans of 256 = 8 phases x 32 columns:
-// column n of phase q is longitude px0 + 8n + q.  For one output latitude ho
-// and one source row sr (input latitude hi and longitude residue rho; row sr
-// holds x[hi, rho + s*j] for j in [0, Wo)), with psi values P[k, d] at signed
-// longitude offsets d,
+// column n of phase q is longitude px0 + 8n + q.  With s = Wi/Wo and psi values
+// P[k, t] of one output latitude ho and one input latitude hi at signed
+// input-column offsets t,
 //
-//   out[k, px0 + 8n + q] = sum_d P[k, d] * xrow[px0 + 8n + q + d]
-//                        = sum_blocks sum_{t<16} P[k, d0 + t - q] * xrow[px0 + 8n + d0 + t]
+//   out[k, px0 + 8n + q] = sum_t P[k, t] * x[hi, s (px0 + 8n + q) + t]
+//                        = sum_blocks sum_{u<16} P[k, t0 + u - s q] * x[hi, s px0 + 8 s n + t0 + u]
 //
-// where the blocks start at offsets d0 that are multiples of 8 and step by 16
-// (the first at floor8(min d), enough of them that d0 + 16 - 7 passes max d).
-// The x operand of a block, xrow[px0 + 8n + d0 + t], does not depend on the
-// phase and is read as aligned 16-byte runs; the phase only shifts psi.  One
-// v_mfma_f32_32x32x16_bf16 per (block, channel, pair of phases) computes 16
-// basis rows for two phases at once.
+// where the blocks start at offsets t0 that are multiples of 8 and step by 16
+// (the first at floor8(min t), enough of them that t0 + 16 - 7 s passes max t).
+// The x operand of a block, x[hi, s px0 + 8 s n + t0 + u], does not depend on
+// the phase and is read as aligned 16-byte runs; the phase only shifts psi.
+// One v_mfma_f32_32x32x16_bf16 per (block, channel, phase group) computes kr
+// basis rows for 32/kr phases at once (kr = 16: two phases, kr = 8: four).
 //
-// Per source row the plan stores psi densely as bf16 (round to nearest even)
-// by e = d - (first block start - 8) and basis k, pairs of e interleaved
-// ([e/2][k][e%2], so one 4-byte word holds two consecutive offsets); per block
-// a descriptor (byte offsets of its psi rows and of its window run in the
-// piece stage); per row the window of source positions px0 + first + i,
-// i < len = span of its blocks + 264.  Blocks are contracted in pairs: a piece
-// with an odd block count gets a zero block.
+// Per input latitude the plan stores psi densely as bf16 (round to nearest
+// even) by e = t - (first block start - 8 s) and basis k, pairs of e
+// interleaved ([e/2][k][e%2], so one 4-byte word holds two consecutive
+// offsets); per block a descriptor (byte offsets of its psi rows and of its
+// window run in the piece stage); per row the window of input columns
+// s px0 + first + i, i < len = span of its blocks + 256 s + 8 (mod Wi).  Blocks
+// are contracted in pairs: a piece with an odd block count gets a zero block.
 //
 // Rows are cut into sub-rows and grouped into pieces; a piece's descriptors,
 // psi and windows (for one chunk of channels) fit one of two LDS stage
@@ -41,8 +40,8 @@ constexpr int kBlkJ = 16;        // offsets per block (MFMA reduction depth)
 constexpr int kFusedSpan = 256;  // output longitudes per workgroup (8 phases x 32 columns)
 
 struct FRow {          // one sub-row of a piece
-    int32_t sr;        // source row = hi * s + rho
-    int32_t start;     // signed offset of the window's first position (window = px0 + start + i)
+    int32_t sr;        // source row = input latitude hi
+    int32_t start;     // signed input-column offset of the window's first position (window = s px0 + start + i)
     int32_t len;       // window length in positions (multiple of 8)
     int32_t win_off;   // element offset of this window inside one channel's window area
 };
@@ -64,6 +63,8 @@ struct FPiece {
 struct FusedPlan {
     bool ok = false;
     int32_t ch = 4;                     // channels per chunk
+    int32_t kr = 16;                    // basis rows per phase in one MFMA (16 or 8)
+    int32_t s = 1;                      // Wi / Wo
     int32_t max_piece_bytes = 0;        // largest streamed piece stage (descriptors + psi + ch windows)
     int32_t max_resident_bytes = 0;     // largest resident layout (descriptors + psi + 2 window buffers)
     int32_t max_win = 0;                // largest window area per channel
@@ -76,12 +77,20 @@ struct FusedPlan {
     int64_t mfma_blocks = 0;            // total blocks over all latitudes
 };
 
+struct PhasePlanParams {
+    int kr = 16;            // basis rows per phase in one MFMA: 16 or 8 (K <= kr)
+    int ch = 4;             // channels per stage
+    int piece_budget = 0;   // LDS bytes of one piece stage
+    int xch_bytes = 0;      // smallest window buffer of a resident latitude
+    bool allow_resident = true;
+};
+
 // Build the plan; a piece stage takes at most `piece_budget` bytes of LDS for
 // `ch` channels; a latitude of one piece is resident when its descriptors,
 // psi and two window buffers of at least `xch_bytes` each fit 2 * piece_budget.
-// ok = false if the shape is outside the packed kernel (K > 16, s > 2, Wo not
-// a multiple of 8).
-void build_fused_plan(const CSRView &c, int ch, int piece_budget, int xch_bytes, FusedPlan &out);
+// ok = false if the shape is outside the packed kernels (K > kr, s > 2, Wo or
+// Wi not a multiple of 8).
+void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &out);
 
 // Bytes of one piece stage in LDS.
 inline int64_t fused_piece_bytes(int64_t desc_words, int64_t a_elems, int64_t ch, int64_t win_elems)
