@@ -48,6 +48,7 @@ struct DevStaged {
 };
 
 constexpr int kLdsPerBlock = 160 * 1024;       // gfx950: a workgroup may allocate the whole 160 KiB
+constexpr int kFwdMfmaStageBytes = 40 * 1024;  // two stages per forward workgroup, two workgroups per CU
 
 struct DevFused {
     bool ok = false;
@@ -57,7 +58,7 @@ struct DevFused {
     uint16_t *adata = nullptr;
     int32_t *ho_piece = nullptr;
     int32_t *ho_order = nullptr;
-    int32_t max_piece_bytes = 0, max_resident_bytes = 0;
+    int32_t max_piece_bytes = 0, max_resident_bytes = 0, kr = 16;
     uint32_t desc_bytes = 0, adata_bytes = 0;
 };
 
@@ -137,6 +138,7 @@ hipError_t upload_fused(DevFused &d, const disco::FusedPlan &p)
     d.ok = true;
     d.max_piece_bytes = p.max_piece_bytes;
     d.max_resident_bytes = p.max_resident_bytes;
+    d.kr = p.kr;
     d.desc_bytes = (uint32_t)(p.descs.size() * sizeof(int32_t));
     d.adata_bytes = (uint32_t)(p.adata.size() * sizeof(uint16_t));
     return hipSuccess;
@@ -222,6 +224,7 @@ struct disco_psi_s {
     DevPlan fwd, bwd;
     DevStaged sfwd[2], sbwd[2];  // staged plans by source dtype: [0] fp32, [1] bf16
     DevFused fused;
+    DevFused fwdm;  // phase-split plan of the matrix-core forward (bf16)
     int32_t *ho_order = nullptr;
 };
 
@@ -333,7 +336,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the staged plan");
     }
-    disco::FusedPlan fup;
+    disco::FusedPlan fup, fwp;
     try {
         // two piece stage buffers share what the W slice leaves of the workgroup's LDS
         const int ch = disco::fused_mfma_channels_per_chunk();
@@ -344,6 +347,13 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         prm.piece_budget = budget;
         prm.xch_bytes = disco::fused_mfma_exchange_bytes();
         disco::build_phase_plan(v, prm, fup);
+        disco::PhasePlanParams fprm;
+        fprm.kr = csr->K <= 8 ? 8 : 16;
+        fprm.ch = disco::fwd_mfma_channels(fprm.kr);
+        fprm.piece_budget = kFwdMfmaStageBytes;
+        fprm.xch_bytes = 0;
+        fprm.allow_resident = false;
+        disco::build_phase_plan(v, fprm, fwp);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
     }
@@ -377,11 +387,13 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         if (e == hipSuccess) e = upload_staged(h->sbwd[d], sbp[d]);
     }
     if (e == hipSuccess) e = upload_fused(h->fused, fup);
+    if (e == hipSuccess) e = upload_fused(h->fwdm, fwp);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(h->fwd);
         free_plan(h->bwd);
         free_fused(h->fused);
+        free_fused(h->fwdm);
         for (int d = 0; d < 2; ++d) {
             free_staged(h->sfwd[d]);
             free_staged(h->sbwd[d]);
@@ -422,6 +434,7 @@ disco_status disco_psi_destroy(disco_psi h)
         free_staged(h->sbwd[d]);
     }
     free_fused(h->fused);
+    free_fused(h->fwdm);
     (void)hipFree(h->ho_order);
     (void)hipSetDevice(prev);
     delete h;
@@ -442,6 +455,23 @@ disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, vo
     if ((st = check_tensor(out, "out", 5, os, h->device)) != DISCO_OK) return st;
     if (x->dtype != out->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
     const int d = x->dtype == DISCO_BF16 ? 1 : 0;
+    const char *fm = getenv("DISCO_FWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
+    if (d == 1 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
+        if (B * C * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
+        const int fch = disco::fwd_mfma_channels(h->fwdm.kr);
+        if (B * h->Ho * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
+            return fail(DISCO_ERR_SHAPE, "forward grid exceeds 2^31 blocks");
+        disco::FwdMfmaLaunch m;
+        m.x = x->data; m.out = out->data;
+        m.pieces = h->fwdm.pieces; m.rows = h->fwdm.rows; m.descs = h->fwdm.descs; m.adata = h->fwdm.adata;
+        m.ho_piece = h->fwdm.ho_piece; m.ho_order = h->fwdm.ho_order;
+        m.B = (int32_t)B; m.C = (int32_t)C; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
+        m.s = h->Wi / h->Wo; m.kr = h->fwdm.kr; m.max_piece_bytes = h->fwdm.max_piece_bytes;
+        m.desc_bytes = h->fwdm.desc_bytes; m.adata_bytes = h->fwdm.adata_bytes;
+        hipError_t e = disco::launch_fwd_mfma(m, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
+        return DISCO_OK;
+    }
     return run_gather(h->fwd, h->sfwd[d], x->data, out->data, d == 1, B * C, (int64_t)h->Hi * h->Wi,
                       (int64_t)h->K * h->Ho * h->Wo, (hipStream_t)stream);
 }

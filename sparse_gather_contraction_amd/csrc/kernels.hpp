@@ -76,6 +76,21 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
 size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_bytes);
 int fused_mfma_channels_per_chunk();
 int fused_mfma_exchange_bytes();     // LDS bytes of the einsum operand exchange
+
+struct FwdMfmaLaunch {
+    const void *x;
+    void *out;
+    const FPiece *pieces;
+    const FRow *rows;
+    const int32_t *descs;
+    const uint16_t *adata;
+    const int32_t *ho_piece, *ho_order;
+    int32_t B, C, K, Ho, Wo, Hi, Wi, s, kr, max_piece_bytes;
+    uint32_t desc_bytes, adata_bytes;
+};
+
+hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream);
+int fwd_mfma_channels(int kr);       // channels per forward workgroup for a psi group of kr rows
 size_t fused_mfma_reserved_bytes();  // LDS bytes besides the two piece stage buffers
 int fused_max_k();  // largest K the fused kernel accepts
 

@@ -105,10 +105,11 @@ __device__ __forceinline__ void copy_units(const Ctx &c, __amdgpu_buffer_rsrc_t 
 // x windows of one piece for the chunk starting at channel c0: window of row r holds input
 // columns s px0 + start + i (mod Wi) of input latitude hi.  Rows go round the waves; a wave
 // handles all channels of its rows (row data is read once, no integer division).
+template <int NCH>
 __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, int c0, bf16_t *win)
 {
     const int nrows = pc.row_end - pc.row_begin;
-    const int ccn = min(kCh, c.C - c0);
+    const int ccn = min(NCH, c.C - c0);
     const bf16_t *plane0 = c.x + ((int64_t)c.b * c.C + c0) * c.plane_sz;
     for (int r = c.wave; r < nrows; r += kWaves) {
         const FRow fr = c.rows[pc.row_begin + r];
@@ -140,7 +141,7 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
                 for (int cl = 0; cl < ccn; ++cl) dst[cl * pc.win_elems + e] = xrow[cl * c.plane_sz + pos];
             }
         }
-        for (int cl = ccn; cl < kCh; ++cl)  // channels past C are zeros
+        for (int cl = ccn; cl < NCH; ++cl)  // channels past C are zeros
             for (int e8 = c.lane; e8 < nch; e8 += 64)
                 *reinterpret_cast<uint4 *>(dst + cl * pc.win_elems + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -153,11 +154,12 @@ __device__ __forceinline__ void stage_psi(const Ctx &c, const FPiece &pc, unsign
     copy_units(c, c.adata_rs, 2u * (uint32_t)pc.a_begin, buf + 4 * pc.desc_words, pc.a_elems / 8);
 }
 
-// One step's stage: block descriptors, psi and windows of piece pc for channels c0..c0+kCh-1.
+// One step's stage: block descriptors, psi and windows of piece pc for channels c0..c0+NCH-1.
+template <int NCH>
 __device__ __forceinline__ void stage_step(const Ctx &c, const FPiece &pc, int c0, unsigned char *buf)
 {
     stage_psi(c, pc, buf);
-    stage_windows(c, pc, c0, reinterpret_cast<bf16_t *>(buf + 4 * pc.desc_words + 2 * pc.a_elems));
+    stage_windows<NCH>(c, pc, c0, reinterpret_cast<bf16_t *>(buf + 4 * pc.desc_words + 2 * pc.a_elems));
 }
 
 // W slice of the chunk starting at c0 in A-operand order: unit (ot, cl), lane l holds
@@ -196,6 +198,8 @@ struct Ops {
     bf16x8 b0, b1;
 };
 
+// KR: basis rows of the psi layout; one offset pair of psi spans KR 4-byte words.
+template <int KR>
 __device__ __forceinline__ void load_ops(Ops &o, const unsigned char *a_base, const unsigned char *x_base, int wel2,
                                          int a_off, int x_off)
 {
@@ -203,7 +207,7 @@ __device__ __forceinline__ void load_ops(Ops &o, const unsigned char *a_base, co
     o.b1 = *reinterpret_cast<const bf16x8 *>(x_base + wel2 + x_off);
     const unsigned *p = reinterpret_cast<const unsigned *>(a_base + a_off);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) o.a[i] = p[16 * i];
+    for (int i = 0; i < 5; ++i) o.a[i] = p[KR * i];
 }
 
 // sel: 0x03020100 (even first offset: words as read) or 0x05040302 (odd: shifted by one offset)
@@ -221,6 +225,7 @@ __device__ __forceinline__ void mfma_ops(const Ops &o, unsigned sel, f32x16 (&d)
 // of one block are read while the other block's MFMAs run, and the descriptors of a pair are
 // read two pairs ahead.  Scheduling barriers keep that order (the compiler would otherwise
 // move the reads next to their uses).
+template <int KR>
 __device__ __forceinline__ void contract(const unsigned char *__restrict__ stage, const unsigned char *__restrict__ win,
                                          const FPiece &pc, int a_lane2, int x_lane2, unsigned sel, int ch0,
                                          f32x16 (&d)[2])
@@ -235,14 +240,14 @@ __device__ __forceinline__ void contract(const unsigned char *__restrict__ stage
     int4 dA = desc[0];
     int4 dB = desc[min(1, lastp)];
     Ops P, Q;
-    load_ops(P, a_base, x_base, wel2, dA.x, dA.y);
+    load_ops<KR>(P, a_base, x_base, wel2, dA.x, dA.y);
     for (int j = 0; j < npair; ++j) {
         const int4 dC = desc[min(j + 2, lastp)];
-        load_ops(Q, a_base, x_base, wel2, dA.z, dA.w);
+        load_ops<KR>(Q, a_base, x_base, wel2, dA.z, dA.w);
         __builtin_amdgcn_sched_barrier(0);
         mfma_ops(P, sel, d);
         __builtin_amdgcn_sched_barrier(0);
-        load_ops(P, a_base, x_base, wel2, dB.x, dB.y);
+        load_ops<KR>(P, a_base, x_base, wel2, dB.x, dB.y);
         __builtin_amdgcn_sched_barrier(0);
         mfma_ops(Q, sel, d);
         __builtin_amdgcn_sched_barrier(0);
@@ -320,11 +325,11 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     if (st + 1 < nsteps) {
         const int p1 = (p + 1 == npieces) ? 0 : p + 1;
         const int t1 = (p + 1 == npieces) ? t + 1 : t;
-        stage_step(c, pieces[p_begin + p1], kCh * t1, nxt);
+        stage_step<kCh>(c, pieces[p_begin + p1], kCh * t1, nxt);
     }
     if (p == 0) zero(d);
     const FPiece pc = pieces[p_begin + p];
-    contract(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, sel, 2 * h2, d);
+    contract<16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, sel, 2 * h2, d);
     if (p + 1 == npieces) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
@@ -344,9 +349,9 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t > 0) stage_w(c, kCh * t, wb);
-    if (t + 1 < nchunks) stage_windows(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
+    if (t + 1 < nchunks) stage_windows<kCh>(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
     zero(d);
-    contract(stage, cur, pc, a_lane2, x_lane2, sel, 2 * h2, d);
+    contract<16>(stage, cur, pc, a_lane2, x_lane2, sel, 2 * h2, d);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // W slice visible; `cur` free for the exchange
     einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         unsigned char *w1 = w0 + pc0.resident;
         stage_w(c, 0, wb);
         stage_psi(c, pc0, stage);
-        stage_windows(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
+        stage_windows<kCh>(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
         for (int t = 0; t < nchunks; t += 2) {
             run_chunk_resident<NOTH>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, sel, pp, h2, d, yacc);
             if (t + 1 < nchunks)
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         }
     } else if (nsteps > 0) {
         stage_w(c, 0, wb);
-        stage_step(c, pieces[p_begin], 0, buf0);
+        stage_step<kCh>(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
         for (int st = 0; st < nsteps; st += 2) {
             run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, sel, pp, h2, d,
@@ -466,9 +471,133 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     }
 }
 
+
+// ---- forward contraction on the matrix cores -------------------------------------------------
+//
+// out[b,c,k,ho,wo] for bf16 inputs (the "kpacked" tensor-core forward of the torch-harmonics
+// "disco-kernel-dev" page, re-derived with the same phase-split psi as the fused kernel).
+// Workgroup = (b, ho, 256 output longitudes, FCH channels), eight waves: wave w takes phase group
+// g = w % NG (PH = 32/KR phases per MFMA) and channel pair w / NG.  The latitude's pieces stream
+// through two LDS stage buffers (two workgroups share a CU, so one computes while the other
+// waits for its stage); every output element is written once, from its accumulator.
+
+template <int KR, int FCH>
+__device__ __forceinline__ void fwd_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
+                                         int p, int c0, unsigned char *__restrict__ cur,
+                                         unsigned char *__restrict__ nxt, int a_lane2, int x_lane2, unsigned sel,
+                                         int cp, f32x16 (&d)[2])
+{
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` have landed
+    __syncthreads();                // everyone's have; the previous step is done with `nxt`
+    if (p + 1 < npieces) stage_step<FCH>(c, pieces[p_begin + p + 1], c0, nxt);
+    const FPiece pc = pieces[p_begin + p];
+    contract<KR>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, sel, 2 * cp, d);
+}
+
+template <int KR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void fwd_mfma_kernel(
+    const bf16_t *__restrict__ x, bf16_t *__restrict__ out, const FPiece *__restrict__ pieces,
+    const FRow *__restrict__ rows, const int32_t *__restrict__ descs, const bf16_t *__restrict__ adata,
+    const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order, int B, int C, int K, int Ho, int L,
+    int Hi, int Wi, int s, int n_pxb, int n_cb, int buf_bytes, uint32_t desc_bytes, uint32_t adata_bytes, int vec_x)
+{
+    constexpr int PH = 32 / KR, NG = 8 / PH, WPG = kWaves / NG, FCH = 2 * WPG;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *buf0 = smem;
+    unsigned char *buf1 = smem + buf_bytes;
+
+    int bid = blockIdx.x;
+    const int pxb = bid % n_pxb;
+    bid /= n_pxb;
+    const int cb = bid % n_cb;
+    bid /= n_cb;
+    Ctx c;
+    c.b = bid % B;
+    const int ho = ho_order[bid / B];
+    c.x = x; c.W = nullptr; c.rows = rows;
+    c.descs_rs = make_rsrc(descs, desc_bytes);
+    c.adata_rs = make_rsrc(adata, adata_bytes);
+    c.w_rs = make_rsrc(nullptr, 0u);
+    c.B = B; c.C = C; c.Co = 0; c.K = K; c.L = L; c.Wi = Wi; c.s = s; c.n_ot = 0;
+    c.tid = threadIdx.x;
+    c.lane = c.tid & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    c.px0 = pxb * kFusedSpan;
+    c.o_base = 0;
+    c.plane_sz = (int64_t)Hi * Wi;
+    c.vec_x = vec_x != 0;
+    c.vec_w = false;
+
+    // lane constants: A row r = lane % 32 is (phase PH g + r / KR, basis k = r % KR)
+    const int g = c.wave % NG, cp = c.wave / NG;
+    const int r = c.lane & 31, hh = c.lane >> 5;
+    const int q = PH * g + r / KR, sq = s * q;
+    const int a_lane2 = 4 * KR * (4 * hh - (sq + 1) / 2) + 4 * (r % KR);  // bytes
+    const unsigned sel = (sq & 1) ? 0x05040302u : 0x03020100u;
+    const int x_lane2 = 2 * (8 * s * r + 8 * hh);                        // bytes
+
+    f32x16 d[2];
+    zero(d);
+    const int p_begin = ho_piece[ho];
+    const int npieces = ho_piece[ho + 1] - p_begin;
+    const int c0 = cb * FCH;
+    if (npieces > 0) {
+        stage_step<FCH>(c, pieces[p_begin], c0, buf0);
+        for (int p = 0; p < npieces; p += 2) {
+            fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p, c0, buf0, buf1, a_lane2, x_lane2, sel, cp, d);
+            if (p + 1 < npieces)
+                fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p + 1, c0, buf1, buf0, a_lane2, x_lane2, sel, cp, d);
+        }
+    }
+
+    // ---- epilogue: register a of lane (n = r, hh) is row 8 (a / 4) + 4 hh + a % 4 = (phase, k) ----
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const int cc = c0 + 2 * cp + cl;
+        if (cc >= C) continue;
+        bf16_t *orow = out + ((int64_t)c.b * C + cc) * K * (int64_t)Ho * L + (int64_t)ho * L;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const int row = 8 * (a >> 2) + 4 * hh + (a & 3);
+            const int k = row % KR, wo = c.px0 + 8 * r + PH * g + row / KR;
+            if (k < K && wo < L) orow[(int64_t)k * Ho * L + wo] = f32_to_bf16(d[cl][a]);
+        }
+    }
+}
+
 }  // namespace
 
 int fused_mfma_channels_per_chunk() { return kCh; }
+
+int fwd_mfma_channels(int kr) { return kr == 8 ? 8 : 4; }
+
+hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
+{
+    if (a.B == 0 || a.C == 0) return hipSuccess;
+    const int fch = fwd_mfma_channels(a.kr);
+    const int n_pxb = (a.Wo + kFusedSpan - 1) / kFusedSpan;
+    const int n_cb = (a.C + fch - 1) / fch;
+    const int buf_bytes = (a.max_piece_bytes + 15) & ~15;
+    const size_t lds = 2 * (size_t)buf_bytes;
+    const void *fn = a.kr == 8 ? (const void *)fwd_mfma_kernel<8> : (const void *)fwd_mfma_kernel<16>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t nblk = (int64_t)a.B * a.Ho * n_cb * n_pxb;
+    const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
+                          (int64_t)a.Hi * a.Wi * 2 * fch < ((int64_t)1 << 31);
+    const int vec_x = planes16 ? 1 : 0;
+    if (a.kr == 8)
+        hipLaunchKernelGGL(fwd_mfma_kernel<8>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x,
+                           (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order,
+                           a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes, a.desc_bytes,
+                           a.adata_bytes, vec_x);
+    else
+        hipLaunchKernelGGL(fwd_mfma_kernel<16>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x,
+                           (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order,
+                           a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes, a.desc_bytes,
+                           a.adata_bytes, vec_x);
+    return hipGetLastError();
+}
 
 int fused_mfma_exchange_bytes() { return kXchBytes; }
 

@@ -347,3 +347,19 @@ def test_fused_both_kernels_agree_with_oracle(mfma, monkeypatch):
     ref = oracle.fused(psi, x, W)
     nrm = oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)
     assert normalised_error(y, ref, nrm) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mfma", ["0", "1"])
+@pytest.mark.parametrize("geom", [(31, 64, 31, 64, 0.5, 4, 2, 9), (33, 128, 17, 64, 0.6, 4, 2, 8),
+                                  (25, 48, 25, 48, 0.7, 4, 4, 5), (19, 144, 19, 72, 0.7, 4, 1, 3)])
+def test_fwd_bf16_both_kernels_agree_with_oracle(geom, mfma, monkeypatch):
+    """bf16 forward on the matrix cores (phase-split psi; K <= 8 and K = 16, s = 1 and 2, ragged
+    channel counts and longitude spans) and, with DISCO_FWD_MFMA=0, on the vector-ALU gather."""
+    monkeypatch.setenv("DISCO_FWD_MFMA", mfma)
+    Hi, Wi, Ho, Wo, tc, nr, na, C = geom
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((2, C, Hi, Wi), 960 + C, "bf16")
+    out = sgc.disco_fwd(h, x.to(DEV))
+    torch.cuda.synchronize()
+    assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL["bf16"]
