@@ -49,6 +49,7 @@ struct DevStaged {
 
 constexpr int kLdsPerBlock = 160 * 1024;       // gfx950: a workgroup may allocate the whole 160 KiB
 constexpr int kFwdMfmaStageBytes = 40 * 1024;  // two stages per forward workgroup, two workgroups per CU
+constexpr int kBwdMfmaRows = 8;                // gradient rows (input row, residue) per matrix-core group
 
 struct DevFused {
     bool ok = false;
@@ -225,6 +226,7 @@ struct disco_psi_s {
     DevStaged sfwd[2], sbwd[2];  // staged plans by source dtype: [0] fp32, [1] bf16
     DevFused fused;
     DevFused fwdm;  // phase-split plan of the matrix-core forward (bf16)
+    DevFused bwdm;  // phase-split plan of the inverse CSR: the matrix-core backward (bf16)
     int32_t *ho_order = nullptr;
 };
 
@@ -336,7 +338,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the staged plan");
     }
-    disco::FusedPlan fup, fwp;
+    disco::FusedPlan fup, fwp, bwp;
     try {
         // two piece stage buffers share what the W slice leaves of the workgroup's LDS
         const int ch = disco::fused_mfma_channels_per_chunk();
@@ -354,6 +356,12 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         fprm.xch_bytes = 0;
         fprm.allow_resident = false;
         disco::build_phase_plan(v, fprm, fwp);
+        disco::InverseCSR inv;
+        disco::build_inverse_csr(v, kBwdMfmaRows, inv);
+        disco::PhasePlanParams bprm = fprm;
+        bprm.kr = kBwdMfmaRows;
+        bprm.ch = disco::fwd_mfma_channels(bprm.kr);
+        disco::build_phase_plan(inv.view, bprm, bwp);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");
     }
@@ -388,12 +396,14 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     }
     if (e == hipSuccess) e = upload_fused(h->fused, fup);
     if (e == hipSuccess) e = upload_fused(h->fwdm, fwp);
+    if (e == hipSuccess) e = upload_fused(h->bwdm, bwp);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(h->fwd);
         free_plan(h->bwd);
         free_fused(h->fused);
         free_fused(h->fwdm);
+        free_fused(h->bwdm);
         for (int d = 0; d < 2; ++d) {
             free_staged(h->sfwd[d]);
             free_staged(h->sbwd[d]);
@@ -435,6 +445,7 @@ disco_status disco_psi_destroy(disco_psi h)
     }
     free_fused(h->fused);
     free_fused(h->fwdm);
+    free_fused(h->bwdm);
     (void)hipFree(h->ho_order);
     (void)hipSetDevice(prev);
     delete h;
@@ -468,6 +479,7 @@ disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, vo
         m.B = (int32_t)B; m.C = (int32_t)C; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
         m.s = h->Wi / h->Wo; m.kr = h->fwdm.kr; m.max_piece_bytes = h->fwdm.max_piece_bytes;
         m.desc_bytes = h->fwdm.desc_bytes; m.adata_bytes = h->fwdm.adata_bytes;
+        m.om.plane = (int64_t)h->K * h->Ho * h->Wo; m.om.inverse = 0; m.om.rows = 0; m.om.wi = 0; m.om.s = 1;
         hipError_t e = disco::launch_fwd_mfma(m, (hipStream_t)stream);
         if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
         return DISCO_OK;
@@ -490,6 +502,26 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
     if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
     if (gout->dtype != gx->dtype) return fail(DISCO_ERR_DTYPE, "gout and gx dtypes differ");
     const int d = gout->dtype == DISCO_BF16 ? 1 : 0;
+    const char *bm = getenv("DISCO_BWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
+    if (d == 1 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
+        if (B * C * h->Hi == 0 || h->Wi == 0) return DISCO_OK;
+        const int fch = disco::fwd_mfma_channels(h->bwdm.kr);
+        const int32_t s = h->Wi / h->Wo;
+        const int32_t groups = (h->Hi * s + kBwdMfmaRows - 1) / kBwdMfmaRows;
+        if (B * groups * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
+            return fail(DISCO_ERR_SHAPE, "backward grid exceeds 2^31 blocks");
+        disco::FwdMfmaLaunch m;
+        m.x = gout->data; m.out = gx->data;
+        m.pieces = h->bwdm.pieces; m.rows = h->bwdm.rows; m.descs = h->bwdm.descs; m.adata = h->bwdm.adata;
+        m.ho_piece = h->bwdm.ho_piece; m.ho_order = h->bwdm.ho_order;
+        m.B = (int32_t)B; m.C = (int32_t)C; m.K = kBwdMfmaRows; m.Ho = groups; m.Wo = h->Wo;
+        m.Hi = h->K * h->Ho; m.Wi = h->Wo; m.s = 1; m.kr = h->bwdm.kr; m.max_piece_bytes = h->bwdm.max_piece_bytes;
+        m.desc_bytes = h->bwdm.desc_bytes; m.adata_bytes = h->bwdm.adata_bytes;
+        m.om.plane = (int64_t)h->Hi * h->Wi; m.om.inverse = 1; m.om.rows = h->Hi * s; m.om.wi = h->Wi; m.om.s = s;
+        hipError_t e = disco::launch_fwd_mfma(m, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
+        return DISCO_OK;
+    }
     return run_gather(h->bwd, h->sbwd[d], gout->data, gx->data, d == 1, B * C, (int64_t)h->K * h->Ho * h->Wo,
                       (int64_t)h->Hi * h->Wi, (hipStream_t)stream);
 }

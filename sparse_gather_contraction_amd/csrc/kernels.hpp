@@ -77,6 +77,16 @@ size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_byte
 int fused_mfma_channels_per_chunk();
 int fused_mfma_exchange_bytes();     // LDS bytes of the einsum operand exchange
 
+// Where the forward kernel writes: out (B, C, K, Ho, Wo), or, for the backward run as a forward
+// over the inverse CSR, gx (B, C, Hi, Wi) with row ho * kr + k = hi * s + rho at columns rho + s * j.
+struct OutMap {
+    int64_t plane;   // elements per (b, c) plane of the output
+    int32_t inverse; // 0: forward layout; 1: gradient layout
+    int32_t rows;    // inverse: Hi * s
+    int32_t wi;      // inverse: Wi
+    int32_t s;       // inverse: Wi / Wo
+};
+
 struct FwdMfmaLaunch {
     const void *x;
     void *out;
@@ -85,8 +95,9 @@ struct FwdMfmaLaunch {
     const int32_t *descs;
     const uint16_t *adata;
     const int32_t *ho_piece, *ho_order;
-    int32_t B, C, K, Ho, Wo, Hi, Wi, s, kr, max_piece_bytes;
+    int32_t B, C, K, Ho, Wo, Hi, Wi, s, kr, max_piece_bytes;  // geometry of the source/psi (the inverse CSR's for the backward)
     uint32_t desc_bytes, adata_bytes;
+    OutMap om;
 };
 
 hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream);

@@ -499,7 +499,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bf16_t *__restrict__ x, bf16_t *__restrict__ out, const FPiece *__restrict__ pieces,
     const FRow *__restrict__ rows, const int32_t *__restrict__ descs, const bf16_t *__restrict__ adata,
     const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order, int B, int C, int K, int Ho, int L,
-    int Hi, int Wi, int s, int n_pxb, int n_cb, int buf_bytes, uint32_t desc_bytes, uint32_t adata_bytes, int vec_x)
+    int Hi, int Wi, int s, int n_pxb, int n_cb, int buf_bytes, uint32_t desc_bytes, uint32_t adata_bytes, int vec_x,
+    OutMap om)
 {
     constexpr int PH = 32 / KR, NG = 8 / PH, WPG = kWaves / NG, FCH = 2 * WPG;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -555,12 +556,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int cl = 0; cl < 2; ++cl) {
         const int cc = c0 + 2 * cp + cl;
         if (cc >= C) continue;
-        bf16_t *orow = out + ((int64_t)c.b * C + cc) * K * (int64_t)Ho * L + (int64_t)ho * L;
+        bf16_t *plane = out + ((int64_t)c.b * C + cc) * om.plane;
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
             const int row = 8 * (a >> 2) + 4 * hh + (a & 3);
             const int k = row % KR, wo = c.px0 + 8 * r + PH * g + row / KR;
-            if (k < K && wo < L) orow[(int64_t)k * Ho * L + wo] = f32_to_bf16(d[cl][a]);
+            if (k >= K || wo >= L) continue;
+            if (om.inverse) {
+                // row ho * KR + k is input row hi = row / s, residue row % s of the gradient
+                const int rr = ho * KR + k;
+                if (rr < om.rows) {
+                    const int hi = rr / om.s;
+                    plane[(int64_t)hi * om.wi + (rr - hi * om.s) + (int64_t)om.s * wo] = f32_to_bf16(d[cl][a]);
+                }
+            } else {
+                plane[((int64_t)k * Ho + ho) * L + wo] = f32_to_bf16(d[cl][a]);
+            }
         }
     }
 }
@@ -590,12 +601,12 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
         hipLaunchKernelGGL(fwd_mfma_kernel<8>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x,
                            (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order,
                            a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes, a.desc_bytes,
-                           a.adata_bytes, vec_x);
+                           a.adata_bytes, vec_x, a.om);
     else
         hipLaunchKernelGGL(fwd_mfma_kernel<16>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x,
                            (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order,
                            a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes, a.desc_bytes,
-                           a.adata_bytes, vec_x);
+                           a.adata_bytes, vec_x, a.om);
     return hipGetLastError();
 }
 

@@ -170,4 +170,45 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
     out.ok = true;
 }
 
+void build_inverse_csr(const CSRView &c, int g, InverseCSR &out)
+{
+    const int32_t s = c.Wi / c.Wo;
+    const int32_t rows = c.Hi * s;
+    const int32_t groups = (rows + g - 1) / g;
+    const int64_t nrow = (int64_t)g * groups;
+    out.row_ptr.assign(nrow + 1, 0);
+    auto target = [&](int64_t e) {
+        const int32_t wi = c.col_wi[e], rho = wi % s, r = c.col_hi[e] * s + rho;
+        return (int64_t)(r % g) * groups + r / g;
+    };
+    for (int64_t e = 0; e < c.nnz; ++e) ++out.row_ptr[target(e) + 1];
+    for (int64_t r = 0; r < nrow; ++r) out.row_ptr[r + 1] += out.row_ptr[r];
+    out.col_hi.resize(c.nnz);
+    out.col_wi.resize(c.nnz);
+    out.val.resize(c.nnz);
+    std::vector<int64_t> fill(out.row_ptr.begin(), out.row_ptr.end() - 1);
+    for (int32_t k = 0; k < c.K; ++k)
+        for (int32_t ho = 0; ho < c.Ho; ++ho) {
+            const int64_t r = (int64_t)k * c.Ho + ho;
+            for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e) {
+                const int32_t wi = c.col_wi[e], rho = wi % s;
+                const int64_t dst = fill[target(e)]++;
+                out.col_hi[dst] = k * c.Ho + ho;
+                out.col_wi[dst] = (c.Wo - (wi - rho) / s) % c.Wo;
+                out.val[dst] = c.val[e];
+            }
+        }
+    out.view = CSRView();
+    out.view.K = g;
+    out.view.Ho = groups;
+    out.view.Wo = c.Wo;
+    out.view.Hi = c.K * c.Ho;
+    out.view.Wi = c.Wo;
+    out.view.nnz = c.nnz;
+    out.view.row_ptr = out.row_ptr.data();
+    out.view.col_hi = out.col_hi.data();
+    out.view.col_wi = out.col_wi.data();
+    out.view.val = out.val.data();
+}
+
 }  // namespace disco

@@ -92,6 +92,20 @@ struct PhasePlanParams {
 // Wi not a multiple of 8).
 void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &out);
 
+// The backward as a forward over the row-inverted psi.  gx[b,c,hi,rho + s j] =
+// sum over entries (k, ho; hi, wi) with wi = rho (mod s) of val * gout[b,c,k,ho,(j - (wi - rho)/s) mod Wo],
+// i.e. output row r = hi s + rho reads gout row k Ho + ho at column (j + delta) mod Wo with
+// delta = -(wi - rho)/s.  The inverse CSR groups g output rows per "latitude": row index
+// (r % g) * Ho' + r / g, Ho' = ceil(Hi s / g); source "latitudes" are the K Ho gout rows (length Wo,
+// stride 1), so the phase-split plan of this CSR drives the forward kernel.
+struct InverseCSR {
+    std::vector<int64_t> row_ptr;
+    std::vector<int32_t> col_hi, col_wi;
+    std::vector<float> val;
+    CSRView view;
+};
+void build_inverse_csr(const CSRView &c, int g, InverseCSR &out);
+
 // Bytes of one piece stage in LDS.
 inline int64_t fused_piece_bytes(int64_t desc_words, int64_t a_elems, int64_t ch, int64_t win_elems)
 {

@@ -363,3 +363,20 @@ def test_fwd_bf16_both_kernels_agree_with_oracle(geom, mfma, monkeypatch):
     out = sgc.disco_fwd(h, x.to(DEV))
     torch.cuda.synchronize()
     assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("mfma", ["0", "1"])
+@pytest.mark.parametrize("geom", [(31, 64, 31, 64, 0.5, 4, 2, 9), (33, 128, 17, 64, 0.6, 4, 2, 8),
+                                  (25, 48, 25, 48, 0.7, 4, 4, 5), (19, 144, 19, 72, 0.7, 4, 1, 3)])
+def test_bwd_bf16_both_kernels_agree_with_oracle(geom, mfma, monkeypatch):
+    """bf16 backward on the matrix cores (a forward over the inverse CSR: gradient rows grouped by
+    eight, s = 1 and 2, K = 4..16, ragged channel counts) and, with DISCO_BWD_MFMA=0, on the
+    vector-ALU gather."""
+    monkeypatch.setenv("DISCO_BWD_MFMA", mfma)
+    Hi, Wi, Ho, Wo, tc, nr, na, C = geom
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
+    h = sgc.disco_psi_create(psi, 0)
+    g = randn((2, C, psi.K, Ho, Wo), 970 + C, "bf16")
+    gx = sgc.disco_bwd(h, g.to(DEV))
+    torch.cuda.synchronize()
+    assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL["bf16"]
