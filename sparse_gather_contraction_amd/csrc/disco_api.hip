@@ -348,6 +348,8 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         prm.ch = ch;
         prm.piece_budget = budget;
         prm.xch_bytes = disco::fused_mfma_exchange_bytes();
+        const char *pcp = getenv("DISCO_PSI_COPIES");  // tuning knob: psi copies for odd strides (1, 2 or 3)
+        if (pcp && (pcp[0] == '1' || pcp[0] == '2' || pcp[0] == '3') && pcp[1] == 0) prm.psi_copies = pcp[0] - '0';
         disco::build_phase_plan(v, prm, fup);
         disco::PhasePlanParams fprm;
         fprm.kr = csr->K <= 8 ? 8 : 16;
@@ -361,6 +363,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         disco::PhasePlanParams bprm = fprm;
         bprm.kr = kBwdMfmaRows;
         bprm.ch = disco::fwd_mfma_channels(bprm.kr);
+        bprm.psi_copies = prm.psi_copies;
         disco::build_phase_plan(inv.view, bprm, bwp);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the fused plan");

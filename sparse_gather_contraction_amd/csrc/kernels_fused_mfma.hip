@@ -193,29 +193,35 @@ __device__ __forceinline__ void stage_w(const Ctx &c, int c0, unsigned char *wb)
 // Operands of one block: five 4-byte words of psi (pairs of consecutive offsets of one basis
 // function; realigned at the point of use, so that the wait for them falls just before the
 // MFMA) and the two channels' x runs.
+template <bool PERM>
 struct Ops {
-    unsigned a[5];
+    unsigned a[PERM ? 5 : 4];
     bf16x8 b0, b1;
 };
 
-// KR: basis rows of the psi layout; one offset pair of psi spans KR 4-byte words.
-template <int KR>
-__device__ __forceinline__ void load_ops(Ops &o, const unsigned char *a_base, const unsigned char *x_base, int wel2,
-                                         int a_off, int x_off)
+// KR: basis rows of the psi layout; one offset pair of psi spans KR 4-byte words.  Without PERM the
+// lane's eight psi values are four aligned words (lanes whose phase shift is odd read the piece's
+// second psi copy, whose words hold the offset pairs that start one offset later, and with s even
+// no shift is odd); with PERM the piece holds one copy and an odd shift reads five words and
+// realigns them.
+template <int KR, bool PERM>
+__device__ __forceinline__ void load_ops(Ops<PERM> &o, const unsigned char *a_base, const unsigned char *x_base,
+                                         int wel2, int a_off, int x_off)
 {
     o.b0 = *reinterpret_cast<const bf16x8 *>(x_base + x_off);
     o.b1 = *reinterpret_cast<const bf16x8 *>(x_base + wel2 + x_off);
     const unsigned *p = reinterpret_cast<const unsigned *>(a_base + a_off);
 #pragma unroll
-    for (int i = 0; i < 5; ++i) o.a[i] = p[KR * i];
+    for (int i = 0; i < (PERM ? 5 : 4); ++i) o.a[i] = p[KR * i];
 }
 
-// sel: 0x03020100 (even first offset: words as read) or 0x05040302 (odd: shifted by one offset)
-__device__ __forceinline__ void mfma_ops(const Ops &o, unsigned sel, f32x16 (&d)[2])
+// sel (PERM only): 0x03020100 (even first offset: words as read) or 0x05040302 (odd: shifted by one)
+template <bool PERM>
+__device__ __forceinline__ void mfma_ops(const Ops<PERM> &o, unsigned sel, f32x16 (&d)[2])
 {
     unsigned w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(o.a[i + 1], o.a[i], sel);
+    for (int i = 0; i < 4; ++i) w[i] = PERM ? __builtin_amdgcn_perm(o.a[i + 1], o.a[i], sel) : o.a[i];
     const bf16x8 a = __builtin_bit_cast(bf16x8, w);
     d[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b0, d[0], 0, 0, 0);
     d[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b1, d[1], 0, 0, 0);
@@ -225,21 +231,16 @@ __device__ __forceinline__ void mfma_ops(const Ops &o, unsigned sel, f32x16 (&d)
 // of one block are read while the other block's MFMAs run, and the descriptors of a pair are
 // read two pairs ahead.  Scheduling barriers keep that order (the compiler would otherwise
 // move the reads next to their uses).
-template <int KR>
-__device__ __forceinline__ void contract(const unsigned char *__restrict__ stage, const unsigned char *__restrict__ win,
-                                         const FPiece &pc, int a_lane2, int x_lane2, unsigned sel, int ch0,
-                                         f32x16 (&d)[2])
+template <int KR, bool PERM>
+__device__ __forceinline__ void contract_pairs(const unsigned char *__restrict__ stage, const unsigned char *a_base,
+                                               const unsigned char *x_base, int wel2, int npair, unsigned sel,
+                                               f32x16 (&d)[2])
 {
-    const int npair = pc.nblk >> 1;
-    if (npair <= 0) return;
     const int4 *desc = reinterpret_cast<const int4 *>(stage);
-    const unsigned char *a_base = stage + 4 * pc.desc_words + a_lane2;
-    const int wel2 = 2 * pc.win_elems;
-    const unsigned char *x_base = win + ch0 * wel2 + x_lane2;
     const int lastp = npair - 1;
     int4 dA = desc[0];
     int4 dB = desc[min(1, lastp)];
-    Ops P, Q;
+    Ops<PERM> P, Q;
     load_ops<KR>(P, a_base, x_base, wel2, dA.x, dA.y);
     for (int j = 0; j < npair; ++j) {
         const int4 dC = desc[min(j + 2, lastp)];
@@ -254,6 +255,23 @@ __device__ __forceinline__ void contract(const unsigned char *__restrict__ stage
         dA = dB;
         dB = dC;
     }
+}
+
+// odd: the lane's phase shift is odd (second psi copy, or the realigning selector)
+template <int KR>
+__device__ __forceinline__ void contract(const unsigned char *__restrict__ stage, const unsigned char *__restrict__ win,
+                                         const FPiece &pc, int a_lane2, int x_lane2, bool odd, int ch0,
+                                         f32x16 (&d)[2])
+{
+    const int npair = pc.nblk >> 1;
+    if (npair <= 0) return;
+    const unsigned char *a_base = stage + 4 * pc.desc_words + a_lane2;
+    const int wel2 = 2 * pc.win_elems;
+    const unsigned char *x_base = win + ch0 * wel2 + x_lane2;
+    if (pc.realign)
+        contract_pairs<KR, true>(stage, a_base, x_base, wel2, npair, odd ? 0x05040302u : 0x03020100u, d);
+    else
+        contract_pairs<KR, false>(stage, a_base + (odd ? pc.a_copy_bytes : 0), x_base, wel2, npair, 0u, d);
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &v, int base)
@@ -317,7 +335,7 @@ template <int NOTH>
 __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int nsteps, int st, int t, int p, unsigned char *__restrict__ cur,
                                          unsigned char *__restrict__ nxt, unsigned char *__restrict__ wb, int a_lane2,
-                                         int x_lane2, unsigned sel, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
+                                         int x_lane2, bool odd, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
 {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` (and W) have landed
     __syncthreads();                // everyone's have; the previous step is done with `nxt` and W
@@ -329,7 +347,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     }
     if (p == 0) zero(d);
     const FPiece pc = pieces[p_begin + p];
-    contract<16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, sel, 2 * h2, d);
+    contract<16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * h2, d);
     if (p + 1 == npieces) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
@@ -343,7 +361,7 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
                                                    const unsigned char *__restrict__ stage,
                                                    unsigned char *__restrict__ cur, unsigned char *__restrict__ nxt,
                                                    unsigned char *__restrict__ wb, int a_lane2, int x_lane2,
-                                                   unsigned sel, int pp, int h2, f32x16 (&d)[2],
+                                                   bool odd, int pp, int h2, f32x16 (&d)[2],
                                                    f32x16 (&yacc)[2][NOTH])
 {
     __builtin_amdgcn_s_waitcnt(0);
@@ -351,7 +369,7 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
     if (t > 0) stage_w(c, kCh * t, wb);
     if (t + 1 < nchunks) stage_windows<kCh>(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
     zero(d);
-    contract<16>(stage, cur, pc, a_lane2, x_lane2, sel, 2 * h2, d);
+    contract<16>(stage, cur, pc, a_lane2, x_lane2, odd, 2 * h2, d);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // W slice visible; `cur` free for the exchange
     einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
@@ -400,11 +418,11 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const int r = c.lane & 31, hh = c.lane >> 5;
     const int m = r & 15;
     const int kb = (m < 8) ? 8 * (m >> 2) + (m & 3) : 8 * ((m - 8) >> 2) + 4 + (m & 3);
-    // psi words: offset pair (base + 8 hh - s q) / 2 rounded down, basis kb; an odd shift reads one
-    // offset early and realigns
+    // psi words: offset pair (base + 8 hh - s q) / 2 rounded down, basis kb; an odd shift reads the
+    // second copy, whose pair m starts at offset 2 m + 1
     const int q = 2 * pp + (r >> 4), sq = s * q;
     const int a_lane2 = 64 * (4 * hh - (sq + 1) / 2) + 4 * kb;  // bytes
-    const unsigned sel = (sq & 1) ? 0x05040302u : 0x03020100u;
+    const bool odd = (sq & 1) != 0;  // reads the second psi copy
     const int x_lane2 = 2 * (8 * s * r + 8 * hh);                // bytes
 
     f32x16 yacc[2][NOTH];
@@ -433,9 +451,9 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_psi(c, pc0, stage);
         stage_windows<kCh>(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
         for (int t = 0; t < nchunks; t += 2) {
-            run_chunk_resident<NOTH>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, sel, pp, h2, d, yacc);
+            run_chunk_resident<NOTH>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d, yacc);
             if (t + 1 < nchunks)
-                run_chunk_resident<NOTH>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, sel, pp, h2, d,
+                run_chunk_resident<NOTH>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
                                          yacc);
         }
     } else if (nsteps > 0) {
@@ -443,11 +461,11 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_step<kCh>(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
         for (int st = 0; st < nsteps; st += 2) {
-            run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, sel, pp, h2, d,
+            run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
                            yacc);
             if (++p == npieces) { p = 0; ++t; }
             if (st + 1 < nsteps) {
-                run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, sel, pp,
+                run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
                                h2, d, yacc);
                 if (++p == npieces) { p = 0; ++t; }
             }
@@ -484,14 +502,14 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 template <int KR, int FCH>
 __device__ __forceinline__ void fwd_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int p, int c0, unsigned char *__restrict__ cur,
-                                         unsigned char *__restrict__ nxt, int a_lane2, int x_lane2, unsigned sel,
+                                         unsigned char *__restrict__ nxt, int a_lane2, int x_lane2, bool odd,
                                          int cp, f32x16 (&d)[2])
 {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` have landed
     __syncthreads();                // everyone's have; the previous step is done with `nxt`
     if (p + 1 < npieces) stage_step<FCH>(c, pieces[p_begin + p + 1], c0, nxt);
     const FPiece pc = pieces[p_begin + p];
-    contract<KR>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, sel, 2 * cp, d);
+    contract<KR>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * cp, d);
 }
 
 template <int KR>
@@ -534,7 +552,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int r = c.lane & 31, hh = c.lane >> 5;
     const int q = PH * g + r / KR, sq = s * q;
     const int a_lane2 = 4 * KR * (4 * hh - (sq + 1) / 2) + 4 * (r % KR);  // bytes
-    const unsigned sel = (sq & 1) ? 0x05040302u : 0x03020100u;
+    const bool odd = (sq & 1) != 0;  // reads the second psi copy
     const int x_lane2 = 2 * (8 * s * r + 8 * hh);                        // bytes
 
     f32x16 d[2];
@@ -545,9 +563,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (npieces > 0) {
         stage_step<FCH>(c, pieces[p_begin], c0, buf0);
         for (int p = 0; p < npieces; p += 2) {
-            fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p, c0, buf0, buf1, a_lane2, x_lane2, sel, cp, d);
+            fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p, c0, buf0, buf1, a_lane2, x_lane2, odd, cp, d);
             if (p + 1 < npieces)
-                fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p + 1, c0, buf1, buf0, a_lane2, x_lane2, sel, cp, d);
+                fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p + 1, c0, buf1, buf0, a_lane2, x_lane2, odd, cp, d);
         }
     }
 

@@ -41,12 +41,26 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
     out.ho_piece.push_back(0);
     std::vector<int64_t> work(c.Ho, 0);
     const int32_t smax = 7 * s;                            // largest phase shift of psi
-    auto ra_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 8 * s + 18; };   // psi e-rows (even)
+    // psi e-rows of a sub-row (even): a lane reads four words (two copies) or five (one copy, the
+    // fifth realigns an odd shift) from pair (base + 8 hh - s q) / 2
+    int32_t tail = 16;
+    auto ra_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 8 * s + tail; };
     auto len_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 256 * s + 8; };  // window positions
     auto cost_of = [&](int64_t nblk, int64_t a_elems, int64_t win) {
         return fused_piece_bytes(2 * nblk, a_elems, ch, win);
     };
-    const int32_t ra_pad = 8 * s + 18;
+    // resident layout of a whole latitude (rows uncut): descriptors, psi and two window buffers
+    auto resident_bytes = [&](const std::vector<SubRow> &whole, int32_t copies) {
+        int64_t nb = 0, ae = 0, we = 0;
+        for (const SubRow &sb : whole) {
+            nb += (int64_t)sb.t0.size();
+            ae += (int64_t)copies * kr * ra_of(sb);
+            we += len_of(sb);
+        }
+        if (nb & 1) { ++nb; ae += (int64_t)copies * kr * (8 * s + tail); }
+        const int64_t wbuf = std::max<int64_t>(2 * (int64_t)ch * we, prm.xch_bytes);
+        return 4 * 2 * nb + 2 * ae + 2 * wbuf;
+    };
 
     for (int32_t ho = 0; ho < c.Ho; ++ho) {
         // dense psi per input latitude: hi -> (t -> P[k]), t = signed input-column offset
@@ -61,31 +75,55 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
                 v[k] = c.val[e];
             }
         }
-        // blocks per source row (skipping blocks that see no entry at any phase), cut into
-        // sub-rows that fit a stage
-        std::vector<SubRow> subs;
+        // blocks per source row (skipping blocks that see no entry at any phase)
+        std::vector<SubRow> whole;
         for (auto &kv : rowsP) {
             const auto &m = kv.second;
             const int32_t tmin = m.begin()->first, tmax = m.rbegin()->first;
             const int32_t T0 = floor8(tmin);
-            std::vector<int32_t> kept;
+            SubRow sr;
+            sr.hi = kv.first;
             for (int32_t t0 = T0; t0 == T0 || t0 - 1 - smax < tmax; t0 += kBlkJ) {
                 auto it = m.lower_bound(t0 - smax);
-                if (it != m.end() && it->first <= t0 + kBlkJ - 1) kept.push_back(t0);
+                if (it != m.end() && it->first <= t0 + kBlkJ - 1) sr.t0.push_back(t0);
             }
-            SubRow cur;
-            cur.hi = kv.first;
-            for (int32_t t0 : kept) {
-                SubRow trial = cur;
-                trial.t0.push_back(t0);
-                if (!cur.t0.empty() &&
-                    cost_of((int64_t)trial.t0.size(), (int64_t)kr * ra_of(trial), len_of(trial)) > prm.piece_budget) {
-                    subs.push_back(cur);
-                    cur.t0.clear();
+            if (!sr.t0.empty()) whole.push_back(sr);
+        }
+        // psi copies: odd phase shifts (s odd) read a second copy whose offset pairs start one offset
+        // later, or realign five words of the one copy.  Resident when the whole latitude (rows uncut)
+        // keeps its descriptors and psi in LDS next to two window buffers; otherwise rows are cut into
+        // sub-rows that fit a streamed stage.
+        int32_t copies = 1;
+        bool resident = false;
+        const int64_t res_budget = 2 * (int64_t)prm.piece_budget;
+        if ((s & 1) && prm.psi_copies == 2) {
+            copies = 2;
+        } else if ((s & 1) && prm.psi_copies == 3 && prm.allow_resident && !whole.empty()) {
+            tail = 16;
+            if (resident_bytes(whole, 2) <= res_budget) copies = 2;
+        }
+        const bool realign = (s & 1) && copies == 1;
+        tail = realign ? 18 : 16;
+        if (prm.allow_resident && !whole.empty()) resident = resident_bytes(whole, copies) <= res_budget;
+        std::vector<SubRow> subs;
+        if (resident) {
+            subs = whole;
+        } else {
+            for (const SubRow &sr : whole) {
+                SubRow cur;
+                cur.hi = sr.hi;
+                for (int32_t t0 : sr.t0) {
+                    SubRow trial = cur;
+                    trial.t0.push_back(t0);
+                    if (!cur.t0.empty() && cost_of((int64_t)trial.t0.size(), (int64_t)copies * kr * ra_of(trial),
+                                                   len_of(trial)) > prm.piece_budget) {
+                        subs.push_back(cur);
+                        cur.t0.clear();
+                    }
+                    cur.t0.push_back(t0);
                 }
-                cur.t0.push_back(t0);
+                if (!cur.t0.empty()) subs.push_back(cur);
             }
-            if (!cur.t0.empty()) subs.push_back(cur);
         }
         // group sub-rows into pieces
         size_t q = 0;
@@ -94,9 +132,10 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
             int64_t nb = 0, ae = 0, we = 0;
             while (q1 < subs.size()) {
                 const int64_t nb2 = nb + (int64_t)subs[q1].t0.size();
-                const int64_t ae2 = ae + (int64_t)kr * ra_of(subs[q1]);
+                const int64_t ae2 = ae + (int64_t)copies * kr * ra_of(subs[q1]);
                 const int64_t we2 = we + len_of(subs[q1]);
-                if (q1 > q && cost_of(nb2 + 1, ae2 + (int64_t)kr * ra_pad, we2) > prm.piece_budget) break;
+                if (!resident && q1 > q && cost_of(nb2 + 1, ae2 + (int64_t)copies * kr * (8 * s + tail), we2) > prm.piece_budget)
+                    break;
                 nb = nb2; ae = ae2; we = we2;
                 ++q1;
             }
@@ -106,10 +145,22 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
             pc.nblk = (int32_t)(nb + (pad ? 1 : 0));
             pc.desc_words = 2 * pc.nblk;
             pc.a_begin = (int32_t)out.adata.size();
-            pc.a_elems = (int32_t)(ae + (pad ? kr * ra_pad : 0));
+            pc.a_elems = (int32_t)(ae + (pad ? copies * kr * (8 * s + tail) : 0));
             pc.row_begin = (int32_t)out.rows.size();
             pc.win_elems = (int32_t)we;
             int32_t a_row_e = 0, win_off = 0;
+            std::vector<uint16_t> copy1;  // second psi copy of the piece (s odd)
+            auto put_pairs = [&](std::vector<uint16_t> &dst, const std::map<int32_t, std::vector<float>> &m,
+                                 int32_t e_base, int32_t ra, int32_t shift) {
+                // [e pair][k][2]: word m holds offsets e_base + shift + 2m and + 1 (relative to first - 8 s)
+                for (int32_t e2 = 0; e2 < ra; e2 += 2) {
+                    auto it0 = m.find(e_base + shift + e2), it1 = m.find(e_base + shift + e2 + 1);
+                    for (int32_t k = 0; k < kr; ++k) {
+                        dst.push_back((it0 != m.end() && k < c.K) ? bf16_rne(it0->second[k]) : (uint16_t)0);
+                        dst.push_back((it1 != m.end() && k < c.K) ? bf16_rne(it1->second[k]) : (uint16_t)0);
+                    }
+                }
+            };
             for (size_t j = q; j < q1; ++j) {
                 const SubRow &sb = subs[j];
                 const int32_t first = sb.first(), ra = ra_of(sb);
@@ -124,28 +175,26 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
                     out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));
                     out.descs.push_back(2 * (win_off + (t0 - first)));
                 }
-                // [e pair][k][2]: psi at offset first - 8 s + e, basis k, at (e / 2) * 2 kr + 2 k + e % 2
-                for (int32_t e2 = 0; e2 < ra; e2 += 2) {
-                    auto it0 = m.find(first - 8 * s + e2), it1 = m.find(first - 8 * s + e2 + 1);
-                    for (int32_t k = 0; k < kr; ++k) {
-                        out.adata.push_back((it0 != m.end() && k < c.K) ? bf16_rne(it0->second[k]) : (uint16_t)0);
-                        out.adata.push_back((it1 != m.end() && k < c.K) ? bf16_rne(it1->second[k]) : (uint16_t)0);
-                    }
-                }
+                put_pairs(out.adata, m, first - 8 * s, ra, 0);
+                if (copies == 2) put_pairs(copy1, m, first - 8 * s, ra, 1);
                 a_row_e += ra;
                 win_off += fr.len;
             }
             if (pad) {  // zero psi rows; the window offset reads the piece's first window
                 out.descs.push_back(2 * kr * (a_row_e + 8 * s));
                 out.descs.push_back(0);
-                out.adata.insert(out.adata.end(), (size_t)kr * ra_pad, (uint16_t)0);
+                out.adata.insert(out.adata.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
+                if (copies == 2) copy1.insert(copy1.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
             }
+            out.adata.insert(out.adata.end(), copy1.begin(), copy1.end());
             pc.row_end = (int32_t)out.rows.size();
             pc.resident = 0;
-            pc.pad[0] = pc.pad[1] = pc.pad[2] = 0;
+            pc.a_copy_bytes = copies == 2 ? pc.a_elems : 0;  // byte offset of the second copy = half the psi bytes
+            pc.realign = realign ? 1 : 0;
+            pc.pad = 0;
             const int64_t stage_bytes = 4 * (int64_t)pc.desc_words + 2 * (int64_t)pc.a_elems;
             const int64_t wbuf = std::max<int64_t>(2 * (int64_t)ch * pc.win_elems, prm.xch_bytes);
-            if (prm.allow_resident && q == 0 && q1 == subs.size() && stage_bytes + 2 * wbuf <= 2 * (int64_t)prm.piece_budget) {
+            if (resident) {
                 pc.resident = (int32_t)wbuf;
                 out.max_resident_bytes = std::max<int32_t>(out.max_resident_bytes, (int32_t)(stage_bytes + 2 * wbuf));
             } else {

@@ -18,7 +18,10 @@
 // Per input latitude the plan stores psi densely as bf16 (round to nearest
 // even) by e = t - (first block start - 8 s) and basis k, pairs of e
 // interleaved ([e/2][k][e%2], so one 4-byte word holds two consecutive
-// offsets); per block a descriptor (byte offsets of its psi rows and of its
+// offsets); when s is odd a lane whose phase shift is odd either reads a second
+// copy that holds the pairs (2m+1, 2m+2), four aligned words, or reads five words
+// of the one copy and realigns them (the plan picks per latitude, PhasePlanParams::
+// psi_copies); per block a descriptor (byte offsets of its psi rows and of its
 // window run in the piece stage); per row the window of input columns
 // s px0 + first + i, i < len = span of its blocks + 256 s + 8 (mod Wi).  Blocks
 // are contracted in pairs: a piece with an odd block count gets a zero block.
@@ -57,7 +60,9 @@ struct FPiece {
     int32_t resident;    // > 0: the latitude's only piece, whose descriptors and psi stay in LDS for all
                          // chunks while the windows are double-buffered; the value is the window buffer
                          // size in bytes (at least the operand exchange)
-    int32_t pad[3];
+    int32_t a_copy_bytes;  // > 0: byte offset of the second psi copy (pairs starting one offset later)
+    int32_t realign;       // one psi copy and odd shifts: lanes read five words and realign them
+    int32_t pad;
 };
 
 struct FusedPlan {
@@ -83,6 +88,9 @@ struct PhasePlanParams {
     int piece_budget = 0;   // LDS bytes of one piece stage
     int xch_bytes = 0;      // smallest window buffer of a resident latitude
     bool allow_resident = true;
+    // s odd: 1 = one psi copy (realigned reads), 2 = two copies, 3 = two copies where the latitude
+    // is resident with them, else one
+    int psi_copies = 3;
 };
 
 // Build the plan; a piece stage takes at most `piece_budget` bytes of LDS for
