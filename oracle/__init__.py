@@ -45,6 +45,7 @@ def _load():
         lib.oracle_fwd.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, i32]
         lib.oracle_bwd.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, i32]
         lib.oracle_fused.argtypes = [i32] * 8 + [P] * 6 + [i32, P, P, i32]
+        lib.oracle_fused_bwd.argtypes = [i32] * 8 + [P] * 7 + [P, P, i32]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -119,3 +120,23 @@ def fused(psi, x, W, ho_list=None, abs_mode: bool = False) -> np.ndarray:
                      x.ctypes.data_as(ctypes.c_void_p), W.ctypes.data_as(ctypes.c_void_p),
                      hl.size, hl_p, y.ctypes.data_as(ctypes.c_void_p), int(abs_mode))
     return y
+
+
+def fused_bwd(psi, x, W, gy, abs_mode: bool = False):
+    """(gx [B, C, Hi, Wi], dW [Co, C, K]) in fp64: the gradients of <gy, y> for the fused op."""
+    lib = _load()
+    x = _np_f32(x)
+    W = _np_f32(W)
+    gy = _np_f32(gy)
+    B, C = x.shape[:2]
+    Co = W.shape[0]
+    assert x.shape[2:] == (psi.Hi, psi.Wi) and W.shape == (Co, C, psi.K)
+    assert gy.shape == (B, Co, psi.Ho, psi.Wo)
+    gx = np.empty((B, C, psi.Hi, psi.Wi), dtype=np.float64)
+    dW = np.empty((Co, C, psi.K), dtype=np.float64)
+    keep, ptrs = _psi_args(psi)
+    lib.oracle_fused_bwd(B, C, Co, psi.K, psi.Ho, psi.Wo, psi.Hi, psi.Wi, *ptrs,
+                         x.ctypes.data_as(ctypes.c_void_p), W.ctypes.data_as(ctypes.c_void_p),
+                         gy.ctypes.data_as(ctypes.c_void_p), gx.ctypes.data_as(ctypes.c_void_p),
+                         dW.ctypes.data_as(ctypes.c_void_p), int(abs_mode))
+    return gx, dW

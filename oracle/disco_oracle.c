@@ -24,9 +24,22 @@
  * operand is replaced by its absolute value, which yields the normaliser
  * sum |val * x| used to scale the parity error.
  *
- * Parity status: fwd, bwd and fused are each pinned by independent checks in
- * the CPU test suite (dense brute force, constant field, equivariance, adjoint,
- * FFT correlation, strided-subsample matmul, hand-worked fixture).
+ * fused_bwd: the gradients of <gy, y> for the fused convolution, the backward
+ * the page pairs with its fused forward (same page, sections "Python dispatch
+ * layer" and "Backward direction — gather vs scatter": the fused autograd
+ * function runs the fused forward and the CSR transpose contraction backward;
+ * section "Test coverage requirements": fused and unfused must agree in output
+ * and gradient).  With the chain rule through y = einsum(W, F x):
+ *
+ *   g[b,c,k,ho,wo]  = sum_o W[o,c,k] * gy[b,o,ho,wo]
+ *   gx[b,c]         = F^T g[b,c]                        (scatter form, as bwd)
+ *   dW[o,c,k]       = sum_{b,ho,wo} gy[b,o,ho,wo] * out[b,c,k,ho,wo],  out = F x
+ *
+ * Parity status: fwd, bwd, fused and fused_bwd are each pinned by independent
+ * checks in the CPU test suite (dense brute force, constant field,
+ * equivariance, adjoint, FFT correlation, strided-subsample matmul, hand-worked
+ * fixture; for fused_bwd: directional derivatives of the fused oracle and the
+ * adjoint identities <gy, y> = <x, gx> = <W, dW>).
  */
 #include <math.h>
 #include <stdint.h>
@@ -140,6 +153,83 @@ void oracle_fused(int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
             }
         }
     }
+    free(t);
+}
+
+/* Backward of the fused convolution over all output latitudes.
+ * x: [B, C, Hi, Wi], W: [Co, C, K], gy: [B, Co, Ho, Wo] fp32;
+ * gx: [B, C, Hi, Wi] and dW: [Co, C, K] double (overwritten).
+ * abs_mode = 1 gives the normalisers (every operand by its absolute value). */
+void oracle_fused_bwd(int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
+                      const int64_t *row_ptr, const int32_t *col_hi, const int32_t *col_wi,
+                      const float *val, const float *x, const float *W, const float *gy,
+                      double *gx, double *dW, int abs_mode)
+{
+    const int s = Wi / Wo;
+    const int64_t HWo = (int64_t)Ho * Wo;
+    double *g = (double *)malloc(sizeof(double) * (size_t)K * HWo);
+    double *t = (double *)malloc(sizeof(double) * (size_t)K * HWo);
+    if (!g || !t) abort();
+    for (int64_t i = 0; i < (int64_t)Co * C * K; ++i) dW[i] = 0.0;
+    for (int b = 0; b < B; ++b) {
+        for (int c = 0; c < C; ++c) {
+            /* g[k, ho, wo] = sum_o W[o,c,k] gy[b,o,ho,wo] */
+            for (int64_t i = 0; i < (int64_t)K * HWo; ++i) g[i] = 0.0;
+            for (int o = 0; o < Co; ++o) {
+                const float *gyo = gy + ((int64_t)b * Co + o) * HWo;
+                for (int k = 0; k < K; ++k) {
+                    const double wv = opnd((double)W[((int64_t)o * C + c) * K + k], abs_mode);
+                    double *gk = g + (int64_t)k * HWo;
+                    for (int64_t i = 0; i < HWo; ++i) gk[i] += wv * opnd((double)gyo[i], abs_mode);
+                }
+            }
+            /* gx[b, c] = F^T g (scatter) */
+            double *gxp = gx + ((int64_t)b * C + c) * (int64_t)Hi * Wi;
+            for (int64_t i = 0; i < (int64_t)Hi * Wi; ++i) gxp[i] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                for (int ho = 0; ho < Ho; ++ho) {
+                    const int64_t r = (int64_t)k * Ho + ho;
+                    const double *gr = g + r * Wo;
+                    for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+                        const double v = opnd((double)val[e], abs_mode);
+                        double *grow = gxp + (int64_t)col_hi[e] * Wi;
+                        for (int wo = 0; wo < Wo; ++wo) {
+                            const int wi = (int)(((int64_t)col_wi[e] + (int64_t)s * wo) % Wi);
+                            grow[wi] += v * gr[wo];
+                        }
+                    }
+                }
+            }
+            /* t[k, ho, wo] = (F x)[b, c]; dW[o, c, k] += sum_{ho,wo} gy[b,o,ho,wo] t[k,ho,wo] */
+            const float *xp = x + ((int64_t)b * C + c) * (int64_t)Hi * Wi;
+            for (int k = 0; k < K; ++k) {
+                for (int ho = 0; ho < Ho; ++ho) {
+                    const int64_t r = (int64_t)k * Ho + ho;
+                    double *tr = t + r * Wo;
+                    for (int wo = 0; wo < Wo; ++wo) tr[wo] = 0.0;
+                    for (int64_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e) {
+                        const double v = opnd((double)val[e], abs_mode);
+                        const float *xrow = xp + (int64_t)col_hi[e] * Wi;
+                        for (int wo = 0; wo < Wo; ++wo) {
+                            const int wi = (int)(((int64_t)col_wi[e] + (int64_t)s * wo) % Wi);
+                            tr[wo] += v * opnd((double)xrow[wi], abs_mode);
+                        }
+                    }
+                }
+            }
+            #pragma omp parallel for schedule(dynamic, 1)
+            for (int o = 0; o < Co; ++o) {
+                const float *gyo = gy + ((int64_t)b * Co + o) * HWo;
+                for (int k = 0; k < K; ++k) {
+                    const double *tk = t + (int64_t)k * HWo;
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < HWo; ++i) acc += opnd((double)gyo[i], abs_mode) * tk[i];
+                    dW[((int64_t)o * C + c) * K + k] += acc;
+                }
+            }
+        }
+    }
+    free(g);
     free(t);
 }
 

@@ -15,7 +15,9 @@ missing term) fails at least one of them:
 * adjoint identity <F x, g> = <x, F^T g> (pins the backward against the forward);
 * same-latitude psi -> numpy FFT circular cross-correlation, subsampled by s;
 * one-entry identity psi -> strided subsample, and fused -> numpy matmul;
-* linearity in x and in the values.
+* linearity in x and in the values;
+* fused backward: unit directional derivatives of the fused oracle, the dense
+  basis, and <gy, y> = <x, gx> = <W, dW>.
 """
 import json
 import math
@@ -204,3 +206,66 @@ def test_fused_matches_einsum_of_forward():
     np.testing.assert_allclose(oracle.fused(psi, x, W), ref, rtol=1e-13, atol=1e-13)
     # ho subset
     np.testing.assert_allclose(oracle.fused(psi, x, W, ho_list=[3, 1]), ref[:, :, [3, 1]], rtol=1e-13, atol=1e-13)
+
+
+# ---- backward of the fused convolution -------------------------------------------------------
+# y = einsum(W, F x) is linear in x and in W, so <gy, y> has gradients
+# gx = F^T (W^T gy) and dW = sum gy * (F x); each is fixed by evaluating the (separately pinned)
+# fused oracle along unit directions, by the dense basis, and by the adjoint identities.
+
+def test_fused_bwd_unit_directions():
+    psi = random_psi(3, 4, 6, 5, 12, 0.25, seed=17, empty_rows=(1,))
+    B, C, Co = 2, 3, 4
+    x = randn((B, C, 5, 12), 41).numpy()
+    W = randn((Co, C, 3), 42).numpy()
+    gy = randn((B, Co, 4, 6), 43).numpy()
+    gx, dW = oracle.fused_bwd(psi, x, W, gy)
+    g64 = gy.astype(np.float64)
+    ref_gx = np.zeros_like(gx)
+    for b in range(B):
+        for c in range(C):
+            for hi in range(5):
+                for wi in range(12):
+                    e = np.zeros_like(x)
+                    e[b, c, hi, wi] = 1.0
+                    ref_gx[b, c, hi, wi] = np.sum(oracle.fused(psi, e, W) * g64)
+    ref_dW = np.zeros_like(dW)
+    for o in range(Co):
+        for c in range(C):
+            for k in range(3):
+                e = np.zeros_like(W)
+                e[o, c, k] = 1.0
+                ref_dW[o, c, k] = np.sum(oracle.fused(psi, x, e) * g64)
+    np.testing.assert_allclose(gx, ref_gx, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dW, ref_dW, rtol=1e-12, atol=1e-12)
+
+
+def test_fused_bwd_dense_brute_force():
+    Hi, Wi, Ho, Wo, tc, n_r, n_a = 9, 16, 9, 8, 0.9, 2, 4
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
+    D = _dense_operator(Hi, Wi, Ho, Wo, tc, n_r, n_a)
+    x = randn((2, 3, Hi, Wi), 44).numpy().astype(np.float64)
+    W = randn((5, 3, psi.K), 45).numpy().astype(np.float64)
+    gy = randn((2, 5, Ho, Wo), 46).numpy().astype(np.float64)
+    g = np.einsum("ock,bohw->bckhw", W, gy)
+    ref_gx = np.einsum("kowhv,bckow->bchv", D, g)
+    ref_dW = np.einsum("bohw,bckhw->ock", gy, np.einsum("kowhv,bchv->bckow", D, x))
+    gx, dW = oracle.fused_bwd(psi, x, W, gy)
+    assert np.abs(gx - ref_gx).max() <= 1e-12 * max(1.0, np.abs(ref_gx).max())
+    assert np.abs(dW - ref_dW).max() <= 1e-12 * max(1.0, np.abs(ref_dW).max())
+
+
+@pytest.mark.parametrize("name", ["tiny_fwd_f32_16x32", "fwdbwd_f32_181x360"])
+def test_fused_bwd_adjoint_identities(name):
+    psi = workload_psi(WORKLOADS[name])
+    B, C, Co = 1, 3, 5
+    x = randn((B, C, psi.Hi, psi.Wi), 47).numpy()
+    W = randn((Co, C, psi.K), 48).numpy()
+    gy = randn((B, Co, psi.Ho, psi.Wo), 49).numpy()
+    lhs = float(np.sum(oracle.fused(psi, x, W) * gy))
+    gx, dW = oracle.fused_bwd(psi, x, W, gy)
+    scale = float(np.sum(oracle.fused(psi, np.abs(x), np.abs(W), abs_mode=True) * np.abs(gy)))
+    assert abs(lhs - float(np.sum(x.astype(np.float64) * gx))) <= 1e-13 * scale
+    assert abs(lhs - float(np.sum(W.astype(np.float64) * dW))) <= 1e-13 * scale
+    ngx, ndW = oracle.fused_bwd(psi, x, W, gy, abs_mode=True)
+    assert np.all(ngx >= np.abs(gx)) and np.all(ndW >= np.abs(dW))
