@@ -38,6 +38,7 @@
 #ifndef DISCO_H
 #define DISCO_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -111,6 +112,24 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
  * (contraction chunks are rounded to bf16 before the MFMA).  BF16 only. */
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
+
+/* Backward of the fused convolution: the gradients of <gy, y> for y = disco_fused_conv(x, W),
+ *   gx[b,c]   = F^T g[b,c],  g[b,c,k,ho,wo] = sum_o W[o,c,k] * gy[b,o,ho,wo]
+ *   dW[o,c,k] = sum_{b,ho,wo} gy[b,o,ho,wo] * out[b,c,k,ho,wo],  out = F x
+ * (torch-harmonics "disco-kernel-dev" page, "Python dispatch layer": the fused autograd function
+ * pairs the fused forward with the CSR transpose backward; "Test coverage requirements": fused
+ * and unfused agree in output and gradient).
+ * x: (B, C, Hi, Wi), W: (Co, C, K), gy: (B, Co, Ho, Wo) -> gx: (B, C, Hi, Wi), dW: (Co, C, K).
+ * BF16 only; Co and Ho*Wo must be multiples of 8 and K <= 256.  Computed in channel chunks of
+ * g (bf16, on the matrix cores), the transpose contraction, the forward contraction (bf16) and
+ * a split product for dW whose fp32 partials are summed in a fixed order: results are bitwise
+ * reproducible run to run.  `workspace` is caller-owned device memory (256-byte aligned) of at
+ * least the size disco_fused_conv_bwd_workspace reports for (B, C, Co); its contents on entry
+ * are ignored and on return are unspecified.  Calls sharing one workspace must not overlap. */
+disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, int64_t Co, size_t *bytes);
+disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disco_tensor *W, const disco_tensor *gy,
+                                  disco_tensor *gx, disco_tensor *dW, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char *disco_last_error(void);

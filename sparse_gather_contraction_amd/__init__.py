@@ -35,7 +35,8 @@ STATUS_NAMES = {
 }
 DISCO_F32 = 0
 DISCO_BF16 = 1
-EXPORTED = ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv", "disco_last_error")
+EXPORTED = ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
+            "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd", "disco_last_error")
 
 
 class DiscoError(RuntimeError):
@@ -73,8 +74,12 @@ def load_library():
         lib.disco_bwd.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(TensorDesc), P]
         lib.disco_fused_conv.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(TensorDesc),
                                          ctypes.POINTER(TensorDesc), P]
+        lib.disco_fused_conv_bwd_workspace.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+        lib.disco_fused_conv_bwd.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 5 + [P, ctypes.c_size_t, P]
         lib.disco_last_error.restype = ctypes.c_char_p
-        for f in ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv"):
+        for f in ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
+                  "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -187,3 +192,29 @@ def disco_fused_conv(psi: Psi, x, W, y=None):
     _check(load_library().disco_fused_conv(psi.handle, ctypes.byref(xd), ctypes.byref(wd), ctypes.byref(yd),
                                            _stream(x.device)))
     return y
+
+
+def disco_fused_conv_bwd_workspace(psi: Psi, B: int, C: int, Co: int) -> int:
+    """Workspace bytes disco_fused_conv_bwd needs for these sizes."""
+    n = ctypes.c_size_t()
+    _check(load_library().disco_fused_conv_bwd_workspace(psi.handle, int(B), int(C), int(Co), ctypes.byref(n)))
+    return int(n.value)
+
+
+def disco_fused_conv_bwd(psi: Psi, x, W, gy, gx=None, dW=None, workspace=None):
+    """(gx, dW): gradients of <gy, disco_fused_conv(x, W)>.  The workspace (a uint8 device tensor)
+    is allocated here when not given."""
+    import torch
+
+    if gx is None:
+        gx = torch.empty_like(x)
+    if dW is None:
+        dW = torch.empty_like(W)
+    need = disco_fused_conv_bwd_workspace(psi, x.shape[0], x.shape[1], W.shape[0])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    descs = [tensor_desc(t) for t in (x, W, gy, gx, dW)]
+    _check(load_library().disco_fused_conv_bwd(psi.handle, *[ctypes.byref(d) for d in descs],
+                                               ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                               _stream(x.device)))
+    return gx, dW

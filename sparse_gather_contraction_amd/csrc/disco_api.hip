@@ -304,6 +304,90 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, 
     return DISCO_OK;
 }
 
+// Forward contraction of B x C planes, src (B, C, Hi, Wi) -> dst (B, C, K, Ho, Wo), after validation.
+disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, bool bf16, int64_t B, int64_t C, hipStream_t stream)
+{
+    const int d = bf16 ? 1 : 0;
+    const char *fm = getenv("DISCO_FWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
+    if (d == 1 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
+        if (B * C * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
+        const int fch = disco::fwd_mfma_channels(h->fwdm.kr);
+        if (B * h->Ho * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
+            return fail(DISCO_ERR_SHAPE, "forward grid exceeds 2^31 blocks");
+        disco::FwdMfmaLaunch m;
+        m.x = src; m.out = dst;
+        m.pieces = h->fwdm.pieces; m.rows = h->fwdm.rows; m.descs = h->fwdm.descs; m.adata = h->fwdm.adata;
+        m.ho_piece = h->fwdm.ho_piece; m.ho_order = h->fwdm.ho_order;
+        m.B = (int32_t)B; m.C = (int32_t)C; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
+        m.s = h->Wi / h->Wo; m.kr = h->fwdm.kr; m.max_piece_bytes = h->fwdm.max_piece_bytes;
+        m.desc_bytes = h->fwdm.desc_bytes; m.adata_bytes = h->fwdm.adata_bytes;
+        m.om.plane = (int64_t)h->K * h->Ho * h->Wo; m.om.inverse = 0; m.om.rows = 0; m.om.wi = 0; m.om.s = 1;
+        hipError_t e = disco::launch_fwd_mfma(m, stream);
+        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
+        return DISCO_OK;
+    }
+    return run_gather(h->fwd, h->sfwd[d], src, dst, d == 1, B * C, (int64_t)h->Hi * h->Wi,
+                      (int64_t)h->K * h->Ho * h->Wo, stream);
+}
+
+// Transpose contraction of B x C planes, src (B, C, K, Ho, Wo) -> dst (B, C, Hi, Wi), after validation.
+disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, bool bf16, int64_t B, int64_t C, hipStream_t stream)
+{
+    const int d = bf16 ? 1 : 0;
+    const char *bm = getenv("DISCO_BWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
+    if (d == 1 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
+        if (B * C * h->Hi == 0 || h->Wi == 0) return DISCO_OK;
+        const int fch = disco::fwd_mfma_channels(h->bwdm.kr);
+        const int32_t s = h->Wi / h->Wo;
+        const int32_t groups = (h->Hi * s + kBwdMfmaRows - 1) / kBwdMfmaRows;
+        if (B * groups * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
+            return fail(DISCO_ERR_SHAPE, "backward grid exceeds 2^31 blocks");
+        disco::FwdMfmaLaunch m;
+        m.x = src; m.out = dst;
+        m.pieces = h->bwdm.pieces; m.rows = h->bwdm.rows; m.descs = h->bwdm.descs; m.adata = h->bwdm.adata;
+        m.ho_piece = h->bwdm.ho_piece; m.ho_order = h->bwdm.ho_order;
+        m.B = (int32_t)B; m.C = (int32_t)C; m.K = kBwdMfmaRows; m.Ho = groups; m.Wo = h->Wo;
+        m.Hi = h->K * h->Ho; m.Wi = h->Wo; m.s = 1; m.kr = h->bwdm.kr; m.max_piece_bytes = h->bwdm.max_piece_bytes;
+        m.desc_bytes = h->bwdm.desc_bytes; m.adata_bytes = h->bwdm.adata_bytes;
+        m.om.plane = (int64_t)h->Hi * h->Wi; m.om.inverse = 1; m.om.rows = h->Hi * s; m.om.wi = h->Wi; m.om.s = s;
+        hipError_t e = disco::launch_fwd_mfma(m, stream);
+        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
+        return DISCO_OK;
+    }
+    return run_gather(h->bwd, h->sbwd[d], src, dst, d == 1, B * C, (int64_t)h->K * h->Ho * h->Wo,
+                      (int64_t)h->Hi * h->Wi, stream);
+}
+
+// Workspace of the fused-convolution backward: W^T, gy^T of every batch, one channel chunk of
+// g = W^T gy (and afterwards of out = F x), and the fp32 partials of dW for one chunk.
+struct FusedBwdLayout {
+    int64_t N = 0;                 // positions Ho Wo
+    int32_t Cc = 0, Mc = 0;        // channels per chunk and its rows cc K
+    int32_t S = 0, kps = 0;        // position splits of dW and their length
+    size_t wt = 0, gyt = 0, gbuf = 0, part = 0, total = 0;  // byte offsets and total
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int64_t Co)
+{
+    FusedBwdLayout L;
+    const int64_t K = h->K;
+    L.N = (int64_t)h->Ho * h->Wo;
+    L.Cc = (int32_t)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(C, 1), 256 / std::max<int64_t>(K, 1)));
+    L.Mc = (int32_t)(L.Cc * K);
+    const int64_t per = std::max<int64_t>(1, (L.N + 255) / 256);  // at most 256 splits
+    L.kps = (int32_t)((per + 31) / 32 * 32);
+    L.S = (int32_t)std::max<int64_t>(1, (L.N + L.kps - 1) / L.kps);
+    size_t off = 0;
+    L.wt = off;   off = align256(off + (size_t)C * K * Co * 2);
+    L.gyt = off;  off = align256(off + (size_t)B * L.N * Co * 2);
+    L.gbuf = off; off = align256(off + (size_t)L.Mc * L.N * 2);
+    L.part = off; off = align256(off + (size_t)B * L.S * Co * L.Mc * 4);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,27 +552,7 @@ disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, vo
     if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(out, "out", 5, os, h->device)) != DISCO_OK) return st;
     if (x->dtype != out->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
-    const int d = x->dtype == DISCO_BF16 ? 1 : 0;
-    const char *fm = getenv("DISCO_FWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
-    if (d == 1 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
-        if (B * C * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
-        const int fch = disco::fwd_mfma_channels(h->fwdm.kr);
-        if (B * h->Ho * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
-            return fail(DISCO_ERR_SHAPE, "forward grid exceeds 2^31 blocks");
-        disco::FwdMfmaLaunch m;
-        m.x = x->data; m.out = out->data;
-        m.pieces = h->fwdm.pieces; m.rows = h->fwdm.rows; m.descs = h->fwdm.descs; m.adata = h->fwdm.adata;
-        m.ho_piece = h->fwdm.ho_piece; m.ho_order = h->fwdm.ho_order;
-        m.B = (int32_t)B; m.C = (int32_t)C; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
-        m.s = h->Wi / h->Wo; m.kr = h->fwdm.kr; m.max_piece_bytes = h->fwdm.max_piece_bytes;
-        m.desc_bytes = h->fwdm.desc_bytes; m.adata_bytes = h->fwdm.adata_bytes;
-        m.om.plane = (int64_t)h->K * h->Ho * h->Wo; m.om.inverse = 0; m.om.rows = 0; m.om.wi = 0; m.om.s = 1;
-        hipError_t e = disco::launch_fwd_mfma(m, (hipStream_t)stream);
-        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
-        return DISCO_OK;
-    }
-    return run_gather(h->fwd, h->sfwd[d], x->data, out->data, d == 1, B * C, (int64_t)h->Hi * h->Wi,
-                      (int64_t)h->K * h->Ho * h->Wo, (hipStream_t)stream);
+    return enqueue_fwd(h, x->data, out->data, x->dtype == DISCO_BF16, B, C, (hipStream_t)stream);
 }
 
 disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, void *stream)
@@ -504,29 +568,7 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
     if ((st = check_tensor(gout, "gout", 5, gs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
     if (gout->dtype != gx->dtype) return fail(DISCO_ERR_DTYPE, "gout and gx dtypes differ");
-    const int d = gout->dtype == DISCO_BF16 ? 1 : 0;
-    const char *bm = getenv("DISCO_BWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
-    if (d == 1 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
-        if (B * C * h->Hi == 0 || h->Wi == 0) return DISCO_OK;
-        const int fch = disco::fwd_mfma_channels(h->bwdm.kr);
-        const int32_t s = h->Wi / h->Wo;
-        const int32_t groups = (h->Hi * s + kBwdMfmaRows - 1) / kBwdMfmaRows;
-        if (B * groups * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
-            return fail(DISCO_ERR_SHAPE, "backward grid exceeds 2^31 blocks");
-        disco::FwdMfmaLaunch m;
-        m.x = gout->data; m.out = gx->data;
-        m.pieces = h->bwdm.pieces; m.rows = h->bwdm.rows; m.descs = h->bwdm.descs; m.adata = h->bwdm.adata;
-        m.ho_piece = h->bwdm.ho_piece; m.ho_order = h->bwdm.ho_order;
-        m.B = (int32_t)B; m.C = (int32_t)C; m.K = kBwdMfmaRows; m.Ho = groups; m.Wo = h->Wo;
-        m.Hi = h->K * h->Ho; m.Wi = h->Wo; m.s = 1; m.kr = h->bwdm.kr; m.max_piece_bytes = h->bwdm.max_piece_bytes;
-        m.desc_bytes = h->bwdm.desc_bytes; m.adata_bytes = h->bwdm.adata_bytes;
-        m.om.plane = (int64_t)h->Hi * h->Wi; m.om.inverse = 1; m.om.rows = h->Hi * s; m.om.wi = h->Wi; m.om.s = s;
-        hipError_t e = disco::launch_fwd_mfma(m, (hipStream_t)stream);
-        if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
-        return DISCO_OK;
-    }
-    return run_gather(h->bwd, h->sbwd[d], gout->data, gx->data, d == 1, B * C, (int64_t)h->K * h->Ho * h->Wo,
-                      (int64_t)h->Hi * h->Wi, (hipStream_t)stream);
+    return enqueue_bwd(h, gout->data, gx->data, gout->dtype == DISCO_BF16, B, C, (hipStream_t)stream);
 }
 
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
@@ -581,6 +623,96 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     a.in_stride = h->fwd.in_stride;
     hipError_t e = disco::launch_fused(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));
+    return DISCO_OK;
+}
+
+
+disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, int64_t Co, size_t *bytes)
+{
+    disco_status st = check_handle(h);
+    if (st != DISCO_OK) return st;
+    if (!bytes) return fail(DISCO_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    if (B < 0 || C < 0 || Co < 0) return fail(DISCO_ERR_SHAPE, "negative batch or channel count");
+    *bytes = fused_bwd_layout(h, B, C, Co).total;
+    return DISCO_OK;
+}
+
+disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disco_tensor *W, const disco_tensor *gy,
+                                  disco_tensor *gx, disco_tensor *dW, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    disco_status st = check_handle(h);
+    if (st != DISCO_OK) return st;
+    if (!x || !W || !gy || !gx || !dW) return fail(DISCO_ERR_INVALID_ARGUMENT, "x, W, gy, gx or dW is NULL");
+    if (x->ndim != 4) return fail(DISCO_ERR_SHAPE, "x must be (B, C, Hi, Wi)");
+    if (W->ndim != 3) return fail(DISCO_ERR_SHAPE, "W must be (Co, C, K)");
+    const int64_t B = x->shape[0], C = x->shape[1], Co = W->shape[0];
+    if (B < 0 || C < 0 || Co < 0) return fail(DISCO_ERR_SHAPE, "negative batch or channel count");
+    const int64_t xs[4] = {B, C, h->Hi, h->Wi};
+    const int64_t ws[3] = {Co, C, h->K};
+    const int64_t ys[4] = {B, Co, h->Ho, h->Wo};
+    if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(W, "W", 3, ws, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(gy, "gy", 4, ys, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
+    if ((st = check_tensor(dW, "dW", 3, ws, h->device)) != DISCO_OK) return st;
+    if (x->dtype != W->dtype || x->dtype != gy->dtype || x->dtype != gx->dtype || x->dtype != dW->dtype)
+        return fail(DISCO_ERR_DTYPE, "x, W, gy, gx and dW dtypes differ");
+    if (x->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution backward supports bf16 only");
+    if (h->K > 256) return fail(DISCO_ERR_SHAPE, "the fused convolution backward supports K <= 256");
+    const FusedBwdLayout L = fused_bwd_layout(h, B, C, Co);
+    if (Co % 8 != 0 || L.N % 8 != 0)
+        return fail(DISCO_ERR_SHAPE, "the fused convolution backward needs Co and Ho*Wo to be multiples of 8");
+    const int64_t lim = (int64_t)1 << 31;
+    if (L.N * Co * 2 >= lim || (int64_t)L.Mc * L.N * 2 >= lim || C * h->K * Co * 2 >= lim)
+        return fail(DISCO_ERR_SHAPE, "a per-batch operand of the fused convolution backward exceeds 2 GiB");
+    if (!workspace && L.total > 0) return fail(DISCO_ERR_INVALID_ARGUMENT, "workspace is NULL");
+    if (workspace_bytes < L.total)
+        return fail(DISCO_ERR_INVALID_ARGUMENT, "workspace is smaller than disco_fused_conv_bwd_workspace reports");
+    if ((uintptr_t)workspace % 256 != 0) return fail(DISCO_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    hipStream_t sm = (hipStream_t)stream;
+    auto hipfail = [&](hipError_t e, const char *what) {
+        return fail(DISCO_ERR_HIP, std::string(what) + " launch failed: " + hipGetErrorString(e));
+    };
+    char *ws_c = (char *)workspace;
+    uint16_t *wt = (uint16_t *)(ws_c + L.wt), *gyt = (uint16_t *)(ws_c + L.gyt), *gbuf = (uint16_t *)(ws_c + L.gbuf);
+    float *part = (float *)(ws_c + L.part);
+    const uint16_t *xp = (const uint16_t *)x->data, *gyp = (const uint16_t *)gy->data;
+    uint16_t *gxp = (uint16_t *)gx->data;
+    const int64_t K = h->K, N = L.N, CK = C * K, plane_in = (int64_t)h->Hi * h->Wi;
+    hipError_t e;
+    // W^T: rows (c, k), columns o
+    if ((e = disco::launch_transpose_bf16(W->data, wt, (int)Co, (int)CK, sm)) != hipSuccess) return hipfail(e, "W transpose");
+    for (int64_t b = 0; b < B; ++b)
+        if ((e = disco::launch_transpose_bf16(gyp + b * Co * N, gyt + b * N * Co, (int)Co, (int)N, sm)) != hipSuccess)
+            return hipfail(e, "gy transpose");
+    for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
+        const int64_t cc = std::min<int64_t>(L.Cc, C - c0);
+        const int32_t Mc = (int32_t)(cc * K);
+        if (cc <= 0) break;
+        for (int64_t b = 0; b < B; ++b) {
+            // g[c k][n] = sum_o W[o, c0 + c, k] gy[b, o, n]
+            disco::GemmNtLaunch g1;
+            g1.A = wt + c0 * K * Co; g1.lda = Co; g1.M = Mc; g1.a_bytes = (uint32_t)((int64_t)Mc * Co * 2);
+            g1.B = gyt + b * N * Co; g1.ldb = Co; g1.N = (int32_t)N; g1.b_bytes = (uint32_t)(N * Co * 2);
+            g1.Kd = (int32_t)Co; g1.k_per_split = 0; g1.out_f32 = false; g1.C = gbuf; g1.ldc = N;
+            if ((e = disco::launch_gemm_nt(g1, sm)) != hipSuccess) return hipfail(e, "W^T gy product");
+            // gx[b, c0 + c] = F^T g
+            if ((st = enqueue_bwd(h, gbuf, gxp + (b * C + c0) * plane_in, true, 1, cc, sm)) != DISCO_OK) return st;
+            // out[c k][n] = (F x)[b, c0 + c]
+            if ((st = enqueue_fwd(h, xp + (b * C + c0) * plane_in, gbuf, true, 1, cc, sm)) != DISCO_OK) return st;
+            // partial dW[o][c k] over each position split
+            disco::GemmNtLaunch g2;
+            g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);
+            g2.B = gbuf; g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
+            g2.Kd = (int32_t)N; g2.k_per_split = L.kps; g2.out_f32 = true;
+            g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc;
+            if ((e = disco::launch_gemm_nt(g2, sm)) != hipSuccess) return hipfail(e, "gy out^T product");
+        }
+        if ((e = disco::launch_reduce_partials(part, (int)(B * L.S), (int)Co, Mc, dW->data, CK, (int)(c0 * K), sm)) !=
+            hipSuccess)
+            return hipfail(e, "dW reduction");
+    }
     return DISCO_OK;
 }
 

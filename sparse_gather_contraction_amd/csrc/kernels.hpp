@@ -105,4 +105,30 @@ int fwd_mfma_channels(int kr);       // channels per forward workgroup for a psi
 size_t fused_mfma_reserved_bytes();  // LDS bytes besides the two piece stage buffers
 int fused_max_k();  // largest K the fused kernel accepts
 
+// C[m][n] = sum_k A[m][k] B[n][k] on bf16 matrix cores (operands contiguous along k; k ranges and
+// Kd multiples of 8; operand buffers below 2 GiB).  out_f32: fp32 partials [split][M][N], one per
+// k range of k_per_split (a multiple of 32); else bf16 C with row stride ldc (k_per_split = 0: one
+// range).
+struct GemmNtLaunch {
+    const void *A;
+    int64_t lda;
+    int32_t M;
+    uint32_t a_bytes;
+    const void *B;
+    int64_t ldb;
+    int32_t N;
+    uint32_t b_bytes;
+    int32_t Kd, k_per_split;
+    bool out_f32;
+    void *C;
+    int64_t ldc;
+};
+hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream);
+// dst (Cn x R) = src (R x Cn)^T, bf16.
+hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream);
+// dW[o][col0 + m] = bf16(sum_{z < Z} P[z][o][m]), summed in increasing z.
+hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0,
+                                  hipStream_t stream);
+int gemm_tile();  // rows and columns of one GEMM tile
+
 }  // namespace disco

@@ -1,0 +1,216 @@
+// kernels_gemm.hip — dense bf16 products on the gfx950 matrix cores for the backward of the fused
+// convolution (the gradients of <gy, y> for y = einsum(W, F x); torch-harmonics
+// "disco-kernel-dev" page, "Python dispatch layer": the fused autograd function pairs the fused
+// forward with the CSR transpose backward).
+//
+//   g[b, c k, n]  = sum_o W[o, c k] gy[b, o, n]           (n = ho Wo + wo)
+//   dW[o, c k]    = sum_{b, n} gy[b, o, n] out[b, c k, n]  (out = F x)
+//
+// Both are "NT" products C[m][n] = sum_k A[m][k] B[n][k] whose operands are contiguous along the
+// reduction index k: g takes A = W^T (rows c k) and B = gy^T (rows n, made by a transpose
+// kernel); dW takes A = gy (rows o) and B = out (rows c k), split over the positions with one
+// fp32 partial per split, summed afterwards in a fixed order (no atomics).
+//
+// Tile: 128 x 128 outputs per workgroup of four waves (64 x 64 each, 2 x 2
+// v_mfma_f32_32x32x16_bf16 accumulators).  The reduction walks 32-wide chunks; both operand
+// chunks (128 rows x 64 bytes) stream into LDS by direct global->LDS loads, double-buffered.
+// A row's four 16-byte column groups are stored XOR-swizzled by (row / 4) % 4 so that the
+// 16-byte operand reads of 16 consecutive rows hit distinct LDS banks.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace disco {
+
+namespace {
+
+constexpr int kGT = 128;                     // tile rows (and columns)
+constexpr int kGK = 32;                      // reduction chunk (elements)
+constexpr int kGThreads = 256;
+constexpr int kGOpBytes = kGT * kGK * 2;     // one operand chunk: 8 KiB
+constexpr int kGStage = 2 * kGOpBytes;       // A + B chunk
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Lane i of the instruction writes LDS base `l` + 16 i (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *l)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)l, 16, voff, 0, 0, 0);
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer used here: the load returns zeros
+
+// One operand chunk: rows row0 .. row0+127 (valid below nrows), reduction indices k .. k+31
+// (valid below k_end; k and k_end are multiples of 8).  LDS slot u (16 bytes) holds row u / 4,
+// column group (u % 4) ^ ((row / 4) % 4).
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, int64_t ld, int row0, int nrows, int k, int k_end,
+                                           unsigned char *dst, int tid, int wave)
+{
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = i * kGThreads + tid;
+        const int row = u >> 2;
+        const int cg = (u & 3) ^ ((row >> 2) & 3);
+        const int grow = row0 + row, kk = k + 8 * cg;
+        const uint32_t voff = (grow < nrows && kk < k_end) ? (uint32_t)((grow * ld + kk) * 2) : kOob;
+        dma16(r, voff, dst + 16 * (i * kGThreads + wave * 64));
+    }
+}
+
+// 16-byte operand of MFMA row `row` (tile-local) for reduction step ks (0 or 1) and lane half h.
+__device__ __forceinline__ bf16x8 frag(const unsigned char *op, int row, int ks, int h)
+{
+    const int slot = (2 * ks + h) ^ ((row >> 2) & 3);
+    return *reinterpret_cast<const bf16x8 *>(op + row * 64 + 16 * slot);
+}
+
+// C[m][n] = sum_{k in [k_begin, k_end)} A[m][k] B[n][k]; blockIdx.z selects the k range (split).
+// OUT_F32: fp32 partial [z][M][N]; else bf16 C with row stride ldc.
+template <bool OUT_F32>
+__global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const bf16_t *__restrict__ A, int64_t lda, int M,
+                                                            uint32_t a_bytes, const bf16_t *__restrict__ Bm,
+                                                            int64_t ldb, int N, uint32_t b_bytes, int Kd,
+                                                            int k_per_split, void *__restrict__ Cout, int64_t ldc)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kGStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT, z = blockIdx.z;
+    const int k_begin = z * k_per_split;
+    const int k_end = min(Kd, k_begin + k_per_split);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes), rb = make_rsrc(Bm, b_bytes);
+
+    f32x16 d[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) d[i][j][a] = 0.0f;
+
+    const int nk = k_end > k_begin ? (k_end - k_begin + kGK - 1) / kGK : 0;
+    if (nk > 0) {
+        load_chunk(ra, lda, m0, M, k_begin, k_end, smem, tid, wave);
+        load_chunk(rb, ldb, n0, N, k_begin, k_end, smem + kGOpBytes, tid, wave);
+    }
+    const int r = lane & 31, h = lane >> 5;
+    for (int t = 0; t < nk; ++t) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // chunk t in LDS; every wave is done with chunk t - 1
+        unsigned char *cur = smem + (t & 1) * kGStage;
+        if (t + 1 < nk) {
+            unsigned char *nxt = smem + ((t + 1) & 1) * kGStage;
+            const int k = k_begin + (t + 1) * kGK;
+            load_chunk(ra, lda, m0, M, k, k_end, nxt, tid, wave);
+            load_chunk(rb, ldb, n0, N, k, k_end, nxt + kGOpBytes, tid, wave);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = frag(cur, 64 * wm + 32 * i + r, ks, h);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fb[j] = frag(cur + kGOpBytes, 64 * wn + 32 * j + r, ks, h);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    d[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], d[i][j], 0, 0, 0);
+        }
+    }
+
+    // lane (column r, half h) holds rows 8 (a / 4) + 4 h + a % 4 of each 32 x 32 accumulator
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + 64 * wn + 32 * j + r;
+            if (n >= N) continue;
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const int m = m0 + 64 * wm + 32 * i + 8 * (a >> 2) + 4 * h + (a & 3);
+                if (m >= M) continue;
+                if constexpr (OUT_F32)
+                    reinterpret_cast<float *>(Cout)[((int64_t)z * M + m) * N + n] = d[i][j][a];
+                else
+                    reinterpret_cast<bf16_t *>(Cout)[(int64_t)m * ldc + n] = f32_to_bf16(d[i][j][a]);
+            }
+        }
+}
+
+// dst[c][r] = src[r][c] for an R x Cn bf16 matrix (row strides Cn and R); 64 x 64 tiles via LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t *__restrict__ src, bf16_t *__restrict__ dst,
+                                                        int R, int Cn)
+{
+    __shared__ bf16_t t[64][66];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int rr = i >> 6, cc = i & 63;
+        const int gr = r0 + rr, gc = c0 + cc;
+        t[rr][cc] = (gr < R && gc < Cn) ? src[(int64_t)gr * Cn + gc] : (bf16_t)0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int cc = i >> 6, rr = i & 63;
+        const int gr = r0 + rr, gc = c0 + cc;
+        if (gr < R && gc < Cn) dst[(int64_t)gc * R + gr] = t[rr][cc];
+    }
+}
+
+// dW[o][col0 + m] = bf16(sum_{z < Z} P[z][o][m]) in increasing z.
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ P, int Z, int Co, int Mc,
+                                                              bf16_t *__restrict__ dW, int64_t ldw, int col0)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)Co * Mc) return;
+    const int o = (int)(i / Mc), m = (int)(i % Mc);
+    float acc = 0.0f;
+    for (int z = 0; z < Z; ++z) acc += P[((int64_t)z * Co + o) * Mc + m];
+    dW[(int64_t)o * ldw + col0 + m] = f32_to_bf16(acc);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream)
+{
+    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    const int splits = g.k_per_split > 0 ? (g.Kd + g.k_per_split - 1) / g.k_per_split : 1;
+    const int kps = g.k_per_split > 0 ? g.k_per_split : g.Kd;
+    dim3 grid((g.N + kGT - 1) / kGT, (g.M + kGT - 1) / kGT, g.out_f32 ? splits : 1);
+    if (g.out_f32)
+        hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGThreads), 0, stream, (const bf16_t *)g.A, g.lda, g.M,
+                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc);
+    else
+        hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kGThreads), 0, stream, (const bf16_t *)g.A, g.lda, g.M,
+                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream)
+{
+    if (R <= 0 || Cn <= 0) return hipSuccess;
+    dim3 grid((Cn + 63) / 64, (R + 63) / 64);
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, (const bf16_t *)src, (bf16_t *)dst, R, Cn);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0,
+                                  hipStream_t stream)
+{
+    const int64_t n = (int64_t)Co * Mc;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, P, Z, Co, Mc,
+                       (bf16_t *)dW, ldw, col0);
+    return hipGetLastError();
+}
+
+int gemm_tile() { return kGT; }
+
+}  // namespace disco

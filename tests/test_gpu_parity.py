@@ -380,3 +380,103 @@ def test_bwd_bf16_both_kernels_agree_with_oracle(geom, mfma, monkeypatch):
     gx = sgc.disco_bwd(h, g.to(DEV))
     torch.cuda.synchronize()
     assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- backward of the fused convolution
+
+def _fused_bwd_check(psi, B, C, Co, seed):
+    h = gpu_psi(psi)
+    x = randn((B, C, psi.Hi, psi.Wi), seed, "bf16")
+    W = randn((Co, C, psi.K), seed + 1, "bf16", std=1.0 / np.sqrt(C * psi.K))
+    gy = randn((B, Co, psi.Ho, psi.Wo), seed + 2, "bf16")
+    gx = nan_like((B, C, psi.Hi, psi.Wi), torch.bfloat16)
+    dW = nan_like((Co, C, psi.K), torch.bfloat16)
+    sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV), gx, dW)
+    torch.cuda.synchronize()
+    rgx, rdW = oracle.fused_bwd(psi, x, W, gy)
+    ngx, ndW = oracle.fused_bwd(psi, x, W, gy, abs_mode=True)
+    return normalised_error(gx, rgx, ngx), normalised_error(dW, rdW, ndW), (gx, dW)
+
+
+@pytest.mark.parametrize("cfg", [
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 20, 24),     # K=16, s=1: two channel chunks (16 + 4), positions not a tile multiple
+    (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 40),     # K=8, s=2: one chunk of 9 channels
+    (25, 48, 25, 48, 0.7, 4, 1, 1, 70, 8),      # K=4: chunks of 64 + 6 channels, Co = 8
+    (16, 32, 16, 32, 2 * np.pi / 16, 3, 1, 3, 5, 136),  # K=3, B=3, Co above one tile
+])
+def test_fused_bwd_small_ragged(cfg):
+    """Input and weight gradients of the fused convolution against the fp64 oracle (bf16 data)."""
+    Hi, Wi, Ho, Wo, tc, nr, na, B, C, Co = cfg
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
+    _log(f"fused bwd {cfg}")
+    egx, edW, _ = _fused_bwd_check(psi, B, C, Co, 1100 + C)
+    assert egx <= TOL["bf16"], egx
+    assert edW <= TOL["bf16"], edW
+
+
+def test_fused_bwd_deterministic_and_workspace_reuse():
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    h = gpu_psi(psi)
+    B, C, Co = 2, 18, 16
+    x = randn((B, C, 31, 64), 1200, "bf16").to(DEV)
+    W = randn((Co, C, psi.K), 1201, "bf16", std=0.05).to(DEV)
+    gy = randn((B, Co, 31, 64), 1202, "bf16").to(DEV)
+    ws = torch.full((sgc.disco_fused_conv_bwd_workspace(h, B, C, Co),), 0x7f, dtype=torch.uint8, device=DEV)
+    a = sgc.disco_fused_conv_bwd(h, x, W, gy, workspace=ws)
+    b = sgc.disco_fused_conv_bwd(h, x, W, gy, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_fused_bwd_rejects_bad_arguments():
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    h = gpu_psi(psi)
+    x = randn((1, 4, 31, 64), 1210, "bf16").to(DEV)
+    W = randn((12, 4, psi.K), 1211, "bf16").to(DEV)   # Co = 12: not a multiple of 8
+    gy = randn((1, 12, 31, 64), 1212, "bf16").to(DEV)
+    gx = nan_like((1, 4, 31, 64), torch.bfloat16)
+    dW = nan_like((12, 4, psi.K), torch.bfloat16)
+    with pytest.raises(sgc.DiscoError, match="multiples of 8"):
+        sgc.disco_fused_conv_bwd(h, x, W, gy, gx, dW)
+    W8 = randn((8, 4, psi.K), 1213, "bf16").to(DEV)
+    gy8 = randn((1, 8, 31, 64), 1214, "bf16").to(DEV)
+    dW8 = nan_like((8, 4, psi.K), torch.bfloat16)
+    small = torch.empty(256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(sgc.DiscoError, match="workspace"):
+        sgc.disco_fused_conv_bwd(h, x, W8, gy8, gx, dW8, workspace=small)
+    with pytest.raises(sgc.DiscoError, match="bf16"):
+        sgc.disco_fused_conv_bwd(h, x.float(), W8.float(), gy8.float(), gx.float(), dW8.float())
+    torch.cuda.synchronize()
+    assert torch.isnan(gx).all() and torch.isnan(dW8).all()
+
+
+def test_fused_bwd_721x1440_full_size_sampled():
+    """The 721x1440 K=16 workload (B=2, C=Co=256) as the benchmark runs it; input-gradient planes
+    and weight-gradient columns of two channels checked against the oracle's transpose and
+    forward contractions (each pinned) composed with exact fp64 products."""
+    w = WORKLOADS["fused_bf16_721x1440"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = workload_x(w)
+    W = workload_weight(w)
+    gy = randn((w.B, w.Co, psi.Ho, psi.Wo), 1300, "bf16")
+    _log("fused bwd 721x1440: GPU")
+    gx, dW = sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV))
+    torch.cuda.synchronize()
+    gx, dW = gx.cpu(), dW.cpu()
+    gy64 = gy.double().numpy().reshape(w.B, w.Co, -1)
+    W64 = W.double().numpy()
+    for c in (131,):
+        _log(f"fused bwd 721x1440: oracle channel {c}")
+        for b in range(w.B):
+            g = (W64[:, c, :].T @ gy64[b]).reshape(1, psi.K, psi.Ho, psi.Wo)
+            ga = (np.abs(W64[:, c, :]).T @ np.abs(gy64[b])).reshape(1, psi.K, psi.Ho, psi.Wo)
+            ref = oracle.bwd(psi, g.astype(np.float32))
+            nrm = oracle.bwd(psi, ga.astype(np.float32), abs_mode=True)
+            # g is rounded to fp32 for the oracle call; the bound below covers that (2^-24 relative)
+            assert normalised_error(gx[b, c][None], ref, nrm) <= TOL["bf16"]
+        out = np.stack([oracle.fwd(psi, x[b, c][None])[0].reshape(psi.K, -1) for b in range(w.B)])
+        outa = np.stack([oracle.fwd(psi, x[b, c][None].abs(), abs_mode=True)[0].reshape(psi.K, -1) for b in range(w.B)])
+        ref = sum(gy64[b] @ out[b].T for b in range(w.B))
+        nrm = sum(np.abs(gy64[b]) @ outa[b].T for b in range(w.B))
+        assert normalised_error(dW[:, c, :], ref, nrm) <= TOL["bf16"]
