@@ -53,6 +53,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="fwd,bwd,fused", help="subset of ops in the step (profiling runs)")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the separate timing of the fused-convolution backward")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -171,6 +173,10 @@ def main():
                 "unit": "TFLOP/s", "frac": dd["mfma_frac"], "traffic": traffic, "kernel": dom,
                 "note": "algorithmic flops: 2 per nnz-update + 2 per einsum MAC; dense bf16 MFMA peak"}
 
+    nxt = None
+    if not args.no_next_rows and "fused" in ops:
+        nxt = {"fused_bwd": time_fused_bwd(sgc, torch, np, h_u, tensors, wu, psi_u, dev, stream)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wf, wb, wu, psi_fb, psi_u)
@@ -194,6 +200,7 @@ def main():
         "per_op": per,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "next_rows": nxt,
     }
     print(json.dumps(line), flush=True)
 
@@ -221,6 +228,41 @@ def counter_traffic(op):
                 if rec.get("kernel") == op and rec.get("source_sha256") == digest:
                     return int(rec["read_bytes"] + rec["write_bytes"])
     return None
+
+
+def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=3):
+    """Backward of the fused convolution on the fused workload (gradient gy ~ N(0,1), bf16), timed
+    apart from the step (it is not part of `value`).  Algorithmic flops: the two dense products
+    (W^T gy and the weight gradient, 2 per MAC each) plus the transpose contraction and the
+    forward contraction it recomputes for the weight gradient (2 per nnz-update each)."""
+    from disco_inputs import randn
+
+    gy = randn((w.B, w.Co, w.Ho, w.Wo), 3100, "bf16").to(dev)
+    gx = torch.empty_like(tensors["x5"])
+    dW = torch.empty_like(tensors["W5"])
+    ws = torch.empty(sgc.disco_fused_conv_bwd_workspace(h, w.B, w.C, w.Co), dtype=torch.uint8, device=dev)
+    for _ in range(warm):
+        sgc.disco_fused_conv_bwd(h, tensors["x5"], tensors["W5"], gy, gx, dW, workspace=ws)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sgc.disco_fused_conv_bwd(h, tensors["x5"], tensors["W5"], gy, gx, dW, workspace=ws)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    macs = w.B * w.Ho * w.Wo * w.Co * w.C * w.K
+    upd = op_updates(w, psi.nnz)
+    alg = 4 * macs + 4 * upd
+    print(f"[bench] fused backward: {ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"ms": round(ms, 4), "einsum_macs_x2": 2 * macs, "nnz_updates_x2": 2 * upd, "bound": "mfma",
+            "mfma_tflops_algorithmic": round(alg / ms / 1e9, 3),
+            "mfma_frac": round(alg / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
+            "workspace_bytes": int(ws.numel()),
+            "shape": {"B": w.B, "C": w.C, "Co": w.Co, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo]}}
 
 
 def cpu_baseline(wf, wb, wu, psi_fb, psi_u):
