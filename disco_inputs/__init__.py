@@ -69,7 +69,7 @@ def workload_psi(w: Workload) -> PsiCSR:
 
 
 def randn(shape, seed: int, dtype: str = "f32", std: float = 1.0):
-    """N(0, std^2) fp32 draw from a seeded CPU torch generator, cast RNE to bf16 if asked.
+    """N(0, std^2) fp32 draw from a seeded CPU torch generator, cast RNE to bf16 or fp16 if asked.
 
     Returns a CPU torch tensor.
     """
@@ -82,6 +82,8 @@ def randn(shape, seed: int, dtype: str = "f32", std: float = 1.0):
         t.mul_(std)
     if dtype == "bf16":
         t = t.to(torch.bfloat16)
+    elif dtype == "f16":
+        t = t.to(torch.float16)
     elif dtype != "f32":
         raise ValueError(dtype)
     return t

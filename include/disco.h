@@ -20,10 +20,13 @@
  *   - Tensors are dense, contiguous, row-major, last index fastest; `data` is a
  *     device pointer on the device the psi handle was created on.  The caller
  *     owns every tensor buffer.
- *   - Supported dtypes: DISCO_F32 and DISCO_BF16.  All tensors of one call
- *     share one dtype.  Accumulation is always fp32; a bf16 output is rounded
- *     once (round-to-nearest-even) from the fp32 accumulator.  psi values are
- *     fp32 (kpacked section of the page: values stored as fp32).
+ *   - Supported dtypes: DISCO_F32, DISCO_BF16 and DISCO_F16 (the precisions
+ *     the page's test rules name, section "Test coverage requirements").  All
+ *     tensors of one call share one dtype.  Accumulation is always fp32; a
+ *     16-bit output is rounded once (round-to-nearest-even) from the fp32
+ *     accumulator.  psi values are fp32 (kpacked section of the page: values
+ *     stored as fp32), except on the bf16 matrix-core paths, which take psi
+ *     rounded to bf16 as their multiplicand.
  *   - Outputs are fully overwritten (no accumulate flag); rows with no psi
  *     entries are written as exact zeros.
  *   - `stream` is a hipStream_t (0 = the null stream).  Work is enqueued
@@ -49,7 +52,7 @@ typedef enum disco_status {
     DISCO_OK = 0,
     DISCO_ERR_INVALID_ARGUMENT = 1,   /* null handle / tensor / data pointer, wrong device */
     DISCO_ERR_SHAPE = 2,              /* Wi % Wo != 0, or shapes disagree with psi / each other */
-    DISCO_ERR_DTYPE = 3,              /* dtype not F32/BF16, or dtypes of one call differ */
+    DISCO_ERR_DTYPE = 3,              /* dtype not F32/BF16/F16, unsupported by the op, or dtypes of one call differ */
     DISCO_ERR_PSI = 4,                /* malformed CSR (row_ptr, column range, nnz >= 2^31) */
     DISCO_ERR_UNSUPPORTED_DEVICE = 5, /* device is not gfx950 */
     DISCO_ERR_OOM = 6,                /* device or host allocation failed */
@@ -58,7 +61,8 @@ typedef enum disco_status {
 
 typedef enum disco_dtype {
     DISCO_F32 = 0,
-    DISCO_BF16 = 1
+    DISCO_BF16 = 1,
+    DISCO_F16 = 2
 } disco_dtype;
 
 /* Host-side CSR filter ("psi").  Rows r = k*Ho + ho, K*Ho rows in all.
@@ -108,8 +112,9 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
 
 /* Fused convolution.  x: (B, C, Hi, Wi), W: (Co, C, K) -> y: (B, Co, Ho, Wo).
  * The contraction is computed on chip in channel chunks and never written to
- * device memory; the einsum runs on bf16 MFMA tiles with fp32 accumulation
- * (contraction chunks are rounded to bf16 before the MFMA).  BF16 only. */
+ * device memory; the einsum runs on bf16 or fp16 MFMA tiles with fp32
+ * accumulation (contraction chunks are rounded to the data type before the
+ * MFMA).  BF16 and F16. */
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
 

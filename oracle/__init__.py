@@ -57,7 +57,7 @@ def _c(a, dtype):
 
 
 def _np_f32(t):
-    """Accept numpy arrays or torch tensors (fp32 or bf16); widen exactly to fp32."""
+    """Accept numpy arrays or torch tensors (fp32, bf16 or fp16); widen exactly to fp32."""
     if hasattr(t, "detach"):
         t = t.detach().cpu().float().numpy()
     return np.ascontiguousarray(t, dtype=np.float32)

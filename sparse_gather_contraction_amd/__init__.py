@@ -35,6 +35,7 @@ STATUS_NAMES = {
 }
 DISCO_F32 = 0
 DISCO_BF16 = 1
+DISCO_F16 = 2
 EXPORTED = ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
             "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd", "disco_last_error")
 
@@ -97,6 +98,8 @@ def _dtype_code(t) -> int:
         return DISCO_F32
     if t.dtype == torch.bfloat16:
         return DISCO_BF16
+    if t.dtype == torch.float16:
+        return DISCO_F16
     return 99  # rejected by the library with DISCO_ERR_DTYPE
 
 

@@ -183,7 +183,7 @@ disco_status check_device(int device)
 disco_status check_tensor(const disco_tensor *t, const char *name, int ndim, const int64_t *shape, int device)
 {
     if (!t) return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(name) + " is NULL");
-    if (t->dtype != DISCO_F32 && t->dtype != DISCO_BF16)
+    if (t->dtype != DISCO_F32 && t->dtype != DISCO_BF16 && t->dtype != DISCO_F16)
         return fail(DISCO_ERR_DTYPE, std::string(name) + " has an unsupported dtype");
     if (t->ndim != ndim) return fail(DISCO_ERR_SHAPE, std::string(name) + " has the wrong number of dimensions");
     int64_t numel = 1;
@@ -251,11 +251,11 @@ bool staged_env_off()
 }
 
 // Launch the gather over all planes, in chunks that keep the grid below 2^31 blocks.
-disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, void *dst, bool bf16, int64_t BC,
+disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, void *dst, int dtype, int64_t BC,
                         int64_t src_plane, int64_t dst_plane, hipStream_t stream)
 {
     if (BC == 0) return DISCO_OK;
-    const size_t esz = bf16 ? 2 : 4;
+    const size_t esz = dtype == DISCO_F32 ? 4 : 2;
     if (sp.ok && !staged_env_off()) {
         const int align = 16 / (int)esz;
         const bool vec = ((uintptr_t)src % 16 == 0) && (src_plane % align == 0) && (sp.row_len % align == 0) &&
@@ -266,7 +266,7 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, 
             disco::StagedLaunch a;
             a.src = (const char *)src + b0 * src_plane * esz;
             a.dst = (char *)dst + b0 * dst_plane * esz;
-            a.bf16 = bf16;
+            a.dtype = dtype;
             a.tasks = sp.tasks; a.stages = sp.stages; a.stage_rows = sp.stage_rows; a.stage_segptr = sp.stage_segptr;
             a.segs = sp.segs; a.vals = sp.vals; a.items = sp.items;
             a.n_tasks = sp.n_tasks;
@@ -287,7 +287,7 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, 
         disco::GatherLaunch a;
         a.src = (const char *)src + b0 * src_plane * esz;
         a.dst = (char *)dst + b0 * dst_plane * esz;
-        a.bf16 = bf16;
+        a.dtype = dtype;
         a.items = p.items;
         a.order = p.order;
         a.segs = p.segs;
@@ -305,11 +305,11 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, 
 }
 
 // Forward contraction of B x C planes, src (B, C, Hi, Wi) -> dst (B, C, K, Ho, Wo), after validation.
-disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, bool bf16, int64_t B, int64_t C, hipStream_t stream)
+disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, int dtype, int64_t B, int64_t C, hipStream_t stream)
 {
-    const int d = bf16 ? 1 : 0;
+    const int d = dtype == DISCO_F32 ? 0 : 1;  // staged plan by element size
     const char *fm = getenv("DISCO_FWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
-    if (d == 1 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
+    if (dtype == DISCO_BF16 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
         if (B * C * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
         const int fch = disco::fwd_mfma_channels(h->fwdm.kr);
         if (B * h->Ho * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
@@ -326,16 +326,16 @@ disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, bool bf16, int
         if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
         return DISCO_OK;
     }
-    return run_gather(h->fwd, h->sfwd[d], src, dst, d == 1, B * C, (int64_t)h->Hi * h->Wi,
+    return run_gather(h->fwd, h->sfwd[d], src, dst, dtype, B * C, (int64_t)h->Hi * h->Wi,
                       (int64_t)h->K * h->Ho * h->Wo, stream);
 }
 
 // Transpose contraction of B x C planes, src (B, C, K, Ho, Wo) -> dst (B, C, Hi, Wi), after validation.
-disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, bool bf16, int64_t B, int64_t C, hipStream_t stream)
+disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int64_t B, int64_t C, hipStream_t stream)
 {
-    const int d = bf16 ? 1 : 0;
+    const int d = dtype == DISCO_F32 ? 0 : 1;  // staged plan by element size
     const char *bm = getenv("DISCO_BWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
-    if (d == 1 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
+    if (dtype == DISCO_BF16 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
         if (B * C * h->Hi == 0 || h->Wi == 0) return DISCO_OK;
         const int fch = disco::fwd_mfma_channels(h->bwdm.kr);
         const int32_t s = h->Wi / h->Wo;
@@ -354,7 +354,7 @@ disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, bool bf16, int
         if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
         return DISCO_OK;
     }
-    return run_gather(h->bwd, h->sbwd[d], src, dst, d == 1, B * C, (int64_t)h->K * h->Ho * h->Wo,
+    return run_gather(h->bwd, h->sbwd[d], src, dst, dtype, B * C, (int64_t)h->K * h->Ho * h->Wo,
                       (int64_t)h->Hi * h->Wi, stream);
 }
 
@@ -552,7 +552,7 @@ disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, vo
     if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(out, "out", 5, os, h->device)) != DISCO_OK) return st;
     if (x->dtype != out->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
-    return enqueue_fwd(h, x->data, out->data, x->dtype == DISCO_BF16, B, C, (hipStream_t)stream);
+    return enqueue_fwd(h, x->data, out->data, x->dtype, B, C, (hipStream_t)stream);
 }
 
 disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, void *stream)
@@ -568,7 +568,7 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
     if ((st = check_tensor(gout, "gout", 5, gs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
     if (gout->dtype != gx->dtype) return fail(DISCO_ERR_DTYPE, "gout and gx dtypes differ");
-    return enqueue_bwd(h, gout->data, gx->data, gout->dtype == DISCO_BF16, B, C, (hipStream_t)stream);
+    return enqueue_bwd(h, gout->data, gx->data, gout->dtype, B, C, (hipStream_t)stream);
 }
 
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
@@ -589,12 +589,12 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     if ((st = check_tensor(W, "W", 3, ws, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(y, "y", 4, ys, h->device)) != DISCO_OK) return st;
     if (x->dtype != W->dtype || x->dtype != y->dtype) return fail(DISCO_ERR_DTYPE, "x, W and y dtypes differ");
-    if (x->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution supports bf16 only");
+    if (x->dtype == DISCO_F32) return fail(DISCO_ERR_DTYPE, "the fused convolution supports bf16 and fp16 only");
     if (B * Co * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
     if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
         return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
     const char *fm = getenv("DISCO_FUSED_MFMA");  // test knob: "0" forces the VALU-contraction fused kernel
-    if (h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
+    if (x->dtype == DISCO_BF16 && h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
         m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs; m.adata = h->fused.adata;
@@ -613,6 +613,7 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     a.x = x->data;
     a.W = W->data;
     a.y = y->data;
+    a.f16 = x->dtype == DISCO_F16;
     a.items = h->fwd.items;
     a.block_ptr = h->fwd.block_ptr;
     a.ho_order = h->ho_order;
@@ -698,9 +699,9 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
             g1.Kd = (int32_t)Co; g1.k_per_split = 0; g1.out_f32 = false; g1.C = gbuf; g1.ldc = N;
             if ((e = disco::launch_gemm_nt(g1, sm)) != hipSuccess) return hipfail(e, "W^T gy product");
             // gx[b, c0 + c] = F^T g
-            if ((st = enqueue_bwd(h, gbuf, gxp + (b * C + c0) * plane_in, true, 1, cc, sm)) != DISCO_OK) return st;
+            if ((st = enqueue_bwd(h, gbuf, gxp + (b * C + c0) * plane_in, DISCO_BF16, 1, cc, sm)) != DISCO_OK) return st;
             // out[c k][n] = (F x)[b, c0 + c]
-            if ((st = enqueue_fwd(h, xp + (b * C + c0) * plane_in, gbuf, true, 1, cc, sm)) != DISCO_OK) return st;
+            if ((st = enqueue_fwd(h, xp + (b * C + c0) * plane_in, gbuf, DISCO_BF16, 1, cc, sm)) != DISCO_OK) return st;
             // partial dW[o][c k] over each position split
             disco::GemmNtLaunch g2;
             g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);

@@ -9,10 +9,11 @@
 
 namespace disco {
 
+// element types of the data: 0 = fp32, 1 = bf16, 2 = fp16
 struct GatherLaunch {
     const void *src;
     void *dst;
-    bool bf16;
+    int32_t dtype;
     const Item *items;     // device
     const int32_t *order;  // device, heaviest item first
     const Seg *segs;       // device
@@ -28,7 +29,7 @@ hipError_t launch_gather(const GatherLaunch &a, hipStream_t stream);
 struct StagedLaunch {
     const void *src;
     void *dst;
-    bool bf16;
+    int32_t dtype;
     const Task *tasks;            // device, heaviest first
     const Stage *stages;
     const int32_t *stage_rows;
@@ -47,9 +48,10 @@ bool staged_supported(int NI, int G, int T, int S);
 hipError_t launch_staged(const StagedLaunch &a, hipStream_t stream);
 
 struct FusedLaunch {
-    const void *x;          // (B, C, Hi, Wi) bf16
-    const void *W;          // (Co, C, K) bf16
-    void *y;                // (B, Co, Ho, Wo) bf16
+    const void *x;          // (B, C, Hi, Wi) bf16 or fp16
+    const void *W;          // (Co, C, K)
+    void *y;                // (B, Co, Ho, Wo)
+    bool f16;               // fp16 data (else bf16)
     const Item *items;      // forward plan items, grouped by ho
     const int32_t *block_ptr;  // [Ho + 1]
     const int32_t *ho_order;   // [Ho], heaviest latitude first

@@ -8,10 +8,10 @@
 // kOBlk output channels.  It walks the input channels in chunks whose
 // (c, k) rows fill kR reduction rows: the chunk is contracted on the vector
 // ALUs (fp32, serial per element, the forward plan's segments), rounded to
-// bf16 into LDS as a [pixel][c*K + k] tile, and then multiplied on the matrix
-// cores: v_mfma_f32_16x16x32_bf16 with W as the A operand (16 o x 32 rows)
-// and the LDS tile as the B operand (32 rows x 16 pixels), fp32 accumulation
-// in registers across all chunks.
+// the data type (bf16 or fp16) into LDS as a [pixel][c*K + k] tile, and then
+// multiplied on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16} with W as the
+// A operand (16 o x 32 rows) and the LDS tile as the B operand (32 rows x 16
+// pixels), fp32 accumulation in registers across all chunks.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -24,14 +24,38 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kPx = 64;        // output longitudes per block
 constexpr int kOBlk = 256;     // output channels per block (64 per wave)
 constexpr int kR = 64;         // reduction rows (c*K + k) per chunk: two MFMA k-steps
-constexpr int kLdsStride = kR + 8;  // bf16 elements per pixel row in LDS (16-byte aligned rows)
+constexpr int kLdsStride = kR + 8;  // 16-bit elements per pixel row in LDS (16-byte aligned rows)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int G>
-__device__ __forceinline__ void contract_item(const bf16_t *__restrict__ plane, const Item &it,
+// 16-bit data types of the kernel: storage, raw bits, and the matching MFMA.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+    typedef bf16x8 vec8;
+    static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+    static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+    static __device__ __forceinline__ short bits(bf16_t v) { return (short)v; }
+    static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Elem<f16_t> {
+    typedef f16x8 vec8;
+    static __device__ __forceinline__ float to_f32(f16_t v) { return (float)v; }
+    static __device__ __forceinline__ f16_t from_f32(float v) { return (f16_t)v; }
+    static __device__ __forceinline__ short bits(f16_t v) { return __builtin_bit_cast(short, v); }
+    static __device__ __forceinline__ f32x4 mfma(vec8 a, vec8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <int G, typename T>
+__device__ __forceinline__ void contract_item(const T *__restrict__ plane, const Item &it,
                                               const Seg *__restrict__ segs, const float *__restrict__ vals,
                                               int Wo, int in_stride, int wo, bool valid, float *acc)
 {
@@ -40,28 +64,30 @@ __device__ __forceinline__ void contract_item(const bf16_t *__restrict__ plane, 
     for (int q = it.seg_begin; q < it.seg_end; ++q) {
         const Seg sg = segs[q];
         const float *v = vals + sg.val_off;
-        const bf16_t *row = plane + sg.in_off;
+        const T *row = plane + sg.in_off;
         for (int t = 0; t < sg.m; ++t) {
             int base = sg.j0 + t;
             if (base >= Wo) base -= Wo;
             int idx = base + wo;
             if (idx >= Wo) idx -= Wo;
-            const float xv = valid ? bf16_to_f32(row[(int64_t)in_stride * idx]) : 0.0f;
+            const float xv = valid ? Elem<T>::to_f32(row[(int64_t)in_stride * idx]) : 0.0f;
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = fmaf(v[t * G + g], xv, acc[g]);
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restrict__ x, const bf16_t *__restrict__ W,
-                                                         bf16_t *__restrict__ y, const Item *__restrict__ items,
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x, const T *__restrict__ W,
+                                                         T *__restrict__ y, const Item *__restrict__ items,
                                                          const int32_t *__restrict__ block_ptr,
                                                          const int32_t *__restrict__ ho_order,
                                                          const Seg *__restrict__ segs, const float *__restrict__ vals,
                                                          int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
                                                          int in_stride, int n_pt, int n_ob)
 {
-    __shared__ __attribute__((aligned(16))) bf16_t tile[kPx * kLdsStride];
+    typedef typename Elem<T>::vec8 vec8;
+    __shared__ __attribute__((aligned(16))) T tile[kPx * kLdsStride];
 
     int bid = blockIdx.x;
     const int pt = bid % n_pt;
@@ -98,20 +124,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restric
             const int px = pair - cl * kPx;
             const int wo = wo0 + px;
             const bool valid = (cl < ccn) && (wo < Wo);
-            const bf16_t *plane = x + ((int64_t)b * C + (c0 + (cl < ccn ? cl : 0))) * plane_sz;
+            const T *plane = x + ((int64_t)b * C + (c0 + (cl < ccn ? cl : 0))) * plane_sz;
             for (int ii = it_begin; ii < it_end; ++ii) {
                 const Item it = items[ii];
                 float a[kMaxGroup];
                 switch (it.G) {
-                case 1: contract_item<1>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                case 2: contract_item<2>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                case 3: contract_item<3>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                default: contract_item<4>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 1: contract_item<1, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 2: contract_item<2, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 3: contract_item<3, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                default: contract_item<4, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
                 }
                 if (cl < CC) {
                     for (int g = 0; g < it.G; ++g) {
                         const int k = it.out_off[g] / HoWo;
-                        tile[px * kLdsStride + cl * K + k] = f32_to_bf16(valid ? a[g] : 0.0f);
+                        tile[px * kLdsStride + cl * K + k] = Elem<T>::from_f32(valid ? a[g] : 0.0f);
                     }
                 }
             }
@@ -119,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restric
         // rows past the chunk's (c, k) range are zero
         for (int e = tid; e < kPx * kR; e += kThreads) {
             const int px = e / kR, r = e - px * kR;
-            if (r >= ccn * K) tile[px * kLdsStride + r] = 0;
+            if (r >= ccn * K) tile[px * kLdsStride + r] = Elem<T>::from_f32(0.0f);
         }
         __syncthreads();
         // ---- einsum on the matrix cores ----
@@ -127,11 +153,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restric
 #pragma unroll
         for (int ks = 0; ks < kR / 32; ++ks) {
             const int rr0 = ks * 32 + 8 * (lane >> 4);
-            bf16x8 bop[4];
+            vec8 bop[4];
 #pragma unroll
             for (int p4 = 0; p4 < 4; ++p4) {
                 const int px = p4 * 16 + (lane & 15);
-                bop[p4] = *reinterpret_cast<const bf16x8 *>(&tile[px * kLdsStride + rr0]);
+                bop[p4] = *reinterpret_cast<const vec8 *>(&tile[px * kLdsStride + rr0]);
             }
 #pragma unroll
             for (int ot = 0; ot < 4; ++ot) {
@@ -140,12 +166,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restric
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int rr = rr0 + i;
-                    av[i] = (o < Co && rr < rvalid) ? (short)W[((int64_t)o * C + c0) * K + rr] : (short)0;
+                    av[i] = (o < Co && rr < rvalid) ? Elem<T>::bits(W[((int64_t)o * C + c0) * K + rr]) : (short)0;
                 }
-                const bf16x8 aop = __builtin_bit_cast(bf16x8, av);
+                const vec8 aop = __builtin_bit_cast(vec8, av);
 #pragma unroll
                 for (int p4 = 0; p4 < 4; ++p4)
-                    acc[ot][p4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[p4], acc[ot][p4], 0, 0, 0);
+                    acc[ot][p4] = Elem<T>::mfma(aop, bop[p4], acc[ot][p4]);
             }
         }
     }
@@ -158,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const bf16_t *__restric
             for (int a = 0; a < 4; ++a) {
                 const int o = o_base + ot * 16 + 4 * (lane >> 4) + a;
                 const int wo = wo0 + p4 * 16 + (lane & 15);
-                if (o < Co && wo < Wo) y[(((int64_t)b * Co + o) * Ho + ho) * Wo + wo] = f32_to_bf16(acc[ot][p4][a]);
+                if (o < Co && wo < Wo) y[(((int64_t)b * Co + o) * Ho + ho) * Wo + wo] = Elem<T>::from_f32(acc[ot][p4][a]);
             }
 }
 
@@ -170,9 +196,14 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
     const int n_pt = (a.Wo + kPx - 1) / kPx;
     const int n_ob = (a.Co + kOBlk - 1) / kOBlk;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pt;
-    hipLaunchKernelGGL(fused_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const bf16_t *)a.x,
-                       (const bf16_t *)a.W, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
-                       a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    if (a.f16)
+        hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
+                           (const f16_t *)a.W, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
+                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    else
+        hipLaunchKernelGGL(fused_kernel<bf16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const bf16_t *)a.x,
+                           (const bf16_t *)a.W, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
+                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
     return hipGetLastError();
 }
 

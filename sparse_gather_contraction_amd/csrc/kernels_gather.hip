@@ -107,7 +107,8 @@ static hipError_t launch_typed(const GatherLaunch &a, hipStream_t stream)
 hipError_t launch_gather(const GatherLaunch &a, hipStream_t stream)
 {
     if (a.n_items == 0 || a.BC == 0) return hipSuccess;
-    if (a.bf16) return launch_typed<bf16_t, bf16_t>(a, stream);
+    if (a.dtype == 1) return launch_typed<bf16_t, bf16_t>(a, stream);
+    if (a.dtype == 2) return launch_typed<f16_t, f16_t>(a, stream);
     return launch_typed<float, float>(a, stream);
 }
 

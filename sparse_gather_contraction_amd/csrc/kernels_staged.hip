@@ -28,6 +28,7 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ float lds_to_f32(const float *p) { return *p; }
 __device__ __forceinline__ float lds_to_f32(const bf16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float lds_to_f32(const f16_t *p) { return (float)*p; }
 
 template <int G, int T, int S, int M, typename TI>
 __device__ __forceinline__ void seg_body(const TI *p, const float *__restrict__ v, float (&acc)[G][T])
@@ -215,7 +216,8 @@ bool staged_supported(int NI, int G, int T, int S)
 hipError_t launch_staged(const StagedLaunch &a, hipStream_t stream)
 {
     if (a.n_tasks == 0 || a.BC == 0) return hipSuccess;
-    if (a.bf16) return dispatch_typed<bf16_t, bf16_t>(a, stream);
+    if (a.dtype == 1) return dispatch_typed<bf16_t, bf16_t>(a, stream);
+    if (a.dtype == 2) return dispatch_typed<f16_t, f16_t>(a, stream);
     return dispatch_typed<float, float>(a, stream);
 }
 

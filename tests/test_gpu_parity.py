@@ -287,9 +287,9 @@ def test_error_paths_leave_outputs_untouched():
     out_bf = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel, device=DEV, dtype=torch.bfloat16)
     st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(out_bf)), None)
     assert st == "DISCO_ERR_DTYPE"
-    x16 = x.half()
-    out16 = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel, device=DEV, dtype=torch.float16)
-    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x16)), ctypes.byref(sgc.tensor_desc(out16)), None)
+    x64 = x.double()  # fp64 data is not a supported dtype
+    out16 = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel, device=DEV, dtype=torch.float64)
+    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x64)), ctypes.byref(sgc.tensor_desc(out16)), None)
     assert st == "DISCO_ERR_DTYPE"
     host = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel)
     st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(host)), None)
@@ -480,3 +480,59 @@ def test_fused_bwd_721x1440_full_size_sampled():
         ref = sum(gy64[b] @ out[b].T for b in range(w.B))
         nrm = sum(np.abs(gy64[b]) @ outa[b].T for b in range(w.B))
         assert normalised_error(dW[:, c, :], ref, nrm) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- fp16 data
+# fp16 tensors (round to nearest even from the N(0,1) draw), fp32 psi and fp32 accumulation; every
+# 16-bit result is rounded once.  Bar: 2e-3 of the normaliser = 4 u with u = 2^-11 the fp16 unit
+# roundoff (output rounding u; for the fused op also the rounding of the contraction chunk, u).
+TOL_F16 = 2e-3
+
+
+@pytest.mark.parametrize("geom", [(31, 64, 31, 64, 0.5, 4, 2, 9), (33, 128, 17, 64, 0.6, 4, 2, 8),
+                                  (19, 144, 19, 72, 0.7, 4, 1, 3), (16, 32, 16, 32, 2 * np.pi / 16, 3, 1, 4)])
+def test_fwd_bwd_f16_agree_with_oracle(geom):
+    Hi, Wi, Ho, Wo, tc, nr, na, C = geom
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
+    h = gpu_psi(psi)
+    x = randn((2, C, Hi, Wi), 1400 + C, "f16")
+    g = randn((2, C, psi.K, Ho, Wo), 1450 + C, "f16")
+    out = sgc.disco_fwd(h, x.to(DEV))
+    gx = sgc.disco_bwd(h, g.to(DEV))
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16 and gx.dtype == torch.float16
+    assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL_F16
+    assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL_F16
+
+
+@pytest.mark.parametrize("cfg", [
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 8, 32),
+    (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 300),
+    (31, 60, 16, 30, 0.6, 3, 1, 1, 23, 20),
+])
+def test_fused_f16_agrees_with_oracle(cfg):
+    Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
+    h = gpu_psi(psi)
+    x = randn((B, C, Hi, Wi), 1500 + C, "f16")
+    W = randn((Co, C, psi.K), 1501 + C, "f16", std=1.0 / np.sqrt(C * psi.K))
+    y = nan_like((B, Co, Ho, Wo), torch.float16)
+    sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.fused(psi, x, W)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)
+    assert normalised_error(y, ref, nrm) <= TOL_F16
+
+
+def test_f16_721x1440_forward_sampled():
+    """The 721x1440 K=8 forward with fp16 data at its benchmark size; two whole channel planes."""
+    w = WORKLOADS["fwd_bf16_721x1440"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = randn((w.B, w.C, w.Hi, w.Wi), 1600, "f16")
+    out = sgc.disco_fwd(h, x.to(DEV))
+    torch.cuda.synchronize()
+    for c in (0, 37):
+        xs = x[:, c:c + 1]
+        assert normalised_error(out[:, c:c + 1].cpu(), oracle.fwd(psi, xs),
+                                oracle.fwd(psi, xs.abs(), abs_mode=True)) <= TOL_F16
