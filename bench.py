@@ -176,6 +176,7 @@ def main():
     nxt = None
     if not args.no_next_rows and "fused" in ops:
         nxt = {"fused_bwd": time_fused_bwd(sgc, torch, np, h_u, tensors, wu, psi_u, dev, stream)}
+        nxt["f16"] = time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -263,6 +264,40 @@ def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps
             "mfma_frac": round(alg / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
             "workspace_bytes": int(ws.numel()),
             "shape": {"B": w.B, "C": w.C, "Co": w.Co, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo]}}
+
+
+def time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream, warm=1, reps=3):
+    """The three ops of the step with fp16 data (same shapes and psi), timed apart from the step:
+    forward and backward run the vector-ALU gathers with fp32 psi, the fused op the vector-ALU
+    contraction with an fp16 matrix-core einsum."""
+    from disco_inputs import randn
+
+    x3 = randn((wf.B, wf.C, wf.Hi, wf.Wi), 3200, "f16").to(dev)
+    g4 = randn((wb.B, wb.C, wb.K, wb.Ho, wb.Wo), 3201, "f16").to(dev)
+    x5 = randn((wu.B, wu.C, wu.Hi, wu.Wi), 3202, "f16").to(dev)
+    W5 = randn((wu.Co, wu.C, wu.K), 3203, "f16", std=1.0 / math.sqrt(wu.C * wu.K)).to(dev)
+    calls = {"fwd": lambda: sgc.disco_fwd(h_fb, x3), "bwd": lambda: sgc.disco_bwd(h_fb, g4),
+             "fused": lambda: sgc.disco_fused_conv(h_u, x5, W5)}
+    res = {}
+    for op, fn in calls.items():
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        w, psi = {"fwd": (wf, psi_fb), "bwd": (wb, psi_fb), "fused": (wu, psi_u)}[op]
+        upd = op_updates(w, psi.nnz)
+        res[op] = {"ms": round(ms, 4), "Gnnz_updates_per_s": round(upd / ms / 1e6, 2)}
+    print(f"[bench] fp16: {res}", file=sys.stderr, flush=True)
+    return res
 
 
 def cpu_baseline(wf, wb, wu, psi_fb, psi_u):

@@ -13,9 +13,14 @@
 //
 // Tile: 128 x 128 outputs per workgroup of four waves (64 x 64 each, 2 x 2
 // v_mfma_f32_32x32x16_bf16 accumulators).  The reduction walks 32-wide chunks; both operand
-// chunks (128 rows x 64 bytes) stream into LDS by direct global->LDS loads, double-buffered.
+// chunks (128 rows x 64 bytes) stream into LDS by direct global->LDS loads through a ring of
+// three buffers, issued two chunks ahead (the products are short per chunk, so the loads need
+// that lead to cover the memory latency).
 // A row's four 16-byte column groups are stored XOR-swizzled by (row / 4) % 4 so that the
 // 16-byte operand reads of 16 consecutive rows hit distinct LDS banks.
+// Workgroups go round the eight XCDs (each with its own L2) by workgroup index; the grid is
+// renumbered so that each XCD takes one contiguous run of tiles in the order (split, column tile,
+// row tile), and the tiles that share an operand run back to back on one L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,6 +33,7 @@ constexpr int kGK = 32;                      // reduction chunk (elements)
 constexpr int kGThreads = 256;
 constexpr int kGOpBytes = kGT * kGK * 2;     // one operand chunk: 8 KiB
 constexpr int kGStage = 2 * kGOpBytes;       // A + B chunk
+constexpr int kGRing = 3;                    // chunks in flight + the one being multiplied
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -70,19 +76,24 @@ __device__ __forceinline__ bf16x8 frag(const unsigned char *op, int row, int ks,
     return *reinterpret_cast<const bf16x8 *>(op + row * 64 + 16 * slot);
 }
 
-// C[m][n] = sum_{k in [k_begin, k_end)} A[m][k] B[n][k]; blockIdx.z selects the k range (split).
+// C[m][n] = sum_{k in [k_begin, k_end)} A[m][k] B[n][k]; the tile index selects the k range (split).
 // OUT_F32: fp32 partial [z][M][N]; else bf16 C with row stride ldc.
 template <bool OUT_F32>
 __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const bf16_t *__restrict__ A, int64_t lda, int M,
                                                             uint32_t a_bytes, const bf16_t *__restrict__ Bm,
                                                             int64_t ldb, int N, uint32_t b_bytes, int Kd,
-                                                            int k_per_split, void *__restrict__ Cout, int64_t ldc)
+                                                            int k_per_split, void *__restrict__ Cout, int64_t ldc,
+                                                            int nt_m, int nt_n, int total)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kGStage];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kGRing * kGStage];
+    const int per_xcd = (int)(gridDim.x >> 3);
+    const int L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (L >= total) return;
+    const int tm = L % nt_m, tn = (L / nt_m) % nt_n, z = L / (nt_m * nt_n);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT, z = blockIdx.z;
+    const int m0 = tm * kGT, n0 = tn * kGT;
     const int k_begin = z * k_per_split;
     const int k_end = min(Kd, k_begin + k_per_split);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes), rb = make_rsrc(Bm, b_bytes);
@@ -96,21 +107,25 @@ __global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const bf16_t *__rest
             for (int a = 0; a < 16; ++a) d[i][j][a] = 0.0f;
 
     const int nk = k_end > k_begin ? (k_end - k_begin + kGK - 1) / kGK : 0;
-    if (nk > 0) {
-        load_chunk(ra, lda, m0, M, k_begin, k_end, smem, tid, wave);
-        load_chunk(rb, ldb, n0, N, k_begin, k_end, smem + kGOpBytes, tid, wave);
-    }
+    // chunk t lives in ring slot t % 3; each chunk is four direct loads per thread
+    auto issue = [&](int t) {
+        unsigned char *dst = smem + (t % kGRing) * kGStage;
+        const int k = k_begin + t * kGK;
+        load_chunk(ra, lda, m0, M, k, k_end, dst, tid, wave);
+        load_chunk(rb, ldb, n0, N, k, k_end, dst + kGOpBytes, tid, wave);
+    };
+    if (nk > 0) issue(0);
+    if (nk > 1) issue(1);
     const int r = lane & 31, h = lane >> 5;
     for (int t = 0; t < nk; ++t) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // chunk t in LDS; every wave is done with chunk t - 1
-        unsigned char *cur = smem + (t & 1) * kGStage;
-        if (t + 1 < nk) {
-            unsigned char *nxt = smem + ((t + 1) & 1) * kGStage;
-            const int k = k_begin + (t + 1) * kGK;
-            load_chunk(ra, lda, m0, M, k, k_end, nxt, tid, wave);
-            load_chunk(rb, ldb, n0, N, k, k_end, nxt + kGOpBytes, tid, wave);
-        }
+        // this thread's loads of chunk t have landed (those of chunk t + 1 may still be in flight)
+        if (t + 1 < nk)
+            __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt <= 4, no wait on the other counters
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // everyone's have; every wave is done with chunk t - 1, whose slot is refilled
+        if (t + 2 < nk) issue(t + 2);
+        const unsigned char *cur = smem + (t % kGRing) * kGStage;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 fa[2], fb[2];
@@ -181,15 +196,20 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
 hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const int splits = g.k_per_split > 0 ? (g.Kd + g.k_per_split - 1) / g.k_per_split : 1;
+    const int splits = (g.out_f32 && g.k_per_split > 0) ? (g.Kd + g.k_per_split - 1) / g.k_per_split : 1;
     const int kps = g.k_per_split > 0 ? g.k_per_split : g.Kd;
-    dim3 grid((g.N + kGT - 1) / kGT, (g.M + kGT - 1) / kGT, g.out_f32 ? splits : 1);
+    const int nt_m = (g.M + kGT - 1) / kGT, nt_n = (g.N + kGT - 1) / kGT;
+    const int64_t total = (int64_t)nt_m * nt_n * splits;
+    if (total >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));  // a multiple of the eight XCDs
     if (g.out_f32)
         hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGThreads), 0, stream, (const bf16_t *)g.A, g.lda, g.M,
-                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc);
+                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m, nt_n,
+                           (int)total);
     else
         hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kGThreads), 0, stream, (const bf16_t *)g.A, g.lda, g.M,
-                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc);
+                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m, nt_n,
+                           (int)total);
     return hipGetLastError();
 }
 
