@@ -267,9 +267,8 @@ def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps
 
 
 def time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream, warm=1, reps=3):
-    """The three ops of the step with fp16 data (same shapes and psi), timed apart from the step:
-    forward and backward run the vector-ALU gathers with fp32 psi, the fused op the vector-ALU
-    contraction with an fp16 matrix-core einsum."""
+    """The three ops of the step with fp16 data (same shapes and psi), timed apart from the step;
+    all three run on the fp16 matrix cores (psi as fp16 of psi * 2^e)."""
     from disco_inputs import randn
 
     x3 = randn((wf.B, wf.C, wf.Hi, wf.Wi), 3200, "f16").to(dev)

@@ -1,6 +1,7 @@
 // disco_api.hip — C ABI of libdisco.so: validation, plan upload and launches.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -56,10 +57,11 @@ struct DevFused {
     disco::FPiece *pieces = nullptr;
     disco::FRow *rows = nullptr;
     int32_t *descs = nullptr;
-    uint16_t *adata = nullptr;
+    uint16_t *adata = nullptr;    // bf16 psi
+    uint16_t *adata16 = nullptr;  // fp16 psi * 2^psi16_exp (same layout)
     int32_t *ho_piece = nullptr;
     int32_t *ho_order = nullptr;
-    int32_t max_piece_bytes = 0, max_resident_bytes = 0, kr = 16;
+    int32_t max_piece_bytes = 0, max_resident_bytes = 0, kr = 16, psi16_exp = 0;
     uint32_t desc_bytes = 0, adata_bytes = 0;
 };
 
@@ -120,6 +122,7 @@ void free_fused(DevFused &d)
     (void)hipFree(d.rows);
     (void)hipFree(d.descs);
     (void)hipFree(d.adata);
+    (void)hipFree(d.adata16);
     (void)hipFree(d.ho_piece);
     (void)hipFree(d.ho_order);
     d = DevFused();
@@ -134,12 +137,14 @@ hipError_t upload_fused(DevFused &d, const disco::FusedPlan &p)
     if ((e = upload(&d.rows, p.rows)) != hipSuccess) return e;
     if ((e = upload(&d.descs, p.descs)) != hipSuccess) return e;
     if ((e = upload(&d.adata, p.adata)) != hipSuccess) return e;
+    if ((e = upload(&d.adata16, p.adata16)) != hipSuccess) return e;
     if ((e = upload(&d.ho_piece, p.ho_piece)) != hipSuccess) return e;
     if ((e = upload(&d.ho_order, p.ho_order)) != hipSuccess) return e;
     d.ok = true;
     d.max_piece_bytes = p.max_piece_bytes;
     d.max_resident_bytes = p.max_resident_bytes;
     d.kr = p.kr;
+    d.psi16_exp = p.psi16_exp;
     d.desc_bytes = (uint32_t)(p.descs.size() * sizeof(int32_t));
     d.adata_bytes = (uint32_t)(p.adata.size() * sizeof(uint16_t));
     return hipSuccess;
@@ -309,14 +314,17 @@ disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, int dtype, int
 {
     const int d = dtype == DISCO_F32 ? 0 : 1;  // staged plan by element size
     const char *fm = getenv("DISCO_FWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
-    if (dtype == DISCO_BF16 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
+    if (dtype != DISCO_F32 && h->fwdm.ok && !(fm && strcmp(fm, "0") == 0)) {
         if (B * C * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
         const int fch = disco::fwd_mfma_channels(h->fwdm.kr);
         if (B * h->Ho * ((C + fch - 1) / fch) * ((h->Wo + 255) / 256) >= ((int64_t)1 << 31))
             return fail(DISCO_ERR_SHAPE, "forward grid exceeds 2^31 blocks");
         disco::FwdMfmaLaunch m;
         m.x = src; m.out = dst;
-        m.pieces = h->fwdm.pieces; m.rows = h->fwdm.rows; m.descs = h->fwdm.descs; m.adata = h->fwdm.adata;
+        m.pieces = h->fwdm.pieces; m.rows = h->fwdm.rows; m.descs = h->fwdm.descs;
+        m.f16 = dtype == DISCO_F16;
+        m.adata = m.f16 ? h->fwdm.adata16 : h->fwdm.adata;
+        m.scale = m.f16 ? std::ldexp(1.0f, -h->fwdm.psi16_exp) : 1.0f;
         m.ho_piece = h->fwdm.ho_piece; m.ho_order = h->fwdm.ho_order;
         m.B = (int32_t)B; m.C = (int32_t)C; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
         m.s = h->Wi / h->Wo; m.kr = h->fwdm.kr; m.max_piece_bytes = h->fwdm.max_piece_bytes;
@@ -335,7 +343,7 @@ disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int
 {
     const int d = dtype == DISCO_F32 ? 0 : 1;  // staged plan by element size
     const char *bm = getenv("DISCO_BWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
-    if (dtype == DISCO_BF16 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
+    if (dtype != DISCO_F32 && h->bwdm.ok && !(bm && strcmp(bm, "0") == 0)) {
         if (B * C * h->Hi == 0 || h->Wi == 0) return DISCO_OK;
         const int fch = disco::fwd_mfma_channels(h->bwdm.kr);
         const int32_t s = h->Wi / h->Wo;
@@ -344,7 +352,10 @@ disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int
             return fail(DISCO_ERR_SHAPE, "backward grid exceeds 2^31 blocks");
         disco::FwdMfmaLaunch m;
         m.x = src; m.out = dst;
-        m.pieces = h->bwdm.pieces; m.rows = h->bwdm.rows; m.descs = h->bwdm.descs; m.adata = h->bwdm.adata;
+        m.pieces = h->bwdm.pieces; m.rows = h->bwdm.rows; m.descs = h->bwdm.descs;
+        m.f16 = dtype == DISCO_F16;
+        m.adata = m.f16 ? h->bwdm.adata16 : h->bwdm.adata;
+        m.scale = m.f16 ? std::ldexp(1.0f, -h->bwdm.psi16_exp) : 1.0f;
         m.ho_piece = h->bwdm.ho_piece; m.ho_order = h->bwdm.ho_order;
         m.B = (int32_t)B; m.C = (int32_t)C; m.K = kBwdMfmaRows; m.Ho = groups; m.Wo = h->Wo;
         m.Hi = h->K * h->Ho; m.Wi = h->Wo; m.s = 1; m.kr = h->bwdm.kr; m.max_piece_bytes = h->bwdm.max_piece_bytes;
@@ -594,10 +605,13 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
         return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
     const char *fm = getenv("DISCO_FUSED_MFMA");  // test knob: "0" forces the VALU-contraction fused kernel
-    if (x->dtype == DISCO_BF16 && h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
+    if (h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
-        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs; m.adata = h->fused.adata;
+        m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs;
+        m.f16 = x->dtype == DISCO_F16;
+        m.adata = m.f16 ? h->fused.adata16 : h->fused.adata;
+        m.scale = m.f16 ? std::ldexp(1.0f, -h->fused.psi16_exp) : 1.0f;
         m.ho_piece = h->fused.ho_piece; m.ho_order = h->fused.ho_order;
         m.B = (int32_t)B; m.C = (int32_t)C; m.Co = (int32_t)Co; m.K = h->K;
         m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi; m.s = h->Wi / h->Wo;

@@ -72,6 +72,8 @@ struct FusedMfmaLaunch {
     const int32_t *ho_piece, *ho_order;
     int32_t B, C, Co, K, Ho, Wo, Hi, Wi, s, max_piece_bytes, max_resident_bytes;
     uint32_t desc_bytes, adata_bytes;  // sizes of the descriptor and psi arrays
+    bool f16;     // fp16 data and psi (adata then holds fp16 psi * 2^e)
+    float scale;  // 2^-e for fp16, 1 for bf16
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
@@ -100,6 +102,8 @@ struct FwdMfmaLaunch {
     int32_t B, C, K, Ho, Wo, Hi, Wi, s, kr, max_piece_bytes;  // geometry of the source/psi (the inverse CSR's for the backward)
     uint32_t desc_bytes, adata_bytes;
     OutMap om;
+    bool f16;     // fp16 data and psi (adata then holds fp16 psi * 2^e)
+    float scale;  // 2^-e for fp16, 1 for bf16
 };
 
 hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream);

@@ -45,6 +45,7 @@ constexpr int kWBytes = kMaxOt * kCh * 1024;  // W slice of one chunk
 constexpr int kXchBytes = kWaves * 4 * 1024;  // operand exchange (2 channels x 2 phases per wave)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -87,7 +88,43 @@ struct Ctx {
     int B, C, Co, K, L, Wi, s, n_ot, b, px0, o_base, tid, wave, lane;
     int64_t plane_sz;
     bool vec_x, vec_w;
+    float scale;  // contraction result scale: 2^-e for fp16 psi, 1 for bf16
 };
+
+// ---- 16-bit operand types ----------------------------------------------------------------------
+// F16 selects fp16 data and psi (psi stored as fp16 of psi * 2^e, the plan's exponent e putting the
+// largest |psi| near 2^14; the contraction result is scaled back by 2^-e exactly in fp32), else
+// bf16.  Operands travel as raw 16-bit patterns.
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(i16x8 a, i16x8 b, f32x16 c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+}
+
+// fp32 -> 16-bit pattern, round to nearest even; fp16 values are scaled first (exact, a power of 2)
+template <bool F16>
+__device__ __forceinline__ short to16(float v, float scale)
+{
+    if constexpr (F16)
+        return __builtin_bit_cast(short, (_Float16)(v * scale));
+    else
+        return __builtin_bit_cast(short, (__bf16)v);
+}
+
+template <bool F16>
+__device__ __forceinline__ i16x8 to_op8(const f32x16 &v, int base, float scale)
+{
+    i16x8 r;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) r[a] = to16<F16>(v[base + a], scale);
+    return r;
+}
 
 // ---- staging ---------------------------------------------------------------------------------
 
@@ -196,7 +233,7 @@ __device__ __forceinline__ void stage_w(const Ctx &c, int c0, unsigned char *wb)
 template <bool PERM>
 struct Ops {
     unsigned a[PERM ? 5 : 4];
-    bf16x8 b0, b1;
+    i16x8 b0, b1;
 };
 
 // KR: basis rows of the psi layout; one offset pair of psi spans KR 4-byte words.  Without PERM the
@@ -208,30 +245,30 @@ template <int KR, bool PERM>
 __device__ __forceinline__ void load_ops(Ops<PERM> &o, const unsigned char *a_base, const unsigned char *x_base,
                                          int wel2, int a_off, int x_off)
 {
-    o.b0 = *reinterpret_cast<const bf16x8 *>(x_base + x_off);
-    o.b1 = *reinterpret_cast<const bf16x8 *>(x_base + wel2 + x_off);
+    o.b0 = *reinterpret_cast<const i16x8 *>(x_base + x_off);
+    o.b1 = *reinterpret_cast<const i16x8 *>(x_base + wel2 + x_off);
     const unsigned *p = reinterpret_cast<const unsigned *>(a_base + a_off);
 #pragma unroll
     for (int i = 0; i < (PERM ? 5 : 4); ++i) o.a[i] = p[KR * i];
 }
 
 // sel (PERM only): 0x03020100 (even first offset: words as read) or 0x05040302 (odd: shifted by one)
-template <bool PERM>
+template <bool F16, bool PERM>
 __device__ __forceinline__ void mfma_ops(const Ops<PERM> &o, unsigned sel, f32x16 (&d)[2])
 {
     unsigned w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = PERM ? __builtin_amdgcn_perm(o.a[i + 1], o.a[i], sel) : o.a[i];
-    const bf16x8 a = __builtin_bit_cast(bf16x8, w);
-    d[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b0, d[0], 0, 0, 0);
-    d[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, o.b1, d[1], 0, 0, 0);
+    const i16x8 a = __builtin_bit_cast(i16x8, w);
+    d[0] = mfma32<F16>(a, o.b0, d[0]);
+    d[1] = mfma32<F16>(a, o.b1, d[1]);
 }
 
 // Contraction of one step for the wave's two channels.  Blocks go in pairs (P, Q): the operands
 // of one block are read while the other block's MFMAs run, and the descriptors of a pair are
 // read two pairs ahead.  Scheduling barriers keep that order (the compiler would otherwise
 // move the reads next to their uses).
-template <int KR, bool PERM>
+template <int KR, bool PERM, bool F16>
 __device__ __forceinline__ void contract_pairs(const unsigned char *__restrict__ stage, const unsigned char *a_base,
                                                const unsigned char *x_base, int wel2, int npair, unsigned sel,
                                                f32x16 (&d)[2])
@@ -246,11 +283,11 @@ __device__ __forceinline__ void contract_pairs(const unsigned char *__restrict__
         const int4 dC = desc[min(j + 2, lastp)];
         load_ops<KR>(Q, a_base, x_base, wel2, dA.z, dA.w);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_ops(P, sel, d);
+        mfma_ops<F16>(P, sel, d);
         __builtin_amdgcn_sched_barrier(0);
         load_ops<KR>(P, a_base, x_base, wel2, dB.x, dB.y);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_ops(Q, sel, d);
+        mfma_ops<F16>(Q, sel, d);
         __builtin_amdgcn_sched_barrier(0);
         dA = dB;
         dB = dC;
@@ -258,7 +295,7 @@ __device__ __forceinline__ void contract_pairs(const unsigned char *__restrict__
 }
 
 // odd: the lane's phase shift is odd (second psi copy, or the realigning selector)
-template <int KR>
+template <int KR, bool F16>
 __device__ __forceinline__ void contract(const unsigned char *__restrict__ stage, const unsigned char *__restrict__ win,
                                          const FPiece &pc, int a_lane2, int x_lane2, bool odd, int ch0,
                                          f32x16 (&d)[2])
@@ -269,33 +306,26 @@ __device__ __forceinline__ void contract(const unsigned char *__restrict__ stage
     const int wel2 = 2 * pc.win_elems;
     const unsigned char *x_base = win + ch0 * wel2 + x_lane2;
     if (pc.realign)
-        contract_pairs<KR, true>(stage, a_base, x_base, wel2, npair, odd ? 0x05040302u : 0x03020100u, d);
+        contract_pairs<KR, true, F16>(stage, a_base, x_base, wel2, npair, odd ? 0x05040302u : 0x03020100u, d);
     else
-        contract_pairs<KR, false>(stage, a_base + (odd ? pc.a_copy_bytes : 0), x_base, wel2, npair, 0u, d);
-}
-
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &v, int base)
-{
-    bf16x8 r;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) r[a] = (__bf16)v[base + a];
-    return r;
+        contract_pairs<KR, false, F16>(stage, a_base + (odd ? pc.a_copy_bytes : 0), x_base, wel2, npair, 0u, d);
 }
 
 // Einsum of a chunk: swap operands with the partner wave through `xch`, then accumulate the
 // wave's NOT/2 output-channel tiles for both phases.  Caller: barrier before (everyone done with
 // `xch` as a stage buffer, W slice visible).
-template <int NOTH>
+template <int NOTH, bool F16>
 __device__ __forceinline__ void einsum(unsigned char *__restrict__ xch, const unsigned char *__restrict__ wb,
-                                       int lane, int pp, int h2, f32x16 (&d)[2], f32x16 (&yacc)[2][NOTH])
+                                       int lane, int pp, int h2, float scale, f32x16 (&d)[2],
+                                       f32x16 (&yacc)[2][NOTH])
 {
-    bf16x8 own[2][2], oth[2][2];
+    i16x8 own[2][2], oth[2][2];
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
         for (int ph = 0; ph < 2; ++ph) {
-            own[cl][ph] = to_bf16x8(d[cl], 8 * ph);
-            *reinterpret_cast<bf16x8 *>(xch + 1024 * (((pp * 2 + h2) * 2 + cl) * 2 + ph) + 16 * lane) = own[cl][ph];
+            own[cl][ph] = to_op8<F16>(d[cl], 8 * ph, scale);
+            *reinterpret_cast<i16x8 *>(xch + 1024 * (((pp * 2 + h2) * 2 + cl) * 2 + ph) + 16 * lane) = own[cl][ph];
         }
     __syncthreads();
 #pragma unroll
@@ -303,18 +333,18 @@ __device__ __forceinline__ void einsum(unsigned char *__restrict__ xch, const un
 #pragma unroll
         for (int ph = 0; ph < 2; ++ph)
             oth[cl][ph] =
-                *reinterpret_cast<const bf16x8 *>(xch + 1024 * (((pp * 2 + (1 - h2)) * 2 + cl) * 2 + ph) + 16 * lane);
+                *reinterpret_cast<const i16x8 *>(xch + 1024 * (((pp * 2 + (1 - h2)) * 2 + cl) * 2 + ph) + 16 * lane);
 #pragma unroll
     for (int j = 0; j < NOTH; ++j) {
         const int ot = h2 * NOTH + j;
 #pragma unroll
         for (int cl = 0; cl < 2; ++cl) {
-            const bf16x8 wo = *reinterpret_cast<const bf16x8 *>(wb + 1024 * (ot * kCh + 2 * h2 + cl) + 16 * lane);
-            const bf16x8 wt = *reinterpret_cast<const bf16x8 *>(wb + 1024 * (ot * kCh + 2 * (1 - h2) + cl) + 16 * lane);
-            yacc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wo, own[cl][0], yacc[0][j], 0, 0, 0);
-            yacc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wo, own[cl][1], yacc[1][j], 0, 0, 0);
-            yacc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wt, oth[cl][0], yacc[0][j], 0, 0, 0);
-            yacc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wt, oth[cl][1], yacc[1][j], 0, 0, 0);
+            const i16x8 wo = *reinterpret_cast<const i16x8 *>(wb + 1024 * (ot * kCh + 2 * h2 + cl) + 16 * lane);
+            const i16x8 wt = *reinterpret_cast<const i16x8 *>(wb + 1024 * (ot * kCh + 2 * (1 - h2) + cl) + 16 * lane);
+            yacc[0][j] = mfma32<F16>(wo, own[cl][0], yacc[0][j]);
+            yacc[1][j] = mfma32<F16>(wo, own[cl][1], yacc[1][j]);
+            yacc[0][j] = mfma32<F16>(wt, oth[cl][0], yacc[0][j]);
+            yacc[1][j] = mfma32<F16>(wt, oth[cl][1], yacc[1][j]);
         }
     }
 }
@@ -331,7 +361,7 @@ __device__ __forceinline__ void zero(f32x16 (&d)[2])
 // chunk start), contract, and run the einsum at the chunk's last piece (the consumed stage
 // buffer then carries the operand exchange).  The buffers are restrict parameters so that the
 // compiler keeps the queued direct loads in flight across the LDS reads of the current stage.
-template <int NOTH>
+template <int NOTH, bool F16>
 __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int nsteps, int st, int t, int p, unsigned char *__restrict__ cur,
                                          unsigned char *__restrict__ nxt, unsigned char *__restrict__ wb, int a_lane2,
@@ -347,16 +377,16 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     }
     if (p == 0) zero(d);
     const FPiece pc = pieces[p_begin + p];
-    contract<16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * h2, d);
+    contract<16, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * h2, d);
     if (p + 1 == npieces) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
-        einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
+        einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
     }
 }
 
 // One chunk of a latitude whose psi stays resident: only the x windows stream (double-buffered).
-template <int NOTH>
+template <int NOTH, bool F16>
 __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &pc, int nchunks, int t,
                                                    const unsigned char *__restrict__ stage,
                                                    unsigned char *__restrict__ cur, unsigned char *__restrict__ nxt,
@@ -369,19 +399,19 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
     if (t > 0) stage_w(c, kCh * t, wb);
     if (t + 1 < nchunks) stage_windows<kCh>(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
     zero(d);
-    contract<16>(stage, cur, pc, a_lane2, x_lane2, odd, 2 * h2, d);
+    contract<16, F16>(stage, cur, pc, a_lane2, x_lane2, odd, 2 * h2, d);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // W slice visible; `cur` free for the exchange
-    einsum<NOTH>(cur, wb, c.lane, pp, h2, d, yacc);
+    einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
 }
 
-template <int NOT>
+template <int NOT, bool F16>
 __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ W, bf16_t *__restrict__ y,
     const FPiece *__restrict__ pieces, const FRow *__restrict__ rows, const int32_t *__restrict__ descs,
     const bf16_t *__restrict__ adata, const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order,
     int B, int C, int Co, int K, int Ho, int L, int Hi, int Wi, int s, int n_pxb, int n_ob, int buf_bytes,
-    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w)
+    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, float scale)
 {
     constexpr int NOTH = NOT / 2;
     // LDS: [W slice: NOT * kCh KiB] [stage buffer 0] [stage buffer 1]
@@ -411,6 +441,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.plane_sz = (int64_t)Hi * Wi;
     c.vec_x = vec_x != 0;
     c.vec_w = vec_w != 0;
+    c.scale = scale;
 
     // lane constants: A row r = lane % 32 is (phase 2 pp + r / 16, MFMA row m = r % 16 -> basis k);
     // the basis order puts k = 8h + a in result register a of lane half h
@@ -451,9 +482,9 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_psi(c, pc0, stage);
         stage_windows<kCh>(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
         for (int t = 0; t < nchunks; t += 2) {
-            run_chunk_resident<NOTH>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d, yacc);
+            run_chunk_resident<NOTH, F16>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d, yacc);
             if (t + 1 < nchunks)
-                run_chunk_resident<NOTH>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
+                run_chunk_resident<NOTH, F16>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
                                          yacc);
         }
     } else if (nsteps > 0) {
@@ -461,11 +492,11 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_step<kCh>(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
         for (int st = 0; st < nsteps; st += 2) {
-            run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
+            run_step<NOTH, F16>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
                            yacc);
             if (++p == npieces) { p = 0; ++t; }
             if (st + 1 < nsteps) {
-                run_step<NOTH>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
+                run_step<NOTH, F16>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
                                h2, d, yacc);
                 if (++p == npieces) { p = 0; ++t; }
             }
@@ -482,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 #pragma unroll
                 for (int a = 0; a < 16; ++a) {
                     const int o = c.o_base + (h2 * NOTH + j) * 32 + 8 * (a >> 2) + 4 * hh + (a & 3);
-                    if (o < Co) y[(((int64_t)c.b * Co + o) * Ho + ho) * L + wo] = f32_to_bf16(yacc[ph][j][a]);
+                    if (o < Co) y[(((int64_t)c.b * Co + o) * Ho + ho) * L + wo] = (bf16_t)to16<F16>(yacc[ph][j][a], 1.0f);
                 }
             }
         }
@@ -499,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
 // through two LDS stage buffers (two workgroups share a CU, so one computes while the other
 // waits for its stage); every output element is written once, from its accumulator.
 
-template <int KR, int FCH>
+template <int KR, int FCH, bool F16>
 __device__ __forceinline__ void fwd_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int p, int c0, unsigned char *__restrict__ cur,
                                          unsigned char *__restrict__ nxt, int a_lane2, int x_lane2, bool odd,
@@ -509,16 +540,16 @@ __device__ __forceinline__ void fwd_step(const Ctx &c, const FPiece *__restrict_
     __syncthreads();                // everyone's have; the previous step is done with `nxt`
     if (p + 1 < npieces) stage_step<FCH>(c, pieces[p_begin + p + 1], c0, nxt);
     const FPiece pc = pieces[p_begin + p];
-    contract<KR>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * cp, d);
+    contract<KR, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * cp, d);
 }
 
-template <int KR>
+template <int KR, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void fwd_mfma_kernel(
     const bf16_t *__restrict__ x, bf16_t *__restrict__ out, const FPiece *__restrict__ pieces,
     const FRow *__restrict__ rows, const int32_t *__restrict__ descs, const bf16_t *__restrict__ adata,
     const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order, int B, int C, int K, int Ho, int L,
     int Hi, int Wi, int s, int n_pxb, int n_cb, int buf_bytes, uint32_t desc_bytes, uint32_t adata_bytes, int vec_x,
-    OutMap om)
+    OutMap om, float scale)
 {
     constexpr int PH = 32 / KR, NG = 8 / PH, WPG = kWaves / NG, FCH = 2 * WPG;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -546,6 +577,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     c.plane_sz = (int64_t)Hi * Wi;
     c.vec_x = vec_x != 0;
     c.vec_w = false;
+    c.scale = scale;
 
     // lane constants: A row r = lane % 32 is (phase PH g + r / KR, basis k = r % KR)
     const int g = c.wave % NG, cp = c.wave / NG;
@@ -563,9 +595,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (npieces > 0) {
         stage_step<FCH>(c, pieces[p_begin], c0, buf0);
         for (int p = 0; p < npieces; p += 2) {
-            fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p, c0, buf0, buf1, a_lane2, x_lane2, odd, cp, d);
+            fwd_step<KR, FCH, F16>(c, pieces, p_begin, npieces, p, c0, buf0, buf1, a_lane2, x_lane2, odd, cp, d);
             if (p + 1 < npieces)
-                fwd_step<KR, FCH>(c, pieces, p_begin, npieces, p + 1, c0, buf1, buf0, a_lane2, x_lane2, odd, cp, d);
+                fwd_step<KR, FCH, F16>(c, pieces, p_begin, npieces, p + 1, c0, buf1, buf0, a_lane2, x_lane2, odd, cp, d);
         }
     }
 
@@ -585,10 +617,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int rr = ho * KR + k;
                 if (rr < om.rows) {
                     const int hi = rr / om.s;
-                    plane[(int64_t)hi * om.wi + (rr - hi * om.s) + (int64_t)om.s * wo] = f32_to_bf16(d[cl][a]);
+                    plane[(int64_t)hi * om.wi + (rr - hi * om.s) + (int64_t)om.s * wo] = (bf16_t)to16<F16>(d[cl][a], scale);
                 }
             } else {
-                plane[((int64_t)k * Ho + ho) * L + wo] = f32_to_bf16(d[cl][a]);
+                plane[((int64_t)k * Ho + ho) * L + wo] = (bf16_t)to16<F16>(d[cl][a], scale);
             }
         }
     }
@@ -608,23 +640,27 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
     const int n_cb = (a.C + fch - 1) / fch;
     const int buf_bytes = (a.max_piece_bytes + 15) & ~15;
     const size_t lds = 2 * (size_t)buf_bytes;
-    const void *fn = a.kr == 8 ? (const void *)fwd_mfma_kernel<8> : (const void *)fwd_mfma_kernel<16>;
+    const void *fn = a.kr == 8 ? (a.f16 ? (const void *)fwd_mfma_kernel<8, true> : (const void *)fwd_mfma_kernel<8, false>)
+                               : (a.f16 ? (const void *)fwd_mfma_kernel<16, true> : (const void *)fwd_mfma_kernel<16, false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_cb * n_pxb;
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
                           (int64_t)a.Hi * a.Wi * 2 * fch < ((int64_t)1 << 31);
     const int vec_x = planes16 ? 1 : 0;
-    if (a.kr == 8)
-        hipLaunchKernelGGL(fwd_mfma_kernel<8>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x,
-                           (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order,
-                           a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes, a.desc_bytes,
-                           a.adata_bytes, vec_x, a.om);
-    else
-        hipLaunchKernelGGL(fwd_mfma_kernel<16>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x,
-                           (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order,
-                           a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes, a.desc_bytes,
-                           a.adata_bytes, vec_x, a.om);
+#define DISCO_FWD_LAUNCH(KR, F16)                                                                                   \
+    hipLaunchKernelGGL((fwd_mfma_kernel<KR, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,             \
+                       (const bf16_t *)a.x, (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata,       \
+                       a.ho_piece, a.ho_order, a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes,    \
+                       a.desc_bytes, a.adata_bytes, vec_x, a.om, a.scale)
+    if (a.kr == 8) {
+        if (a.f16) DISCO_FWD_LAUNCH(8, true);
+        else DISCO_FWD_LAUNCH(8, false);
+    } else {
+        if (a.f16) DISCO_FWD_LAUNCH(16, true);
+        else DISCO_FWD_LAUNCH(16, false);
+    }
+#undef DISCO_FWD_LAUNCH
     return hipGetLastError();
 }
 
@@ -647,9 +683,12 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
     const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
     const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_bytes, a.max_resident_bytes);
-    const void *fn = n_ot == 2 ? (const void *)fused_mfma_kernel<2>
-                   : n_ot == 4 ? (const void *)fused_mfma_kernel<4>
-                               : (const void *)fused_mfma_kernel<8>;
+    const void *fn = a.f16 ? (n_ot == 2   ? (const void *)fused_mfma_kernel<2, true>
+                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, true>
+                                          : (const void *)fused_mfma_kernel<8, true>)
+                           : (n_ot == 2   ? (const void *)fused_mfma_kernel<2, false>
+                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, false>
+                                          : (const void *)fused_mfma_kernel<8, false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pxb;
@@ -658,15 +697,23 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
                           (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
     const int vec_x = planes16 ? 1 : 0;
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
-#define DISCO_FUSED_LAUNCH(N)                                                                                  \
-    hipLaunchKernelGGL(fused_mfma_kernel<N>, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const bf16_t *)a.x, \
-                       (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata,        \
-                       a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_ob,         \
-                       buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w)
-    switch (n_ot) {
-    case 2: DISCO_FUSED_LAUNCH(2); break;
-    case 4: DISCO_FUSED_LAUNCH(4); break;
-    default: DISCO_FUSED_LAUNCH(8); break;
+#define DISCO_FUSED_LAUNCH(N, F16)                                                                               \
+    hipLaunchKernelGGL((fused_mfma_kernel<N, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,             \
+                       (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.descs,            \
+                       (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi,  \
+                       a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, a.scale)
+    if (a.f16) {
+        switch (n_ot) {
+        case 2: DISCO_FUSED_LAUNCH(2, true); break;
+        case 4: DISCO_FUSED_LAUNCH(4, true); break;
+        default: DISCO_FUSED_LAUNCH(8, true); break;
+        }
+    } else {
+        switch (n_ot) {
+        case 2: DISCO_FUSED_LAUNCH(2, false); break;
+        case 4: DISCO_FUSED_LAUNCH(4, false); break;
+        default: DISCO_FUSED_LAUNCH(8, false); break;
+        }
     }
 #undef DISCO_FUSED_LAUNCH
     return hipGetLastError();

@@ -2,6 +2,7 @@
 #include "plan_fused.hpp"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <map>
@@ -17,6 +18,27 @@ uint16_t bf16_rne(float f)
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16 bits, round to nearest even (subnormals and overflow to infinity included); the
+// rounding is done in double, where every step is exact.
+uint16_t f16_rne(float f)
+{
+    const double v = (double)f;
+    const uint16_t sign = std::signbit(v) ? 0x8000u : 0u;
+    const double a = std::fabs(v);
+    if (std::isnan(v)) return (uint16_t)(sign | 0x7e00u);
+    if (a < std::ldexp(1.0, -14)) {  // subnormal range: multiples of 2^-24
+        const double q = std::nearbyint(a * std::ldexp(1.0, 24));
+        return (uint16_t)(sign | (uint16_t)q);  // q = 1024 is the smallest normal
+    }
+    int e = 0;
+    const double m = std::frexp(a, &e);  // a = m 2^e, m in [0.5, 1)
+    double q = std::nearbyint(m * 2048.0);  // 11 significant bits
+    if (q == 2048.0) { q = 1024.0; ++e; }
+    const int ef = e - 1 + 15;  // biased exponent of 1.f x 2^(e-1)
+    if (ef >= 31) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)(ef << 10) | (uint16_t)(q - 1024.0));
 }
 
 int32_t floor8(int32_t v) { return (v >= 0) ? (v / 8) * 8 : -(((-v) + 7) / 8) * 8; }
@@ -39,6 +61,14 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
     out.kr = kr;
     out.s = s;
     out.ho_piece.push_back(0);
+    {
+        float vmax = 0.0f;
+        for (int64_t e = 0; e < c.nnz; ++e) vmax = std::max(vmax, std::fabs(c.val[e]));
+        int ex = 0;
+        if (vmax > 0.0f && std::isfinite(vmax)) std::frexp((double)vmax, &ex);  // vmax in [2^(ex-1), 2^ex)
+        out.psi16_exp = vmax > 0.0f ? 15 - ex : 0;
+    }
+    const double psi16_scale = std::ldexp(1.0, out.psi16_exp);
     std::vector<int64_t> work(c.Ho, 0);
     const int32_t smax = 7 * s;                            // largest phase shift of psi
     // psi e-rows of a sub-row (even): a lane reads four words (two copies) or five (one copy, the
@@ -150,14 +180,20 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
             pc.win_elems = (int32_t)we;
             int32_t a_row_e = 0, win_off = 0;
             std::vector<uint16_t> copy1;  // second psi copy of the piece (s odd)
-            auto put_pairs = [&](std::vector<uint16_t> &dst, const std::map<int32_t, std::vector<float>> &m,
-                                 int32_t e_base, int32_t ra, int32_t shift) {
+            std::vector<uint16_t> copy1_16;
+            auto put_pairs = [&](std::vector<uint16_t> &dst, std::vector<uint16_t> &dst16,
+                                 const std::map<int32_t, std::vector<float>> &m, int32_t e_base, int32_t ra,
+                                 int32_t shift) {
                 // [e pair][k][2]: word m holds offsets e_base + shift + 2m and + 1 (relative to first - 8 s)
                 for (int32_t e2 = 0; e2 < ra; e2 += 2) {
                     auto it0 = m.find(e_base + shift + e2), it1 = m.find(e_base + shift + e2 + 1);
                     for (int32_t k = 0; k < kr; ++k) {
-                        dst.push_back((it0 != m.end() && k < c.K) ? bf16_rne(it0->second[k]) : (uint16_t)0);
-                        dst.push_back((it1 != m.end() && k < c.K) ? bf16_rne(it1->second[k]) : (uint16_t)0);
+                        const float v0 = (it0 != m.end() && k < c.K) ? it0->second[k] : 0.0f;
+                        const float v1 = (it1 != m.end() && k < c.K) ? it1->second[k] : 0.0f;
+                        dst.push_back(bf16_rne(v0));
+                        dst.push_back(bf16_rne(v1));
+                        dst16.push_back(f16_rne((float)(v0 * psi16_scale)));
+                        dst16.push_back(f16_rne((float)(v1 * psi16_scale)));
                     }
                 }
             };
@@ -175,8 +211,8 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
                     out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));
                     out.descs.push_back(2 * (win_off + (t0 - first)));
                 }
-                put_pairs(out.adata, m, first - 8 * s, ra, 0);
-                if (copies == 2) put_pairs(copy1, m, first - 8 * s, ra, 1);
+                put_pairs(out.adata, out.adata16, m, first - 8 * s, ra, 0);
+                if (copies == 2) put_pairs(copy1, copy1_16, m, first - 8 * s, ra, 1);
                 a_row_e += ra;
                 win_off += fr.len;
             }
@@ -184,9 +220,14 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
                 out.descs.push_back(2 * kr * (a_row_e + 8 * s));
                 out.descs.push_back(0);
                 out.adata.insert(out.adata.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
-                if (copies == 2) copy1.insert(copy1.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
+                out.adata16.insert(out.adata16.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
+                if (copies == 2) {
+                    copy1.insert(copy1.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
+                    copy1_16.insert(copy1_16.end(), (size_t)kr * (8 * s + tail), (uint16_t)0);
+                }
             }
             out.adata.insert(out.adata.end(), copy1.begin(), copy1.end());
+            out.adata16.insert(out.adata16.end(), copy1_16.begin(), copy1_16.end());
             pc.row_end = (int32_t)out.rows.size();
             pc.resident = 0;
             pc.a_copy_bytes = copies == 2 ? pc.a_elems : 0;  // byte offset of the second copy = half the psi bytes

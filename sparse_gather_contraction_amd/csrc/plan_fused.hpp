@@ -79,6 +79,8 @@ struct FusedPlan {
     std::vector<FRow> rows;
     std::vector<int32_t> descs;         // per block: byte offsets (psi rows, window run) in the piece stage
     std::vector<uint16_t> adata;        // bf16 psi, [e][16] per sub-row
+    std::vector<uint16_t> adata16;      // the same layout as fp16 of psi * 2^psi16_exp
+    int32_t psi16_exp = 0;              // puts the largest |psi| in [2^14, 2^15)
     int64_t mfma_blocks = 0;            // total blocks over all latitudes
 };
 

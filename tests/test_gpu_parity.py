@@ -483,15 +483,20 @@ def test_fused_bwd_721x1440_full_size_sampled():
 
 
 # ---------------------------------------------------------------- fp16 data
-# fp16 tensors (round to nearest even from the N(0,1) draw), fp32 psi and fp32 accumulation; every
-# 16-bit result is rounded once.  Bar: 2e-3 of the normaliser = 4 u with u = 2^-11 the fp16 unit
-# roundoff (output rounding u; for the fused op also the rounding of the contraction chunk, u).
+# fp16 tensors (round to nearest even from the N(0,1) draw) and fp32 accumulation; every 16-bit
+# result is rounded once.  The matrix-core paths take psi as fp16 of psi * 2^e (e puts the largest
+# |psi| near 2^14; the power of two is undone exactly in fp32), the vector-ALU paths fp32 psi.
+# Bar: 2e-3 of the normaliser, above the worst case 3 u (u = 2^-11, the fp16 unit roundoff: psi,
+# the contraction chunk of the fused op, and the output).
 TOL_F16 = 2e-3
 
 
+@pytest.mark.parametrize("mfma", ["0", "1"])
 @pytest.mark.parametrize("geom", [(31, 64, 31, 64, 0.5, 4, 2, 9), (33, 128, 17, 64, 0.6, 4, 2, 8),
                                   (19, 144, 19, 72, 0.7, 4, 1, 3), (16, 32, 16, 32, 2 * np.pi / 16, 3, 1, 4)])
-def test_fwd_bwd_f16_agree_with_oracle(geom):
+def test_fwd_bwd_f16_agree_with_oracle(geom, mfma, monkeypatch):
+    monkeypatch.setenv("DISCO_FWD_MFMA", mfma)
+    monkeypatch.setenv("DISCO_BWD_MFMA", mfma)
     Hi, Wi, Ho, Wo, tc, nr, na, C = geom
     psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
     h = gpu_psi(psi)
@@ -505,12 +510,15 @@ def test_fwd_bwd_f16_agree_with_oracle(geom):
     assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL_F16
 
 
+@pytest.mark.parametrize("mfma", ["0", "1"])
 @pytest.mark.parametrize("cfg", [
     (31, 64, 31, 64, 0.5, 4, 4, 2, 8, 32),
+    (31, 64, 31, 64, 1.5, 4, 4, 1, 6, 33),
     (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 300),
     (31, 60, 16, 30, 0.6, 3, 1, 1, 23, 20),
 ])
-def test_fused_f16_agrees_with_oracle(cfg):
+def test_fused_f16_agrees_with_oracle(cfg, mfma, monkeypatch):
+    monkeypatch.setenv("DISCO_FUSED_MFMA", mfma)
     Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
     psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
     h = gpu_psi(psi)
@@ -525,7 +533,8 @@ def test_fused_f16_agrees_with_oracle(cfg):
 
 
 def test_f16_721x1440_forward_sampled():
-    """The 721x1440 K=8 forward with fp16 data at its benchmark size; two whole channel planes."""
+    """The 721x1440 K=8 forward with fp16 data at its benchmark size (matrix cores); two whole
+    channel planes."""
     w = WORKLOADS["fwd_bf16_721x1440"]
     psi = workload_psi(w)
     h = gpu_psi(psi)
@@ -536,3 +545,19 @@ def test_f16_721x1440_forward_sampled():
         xs = x[:, c:c + 1]
         assert normalised_error(out[:, c:c + 1].cpu(), oracle.fwd(psi, xs),
                                 oracle.fwd(psi, xs.abs(), abs_mode=True)) <= TOL_F16
+
+
+def test_f16_fused_721x1440_sampled():
+    """The 721x1440 K=16 fused op with fp16 data at its benchmark size (matrix cores); whole output
+    latitudes from pole to equator."""
+    w = WORKLOADS["fused_bf16_721x1440"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = randn((w.B, w.C, w.Hi, w.Wi), 1700, "f16")
+    W = randn((w.Co, w.C, w.K), 1701, "f16", std=1.0 / np.sqrt(w.C * w.K))
+    y = sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    hos = [0, 3, 200, 360]
+    ref = oracle.fused(psi, x[:1], W, ho_list=hos)
+    nrm = oracle.fused(psi, x[:1].abs(), W.abs(), ho_list=hos, abs_mode=True)
+    assert normalised_error(y[:1, :, hos].cpu(), ref, nrm) <= TOL_F16
