@@ -310,7 +310,9 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, 
 }
 
 // Forward contraction of B x C planes, src (B, C, Hi, Wi) -> dst (B, C, K, Ho, Wo), after validation.
-disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, int dtype, int64_t B, int64_t C, hipStream_t stream)
+// src_bs / dst_bs: elements between batches (0: the C planes of a batch follow one another).
+disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, int dtype, int64_t B, int64_t C, hipStream_t stream,
+                         int64_t src_bs = 0, int64_t dst_bs = 0)
 {
     const int d = dtype == DISCO_F32 ? 0 : 1;  // staged plan by element size
     const char *fm = getenv("DISCO_FWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
@@ -330,16 +332,27 @@ disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, int dtype, int
         m.s = h->Wi / h->Wo; m.kr = h->fwdm.kr; m.max_piece_bytes = h->fwdm.max_piece_bytes;
         m.desc_bytes = h->fwdm.desc_bytes; m.adata_bytes = h->fwdm.adata_bytes;
         m.om.plane = (int64_t)h->K * h->Ho * h->Wo; m.om.inverse = 0; m.om.rows = 0; m.om.wi = 0; m.om.s = 1;
+        m.x_bstride = src_bs; m.out_bstride = dst_bs;
         hipError_t e = disco::launch_fwd_mfma(m, stream);
         if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("forward launch failed: ") + hipGetErrorString(e));
         return DISCO_OK;
     }
-    return run_gather(h->fwd, h->sfwd[d], src, dst, dtype, B * C, (int64_t)h->Hi * h->Wi,
-                      (int64_t)h->K * h->Ho * h->Wo, stream);
+    const int64_t sp = (int64_t)h->Hi * h->Wi, dp = (int64_t)h->K * h->Ho * h->Wo;
+    if ((src_bs == 0 || src_bs == C * sp) && (dst_bs == 0 || dst_bs == C * dp))
+        return run_gather(h->fwd, h->sfwd[d], src, dst, dtype, B * C, sp, dp, stream);
+    const size_t esz = dtype == DISCO_F32 ? 4 : 2;
+    for (int64_t b = 0; b < B; ++b) {
+        disco_status st = run_gather(h->fwd, h->sfwd[d], (const char *)src + b * src_bs * esz,
+                                     (char *)dst + b * dst_bs * esz, dtype, C, sp, dp, stream);
+        if (st != DISCO_OK) return st;
+    }
+    return DISCO_OK;
 }
 
 // Transpose contraction of B x C planes, src (B, C, K, Ho, Wo) -> dst (B, C, Hi, Wi), after validation.
-disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int64_t B, int64_t C, hipStream_t stream)
+// src_bs / dst_bs: elements between batches (0: the C planes of a batch follow one another).
+disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int64_t B, int64_t C, hipStream_t stream,
+                         int64_t src_bs = 0, int64_t dst_bs = 0)
 {
     const int d = dtype == DISCO_F32 ? 0 : 1;  // staged plan by element size
     const char *bm = getenv("DISCO_BWD_MFMA");  // test knob: "0" forces the vector-ALU gather for bf16
@@ -361,16 +374,26 @@ disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int
         m.Hi = h->K * h->Ho; m.Wi = h->Wo; m.s = 1; m.kr = h->bwdm.kr; m.max_piece_bytes = h->bwdm.max_piece_bytes;
         m.desc_bytes = h->bwdm.desc_bytes; m.adata_bytes = h->bwdm.adata_bytes;
         m.om.plane = (int64_t)h->Hi * h->Wi; m.om.inverse = 1; m.om.rows = h->Hi * s; m.om.wi = h->Wi; m.om.s = s;
+        m.x_bstride = src_bs; m.out_bstride = dst_bs;
         hipError_t e = disco::launch_fwd_mfma(m, stream);
         if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("backward launch failed: ") + hipGetErrorString(e));
         return DISCO_OK;
     }
-    return run_gather(h->bwd, h->sbwd[d], src, dst, dtype, B * C, (int64_t)h->K * h->Ho * h->Wo,
-                      (int64_t)h->Hi * h->Wi, stream);
+    const int64_t sp = (int64_t)h->K * h->Ho * h->Wo, dp = (int64_t)h->Hi * h->Wi;
+    if ((src_bs == 0 || src_bs == C * sp) && (dst_bs == 0 || dst_bs == C * dp))
+        return run_gather(h->bwd, h->sbwd[d], src, dst, dtype, B * C, sp, dp, stream);
+    const size_t esz = dtype == DISCO_F32 ? 4 : 2;
+    for (int64_t b = 0; b < B; ++b) {
+        disco_status st = run_gather(h->bwd, h->sbwd[d], (const char *)src + b * src_bs * esz,
+                                     (char *)dst + b * dst_bs * esz, dtype, C, sp, dp, stream);
+        if (st != DISCO_OK) return st;
+    }
+    return DISCO_OK;
 }
 
 // Workspace of the fused-convolution backward: W^T, gy^T of every batch, one channel chunk of
-// g = W^T gy (and afterwards of out = F x), and the fp32 partials of dW for one chunk.
+// g = W^T gy for every batch (and afterwards of out = F x), and the fp32 partials of dW for one
+// chunk.  A chunk holds up to 512 (c, k) rows.
 struct FusedBwdLayout {
     int64_t N = 0;                 // positions Ho Wo
     int32_t Cc = 0, Mc = 0;        // channels per chunk and its rows cc K
@@ -385,7 +408,7 @@ FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int6
     FusedBwdLayout L;
     const int64_t K = h->K;
     L.N = (int64_t)h->Ho * h->Wo;
-    L.Cc = (int32_t)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(C, 1), 256 / std::max<int64_t>(K, 1)));
+    L.Cc = (int32_t)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(C, 1), 512 / std::max<int64_t>(K, 1)));
     L.Mc = (int32_t)(L.Cc * K);
     const int64_t per = std::max<int64_t>(1, (L.N + 255) / 256);  // at most 256 splits
     L.kps = (int32_t)((per + 31) / 32 * 32);
@@ -393,7 +416,7 @@ FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int6
     size_t off = 0;
     L.wt = off;   off = align256(off + (size_t)C * K * Co * 2);
     L.gyt = off;  off = align256(off + (size_t)B * L.N * Co * 2);
-    L.gbuf = off; off = align256(off + (size_t)L.Mc * L.N * 2);
+    L.gbuf = off; off = align256(off + (size_t)B * L.Mc * L.N * 2);
     L.part = off; off = align256(off + (size_t)B * L.S * Co * L.Mc * 4);
     L.total = off;
     return L;
@@ -705,21 +728,43 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
         const int64_t cc = std::min<int64_t>(L.Cc, C - c0);
         const int32_t Mc = (int32_t)(cc * K);
         if (cc <= 0) break;
+        uint16_t *gb = gbuf;  // [b][c k][n] of this chunk
+        const int64_t gstride = (int64_t)Mc * N;
         for (int64_t b = 0; b < B; ++b) {
             // g[c k][n] = sum_o W[o, c0 + c, k] gy[b, o, n]
             disco::GemmNtLaunch g1;
             g1.A = wt + c0 * K * Co; g1.lda = Co; g1.M = Mc; g1.a_bytes = (uint32_t)((int64_t)Mc * Co * 2);
             g1.B = gyt + b * N * Co; g1.ldb = Co; g1.N = (int32_t)N; g1.b_bytes = (uint32_t)(N * Co * 2);
-            g1.Kd = (int32_t)Co; g1.k_per_split = 0; g1.out_f32 = false; g1.C = gbuf; g1.ldc = N;
+            g1.Kd = (int32_t)Co; g1.k_per_split = 0; g1.out_f32 = false; g1.C = gb + b * gstride; g1.ldc = N;
             if ((e = disco::launch_gemm_nt(g1, sm)) != hipSuccess) return hipfail(e, "W^T gy product");
-            // gx[b, c0 + c] = F^T g
-            if ((st = enqueue_bwd(h, gbuf, gxp + (b * C + c0) * plane_in, DISCO_BF16, 1, cc, sm)) != DISCO_OK) return st;
-            // out[c k][n] = (F x)[b, c0 + c]
-            if ((st = enqueue_fwd(h, xp + (b * C + c0) * plane_in, gbuf, DISCO_BF16, 1, cc, sm)) != DISCO_OK) return st;
+        }
+        // gx[b, c0 + c] = F^T g, every batch in one launch
+        if ((st = enqueue_bwd(h, gb, gxp + c0 * plane_in, DISCO_BF16, B, cc, sm, gstride, C * plane_in)) != DISCO_OK)
+            return st;
+        // out[b][c k][n] = (F x)[b, c0 + c]: the fused kernel's contraction (psi resident across the
+        // chunk's channels) where its plan exists, else the forward contraction
+        const char *fc = getenv("DISCO_FUSED_MFMA");  // test knob: "0" also turns this path off
+        if (h->fused.ok && !(fc && strcmp(fc, "0") == 0)) {
+            disco::FusedContractLaunch m;
+            m.x = xp + c0 * plane_in; m.out = gb;
+            m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs; m.adata = h->fused.adata;
+            m.ho_piece = h->fused.ho_piece; m.ho_order = h->fused.ho_order;
+            m.B = (int32_t)B; m.C = (int32_t)cc; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
+            m.s = h->Wi / h->Wo; m.max_piece_bytes = h->fused.max_piece_bytes;
+            m.max_resident_bytes = h->fused.max_resident_bytes;
+            m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
+            m.f16 = false; m.scale = 1.0f;
+            m.x_bstride = C * plane_in; m.out_bstride = gstride;
+            if ((e = disco::launch_fused_contract(m, sm)) != hipSuccess) return hipfail(e, "contraction");
+        } else if ((st = enqueue_fwd(h, xp + c0 * plane_in, gb, DISCO_BF16, B, cc, sm, C * plane_in, gstride)) !=
+                   DISCO_OK) {
+            return st;
+        }
+        for (int64_t b = 0; b < B; ++b) {
             // partial dW[o][c k] over each position split
             disco::GemmNtLaunch g2;
             g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);
-            g2.B = gbuf; g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
+            g2.B = gb + b * gstride; g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
             g2.Kd = (int32_t)N; g2.k_per_split = L.kps; g2.out_f32 = true;
             g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc;
             if ((e = disco::launch_gemm_nt(g2, sm)) != hipSuccess) return hipfail(e, "gy out^T product");

@@ -77,6 +77,24 @@ struct FusedMfmaLaunch {
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
+
+// The fused kernel's contraction alone, out[b, c, k, ho, wo] (K <= 16), over the fused op's plan:
+// each block walks all channels with the latitude's psi resident where it fits.
+struct FusedContractLaunch {
+    const void *x;
+    void *out;
+    const FPiece *pieces;
+    const FRow *rows;
+    const int32_t *descs;
+    const uint16_t *adata;
+    const int32_t *ho_piece, *ho_order;
+    int32_t B, C, K, Ho, Wo, Hi, Wi, s, max_piece_bytes, max_resident_bytes;
+    uint32_t desc_bytes, adata_bytes;
+    bool f16;
+    float scale;
+    int64_t x_bstride = 0, out_bstride = 0;  // elements between batches (0: contiguous)
+};
+hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t stream);
 size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_bytes);
 int fused_mfma_channels_per_chunk();
 int fused_mfma_exchange_bytes();     // LDS bytes of the einsum operand exchange
@@ -104,6 +122,7 @@ struct FwdMfmaLaunch {
     OutMap om;
     bool f16;     // fp16 data and psi (adata then holds fp16 psi * 2^e)
     float scale;  // 2^-e for fp16, 1 for bf16
+    int64_t x_bstride = 0, out_bstride = 0;  // elements between batches (0: C contiguous planes)
 };
 
 hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream);

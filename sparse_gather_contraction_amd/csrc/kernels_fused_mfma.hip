@@ -87,8 +87,13 @@ struct Ctx {
     const FRow *rows;
     int B, C, Co, K, L, Wi, s, n_ot, b, px0, o_base, tid, wave, lane;
     int64_t plane_sz;
+    int64_t x_bstride;  // elements between batches of x (C planes when contiguous)
     bool vec_x, vec_w;
     float scale;  // contraction result scale: 2^-e for fp16 psi, 1 for bf16
+    // contraction-only mode: out[b, c, k, ho, wo] at out + b * out_bstride
+    bf16_t *out;
+    int64_t out_bstride;
+    int Ho, ho;
 };
 
 // ---- 16-bit operand types ----------------------------------------------------------------------
@@ -147,7 +152,7 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
 {
     const int nrows = pc.row_end - pc.row_begin;
     const int ccn = min(NCH, c.C - c0);
-    const bf16_t *plane0 = c.x + ((int64_t)c.b * c.C + c0) * c.plane_sz;
+    const bf16_t *plane0 = c.x + (int64_t)c.b * c.x_bstride + (int64_t)c0 * c.plane_sz;
     for (int r = c.wave; r < nrows; r += kWaves) {
         const FRow fr = c.rows[pc.row_begin + r];
         bf16_t *dst = win + fr.win_off;
@@ -361,7 +366,31 @@ __device__ __forceinline__ void zero(f32x16 (&d)[2])
 // chunk start), contract, and run the einsum at the chunk's last piece (the consumed stage
 // buffer then carries the operand exchange).  The buffers are restrict parameters so that the
 // compiler keeps the queued direct loads in flight across the LDS reads of the current stage.
-template <int NOTH, bool F16>
+// Contraction-only mode: write the chunk's contraction result (channels kCh t + 2 h2 + cl) from the
+// accumulators.  Register a of lane (n, hh) is MFMA row 8 (a / 4) + 4 hh + a % 4: phase 2 pp + row / 16,
+// basis kb(row % 16) in the order the psi rows were read.
+template <bool F16>
+__device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d)[2], int t, int pp, int h2)
+{
+    const int r = c.lane & 31, hh = c.lane >> 5;
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl) {
+        const int ch = kCh * t + 2 * h2 + cl;
+        if (ch >= c.C) continue;
+        bf16_t *plane = c.out + (int64_t)c.b * c.out_bstride + (int64_t)ch * c.K * c.Ho * c.L;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const int row = 8 * (a >> 2) + 4 * hh + (a & 3);
+            const int m = row & 15;
+            const int k = (m < 8) ? 8 * (m >> 2) + (m & 3) : 8 * ((m - 8) >> 2) + 4 + (m & 3);
+            const int wo = c.px0 + 8 * r + 2 * pp + (row >> 4);
+            if (k < c.K && wo < c.L) plane[((int64_t)k * c.Ho + c.ho) * c.L + wo] = (bf16_t)to16<F16>(d[cl][a], c.scale);
+        }
+    }
+}
+
+// EIN: fused op (einsum into yacc); else contraction-only (the chunk's result is written out).
+template <int NOTH, bool F16, bool EIN>
 __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int nsteps, int st, int t, int p, unsigned char *__restrict__ cur,
                                          unsigned char *__restrict__ nxt, unsigned char *__restrict__ wb, int a_lane2,
@@ -369,7 +398,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
 {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into `cur` (and W) have landed
     __syncthreads();                // everyone's have; the previous step is done with `nxt` and W
-    if (p == 0 && t > 0) stage_w(c, kCh * t, wb);
+    if (EIN && p == 0 && t > 0) stage_w(c, kCh * t, wb);
     if (st + 1 < nsteps) {
         const int p1 = (p + 1 == npieces) ? 0 : p + 1;
         const int t1 = (p + 1 == npieces) ? t + 1 : t;
@@ -379,14 +408,18 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     const FPiece pc = pieces[p_begin + p];
     contract<16, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * h2, d);
     if (p + 1 == npieces) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // W slice visible; `cur` free for the exchange
-        einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
+        if constexpr (EIN) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // W slice visible; `cur` free for the exchange
+            einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
+        } else {
+            store_contraction<F16>(c, d, t, pp, h2);
+        }
     }
 }
 
 // One chunk of a latitude whose psi stays resident: only the x windows stream (double-buffered).
-template <int NOTH, bool F16>
+template <int NOTH, bool F16, bool EIN>
 __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &pc, int nchunks, int t,
                                                    const unsigned char *__restrict__ stage,
                                                    unsigned char *__restrict__ cur, unsigned char *__restrict__ nxt,
@@ -396,22 +429,27 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
 {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t > 0) stage_w(c, kCh * t, wb);
+    if (EIN && t > 0) stage_w(c, kCh * t, wb);
     if (t + 1 < nchunks) stage_windows<kCh>(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
     zero(d);
     contract<16, F16>(stage, cur, pc, a_lane2, x_lane2, odd, 2 * h2, d);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // W slice visible; `cur` free for the exchange
-    einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
+    if constexpr (EIN) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // W slice visible; `cur` free for the exchange
+        einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
+    } else {
+        store_contraction<F16>(c, d, t, pp, h2);
+    }
 }
 
-template <int NOT, bool F16>
+template <int NOT, bool F16, bool EIN>
 __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ W, bf16_t *__restrict__ y,
     const FPiece *__restrict__ pieces, const FRow *__restrict__ rows, const int32_t *__restrict__ descs,
     const bf16_t *__restrict__ adata, const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order,
     int B, int C, int Co, int K, int Ho, int L, int Hi, int Wi, int s, int n_pxb, int n_ob, int buf_bytes,
-    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, float scale)
+    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, float scale, int64_t x_bstride,
+    int64_t out_bstride)
 {
     constexpr int NOTH = NOT / 2;
     // LDS: [W slice: NOT * kCh KiB] [stage buffer 0] [stage buffer 1]
@@ -439,9 +477,14 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.px0 = pxb * kFusedSpan;
     c.o_base = ob * (kMaxOt * 32);
     c.plane_sz = (int64_t)Hi * Wi;
+    c.x_bstride = x_bstride;
     c.vec_x = vec_x != 0;
     c.vec_w = vec_w != 0;
     c.scale = scale;
+    c.out = y;
+    c.out_bstride = out_bstride;
+    c.Ho = Ho;
+    c.ho = ho;
 
     // lane constants: A row r = lane % 32 is (phase 2 pp + r / 16, MFMA row m = r % 16 -> basis k);
     // the basis order puts k = 8h + a in result register a of lane half h
@@ -478,25 +521,26 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         unsigned char *stage = buf0;
         unsigned char *w0 = stage + 4 * pc0.desc_words + 2 * pc0.a_elems;
         unsigned char *w1 = w0 + pc0.resident;
-        stage_w(c, 0, wb);
+        if (EIN) stage_w(c, 0, wb);
         stage_psi(c, pc0, stage);
         stage_windows<kCh>(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
         for (int t = 0; t < nchunks; t += 2) {
-            run_chunk_resident<NOTH, F16>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d, yacc);
+            run_chunk_resident<NOTH, F16, EIN>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d,
+                                               yacc);
             if (t + 1 < nchunks)
-                run_chunk_resident<NOTH, F16>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
+                run_chunk_resident<NOTH, F16, EIN>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
                                          yacc);
         }
     } else if (nsteps > 0) {
-        stage_w(c, 0, wb);
+        if (EIN) stage_w(c, 0, wb);
         stage_step<kCh>(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
         for (int st = 0; st < nsteps; st += 2) {
-            run_step<NOTH, F16>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
+            run_step<NOTH, F16, EIN>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
                            yacc);
             if (++p == npieces) { p = 0; ++t; }
             if (st + 1 < nsteps) {
-                run_step<NOTH, F16>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
+                run_step<NOTH, F16, EIN>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
                                h2, d, yacc);
                 if (++p == npieces) { p = 0; ++t; }
             }
@@ -504,6 +548,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     }
 
     // ---- epilogue: yacc[ph][j] row = output channel, column n = longitude px0 + 8n + 2 pp + ph ----
+    if constexpr (!EIN) return;
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
         const int wo = c.px0 + 8 * r + 2 * pp + ph;
@@ -549,7 +594,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const FRow *__restrict__ rows, const int32_t *__restrict__ descs, const bf16_t *__restrict__ adata,
     const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order, int B, int C, int K, int Ho, int L,
     int Hi, int Wi, int s, int n_pxb, int n_cb, int buf_bytes, uint32_t desc_bytes, uint32_t adata_bytes, int vec_x,
-    OutMap om, float scale)
+    OutMap om, float scale, int64_t x_bstride, int64_t out_bstride)
 {
     constexpr int PH = 32 / KR, NG = 8 / PH, WPG = kWaves / NG, FCH = 2 * WPG;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -575,6 +620,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     c.px0 = pxb * kFusedSpan;
     c.o_base = 0;
     c.plane_sz = (int64_t)Hi * Wi;
+    c.x_bstride = x_bstride;
     c.vec_x = vec_x != 0;
     c.vec_w = false;
     c.scale = scale;
@@ -606,7 +652,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     for (int cl = 0; cl < 2; ++cl) {
         const int cc = c0 + 2 * cp + cl;
         if (cc >= C) continue;
-        bf16_t *plane = out + ((int64_t)c.b * C + cc) * om.plane;
+        bf16_t *plane = out + (int64_t)c.b * out_bstride + (int64_t)cc * om.plane;
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
             const int row = 8 * (a >> 2) + 4 * hh + (a & 3);
@@ -645,14 +691,16 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_cb * n_pxb;
+    const int64_t x_bs = a.x_bstride > 0 ? a.x_bstride : (int64_t)a.C * a.Hi * a.Wi;
+    const int64_t out_bs = a.out_bstride > 0 ? a.out_bstride : (int64_t)a.C * a.om.plane;
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
                           (int64_t)a.Hi * a.Wi * 2 * fch < ((int64_t)1 << 31);
-    const int vec_x = planes16 ? 1 : 0;
+    const int vec_x = planes16 && (x_bs % 8) == 0 ? 1 : 0;
 #define DISCO_FWD_LAUNCH(KR, F16)                                                                                   \
     hipLaunchKernelGGL((fwd_mfma_kernel<KR, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,             \
                        (const bf16_t *)a.x, (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata,       \
                        a.ho_piece, a.ho_order, a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes,    \
-                       a.desc_bytes, a.adata_bytes, vec_x, a.om, a.scale)
+                       a.desc_bytes, a.adata_bytes, vec_x, a.om, a.scale, x_bs, out_bs)
     if (a.kr == 8) {
         if (a.f16) DISCO_FWD_LAUNCH(8, true);
         else DISCO_FWD_LAUNCH(8, false);
@@ -661,6 +709,32 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
         else DISCO_FWD_LAUNCH(16, false);
     }
 #undef DISCO_FWD_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t stream)
+{
+    if (a.B == 0 || a.C == 0) return hipSuccess;
+    const int n_pxb = (a.Wo + kFusedSpan - 1) / kFusedSpan;
+    const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
+    const size_t lds = fused_mfma_lds_bytes(2, a.max_piece_bytes, a.max_resident_bytes);
+    const void *fn = a.f16 ? (const void *)fused_mfma_kernel<2, true, false> : (const void *)fused_mfma_kernel<2, false, false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t nblk = (int64_t)a.B * a.Ho * n_pxb;
+    const int64_t x_bs = a.x_bstride > 0 ? a.x_bstride : (int64_t)a.C * a.Hi * a.Wi;
+    const int64_t out_bs = a.out_bstride > 0 ? a.out_bstride : (int64_t)a.C * a.K * a.Ho * a.Wo;
+    const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
+                          x_bs % 8 == 0 && (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
+    const int vec_x = planes16 ? 1 : 0;
+#define DISCO_CONTRACT_LAUNCH(F16)                                                                               \
+    hipLaunchKernelGGL((fused_mfma_kernel<2, F16, false>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,      \
+                       (const bf16_t *)a.x, (const bf16_t *)nullptr, (bf16_t *)a.out, a.pieces, a.rows, a.descs,      \
+                       (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, 0, a.K, a.Ho, a.Wo, a.Hi, a.Wi,     \
+                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, 0, a.scale, x_bs, out_bs)
+    if (a.f16) DISCO_CONTRACT_LAUNCH(true);
+    else DISCO_CONTRACT_LAUNCH(false);
+#undef DISCO_CONTRACT_LAUNCH
     return hipGetLastError();
 }
 
@@ -683,12 +757,12 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
     const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
     const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_bytes, a.max_resident_bytes);
-    const void *fn = a.f16 ? (n_ot == 2   ? (const void *)fused_mfma_kernel<2, true>
-                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, true>
-                                          : (const void *)fused_mfma_kernel<8, true>)
-                           : (n_ot == 2   ? (const void *)fused_mfma_kernel<2, false>
-                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, false>
-                                          : (const void *)fused_mfma_kernel<8, false>);
+    const void *fn = a.f16 ? (n_ot == 2   ? (const void *)fused_mfma_kernel<2, true, true>
+                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, true, true>
+                                          : (const void *)fused_mfma_kernel<8, true, true>)
+                           : (n_ot == 2   ? (const void *)fused_mfma_kernel<2, false, true>
+                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, false, true>
+                                          : (const void *)fused_mfma_kernel<8, false, true>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pxb;
@@ -697,11 +771,13 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
                           (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
     const int vec_x = planes16 ? 1 : 0;
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
+    const int64_t x_bs = (int64_t)a.C * a.Hi * a.Wi;
 #define DISCO_FUSED_LAUNCH(N, F16)                                                                               \
-    hipLaunchKernelGGL((fused_mfma_kernel<N, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,             \
+    hipLaunchKernelGGL((fused_mfma_kernel<N, F16, true>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,       \
                        (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.descs,            \
                        (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi,  \
-                       a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, a.scale)
+                       a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, a.scale, x_bs,         \
+                       (int64_t)0)
     if (a.f16) {
         switch (n_ot) {
         case 2: DISCO_FUSED_LAUNCH(2, true); break;
