@@ -177,6 +177,7 @@ def main():
     if not args.no_next_rows and "fused" in ops:
         nxt = {"fused_bwd": time_fused_bwd(sgc, torch, np, h_u, tensors, wu, psi_u, dev, stream)}
         nxt["f16"] = time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream)
+        nxt["page_shapes"] = time_page_shapes(sgc, torch, np, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -296,6 +297,53 @@ def time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream, 
         upd = op_updates(w, psi.nnz)
         res[op] = {"ms": round(ms, 4), "Gnnz_updates_per_s": round(upd / ms / 1e6, 2)}
     print(f"[bench] fp16: {res}", file=sys.stderr, flush=True)
+    return res
+
+
+def time_page_shapes(sgc, torch, np, dev, stream, reps=3):
+    """The DISCO page's own benchmark shapes (section "Serial Benchmarks": Gauss-Legendre grids,
+    theta_c = 0.017, K = 9 stand-in basis, batch 1), bf16: fused convolution and its backward."""
+    from disco_inputs import WORKLOADS, randn, workload_psi, workload_weight, workload_x
+
+    res = {}
+    for name in ("page_self_256x360x720", "page_self_512x360x720", "page_down_80x721x1440"):
+        w = WORKLOADS[name]
+        psi = workload_psi(w)
+        h = sgc.disco_psi_create(psi, 0)
+        x = workload_x(w).to(dev)
+        W = workload_weight(w).to(dev)
+        gy = randn((w.B, w.Co, w.Ho, w.Wo), 3300 + w.index, "bf16").to(dev)
+        y = torch.empty((w.B, w.Co, w.Ho, w.Wo), dtype=torch.bfloat16, device=dev)
+        gx = torch.empty_like(x)
+        dW = torch.empty_like(W)
+        ws = torch.empty(max(1, sgc.disco_fused_conv_bwd_workspace(h, w.B, w.C, w.Co)), dtype=torch.uint8, device=dev)
+        fns = {"fused": lambda: sgc.disco_fused_conv(h, x, W, y),
+               "fused_bwd": lambda: sgc.disco_fused_conv_bwd(h, x, W, gy, gx, dW, workspace=ws)}
+        upd = op_updates(w, psi.nnz)
+        macs = w.B * w.Ho * w.Wo * w.Co * w.C * w.K
+        r = {"shape": {"B": w.B, "C": w.C, "Co": w.Co, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo],
+                       "nnz": psi.nnz, "grids": [w.grid_in, w.grid_out]}}
+        for op, fn in fns.items():
+            fn()
+            torch.cuda.synchronize()
+            ev = []
+            for _ in range(reps):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            alg = (2 * upd + 2 * macs) * (2 if op == "fused_bwd" else 1)
+            r[op] = {"ms": round(ms, 4), "mfma_tflops_algorithmic": round(alg / ms / 1e9, 3),
+                     "mfma_frac": round(alg / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4)}
+        res[name] = r
+        h.close()
+        del x, W, gy, y, gx, dW, ws
+    print(f"[bench] page shapes: { {k: (v['fused']['ms'], v['fused_bwd']['ms']) for k, v in res.items()} }",
+          file=sys.stderr, flush=True)
     return res
 
 

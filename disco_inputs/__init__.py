@@ -29,9 +29,11 @@ class Workload:
     n_r: int
     n_a: int
     theta_c: float
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     ops: tuple
     Co: int = 0
+    grid_in: str = "equiangular"
+    grid_out: str = "equiangular"
 
     @property
     def K(self) -> int:
@@ -56,15 +58,23 @@ WORKLOADS = {
     "fwd_bf16_721x1440": Workload("fwd_bf16_721x1440", 2, 1, 64, 721, 1440, 361, 720, 4, 2, 3 * math.pi / 180, "bf16", ("fwd",)),
     "bwd_bf16_721x1440": Workload("bwd_bf16_721x1440", 3, 1, 64, 721, 1440, 361, 720, 4, 2, 3 * math.pi / 180, "bf16", ("bwd",)),
     "fused_bf16_721x1440": Workload("fused_bf16_721x1440", 4, 2, 256, 721, 1440, 721, 1440, 4, 4, 2 * math.pi / 180, "bf16", ("fused",), Co=256),
+    # the benchmark shapes of the DISCO page (section "Serial Benchmarks"): batch 1 (the page gives
+    # none), theta_c = 0.017 rad, kernel_shape (3, 3) read as 3 radial hats x {1, cos a, sin a}
+    "page_self_256x360x720": Workload("page_self_256x360x720", 5, 1, 256, 360, 720, 360, 720, 3, 3, 0.017, "bf16",
+                                      ("fused",), Co=256, grid_in="legendre-gauss", grid_out="legendre-gauss"),
+    "page_self_512x360x720": Workload("page_self_512x360x720", 6, 1, 512, 360, 720, 360, 720, 3, 3, 0.017, "bf16",
+                                      ("fused",), Co=512, grid_in="legendre-gauss", grid_out="legendre-gauss"),
+    "page_down_80x721x1440": Workload("page_down_80x721x1440", 7, 1, 80, 721, 1440, 360, 720, 3, 3, 0.017, "bf16",
+                                      ("fused",), Co=512, grid_in="equiangular", grid_out="legendre-gauss"),
 }
 
 _PSI_CACHE: dict = {}
 
 
 def workload_psi(w: Workload) -> PsiCSR:
-    key = (w.Hi, w.Wi, w.Ho, w.Wo, w.theta_c, w.n_r, w.n_a)
+    key = (w.Hi, w.Wi, w.Ho, w.Wo, w.theta_c, w.n_r, w.n_a, w.grid_in, w.grid_out)
     if key not in _PSI_CACHE:
-        _PSI_CACHE[key] = build_psi(w.Hi, w.Wi, w.Ho, w.Wo, w.theta_c, w.n_r, w.n_a)
+        _PSI_CACHE[key] = build_psi(w.Hi, w.Wi, w.Ho, w.Wo, w.theta_c, w.n_r, w.n_a, w.grid_in, w.grid_out)
     return _PSI_CACHE[key]
 
 

@@ -14,11 +14,17 @@ plain readings used here are:
   phi_i = 2*pi*i/W (input and output grids alike);
 * quadrature weight q_j = sin(theta_j) * dtheta * dphi, with sin set to exactly
   0 at both poles (so polar input rows carry no entries);
+* the page's benchmark shapes also name a "legendre-gauss" grid (section
+  "Serial Benchmarks"): colatitudes theta_j = arccos(x_j) for the H Gauss-Legendre
+  nodes x_j in decreasing order (north to south), weights q_j = w_j * dphi with
+  w_j the Gauss weights (they sum to 2, so the weights of the sphere sum to 4 pi);
 * geodesic distance by the haversine formula in colatitude;
 * isotropic piecewise-linear hats: dr = theta_c / n_r, centres r_m = m*dr,
   hat_m(d) = max(0, 1 - |d - r_m| / dr) for d < theta_c, else 0;
 * azimuthal factors of the bearing alpha seen from the output point:
-  n_a = 1 -> {1}; 2 -> {cos a, sin a}; 4 -> {cos a, sin a, cos 2a, sin 2a};
+  n_a = 1 -> {1}; 2 -> {cos a, sin a}; 3 -> {1, cos a, sin a};
+  4 -> {cos a, sin a, cos 2a, sin 2a} (the page's "harmonic" kernel_shape (3, 3)
+  is read as 3 radial hats x these 3 azimuthal factors, K = 9);
 * basis index k = m * n_a + a (radial outer, azimuthal inner);
 * an entry (k, ho; hi, wi) is stored iff hat_m(d) > 0 and q_hi > 0 (the
   azimuthal factor never removes an entry, so all n_a rows of one hat share
@@ -80,6 +86,30 @@ def quadrature_weights(H: int, W: int) -> np.ndarray:
     return s * (np.pi / (H - 1)) * (2.0 * np.pi / W)
 
 
+def legendre_gauss_colatitudes(n: int):
+    """(colatitudes, Gauss weights) for n Gauss-Legendre latitudes, north to south."""
+    x, w = np.polynomial.legendre.leggauss(n)
+    order = np.argsort(-x)  # x = cos(theta) decreasing: theta increasing
+    return np.arccos(x[order]), w[order]
+
+
+def grid_colatitudes(grid: str, H: int) -> np.ndarray:
+    if grid == "equiangular":
+        return equiangular_colatitudes(H)
+    if grid == "legendre-gauss":
+        return legendre_gauss_colatitudes(H)[0]
+    raise ValueError(f"unknown grid {grid}")
+
+
+def grid_quadrature(grid: str, H: int, W: int) -> np.ndarray:
+    """Per-latitude quadrature weights of the grid (sum over the sphere = W * sum = 4 pi)."""
+    if grid == "equiangular":
+        return quadrature_weights(H, W)
+    if grid == "legendre-gauss":
+        return legendre_gauss_colatitudes(H)[1] * (2.0 * np.pi / W)
+    raise ValueError(f"unknown grid {grid}")
+
+
 def geodesic_distance(theta_o, theta_i, dphi):
     """Great-circle distance (haversine form, colatitudes)."""
     h = np.sin(0.5 * (theta_i - theta_o)) ** 2 + np.sin(theta_o) * np.sin(theta_i) * np.sin(0.5 * dphi) ** 2
@@ -108,6 +138,8 @@ def azimuthal_factors(alpha, n_a: int) -> np.ndarray:
         return np.ones((1,) + np.shape(alpha))
     if n_a == 2:
         return np.stack([np.cos(alpha), np.sin(alpha)])
+    if n_a == 3:
+        return np.stack([np.ones_like(np.asarray(alpha, dtype=np.float64)), np.cos(alpha), np.sin(alpha)])
     if n_a == 4:
         return np.stack([np.cos(alpha), np.sin(alpha), np.cos(2 * alpha), np.sin(2 * alpha)])
     raise ValueError(f"unsupported number of azimuthal factors {n_a}")
@@ -125,14 +157,15 @@ def basis_values(theta_o, theta_i, dphi, theta_c: float, n_r: int, n_a: int, q) 
     return vals.reshape((n_r * n_a,) + vals.shape[2:]), hats
 
 
-def build_psi(Hi: int, Wi: int, Ho: int, Wo: int, theta_c: float, n_r: int, n_a: int = 1) -> PsiCSR:
-    """Build the CSR psi for an equiangular Hi x Wi -> Ho x Wo convolution."""
+def build_psi(Hi: int, Wi: int, Ho: int, Wo: int, theta_c: float, n_r: int, n_a: int = 1,
+              grid_in: str = "equiangular", grid_out: str = "equiangular") -> PsiCSR:
+    """Build the CSR psi for a Hi x Wi -> Ho x Wo convolution on the given latitude grids."""
     if Wi % Wo != 0:
         raise ValueError("Wi must be an integer multiple of Wo")
     K = n_r * n_a
-    theta_in = equiangular_colatitudes(Hi)
-    theta_out = equiangular_colatitudes(Ho)
-    q = quadrature_weights(Hi, Wi)
+    theta_in = grid_colatitudes(grid_in, Hi)
+    theta_out = grid_colatitudes(grid_out, Ho)
+    q = grid_quadrature(grid_in, Hi, Wi)
     dphi_all = 2.0 * np.pi * np.arange(Wi, dtype=np.float64) / Wi
 
     # rows are emitted per (k, ho); collect per ho first, then order by k

@@ -561,3 +561,47 @@ def test_f16_fused_721x1440_sampled():
     ref = oracle.fused(psi, x[:1], W, ho_list=hos)
     nrm = oracle.fused(psi, x[:1].abs(), W.abs(), ho_list=hos, abs_mode=True)
     assert normalised_error(y[:1, :, hos].cpu(), ref, nrm) <= TOL_F16
+
+
+# ---------------------------------------------------------------- the page's benchmark shapes
+
+@pytest.mark.parametrize("name", ["page_self_256x360x720", "page_self_512x360x720", "page_down_80x721x1440"])
+def test_page_shapes_fused_sampled(name):
+    """Fused convolution at the DISCO page's benchmark shapes (Gauss-Legendre grids, K = 9): whole
+    output latitudes from pole to equator against the oracle."""
+    w = WORKLOADS[name]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = workload_x(w)
+    W = workload_weight(w)
+    _log(f"{name}: GPU")
+    y = sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    hos = [0, 1, 90, 179, 359]
+    ref = oracle.fused(psi, x, W, ho_list=hos)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), ho_list=hos, abs_mode=True)
+    assert normalised_error(y[:, :, hos].cpu(), ref, nrm) <= TOL["bf16"]
+
+
+def test_page_shape_fused_bwd_sampled():
+    """Fused backward at the page's down-sampling shape (721x1440 equiangular -> 360x720
+    Gauss-Legendre, s = 2, 80 -> 512 channels); one input channel's gradients checked."""
+    w = WORKLOADS["page_down_80x721x1440"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = workload_x(w)
+    W = workload_weight(w)
+    gy = randn((w.B, w.Co, psi.Ho, psi.Wo), 1800, "bf16")
+    gx, dW = sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV))
+    torch.cuda.synchronize()
+    gx, dW = gx.cpu(), dW.cpu()
+    gy64 = gy.double().numpy().reshape(w.B, w.Co, -1)
+    W64 = W.double().numpy()
+    c = 37
+    g = (W64[:, c, :].T @ gy64[0]).reshape(1, psi.K, psi.Ho, psi.Wo)
+    ga = (np.abs(W64[:, c, :]).T @ np.abs(gy64[0])).reshape(1, psi.K, psi.Ho, psi.Wo)
+    assert normalised_error(gx[0, c][None], oracle.bwd(psi, g.astype(np.float32)),
+                            oracle.bwd(psi, ga.astype(np.float32), abs_mode=True)) <= TOL["bf16"]
+    out = oracle.fwd(psi, x[0, c][None])[0].reshape(psi.K, -1)
+    outa = oracle.fwd(psi, x[0, c][None].abs(), abs_mode=True)[0].reshape(psi.K, -1)
+    assert normalised_error(dW[:, c, :], gy64[0] @ out.T, np.abs(gy64[0]) @ outa.T) <= TOL["bf16"]

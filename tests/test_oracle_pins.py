@@ -28,7 +28,8 @@ import pytest
 
 import oracle
 from disco_inputs import WORKLOADS, randn, workload_psi
-from disco_inputs.psi import (PsiCSR, basis_values, build_psi, equiangular_colatitudes, quadrature_weights,
+from disco_inputs.psi import (PsiCSR, basis_values, build_psi, equiangular_colatitudes, grid_colatitudes,
+                              grid_quadrature, quadrature_weights,
                               random_psi)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -50,15 +51,15 @@ def test_hand_worked_fixture():
     np.testing.assert_array_equal(oracle.fused(psi, x, W)[0], np.array(d["y"]))
 
 
-def _dense_operator(Hi, Wi, Ho, Wo, theta_c, n_r, n_a):
+def _dense_operator(Hi, Wi, Ho, Wo, theta_c, n_r, n_a, grid_in="equiangular", grid_out="equiangular"):
     """D[k, ho, wo, hi, wi]: basis evaluated at the true output longitude 2*pi*wo/Wo.
 
     The longitude difference is taken from the integer (wi - s*wo) mod Wi, so
     membership is decided exactly as in the CSR built for output longitude 0.
     """
     s = Wi // Wo
-    ti, to = equiangular_colatitudes(Hi), equiangular_colatitudes(Ho)
-    q = quadrature_weights(Hi, Wi)
+    ti, to = grid_colatitudes(grid_in, Hi), grid_colatitudes(grid_out, Ho)
+    q = grid_quadrature(grid_in, Hi, Wi)
     K = n_r * n_a
     D = np.zeros((K, Ho, Wo, Hi, Wi))
     wi = np.arange(Wi)
@@ -269,3 +270,25 @@ def test_fused_bwd_adjoint_identities(name):
     assert abs(lhs - float(np.sum(W.astype(np.float64) * dW))) <= 1e-13 * scale
     ngx, ndW = oracle.fused_bwd(psi, x, W, gy, abs_mode=True)
     assert np.all(ngx >= np.abs(gx)) and np.all(ndW >= np.abs(dW))
+
+
+
+@pytest.mark.parametrize("geom", [
+    (12, 24, 12, 24, 0.5, 3, 3, "legendre-gauss", "legendre-gauss"),
+    (13, 32, 8, 16, 0.6, 3, 3, "equiangular", "legendre-gauss"),
+])
+def test_dense_brute_force_legendre_gauss(geom):
+    """The page's benchmark grids: Gauss-Legendre latitudes (and equiangular -> Gauss-Legendre with
+    s = 2), three azimuthal factors; fwd, bwd and fused against the dense basis."""
+    Hi, Wi, Ho, Wo, tc, n_r, n_a, gi, go = geom
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a, gi, go)
+    D = _dense_operator(Hi, Wi, Ho, Wo, tc, n_r, n_a, gi, go)
+    x = randn((2, 3, Hi, Wi), 61).numpy()
+    g = randn((2, 3, psi.K, Ho, Wo), 62).numpy()
+    W = randn((4, 3, psi.K), 63).numpy()
+    ref_out = np.einsum("kowhv,bchv->bckow", D, x.astype(np.float64))
+    ref_gx = np.einsum("kowhv,bckow->bchv", D, g.astype(np.float64))
+    ref_y = np.einsum("ock,bckhw->bohw", W.astype(np.float64), ref_out)
+    assert np.abs(oracle.fwd(psi, x) - ref_out).max() <= 1e-12 * max(1.0, np.abs(ref_out).max())
+    assert np.abs(oracle.bwd(psi, g) - ref_gx).max() <= 1e-12 * max(1.0, np.abs(ref_gx).max())
+    assert np.abs(oracle.fused(psi, x, W) - ref_y).max() <= 1e-12 * max(1.0, np.abs(ref_y).max())

@@ -86,3 +86,28 @@ def test_workload_psi_invariants_and_nnz(name):
                     other = psi.row(m * w.n_a + a, ho)
                     np.testing.assert_array_equal(base[0], other[0])
                     np.testing.assert_array_equal(base[1], other[1])
+
+
+
+def test_legendre_gauss_grid_quadrature():
+    """Gauss-Legendre latitudes: the weights integrate polynomials in cos(theta) of degree < 2H
+    exactly; the sphere's area is 4 pi and the nodes are symmetric about the equator."""
+    from disco_inputs.psi import grid_colatitudes, grid_quadrature
+    for H, W in ((12, 24), (360, 720)):
+        th = grid_colatitudes("legendre-gauss", H)
+        q = grid_quadrature("legendre-gauss", H, W)
+        assert np.all(np.diff(th) > 0) and th[0] > 0 and th[-1] < np.pi
+        np.testing.assert_allclose(th + th[::-1], np.pi, atol=1e-12)
+        np.testing.assert_allclose(W * q.sum(), 4 * np.pi, rtol=1e-13)
+        # integral over the sphere of cos^2(theta) = 4 pi / 3
+        np.testing.assert_allclose(W * np.sum(q * np.cos(th) ** 2), 4 * np.pi / 3, rtol=1e-12)
+
+
+def test_page_benchmark_workloads():
+    from disco_inputs import WORKLOADS, workload_psi
+    for name in ("page_self_256x360x720", "page_down_80x721x1440"):
+        w = WORKLOADS[name]
+        p = workload_psi(w)
+        assert p.K == 9 and (p.Ho, p.Wo, p.Hi, p.Wi) == (w.Ho, w.Wo, w.Hi, w.Wi)
+        assert np.all(np.diff(p.row_ptr) > 0)  # every row sees some input at theta_c = 0.017
+        assert p.col_hi.min() >= 0 and p.col_hi.max() < p.Hi and p.col_wi.max() < p.Wi
