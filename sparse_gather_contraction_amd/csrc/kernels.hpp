@@ -154,6 +154,5 @@ hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipS
 // dW[o][col0 + m] = bf16(sum_{z < Z} P[z][o][m]), summed in increasing z.
 hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0,
                                   hipStream_t stream);
-int gemm_tile();  // rows and columns of one GEMM tile
 
 }  // namespace disco

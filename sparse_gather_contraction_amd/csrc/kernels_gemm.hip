@@ -28,12 +28,22 @@ namespace disco {
 
 namespace {
 
-constexpr int kGT = 128;                     // tile rows (and columns)
-constexpr int kGK = 32;                      // reduction chunk (elements)
-constexpr int kGThreads = 256;
-constexpr int kGOpBytes = kGT * kGK * 2;     // one operand chunk: 8 KiB
-constexpr int kGStage = 2 * kGOpBytes;       // A + B chunk
-constexpr int kGRing = 3;                    // chunks in flight + the one being multiplied
+constexpr int kGK = 32;      // reduction chunk (elements): 64 bytes per operand row
+constexpr int kGRing = 3;    // chunks in flight + the one being multiplied
+
+// Tile shapes: TM x TN outputs per workgroup of WM x WN waves, each wave (TM / WM) x (TN / WN).
+//   small: 128 x 128, 2 x 2 waves (64 x 64 each)
+//   large: 256 x 256, 2 x 4 waves (128 x 64 each): half the operand bytes per MFMA
+template <int TM_, int TN_, int WM_, int WN_>
+struct GTile {
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int FM = TM / WM / 32, FN = TN / WN / 32;  // 32 x 32 accumulators per wave
+    static constexpr int kABytes = TM * kGK * 2, kBBytes = TN * kGK * 2;
+    static constexpr int kStage = kABytes + kBBytes;
+};
+typedef GTile<128, 128, 2, 2> GSmall;
+typedef GTile<256, 256, 2, 4> GLarge;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -52,20 +62,22 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, v
 
 constexpr uint32_t kOob = 0x80000000u;  // beyond every buffer used here: the load returns zeros
 
-// One operand chunk: rows row0 .. row0+127 (valid below nrows), reduction indices k .. k+31
+// One operand chunk: rows row0 .. row0+ROWS-1 (valid below nrows), reduction indices k .. k+31
 // (valid below k_end; k and k_end are multiples of 8).  LDS slot u (16 bytes) holds row u / 4,
-// column group (u % 4) ^ ((row / 4) % 4).
+// column group (u % 4) ^ ((row / 4) % 4).  Every thread issues ROWS * 4 / THREADS loads.
+template <int ROWS, int THREADS>
 __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, int64_t ld, int row0, int nrows, int k, int k_end,
                                            unsigned char *dst, int tid, int wave)
 {
+    static_assert(ROWS * 4 % THREADS == 0, "whole loads per thread");
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int u = i * kGThreads + tid;
+    for (int i = 0; i < ROWS * 4 / THREADS; ++i) {
+        const int u = i * THREADS + tid;
         const int row = u >> 2;
         const int cg = (u & 3) ^ ((row >> 2) & 3);
         const int grow = row0 + row, kk = k + 8 * cg;
         const uint32_t voff = (grow < nrows && kk < k_end) ? (uint32_t)((grow * ld + kk) * 2) : kOob;
-        dma16(r, voff, dst + 16 * (i * kGThreads + wave * 64));
+        dma16(r, voff, dst + 16 * (i * THREADS + wave * 64));
     }
 }
 
@@ -78,79 +90,82 @@ __device__ __forceinline__ bf16x8 frag(const unsigned char *op, int row, int ks,
 
 // C[m][n] = sum_{k in [k_begin, k_end)} A[m][k] B[n][k]; the tile index selects the k range (split).
 // OUT_F32: fp32 partial [z][M][N]; else bf16 C with row stride ldc.
-template <bool OUT_F32>
-__global__ __launch_bounds__(kGThreads) void gemm_nt_kernel(const bf16_t *__restrict__ A, int64_t lda, int M,
-                                                            uint32_t a_bytes, const bf16_t *__restrict__ Bm,
-                                                            int64_t ldb, int N, uint32_t b_bytes, int Kd,
-                                                            int k_per_split, void *__restrict__ Cout, int64_t ldc,
-                                                            int nt_m, int nt_n, int total)
+template <typename T, bool OUT_F32>
+__global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__restrict__ A, int64_t lda, int M,
+                                                              uint32_t a_bytes, const bf16_t *__restrict__ Bm,
+                                                              int64_t ldb, int N, uint32_t b_bytes, int Kd,
+                                                              int k_per_split, void *__restrict__ Cout, int64_t ldc,
+                                                              int nt_m, int nt_n, int total)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kGRing * kGStage];
+    constexpr int FM = T::FM, FN = T::FN;
+    constexpr int LOADS = (T::TM + T::TN) * 4 / T::kThreads;  // direct loads per thread per chunk
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kGRing * T::kStage];
     const int per_xcd = (int)(gridDim.x >> 3);
     const int L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
     if (L >= total) return;
     const int tm = L % nt_m, tn = (L / nt_m) % nt_n, z = L / (nt_m * nt_n);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = tm * kGT, n0 = tn * kGT;
+    const int wm = wave % T::WM, wn = wave / T::WM;
+    const int m0 = tm * T::TM, n0 = tn * T::TN;
     const int k_begin = z * k_per_split;
     const int k_end = min(Kd, k_begin + k_per_split);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes), rb = make_rsrc(Bm, b_bytes);
 
-    f32x16 d[2][2];
+    f32x16 d[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int a = 0; a < 16; ++a) d[i][j][a] = 0.0f;
 
     const int nk = k_end > k_begin ? (k_end - k_begin + kGK - 1) / kGK : 0;
-    // chunk t lives in ring slot t % 3; each chunk is four direct loads per thread
+    // chunk t lives in ring slot t % 3
     auto issue = [&](int t) {
-        unsigned char *dst = smem + (t % kGRing) * kGStage;
+        unsigned char *dst = smem + (t % kGRing) * T::kStage;
         const int k = k_begin + t * kGK;
-        load_chunk(ra, lda, m0, M, k, k_end, dst, tid, wave);
-        load_chunk(rb, ldb, n0, N, k, k_end, dst + kGOpBytes, tid, wave);
+        load_chunk<T::TM, T::kThreads>(ra, lda, m0, M, k, k_end, dst, tid, wave);
+        load_chunk<T::TN, T::kThreads>(rb, ldb, n0, N, k, k_end, dst + T::kABytes, tid, wave);
     };
     if (nk > 0) issue(0);
     if (nk > 1) issue(1);
     const int r = lane & 31, h = lane >> 5;
     for (int t = 0; t < nk; ++t) {
         // this thread's loads of chunk t have landed (those of chunk t + 1 may still be in flight)
+        static_assert(LOADS == 4, "the wait below leaves one chunk of four loads in flight");
         if (t + 1 < nk)
             __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt <= 4, no wait on the other counters
         else
             __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // everyone's have; every wave is done with chunk t - 1, whose slot is refilled
         if (t + 2 < nk) issue(t + 2);
-        const unsigned char *cur = smem + (t % kGRing) * kGStage;
+        const unsigned char *cur = smem + (t % kGRing) * T::kStage;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 fa[2], fb[2];
+            bf16x8 fa[FM], fb[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = frag(cur, 64 * wm + 32 * i + r, ks, h);
+            for (int i = 0; i < FM; ++i) fa[i] = frag(cur, (T::TM / T::WM) * wm + 32 * i + r, ks, h);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = frag(cur + kGOpBytes, 64 * wn + 32 * j + r, ks, h);
+            for (int j = 0; j < FN; ++j) fb[j] = frag(cur + T::kABytes, (T::TN / T::WN) * wn + 32 * j + r, ks, h);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < FN; ++j)
                     d[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], d[i][j], 0, 0, 0);
         }
     }
 
     // lane (column r, half h) holds rows 8 (a / 4) + 4 h + a % 4 of each 32 x 32 accumulator
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + 64 * wn + 32 * j + r;
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + (T::TN / T::WN) * wn + 32 * j + r;
             if (n >= N) continue;
 #pragma unroll
             for (int a = 0; a < 16; ++a) {
-                const int m = m0 + 64 * wm + 32 * i + 8 * (a >> 2) + 4 * h + (a & 3);
+                const int m = m0 + (T::TM / T::WM) * wm + 32 * i + 8 * (a >> 2) + 4 * h + (a & 3);
                 if (m >= M) continue;
                 if constexpr (OUT_F32)
                     reinterpret_cast<float *>(Cout)[((int64_t)z * M + m) * N + n] = d[i][j][a];
@@ -191,26 +206,34 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
     dW[(int64_t)o * ldw + col0 + m] = f32_to_bf16(acc);
 }
 
+template <typename T>
+hipError_t launch_gemm_tiles(const GemmNtLaunch &g, hipStream_t stream)
+{
+    const int splits = (g.out_f32 && g.k_per_split > 0) ? (g.Kd + g.k_per_split - 1) / g.k_per_split : 1;
+    const int kps = g.k_per_split > 0 ? g.k_per_split : g.Kd;
+    const int nt_m = (g.M + T::TM - 1) / T::TM, nt_n = (g.N + T::TN - 1) / T::TN;
+    const int64_t total = (int64_t)nt_m * nt_n * splits;
+    if (total >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));  // a multiple of the eight XCDs
+    if (g.out_f32)
+        hipLaunchKernelGGL((gemm_nt_kernel<T, true>), grid, dim3(T::kThreads), 0, stream, (const bf16_t *)g.A, g.lda,
+                           g.M, g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m,
+                           nt_n, (int)total);
+    else
+        hipLaunchKernelGGL((gemm_nt_kernel<T, false>), grid, dim3(T::kThreads), 0, stream, (const bf16_t *)g.A, g.lda,
+                           g.M, g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m,
+                           nt_n, (int)total);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const int splits = (g.out_f32 && g.k_per_split > 0) ? (g.Kd + g.k_per_split - 1) / g.k_per_split : 1;
-    const int kps = g.k_per_split > 0 ? g.k_per_split : g.Kd;
-    const int nt_m = (g.M + kGT - 1) / kGT, nt_n = (g.N + kGT - 1) / kGT;
-    const int64_t total = (int64_t)nt_m * nt_n * splits;
-    if (total >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((total + 7) / 8 * 8));  // a multiple of the eight XCDs
-    if (g.out_f32)
-        hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGThreads), 0, stream, (const bf16_t *)g.A, g.lda, g.M,
-                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m, nt_n,
-                           (int)total);
-    else
-        hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kGThreads), 0, stream, (const bf16_t *)g.A, g.lda, g.M,
-                           g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m, nt_n,
-                           (int)total);
-    return hipGetLastError();
+    // the large tile when both output dimensions fill it
+    if (g.M >= 256 && g.N >= 256) return launch_gemm_tiles<GLarge>(g, stream);
+    return launch_gemm_tiles<GSmall>(g, stream);
 }
 
 hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream)
@@ -231,6 +254,5 @@ hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *d
     return hipGetLastError();
 }
 
-int gemm_tile() { return kGT; }
 
 }  // namespace disco
