@@ -372,19 +372,20 @@ __device__ __forceinline__ void zero(f32x16 (&d)[2])
 template <bool F16>
 __device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d)[2], int t, int pp, int h2)
 {
+    // with the basis order above, register a holds basis k = 8 hh + a % 8 of phase 2 pp + a / 8
     const int r = c.lane & 31, hh = c.lane >> 5;
+    const int64_t HoL = (int64_t)c.Ho * c.L;
+    const int wo0 = c.px0 + 8 * r + 2 * pp;
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl) {
         const int ch = kCh * t + 2 * h2 + cl;
         if (ch >= c.C) continue;
-        bf16_t *plane = c.out + (int64_t)c.b * c.out_bstride + (int64_t)ch * c.K * c.Ho * c.L;
+        bf16_t *base = c.out + (int64_t)c.b * c.out_bstride + (int64_t)ch * c.K * HoL + (int64_t)(8 * hh) * HoL +
+                       (int64_t)c.ho * c.L + wo0;
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
-            const int row = 8 * (a >> 2) + 4 * hh + (a & 3);
-            const int m = row & 15;
-            const int k = (m < 8) ? 8 * (m >> 2) + (m & 3) : 8 * ((m - 8) >> 2) + 4 + (m & 3);
-            const int wo = c.px0 + 8 * r + 2 * pp + (row >> 4);
-            if (k < c.K && wo < c.L) plane[((int64_t)k * c.Ho + c.ho) * c.L + wo] = (bf16_t)to16<F16>(d[cl][a], c.scale);
+            const int k = 8 * hh + (a & 7), ph = a >> 3;
+            if (k < c.K && wo0 + ph < c.L) base[(a & 7) * HoL + ph] = (bf16_t)to16<F16>(d[cl][a], c.scale);
         }
     }
 }
