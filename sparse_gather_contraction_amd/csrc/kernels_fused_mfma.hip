@@ -65,22 +65,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)l, 16, voff, 0, 0, 0);
 }
 
-// Eight bf16 at p[0], p[16], ..., p[112] (psi column of one basis function).
-__device__ __forceinline__ bf16x8 lds_col8(const bf16_t *p)
-{
-    const __bf16 *q = reinterpret_cast<const __bf16 *>(p);
-    bf16x8 v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = q[16 * i];
-    return v;
-}
-
-__device__ __forceinline__ int mod_l(int g, int L)
-{
-    g %= L;
-    return g < 0 ? g + L : g;
-}
-
 struct Ctx {
     const bf16_t *x, *W;
     __amdgpu_buffer_rsrc_t descs_rs, adata_rs, w_rs;
