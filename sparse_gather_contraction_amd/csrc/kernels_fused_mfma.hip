@@ -73,6 +73,7 @@ struct Ctx {
     int64_t plane_sz;
     int64_t x_bstride;  // elements between batches of x (C planes when contiguous)
     bool vec_x, vec_w;
+    bool vec_out;  // contraction-only mode: output rows are 16-byte aligned (L, strides multiples of 8)
     float scale;  // contraction result scale: 2^-e for fp16 psi, 1 for bf16
     // contraction-only mode: out[b, c, k, ho, wo] at out + b * out_bstride
     bf16_t *out;
@@ -350,26 +351,38 @@ __device__ __forceinline__ void zero(f32x16 (&d)[2])
 // chunk start), contract, and run the einsum at the chunk's last piece (the consumed stage
 // buffer then carries the operand exchange).  The buffers are restrict parameters so that the
 // compiler keeps the queued direct loads in flight across the LDS reads of the current stage.
-// Contraction-only mode: write the chunk's contraction result (channels kCh t + 2 h2 + cl) from the
-// accumulators.  Register a of lane (n, hh) is MFMA row 8 (a / 4) + 4 hh + a % 4: phase 2 pp + row / 16,
-// basis kb(row % 16) in the order the psi rows were read.
+// Contraction-only mode: the chunk's contraction result (channels kCh t + 2 h2 + cl) goes through
+// an LDS tile [channel][basis][256 longitudes] (the 32 KiB the fused op keeps for its W slice), so
+// that each output row leaves as 16-byte stores rather than 2-byte stores 16 bytes apart.  With the
+// basis order the psi rows were read in, register a of lane (n, hh) holds basis k = 8 hh + a % 8 of
+// phase 2 pp + a / 8; registers a and a + 8 are neighbouring longitudes and share one LDS word.
+// The tile is reused at the next chunk only after that chunk's opening barrier.
 template <bool F16>
-__device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d)[2], int t, int pp, int h2)
+__device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d)[2], int t, int pp, int h2,
+                                                  unsigned char *__restrict__ tile_bytes)
 {
-    // with the basis order above, register a holds basis k = 8 hh + a % 8 of phase 2 pp + a / 8
     const int r = c.lane & 31, hh = c.lane >> 5;
+    uint32_t *tile32 = reinterpret_cast<uint32_t *>(tile_bytes);
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = (uint16_t)to16<F16>(d[cl][j], c.scale), hi = (uint16_t)to16<F16>(d[cl][j + 8], c.scale);
+            tile32[(((2 * h2 + cl) * 16 + 8 * hh + j) * 256 + 8 * r + 2 * pp) >> 1] = lo | (hi << 16);
+        }
+    __syncthreads();
+    const bf16_t *tile = reinterpret_cast<const bf16_t *>(tile_bytes);
     const int64_t HoL = (int64_t)c.Ho * c.L;
-    const int wo0 = c.px0 + 8 * r + 2 * pp;
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl) {
-        const int ch = kCh * t + 2 * h2 + cl;
-        if (ch >= c.C) continue;
-        bf16_t *base = c.out + (int64_t)c.b * c.out_bstride + (int64_t)ch * c.K * HoL + (int64_t)(8 * hh) * HoL +
-                       (int64_t)c.ho * c.L + wo0;
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-            const int k = 8 * hh + (a & 7), ph = a >> 3;
-            if (k < c.K && wo0 + ph < c.L) base[(a & 7) * HoL + ph] = (bf16_t)to16<F16>(d[cl][a], c.scale);
+    for (int u = c.tid; u < kCh * 16 * 32; u += kThreads) {
+        const int seg = u & 31, row = u >> 5, k = row & 15, ch = kCh * t + (row >> 4);
+        const int wo = c.px0 + 8 * seg;
+        if (k >= c.K || ch >= c.C || wo >= c.L) continue;
+        bf16_t *dst = c.out + (int64_t)c.b * c.out_bstride + ((int64_t)ch * c.K + k) * HoL + (int64_t)c.ho * c.L + wo;
+        const bf16_t *src = tile + row * 256 + 8 * seg;
+        if (c.vec_out && wo + 8 <= c.L) {
+            *reinterpret_cast<i16x8 *>(dst) = *reinterpret_cast<const i16x8 *>(src);
+        } else {
+            for (int e = 0; e < 8 && wo + e < c.L; ++e) dst[e] = src[e];
         }
     }
 }
@@ -398,7 +411,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
             __syncthreads();  // W slice visible; `cur` free for the exchange
             einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
         } else {
-            store_contraction<F16>(c, d, t, pp, h2);
+            store_contraction<F16>(c, d, t, pp, h2, wb);
         }
     }
 }
@@ -423,7 +436,7 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
         __syncthreads();  // W slice visible; `cur` free for the exchange
         einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
     } else {
-        store_contraction<F16>(c, d, t, pp, h2);
+        store_contraction<F16>(c, d, t, pp, h2, wb);
     }
 }
 
@@ -436,11 +449,12 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, float scale, int64_t x_bstride,
     int64_t out_bstride)
 {
+    // vec_w: the fused op reads W rows as 16-byte runs; contraction-only mode: output rows are 16-byte aligned
     constexpr int NOTH = NOT / 2;
-    // LDS: [W slice: NOT * kCh KiB] [stage buffer 0] [stage buffer 1]
+    // LDS: [W slice: NOT * kCh KiB; contraction-only: the 32 KiB output tile] [stage buffer 0] [stage buffer 1]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *wb = smem;
-    unsigned char *buf0 = smem + NOT * kCh * 1024;
+    unsigned char *buf0 = smem + (EIN ? NOT * kCh * 1024 : kWBytes);
     unsigned char *buf1 = buf0 + buf_bytes;
 
     int bid = blockIdx.x;
@@ -454,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.x = x; c.W = W; c.rows = rows;
     c.descs_rs = make_rsrc(descs, desc_bytes);
     c.adata_rs = make_rsrc(adata, adata_bytes);
-    c.w_rs = make_rsrc(W, vec_w ? (uint32_t)(2 * (int64_t)Co * C * 16) : 0u);
+    c.w_rs = make_rsrc(W, EIN && vec_w ? (uint32_t)(2 * (int64_t)Co * C * 16) : 0u);
     c.B = B; c.C = C; c.Co = Co; c.K = K; c.L = L; c.Wi = Wi; c.s = s; c.n_ot = NOT;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
@@ -464,7 +478,8 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.plane_sz = (int64_t)Hi * Wi;
     c.x_bstride = x_bstride;
     c.vec_x = vec_x != 0;
-    c.vec_w = vec_w != 0;
+    c.vec_w = EIN && vec_w != 0;
+    c.vec_out = !EIN && vec_w != 0;
     c.scale = scale;
     c.out = y;
     c.out_bstride = out_bstride;
@@ -579,9 +594,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const FRow *__restrict__ rows, const int32_t *__restrict__ descs, const bf16_t *__restrict__ adata,
     const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order, int B, int C, int K, int Ho, int L,
     int Hi, int Wi, int s, int n_pxb, int n_cb, int buf_bytes, uint32_t desc_bytes, uint32_t adata_bytes, int vec_x,
-    OutMap om, float scale, int64_t x_bstride, int64_t out_bstride)
+    OutMap om, float scale, int64_t x_bstride, int64_t out_bstride, int vec_out)
 {
+    // vec_out: output rows start 16-byte aligned (row length, plane and batch strides multiples of 8)
     constexpr int PH = 32 / KR, NG = 8 / PH, WPG = kWaves / NG, FCH = 2 * WPG;
+    static_assert(FCH * KR * 256 * 2 == 32768, "the epilogue tile is 32 KiB");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     unsigned char *buf0 = smem;
     unsigned char *buf1 = smem + buf_bytes;
@@ -608,6 +625,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     c.x_bstride = x_bstride;
     c.vec_x = vec_x != 0;
     c.vec_w = false;
+    c.vec_out = false;
     c.scale = scale;
 
     // lane constants: A row r = lane % 32 is (phase PH g + r / KR, basis k = r % KR)
@@ -633,6 +651,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 
     // ---- epilogue: register a of lane (n = r, hh) is row 8 (a / 4) + 4 hh + a % 4 = (phase, k) ----
+    // The block's result goes through an LDS tile so that output rows leave as 16-byte stores.  Forward
+    // layout: tile [channel][k][256 longitudes], row (c, k) is out[b, c, k, ho, px0 ...].  Gradient
+    // layout: the KR rows of group ho are input rows hi = (ho KR + k) / s with residue (ho KR + k) % s
+    // at longitude s wo + residue, so the tile is [channel][KR / s][s 256] and row (c, j) is
+    // gx[b, c, ho KR / s + j, s px0 ...]; this needs KR % s == 0, else the 2-byte stores below.
+    const int sr = om.inverse ? om.s : 1;
+    if (sr > 0 && KR % sr == 0) {
+        __syncthreads();  // every wave is done with the stage buffers
+        bf16_t *tile = reinterpret_cast<bf16_t *>(smem);
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const int row = 8 * (a >> 2) + 4 * hh + (a & 3);
+                const int k = row % KR, wl = 8 * r + PH * g + row / KR;
+                tile[((2 * cp + cl) * KR + k - k % sr) * 256 + sr * wl + k % sr] = (bf16_t)to16<F16>(d[cl][a], scale);
+            }
+        __syncthreads();
+        const int row_len = om.inverse ? om.wi : L;  // elements of an output row
+        const int seg_per_row = 32 * sr, rows_per_ch = KR / sr;
+        for (int u = c.tid; u < FCH * KR * 32; u += kThreads) {
+            const int ch_l = u / (KR * 32), v = u - ch_l * (KR * 32);
+            const int j = v / seg_per_row, seg = v - j * seg_per_row;
+            const int cc = c0 + ch_l;
+            const int pos = sr * c.px0 + 8 * seg;  // first element of the segment within its output row
+            if (cc >= C || pos >= row_len) continue;
+            int64_t row_off;
+            if (om.inverse) {
+                const int rr = ho * KR + j * sr;  // first of the sr rows that share input row rr / sr
+                if (rr >= om.rows) continue;
+                row_off = (int64_t)(rr / sr) * om.wi;
+            } else {
+                if (j >= K) continue;
+                row_off = ((int64_t)j * Ho + ho) * L;
+            }
+            bf16_t *dst = out + (int64_t)c.b * out_bstride + (int64_t)cc * om.plane + row_off + pos;
+            const bf16_t *src = tile + (ch_l * rows_per_ch + j) * (256 * sr) + 8 * seg;
+            if (vec_out && pos + 8 <= row_len) {
+                *reinterpret_cast<i16x8 *>(dst) = *reinterpret_cast<const i16x8 *>(src);
+            } else {
+                for (int e = 0; e < 8 && pos + e < row_len; ++e) dst[e] = src[e];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int cl = 0; cl < 2; ++cl) {
         const int cc = c0 + 2 * cp + cl;
@@ -670,7 +733,7 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
     const int n_pxb = (a.Wo + kFusedSpan - 1) / kFusedSpan;
     const int n_cb = (a.C + fch - 1) / fch;
     const int buf_bytes = (a.max_piece_bytes + 15) & ~15;
-    const size_t lds = 2 * (size_t)buf_bytes;
+    const size_t lds = std::max<size_t>(2 * (size_t)buf_bytes, 32768);  // stage buffers; the epilogue's tile
     const void *fn = a.kr == 8 ? (a.f16 ? (const void *)fwd_mfma_kernel<8, true> : (const void *)fwd_mfma_kernel<8, false>)
                                : (a.f16 ? (const void *)fwd_mfma_kernel<16, true> : (const void *)fwd_mfma_kernel<16, false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -681,11 +744,13 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
                           (int64_t)a.Hi * a.Wi * 2 * fch < ((int64_t)1 << 31);
     const int vec_x = planes16 && (x_bs % 8) == 0 ? 1 : 0;
+    const int64_t row_len = a.om.inverse ? a.om.wi : a.Wo;
+    const int vec_out = (row_len % 8 == 0 && a.om.plane % 8 == 0 && out_bs % 8 == 0 && ((uintptr_t)a.out % 16) == 0) ? 1 : 0;
 #define DISCO_FWD_LAUNCH(KR, F16)                                                                                   \
     hipLaunchKernelGGL((fwd_mfma_kernel<KR, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,             \
                        (const bf16_t *)a.x, (bf16_t *)a.out, a.pieces, a.rows, a.descs, (const bf16_t *)a.adata,       \
                        a.ho_piece, a.ho_order, a.B, a.C, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.s, n_pxb, n_cb, buf_bytes,    \
-                       a.desc_bytes, a.adata_bytes, vec_x, a.om, a.scale, x_bs, out_bs)
+                       a.desc_bytes, a.adata_bytes, vec_x, a.om, a.scale, x_bs, out_bs, vec_out)
     if (a.kr == 8) {
         if (a.f16) DISCO_FWD_LAUNCH(8, true);
         else DISCO_FWD_LAUNCH(8, false);
@@ -702,7 +767,7 @@ hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t strea
     if (a.B == 0 || a.C == 0) return hipSuccess;
     const int n_pxb = (a.Wo + kFusedSpan - 1) / kFusedSpan;
     const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
-    const size_t lds = fused_mfma_lds_bytes(2, a.max_piece_bytes, a.max_resident_bytes);
+    const size_t lds = fused_mfma_lds_bytes(kMaxOt, a.max_piece_bytes, a.max_resident_bytes);  // 32 KiB output tile
     const void *fn = a.f16 ? (const void *)fused_mfma_kernel<2, true, false> : (const void *)fused_mfma_kernel<2, false, false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -712,11 +777,12 @@ hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t strea
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
                           x_bs % 8 == 0 && (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
     const int vec_x = planes16 ? 1 : 0;
+    const int vec_out = (a.Wo % 8 == 0 && out_bs % 8 == 0 && ((uintptr_t)a.out % 16) == 0) ? 1 : 0;
 #define DISCO_CONTRACT_LAUNCH(F16)                                                                               \
     hipLaunchKernelGGL((fused_mfma_kernel<2, F16, false>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,      \
                        (const bf16_t *)a.x, (const bf16_t *)nullptr, (bf16_t *)a.out, a.pieces, a.rows, a.descs,      \
                        (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, 0, a.K, a.Ho, a.Wo, a.Hi, a.Wi,     \
-                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, 0, a.scale, x_bs, out_bs)
+                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_out, a.scale, x_bs, out_bs)
     if (a.f16) DISCO_CONTRACT_LAUNCH(true);
     else DISCO_CONTRACT_LAUNCH(false);
 #undef DISCO_CONTRACT_LAUNCH
