@@ -446,10 +446,10 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const FPiece *__restrict__ pieces, const FRow *__restrict__ rows, const int32_t *__restrict__ descs,
     const bf16_t *__restrict__ adata, const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order,
     int B, int C, int Co, int K, int Ho, int L, int Hi, int Wi, int s, int n_pxb, int n_ob, int buf_bytes,
-    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, float scale, int64_t x_bstride,
+    uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, int vec_out, float scale, int64_t x_bstride,
     int64_t out_bstride)
 {
-    // vec_w: the fused op reads W rows as 16-byte runs; contraction-only mode: output rows are 16-byte aligned
+    // vec_w: W rows load as 16-byte runs; vec_out: output rows (y, or out in contraction-only mode) start 16-byte aligned
     constexpr int NOTH = NOT / 2;
     // LDS: [W slice: NOT * kCh KiB; contraction-only: the 32 KiB output tile] [stage buffer 0] [stage buffer 1]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.x = x; c.W = W; c.rows = rows;
     c.descs_rs = make_rsrc(descs, desc_bytes);
     c.adata_rs = make_rsrc(adata, adata_bytes);
-    c.w_rs = make_rsrc(W, EIN && vec_w ? (uint32_t)(2 * (int64_t)Co * C * 16) : 0u);
+    c.w_rs = make_rsrc(W, vec_w ? (uint32_t)(2 * (int64_t)Co * C * 16) : 0u);
     c.B = B; c.C = C; c.Co = Co; c.K = K; c.L = L; c.Wi = Wi; c.s = s; c.n_ot = NOT;
     c.tid = threadIdx.x;
     c.lane = c.tid & 63;
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.x_bstride = x_bstride;
     c.vec_x = vec_x != 0;
     c.vec_w = EIN && vec_w != 0;
-    c.vec_out = !EIN && vec_w != 0;
+    c.vec_out = vec_out != 0;
     c.scale = scale;
     c.out = y;
     c.out_bstride = out_bstride;
@@ -547,19 +547,33 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         }
     }
 
-    // ---- epilogue: yacc[ph][j] row = output channel, column n = longitude px0 + 8n + 2 pp + ph ----
+    // ---- epilogue: yacc[ph][j] row = output channel (h2 NOTH + j) 32 + 8 (a / 4) + 4 hh + a % 4, column
+    // n = longitude px0 + 8n + 2 pp + ph.  Pass j writes the 64 channels of tile j of both wave halves
+    // through a 32 KiB LDS tile [channel][256 longitudes] (stage buffer space, free once the last chunk
+    // is done), so that output rows leave as 16-byte stores; the two phases of a register share a word.
     if constexpr (!EIN) return;
+    uint32_t *tile32 = reinterpret_cast<uint32_t *>(buf0);
+    const bf16_t *tile = reinterpret_cast<const bf16_t *>(buf0);
 #pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-        const int wo = c.px0 + 8 * r + 2 * pp + ph;
-        if (wo < L) {
+    for (int j = 0; j < NOTH; ++j) {
+        __syncthreads();  // the last chunk (or the previous pass) is done with the tile's space
 #pragma unroll
-            for (int j = 0; j < NOTH; ++j) {
-#pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int o = c.o_base + (h2 * NOTH + j) * 32 + 8 * (a >> 2) + 4 * hh + (a & 3);
-                    if (o < Co) y[(((int64_t)c.b * Co + o) * Ho + ho) * L + wo] = (bf16_t)to16<F16>(yacc[ph][j][a], 1.0f);
-                }
+        for (int a = 0; a < 16; ++a) {
+            const int ol = 32 * h2 + 8 * (a >> 2) + 4 * hh + (a & 3);
+            const uint32_t lo = (uint16_t)to16<F16>(yacc[0][j][a], 1.0f), hi = (uint16_t)to16<F16>(yacc[1][j][a], 1.0f);
+            tile32[(ol * 256 + 8 * r + 2 * pp) >> 1] = lo | (hi << 16);
+        }
+        __syncthreads();
+        for (int u = c.tid; u < 64 * 32; u += kThreads) {
+            const int seg = u & 31, ol = u >> 5;
+            const int o = c.o_base + ((ol >> 5) * NOTH + j) * 32 + (ol & 31), wo = c.px0 + 8 * seg;
+            if (o >= Co || wo >= L) continue;
+            bf16_t *dst = y + (((int64_t)c.b * Co + o) * Ho + ho) * L + wo;
+            const bf16_t *src = tile + ol * 256 + 8 * seg;
+            if (c.vec_out && wo + 8 <= L) {
+                *reinterpret_cast<i16x8 *>(dst) = *reinterpret_cast<const i16x8 *>(src);
+            } else {
+                for (int e = 0; e < 8 && wo + e < L; ++e) dst[e] = src[e];
             }
         }
     }
@@ -782,7 +796,7 @@ hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t strea
     hipLaunchKernelGGL((fused_mfma_kernel<2, F16, false>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,      \
                        (const bf16_t *)a.x, (const bf16_t *)nullptr, (bf16_t *)a.out, a.pieces, a.rows, a.descs,      \
                        (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, 0, a.K, a.Ho, a.Wo, a.Hi, a.Wi,     \
-                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_out, a.scale, x_bs, out_bs)
+                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, 0, vec_out, a.scale, x_bs, out_bs)
     if (a.f16) DISCO_CONTRACT_LAUNCH(true);
     else DISCO_CONTRACT_LAUNCH(false);
 #undef DISCO_CONTRACT_LAUNCH
@@ -822,12 +836,13 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
                           (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
     const int vec_x = planes16 ? 1 : 0;
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
+    const int vec_y = (a.Wo % 8 == 0 && ((uintptr_t)a.y % 16) == 0) ? 1 : 0;
     const int64_t x_bs = (int64_t)a.C * a.Hi * a.Wi;
 #define DISCO_FUSED_LAUNCH(N, F16)                                                                               \
     hipLaunchKernelGGL((fused_mfma_kernel<N, F16, true>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,       \
                        (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.descs,            \
                        (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi,  \
-                       a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, a.scale, x_bs,         \
+                       a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, vec_y, a.scale, x_bs,  \
                        (int64_t)0)
     if (a.f16) {
         switch (n_ot) {
