@@ -55,6 +55,8 @@ def main():
     ap.add_argument("--ops", default="fwd,bwd,fused", help="subset of ops in the step (profiling runs)")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the separate timing of the fused-convolution backward")
+    ap.add_argument("--no-einsum", action="store_true",
+                    help="skip the timing of the fused op's einsum alone")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -179,6 +181,10 @@ def main():
         nxt["f16"] = time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream)
         nxt["page_shapes"] = time_page_shapes(sgc, torch, np, dev, stream)
 
+    ein = None
+    if not args.no_einsum and "fused" in ops:
+        ein = time_einsum(sgc, torch, np, wu, tensors, dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wf, wb, wu, psi_fb, psi_u)
@@ -202,6 +208,7 @@ def main():
         "per_op": per,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "einsum_standalone": ein,
         "next_rows": nxt,
     }
     print(json.dumps(line), flush=True)
@@ -231,6 +238,44 @@ def counter_traffic(op):
                     return int(rec["read_bytes"] + rec["write_bytes"])
     return None
 
+
+
+def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
+    """The fused op's einsum alone at its GEMM shape (M = Co = 256, K = C*K = 4096, N = B*Ho*Wo =
+    2,076,480): disco_einsum on the fused kernel's matrix-core einsum tile, with the contraction
+    t (B, C, K, Ho, Wo) staged in device memory as bf16 (a seeded device draw, 17 GB: far beyond
+    the caches, so every tile comes from HBM).  Timed apart from the step (not part of `value`)."""
+    from disco_inputs import randn_device
+
+    t = randn_device((w.B, w.C, w.K, w.Ho, w.Wo), 3500, "bf16", dev)
+    W = tensors["W5"]
+    y = torch.empty((w.B, w.Co, w.Ho, w.Wo), dtype=torch.bfloat16, device=dev)
+    for _ in range(warm):
+        sgc.disco_einsum(W, t, y)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sgc.disco_einsum(W, t, y)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    macs = w.B * w.Ho * w.Wo * w.Co * w.C * w.K
+    byt = 2 * (t.numel() + W.numel() + y.numel())
+    del t, y
+    torch.cuda.empty_cache()
+    res = {"ms": round(ms, 4), "macs": macs, "bound": "mfma",
+           "mfma_tflops": round(2 * macs / ms / 1e9, 3),
+           "mfma_frac": round(2 * macs / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
+           "bytes": byt, "GBps": round(byt / ms / 1e6, 2), "hbm_frac": round(byt / ms / 1e6 / PEAK_HBM_GBS, 4),
+           "gemm_mkn": [w.Co, w.C * w.K, w.B * w.Ho * w.Wo],
+           "operand": "bf16 contraction (2,256,16,721,1440) in HBM, W (256,256,16), y (2,256,721,1440)"}
+    print(f"[bench] einsum alone: {ms:.3f} ms ({res['mfma_tflops']} TFLOP/s, {res['GBps']} GB/s)",
+          file=sys.stderr, flush=True)
+    return res
 
 def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=3):
     """Backward of the fused convolution on the fused workload (gradient gy ~ N(0,1), bf16), timed

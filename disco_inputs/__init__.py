@@ -99,6 +99,18 @@ def randn(shape, seed: int, dtype: str = "f32", std: float = 1.0):
     return t
 
 
+
+def randn_device(shape, seed: int, dtype: str, device):
+    """N(0, 1) draw from a seeded torch generator on `device`, in bf16 or fp16 (for operands too
+    large to draw on the host, such as a full-size contraction (B, C, K, Ho, Wo)).  Deterministic
+    for a given device type and seed; a test copies the part it checks back to the host."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return torch.randn(tuple(int(s) for s in shape), generator=g, dtype=tdt, device=device)
+
 def workload_x(w: Workload):
     return randn((w.B, w.C, w.Hi, w.Wi), w.x_seed, w.dtype)
 

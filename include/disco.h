@@ -118,6 +118,16 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
 
+/* The einsum alone: the second half of the fused convolution, for a contraction that is already
+ * in device memory (for instance the forward's output kept for the weight gradient).  Same page,
+ * "Architecture snapshot" ("contraction + einsum"):
+ *   y[b,o,ho,wo] = sum_{c,k} W[o,c,k] * t[b,c,k,ho,wo]
+ * t: (B, C, K, Ho, Wo), W: (Co, C, K) -> y: (B, Co, Ho, Wo), on the current device (no psi).
+ * BF16 and F16 only, K <= 16 (DISCO_ERR_SHAPE otherwise).  Runs the fused kernel's matrix-core
+ * einsum tile with t streamed from device memory: fp32 accumulation in a fixed order, y rounded
+ * once (RNE), bitwise reproducible run to run.  All tensors are caller-owned; y is overwritten. */
+disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_tensor *y, void *stream);
+
 /* Backward of the fused convolution: the gradients of <gy, y> for y = disco_fused_conv(x, W),
  *   gx[b,c]   = F^T g[b,c],  g[b,c,k,ho,wo] = sum_o W[o,c,k] * gy[b,o,ho,wo]
  *   dW[o,c,k] = sum_{b,ho,wo} gy[b,o,ho,wo] * out[b,c,k,ho,wo],  out = F x

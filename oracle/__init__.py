@@ -45,6 +45,7 @@ def _load():
         lib.oracle_fwd.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, i32]
         lib.oracle_bwd.argtypes = [i64, i32, i32, i32, i32, i32, P, P, P, P, P, P, i32]
         lib.oracle_fused.argtypes = [i32] * 8 + [P] * 6 + [i32, P, P, i32]
+        lib.oracle_einsum.argtypes = [i32, i32, i32, i32, i64, P, P, P, i32]
         lib.oracle_fused_bwd.argtypes = [i32] * 8 + [P] * 7 + [P, P, i32]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -121,6 +122,24 @@ def fused(psi, x, W, ho_list=None, abs_mode: bool = False) -> np.ndarray:
                      hl.size, hl_p, y.ctypes.data_as(ctypes.c_void_p), int(abs_mode))
     return y
 
+
+def einsum(W, t, abs_mode: bool = False) -> np.ndarray:
+    """y[b, o, ...] in fp64 for a contraction t [B, C, K, ...] (fp64, or fp32/bf16/fp16 widened
+    exactly) and W [Co, C, K]: the fused convolution's einsum alone."""
+    lib = _load()
+    if hasattr(t, "detach"):
+        t = t.detach().cpu().double().numpy()
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    W = _np_f32(W)
+    B, C, K = t.shape[:3]
+    Co = W.shape[0]
+    assert W.shape == (Co, C, K)
+    pos = t.shape[3:]
+    P = int(np.prod(pos)) if pos else 1
+    y = np.empty((B, Co) + pos, dtype=np.float64)
+    lib.oracle_einsum(B, C, Co, K, P, W.ctypes.data_as(ctypes.c_void_p), t.ctypes.data_as(ctypes.c_void_p),
+                      y.ctypes.data_as(ctypes.c_void_p), int(abs_mode))
+    return y
 
 def fused_bwd(psi, x, W, gy, abs_mode: bool = False):
     """(gx [B, C, Hi, Wi], dW [Co, C, K]) in fp64: the gradients of <gy, y> for the fused op."""

@@ -35,11 +35,16 @@
  *   gx[b,c]         = F^T g[b,c]                        (scatter form, as bwd)
  *   dW[o,c,k]       = sum_{b,ho,wo} gy[b,o,ho,wo] * out[b,c,k,ho,wo],  out = F x
  *
- * Parity status: fwd, bwd, fused and fused_bwd are each pinned by independent
+ * einsum: the fused convolution's second half alone, y[b,o,p] = sum_{c,k} W[o,c,k] * t[b,c,k,p]
+ * for a contraction t given as input (p an output position).
+ *
+ * Parity status: fwd, bwd, fused, einsum and fused_bwd are each pinned by independent
  * checks in the CPU test suite (dense brute force, constant field,
  * equivariance, adjoint, FFT correlation, strided-subsample matmul, hand-worked
  * fixture; for fused_bwd: directional derivatives of the fused oracle and the
- * adjoint identities <gy, y> = <x, gx> = <W, dW>).
+ * adjoint identities <gy, y> = <x, gx> = <W, dW>; for einsum: einsum of the forward oracle
+ * reproduces the fused oracle bitwise, the hand-worked fixture, and K = 1 reduces to a numpy
+ * matrix product).
  */
 #include <math.h>
 #include <stdint.h>
@@ -154,6 +159,28 @@ void oracle_fused(int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
         }
     }
     free(t);
+}
+
+/* The einsum alone (the second half of the fused convolution, for a contraction given as input):
+ * t: [B, C, K, P] double (P output positions), W: [Co, C, K] fp32 -> y: [B, Co, P] double.
+ * Summed over c, then k, in the order oracle_fused uses, so that einsum(W, fwd(x)) reproduces
+ * oracle_fused(x, W). */
+void oracle_einsum(int B, int C, int Co, int K, int64_t P, const float *W, const double *t, double *y, int abs_mode)
+{
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        for (int o = 0; o < Co; ++o) {
+            double *yo = y + ((int64_t)b * Co + o) * P;
+            for (int64_t p = 0; p < P; ++p) yo[p] = 0.0;
+            for (int c = 0; c < C; ++c) {
+                for (int k = 0; k < K; ++k) {
+                    const double wv = opnd((double)W[((int64_t)o * C + c) * K + k], abs_mode);
+                    const double *tk = t + (((int64_t)b * C + c) * K + k) * P;
+                    for (int64_t p = 0; p < P; ++p) yo[p] += wv * opnd(tk[p], abs_mode);
+                }
+            }
+        }
+    }
 }
 
 /* Backward of the fused convolution over all output latitudes.

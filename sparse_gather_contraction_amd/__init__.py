@@ -37,7 +37,7 @@ DISCO_F32 = 0
 DISCO_BF16 = 1
 DISCO_F16 = 2
 EXPORTED = ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
-            "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd", "disco_last_error")
+            "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd", "disco_last_error")
 
 
 class DiscoError(RuntimeError):
@@ -75,12 +75,13 @@ def load_library():
         lib.disco_bwd.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(TensorDesc), P]
         lib.disco_fused_conv.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(TensorDesc),
                                          ctypes.POINTER(TensorDesc), P]
+        lib.disco_einsum.argtypes = [ctypes.POINTER(TensorDesc)] * 3 + [P]
         lib.disco_fused_conv_bwd_workspace.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                        ctypes.POINTER(ctypes.c_size_t)]
         lib.disco_fused_conv_bwd.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 5 + [P, ctypes.c_size_t, P]
         lib.disco_last_error.restype = ctypes.c_char_p
         for f in ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
-                  "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd"):
+                  "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -196,6 +197,17 @@ def disco_fused_conv(psi: Psi, x, W, y=None):
                                            _stream(x.device)))
     return y
 
+
+
+def disco_einsum(W, t, y=None):
+    """y[b, o, ho, wo] = sum_{c,k} W[o, c, k] t[b, c, k, ho, wo] on the current device (no psi)."""
+    import torch
+
+    if y is None:
+        y = torch.empty((t.shape[0], W.shape[0], t.shape[3], t.shape[4]), dtype=t.dtype, device=t.device)
+    wd, td, yd = tensor_desc(W), tensor_desc(t), tensor_desc(y)
+    _check(load_library().disco_einsum(ctypes.byref(wd), ctypes.byref(td), ctypes.byref(yd), _stream(t.device)))
+    return y
 
 def disco_fused_conv_bwd_workspace(psi: Psi, B: int, C: int, Co: int) -> int:
     """Workspace bytes disco_fused_conv_bwd needs for these sizes."""

@@ -1,4 +1,5 @@
 // disco_api.hip — C ABI of libdisco.so: validation, plan upload and launches.
+#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -664,6 +665,52 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     return DISCO_OK;
 }
 
+
+disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_tensor *y, void *stream)
+{
+    if (!W || !t || !y) return fail(DISCO_ERR_INVALID_ARGUMENT, "W, t or y is NULL");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_HIP, "hipGetDevice failed");
+    }
+    // the architecture check of a device runs once per process (its answer cannot change)
+    static std::atomic<int> arch_ok[64];
+    if (dev < 0 || dev >= 64) return fail(DISCO_ERR_INVALID_ARGUMENT, "device ordinal out of range");
+    if (arch_ok[dev].load() != 1) {
+        disco_status st = check_device(dev);
+        if (st != DISCO_OK) return st;
+        arch_ok[dev].store(1);
+    }
+    if (t->ndim != 5) return fail(DISCO_ERR_SHAPE, "t must be (B, C, K, Ho, Wo)");
+    if (W->ndim != 3) return fail(DISCO_ERR_SHAPE, "W must be (Co, C, K)");
+    const int64_t B = t->shape[0], C = t->shape[1], K = t->shape[2], Ho = t->shape[3], Wo = t->shape[4];
+    const int64_t Co = W->shape[0];
+    if (B < 0 || C < 0 || K < 0 || Ho < 0 || Wo < 0 || Co < 0) return fail(DISCO_ERR_SHAPE, "negative dimension");
+    if (K > 16) return fail(DISCO_ERR_SHAPE, "the einsum kernel supports K <= 16");
+    if (B > INT32_MAX || C > INT32_MAX || Co > INT32_MAX) return fail(DISCO_ERR_SHAPE, "dimension exceeds 2^31");
+    const int64_t ts[5] = {B, C, K, Ho, Wo};
+    const int64_t ws[3] = {Co, C, K};
+    const int64_t ys[4] = {B, Co, Ho, Wo};
+    disco_status st;
+    if ((st = check_tensor(t, "t", 5, ts, dev)) != DISCO_OK) return st;
+    if ((st = check_tensor(W, "W", 3, ws, dev)) != DISCO_OK) return st;
+    if ((st = check_tensor(y, "y", 4, ys, dev)) != DISCO_OK) return st;
+    if (t->dtype != W->dtype || t->dtype != y->dtype) return fail(DISCO_ERR_DTYPE, "t, W and y dtypes differ");
+    if (t->dtype == DISCO_F32) return fail(DISCO_ERR_DTYPE, "the einsum supports bf16 and fp16 only");
+    const int64_t HW = Ho * Wo;
+    if (B * Co * HW == 0) return DISCO_OK;
+    if (B * ((Co + 255) / 256) * ((HW + 255) / 256) >= ((int64_t)1 << 31))
+        return fail(DISCO_ERR_SHAPE, "einsum grid exceeds 2^31 blocks");
+    disco::EinsumLaunch a;
+    a.t = t->data; a.W = W->data; a.y = y->data;
+    a.B = (int32_t)B; a.C = (int32_t)C; a.Co = (int32_t)Co; a.K = (int32_t)K;
+    a.HW = HW;
+    a.f16 = t->dtype == DISCO_F16;
+    hipError_t e = disco::launch_einsum_mfma(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("einsum launch failed: ") + hipGetErrorString(e));
+    return DISCO_OK;
+}
 
 disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, int64_t Co, size_t *bytes)
 {

@@ -95,6 +95,17 @@ struct FusedContractLaunch {
     int64_t x_bstride = 0, out_bstride = 0;  // elements between batches (0: contiguous)
 };
 hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t stream);
+
+// The einsum alone, y[b, o, p] = sum_{c,k} W[o, c, k] * t[b, c, k, p] (p = ho Wo + wo, K <= 16),
+// on the fused kernel's matrix-core einsum tile with t staged from device memory.
+struct EinsumLaunch {
+    const void *t, *W;
+    void *y;
+    int32_t B, C, Co, K;
+    int64_t HW;
+    bool f16;
+};
+hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream);
 size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_bytes);
 int fused_mfma_channels_per_chunk();
 int fused_mfma_exchange_bytes();     // LDS bytes of the einsum operand exchange

@@ -861,4 +861,228 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// ---- the einsum alone ------------------------------------------------------------------------
+//
+// y[b, o, p] = sum_{c,k} W[o, c, k] * t[b, c, k, p] over flattened output positions p = ho Wo + wo
+// ("contraction + einsum" of the torch-harmonics "disco-kernel-dev" page, "Architecture snapshot",
+// with the contraction already in device memory): the fused kernel's einsum tile fed from memory.
+// Workgroup = (b, 256 positions, up to 256 output channels), eight waves; wave w takes positions
+// p0 + 64 (w % 4) + 2n + ph (n < 32, ph = 0, 1: the two MFMA column sets) and output-channel tiles
+// h2 NOTH .. + NOTH - 1 (h2 = w / 4), fp32 accumulators in registers for all channel chunks.  Per
+// chunk of kCh channels, the t tile [channel][basis][256 positions] (32 KiB) and the W slice (A
+// operand order, as in the fused kernel) come in by direct global->LDS loads, double-buffered, one
+// chunk ahead.  A lane's B operand (basis 8 hh .. 8 hh + 7 at one position) is assembled from eight
+// 4-byte LDS words, each holding the two neighbouring positions of both column sets.  The 16-byte
+// units of a tile row are XOR-swizzled by 8 on rows whose basis index has bit 3 set, so the two lane
+// halves (basis 0..7 and 8..15) read disjoint bank halves.
+
+namespace {
+
+constexpr int kTileBytes = kCh * 16 * kFusedSpan * 2;
+
+__device__ __forceinline__ void stage_tile(const Ctx &c, const bf16_t *t, int64_t HW, int64_t p0, int c0, bool vec,
+                                           unsigned char *tile)
+{
+    const int ccn = min(kCh, c.C - c0);
+    const bf16_t *base = t + ((int64_t)c.b * c.C + c0) * c.K * HW;
+    constexpr int kUnits = kTileBytes / 16;  // 2048: 64 rows of 32 units
+    if (vec) {
+        // one resource over the chunk's valid channels (fewer than 2^31 bytes: checked by the launcher)
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(2 * (int64_t)ccn * c.K * HW));
+#pragma unroll
+        for (int i = 0; i < kUnits / kThreads; ++i) {
+            const int slot = i * kThreads + c.tid;
+            const int R = slot >> 5, u = (slot & 31) ^ (8 * ((R >> 3) & 1));
+            const int cl = R >> 4, k = R & 15;
+            const int64_t p = p0 + 8 * u;
+            const bool ok = k < c.K && cl < ccn && p < HW;
+            const uint32_t voff = ok ? (uint32_t)(2 * ((int64_t)(cl * c.K + k) * HW + p)) : 0x80000000u;
+            dma16(rs, voff, tile + 16 * (i * kThreads + 64 * c.wave));
+        }
+    } else {
+        for (int slot = c.tid; slot < kUnits; slot += kThreads) {
+            const int R = slot >> 5, u = (slot & 31) ^ (8 * ((R >> 3) & 1));
+            const int cl = R >> 4, k = R & 15;
+            const int64_t p = p0 + 8 * u;
+            i16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = (k < c.K && cl < ccn && p + e < HW) ? (short)base[(int64_t)(cl * c.K + k) * HW + p + e] : (short)0;
+            *reinterpret_cast<i16x8 *>(tile + 16 * slot) = v;
+        }
+    }
+}
+
+// One chunk: B operands of the kCh channels from the tile, MFMAs against the W slice.
+template <int NOTH, bool F16>
+__device__ __forceinline__ void einsum_chunk(const unsigned char *__restrict__ tile, const unsigned char *__restrict__ wb,
+                                             int lane, int pp, int h2, f32x16 (&yacc)[2][NOTH])
+{
+    const int r = lane & 31, hh = lane >> 5;
+    const unsigned *t32 = reinterpret_cast<const unsigned *>(tile);
+    // word of a row with basis bit 3 = hh holding positions 64 pp + 2 r and + 1
+    const int col = 4 * ((8 * pp + (r >> 2)) ^ (8 * hh)) + (r & 3);
+#pragma unroll
+    for (int ch = 0; ch < kCh; ++ch) {
+        unsigned w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = t32[(ch * 16 + 8 * hh + j) * 128 + col];
+        unsigned e0[4], e1[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            e0[a] = __builtin_amdgcn_perm(w[2 * a + 1], w[2 * a], 0x05040100u);  // low halves: even positions
+            e1[a] = __builtin_amdgcn_perm(w[2 * a + 1], w[2 * a], 0x07060302u);  // high halves: odd positions
+        }
+        const i16x8 b0 = __builtin_bit_cast(i16x8, e0), b1 = __builtin_bit_cast(i16x8, e1);
+#pragma unroll
+        for (int j = 0; j < NOTH; ++j) {
+            const i16x8 a = *reinterpret_cast<const i16x8 *>(wb + 1024 * ((h2 * NOTH + j) * kCh + ch) + 16 * lane);
+            yacc[0][j] = mfma32<F16>(a, b0, yacc[0][j]);
+            yacc[1][j] = mfma32<F16>(a, b1, yacc[1][j]);
+        }
+    }
+}
+
+template <int NOTH, bool F16>
+__device__ __forceinline__ void einsum_step(const Ctx &c, const bf16_t *t, int64_t HW, int64_t p0, bool vec, int ci,
+                                            int nchunks, const unsigned char *__restrict__ tcur,
+                                            const unsigned char *__restrict__ wcur, unsigned char *__restrict__ tnxt,
+                                            unsigned char *__restrict__ wnxt, int pp, int h2,
+                                            f32x16 (&yacc)[2][NOTH])
+{
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into the current buffers have landed
+    __syncthreads();                // everyone's have; the previous chunk is done with the next buffers
+    if (ci + 1 < nchunks) {
+        stage_w(c, kCh * (ci + 1), wnxt);
+        stage_tile(c, t, HW, p0, kCh * (ci + 1), vec, tnxt);
+    }
+    einsum_chunk<NOTH, F16>(tcur, wcur, c.lane, pp, h2, yacc);
+}
+
+template <int NOT, bool F16>
+__global__ __launch_bounds__(kThreads) void einsum_mfma_kernel(const bf16_t *__restrict__ t, const bf16_t *__restrict__ W,
+                                                               bf16_t *__restrict__ y, int B, int C, int Co, int K,
+                                                               int64_t HW, int n_pt, int n_ob, int vec_t, int vec_w,
+                                                               int vec_y)
+{
+    constexpr int NOTH = NOT / 2;
+    constexpr int kW = NOT * kCh * 1024;
+    // LDS: [W slice 0][W slice 1][tile 0][tile 1]
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *wb0 = smem, *wb1 = smem + kW;
+    unsigned char *tb0 = smem + 2 * kW, *tb1 = tb0 + kTileBytes;
+
+    int bid = blockIdx.x;
+    const int pt = bid % n_pt;
+    bid /= n_pt;
+    const int ob = bid % n_ob;
+    Ctx c;
+    c.b = bid / n_ob;
+    c.W = W;
+    c.w_rs = make_rsrc(W, vec_w ? (uint32_t)(2 * (int64_t)Co * C * 16) : 0u);
+    c.B = B; c.C = C; c.Co = Co; c.K = K; c.n_ot = NOT;
+    c.tid = threadIdx.x;
+    c.lane = c.tid & 63;
+    c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+    c.o_base = ob * (kMaxOt * 32);
+    c.vec_w = vec_w != 0;
+    const int64_t p0 = (int64_t)pt * kFusedSpan;
+    const bool vec = vec_t != 0;
+    const int pp = c.wave & 3, h2 = c.wave >> 2;
+    const int r = c.lane & 31, hh = c.lane >> 5;
+
+    f32x16 yacc[2][NOTH];
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph)
+#pragma unroll
+        for (int j = 0; j < NOTH; ++j)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) yacc[ph][j][a] = 0.0f;
+
+    const int nchunks = (C + kCh - 1) / kCh;
+    stage_w(c, 0, wb0);
+    stage_tile(c, t, HW, p0, 0, vec, tb0);
+    for (int ci = 0; ci < nchunks; ci += 2) {
+        einsum_step<NOTH, F16>(c, t, HW, p0, vec, ci, nchunks, tb0, wb0, tb1, wb1, pp, h2, yacc);
+        if (ci + 1 < nchunks) einsum_step<NOTH, F16>(c, t, HW, p0, vec, ci + 1, nchunks, tb1, wb1, tb0, wb0, pp, h2, yacc);
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);  // no load into tile 0 is in flight (C = 0 issues one and no step)
+
+    // epilogue: yacc[ph][j] row = output channel (h2 NOTH + j) 32 + 8 (a / 4) + 4 hh + a % 4, column
+    // = position p0 + 64 pp + 2 r + ph.  Pass j writes 64 channels through a 32 KiB LDS tile
+    // [channel][256 positions] (tile 0's space) so that rows leave as 16-byte stores.
+    uint32_t *tile32 = reinterpret_cast<uint32_t *>(tb0);
+    const bf16_t *tile = reinterpret_cast<const bf16_t *>(tb0);
+#pragma unroll
+    for (int j = 0; j < NOTH; ++j) {
+        __syncthreads();  // the last chunk (or the previous pass) is done with the tile's space
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+            const int ol = 32 * h2 + 8 * (a >> 2) + 4 * hh + (a & 3);
+            const uint32_t lo = (uint16_t)to16<F16>(yacc[0][j][a], 1.0f), hi = (uint16_t)to16<F16>(yacc[1][j][a], 1.0f);
+            tile32[ol * 128 + 32 * pp + r] = lo | (hi << 16);
+        }
+        __syncthreads();
+        for (int u = c.tid; u < 64 * 32; u += kThreads) {
+            const int seg = u & 31, ol = u >> 5;
+            const int o = c.o_base + ((ol >> 5) * NOTH + j) * 32 + (ol & 31);
+            const int64_t p = p0 + 8 * seg;
+            if (o >= Co || p >= HW) continue;
+            bf16_t *dst = y + ((int64_t)c.b * Co + o) * HW + p;
+            const bf16_t *src = tile + ol * 256 + 8 * seg;
+            if (vec_y && p + 8 <= HW) {
+                *reinterpret_cast<i16x8 *>(dst) = *reinterpret_cast<const i16x8 *>(src);
+            } else {
+                for (int e = 0; e < 8 && p + e < HW; ++e) dst[e] = src[e];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream)
+{
+    if (a.B == 0 || a.Co == 0 || a.HW == 0) return hipSuccess;
+    const int n_pt = (int)((a.HW + kFusedSpan - 1) / kFusedSpan);
+    const int n_ob = (a.Co + kMaxOt * 32 - 1) / (kMaxOt * 32);
+    const int n_ot1 = std::min(kMaxOt, (a.Co + 31) / 32);
+    const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
+    const size_t lds = 2 * (size_t)n_ot * kCh * 1024 + 2 * (size_t)kTileBytes;
+    const void *fn = a.f16 ? (n_ot == 2   ? (const void *)einsum_mfma_kernel<2, true>
+                              : n_ot == 4 ? (const void *)einsum_mfma_kernel<4, true>
+                                          : (const void *)einsum_mfma_kernel<8, true>)
+                           : (n_ot == 2   ? (const void *)einsum_mfma_kernel<2, false>
+                              : n_ot == 4 ? (const void *)einsum_mfma_kernel<4, false>
+                                          : (const void *)einsum_mfma_kernel<8, false>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t nblk = (int64_t)a.B * n_ob * n_pt;
+    // direct loads: 16-byte aligned runs, and one chunk's channels addressable with 32-bit offsets
+    const int vec_t = (a.HW % 8 == 0 && ((uintptr_t)a.t % 16) == 0 &&
+                       (int64_t)2 * kCh * a.K * a.HW < ((int64_t)1 << 31)) ? 1 : 0;
+    const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
+    const int vec_y = (a.HW % 8 == 0 && ((uintptr_t)a.y % 16) == 0) ? 1 : 0;
+#define DISCO_EINSUM_LAUNCH(N, F16)                                                                              \
+    hipLaunchKernelGGL((einsum_mfma_kernel<N, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,           \
+                       (const bf16_t *)a.t, (const bf16_t *)a.W, (bf16_t *)a.y, a.B, a.C, a.Co, a.K, a.HW, n_pt,     \
+                       n_ob, vec_t, vec_w, vec_y)
+    if (a.f16) {
+        switch (n_ot) {
+        case 2: DISCO_EINSUM_LAUNCH(2, true); break;
+        case 4: DISCO_EINSUM_LAUNCH(4, true); break;
+        default: DISCO_EINSUM_LAUNCH(8, true); break;
+        }
+    } else {
+        switch (n_ot) {
+        case 2: DISCO_EINSUM_LAUNCH(2, false); break;
+        case 4: DISCO_EINSUM_LAUNCH(4, false); break;
+        default: DISCO_EINSUM_LAUNCH(8, false); break;
+        }
+    }
+#undef DISCO_EINSUM_LAUNCH
+    return hipGetLastError();
+}
+
 }  // namespace disco

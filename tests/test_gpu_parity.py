@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import sparse_gather_contraction_amd as sgc
-from disco_inputs import WORKLOADS, randn, workload_gout, workload_psi, workload_weight, workload_x
+from disco_inputs import WORKLOADS, randn, randn_device, workload_gout, workload_psi, workload_weight, workload_x
 from disco_inputs.psi import PsiCSR, build_psi, random_psi
 
 pytestmark = pytest.mark.gpu
@@ -605,3 +605,77 @@ def test_page_shape_fused_bwd_sampled():
     out = oracle.fwd(psi, x[0, c][None])[0].reshape(psi.K, -1)
     outa = oracle.fwd(psi, x[0, c][None].abs(), abs_mode=True)[0].reshape(psi.K, -1)
     assert normalised_error(dW[:, c, :], gy64[0] @ out.T, np.abs(gy64[0]) @ outa.T) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- the einsum alone
+
+TOL_EIN = {"bf16": 2e-2, "f16": 2e-3}
+
+
+@pytest.mark.parametrize("cfg", [
+    # (B, C, Co, K, Ho, Wo, dtype)
+    (2, 5, 40, 3, 7, 37, "bf16"),      # ragged channel chunk, K < 16, 259 positions (element loads, ragged tile)
+    (1, 8, 256, 16, 16, 64, "bf16"),   # direct loads of t and W, one full output-channel block
+    (2, 9, 300, 8, 5, 48, "bf16"),     # two output-channel blocks (the second ragged), K = 8
+    (1, 12, 64, 16, 3, 100, "f16"),    # fp16, 300 positions (ragged last tile)
+    (1, 4, 33, 16, 1, 8, "f16"),       # one partial tile
+])
+def test_einsum_small_ragged(cfg):
+    B, C, Co, K, Ho, Wo, dt = cfg
+    _log(f"einsum {cfg}")
+    t = randn((B, C, K, Ho, Wo), 3100 + C, dt)
+    W = randn((Co, C, K), 3200 + C, dt, std=1.0 / np.sqrt(C * K))
+    y = nan_like((B, Co, Ho, Wo), t.dtype)
+    sgc.disco_einsum(W.to(DEV), t.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.einsum(W, t)
+    nrm = oracle.einsum(W.abs(), t.abs(), abs_mode=True)
+    assert normalised_error(y.cpu(), ref, nrm) <= TOL_EIN[dt]
+
+
+def test_einsum_edge_cases_and_errors():
+    _log("einsum edge cases")
+    # no input channels: y is exactly zero; no positions: nothing to do
+    W0 = torch.empty((8, 0, 16), dtype=torch.bfloat16, device=DEV)
+    t0 = torch.empty((1, 0, 16, 4, 8), dtype=torch.bfloat16, device=DEV)
+    y0 = sgc.disco_einsum(W0, t0, nan_like((1, 8, 4, 8), torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.all(y0 == 0)
+    sgc.disco_einsum(torch.zeros((8, 3, 4), dtype=torch.bfloat16, device=DEV),
+                     torch.zeros((2, 3, 4, 0, 8), dtype=torch.bfloat16, device=DEV))
+    # rejected calls leave the output untouched
+    t = randn((1, 3, 4, 2, 8), 3300, "bf16").to(DEV)
+    W = randn((5, 3, 4), 3301, "bf16").to(DEV)
+    y = nan_like((1, 5, 2, 8), torch.bfloat16)
+    bad = [
+        (W, randn((1, 3, 17, 2, 8), 3302, "bf16").to(DEV), y, "DISCO_ERR_SHAPE"),  # K > 16
+        (W.float(), t.float(), y.float(), "DISCO_ERR_DTYPE"),                        # fp32
+        (W, t, nan_like((1, 5, 2, 8), torch.float16), "DISCO_ERR_DTYPE"),            # dtypes differ
+        (W, t, nan_like((1, 4, 2, 8), torch.bfloat16), "DISCO_ERR_SHAPE"),           # y channels
+        (randn((5, 2, 4), 3303, "bf16").to(DEV), t, y, "DISCO_ERR_SHAPE"),            # W channels
+    ]
+    for Wb, tb, yb, code in bad:
+        with pytest.raises(sgc.DiscoError) as e:
+            sgc.disco_einsum(Wb, tb, yb)
+        assert e.value.status_name == code
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(y))
+
+
+def test_einsum_721x1440_full_size_sampled():
+    """The einsum at the fused workload's GEMM shape (B=2, C=Co=256, K=16, 721x1440), launched as the
+    bench times it; whole output latitudes from pole to equator against the oracle, and bitwise
+    run-to-run determinism."""
+    w = WORKLOADS["fused_bf16_721x1440"]
+    _log("einsum 721x1440")
+    t = randn_device((w.B, w.C, w.K, w.Ho, w.Wo), 3400, "bf16", DEV)
+    W = workload_weight(w)
+    y = sgc.disco_einsum(W.to(DEV), t)
+    y2 = sgc.disco_einsum(W.to(DEV), t)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    hos = [0, 360, 720]
+    ts = t[:, :, :, hos].cpu()
+    ref = oracle.einsum(W, ts)
+    nrm = oracle.einsum(W.abs(), ts.abs(), abs_mode=True)
+    assert normalised_error(y[:, :, hos].cpu(), ref, nrm) <= TOL_EIN["bf16"]

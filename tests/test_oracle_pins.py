@@ -16,6 +16,8 @@ missing term) fails at least one of them:
 * same-latitude psi -> numpy FFT circular cross-correlation, subsampled by s;
 * one-entry identity psi -> strided subsample, and fused -> numpy matmul;
 * linearity in x and in the values;
+* einsum alone: einsum of the forward oracle reproduces the fused oracle
+  bitwise, the hand-worked fixture's fused values, and K = 1 -> numpy matmul;
 * fused backward: unit directional derivatives of the fused oracle, the dense
   basis, and <gy, y> = <x, gx> = <W, dW>.
 """
@@ -208,6 +210,34 @@ def test_fused_matches_einsum_of_forward():
     # ho subset
     np.testing.assert_allclose(oracle.fused(psi, x, W, ho_list=[3, 1]), ref[:, :, [3, 1]], rtol=1e-13, atol=1e-13)
 
+
+
+def test_einsum_of_forward_is_fused_bitwise():
+    # the fused oracle is pinned on its own (dense brute force, fixture, matmul special case)
+    psi = random_psi(3, 4, 6, 5, 12, 0.25, seed=7)
+    x = randn((2, 3, 5, 12), 22).numpy()
+    W = randn((4, 3, 3), 23).numpy()
+    np.testing.assert_array_equal(oracle.einsum(W, oracle.fwd(psi, x)), oracle.fused(psi, x, W))
+    n = oracle.einsum(W, oracle.fwd(psi, x, abs_mode=True), abs_mode=True)
+    np.testing.assert_array_equal(n, oracle.fused(psi, x, W, abs_mode=True))
+
+
+def test_einsum_hand_worked_fixture():
+    d = json.load(open(os.path.join(GOLDEN, "hand_tiny.json")))
+    out = np.array(d["out"], np.float64)[None, None]
+    y = oracle.einsum(np.array(d["W"], np.float32), out)
+    np.testing.assert_array_equal(y[0], np.array(d["y"]))
+
+
+def test_einsum_single_basis_is_matmul():
+    t = randn((2, 5, 1, 3, 7), 24).numpy()
+    W = randn((6, 5, 1), 25).numpy()
+    ref = np.stack([W[:, :, 0].astype(np.float64) @ t[b, :, 0].reshape(5, -1).astype(np.float64) for b in range(2)])
+    np.testing.assert_allclose(oracle.einsum(W, t).reshape(2, 6, -1), ref, rtol=1e-13, atol=1e-13)
+    # a transposed W (o and c swapped) would not even have this shape; check a non-symmetric square case too
+    W2 = randn((5, 5, 1), 26).numpy()
+    ref2 = np.stack([W2[:, :, 0].astype(np.float64) @ t[b, :, 0].reshape(5, -1).astype(np.float64) for b in range(2)])
+    np.testing.assert_allclose(oracle.einsum(W2, t).reshape(2, 5, -1), ref2, rtol=1e-13, atol=1e-13)
 
 # ---- backward of the fused convolution -------------------------------------------------------
 # y = einsum(W, F x) is linear in x and in W, so <gy, y> has gradients
