@@ -214,7 +214,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-KERNEL_SOURCES = {"fused": "kernels_fused_mfma.hip"}
+KERNEL_SOURCES = {"fused": "kernels_fused_mfma.hip", "einsum": "kernels_fused_mfma.hip"}
 
 
 def counter_traffic(op):
@@ -271,7 +271,7 @@ def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
            "mfma_tflops": round(2 * macs / ms / 1e9, 3),
            "mfma_frac": round(2 * macs / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
            "bytes": byt, "GBps": round(byt / ms / 1e6, 2), "hbm_frac": round(byt / ms / 1e6 / PEAK_HBM_GBS, 4),
-           "gemm_mkn": [w.Co, w.C * w.K, w.B * w.Ho * w.Wo],
+           "gemm_mkn": [w.Co, w.C * w.K, w.B * w.Ho * w.Wo], "traffic": counter_traffic("einsum"),
            "operand": "bf16 contraction (2,256,16,721,1440) in HBM, W (256,256,16), y (2,256,721,1440)"}
     print(f"[bench] einsum alone: {ms:.3f} ms ({res['mfma_tflops']} TFLOP/s, {res['GBps']} GB/s)",
           file=sys.stderr, flush=True)

@@ -868,29 +868,64 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
 // with the contraction already in device memory): the fused kernel's einsum tile fed from memory.
 // Workgroup = (b, 256 positions, up to 256 output channels), eight waves; wave w takes positions
 // p0 + 64 (w % 4) + 2n + ph (n < 32, ph = 0, 1: the two MFMA column sets) and output-channel tiles
-// h2 NOTH .. + NOTH - 1 (h2 = w / 4), fp32 accumulators in registers for all channel chunks.  Per
-// chunk of kCh channels, the t tile [channel][basis][256 positions] (32 KiB) and the W slice (A
-// operand order, as in the fused kernel) come in by direct global->LDS loads, double-buffered, one
-// chunk ahead.  A lane's B operand (basis 8 hh .. 8 hh + 7 at one position) is assembled from eight
-// 4-byte LDS words, each holding the two neighbouring positions of both column sets.  The 16-byte
-// units of a tile row are XOR-swizzled by 8 on rows whose basis index has bit 3 set, so the two lane
-// halves (basis 0..7 and 8..15) read disjoint bank halves.
+// h2 NOTH .. + NOTH - 1 (h2 = w / 4), fp32 accumulators in registers for all channels.  A step
+// covers kEch input channels; its stage holds the W slice (A operand order, as in the fused
+// kernel) and the t tile [channel][basis][256 positions], both brought in by direct global->LDS
+// loads through a ring of kEring stages issued kEring - 1 steps ahead.  A lane's B operand (basis
+// 8 hh .. 8 hh + 7 at one position) is assembled from eight 4-byte LDS words, each holding the two
+// neighbouring positions of both column sets.  The 16-byte units of a tile row are XOR-swizzled by
+// 8 on rows whose basis index has bit 3 set, so the two lane halves (basis 0..7 and 8..15) read
+// disjoint bank halves.  At 256 channels and K = 16 the tile reads t once from HBM (the W slices
+// come from L2), and the op is bound by that stream: 256 flops per byte of t, below the ratio of
+// the bf16 matrix-core peak to the HBM bandwidth.  Four channels per step with two stages measured
+// faster than two channels per step with three to five stages (fewer barriers per MFMA).
 
 namespace {
 
-constexpr int kTileBytes = kCh * 16 * kFusedSpan * 2;
+constexpr int kEch = 4;                                  // input channels per step
+constexpr int kEring = 2;                                // stages in the ring
+constexpr int kTileBytes = kEch * 16 * kFusedSpan * 2;   // 32 KiB
+constexpr int kTileLoads = kTileBytes / 16 / kThreads;   // direct loads per thread per tile
+
+// W slice of the step starting at channel c0, unit (ot, cl) = W[o_base + 32 ot + l % 32, c0 + cl,
+// 8 (l / 32) .. + 7] for lane l.  With vec_w every unit is one direct load (rows past Co or C
+// read zeros), so with NOT = 8 (16 units over 8 waves) each thread issues exactly two.
+__device__ __forceinline__ void stage_w_ein(const Ctx &c, int c0, unsigned char *wb)
+{
+    const int o = c.o_base + (c.lane & 31);
+    const int hh = c.lane >> 5;
+    for (int u = c.wave; u < c.n_ot * kEch; u += kWaves) {
+        const int ot = u / kEch, cl = u - ot * kEch;
+        const int oo = o + 32 * ot, ch = c0 + cl;
+        unsigned char *dst = wb + 1024 * u;
+        const bool ok = oo < c.Co && ch < c.C;
+        if (c.vec_w) {
+            // rows past Co or C read zeros through the buffer bounds (one load per unit either way)
+            const uint32_t voff = ok ? 2u * (uint32_t)(((int64_t)oo * c.C + ch) * 16 + 8 * hh) : 0x80000000u;
+            dma16(c.w_rs, voff, dst);
+        } else {
+            i16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = 8 * hh + i;
+                v[i] = (ok && k < c.K) ? (short)c.W[((int64_t)oo * c.C + ch) * c.K + k] : (short)0;
+            }
+            *reinterpret_cast<i16x8 *>(dst + 16 * c.lane) = v;
+        }
+    }
+}
 
 __device__ __forceinline__ void stage_tile(const Ctx &c, const bf16_t *t, int64_t HW, int64_t p0, int c0, bool vec,
                                            unsigned char *tile)
 {
-    const int ccn = min(kCh, c.C - c0);
+    const int ccn = min(kEch, c.C - c0);
     const bf16_t *base = t + ((int64_t)c.b * c.C + c0) * c.K * HW;
-    constexpr int kUnits = kTileBytes / 16;  // 2048: 64 rows of 32 units
+    constexpr int kUnits = kTileBytes / 16;  // 32 rows of 32 units
     if (vec) {
-        // one resource over the chunk's valid channels (fewer than 2^31 bytes: checked by the launcher)
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(2 * (int64_t)ccn * c.K * HW));
+        // one resource over the step's valid channels (fewer than 2^31 bytes: checked by the launcher)
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(2 * (int64_t)max(ccn, 0) * c.K * HW));
 #pragma unroll
-        for (int i = 0; i < kUnits / kThreads; ++i) {
+        for (int i = 0; i < kTileLoads; ++i) {
             const int slot = i * kThreads + c.tid;
             const int R = slot >> 5, u = (slot & 31) ^ (8 * ((R >> 3) & 1));
             const int cl = R >> 4, k = R & 15;
@@ -913,7 +948,9 @@ __device__ __forceinline__ void stage_tile(const Ctx &c, const bf16_t *t, int64_
     }
 }
 
-// One chunk: B operands of the kCh channels from the tile, MFMAs against the W slice.
+// One step: B operands of the kEch channels from the tile, MFMAs against the W slice.  The LDS
+// reads of channel ch + 1 (eight words of t, NOTH W operands) are issued before the MFMAs of
+// channel ch, so their latency hides behind those MFMAs; scheduling barriers keep that order.
 template <int NOTH, bool F16>
 __device__ __forceinline__ void einsum_chunk(const unsigned char *__restrict__ tile, const unsigned char *__restrict__ wb,
                                              int lane, int pp, int h2, f32x16 (&yacc)[2][NOTH])
@@ -921,42 +958,47 @@ __device__ __forceinline__ void einsum_chunk(const unsigned char *__restrict__ t
     const int r = lane & 31, hh = lane >> 5;
     const unsigned *t32 = reinterpret_cast<const unsigned *>(tile);
     // word of a row with basis bit 3 = hh holding positions 64 pp + 2 r and + 1
-    const int col = 4 * ((8 * pp + (r >> 2)) ^ (8 * hh)) + (r & 3);
+    const unsigned *tl = t32 + 8 * hh * 128 + 4 * ((8 * pp + (r >> 2)) ^ (8 * hh)) + (r & 3);
+    // A operand of tile ot = h2 NOTH + j and channel ch at wl + 1024 (j kEch + ch)
+    const unsigned char *wl = wb + 1024 * (h2 * NOTH * kEch) + 16 * lane;
+    unsigned w[2][8];
+    i16x8 a[2][NOTH];
 #pragma unroll
-    for (int ch = 0; ch < kCh; ++ch) {
-        unsigned w[8];
+    for (int i = 0; i < 8; ++i) w[0][i] = tl[i * 128];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = t32[(ch * 16 + 8 * hh + j) * 128 + col];
+    for (int j = 0; j < NOTH; ++j) a[0][j] = *reinterpret_cast<const i16x8 *>(wl + 1024 * (j * kEch));
+#pragma unroll
+    for (int ch = 0; ch < kEch; ++ch) {
+        const int sl = ch & 1;
+        if (ch + 1 < kEch) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[sl ^ 1][i] = tl[((ch + 1) * 16 + i) * 128];
+#pragma unroll
+            for (int j = 0; j < NOTH; ++j) a[sl ^ 1][j] = *reinterpret_cast<const i16x8 *>(wl + 1024 * (j * kEch + ch + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
         unsigned e0[4], e1[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            e0[a] = __builtin_amdgcn_perm(w[2 * a + 1], w[2 * a], 0x05040100u);  // low halves: even positions
-            e1[a] = __builtin_amdgcn_perm(w[2 * a + 1], w[2 * a], 0x07060302u);  // high halves: odd positions
+        for (int q = 0; q < 4; ++q) {
+            e0[q] = __builtin_amdgcn_perm(w[sl][2 * q + 1], w[sl][2 * q], 0x05040100u);  // low halves: even positions
+            e1[q] = __builtin_amdgcn_perm(w[sl][2 * q + 1], w[sl][2 * q], 0x07060302u);  // high halves: odd positions
         }
         const i16x8 b0 = __builtin_bit_cast(i16x8, e0), b1 = __builtin_bit_cast(i16x8, e1);
 #pragma unroll
         for (int j = 0; j < NOTH; ++j) {
-            const i16x8 a = *reinterpret_cast<const i16x8 *>(wb + 1024 * ((h2 * NOTH + j) * kCh + ch) + 16 * lane);
-            yacc[0][j] = mfma32<F16>(a, b0, yacc[0][j]);
-            yacc[1][j] = mfma32<F16>(a, b1, yacc[1][j]);
+            yacc[0][j] = mfma32<F16>(a[sl][j], b0, yacc[0][j]);
+            yacc[1][j] = mfma32<F16>(a[sl][j], b1, yacc[1][j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <int NOTH, bool F16>
-__device__ __forceinline__ void einsum_step(const Ctx &c, const bf16_t *t, int64_t HW, int64_t p0, bool vec, int ci,
-                                            int nchunks, const unsigned char *__restrict__ tcur,
-                                            const unsigned char *__restrict__ wcur, unsigned char *__restrict__ tnxt,
-                                            unsigned char *__restrict__ wnxt, int pp, int h2,
-                                            f32x16 (&yacc)[2][NOTH])
+// Wait until at most N of this thread's direct loads are in flight and its LDS writes are done.
+template <int N>
+__device__ __forceinline__ void wait_loads()
 {
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's loads into the current buffers have landed
-    __syncthreads();                // everyone's have; the previous chunk is done with the next buffers
-    if (ci + 1 < nchunks) {
-        stage_w(c, kCh * (ci + 1), wnxt);
-        stage_tile(c, t, HW, p0, kCh * (ci + 1), vec, tnxt);
-    }
-    einsum_chunk<NOTH, F16>(tcur, wcur, c.lane, pp, h2, yacc);
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt N, expcnt 7 (no wait), lgkmcnt 0
 }
 
 template <int NOT, bool F16>
@@ -966,11 +1008,10 @@ __global__ __launch_bounds__(kThreads) void einsum_mfma_kernel(const bf16_t *__r
                                                                int vec_y)
 {
     constexpr int NOTH = NOT / 2;
-    constexpr int kW = NOT * kCh * 1024;
-    // LDS: [W slice 0][W slice 1][tile 0][tile 1]
+    constexpr int kW = NOT * kEch * 1024;
+    constexpr int kStage = kW + kTileBytes;
+    // LDS: ring of kEring stages [W slice][t tile]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    unsigned char *wb0 = smem, *wb1 = smem + kW;
-    unsigned char *tb0 = smem + 2 * kW, *tb1 = tb0 + kTileBytes;
 
     int bid = blockIdx.x;
     const int pt = bid % n_pt;
@@ -999,24 +1040,44 @@ __global__ __launch_bounds__(kThreads) void einsum_mfma_kernel(const bf16_t *__r
 #pragma unroll
             for (int a = 0; a < 16; ++a) yacc[ph][j][a] = 0.0f;
 
-    const int nchunks = (C + kCh - 1) / kCh;
-    stage_w(c, 0, wb0);
-    stage_tile(c, t, HW, p0, 0, vec, tb0);
-    for (int ci = 0; ci < nchunks; ci += 2) {
-        einsum_step<NOTH, F16>(c, t, HW, p0, vec, ci, nchunks, tb0, wb0, tb1, wb1, pp, h2, yacc);
-        if (ci + 1 < nchunks) einsum_step<NOTH, F16>(c, t, HW, p0, vec, ci + 1, nchunks, tb1, wb1, tb0, wb0, pp, h2, yacc);
+    // Per step a thread issues exactly kLoads direct loads when both operands load directly and
+    // NOT = 8 (W: 8 kEch units over 8 waves; t: kTileLoads), so "at most kLoads * m in flight"
+    // means that every step but the next m has landed.  Otherwise wait for everything.
+    constexpr int kLoads = NOT * kEch / kWaves + kTileLoads;
+    static_assert(kEring <= 4, "the waits below cover up to two steps in flight");
+    const bool ring = vec && c.vec_w && NOT == 8;
+    const int nsteps = (C + kEch - 1) / kEch;
+    auto issue = [&](int st) {
+        unsigned char *dst = smem + (st % kEring) * kStage;
+        stage_w_ein(c, kEch * st, dst);
+        stage_tile(c, t, HW, p0, kEch * st, vec, dst + kW);
+    };
+    for (int st = 0; st < kEring - 1 && st < nsteps; ++st) issue(st);
+    for (int st = 0; st < nsteps; ++st) {
+        // A bare barrier: __syncthreads() would add a workgroup release fence, and the compiler makes
+        // such a fence wait for every direct load into LDS still in flight (the later steps' too).
+        // The compiler-level fences keep LDS accesses on their side of the barrier.
+        const int ahead = ring ? min(kEring - 2, nsteps - 1 - st) : 0;  // steps issued after this one
+        if (ahead == 2) wait_loads<2 * kLoads>();
+        else if (ahead == 1) wait_loads<kLoads>();
+        else __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // everyone's loads have landed; every wave is done with step st - 1
+        asm volatile("" ::: "memory");
+        if (st + kEring - 1 < nsteps) issue(st + kEring - 1);  // into step st - 1's stage
+        const unsigned char *cur = smem + (st % kEring) * kStage;
+        einsum_chunk<NOTH, F16>(cur + kW, cur, c.lane, pp, h2, yacc);
     }
-
-    __builtin_amdgcn_s_waitcnt(0);  // no load into tile 0 is in flight (C = 0 issues one and no step)
+    __builtin_amdgcn_s_waitcnt(0);  // nothing in flight before the ring's space is reused
 
     // epilogue: yacc[ph][j] row = output channel (h2 NOTH + j) 32 + 8 (a / 4) + 4 hh + a % 4, column
     // = position p0 + 64 pp + 2 r + ph.  Pass j writes 64 channels through a 32 KiB LDS tile
-    // [channel][256 positions] (tile 0's space) so that rows leave as 16-byte stores.
-    uint32_t *tile32 = reinterpret_cast<uint32_t *>(tb0);
-    const bf16_t *tile = reinterpret_cast<const bf16_t *>(tb0);
+    // [channel][256 positions] (the ring's first 32 KiB) so that rows leave as 16-byte stores.
+    uint32_t *tile32 = reinterpret_cast<uint32_t *>(smem);
+    const bf16_t *tile = reinterpret_cast<const bf16_t *>(smem);
 #pragma unroll
     for (int j = 0; j < NOTH; ++j) {
-        __syncthreads();  // the last chunk (or the previous pass) is done with the tile's space
+        __syncthreads();  // the last step (or the previous pass) is done with the tile's space
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
             const int ol = 32 * h2 + 8 * (a >> 2) + 4 * hh + (a & 3);
@@ -1049,7 +1110,7 @@ hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream)
     const int n_ob = (a.Co + kMaxOt * 32 - 1) / (kMaxOt * 32);
     const int n_ot1 = std::min(kMaxOt, (a.Co + 31) / 32);
     const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
-    const size_t lds = 2 * (size_t)n_ot * kCh * 1024 + 2 * (size_t)kTileBytes;
+    const size_t lds = (size_t)kEring * ((size_t)n_ot * kEch * 1024 + kTileBytes);  // 160 KiB at 256 channels
     const void *fn = a.f16 ? (n_ot == 2   ? (const void *)einsum_mfma_kernel<2, true>
                               : n_ot == 4 ? (const void *)einsum_mfma_kernel<4, true>
                                           : (const void *)einsum_mfma_kernel<8, true>)
@@ -1061,7 +1122,7 @@ hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream)
     const int64_t nblk = (int64_t)a.B * n_ob * n_pt;
     // direct loads: 16-byte aligned runs, and one chunk's channels addressable with 32-bit offsets
     const int vec_t = (a.HW % 8 == 0 && ((uintptr_t)a.t % 16) == 0 &&
-                       (int64_t)2 * kCh * a.K * a.HW < ((int64_t)1 << 31)) ? 1 : 0;
+                       (int64_t)2 * kEch * a.K * a.HW < ((int64_t)1 << 31)) ? 1 : 0;
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
     const int vec_y = (a.HW % 8 == 0 && ((uintptr_t)a.y % 16) == 0) ? 1 : 0;
 #define DISCO_EINSUM_LAUNCH(N, F16)                                                                              \
