@@ -21,24 +21,27 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "disco_oracle.c")
-_LIB = os.path.join(_HERE, "libdisco_oracle.so")
+# DISCO_ORACLE_LIB: load this build instead (the mutation test points it at copies of the
+# source with a planted mistake, to show that the pins catch each one)
+_BUILT = os.path.join(_HERE, "libdisco_oracle.so")
+_LIB = os.environ.get("DISCO_ORACLE_LIB") or _BUILT
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (fp64, no fast-math, OpenMP across planes)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+    if force or not os.path.exists(_BUILT):
+        tmp = _BUILT + ".tmp"
         subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
                         "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _BUILT)
+    return _BUILT
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _LIB == _BUILT and not os.path.exists(_LIB):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         i64, i32, P = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
