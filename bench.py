@@ -184,6 +184,7 @@ def main():
     ein = None
     if not args.no_einsum and "fused" in ops:
         ein = time_einsum(sgc, torch, np, wu, tensors, dev, stream)
+    ach = None if args.no_einsum else achievable_copy(torch, np, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -209,6 +210,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "einsum_standalone": ein,
+        "achievable": ach,
         "next_rows": nxt,
     }
     print(json.dumps(line), flush=True)
@@ -276,6 +278,30 @@ def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
     print(f"[bench] einsum alone: {ms:.3f} ms ({res['mfma_tflops']} TFLOP/s, {res['GBps']} GB/s)",
           file=sys.stderr, flush=True)
     return res
+
+
+def achievable_copy(torch, np, dev, stream, mib=1024, reps=5):
+    """What a plain device copy reaches on this machine (torch's copy of `mib` MiB, read + write, HIP
+    events on the launch stream): the practical HBM ceiling beside the 8 TB/s spec peak."""
+    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * mib * (1 << 20) / ms / 1e6
+    return {"copy_GBps": round(gbs, 1), "copy_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "note": f"device copy of {mib} MiB (read + write), median of {reps}"}
 
 def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=3):
     """Backward of the fused convolution on the fused workload (gradient gy ~ N(0,1), bf16), timed
