@@ -280,28 +280,36 @@ def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
     return res
 
 
-def achievable_copy(torch, np, dev, stream, mib=1024, reps=5):
-    """What a plain device copy reaches on this machine (torch's copy of `mib` MiB, read + write, HIP
-    events on the launch stream): the practical HBM ceiling beside the 8 TB/s spec peak."""
+def achievable_copy(torch, np, dev, stream, mib=1024, reps=5, read_gib=4):
+    """What plain streaming reaches on this machine, beside the 8 TB/s spec peak: torch's device copy of
+    `mib` MiB (read + write) and torch's sum over `read_gib` GiB of bf16 (read only), median of
+    `reps` each, HIP events on the launch stream."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
     src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    ev = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        dst.copy_(src)
-        b.record(stream)
-        ev.append((a, b))
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    copy_gbs = 2 * mib * (1 << 20) / timed(lambda: dst.copy_(src)) / 1e6
     del src, dst
+    x = torch.ones(read_gib * (1 << 30) // 2, dtype=torch.bfloat16, device=dev)
+    read_gbs = read_gib * (1 << 30) / timed(lambda: x.sum(dtype=torch.float32)) / 1e6
+    del x
     torch.cuda.empty_cache()
-    gbs = 2 * mib * (1 << 20) / ms / 1e6
-    return {"copy_GBps": round(gbs, 1), "copy_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "note": f"device copy of {mib} MiB (read + write), median of {reps}"}
+    return {"copy_GBps": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "read_GBps": round(read_gbs, 1), "read_frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
+            "note": f"device copy of {mib} MiB (read + write) and a bf16 sum over {read_gib} GiB (read only), "
+                    f"median of {reps} each"}
 
 def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=3):
     """Backward of the fused convolution on the fused workload (gradient gy ~ N(0,1), bf16), timed
