@@ -21,7 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "disco_oracle.c")
-# DISCO_ORACLE_LIB: load this build instead (the mutation test points it at copies of the
+# DISCO_ORACLE_LIB: load this library file instead (the mutation test points it at copies of the
 # source with a planted mistake, to show that the pins catch each one)
 _BUILT = os.path.join(_HERE, "libdisco_oracle.so")
 _LIB = os.environ.get("DISCO_ORACLE_LIB") or _BUILT
