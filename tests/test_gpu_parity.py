@@ -679,3 +679,29 @@ def test_einsum_721x1440_full_size_sampled():
     ref = oracle.einsum(W, ts)
     nrm = oracle.einsum(W.abs(), ts.abs(), abs_mode=True)
     assert normalised_error(y[:, :, hos].cpu(), ref, nrm) <= TOL_EIN["bf16"]
+
+
+def test_one_handle_from_two_streams():
+    """A psi handle is read-only after creation and may be used from several streams at once: the
+    forward and backward on one side stream, the fused op and the einsum on another, concurrently,
+    each equal bitwise to the same call on the default stream."""
+    _log("two streams")
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((2, 8, 31, 64), 3600, "bf16").to(DEV)
+    g = randn((2, 8, psi.K, 31, 64), 3601, "bf16").to(DEV)
+    W = randn((16, 8, psi.K), 3602, "bf16", std=0.1).to(DEV)
+    ref = (sgc.disco_fwd(h, x), sgc.disco_bwd(h, g), sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g))
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)  # default priority
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            o, gx = sgc.disco_fwd(h, x), sgc.disco_bwd(h, g)
+        with torch.cuda.stream(sb):
+            y, ye = sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g)
+        outs.append((o, gx, y, ye))
+    torch.cuda.synchronize()
+    for got in outs:
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
