@@ -135,10 +135,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__re
         // this thread's loads of chunk t have landed (those of chunk t + 1 may still be in flight)
         static_assert(LOADS == 4, "the wait below leaves one chunk of four loads in flight");
         if (t + 1 < nk)
-            __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt <= 4, no wait on the other counters
+            __builtin_amdgcn_s_waitcnt(0x074);  // vmcnt <= 4, lgkmcnt 0
         else
             __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // everyone's have; every wave is done with chunk t - 1, whose slot is refilled
+        // A bare barrier: __syncthreads() adds a workgroup release fence, which the compiler turns
+        // into a wait for every direct load into LDS in flight, chunk t + 1's too.  The wait above
+        // covers this thread's loads of chunk t; the compiler-level fences keep LDS accesses on
+        // their side of the barrier.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // everyone's have landed; every wave is done with chunk t - 1, whose slot is refilled
+        asm volatile("" ::: "memory");
         if (t + 2 < nk) issue(t + 2);
         const unsigned char *cur = smem + (t % kGRing) * T::kStage;
 #pragma unroll
