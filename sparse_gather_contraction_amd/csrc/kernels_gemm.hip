@@ -163,6 +163,45 @@ __global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__re
     }
 
     // lane (column r, half h) holds rows 8 (a / 4) + 4 h + a % 4 of each 32 x 32 accumulator
+    if constexpr (!OUT_F32) {
+        // bf16 output through LDS (the ring is free: the last chunk waited for every load): pass p
+        // stages the TM / WM rows of the waves with wm == p as [row][TN + 8] bf16 (the 16-byte pad
+        // puts rows 4 apart, the two lane halves, on different banks), then every thread writes
+        // 16-byte row segments instead of 2-byte elements.
+        constexpr int PR = T::TM / T::WM, PITCH = T::TN + 8;
+        static_assert(PR * PITCH * 2 <= kGRing * T::kStage, "a pass fits the ring's space");
+        bf16_t *tile = reinterpret_cast<bf16_t *>(smem);
+        const bool vec = ldc % 8 == 0 && ((uintptr_t)Cout % 16) == 0;
+#pragma unroll
+        for (int pass = 0; pass < T::WM; ++pass) {
+            __syncthreads();  // every wave is done with the ring, or with the previous pass's tile
+            if (wm == pass) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int a = 0; a < 16; ++a) {
+                            const int ml = 32 * i + 8 * (a >> 2) + 4 * h + (a & 3);
+                            tile[ml * PITCH + (T::TN / T::WN) * wn + 32 * j + r] = f32_to_bf16(d[i][j][a]);
+                        }
+            }
+            __syncthreads();
+            for (int u = tid; u < PR * (T::TN / 8); u += T::kThreads) {
+                const int ml = u / (T::TN / 8), seg = u - ml * (T::TN / 8);
+                const int m = m0 + PR * pass + ml, n = n0 + 8 * seg;
+                if (m >= M || n >= N) continue;
+                bf16_t *dst = reinterpret_cast<bf16_t *>(Cout) + (int64_t)m * ldc + n;
+                const bf16_t *src = tile + ml * PITCH + 8 * seg;
+                if (vec && n + 8 <= N) {
+                    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+                } else {
+                    for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = src[e];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
