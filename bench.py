@@ -178,6 +178,8 @@ def main():
     nxt = None
     if not args.no_next_rows and "fused" in ops:
         nxt = {"fused_bwd": time_fused_bwd(sgc, torch, np, h_u, tensors, wu, psi_u, dev, stream)}
+        nxt["fused_saved"] = time_fused_saved(sgc, torch, np, h_u, tensors, wu, dev, stream)
+        nxt["fused_saved"]["recompute_step_ms"] = round(per["fused"]["ms"] + nxt["fused_bwd"]["ms"], 4)
         nxt["f16"] = time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream)
         nxt["page_shapes"] = time_page_shapes(sgc, torch, np, dev, stream)
 
@@ -345,6 +347,43 @@ def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps
             "workspace_bytes": int(ws.numel()),
             "shape": {"B": w.B, "C": w.C, "Co": w.Co, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo]}}
 
+
+
+def time_fused_saved(sgc, torch, np, h, tensors, w, dev, stream, warm=2, reps=3):
+    """A training step of the fused convolution that keeps its contraction: disco_fused_conv_save
+    (y and out = F x, 17 GB of bf16 written) then disco_fused_conv_bwd_saved (no recompute of F x),
+    timed apart from the step; compare `recompute_step_ms` (fused op + the recomputing backward)."""
+    from disco_inputs import randn
+
+    gy = randn((w.B, w.Co, w.Ho, w.Wo), 3100, "bf16").to(dev)
+    x, W = tensors["x5"], tensors["W5"]
+    y = torch.empty((w.B, w.Co, w.Ho, w.Wo), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.B, w.C, w.K, w.Ho, w.Wo), dtype=torch.bfloat16, device=dev)
+    gx = torch.empty_like(x)
+    dW = torch.empty_like(W)
+    ws = torch.empty(sgc.disco_fused_conv_bwd_workspace(h, w.B, w.C, w.Co), dtype=torch.uint8, device=dev)
+    fns = {"fwd_save": lambda: sgc.disco_fused_conv_save(h, x, W, y, out),
+           "bwd_saved": lambda: sgc.disco_fused_conv_bwd_saved(h, out, W, gy, gx, dW, workspace=ws)}
+    res = {}
+    for name, fn in fns.items():
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(float(np.mean([a.elapsed_time(b) for a, b in ev])), 4)
+    res["step_ms"] = round(res["fwd_save_ms"] + res["bwd_saved_ms"], 4)
+    del out, ws
+    torch.cuda.empty_cache()
+    print(f"[bench] fused training step keeping the contraction: {res}", file=sys.stderr, flush=True)
+    return res
 
 def time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream, warm=1, reps=3):
     """The three ops of the step with fp16 data (same shapes and psi), timed apart from the step;

@@ -118,6 +118,14 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
 
+/* Fused convolution that also keeps its contraction, for a training step whose backward then need not
+ * recompute it: y as disco_fused_conv, and out[b,c,k,ho,wo] = the contraction F x (B, C, K, Ho, Wo) in
+ * the data type — the very values the einsum multiplied (each fp32 accumulator rounded once, RNE).
+ * Same page, "Python dispatch layer": the fused autograd function keeps what its backward needs.
+ * BF16 and F16.  out is caller-owned and overwritten; it must not alias x, W or y. */
+disco_status disco_fused_conv_save(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
+                                   disco_tensor *out, void *stream);
+
 /* The einsum alone: the second half of the fused convolution, for a contraction that is already
  * in device memory (for instance the forward's output kept for the weight gradient).  Same page,
  * "Architecture snapshot" ("contraction + einsum"):
@@ -145,6 +153,14 @@ disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, i
 disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disco_tensor *W, const disco_tensor *gy,
                                   disco_tensor *gx, disco_tensor *dW, void *workspace, size_t workspace_bytes,
                                   void *stream);
+
+/* The same backward with the weight gradient's operand taken from `out`, the contraction that
+ * disco_fused_conv_save wrote for the same x, instead of recomputing it from x (x is not needed).
+ * out: (B, C, K, Ho, Wo); the other arguments, the workspace and the results as disco_fused_conv_bwd,
+ * whose results it reproduces bitwise when out comes from disco_fused_conv_save. */
+disco_status disco_fused_conv_bwd_saved(disco_psi h, const disco_tensor *out, const disco_tensor *W,
+                                        const disco_tensor *gy, disco_tensor *gx, disco_tensor *dW, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char *disco_last_error(void);

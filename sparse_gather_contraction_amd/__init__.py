@@ -37,7 +37,8 @@ DISCO_F32 = 0
 DISCO_BF16 = 1
 DISCO_F16 = 2
 EXPORTED = ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
-            "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd", "disco_last_error")
+            "disco_fused_conv_save", "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd",
+            "disco_fused_conv_bwd_saved", "disco_last_error")
 
 
 class DiscoError(RuntimeError):
@@ -76,12 +77,15 @@ def load_library():
         lib.disco_fused_conv.argtypes = [P, ctypes.POINTER(TensorDesc), ctypes.POINTER(TensorDesc),
                                          ctypes.POINTER(TensorDesc), P]
         lib.disco_einsum.argtypes = [ctypes.POINTER(TensorDesc)] * 3 + [P]
+        lib.disco_fused_conv_save.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 4 + [P]
+        lib.disco_fused_conv_bwd_saved.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 5 + [P, ctypes.c_size_t, P]
         lib.disco_fused_conv_bwd_workspace.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                        ctypes.POINTER(ctypes.c_size_t)]
         lib.disco_fused_conv_bwd.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 5 + [P, ctypes.c_size_t, P]
         lib.disco_last_error.restype = ctypes.c_char_p
         for f in ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
-                  "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd"):
+                  "disco_fused_conv_save", "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd",
+                  "disco_fused_conv_bwd_saved"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -199,6 +203,20 @@ def disco_fused_conv(psi: Psi, x, W, y=None):
 
 
 
+
+def disco_fused_conv_save(psi: Psi, x, W, y=None, out=None):
+    """(y, out): the fused convolution and the contraction F x it multiplied (kept for the backward)."""
+    import torch
+
+    if y is None:
+        y = torch.empty((x.shape[0], W.shape[0], psi.Ho, psi.Wo), dtype=x.dtype, device=x.device)
+    if out is None:
+        out = torch.empty((x.shape[0], x.shape[1], psi.K, psi.Ho, psi.Wo), dtype=x.dtype, device=x.device)
+    xd, wd, yd, od = tensor_desc(x), tensor_desc(W), tensor_desc(y), tensor_desc(out)
+    _check(load_library().disco_fused_conv_save(psi.handle, ctypes.byref(xd), ctypes.byref(wd), ctypes.byref(yd),
+                                                ctypes.byref(od), _stream(x.device)))
+    return y, out
+
 def disco_einsum(W, t, y=None):
     """y[b, o, ho, wo] = sum_{c,k} W[o, c, k] t[b, c, k, ho, wo] on the current device (no psi)."""
     import torch
@@ -232,4 +250,23 @@ def disco_fused_conv_bwd(psi: Psi, x, W, gy, gx=None, dW=None, workspace=None):
     _check(load_library().disco_fused_conv_bwd(psi.handle, *[ctypes.byref(d) for d in descs],
                                                ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                                _stream(x.device)))
+    return gx, dW
+
+
+def disco_fused_conv_bwd_saved(psi: Psi, out, W, gy, gx=None, dW=None, workspace=None):
+    """(gx, dW) as disco_fused_conv_bwd, with the contraction `out` from disco_fused_conv_save in place of x."""
+    import torch
+
+    B, C = out.shape[0], out.shape[1]
+    if gx is None:
+        gx = torch.empty((B, C, psi.Hi, psi.Wi), dtype=out.dtype, device=out.device)
+    if dW is None:
+        dW = torch.empty_like(W)
+    need = disco_fused_conv_bwd_workspace(psi, B, C, W.shape[0])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=out.device)
+    descs = [tensor_desc(t) for t in (out, W, gy, gx, dW)]
+    _check(load_library().disco_fused_conv_bwd_saved(psi.handle, *[ctypes.byref(d) for d in descs],
+                                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                                     _stream(out.device)))
     return gx, dW

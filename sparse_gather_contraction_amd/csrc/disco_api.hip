@@ -250,6 +250,12 @@ disco_status check_handle(disco_psi h)
     return DISCO_OK;
 }
 
+bool getenv_is0(const char *name)  // test knobs: "0" turns a kernel path off
+{
+    const char *e = getenv(name);
+    return e && strcmp(e, "0") == 0;
+}
+
 bool staged_env_off()
 {
     const char *e = getenv("DISCO_STAGED");  // test knob: "0" forces the plain gather kernel
@@ -611,8 +617,11 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
     return enqueue_bwd(h, gout->data, gx->data, gout->dtype, B, C, (hipStream_t)stream);
 }
 
-disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
-                              void *stream)
+namespace {
+
+// The fused convolution; with `save` it also writes the contraction (B, C, K, Ho, Wo).
+disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
+                             disco_tensor *save, void *stream)
 {
     disco_status st = check_handle(h);
     if (st != DISCO_OK) return st;
@@ -630,11 +639,19 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     if ((st = check_tensor(y, "y", 4, ys, h->device)) != DISCO_OK) return st;
     if (x->dtype != W->dtype || x->dtype != y->dtype) return fail(DISCO_ERR_DTYPE, "x, W and y dtypes differ");
     if (x->dtype == DISCO_F32) return fail(DISCO_ERR_DTYPE, "the fused convolution supports bf16 and fp16 only");
+    if (save) {
+        const int64_t os[5] = {B, C, h->K, h->Ho, h->Wo};
+        if ((st = check_tensor(save, "out", 5, os, h->device)) != DISCO_OK) return st;
+        if (save->dtype != x->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
+    }
+    if (save && B * C * h->Ho * h->Wo > 0 && (B * Co == 0 || !h->fused.ok || getenv_is0("DISCO_FUSED_MFMA"))) {
+        // no matrix-core fused kernel to keep the contraction from: the forward writes it
+        if ((st = enqueue_fwd(h, x->data, save->data, x->dtype, B, C, (hipStream_t)stream)) != DISCO_OK) return st;
+    }
     if (B * Co * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
     if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
         return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
-    const char *fm = getenv("DISCO_FUSED_MFMA");  // test knob: "0" forces the VALU-contraction fused kernel
-    if (h->fused.ok && !(fm && strcmp(fm, "0") == 0)) {
+    if (h->fused.ok && !getenv_is0("DISCO_FUSED_MFMA")) {  // test knob: "0" forces the VALU-contraction fused kernel
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
         m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs;
@@ -647,6 +664,7 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
         m.max_piece_bytes = h->fused.max_piece_bytes;
         m.max_resident_bytes = h->fused.max_resident_bytes;
         m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
+        m.save = save ? save->data : nullptr;
         hipError_t e = disco::launch_fused_mfma(m, (hipStream_t)stream);
         if (e != hipSuccess)
             return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));
@@ -668,6 +686,21 @@ disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_te
     hipError_t e = disco::launch_fused(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));
     return DISCO_OK;
+}
+
+}  // namespace
+
+disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
+                              void *stream)
+{
+    return fused_conv_impl(h, x, W, y, nullptr, stream);
+}
+
+disco_status disco_fused_conv_save(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
+                                   disco_tensor *out, void *stream)
+{
+    if (!out) return fail(DISCO_ERR_INVALID_ARGUMENT, "out is NULL");
+    return fused_conv_impl(h, x, W, y, out, stream);
 }
 
 
@@ -727,28 +760,37 @@ disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, i
     return DISCO_OK;
 }
 
-disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disco_tensor *W, const disco_tensor *gy,
-                                  disco_tensor *gx, disco_tensor *dW, void *workspace, size_t workspace_bytes,
-                                  void *stream)
+namespace {
+
+// Backward of the fused convolution; the dW operand out = F x is recomputed from x, or taken from
+// `saved` (the contraction disco_fused_conv_save wrote) when x is NULL.
+disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco_tensor *saved, const disco_tensor *W,
+                                 const disco_tensor *gy, disco_tensor *gx, disco_tensor *dW, void *workspace,
+                                 size_t workspace_bytes, void *stream)
 {
     disco_status st = check_handle(h);
     if (st != DISCO_OK) return st;
-    if (!x || !W || !gy || !gx || !dW) return fail(DISCO_ERR_INVALID_ARGUMENT, "x, W, gy, gx or dW is NULL");
-    if (x->ndim != 4) return fail(DISCO_ERR_SHAPE, "x must be (B, C, Hi, Wi)");
+    const disco_tensor *src = x ? x : saved;
+    if (!src || !W || !gy || !gx || !dW)
+        return fail(DISCO_ERR_INVALID_ARGUMENT, x || !saved ? "x, W, gy, gx or dW is NULL" : "out, W, gy, gx or dW is NULL");
+    if (x && x->ndim != 4) return fail(DISCO_ERR_SHAPE, "x must be (B, C, Hi, Wi)");
+    if (!x && saved->ndim != 5) return fail(DISCO_ERR_SHAPE, "out must be (B, C, K, Ho, Wo)");
     if (W->ndim != 3) return fail(DISCO_ERR_SHAPE, "W must be (Co, C, K)");
-    const int64_t B = x->shape[0], C = x->shape[1], Co = W->shape[0];
+    const int64_t B = src->shape[0], C = src->shape[1], Co = W->shape[0];
     if (B < 0 || C < 0 || Co < 0) return fail(DISCO_ERR_SHAPE, "negative batch or channel count");
     const int64_t xs[4] = {B, C, h->Hi, h->Wi};
+    const int64_t os[5] = {B, C, h->K, h->Ho, h->Wo};
     const int64_t ws[3] = {Co, C, h->K};
     const int64_t ys[4] = {B, Co, h->Ho, h->Wo};
-    if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
+    if (x && (st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
+    if (!x && (st = check_tensor(saved, "out", 5, os, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(W, "W", 3, ws, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(gy, "gy", 4, ys, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(dW, "dW", 3, ws, h->device)) != DISCO_OK) return st;
-    if (x->dtype != W->dtype || x->dtype != gy->dtype || x->dtype != gx->dtype || x->dtype != dW->dtype)
-        return fail(DISCO_ERR_DTYPE, "x, W, gy, gx and dW dtypes differ");
-    if (x->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution backward supports bf16 only");
+    if (src->dtype != W->dtype || src->dtype != gy->dtype || src->dtype != gx->dtype || src->dtype != dW->dtype)
+        return fail(DISCO_ERR_DTYPE, x ? "x, W, gy, gx and dW dtypes differ" : "out, W, gy, gx and dW dtypes differ");
+    if (src->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution backward supports bf16 only");
     if (h->K > 256) return fail(DISCO_ERR_SHAPE, "the fused convolution backward supports K <= 256");
     const FusedBwdLayout L = fused_bwd_layout(h, B, C, Co);
     if (Co % 8 != 0 || L.N % 8 != 0)
@@ -767,7 +809,8 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
     char *ws_c = (char *)workspace;
     uint16_t *wt = (uint16_t *)(ws_c + L.wt), *gyt = (uint16_t *)(ws_c + L.gyt), *gbuf = (uint16_t *)(ws_c + L.gbuf);
     float *part = (float *)(ws_c + L.part);
-    const uint16_t *xp = (const uint16_t *)x->data, *gyp = (const uint16_t *)gy->data;
+    const uint16_t *xp = x ? (const uint16_t *)x->data : nullptr, *gyp = (const uint16_t *)gy->data;
+    const uint16_t *svp = x ? nullptr : (const uint16_t *)saved->data;  // saved contraction (B, C, K, N)
     uint16_t *gxp = (uint16_t *)gx->data;
     const int64_t K = h->K, N = L.N, CK = C * K, plane_in = (int64_t)h->Hi * h->Wi;
     hipError_t e;
@@ -794,9 +837,10 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
         if ((st = enqueue_bwd(h, gb, gxp + c0 * plane_in, DISCO_BF16, B, cc, sm, gstride, C * plane_in)) != DISCO_OK)
             return st;
         // out[b][c k][n] = (F x)[b, c0 + c]: the fused kernel's contraction (psi resident across the
-        // chunk's channels) where its plan exists, else the forward contraction
-        const char *fc = getenv("DISCO_FUSED_MFMA");  // test knob: "0" also turns this path off
-        if (h->fused.ok && !(fc && strcmp(fc, "0") == 0)) {
+        // chunk's channels) where its plan exists, else the forward contraction; nothing to compute
+        // when the caller kept the contraction
+        if (svp) {
+        } else if (h->fused.ok && !getenv_is0("DISCO_FUSED_MFMA")) {  // test knob: "0" also turns this path off
             disco::FusedContractLaunch m;
             m.x = xp + c0 * plane_in; m.out = gb;
             m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs; m.adata = h->fused.adata;
@@ -816,7 +860,8 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
             // partial dW[o][c k] over each position split
             disco::GemmNtLaunch g2;
             g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);
-            g2.B = gb + b * gstride; g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
+            g2.B = svp ? svp + (b * C + c0) * K * N : gb + b * gstride;
+            g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
             g2.Kd = (int32_t)N; g2.k_per_split = L.kps; g2.out_f32 = true;
             g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc;
             if ((e = disco::launch_gemm_nt(g2, sm)) != hipSuccess) return hipfail(e, "gy out^T product");
@@ -826,6 +871,24 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
             return hipfail(e, "dW reduction");
     }
     return DISCO_OK;
+}
+
+}  // namespace
+
+disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disco_tensor *W, const disco_tensor *gy,
+                                  disco_tensor *gx, disco_tensor *dW, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    if (!x) return fail(DISCO_ERR_INVALID_ARGUMENT, "x is NULL");
+    return fused_conv_bwd_impl(h, x, nullptr, W, gy, gx, dW, workspace, workspace_bytes, stream);
+}
+
+disco_status disco_fused_conv_bwd_saved(disco_psi h, const disco_tensor *out, const disco_tensor *W,
+                                        const disco_tensor *gy, disco_tensor *gx, disco_tensor *dW, void *workspace,
+                                        size_t workspace_bytes, void *stream)
+{
+    if (!out) return fail(DISCO_ERR_INVALID_ARGUMENT, "out is NULL");
+    return fused_conv_bwd_impl(h, nullptr, out, W, gy, gx, dW, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

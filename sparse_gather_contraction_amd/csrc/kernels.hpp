@@ -74,6 +74,7 @@ struct FusedMfmaLaunch {
     uint32_t desc_bytes, adata_bytes;  // sizes of the descriptor and psi arrays
     bool f16;     // fp16 data and psi (adata then holds fp16 psi * 2^e)
     float scale;  // 2^-e for fp16, 1 for bf16
+    void *save = nullptr;  // non-null: also write the contraction (B, C, K, Ho, Wo), data type, contiguous
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);

@@ -79,6 +79,10 @@ struct Ctx {
     bf16_t *out;
     int64_t out_bstride;
     int Ho, ho;
+    // fused op that also keeps its contraction: save[b, c, k, ho, wo] at save + b * save_bstride
+    bf16_t *save;
+    int64_t save_bstride;
+    bool vec_save;  // save rows are 16-byte aligned
 };
 
 // ---- 16-bit operand types ----------------------------------------------------------------------
@@ -387,8 +391,43 @@ __device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d
     }
 }
 
+// Fused op that keeps its contraction: chunk t's result (channels kCh t .. + 3), read back from the
+// einsum's operand exchange — the fp32 accumulators rounded to the data type, exactly the values
+// the einsum multiplied and the values the contraction-only mode writes — to save[b, c, k, ho, ...]
+// as 16-byte row segments.  Exchange unit (pp, h2, cl, ph), lane (r, hh) holds basis 8 hh .. + 7
+// of longitude px0 + 8 r + 2 pp + ph, channel kCh t + 2 h2 + cl.  Called after the einsum (every
+// wave's operands are in the exchange); the exchange is overwritten only after the next step's
+// opening barrier.
+__device__ __forceinline__ void save_contraction(const Ctx &c, const unsigned char *__restrict__ xch, int t)
+{
+    const int64_t HoL = (int64_t)c.Ho * c.L;
+    for (int u = c.tid; u < kCh * 16 * 32; u += kThreads) {
+        const int r = u & 31, row = u >> 5, k = row & 15, chl = row >> 4;
+        const int ch = kCh * t + chl, wo = c.px0 + 8 * r;
+        if (k >= c.K || ch >= c.C || wo >= c.L) continue;
+        const int h2 = chl >> 1, cl = chl & 1;
+        const unsigned char *src = xch + 1024 * ((h2 * 2 + cl) * 2) + 16 * (r + 32 * (k >> 3)) + 2 * (k & 7);
+        uint16_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)  // q = 2 pp + ph: unit offset 1024 (8 pp + ph)
+            v[q] = *reinterpret_cast<const uint16_t *>(src + 1024 * (8 * (q >> 1) + (q & 1)));
+        bf16_t *dst = c.save + (int64_t)c.b * c.save_bstride + ((int64_t)ch * c.K + k) * HoL + (int64_t)c.ho * c.L + wo;
+        if (c.vec_save && wo + 8 <= c.L) {
+            uint4 w;
+            w.x = v[0] | ((uint32_t)v[1] << 16);
+            w.y = v[2] | ((uint32_t)v[3] << 16);
+            w.z = v[4] | ((uint32_t)v[5] << 16);
+            w.w = v[6] | ((uint32_t)v[7] << 16);
+            *reinterpret_cast<uint4 *>(dst) = w;
+        } else {
+            for (int e = 0; e < 8 && wo + e < c.L; ++e) dst[e] = v[e];
+        }
+    }
+}
+
 // EIN: fused op (einsum into yacc); else contraction-only (the chunk's result is written out).
-template <int NOTH, bool F16, bool EIN>
+// SAVE (with EIN): the fused op also writes each chunk's contraction to c.save.
+template <int NOTH, bool F16, bool EIN, bool SAVE = false>
 __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict__ pieces, int p_begin, int npieces,
                                          int nsteps, int st, int t, int p, unsigned char *__restrict__ cur,
                                          unsigned char *__restrict__ nxt, unsigned char *__restrict__ wb, int a_lane2,
@@ -410,6 +449,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // W slice visible; `cur` free for the exchange
             einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
+            if constexpr (SAVE) save_contraction(c, cur, t);
         } else {
             store_contraction<F16>(c, d, t, pp, h2, wb);
         }
@@ -417,7 +457,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
 }
 
 // One chunk of a latitude whose psi stays resident: only the x windows stream (double-buffered).
-template <int NOTH, bool F16, bool EIN>
+template <int NOTH, bool F16, bool EIN, bool SAVE = false>
 __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &pc, int nchunks, int t,
                                                    const unsigned char *__restrict__ stage,
                                                    unsigned char *__restrict__ cur, unsigned char *__restrict__ nxt,
@@ -435,19 +475,20 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
         einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
+        if constexpr (SAVE) save_contraction(c, cur, t);
     } else {
         store_contraction<F16>(c, d, t, pp, h2, wb);
     }
 }
 
-template <int NOT, bool F16, bool EIN>
+template <int NOT, bool F16, bool EIN, bool SAVE = false>
 __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ W, bf16_t *__restrict__ y,
     const FPiece *__restrict__ pieces, const FRow *__restrict__ rows, const int32_t *__restrict__ descs,
     const bf16_t *__restrict__ adata, const int32_t *__restrict__ ho_piece, const int32_t *__restrict__ ho_order,
     int B, int C, int Co, int K, int Ho, int L, int Hi, int Wi, int s, int n_pxb, int n_ob, int buf_bytes,
     uint32_t desc_bytes, uint32_t adata_bytes, int vec_x, int vec_w, int vec_out, float scale, int64_t x_bstride,
-    int64_t out_bstride)
+    int64_t out_bstride, bf16_t *__restrict__ save, int64_t save_bstride, int vec_save)
 {
     // vec_w: W rows load as 16-byte runs; vec_out: output rows (y, or out in contraction-only mode) start 16-byte aligned
     constexpr int NOTH = NOT / 2;
@@ -485,6 +526,9 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     c.out_bstride = out_bstride;
     c.Ho = Ho;
     c.ho = ho;
+    c.save = save;
+    c.save_bstride = save_bstride;
+    c.vec_save = vec_save != 0;
 
     // lane constants: A row r = lane % 32 is (phase 2 pp + r / 16, MFMA row m = r % 16 -> basis k);
     // the basis order puts k = 8h + a in result register a of lane half h
@@ -525,10 +569,10 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_psi(c, pc0, stage);
         stage_windows<kCh>(c, pc0, 0, reinterpret_cast<bf16_t *>(w0));
         for (int t = 0; t < nchunks; t += 2) {
-            run_chunk_resident<NOTH, F16, EIN>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d,
+            run_chunk_resident<NOTH, F16, EIN, SAVE>(c, pc0, nchunks, t, stage, w0, w1, wb, a_lane2, x_lane2, odd, pp, h2, d,
                                                yacc);
             if (t + 1 < nchunks)
-                run_chunk_resident<NOTH, F16, EIN>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
+                run_chunk_resident<NOTH, F16, EIN, SAVE>(c, pc0, nchunks, t + 1, stage, w1, w0, wb, a_lane2, x_lane2, odd, pp, h2, d,
                                          yacc);
         }
     } else if (nsteps > 0) {
@@ -536,11 +580,11 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
         stage_step<kCh>(c, pieces[p_begin], 0, buf0);
         int t = 0, p = 0;
         for (int st = 0; st < nsteps; st += 2) {
-            run_step<NOTH, F16, EIN>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
+            run_step<NOTH, F16, EIN, SAVE>(c, pieces, p_begin, npieces, nsteps, st, t, p, buf0, buf1, wb, a_lane2, x_lane2, odd, pp, h2, d,
                            yacc);
             if (++p == npieces) { p = 0; ++t; }
             if (st + 1 < nsteps) {
-                run_step<NOTH, F16, EIN>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
+                run_step<NOTH, F16, EIN, SAVE>(c, pieces, p_begin, npieces, nsteps, st + 1, t, p, buf1, buf0, wb, a_lane2, x_lane2, odd, pp,
                                h2, d, yacc);
                 if (++p == npieces) { p = 0; ++t; }
             }
@@ -796,7 +840,8 @@ hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t strea
     hipLaunchKernelGGL((fused_mfma_kernel<2, F16, false>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,      \
                        (const bf16_t *)a.x, (const bf16_t *)nullptr, (bf16_t *)a.out, a.pieces, a.rows, a.descs,      \
                        (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, 0, a.K, a.Ho, a.Wo, a.Hi, a.Wi,     \
-                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, 0, vec_out, a.scale, x_bs, out_bs)
+                       a.s, n_pxb, 1, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, 0, vec_out, a.scale, x_bs, out_bs,  \
+                       (bf16_t *)nullptr, (int64_t)0, 0)
     if (a.f16) DISCO_CONTRACT_LAUNCH(true);
     else DISCO_CONTRACT_LAUNCH(false);
 #undef DISCO_CONTRACT_LAUNCH
@@ -822,12 +867,11 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
     const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
     const size_t lds = fused_mfma_lds_bytes(n_ot, a.max_piece_bytes, a.max_resident_bytes);
-    const void *fn = a.f16 ? (n_ot == 2   ? (const void *)fused_mfma_kernel<2, true, true>
-                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, true, true>
-                                          : (const void *)fused_mfma_kernel<8, true, true>)
-                           : (n_ot == 2   ? (const void *)fused_mfma_kernel<2, false, true>
-                              : n_ot == 4 ? (const void *)fused_mfma_kernel<4, false, true>
-                                          : (const void *)fused_mfma_kernel<8, false, true>);
+    const bool sv = a.save != nullptr;
+#define DISCO_FUSED_FN(N, F16) (sv ? (const void *)fused_mfma_kernel<N, F16, true, true> : (const void *)fused_mfma_kernel<N, F16, true, false>)
+    const void *fn = a.f16 ? (n_ot == 2 ? DISCO_FUSED_FN(2, true) : n_ot == 4 ? DISCO_FUSED_FN(4, true) : DISCO_FUSED_FN(8, true))
+                           : (n_ot == 2 ? DISCO_FUSED_FN(2, false) : n_ot == 4 ? DISCO_FUSED_FN(4, false) : DISCO_FUSED_FN(8, false));
+#undef DISCO_FUSED_FN
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pxb;
@@ -838,12 +882,21 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
     const int vec_y = (a.Wo % 8 == 0 && ((uintptr_t)a.y % 16) == 0) ? 1 : 0;
     const int64_t x_bs = (int64_t)a.C * a.Hi * a.Wi;
+    const int64_t save_bs = (int64_t)a.C * a.K * a.Ho * a.Wo;  // save is (B, C, K, Ho, Wo), contiguous
+    const int vec_save = (sv && a.Wo % 8 == 0 && ((uintptr_t)a.save % 16) == 0) ? 1 : 0;
 #define DISCO_FUSED_LAUNCH(N, F16)                                                                               \
-    hipLaunchKernelGGL((fused_mfma_kernel<N, F16, true>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,       \
-                       (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows, a.descs,            \
-                       (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi,  \
-                       a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, vec_y, a.scale, x_bs,  \
-                       (int64_t)0)
+    if (sv)                                                                                                      \
+        hipLaunchKernelGGL((fused_mfma_kernel<N, F16, true, true>), dim3((unsigned)nblk), dim3(kThreads), lds,     \
+                           stream, (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows,         \
+                           a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, \
+                           a.Hi, a.Wi, a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, vec_y, \
+                           a.scale, x_bs, (int64_t)0, (bf16_t *)a.save, save_bs, vec_save);                          \
+    else                                                                                                         \
+        hipLaunchKernelGGL((fused_mfma_kernel<N, F16, true, false>), dim3((unsigned)nblk), dim3(kThreads), lds,    \
+                           stream, (const bf16_t *)a.x, (const bf16_t *)a.W, (bf16_t *)a.y, a.pieces, a.rows,         \
+                           a.descs, (const bf16_t *)a.adata, a.ho_piece, a.ho_order, a.B, a.C, a.Co, a.K, a.Ho, a.Wo, \
+                           a.Hi, a.Wi, a.s, n_pxb, n_ob, buf_bytes, a.desc_bytes, a.adata_bytes, vec_x, vec_w, vec_y, \
+                           a.scale, x_bs, (int64_t)0, (bf16_t *)nullptr, (int64_t)0, 0)
     if (a.f16) {
         switch (n_ot) {
         case 2: DISCO_FUSED_LAUNCH(2, true); break;

@@ -705,3 +705,66 @@ def test_one_handle_from_two_streams():
     for got in outs:
         for a, b in zip(got, ref):
             assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- fused op that keeps its contraction
+
+@pytest.mark.parametrize("geom,B,C,Co", [
+    ((31, 64, 31, 64, 0.5, 4, 4), 2, 12, 24),   # three 4-channel chunks, Co below one 32-row tile
+    ((33, 128, 17, 64, 0.6, 4, 4), 1, 7, 40),   # s = 2, ragged channel chunk and output tiles
+])
+def test_fused_save_and_saved_backward(geom, B, C, Co):
+    """disco_fused_conv_save: y equal bitwise to disco_fused_conv, the kept contraction within the bar of
+    the oracle's forward; disco_fused_conv_bwd_saved on it equal bitwise to disco_fused_conv_bwd."""
+    _log(f"fused save {geom} B={B} C={C} Co={Co}")
+    psi = build_psi(*geom)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((B, C, psi.Hi, psi.Wi), 3700 + C, "bf16").to(DEV)
+    W = randn((Co, C, psi.K), 3701 + C, "bf16", std=0.1).to(DEV)
+    gy = randn((B, Co, psi.Ho, psi.Wo), 3702 + C, "bf16").to(DEV)
+    y0 = sgc.disco_fused_conv(h, x, W)
+    y, out = sgc.disco_fused_conv_save(h, x, W)
+    gx0, dW0 = sgc.disco_fused_conv_bwd(h, x, W, gy)
+    gx, dW = sgc.disco_fused_conv_bwd_saved(h, out, W, gy)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    xc = x.cpu()
+    assert normalised_error(out.cpu(), oracle.fwd(psi, xc), oracle.fwd(psi, xc.abs(), abs_mode=True)) <= TOL["bf16"]
+    assert torch.equal(gx, gx0) and torch.equal(dW, dW0)
+
+
+def test_fused_save_fallback_path(monkeypatch):
+    """Without the matrix-core fused kernel the contraction is kept by the forward kernel; both
+    results within the bar of the oracle."""
+    monkeypatch.setenv("DISCO_FUSED_MFMA", "0")
+    psi = build_psi(31, 60, 31, 60, 0.5, 4, 4)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((1, 6, 31, 60), 3710, "bf16")
+    W = randn((16, 6, psi.K), 3711, "bf16", std=0.1)
+    y, out = sgc.disco_fused_conv_save(h, x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    assert normalised_error(out.cpu(), oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL["bf16"]
+    assert normalised_error(y.cpu(), oracle.fused(psi, x, W), oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)) <= TOL["bf16"]
+
+
+def test_fused_save_721x1440_full_size():
+    """The fused workload (B=2, C=Co=256, K=16, 721x1440) as the bench times it: y of the saving
+    forward equal bitwise to the fused op's, and the saved backward equal bitwise to the recomputing
+    one (which the oracle checks at this size in test_fused_bwd_721x1440_full_size_sampled)."""
+    w = WORKLOADS["fused_bf16_721x1440"]
+    _log("fused save 721x1440")
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = workload_x(w).to(DEV)
+    W = workload_weight(w).to(DEV)
+    gy = randn((w.B, w.Co, w.Ho, w.Wo), 3720, "bf16").to(DEV)
+    y0 = sgc.disco_fused_conv(h, x, W)
+    y, out = sgc.disco_fused_conv_save(h, x, W)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    del y0
+    ws = torch.empty(sgc.disco_fused_conv_bwd_workspace(h, w.B, w.C, w.Co), dtype=torch.uint8, device=DEV)
+    gx0, dW0 = sgc.disco_fused_conv_bwd(h, x, W, gy, workspace=ws)
+    gx, dW = sgc.disco_fused_conv_bwd_saved(h, out, W, gy, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(gx, gx0) and torch.equal(dW, dW0)
