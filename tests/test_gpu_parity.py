@@ -768,3 +768,30 @@ def test_fused_save_721x1440_full_size():
     gx, dW = sgc.disco_fused_conv_bwd_saved(h, out, W, gy, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(gx, gx0) and torch.equal(dW, dW0)
+
+
+def test_fused_save_rejects_bad_arguments():
+    """The saving forward and the saved backward validate `out` before anything is enqueued; rejected
+    calls leave every output untouched."""
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((1, 4, 31, 64), 3730, "bf16").to(DEV)
+    W = randn((8, 4, psi.K), 3731, "bf16").to(DEV)
+    gy = randn((1, 8, 31, 64), 3732, "bf16").to(DEV)
+    y = nan_like((1, 8, 31, 64), torch.bfloat16)
+    out_bad = nan_like((1, 4, psi.K - 1, 31, 64), torch.bfloat16)
+    for out, name in ((out_bad, "DISCO_ERR_SHAPE"), (nan_like((1, 4, psi.K, 31, 64), torch.float16), "DISCO_ERR_DTYPE")):
+        with pytest.raises(sgc.DiscoError) as e:
+            sgc.disco_fused_conv_save(h, x, W, y, out)
+        assert e.value.status_name == name
+    lib = sgc.load_library()
+    descs = [sgc.tensor_desc(t) for t in (x, W, y)]
+    st = lib.disco_fused_conv_save(h.handle, *[ctypes.byref(d) for d in descs], None, sgc._stream(DEV))
+    assert sgc.STATUS_NAMES[st] == "DISCO_ERR_INVALID_ARGUMENT"
+    gx = nan_like((1, 4, 31, 64), torch.bfloat16)
+    dW = nan_like((8, 4, psi.K), torch.bfloat16)
+    with pytest.raises(sgc.DiscoError) as e:
+        sgc.disco_fused_conv_bwd_saved(h, out_bad, W, gy, gx, dW)
+    assert e.value.status_name == "DISCO_ERR_SHAPE"
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(y)) and torch.all(torch.isnan(gx)) and torch.all(torch.isnan(dW))
