@@ -1,5 +1,6 @@
 // disco_api.hip — C ABI of libdisco.so: validation, plan upload and launches.
 #include <atomic>
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -254,6 +255,25 @@ bool getenv_is0(const char *name)  // test knobs: "0" turns a kernel path off
 {
     const char *e = getenv(name);
     return e && strcmp(e, "0") == 0;
+}
+
+// A second stream per device (default priority), created on first use and kept for the life of the
+// process, for work that can overlap the caller's stream inside one call.  nullptr if it cannot be made.
+hipStream_t side_stream(int device)
+{
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    if (device < 0 || device >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[device]) {
+        hipStream_t s = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        streams[device] = s;
+    }
+    return streams[device];
 }
 
 bool staged_env_off()
@@ -819,6 +839,48 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
     for (int64_t b = 0; b < B; ++b)
         if ((e = disco::launch_transpose_bf16(gyp + b * Co * N, gyt + b * N * Co, (int)Co, (int)N, sm)) != hipSuccess)
             return hipfail(e, "gy transpose");
+    // dW partials of chunk c0 (gy times the contraction, over S position splits) and their fixed-order sum
+    auto dw_chunk = [&](int64_t c0, int32_t Mc, const uint16_t *outp, int64_t ostride, hipStream_t sd) -> disco_status {
+        for (int64_t b = 0; b < B; ++b) {
+            disco::GemmNtLaunch g2;
+            g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);
+            g2.B = outp + b * ostride; g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
+            g2.Kd = (int32_t)N; g2.k_per_split = L.kps; g2.out_f32 = true;
+            g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc;
+            if ((e = disco::launch_gemm_nt(g2, sd)) != hipSuccess) return hipfail(e, "gy out^T product");
+        }
+        if ((e = disco::launch_reduce_partials(part, (int)(B * L.S), (int)Co, Mc, dW->data, CK, (int)(c0 * K), sd)) !=
+            hipSuccess)
+            return hipfail(e, "dW reduction");
+        return DISCO_OK;
+    };
+    // With the contraction kept, dW depends on the inputs only: it runs on a second stream, overlapping
+    // the chain W^T gy -> transpose contraction on the caller's stream (ordered by events at both ends).
+    struct Events {
+        hipEvent_t in = nullptr, done = nullptr;
+        ~Events() {
+            if (in) (void)hipEventDestroy(in);
+            if (done) (void)hipEventDestroy(done);
+        }
+    } ev;
+    hipStream_t sd = sm;
+    if (svp && C > 0) {
+        hipStream_t side = side_stream(h->device);
+        if (side && hipEventCreateWithFlags(&ev.in, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ev.done, hipEventDisableTiming) == hipSuccess &&
+            hipEventRecord(ev.in, sm) == hipSuccess && hipStreamWaitEvent(side, ev.in, 0) == hipSuccess) {
+            sd = side;
+        } else {
+            (void)hipGetLastError();  // no second stream: everything on the caller's
+        }
+        for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
+            const int32_t Mc = (int32_t)(std::min<int64_t>(L.Cc, C - c0) * K);
+            if ((st = dw_chunk(c0, Mc, svp + c0 * K * N, C * K * N, sd)) != DISCO_OK) return st;
+        }
+        if (sd != sm) {
+            if ((e = hipEventRecord(ev.done, sd)) != hipSuccess) return hipfail(e, "event record");
+        }
+    }
     for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
         const int64_t cc = std::min<int64_t>(L.Cc, C - c0);
         const int32_t Mc = (int32_t)(cc * K);
@@ -856,19 +918,10 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
                    DISCO_OK) {
             return st;
         }
-        for (int64_t b = 0; b < B; ++b) {
-            // partial dW[o][c k] over each position split
-            disco::GemmNtLaunch g2;
-            g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);
-            g2.B = svp ? svp + (b * C + c0) * K * N : gb + b * gstride;
-            g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
-            g2.Kd = (int32_t)N; g2.k_per_split = L.kps; g2.out_f32 = true;
-            g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc;
-            if ((e = disco::launch_gemm_nt(g2, sm)) != hipSuccess) return hipfail(e, "gy out^T product");
-        }
-        if ((e = disco::launch_reduce_partials(part, (int)(B * L.S), (int)Co, Mc, dW->data, CK, (int)(c0 * K), sm)) !=
-            hipSuccess)
-            return hipfail(e, "dW reduction");
+        if (!svp && (st = dw_chunk(c0, Mc, gb, gstride, sm)) != DISCO_OK) return st;
+    }
+    if (sd != sm) {
+        if ((e = hipStreamWaitEvent(sm, ev.done, 0)) != hipSuccess) return hipfail(e, "stream wait");
     }
     return DISCO_OK;
 }
