@@ -795,3 +795,18 @@ def test_fused_save_rejects_bad_arguments():
     assert e.value.status_name == "DISCO_ERR_SHAPE"
     torch.cuda.synchronize()
     assert torch.all(torch.isnan(y)) and torch.all(torch.isnan(gx)) and torch.all(torch.isnan(dW))
+
+
+def test_fused_save_f16():
+    """fp16 data: the saving fused op's y equals the fused op's bitwise; the kept contraction (fp16 of the
+    unscaled accumulator) within the fp16 bar of the oracle's forward."""
+    _log("fused save fp16")
+    psi = build_psi(33, 128, 17, 64, 0.6, 4, 4)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((1, 6, psi.Hi, psi.Wi), 3740, "f16")
+    W = randn((24, 6, psi.K), 3741, "f16", std=0.1)
+    y0 = sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV))
+    y, out = sgc.disco_fused_conv_save(h, x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    assert normalised_error(out.cpu(), oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL_F16
