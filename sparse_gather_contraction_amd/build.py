@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdisco.so")
 
-SOURCES = ["plan.cpp", "plan_fused.cpp", "disco_api.hip", "kernels_gather.hip", "kernels_staged.hip", "kernels_fused.hip",
+SOURCES = ["plan.cpp", "plan_fused.cpp", "plan_tile.cpp", "kernels_tile.hip", "disco_api.hip", "kernels_gather.hip", "kernels_staged.hip", "kernels_fused.hip",
            "kernels_fused_mfma.hip", "kernels_gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -50,6 +50,21 @@ struct DevStaged {
     int32_t NI = 1, G = 1, T = 3, S = 1;
 };
 
+constexpr int kTileLdsBudget = 40 * 1024;  // bytes of LDS per register-tiled workgroup (four per CU)
+
+struct DevTile {
+    bool ok = false;
+    disco::Task *tasks = nullptr;
+    disco::Stage *stages = nullptr;
+    int32_t *stage_rows = nullptr;
+    int32_t *stage_recptr = nullptr;
+    disco::TileRec *recs = nullptr;
+    disco::Item *items = nullptr;
+    int32_t n_tasks = 0;
+    int32_t L = 0, row_len = 0, lrow = 0, deint = 1, rows_per_stage = 0, NI = 1, G = 1, PW = 1;
+    int32_t n_ws4 = 0, n_ws2 = 0, max_recs = 0;
+};
+
 constexpr int kLdsPerBlock = 160 * 1024;       // gfx950: a workgroup may allocate the whole 160 KiB
 constexpr int kFwdMfmaStageBytes = 40 * 1024;  // two stages per forward workgroup, two workgroups per CU
 constexpr int kBwdMfmaRows = 8;                // gradient rows (input row, residue) per matrix-core group
@@ -115,6 +130,36 @@ hipError_t upload_staged(DevStaged &d, const disco::StagedPlan &p)
     d.n_tasks = (int32_t)p.tasks.size();
     d.L = p.L; d.row_len = p.row_len; d.lrow = p.lrow; d.halo = p.halo; d.rows_per_stage = p.rows_per_stage;
     d.wpp = p.wpp; d.NP = p.NP; d.NI = p.NI; d.G = p.G; d.T = p.T; d.S = p.S;
+    return hipSuccess;
+}
+
+void free_tile(DevTile &d)
+{
+    (void)hipFree(d.tasks);
+    (void)hipFree(d.stages);
+    (void)hipFree(d.stage_rows);
+    (void)hipFree(d.stage_recptr);
+    (void)hipFree(d.recs);
+    (void)hipFree(d.items);
+    d = DevTile();
+}
+
+hipError_t upload_tile(DevTile &d, const disco::TilePlan &p)
+{
+    d = DevTile();
+    if (!p.ok || !disco::tile_supported(p.NI, p.G, p.PW)) return hipSuccess;
+    hipError_t e;
+    if ((e = upload(&d.tasks, p.tasks)) != hipSuccess) return e;
+    if ((e = upload(&d.stages, p.stages)) != hipSuccess) return e;
+    if ((e = upload(&d.stage_rows, p.stage_rows)) != hipSuccess) return e;
+    if ((e = upload(&d.stage_recptr, p.stage_recptr)) != hipSuccess) return e;
+    if ((e = upload(&d.recs, p.recs)) != hipSuccess) return e;
+    if ((e = upload(&d.items, p.items)) != hipSuccess) return e;
+    d.ok = true;
+    d.n_tasks = (int32_t)p.tasks.size();
+    d.L = p.L; d.row_len = p.row_len; d.lrow = p.lrow; d.deint = p.deint; d.rows_per_stage = p.rows_per_stage;
+    d.NI = p.NI; d.G = p.G; d.PW = p.PW;
+    d.n_ws4 = p.n_ws4; d.n_ws2 = p.n_ws2; d.max_recs = p.max_recs;
     return hipSuccess;
 }
 
@@ -231,6 +276,7 @@ struct disco_psi_s {
     int64_t nnz;
     DevPlan fwd, bwd;
     DevStaged sfwd[2], sbwd[2];  // staged plans by source dtype: [0] fp32, [1] bf16
+    DevTile tfwd, tbwd;          // register-tiled fp32 plans
     DevFused fused;
     DevFused fwdm;  // phase-split plan of the matrix-core forward (bf16)
     DevFused bwdm;  // phase-split plan of the inverse CSR: the matrix-core backward (bf16)
@@ -283,11 +329,36 @@ bool staged_env_off()
 }
 
 // Launch the gather over all planes, in chunks that keep the grid below 2^31 blocks.
-disco_status run_gather(const DevPlan &p, const DevStaged &sp, const void *src, void *dst, int dtype, int64_t BC,
-                        int64_t src_plane, int64_t dst_plane, hipStream_t stream)
+disco_status run_gather(const DevPlan &p, const DevStaged &sp, const DevTile &tp, const void *src, void *dst,
+                        int dtype, int64_t BC, int64_t src_plane, int64_t dst_plane, hipStream_t stream)
 {
     if (BC == 0) return DISCO_OK;
     const size_t esz = dtype == DISCO_F32 ? 4 : 2;
+    if (dtype == DISCO_F32 && tp.ok && !getenv_is0("DISCO_TILE")) {  // test knob: "0" turns the tiled gather off
+        const bool vec = ((uintptr_t)src % 16 == 0) && (src_plane % 4 == 0) && (tp.row_len % 4 == 0) &&
+                         tp.L >= disco::kTileHalo;
+        // at most one workgroup per PW planes per task: keep the grid below 2^31 workgroups
+        const int64_t n_pg_max = (((int64_t)1 << 31) - 1) / std::max<int32_t>(1, tp.n_tasks);
+        const int64_t chunk = std::max<int64_t>(1, n_pg_max) * tp.PW;
+        for (int64_t b0 = 0; b0 < BC; b0 += chunk) {
+            disco::TileLaunch a;
+            a.src = (const float *)src + b0 * src_plane;
+            a.dst = (float *)dst + b0 * dst_plane;
+            a.tasks = tp.tasks; a.stages = tp.stages; a.stage_rows = tp.stage_rows; a.stage_recptr = tp.stage_recptr;
+            a.recs = tp.recs; a.items = tp.items;
+            a.n_tasks = tp.n_tasks;
+            a.BC = (int32_t)std::min<int64_t>(chunk, BC - b0);
+            a.n_ws4 = tp.n_ws4; a.n_ws2 = tp.n_ws2; a.max_recs = tp.max_recs;
+            a.src_plane = src_plane; a.dst_plane = dst_plane;
+            a.L = tp.L; a.row_len = tp.row_len; a.lrow = tp.lrow; a.deint = tp.deint;
+            a.rows_per_stage = tp.rows_per_stage; a.NI = tp.NI; a.G = tp.G; a.PW = tp.PW;
+            a.vec = vec ? 1 : 0;
+            hipError_t e = disco::launch_tile(a, stream);
+            if (e != hipSuccess)
+                return fail(DISCO_ERR_HIP, std::string("tiled gather launch failed: ") + hipGetErrorString(e));
+        }
+        return DISCO_OK;
+    }
     if (sp.ok && !staged_env_off()) {
         const int align = 16 / (int)esz;
         const bool vec = ((uintptr_t)src % 16 == 0) && (src_plane % align == 0) && (sp.row_len % align == 0) &&
@@ -366,10 +437,10 @@ disco_status enqueue_fwd(disco_psi h, const void *src, void *dst, int dtype, int
     }
     const int64_t sp = (int64_t)h->Hi * h->Wi, dp = (int64_t)h->K * h->Ho * h->Wo;
     if ((src_bs == 0 || src_bs == C * sp) && (dst_bs == 0 || dst_bs == C * dp))
-        return run_gather(h->fwd, h->sfwd[d], src, dst, dtype, B * C, sp, dp, stream);
+        return run_gather(h->fwd, h->sfwd[d], h->tfwd, src, dst, dtype, B * C, sp, dp, stream);
     const size_t esz = dtype == DISCO_F32 ? 4 : 2;
     for (int64_t b = 0; b < B; ++b) {
-        disco_status st = run_gather(h->fwd, h->sfwd[d], (const char *)src + b * src_bs * esz,
+        disco_status st = run_gather(h->fwd, h->sfwd[d], h->tfwd, (const char *)src + b * src_bs * esz,
                                      (char *)dst + b * dst_bs * esz, dtype, C, sp, dp, stream);
         if (st != DISCO_OK) return st;
     }
@@ -408,10 +479,10 @@ disco_status enqueue_bwd(disco_psi h, const void *src, void *dst, int dtype, int
     }
     const int64_t sp = (int64_t)h->K * h->Ho * h->Wo, dp = (int64_t)h->Hi * h->Wi;
     if ((src_bs == 0 || src_bs == C * sp) && (dst_bs == 0 || dst_bs == C * dp))
-        return run_gather(h->bwd, h->sbwd[d], src, dst, dtype, B * C, sp, dp, stream);
+        return run_gather(h->bwd, h->sbwd[d], h->tbwd, src, dst, dtype, B * C, sp, dp, stream);
     const size_t esz = dtype == DISCO_F32 ? 4 : 2;
     for (int64_t b = 0; b < B; ++b) {
-        disco_status st = run_gather(h->bwd, h->sbwd[d], (const char *)src + b * src_bs * esz,
+        disco_status st = run_gather(h->bwd, h->sbwd[d], h->tbwd, (const char *)src + b * src_bs * esz,
                                      (char *)dst + b * dst_bs * esz, dtype, C, sp, dp, stream);
         if (st != DISCO_OK) return st;
     }
@@ -488,6 +559,16 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the staged plan");
     }
+    disco::TilePlan tfp, tbp;
+    try {
+        int tile_lds = kTileLdsBudget;
+        const char *tl = getenv("DISCO_TILE_LDS");  // tuning knob: LDS bytes per tiled workgroup
+        if (tl && atoi(tl) >= 4096 && atoi(tl) <= 64 * 1024) tile_lds = atoi(tl);
+        disco::build_tile_plan(v, fp, false, tile_lds, tfp);
+        disco::build_tile_plan(v, bp, true, tile_lds, tbp);
+    } catch (const std::bad_alloc &) {
+        return fail(DISCO_ERR_OOM, "host allocation failed while building the tiled plan");
+    }
     disco::FusedPlan fup, fwp, bwp;
     try {
         // two piece stage buffers share what the W slice leaves of the workgroup's LDS
@@ -547,6 +628,8 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         e = upload_staged(h->sfwd[d], sfp[d]);
         if (e == hipSuccess) e = upload_staged(h->sbwd[d], sbp[d]);
     }
+    if (e == hipSuccess) e = upload_tile(h->tfwd, tfp);
+    if (e == hipSuccess) e = upload_tile(h->tbwd, tbp);
     if (e == hipSuccess) e = upload_fused(h->fused, fup);
     if (e == hipSuccess) e = upload_fused(h->fwdm, fwp);
     if (e == hipSuccess) e = upload_fused(h->bwdm, bwp);
@@ -557,6 +640,8 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         free_fused(h->fused);
         free_fused(h->fwdm);
         free_fused(h->bwdm);
+        free_tile(h->tfwd);
+        free_tile(h->tbwd);
         for (int d = 0; d < 2; ++d) {
             free_staged(h->sfwd[d]);
             free_staged(h->sbwd[d]);
@@ -599,6 +684,8 @@ disco_status disco_psi_destroy(disco_psi h)
     free_fused(h->fused);
     free_fused(h->fwdm);
     free_fused(h->bwdm);
+    free_tile(h->tfwd);
+    free_tile(h->tbwd);
     (void)hipFree(h->ho_order);
     (void)hipSetDevice(prev);
     delete h;

@@ -6,6 +6,7 @@
 
 #include "plan.hpp"
 #include "plan_fused.hpp"
+#include "plan_tile.hpp"
 
 namespace disco {
 
@@ -42,6 +43,26 @@ struct StagedLaunch {
     int32_t L, row_len, copy_len, lrow, wpp, NP, stage_elems, vec;
     int32_t NI, G, T, S;
 };
+
+// Register-tiled fp32 gather (kernels_tile.hip) over a TilePlan.
+struct TileLaunch {
+    const float *src;
+    float *dst;
+    const Task *tasks;          // device, heaviest first
+    const Stage *stages;
+    const int32_t *stage_rows;
+    const int32_t *stage_recptr;
+    const TileRec *recs;
+    const Item *items;
+    int32_t n_tasks, BC;        // tasks, planes
+    int32_t n_ws4, n_ws2;       // task classes by wave split (see TilePlan)
+    int64_t src_plane, dst_plane;
+    int32_t L, row_len, lrow, deint, rows_per_stage, NI, G, PW;
+    int32_t max_recs;           // records of the largest stage (LDS after the rows)
+    int32_t vec;                // source rows are 16-byte aligned (row_len and plane a multiple of 4), L >= halo
+};
+bool tile_supported(int NI, int G, int PW);
+hipError_t launch_tile(const TileLaunch &a, hipStream_t stream);
 
 // true when the staged kernel has an instantiation for these parameters
 bool staged_supported(int NI, int G, int T, int S);

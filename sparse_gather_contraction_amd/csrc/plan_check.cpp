@@ -1,0 +1,429 @@
+// plan_check.cpp — host-only checker of the device work plans (built with g++ and the address
+// and undefined-behaviour sanitizers by the CPU test suite; it never touches a GPU).
+//
+// For one CSR read from a file it builds every plan disco_psi_create builds and checks
+//   * that every index a kernel derives from a plan stays inside the buffer it addresses
+//     (segments, records and stages of the plain, staged and tiled gathers, LDS reads and
+//     writes, output offsets), and
+//   * that the gather plans reproduce the contraction: each kernel's loop structure is
+//     replayed on the CPU in fp64 and compared with the CSR definition, and every
+//     destination element is written by exactly one item.
+// Usage: plan_check <csr file>; exit status 0 when every check passes.
+// File layout (little endian): int32 K, Ho, Wo, Hi, Wi; int64 nnz; int64 row_ptr[K Ho + 1];
+// int32 col_hi[nnz]; int32 col_wi[nnz]; float val[nnz].
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "plan.hpp"
+#include "plan_tile.hpp"
+
+using namespace disco;
+
+namespace {
+
+int g_fail = 0;
+
+void report(const std::string &what)
+{
+    if (g_fail < 20) fprintf(stderr, "FAIL: %s\n", what.c_str());
+    ++g_fail;
+}
+
+// the message is built only when the check fails (checks run in the replay's inner loops)
+#define check(ok, what)            \
+    do {                           \
+        if (!(ok)) report(what);   \
+    } while (0)
+
+// CSR definition in fp64: out[k, ho, wo] for one plane
+std::vector<double> ref_fwd(const CSRView &c, const std::vector<double> &x)
+{
+    const int s = c.Wi / c.Wo;
+    std::vector<double> out((size_t)c.K * c.Ho * c.Wo, 0.0);
+    for (int64_t r = 0; r < (int64_t)c.K * c.Ho; ++r)
+        for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e)
+            for (int wo = 0; wo < c.Wo; ++wo)
+                out[r * c.Wo + wo] += (double)c.val[e] * x[(size_t)c.col_hi[e] * c.Wi + (c.col_wi[e] + s * wo) % c.Wi];
+    return out;
+}
+
+std::vector<double> ref_bwd(const CSRView &c, const std::vector<double> &g)
+{
+    const int s = c.Wi / c.Wo;
+    std::vector<double> gx((size_t)c.Hi * c.Wi, 0.0);
+    for (int64_t r = 0; r < (int64_t)c.K * c.Ho; ++r)
+        for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e)
+            for (int wo = 0; wo < c.Wo; ++wo)
+                gx[(size_t)c.col_hi[e] * c.Wi + (c.col_wi[e] + s * wo) % c.Wi] += (double)c.val[e] * g[r * c.Wo + wo];
+    return gx;
+}
+
+void compare(const std::vector<double> &got, const std::vector<double> &want, const std::vector<int> &writes,
+             const char *what)
+{
+    double err = 0.0, scale = 0.0;
+    for (size_t i = 0; i < want.size(); ++i) scale = std::max(scale, std::fabs(want[i]));
+    int64_t bad_writes = 0;
+    for (size_t i = 0; i < want.size(); ++i) {
+        err = std::max(err, std::fabs(got[i] - want[i]));
+        if (writes[i] != 1) ++bad_writes;
+    }
+    check(err <= 1e-9 * std::max(scale, 1.0), std::string(what) + ": replay differs from the CSR definition");
+    check(bad_writes == 0, std::string(what) + ": " + std::to_string(bad_writes) +
+                               " destination elements not written exactly once");
+}
+
+// ---- plain gather (kernels_gather.hip) -------------------------------------------------------
+void check_gather(const CSRView &c, const GatherPlan &p, bool backward, const std::vector<double> &src,
+                  const std::vector<double> &want)
+{
+    const char *what = backward ? "gather plan (backward)" : "gather plan (forward)";
+    const int64_t src_plane = backward ? (int64_t)c.K * c.Ho * c.Wo : (int64_t)c.Hi * c.Wi;
+    const int64_t dst_plane = backward ? (int64_t)c.Hi * c.Wi : (int64_t)c.K * c.Ho * c.Wo;
+    std::vector<double> got(dst_plane, 0.0);
+    std::vector<int> writes(dst_plane, 0);
+    check(p.order.size() == p.items.size(), std::string(what) + ": order size");
+    for (size_t i = 0; i < p.items.size(); ++i) {
+        const Item &it = p.items[i];
+        check(it.G >= 1 && it.G <= kMaxGroup, std::string(what) + ": item G");
+        check(it.seg_begin >= 0 && it.seg_begin <= it.seg_end && it.seg_end <= (int32_t)p.segs.size(),
+              std::string(what) + ": item segment range");
+        std::vector<double> acc((size_t)it.G * p.L, 0.0);
+        for (int32_t q = it.seg_begin; q < it.seg_end && q < (int32_t)p.segs.size(); ++q) {
+            const Seg &sg = p.segs[q];
+            check(sg.m >= 1 && sg.m <= kMaxSegLen && sg.j0 >= 0 && sg.j0 < p.L, std::string(what) + ": segment fields");
+            check(sg.val_off >= 0 && (int64_t)sg.val_off + (int64_t)sg.m * it.G <= (int64_t)p.vals.size(),
+                  std::string(what) + ": segment values out of range");
+            for (int32_t t = 0; t < sg.m; ++t) {
+                int base = sg.j0 + t;
+                if (base >= p.L) base -= p.L;
+                for (int j = 0; j < p.L; ++j) {
+                    int idx = base + j;
+                    if (idx >= p.L) idx -= p.L;
+                    const int64_t a = (int64_t)sg.in_off + (int64_t)p.in_stride * idx;
+                    check(a >= 0 && a < src_plane, std::string(what) + ": source read out of the plane");
+                    if (a < 0 || a >= src_plane) return;
+                    for (int g = 0; g < it.G; ++g)
+                        acc[(size_t)g * p.L + j] += (double)p.vals[sg.val_off + t * it.G + g] * src[a];
+                }
+            }
+        }
+        for (int g = 0; g < it.G; ++g)
+            for (int j = 0; j < p.L; ++j) {
+                const int64_t o = (int64_t)it.out_off[g] + (int64_t)it.out_stride * j;
+                check(o >= 0 && o < dst_plane, std::string(what) + ": store out of the plane");
+                if (o < 0 || o >= dst_plane) return;
+                got[o] = acc[(size_t)g * p.L + j];
+                writes[o]++;
+            }
+    }
+    compare(got, want, writes, what);
+}
+
+// ---- LDS-staged gather (kernels_staged.hip) ----------------------------------------------------
+void check_staged(const CSRView &c, const StagedPlan &sp, bool backward, int elem_bytes, int lds_budget,
+                  const std::vector<double> &src, const std::vector<double> &want)
+{
+    if (!sp.ok) return;
+    const std::string what = std::string("staged plan (") + (backward ? "backward" : "forward") + ", " +
+                             std::to_string(elem_bytes) + "-byte elements)";
+    const int64_t dst_plane = backward ? (int64_t)c.Hi * c.Wi : (int64_t)c.K * c.Ho * c.Wo;
+    const int64_t nsrc_rows = backward ? (int64_t)c.K * c.Ho : c.Hi;
+    check((int64_t)sp.NP * sp.rows_per_stage * sp.lrow * elem_bytes <= lds_budget, what + ": stage exceeds its LDS");
+    check(sp.lrow >= sp.row_len + sp.halo, what + ": LDS row shorter than row + halo");
+    if (sp.lrow < sp.row_len + sp.halo) return;  // the replay below would write past its rows
+    std::vector<double> got(dst_plane, 0.0);
+    std::vector<int> writes(dst_plane, 0);
+    const int T = sp.T, S_ = sp.S;
+    const int lanes = 64 * sp.wpp;
+    for (const Task &task : sp.tasks) {
+        check(task.item_begin >= 0 && task.item_begin + sp.NI <= (int32_t)sp.items.size(), what + ": task items");
+        check(task.stage_begin >= 0 && task.stage_begin <= task.stage_end && task.stage_end <= (int32_t)sp.stages.size(),
+              what + ": task stages");
+        std::vector<double> acc((size_t)sp.NI * sp.G * sp.L, 0.0);
+        for (int32_t st = task.stage_begin; st < task.stage_end; ++st) {
+            const Stage &sg = sp.stages[st];
+            const int nrows = sg.row_end - sg.row_begin;
+            check(nrows >= 1 && nrows <= sp.rows_per_stage, what + ": rows per stage");
+            // LDS image of the stage: row r holds source positions (e mod row_len) for e < row_len + halo
+            std::vector<double> lds((size_t)sp.rows_per_stage * sp.lrow, NAN);
+            for (int r = 0; r < nrows; ++r) {
+                const int32_t row = sp.stage_rows[sg.row_begin + r];
+                check(row >= 0 && row < nsrc_rows, what + ": stage row out of the plane");
+                for (int e = 0; e < sp.row_len + sp.halo; ++e) lds[(size_t)r * sp.lrow + e] = src[(size_t)row * sp.row_len + e % sp.row_len];
+            }
+            for (int i = 0; i < sp.NI; ++i) {
+                const int32_t q0 = sp.stage_segptr[sg.segptr + i], q1 = sp.stage_segptr[sg.segptr + i + 1];
+                check(q0 >= 0 && q0 <= q1 && q1 <= (int32_t)sp.segs.size(), what + ": stage segment range");
+                for (int32_t q = q0; q < q1; ++q) {
+                    const Seg &s = sp.segs[q];
+                    check(s.m >= 1 && s.m <= kStagedSegLen, what + ": segment length");
+                    check((int64_t)s.val_off + (int64_t)s.m * sp.G <= (int64_t)sp.vals.size(), what + ": segment values");
+                    for (int lane = 0; lane < lanes; ++lane) {
+                        const int jl = lane * T;
+                        if (jl >= sp.L) continue;
+                        int base = s.j0 + jl;
+                        if (base >= sp.L) base -= sp.L;
+                        for (int u = 0; u < s.m + T - 1; ++u) {
+                            const int64_t a = s.in_off + (int64_t)S_ * (base + u);
+                            check(a >= 0 && a < (int64_t)nrows * sp.lrow, what + ": LDS read outside the staged rows");
+                            if (a < 0 || a >= (int64_t)nrows * sp.lrow) return;
+                            check(!std::isnan(lds[a]), what + ": LDS read of an unstaged word");
+                        }
+                        for (int t = 0; t < T && jl + t < sp.L; ++t)
+                            for (int e = 0; e < s.m; ++e)
+                                for (int g = 0; g < sp.G; ++g)
+                                    acc[((size_t)i * sp.G + g) * sp.L + jl + t] +=
+                                        (double)sp.vals[s.val_off + e * sp.G + g] * lds[s.in_off + S_ * (base + e + t)];
+                    }
+                }
+            }
+        }
+        for (int i = 0; i < sp.NI; ++i) {
+            const Item &it = sp.items[task.item_begin + i];
+            for (int g = 0; g < sp.G; ++g)
+                for (int j = 0; j < sp.L; ++j) {
+                    const int64_t o = (int64_t)it.out_off[g] + (int64_t)it.out_stride * j;
+                    check(o >= 0 && o < dst_plane, what + ": store out of the plane");
+                    if (o < 0 || o >= dst_plane) return;
+                    got[o] = acc[((size_t)i * sp.G + g) * sp.L + j];
+                    writes[o]++;
+                }
+        }
+    }
+    compare(got, want, writes, what.c_str());
+}
+
+// ---- register-tiled fp32 gather (kernels_tile.hip) ---------------------------------------------
+void check_tile(const CSRView &c, const TilePlan &tp, bool backward, int lds_budget, const std::vector<double> &src,
+                const std::vector<double> &want)
+{
+    if (!tp.ok) return;
+    const std::string what = std::string("tiled plan (") + (backward ? "backward" : "forward") + ")";
+    const int64_t dst_plane = backward ? (int64_t)c.Hi * c.Wi : (int64_t)c.K * c.Ho * c.Wo;
+    const int64_t nsrc_rows = backward ? (int64_t)c.K * c.Ho : c.Hi;
+    const int T = kTileT;
+    const int stage_floats = tp.rows_per_stage * tp.deint * tp.lrow;
+    check((int64_t)tp.NP * stage_floats * 4 + (int64_t)sizeof(TileRec) * tp.max_recs <= lds_budget,
+          what + ": stage rows and records exceed the LDS");
+    check(tp.lrow % 4 == 0 && tp.lrow >= tp.L + kTileHalo, what + ": LDS row layout");
+    if (tp.lrow < tp.L + kTileHalo || tp.deint < 1) return;  // the replay below would write past its rows
+    check(tp.deint * tp.L == tp.row_len, what + ": residue rows do not tile the source row");
+    check(tp.NP == 4 * tp.PW && (tp.PW == 1 || tp.PW == 2) && (64 / tp.PW) * T >= tp.L, what + ": lane layout");
+    check(0 <= tp.n_ws4 && tp.n_ws4 <= tp.n_ws2 && tp.n_ws2 <= (int32_t)tp.tasks.size(), what + ": wave-split classes");
+    check(tp.NI * tp.G <= kTileMaxRows, what + ": more accumulator rows than the kernel holds");
+    check(tp.n_ws2 == 0 || 3LL * 64 * tp.NI * tp.G * T * 4 <= lds_budget, what + ": wave-split sums exceed the LDS");
+    std::vector<double> got(dst_plane, 0.0);
+    std::vector<int> writes(dst_plane, 0);
+    const int lanes = 64 / tp.PW;  // lanes of one plane
+    const int cmax = tile_piece_max(tp.G);
+    for (const Task &task : tp.tasks) {
+        check(task.item_begin >= 0 && task.item_begin + tp.NI <= (int32_t)tp.items.size(), what + ": task items");
+        check(task.stage_begin >= 0 && task.stage_begin <= task.stage_end && task.stage_end <= (int32_t)tp.stages.size(),
+              what + ": task stages");
+        std::vector<double> acc((size_t)tp.NI * tp.G * tp.L, 0.0);
+        for (int32_t st = task.stage_begin; st < task.stage_end; ++st) {
+            const Stage &sg = tp.stages[st];
+            const int nrows = sg.row_end - sg.row_begin;
+            check(nrows >= 1 && nrows <= tp.rows_per_stage, what + ": rows per stage");
+            check(tp.stage_recptr[sg.segptr + tp.NI * kTileClasses] - tp.stage_recptr[sg.segptr] <= tp.max_recs,
+                  what + ": stage holds more records than its LDS area");
+            // LDS image as the staging loop writes it: residue rho of staged row r at (r deint + rho) lrow,
+            // positions [0, L) and the halo [L, L + kTileHalo)
+            std::vector<double> lds((size_t)stage_floats, NAN);
+            for (int r = 0; r < nrows; ++r) {
+                const int32_t row = tp.stage_rows[sg.row_begin + r];
+                check(row >= 0 && row < nsrc_rows, what + ": stage row out of the plane");
+                if (row < 0 || row >= nsrc_rows) return;
+                for (int e = 0; e < tp.row_len; ++e) {
+                    const int rho = e % tp.deint, jj = e / tp.deint;
+                    lds[(size_t)(r * tp.deint + rho) * tp.lrow + jj] = src[(size_t)row * tp.row_len + e];
+                }
+                for (int h = 0; h < tp.deint * kTileHalo; ++h) {
+                    const int rho = h / kTileHalo, pos = h % kTileHalo;
+                    lds[(size_t)(r * tp.deint + rho) * tp.lrow + tp.L + pos] =
+                        src[(size_t)row * tp.row_len + rho + tp.deint * (pos % tp.L)];
+                }
+            }
+            for (int i = 0; i < tp.NI; ++i) {
+                for (int cl = 0; cl < kTileClasses; ++cl) {
+                const int32_t r0 = tp.stage_recptr[sg.segptr + i * kTileClasses + cl];
+                const int32_t r1 = tp.stage_recptr[sg.segptr + i * kTileClasses + cl + 1];
+                check(r0 >= 0 && r0 <= r1 && r1 <= (int32_t)tp.recs.size(), what + ": stage record range");
+                for (int32_t q = r0; q < r1; ++q) {
+                    const TileRec &rec = tp.recs[q];
+                    const int rc = rec.c;
+                    check(rc == cl + 1, what + ": record in the wrong entry-count class");
+                    check(rc >= 1 && rc <= cmax && rc * tp.G <= kTileRecVals, what + ": record entry count");
+                    check(rec.j0 >= 0 && rec.j0 < tp.L && rec.w == tp.L - rec.j0, what + ": record shift");
+                    const int lds_off = rec.a / 4 - rec.j0;  // float offset of the record's LDS row
+                    check(rec.a % 4 == 0 && lds_off >= 0 && lds_off % tp.lrow == 0 && lds_off / tp.lrow < nrows * tp.deint,
+                          what + ": record LDS row");
+                    for (int lane = 0; lane < lanes; ++lane) {
+                        const int jl = lane * T;
+                        const int jlc = jl < tp.L ? jl : 0;
+                        // the kernel's address: 4 jlc + a, less 4 L when jlc >= w
+                        const int64_t byte = 4LL * jlc + rec.a - (jlc >= rec.w ? 4LL * tp.L : 0);
+                        const int64_t base = byte / 4 - lds_off;  // position within the row
+                        check(byte % 4 == 0 && base >= 0 && base < tp.L, what + ": window start outside its row");
+                        if (base < 0 || base >= tp.L) return;
+                        for (int u = 0; u < rc + T - 1; ++u) {
+                            const int64_t a = (int64_t)lds_off + base + u;
+                            const bool in_row = base + u < tp.lrow;
+                            check(in_row && a < stage_floats, what + ": LDS read past its row");
+                            if (!in_row || a >= stage_floats) return;
+                            check(!std::isnan(lds[a]), what + ": LDS read of an unstaged word");
+                        }
+                        if (jl >= tp.L) continue;
+                        check(base == (rec.j0 + jl) % tp.L, what + ": window start is not (j0 + j) mod L");
+                        for (int t = 0; t < T && jl + t < tp.L; ++t)
+                            for (int e = 0; e < rc; ++e)
+                                for (int g = 0; g < tp.G; ++g)
+                                    acc[((size_t)i * tp.G + g) * tp.L + jl + t] +=
+                                        (double)rec.v[e * tp.G + g] * lds[lds_off + base + e + t];
+                    }
+                }
+                }
+            }
+        }
+        for (int i = 0; i < tp.NI; ++i) {
+            const Item &it = tp.items[task.item_begin + i];
+            if (it.out_off[0] < 0) continue;
+            for (int g = 0; g < tp.G; ++g)
+                for (int j = 0; j < tp.L; ++j) {
+                    const int64_t o = (int64_t)it.out_off[g] + (int64_t)it.out_stride * j;
+                    check(o >= 0 && o < dst_plane, what + ": store out of the plane");
+                    if (o < 0 || o >= dst_plane) return;
+                    got[o] = acc[((size_t)i * tp.G + g) * tp.L + j];
+                    writes[o]++;
+                }
+        }
+    }
+    compare(got, want, writes, what.c_str());
+}
+
+// The tiled kernel's workgroup -> (task, planes, record share) decode, replayed for BC planes:
+// every (task, plane) pair must be served by exactly WS waves with distinct shares.
+void check_tile_grid(const TilePlan &tp, int BC)
+{
+    if (!tp.ok) return;
+    const std::string what = "tiled grid (" + std::to_string(BC) + " planes)";
+    const int PW = tp.PW, nt = (int)tp.tasks.size();
+    const int npg4 = (BC + PW - 1) / PW, npg2 = (BC + 2 * PW - 1) / (2 * PW), npg1 = (BC + 4 * PW - 1) / (4 * PW);
+    const int64_t nblk = (int64_t)tp.n_ws4 * npg4 + (int64_t)(tp.n_ws2 - tp.n_ws4) * npg2 + (int64_t)(nt - tp.n_ws2) * npg1;
+    std::vector<int> seen((size_t)nt * BC, 0);
+    for (int64_t b = 0; b < nblk; ++b) {
+        int bid = (int)b, ti, pg, WS;
+        const int nb4 = tp.n_ws4 * npg4, nb2 = (tp.n_ws2 - tp.n_ws4) * npg2;
+        if (bid < nb4) {
+            WS = 4; ti = bid / npg4; pg = bid - ti * npg4;
+        } else if (bid < nb4 + nb2) {
+            bid -= nb4;
+            WS = 2; ti = tp.n_ws4 + bid / npg2; pg = bid - (ti - tp.n_ws4) * npg2;
+        } else {
+            bid -= nb4 + nb2;
+            WS = 1; ti = tp.n_ws2 + bid / npg1; pg = bid - (ti - tp.n_ws2) * npg1;
+        }
+        check(ti >= 0 && ti < nt, what + ": task index out of range");
+        if (ti < 0 || ti >= nt) return;
+        const int NPB = 4 * PW / WS;
+        check(NPB <= tp.NP, what + ": more planes in a workgroup than its LDS holds");
+        for (int wave = 0; wave < 4; ++wave)
+            for (int half = 0; half < PW; ++half) {
+                const int wsi = wave % WS;
+                const int ps = (wave / WS) * PW + half;
+                check(ps < NPB, what + ": plane slot outside the workgroup's planes");
+                const int plane = pg * NPB + ps;
+                if (plane < BC) seen[(size_t)ti * BC + plane] |= 1 << wsi;
+            }
+    }
+    for (int ti = 0; ti < nt; ++ti) {
+        const int WS = ti < tp.n_ws4 ? 4 : (ti < tp.n_ws2 ? 2 : 1);
+        for (int pl = 0; pl < BC; ++pl)
+            check(seen[(size_t)ti * BC + pl] == (1 << WS) - 1, what + ": a (task, plane) is not served by each share once");
+    }
+}
+
+}  // namespace
+
+int main(int argc, char **argv)
+{
+    if (argc != 2) {
+        fprintf(stderr, "usage: %s <csr file>\n", argv[0]);
+        return 2;
+    }
+    FILE *f = fopen(argv[1], "rb");
+    if (!f) {
+        fprintf(stderr, "cannot open %s\n", argv[1]);
+        return 2;
+    }
+    int32_t hdr[5];
+    int64_t nnz = 0;
+    if (fread(hdr, 4, 5, f) != 5 || fread(&nnz, 8, 1, f) != 1 || nnz < 0) {
+        fprintf(stderr, "bad header\n");
+        return 2;
+    }
+    const int64_t R = (int64_t)hdr[0] * hdr[1];
+    std::vector<int64_t> row_ptr(R + 1);
+    std::vector<int32_t> col_hi(nnz), col_wi(nnz);
+    std::vector<float> val(nnz);
+    if (fread(row_ptr.data(), 8, R + 1, f) != (size_t)(R + 1) || fread(col_hi.data(), 4, nnz, f) != (size_t)nnz ||
+        fread(col_wi.data(), 4, nnz, f) != (size_t)nnz || fread(val.data(), 4, nnz, f) != (size_t)nnz) {
+        fprintf(stderr, "short file\n");
+        return 2;
+    }
+    fclose(f);
+    CSRView c{hdr[0], hdr[1], hdr[2], hdr[3], hdr[4], nnz, row_ptr.data(), col_hi.data(), col_wi.data(), val.data()};
+    int code = 0;
+    const std::string msg = validate_csr(c, &code);
+    if (code != 0) {
+        fprintf(stderr, "CSR rejected: %s\n", msg.c_str());
+        return 3;
+    }
+
+    std::mt19937_64 rng(12345);
+    std::normal_distribution<double> nd;
+    std::vector<double> x((size_t)c.Hi * c.Wi), g((size_t)c.K * c.Ho * c.Wo);
+    for (auto &v : x) v = (double)(float)nd(rng);
+    for (auto &v : g) v = (double)(float)nd(rng);
+    const std::vector<double> want_f = ref_fwd(c, x), want_b = ref_bwd(c, g);
+
+    GatherPlan fp, bp;
+    build_forward_plan(c, fp);
+    build_backward_plan(c, bp);
+    check_gather(c, fp, false, x, want_f);
+    check_gather(c, bp, true, g, want_b);
+    // the library's budgets (disco_api.hip): 40 KiB per staged or tiled workgroup
+    const int budget = 40 * 1024;
+    for (int esz : {4, 2}) {
+        StagedPlan sf, sb;
+        build_staged_plan(c, fp, false, esz, budget, sf);
+        build_staged_plan(c, bp, true, esz, budget, sb);
+        check_staged(c, sf, false, esz, budget, x, want_f);
+        check_staged(c, sb, true, esz, budget, g, want_b);
+    }
+    TilePlan tf, tb;
+    build_tile_plan(c, fp, false, budget, tf);
+    build_tile_plan(c, bp, true, budget, tb);
+    check_tile(c, tf, false, budget, x, want_f);
+    check_tile(c, tb, true, budget, g, want_b);
+    for (int BC : {1, 2, 3, 5, 8, 13, 128}) {
+        check_tile_grid(tf, BC);
+        check_tile_grid(tb, BC);
+    }
+
+    printf("plan_check: K=%d Ho=%d Wo=%d Hi=%d Wi=%d nnz=%lld tiled fwd %s (NI=%d G=%d, %zu tasks, %d/%d split) "
+           "bwd %s (NI=%d, %zu tasks, %d/%d split)\n",
+           c.K, c.Ho, c.Wo, c.Hi, c.Wi, (long long)c.nnz, tf.ok ? "on" : "off", tf.NI, tf.G, tf.tasks.size(), tf.n_ws4,
+           tf.n_ws2, tb.ok ? "on" : "off", tb.NI, tb.tasks.size(), tb.n_ws4, tb.n_ws2);
+    if (g_fail) {
+        fprintf(stderr, "plan_check: %d check(s) failed\n", g_fail);
+        return 1;
+    }
+    return 0;
+}

@@ -317,10 +317,15 @@ def test_architecture_refusal_knob(monkeypatch):
     sgc.disco_psi_create(psi, 0).close()
 
 
-@pytest.mark.parametrize("staged", ["0", "1"])
-def test_plain_and_staged_gather_agree_with_oracle(staged, monkeypatch):
-    """DISCO_STAGED=0 forces the plain gather kernel on shapes the staged kernel covers."""
-    monkeypatch.setenv("DISCO_STAGED", staged)
+@pytest.mark.parametrize("path", ["tiled", "staged", "plain"])
+def test_plain_staged_and_tiled_gather_agree_with_oracle(path, monkeypatch):
+    """fp32 data runs the register-tiled gather where its plan covers the shape; DISCO_TILE=0 falls
+    back to the LDS-staged gather and DISCO_TILE=0 DISCO_STAGED=0 to the plain one (bf16 data with
+    DISCO_FWD_MFMA=0 / DISCO_BWD_MFMA=0 takes the same vector-ALU gathers)."""
+    monkeypatch.setenv("DISCO_TILE", "1" if path == "tiled" else "0")
+    monkeypatch.setenv("DISCO_STAGED", "0" if path == "plain" else "1")
+    monkeypatch.setenv("DISCO_FWD_MFMA", "0")
+    monkeypatch.setenv("DISCO_BWD_MFMA", "0")
     w = WORKLOADS["fwdbwd_f32_181x360"]
     psi = workload_psi(w)
     h = gpu_psi(psi)

@@ -1,0 +1,126 @@
+"""Host plan code under the address and undefined-behaviour sanitizers (CPU only).
+
+`sparse_gather_contraction_amd/csrc/plan_check.cpp` builds every gather plan that
+disco_psi_create builds (plain, LDS-staged for 4- and 2-byte elements, register-tiled),
+replays each kernel's indexing on the CPU and checks that every index stays inside the
+buffer it addresses, that every destination element is written exactly once, that the
+replay reproduces the CSR definition in fp64, and that the tiled kernel's workgroup
+decode serves every (task, plane) pair.  A plan bug would otherwise surface as a GPU
+memory fault.  The checker is compiled here with g++ and -fsanitize=address,undefined.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from disco_inputs import WORKLOADS, workload_psi
+from disco_inputs.psi import build_psi, random_psi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_gather_contraction_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("plan_check") / "plan_check")
+    cmd = ["g++", "-O2", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-I", CSRC,
+           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "plan_tile.cpp"), os.path.join(CSRC, "plan_check.cpp"),
+           "-o", out]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    return out
+
+
+def _write_csr(p, path):
+    with open(path, "wb") as f:
+        np.array([p.K, p.Ho, p.Wo, p.Hi, p.Wi], np.int32).tofile(f)
+        np.array([int(np.asarray(p.row_ptr)[-1])], np.int64).tofile(f)
+        np.asarray(p.row_ptr, np.int64).tofile(f)
+        np.asarray(p.col_hi, np.int32).tofile(f)
+        np.asarray(p.col_wi, np.int32).tofile(f)
+        np.asarray(p.val, np.float32).tofile(f)
+
+
+def _run(checker, psi, tmp_path):
+    path = str(tmp_path / "psi.csr")
+    _write_csr(psi, path)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([checker, path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, env=env,
+                       timeout=600)
+    assert r.returncode == 0, r.stdout
+    return r.stdout
+
+
+CASES = {
+    # Hi, Wi, Ho, Wo, theta_c, n_r, n_a (generated hat-basis psi)
+    "caps_s3": lambda: build_psi(31, 60, 16, 20, 0.5, 2, 2),
+    "whole_rings_k12": lambda: build_psi(31, 60, 31, 20, 1.5, 3, 4),
+    "k8_s3": lambda: build_psi(37, 72, 19, 24, 0.9, 4, 2),
+    "k16_s1": lambda: build_psi(31, 64, 31, 64, 1.5, 4, 4),
+    # random CSRs: empty rows, dense rows (long runs), odd row lengths, the row-length limits of
+    # the tiled kernel (192 / 193 and 384), rows longer than every staged plan
+    "rand_long": lambda: random_psi(3, 4, 1100, 5, 2200, 0.05, seed=11, empty_rows=(0, 5, 11)),
+    "rand_dense": lambda: random_psi(2, 3, 40, 4, 80, 0.9, seed=12, empty_rows=(1,)),
+    "rand_empty": lambda: random_psi(2, 5, 16, 6, 32, 0.2, seed=13, empty_rows=(0, 3, 7)),
+    "rand_odd_s1": lambda: random_psi(3, 7, 15, 9, 15, 0.3, seed=5),
+    "rand_odd_s2": lambda: random_psi(2, 7, 13, 9, 26, 0.3, seed=6),
+    "rand_L384": lambda: random_psi(2, 3, 384, 4, 768, 0.02, seed=7),
+    "rand_L193": lambda: random_psi(2, 3, 193, 4, 386, 0.05, seed=8),
+    "rand_L192": lambda: random_psi(3, 3, 192, 4, 384, 0.05, seed=9),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_plans_of_generated_and_random_psi(checker, name, tmp_path):
+    _run(checker, CASES[name](), tmp_path)
+
+
+@pytest.mark.parametrize("name", ["tiny_fwd_f32_16x32", "fwdbwd_f32_181x360"])
+def test_plans_of_the_fp32_workloads(checker, name, tmp_path):
+    out = _run(checker, workload_psi(WORKLOADS[name]), tmp_path)
+    assert "tiled fwd on" in out and "bwd on" in out  # both fp32 workloads run the tiled kernel
+
+
+def test_checker_catches_a_bad_plan_index(checker, tmp_path):
+    """The checker must fail on a CSR it rejects (a column outside the grid): exit status 3."""
+    p = random_psi(2, 3, 16, 4, 32, 0.3, seed=21)
+    col_wi = np.asarray(p.col_wi).copy()
+    col_wi[0] = 32  # == Wi: outside [0, Wi)
+    bad = type(p)(p.K, p.Ho, p.Wo, p.Hi, p.Wi, p.row_ptr, p.col_hi, col_wi, p.val)
+    path = str(tmp_path / "bad.csr")
+    _write_csr(bad, path)
+    r = subprocess.run([checker, path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=60)
+    assert r.returncode == 3 and "CSR rejected" in r.stdout
+
+
+MUTANTS = {
+    # each replaces one line of plan_tile.cpp with a plausible mistake the checker must catch
+    "window offset drops the residue row": ("rec.a = 4 * ((slot * out.deint + rho) * out.lrow + rec.j0);",
+                                            "rec.a = 4 * ((slot * out.deint) * out.lrow + rec.j0);"),
+    "first shift off by one": ("rec.j0 = (sg.j0 + off) % L;", "rec.j0 = (sg.j0 + off + 1) % L;"),
+    "wrap threshold off by one": ("rec.w = L - rec.j0;", "rec.w = L - rec.j0 + 1;"),
+    "halo too short for the longest record": ("out.lrow = (L + kTileHalo + 3) / 4 * 4;",
+                                              "out.lrow = (L + 4 + 3) / 4 * 4;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_checker_catches_planted_plan_mistakes(name, tmp_path):
+    """Sensitivity: a copy of plan_tile.cpp with one planted mistake must fail the checker on the
+    181x360 workload's psi (built without sanitizers, only the verdict matters)."""
+    old, new = MUTANTS[name]
+    src = open(os.path.join(CSRC, "plan_tile.cpp")).read()
+    assert src.count(old) == 1, name
+    mut = tmp_path / "plan_tile_mut.cpp"
+    mut.write_text(src.replace(old, new))
+    exe = str(tmp_path / "plan_check_mut")
+    cmd = ["g++", "-O1", "-std=c++17", "-I", CSRC, os.path.join(CSRC, "plan.cpp"), str(mut),
+           os.path.join(CSRC, "plan_check.cpp"), "-o", exe]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    path = str(tmp_path / "psi.csr")
+    _write_csr(workload_psi(WORKLOADS["fwdbwd_f32_181x360"]), path)
+    r = subprocess.run([exe, path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
+    assert r.returncode == 1 and "FAIL:" in r.stdout, r.stdout[-2000:]
