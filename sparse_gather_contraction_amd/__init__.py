@@ -38,7 +38,7 @@ DISCO_BF16 = 1
 DISCO_F16 = 2
 EXPORTED = ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
             "disco_fused_conv_save", "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd",
-            "disco_fused_conv_bwd_saved", "disco_last_error")
+            "disco_fused_conv_bwd_saved", "disco_fused_conv_bwd_noalloc", "disco_last_error")
 
 
 class DiscoError(RuntimeError):
@@ -82,10 +82,11 @@ def load_library():
         lib.disco_fused_conv_bwd_workspace.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                        ctypes.POINTER(ctypes.c_size_t)]
         lib.disco_fused_conv_bwd.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 5 + [P, ctypes.c_size_t, P]
+        lib.disco_fused_conv_bwd_noalloc.argtypes = [P] + [ctypes.POINTER(TensorDesc)] * 5 + [P]
         lib.disco_last_error.restype = ctypes.c_char_p
         for f in ("disco_psi_create", "disco_psi_destroy", "disco_fwd", "disco_bwd", "disco_fused_conv",
                   "disco_fused_conv_save", "disco_einsum", "disco_fused_conv_bwd_workspace", "disco_fused_conv_bwd",
-                  "disco_fused_conv_bwd_saved"):
+                  "disco_fused_conv_bwd_saved", "disco_fused_conv_bwd_noalloc"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -250,6 +251,21 @@ def disco_fused_conv_bwd(psi: Psi, x, W, gy, gx=None, dW=None, workspace=None):
     _check(load_library().disco_fused_conv_bwd(psi.handle, *[ctypes.byref(d) for d in descs],
                                                ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                                _stream(x.device)))
+    return gx, dW
+
+
+def disco_fused_conv_bwd_noalloc(psi: Psi, x, W, gy, gx=None, dW=None):
+    """(gx, dW) as disco_fused_conv_bwd, with the library's per-device scratch array as workspace
+    (no device allocation inside the call; gx and dW are allocated here when not given)."""
+    import torch
+
+    if gx is None:
+        gx = torch.empty_like(x)
+    if dW is None:
+        dW = torch.empty_like(W)
+    descs = [tensor_desc(t) for t in (x, W, gy, gx, dW)]
+    _check(load_library().disco_fused_conv_bwd_noalloc(psi.handle, *[ctypes.byref(d) for d in descs],
+                                                       _stream(x.device)))
     return gx, dW
 
 

@@ -501,28 +501,68 @@ struct FusedBwdLayout {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int64_t Co)
+// `cap`: the largest workspace the caller can give; channel chunks shrink (down to one channel) until
+// the layout fits, if it can.
+FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int64_t Co, size_t cap = SIZE_MAX)
 {
-    FusedBwdLayout L;
     const int64_t K = h->K;
-    L.N = (int64_t)h->Ho * h->Wo;
+    const int64_t N = (int64_t)h->Ho * h->Wo;
     // up to 1024 (c, k) rows per chunk (1024 measured 6 % faster than 512 at 721x1440: fewer launches,
     // gy^T read fewer times), and few enough that one batch's chunk stays below 2 GiB
-    const int64_t rows = std::min<int64_t>(1024, (((int64_t)1 << 31) - 1) / std::max<int64_t>(2 * L.N, 1));
-    L.Cc = (int32_t)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(C, 1), rows / std::max<int64_t>(K, 1)));
-    L.Mc = (int32_t)(L.Cc * K);
-    // at most 64 splits: fewer fp32 partials to sum (64 measured 2 % faster than 256 per backward
-    // at 721x1440 and still >= one workgroup per CU there)
-    const int64_t per = std::max<int64_t>(1, (L.N + 63) / 64);
-    L.kps = (int32_t)((per + 31) / 32 * 32);
-    L.S = (int32_t)std::max<int64_t>(1, (L.N + L.kps - 1) / L.kps);
-    size_t off = 0;
-    L.wt = off;   off = align256(off + (size_t)C * K * Co * 2);
-    L.gyt = off;  off = align256(off + (size_t)B * L.N * Co * 2);
-    L.gbuf = off; off = align256(off + (size_t)B * L.Mc * L.N * 2);
-    L.part = off; off = align256(off + (size_t)B * L.S * Co * L.Mc * 4);
-    L.total = off;
-    return L;
+    const int64_t rows = std::min<int64_t>(1024, (((int64_t)1 << 31) - 1) / std::max<int64_t>(2 * N, 1));
+    int64_t cc = std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(C, 1), rows / std::max<int64_t>(K, 1)));
+    for (;;) {
+        FusedBwdLayout L;
+        L.N = N;
+        L.Cc = (int32_t)cc;
+        L.Mc = (int32_t)(L.Cc * K);
+        // at most 64 splits: fewer fp32 partials to sum (64 measured 2 % faster than 256 per backward
+        // at 721x1440 and still >= one workgroup per CU there)
+        const int64_t per = std::max<int64_t>(1, (L.N + 63) / 64);
+        L.kps = (int32_t)((per + 31) / 32 * 32);
+        L.S = (int32_t)std::max<int64_t>(1, (L.N + L.kps - 1) / L.kps);
+        size_t off = 0;
+        L.wt = off;   off = align256(off + (size_t)C * K * Co * 2);
+        L.gyt = off;  off = align256(off + (size_t)B * L.N * Co * 2);
+        L.gbuf = off; off = align256(off + (size_t)B * L.Mc * L.N * 2);
+        L.part = off; off = align256(off + (size_t)B * L.S * Co * L.Mc * 4);
+        L.total = off;
+        if (L.total <= cap || cc == 1) return L;
+        cc = (cc + 1) / 2;
+    }
+}
+
+// File-scope scratch of disco_fused_conv_bwd_noalloc: each device that runs the library holds its own
+// copy until the process ends.  In host code `scratch` only names the symbol; its device address is
+// looked up once per device (init_scratch, called by disco_psi_create with the device current) and
+// that pointer is what the kernels receive.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+// The current device must be `device`.
+disco_status init_scratch(int device)
+{
+    if (device < 0 || device >= 64) return fail(DISCO_ERR_INVALID_ARGUMENT, "device ordinal out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device]) return DISCO_OK;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return fail(DISCO_ERR_HIP, std::string("cannot look up the scratch array: ") + hipGetErrorString(e));
+    }
+    g_scratch_ptr[device] = p;
+    return DISCO_OK;
+}
+
+void *scratch_ptr(int device)
+{
+    if (device < 0 || device >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
 }
 
 }  // namespace
@@ -612,6 +652,10 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) {
         (void)hipGetLastError();
         return fail(DISCO_ERR_HIP, "cannot select the device");
+    }
+    if ((st = init_scratch(device)) != DISCO_OK) {
+        (void)hipSetDevice(prev);
+        return st;
     }
     disco_psi h = new (std::nothrow) disco_psi_s();
     if (!h) {
@@ -871,9 +915,11 @@ namespace {
 
 // Backward of the fused convolution; the dW operand out = F x is recomputed from x, or taken from
 // `saved` (the contraction disco_fused_conv_save wrote) when x is NULL.
+// `cap` < SIZE_MAX: the workspace is the library's scratch array of `cap` bytes (the no-allocation
+// variant): the layout shrinks its channel chunks to fit, and a shape that cannot fit is refused.
 disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco_tensor *saved, const disco_tensor *W,
                                  const disco_tensor *gy, disco_tensor *gx, disco_tensor *dW, void *workspace,
-                                 size_t workspace_bytes, void *stream)
+                                 size_t workspace_bytes, void *stream, size_t cap = SIZE_MAX)
 {
     disco_status st = check_handle(h);
     if (st != DISCO_OK) return st;
@@ -899,12 +945,19 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
         return fail(DISCO_ERR_DTYPE, x ? "x, W, gy, gx and dW dtypes differ" : "out, W, gy, gx and dW dtypes differ");
     if (src->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution backward supports bf16 only");
     if (h->K > 256) return fail(DISCO_ERR_SHAPE, "the fused convolution backward supports K <= 256");
-    const FusedBwdLayout L = fused_bwd_layout(h, B, C, Co);
+    const FusedBwdLayout L = fused_bwd_layout(h, B, C, Co, cap);
     if (Co % 8 != 0 || L.N % 8 != 0)
         return fail(DISCO_ERR_SHAPE, "the fused convolution backward needs Co and Ho*Wo to be multiples of 8");
     const int64_t lim = (int64_t)1 << 31;
     if (L.N * Co * 2 >= lim || (int64_t)L.Mc * L.N * 2 >= lim || C * h->K * Co * 2 >= lim)
         return fail(DISCO_ERR_SHAPE, "a per-batch operand of the fused convolution backward exceeds 2 GiB");
+    if (cap != SIZE_MAX && L.total > cap) {
+        char buf[200];
+        snprintf(buf, sizeof buf,
+                 "this backward needs %zu bytes of scratch; the no-allocation entry point holds at most %zu",
+                 L.total, cap);
+        return fail(DISCO_ERR_SHAPE, buf);
+    }
     if (!workspace && L.total > 0) return fail(DISCO_ERR_INVALID_ARGUMENT, "workspace is NULL");
     if (workspace_bytes < L.total)
         return fail(DISCO_ERR_INVALID_ARGUMENT, "workspace is smaller than disco_fused_conv_bwd_workspace reports");
@@ -1021,6 +1074,17 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
 {
     if (!x) return fail(DISCO_ERR_INVALID_ARGUMENT, "x is NULL");
     return fused_conv_bwd_impl(h, x, nullptr, W, gy, gx, dW, workspace, workspace_bytes, stream);
+}
+
+disco_status disco_fused_conv_bwd_noalloc(disco_psi h, const disco_tensor *x, const disco_tensor *W,
+                                          const disco_tensor *gy, disco_tensor *gx, disco_tensor *dW, void *stream)
+{
+    disco_status st = check_handle(h);
+    if (st != DISCO_OK) return st;
+    if (!x) return fail(DISCO_ERR_INVALID_ARGUMENT, "x is NULL");
+    void *ws = scratch_ptr(h->device);
+    if (!ws) return fail(DISCO_ERR_HIP, "the scratch array of this device was not set up");
+    return fused_conv_bwd_impl(h, x, nullptr, W, gy, gx, dW, ws, kScratchBytes, stream, kScratchBytes);
 }
 
 disco_status disco_fused_conv_bwd_saved(disco_psi h, const disco_tensor *out, const disco_tensor *W,
