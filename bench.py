@@ -26,7 +26,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+# Published vector fp32 figure: 256 CUs x 4 SIMDs x 32 fp32 FMA per clock x 2 flops x 2.4 GHz.  The
+# library is built with packed fp32 ops disabled; the FMA-loop probe (plain v_fma_f32, no packed math)
+# reaches 112.7 TFLOP/s on the box, above what 16 lanes per SIMD per clock could give (78.6), so the
+# published figure is the vector-ALU roof of this code too.
 PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_FP32_FMA_TFLOPS = PEAK_FP32_VALU_TFLOPS
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 
 
@@ -57,6 +62,10 @@ def main():
                     help="skip the separate timing of the fused-convolution backward")
     ap.add_argument("--no-einsum", action="store_true",
                     help="skip the timing of the fused op's einsum alone")
+    ap.add_argument("--no-fp32-configs", action="store_true",
+                    help="skip the fp32 16x32 and 181x360 configurations")
+    ap.add_argument("--fp32-only", action="store_true",
+                    help="time only the fp32 configurations (profiling runs of their kernels)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -74,6 +83,20 @@ def main():
     ops = [o for o in args.ops.split(",") if o]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
+    if args.fp32_only:
+        stream = torch.cuda.current_stream(dev)
+        print(json.dumps({"fp32_configs": time_fp32_configs(sgc, torch, np, dev, stream)}), flush=True)
+        return
     wf = WORKLOADS["fwd_bf16_721x1440"]
     wb = WORKLOADS["bwd_bf16_721x1440"]
     wu = WORKLOADS["fused_bf16_721x1440"]
@@ -107,17 +130,6 @@ def main():
         else:
             sgc.disco_fused_conv(h_u, tensors["x5"], tensors["W5"], tensors["y5"])
 
-    if args.copy_calib_mib:
-        n = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written",
-              file=sys.stderr, flush=True)
-        del src, dst
-
     for i in range(args.warmup):
         for op in ops:
             run(op)
@@ -147,12 +159,15 @@ def main():
     total_bytes = 0
     for op in ops:
         w, psi, Co = cfg[op]
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[op]]))
+        times = np.array([a.elapsed_time(b) for a, b in ev[op]])
+        ms = float(np.mean(times))
         upd = op_updates(w, psi.nnz)
         byt = op_bytes(op, w, psi.nnz, Co)
         total_updates += upd
         total_bytes += byt
-        d = {"ms": round(ms, 4), "GBps": round(byt / ms / 1e6, 2), "Gnnz_updates_per_s": round(upd / ms / 1e6, 2),
+        d = {"ms": round(ms, 4), "ms_median": round(float(np.median(times)), 4),
+             "ms_p10": round(float(np.percentile(times, 10)), 4), "ms_p90": round(float(np.percentile(times, 90)), 4),
+             "GBps": round(byt / ms / 1e6, 2), "Gnnz_updates_per_s": round(upd / ms / 1e6, 2),
              "hbm_frac": round(byt / ms / 1e6 / PEAK_HBM_GBS, 5),
              "shape": {"B": w.B, "C": w.C, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo], "nnz": psi.nnz}}
         # every op of the step runs on bf16 matrix cores (psi packed into dense 16-offset blocks);
@@ -186,7 +201,8 @@ def main():
     ein = None
     if not args.no_einsum and "fused" in ops:
         ein = time_einsum(sgc, torch, np, wu, tensors, dev, stream)
-    ach = None if args.no_einsum else achievable_copy(torch, np, dev, stream)
+    fp32 = None if args.no_fp32_configs else time_fp32_configs(sgc, torch, np, dev, stream)
+    ach = None if args.no_einsum else achievable(torch, np, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -212,6 +228,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "einsum_standalone": ein,
+        "fp32_configs": fp32,
         "achievable": ach,
         "next_rows": nxt,
     }
@@ -282,36 +299,130 @@ def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
     return res
 
 
-def achievable_copy(torch, np, dev, stream, mib=1024, reps=5, read_gib=4):
-    """What plain streaming reaches on this machine, beside the 8 TB/s spec peak: torch's device copy of
-    `mib` MiB (read + write) and torch's sum over `read_gib` GiB of bf16 (read only), median of
-    `reps` each, HIP events on the launch stream."""
-    def timed(fn):
+def _timed(torch, np, stream, fn, reps):
+    """Median and spread of `reps` calls of fn (one untimed call first), HIP events on `stream`."""
+    fn()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         fn()
-        torch.cuda.synchronize()
-        ev = []
-        for _ in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            ev.append((a, b))
-        torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
-    src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
+    """What this machine reaches beside the published peaks, measured with microbenchmark kernels built
+    here (sparse_gather_contraction_amd/csrc/probes.hip): a read-only stream over `read_gib` GiB with
+    16-byte loads, a copy of `copy_mib` MiB (read + write), an fp32 FMA loop (no packed math, as in the
+    library) and a bf16 MFMA loop (v_mfma_f32_32x32x16_bf16); medians of `reps` each."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_gather_contraction_amd", "libdisco_probes.so"))
+    for f in ("disco_probe_read", "disco_probe_copy", "disco_probe_fma", "disco_probe_mfma"):
+        getattr(lib, f).restype = ctypes.c_int
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    lib.disco_probe_read.argtypes = [P, S, P, ctypes.c_int, P]
+    lib.disco_probe_copy.argtypes = [P, P, S, ctypes.c_int, P]
+    lib.disco_probe_fma.argtypes = [ctypes.c_int, P, ctypes.c_int, P]
+    lib.disco_probe_mfma.argtypes = [ctypes.c_int, P, ctypes.c_int, P]
+    sp = stream.cuda_stream
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError(f"probe launch failed with HIP status {st}")
+
+    blocks = 256 * 8
+    out = torch.zeros(blocks * 256, dtype=torch.float32, device=dev)
+    buf = torch.ones(read_gib * (1 << 30) // 4, dtype=torch.float32, device=dev)
+    nb = buf.numel() * 4
+    ms_r = _timed(torch, np, stream, lambda: ok(lib.disco_probe_read(buf.data_ptr(), nb, out.data_ptr(), blocks, sp)),
+                  reps)
+    del buf
+    src = torch.ones(copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    copy_gbs = 2 * mib * (1 << 20) / timed(lambda: dst.copy_(src)) / 1e6
+    ms_c = _timed(torch, np, stream, lambda: ok(lib.disco_probe_copy(src.data_ptr(), dst.data_ptr(), src.numel() * 4,
+                                                                     blocks, sp)), reps)
     del src, dst
-    x = torch.ones(read_gib * (1 << 30) // 2, dtype=torch.bfloat16, device=dev)
-    read_gbs = read_gib * (1 << 30) / timed(lambda: x.sum(dtype=torch.float32)) / 1e6
-    del x
+    iters = 4096
+    ms_f = _timed(torch, np, stream, lambda: ok(lib.disco_probe_fma(iters, out.data_ptr(), blocks, sp)), reps)
+    miters = 2048
+    ms_m = _timed(torch, np, stream, lambda: ok(lib.disco_probe_mfma(miters, out.data_ptr(), blocks, sp)), reps)
     torch.cuda.empty_cache()
-    return {"copy_GBps": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
-            "read_GBps": round(read_gbs, 1), "read_frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
-            "note": f"device copy of {mib} MiB (read + write) and a bf16 sum over {read_gib} GiB (read only), "
-                    f"median of {reps} each"}
+    read_gbs = nb / ms_r[0] / 1e6
+    copy_gbs = 2 * copy_mib * (1 << 20) / ms_c[0] / 1e6
+    fma_tf = blocks * 256 * iters * 8 * 2 / ms_f[0] / 1e9
+    mfma_tf = blocks * 4 * miters * 4 * (32 * 32 * 16 * 2) / ms_m[0] / 1e9
+    res = {"read_GBps": round(read_gbs, 1), "read_frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
+           "copy_GBps": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+           "fp32_fma_TFLOPs": round(fma_tf, 2), "fp32_fma_frac_of_peak": round(fma_tf / PEAK_FP32_VALU_TFLOPS, 4),
+           "bf16_mfma_TFLOPs": round(mfma_tf, 1), "bf16_mfma_frac_of_peak": round(mfma_tf / PEAK_BF16_MFMA_TFLOPS, 4),
+           "note": f"HIP probes built here: read stream of {read_gib} GiB (16-byte loads), copy of {copy_mib} MiB "
+                   f"(read + write), fp32 FMA loop, bf16 MFMA loop; medians of {reps}"}
+    print(f"[bench] achievable: {res}", file=sys.stderr, flush=True)
+    return res
+
+
+def time_fp32_configs(sgc, torch, np, dev, stream, warm=10, reps=60):
+    """The two fp32 configurations: the tiny 16x32 forward (launch-latency bound) and the 181x360 ->
+    91x180 forward and backward.  Each timed call reads and writes a different set of buffers, eight
+    sets in rotation for 181x360 (8 x 67 MB > 512 MiB: beyond the 256 MiB last-level cache, so the
+    bytes come from HBM); medians and spread of `reps` calls after `warm`.  Roofline: one fp32 FMA per
+    nnz-update on the vector ALU (2 flops) against 16 flops per algorithmic byte: the ALU floor (6.8 us
+    at 157.3 TFLOP/s) lies below the HBM floor (8.4 us at 8 TB/s), so the bound is HBM."""
+    from disco_inputs import WORKLOADS, workload_gout, workload_psi, workload_x
+
+    res = {}
+    for name, nrot in (("tiny_fwd_f32_16x32", 1), ("fwdbwd_f32_181x360", 8)):
+        w = WORKLOADS[name]
+        psi = workload_psi(w)
+        h = sgc.disco_psi_create(psi, 0)
+        xs = [workload_x(w).to(dev) for _ in range(nrot)]
+        outs = [torch.empty((w.B, w.C, w.K, w.Ho, w.Wo), dtype=torch.float32, device=dev) for _ in range(nrot)]
+        calls = {"fwd": [lambda i=i: sgc.disco_fwd(h, xs[i], outs[i]) for i in range(nrot)]}
+        if "bwd" in w.ops:
+            gs = [workload_gout(w).to(dev) for _ in range(nrot)]
+            gxs = [torch.empty((w.B, w.C, w.Hi, w.Wi), dtype=torch.float32, device=dev) for _ in range(nrot)]
+            calls["bwd"] = [lambda i=i: sgc.disco_bwd(h, gs[i], gxs[i]) for i in range(nrot)]
+        upd = op_updates(w, psi.nnz)
+        for op, fns in calls.items():
+            for i in range(warm):
+                fns[i % nrot]()
+            torch.cuda.synchronize()
+            ev = []
+            for i in range(reps):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fns[i % nrot]()
+                b.record(stream)
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in ev])
+            ms = float(np.median(t))
+            byt = op_bytes(op, w, psi.nnz)
+            tf = 2 * upd / ms / 1e9
+            res[f"{name}:{op}"] = {
+                "ms_median": round(ms, 5), "ms_p10": round(float(np.percentile(t, 10)), 5),
+                "ms_p90": round(float(np.percentile(t, 90)), 5), "calls": reps, "buffer_sets": nrot,
+                "bytes": byt, "updates": upd, "GBps": round(byt / ms / 1e6, 2),
+                "Gnnz_updates_per_s": round(upd / ms / 1e6, 2), "hbm_frac": round(byt / ms / 1e6 / PEAK_HBM_GBS, 5),
+                "bound": ("launch latency" if name == "tiny_fwd_f32_16x32" else
+                          ("hbm" if byt / PEAK_HBM_GBS >= 2 * upd / PEAK_FP32_FMA_TFLOPS / 1e3 else "alu")),
+                "valu_tflops": round(tf, 3), "valu_frac": round(tf / PEAK_FP32_FMA_TFLOPS, 4),
+                "hbm_floor_us": round(byt / PEAK_HBM_GBS / 1e3, 2),
+                "alu_floor_us": round(2 * upd / PEAK_FP32_FMA_TFLOPS / 1e6, 2),
+                "shape": {"B": w.B, "C": w.C, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo], "nnz": psi.nnz}}
+        h.close()
+        del xs, outs
+        torch.cuda.empty_cache()
+    print(f"[bench] fp32 configs: { {k: v['ms_median'] for k, v in res.items()} }", file=sys.stderr, flush=True)
+    return res
 
 def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=3):
     """Backward of the fused convolution on the fused workload (gradient gy ~ N(0,1), bf16), timed
@@ -488,8 +599,9 @@ def cpu_baseline(wf, wb, wu, psi_fb, psi_u):
     nnz_ho = sum(int(r0[k * wu.Ho + h + 1] - r0[k * wu.Ho + h]) for k in range(wu.K) for h in hos)
     upd_u = wu.C * wu.Wo * nnz_ho
     total = upd + upd_u
-    return {"value": round(total / (t_fb + t_u) / 1e9, 4), "unit": "Gnnz-updates/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    return {"value": round(total / (t_fb + t_u) / 1e9, 4), "unit": "Gnnz-updates/s",
+            "cores": len(os.sched_getaffinity(0)), "threads": oracle.num_threads(), "kind": "oracle",
+            "legs_s": {"fwd_bwd": round(t_fb, 2), "fused": round(t_u, 2)},
             "sample": f"fwd+bwd on {planes}/64 channel planes of the 721x1440 K=8 workload "
                       f"({t_fb:.1f}s) + fused contraction and einsum for latitudes {hos} of batch 0 of the "
                       f"K=16 workload ({t_u:.1f}s); updates counted as in value",

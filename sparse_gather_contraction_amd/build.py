@@ -15,6 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdisco.so")
+PROBE_LIB = os.path.join(PKG, "libdisco_probes.so")  # microbenchmarks of the device (measurement only)
 
 SOURCES = ["plan.cpp", "plan_fused.cpp", "plan_tile.cpp", "kernels_tile.hip", "disco_api.hip", "kernels_gather.hip", "kernels_staged.hip", "kernels_fused.hip",
            "kernels_fused_mfma.hip", "kernels_gemm.hip"]
@@ -58,8 +59,15 @@ def build(verbose: bool = False) -> str:
     if missing:
         raise RuntimeError("libdisco.so has undefined symbols of its own: " + ", ".join(missing))
     os.replace(tmp, LIB)
+    probe_obj = _compile("probes.hip")
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", probe_obj, "-o", tmp],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe link failed:\n" + r.stdout)
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
