@@ -112,17 +112,22 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
 
 /* Fused convolution.  x: (B, C, Hi, Wi), W: (Co, C, K) -> y: (B, Co, Ho, Wo).
  * The contraction is computed on chip in channel chunks and never written to
- * device memory; the einsum runs on bf16 or fp16 MFMA tiles with fp32
- * accumulation (contraction chunks are rounded to the data type before the
- * MFMA).  BF16 and F16. */
+ * device memory.  BF16 and F16: the einsum runs on bf16 or fp16 MFMA tiles with
+ * fp32 accumulation (contraction chunks are rounded to the data type before the
+ * MFMA).  F32: fp32 throughout (fp32 psi, an fp32 contraction chunk, the einsum
+ * on the fp32 matrix cores) — the fp32 variant the 16-bit ones are compared
+ * with (same page, "Test coverage requirements"). */
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
 
 /* Fused convolution that also keeps its contraction, for a training step whose backward then need not
  * recompute it: y as disco_fused_conv, and out[b,c,k,ho,wo] = the contraction F x (B, C, K, Ho, Wo) in
- * the data type — the very values the einsum multiplied (each fp32 accumulator rounded once, RNE).
- * Same page, "Python dispatch layer": the fused autograd function keeps what its backward needs.
- * BF16 and F16.  out is caller-owned and overwritten; it must not alias x, W or y. */
+ * the data type (each fp32 accumulator rounded once, RNE).  On the matrix-core fused kernel (BF16 and
+ * F16 data on its plan) out holds the very values the einsum multiplied; otherwise (F32 data, shapes
+ * outside that plan) out comes from disco_fwd, whose summation order may differ from the fused
+ * kernel's by rounding.  Same page, "Python dispatch layer": the fused autograd function keeps what
+ * its backward needs.  out is caller-owned and overwritten; it must not overlap x, W or y
+ * (DISCO_ERR_INVALID_ARGUMENT). */
 disco_status disco_fused_conv_save(disco_psi h, const disco_tensor *x, const disco_tensor *W, disco_tensor *y,
                                    disco_tensor *out, void *stream);
 
@@ -143,10 +148,12 @@ disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_te
  * pairs the fused forward with the CSR transpose backward; "Test coverage requirements": fused
  * and unfused agree in output and gradient).
  * x: (B, C, Hi, Wi), W: (Co, C, K), gy: (B, Co, Ho, Wo) -> gx: (B, C, Hi, Wi), dW: (Co, C, K).
- * BF16 only; Co and Ho*Wo must be multiples of 8 and K <= 256.  Computed in channel chunks of
- * g (bf16, on the matrix cores), the transpose contraction, the forward contraction (bf16) and
- * a split product for dW whose fp32 partials are summed in a fixed order: results are bitwise
- * reproducible run to run.  `workspace` is caller-owned device memory (256-byte aligned) of at
+ * BF16 and F16; Co and Ho*Wo must be multiples of 8, K <= 256, and one batch of gy, of a channel
+ * chunk of g, and W must each stay below 2 GiB (the matrix-core loads address 32-bit offsets).
+ * Computed in channel chunks of g (the data type, on the matrix cores), the transpose contraction,
+ * the forward contraction (the data type) and a split product for dW whose fp32 partials are summed
+ * in a fixed order: results are bitwise reproducible run to run.  gx and dW must not overlap any
+ * input (DISCO_ERR_INVALID_ARGUMENT).  `workspace` is caller-owned device memory (256-byte aligned) of at
  * least the size disco_fused_conv_bwd_workspace reports for (B, C, Co); its contents on entry
  * are ignored and on return are unspecified.  Calls sharing one workspace must not overlap. */
 disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, int64_t Co, size_t *bytes);
@@ -157,7 +164,13 @@ disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disc
 /* The same backward with the weight gradient's operand taken from `out`, the contraction that
  * disco_fused_conv_save wrote for the same x, instead of recomputing it from x (x is not needed).
  * out: (B, C, K, Ho, Wo); the other arguments, the workspace and the results as disco_fused_conv_bwd,
- * whose results it reproduces bitwise when out comes from disco_fused_conv_save. */
+ * whose results it reproduces bitwise when out comes from disco_fused_conv_save.
+ * The weight-gradient products run on a second stream that the library keeps per device (default
+ * priority, created on first use, never destroyed): it waits for everything enqueued on `stream`
+ * before the call, and `stream` waits for it before the call returns (also on an error return), so
+ * the call behaves as if everything ran on `stream`.  Concurrent calls on one device share that
+ * stream, so their weight-gradient work serialises; under graph capture of `stream` the fork and
+ * join are captured as event dependencies. */
 disco_status disco_fused_conv_bwd_saved(disco_psi h, const disco_tensor *out, const disco_tensor *W,
                                         const disco_tensor *gy, disco_tensor *gx, disco_tensor *dW, void *workspace,
                                         size_t workspace_bytes, void *stream);

@@ -262,6 +262,28 @@ disco_status check_tensor(const disco_tensor *t, const char *name, int ndim, con
     return DISCO_OK;
 }
 
+// Byte range of a tensor view (empty when it has no elements).
+void byte_range(const disco_tensor *t, uintptr_t &lo, uintptr_t &hi)
+{
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim && i < 5; ++i) n *= t->shape[i];
+    const int64_t esz = t->dtype == DISCO_F32 ? 4 : 2;
+    lo = (uintptr_t)t->data;
+    hi = lo + (uintptr_t)(n > 0 ? n * esz : 0);
+}
+
+// DISCO_ERR_INVALID_ARGUMENT when output `o` shares bytes with `t` (both already validated).
+disco_status check_disjoint(const disco_tensor *o, const char *oname, const disco_tensor *t, const char *tname)
+{
+    if (!o || !t || !o->data || !t->data) return DISCO_OK;
+    uintptr_t a0, a1, b0, b1;
+    byte_range(o, a0, a1);
+    byte_range(t, b0, b1);
+    if (a0 < b1 && b0 < a1)
+        return fail(DISCO_ERR_INVALID_ARGUMENT, std::string(oname) + " overlaps " + tname);
+    return DISCO_OK;
+}
+
 bool log_enabled()
 {
     const char *e = getenv("DISCO_LOG");
@@ -749,6 +771,7 @@ disco_status disco_fwd(disco_psi h, const disco_tensor *x, disco_tensor *out, vo
     if ((st = check_tensor(x, "x", 4, xs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(out, "out", 5, os, h->device)) != DISCO_OK) return st;
     if (x->dtype != out->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
+    if ((st = check_disjoint(out, "out", x, "x")) != DISCO_OK) return st;
     return enqueue_fwd(h, x->data, out->data, x->dtype, B, C, (hipStream_t)stream);
 }
 
@@ -765,6 +788,7 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
     if ((st = check_tensor(gout, "gout", 5, gs, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(gx, "gx", 4, xs, h->device)) != DISCO_OK) return st;
     if (gout->dtype != gx->dtype) return fail(DISCO_ERR_DTYPE, "gout and gx dtypes differ");
+    if ((st = check_disjoint(gx, "gx", gout, "gout")) != DISCO_OK) return st;
     return enqueue_bwd(h, gout->data, gx->data, gout->dtype, B, C, (hipStream_t)stream);
 }
 
@@ -789,20 +813,26 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
     if ((st = check_tensor(W, "W", 3, ws, h->device)) != DISCO_OK) return st;
     if ((st = check_tensor(y, "y", 4, ys, h->device)) != DISCO_OK) return st;
     if (x->dtype != W->dtype || x->dtype != y->dtype) return fail(DISCO_ERR_DTYPE, "x, W and y dtypes differ");
-    if (x->dtype == DISCO_F32) return fail(DISCO_ERR_DTYPE, "the fused convolution supports bf16 and fp16 only");
     if (save) {
         const int64_t os[5] = {B, C, h->K, h->Ho, h->Wo};
         if ((st = check_tensor(save, "out", 5, os, h->device)) != DISCO_OK) return st;
         if (save->dtype != x->dtype) return fail(DISCO_ERR_DTYPE, "x and out dtypes differ");
+        if ((st = check_disjoint(save, "out", x, "x")) != DISCO_OK) return st;
+        if ((st = check_disjoint(save, "out", W, "W")) != DISCO_OK) return st;
+        if ((st = check_disjoint(save, "out", y, "y")) != DISCO_OK) return st;
     }
-    if (save && B * C * h->Ho * h->Wo > 0 && (B * Co == 0 || !h->fused.ok || getenv_is0("DISCO_FUSED_MFMA"))) {
+    if ((st = check_disjoint(y, "y", x, "x")) != DISCO_OK) return st;
+    if ((st = check_disjoint(y, "y", W, "W")) != DISCO_OK) return st;
+    // every check before anything is enqueued (the fallback below writes `out` first)
+    if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
+        return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
+    if (save && B * C * h->Ho * h->Wo > 0 &&
+        (B * Co == 0 || x->dtype == DISCO_F32 || !h->fused.ok || getenv_is0("DISCO_FUSED_MFMA"))) {
         // no matrix-core fused kernel to keep the contraction from: the forward writes it
         if ((st = enqueue_fwd(h, x->data, save->data, x->dtype, B, C, (hipStream_t)stream)) != DISCO_OK) return st;
     }
     if (B * Co * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
-    if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
-        return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
-    if (h->fused.ok && !getenv_is0("DISCO_FUSED_MFMA")) {  // test knob: "0" forces the VALU-contraction fused kernel
+    if (x->dtype != DISCO_F32 && h->fused.ok && !getenv_is0("DISCO_FUSED_MFMA")) {  // test knob: "0" forces the VALU-contraction fused kernel
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
         m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs;
@@ -826,6 +856,7 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
     a.W = W->data;
     a.y = y->data;
     a.f16 = x->dtype == DISCO_F16;
+    a.f32 = x->dtype == DISCO_F32;
     a.items = h->fwd.items;
     a.block_ptr = h->fwd.block_ptr;
     a.ho_order = h->ho_order;
@@ -886,6 +917,8 @@ disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_te
     if ((st = check_tensor(W, "W", 3, ws, dev)) != DISCO_OK) return st;
     if ((st = check_tensor(y, "y", 4, ys, dev)) != DISCO_OK) return st;
     if (t->dtype != W->dtype || t->dtype != y->dtype) return fail(DISCO_ERR_DTYPE, "t, W and y dtypes differ");
+    if ((st = check_disjoint(y, "y", t, "t")) != DISCO_OK) return st;
+    if ((st = check_disjoint(y, "y", W, "W")) != DISCO_OK) return st;
     if (t->dtype == DISCO_F32) return fail(DISCO_ERR_DTYPE, "the einsum supports bf16 and fp16 only");
     const int64_t HW = Ho * Wo;
     if (B * Co * HW == 0) return DISCO_OK;
@@ -943,7 +976,19 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
     if ((st = check_tensor(dW, "dW", 3, ws, h->device)) != DISCO_OK) return st;
     if (src->dtype != W->dtype || src->dtype != gy->dtype || src->dtype != gx->dtype || src->dtype != dW->dtype)
         return fail(DISCO_ERR_DTYPE, x ? "x, W, gy, gx and dW dtypes differ" : "out, W, gy, gx and dW dtypes differ");
-    if (src->dtype != DISCO_BF16) return fail(DISCO_ERR_DTYPE, "the fused convolution backward supports bf16 only");
+    if (src->dtype != DISCO_BF16 && src->dtype != DISCO_F16)
+        return fail(DISCO_ERR_DTYPE, "the fused convolution backward supports bf16 and fp16 only");
+    const int dt = src->dtype;
+    const bool f16 = dt == DISCO_F16;
+    {
+        const disco_tensor *ins[3] = {src, W, gy};
+        const char *names[3] = {x ? "x" : "out", "W", "gy"};
+        for (int i = 0; i < 3; ++i) {
+            if ((st = check_disjoint(gx, "gx", ins[i], names[i])) != DISCO_OK) return st;
+            if ((st = check_disjoint(dW, "dW", ins[i], names[i])) != DISCO_OK) return st;
+        }
+        if ((st = check_disjoint(dW, "dW", gx, "gx")) != DISCO_OK) return st;
+    }
     if (h->K > 256) return fail(DISCO_ERR_SHAPE, "the fused convolution backward supports K <= 256");
     const FusedBwdLayout L = fused_bwd_layout(h, B, C, Co, cap);
     if (Co % 8 != 0 || L.N % 8 != 0)
@@ -986,39 +1031,56 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
             g2.A = gyp + b * Co * N; g2.lda = N; g2.M = (int32_t)Co; g2.a_bytes = (uint32_t)(Co * N * 2);
             g2.B = outp + b * ostride; g2.ldb = N; g2.N = Mc; g2.b_bytes = (uint32_t)((int64_t)Mc * N * 2);
             g2.Kd = (int32_t)N; g2.k_per_split = L.kps; g2.out_f32 = true;
-            g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc;
+            g2.C = part + b * (int64_t)L.S * Co * Mc; g2.ldc = Mc; g2.f16 = f16;
             if ((e = disco::launch_gemm_nt(g2, sd)) != hipSuccess) return hipfail(e, "gy out^T product");
         }
-        if ((e = disco::launch_reduce_partials(part, (int)(B * L.S), (int)Co, Mc, dW->data, CK, (int)(c0 * K), sd)) !=
+        if ((e = disco::launch_reduce_partials(part, (int)(B * L.S), (int)Co, Mc, dW->data, CK, (int)(c0 * K), f16, sd)) !=
             hipSuccess)
             return hipfail(e, "dW reduction");
         return DISCO_OK;
     };
     // With the contraction kept, dW depends on the inputs only: it runs on a second stream, overlapping
     // the chain W^T gy -> transpose contraction on the caller's stream (ordered by events at both ends).
-    struct Events {
+    // Once the side stream waits on the caller's, every exit joins it back (the guard's destructor on
+    // an early error return), so no side-stream work outlives the call unordered.
+    struct Fork {
         hipEvent_t in = nullptr, done = nullptr;
-        ~Events() {
+        hipStream_t main = nullptr, side = nullptr;  // side set once it waits on `in`
+        hipError_t join()
+        {
+            if (!side) return hipSuccess;
+            hipStream_t s = side;
+            side = nullptr;
+            hipError_t e = hipEventRecord(done, s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(main, done, 0);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                (void)hipStreamSynchronize(s);  // cannot order on the device: wait on the host instead
+            }
+            return e;
+        }
+        ~Fork()
+        {
+            (void)join();
             if (in) (void)hipEventDestroy(in);
             if (done) (void)hipEventDestroy(done);
         }
-    } ev;
+    } fork;
     hipStream_t sd = sm;
     if (svp && C > 0) {
         hipStream_t side = side_stream(h->device);
-        if (side && hipEventCreateWithFlags(&ev.in, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&ev.done, hipEventDisableTiming) == hipSuccess &&
-            hipEventRecord(ev.in, sm) == hipSuccess && hipStreamWaitEvent(side, ev.in, 0) == hipSuccess) {
+        fork.main = sm;
+        if (side && hipEventCreateWithFlags(&fork.in, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&fork.done, hipEventDisableTiming) == hipSuccess &&
+            hipEventRecord(fork.in, sm) == hipSuccess && hipStreamWaitEvent(side, fork.in, 0) == hipSuccess) {
             sd = side;
+            fork.side = side;
         } else {
             (void)hipGetLastError();  // no second stream: everything on the caller's
         }
         for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
             const int32_t Mc = (int32_t)(std::min<int64_t>(L.Cc, C - c0) * K);
             if ((st = dw_chunk(c0, Mc, svp + c0 * K * N, C * K * N, sd)) != DISCO_OK) return st;
-        }
-        if (sd != sm) {
-            if ((e = hipEventRecord(ev.done, sd)) != hipSuccess) return hipfail(e, "event record");
         }
     }
     for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
@@ -1033,10 +1095,11 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
             g1.A = wt + c0 * K * Co; g1.lda = Co; g1.M = Mc; g1.a_bytes = (uint32_t)((int64_t)Mc * Co * 2);
             g1.B = gyt + b * N * Co; g1.ldb = Co; g1.N = (int32_t)N; g1.b_bytes = (uint32_t)(N * Co * 2);
             g1.Kd = (int32_t)Co; g1.k_per_split = 0; g1.out_f32 = false; g1.C = gb + b * gstride; g1.ldc = N;
+            g1.f16 = f16;
             if ((e = disco::launch_gemm_nt(g1, sm)) != hipSuccess) return hipfail(e, "W^T gy product");
         }
         // gx[b, c0 + c] = F^T g, every batch in one launch
-        if ((st = enqueue_bwd(h, gb, gxp + c0 * plane_in, DISCO_BF16, B, cc, sm, gstride, C * plane_in)) != DISCO_OK)
+        if ((st = enqueue_bwd(h, gb, gxp + c0 * plane_in, dt, B, cc, sm, gstride, C * plane_in)) != DISCO_OK)
             return st;
         // out[b][c k][n] = (F x)[b, c0 + c]: the fused kernel's contraction (psi resident across the
         // chunk's channels) where its plan exists, else the forward contraction; nothing to compute
@@ -1045,24 +1108,23 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
         } else if (h->fused.ok && !getenv_is0("DISCO_FUSED_MFMA")) {  // test knob: "0" also turns this path off
             disco::FusedContractLaunch m;
             m.x = xp + c0 * plane_in; m.out = gb;
-            m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs; m.adata = h->fused.adata;
+            m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs;
+            m.adata = f16 ? h->fused.adata16 : h->fused.adata;
             m.ho_piece = h->fused.ho_piece; m.ho_order = h->fused.ho_order;
             m.B = (int32_t)B; m.C = (int32_t)cc; m.K = h->K; m.Ho = h->Ho; m.Wo = h->Wo; m.Hi = h->Hi; m.Wi = h->Wi;
             m.s = h->Wi / h->Wo; m.max_piece_bytes = h->fused.max_piece_bytes;
             m.max_resident_bytes = h->fused.max_resident_bytes;
             m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
-            m.f16 = false; m.scale = 1.0f;
+            m.f16 = f16; m.scale = f16 ? std::ldexp(1.0f, -h->fused.psi16_exp) : 1.0f;
             m.x_bstride = C * plane_in; m.out_bstride = gstride;
             if ((e = disco::launch_fused_contract(m, sm)) != hipSuccess) return hipfail(e, "contraction");
-        } else if ((st = enqueue_fwd(h, xp + c0 * plane_in, gb, DISCO_BF16, B, cc, sm, C * plane_in, gstride)) !=
+        } else if ((st = enqueue_fwd(h, xp + c0 * plane_in, gb, dt, B, cc, sm, C * plane_in, gstride)) !=
                    DISCO_OK) {
             return st;
         }
         if (!svp && (st = dw_chunk(c0, Mc, gb, gstride, sm)) != DISCO_OK) return st;
     }
-    if (sd != sm) {
-        if ((e = hipStreamWaitEvent(sm, ev.done, 0)) != hipSuccess) return hipfail(e, "stream wait");
-    }
+    if ((e = fork.join()) != hipSuccess) return hipfail(e, "side-stream join");
     return DISCO_OK;
 }
 

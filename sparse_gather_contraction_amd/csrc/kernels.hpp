@@ -69,10 +69,11 @@ bool staged_supported(int NI, int G, int T, int S);
 hipError_t launch_staged(const StagedLaunch &a, hipStream_t stream);
 
 struct FusedLaunch {
-    const void *x;          // (B, C, Hi, Wi) bf16 or fp16
+    const void *x;          // (B, C, Hi, Wi) bf16, fp16 or fp32
     const void *W;          // (Co, C, K)
     void *y;                // (B, Co, Ho, Wo)
     bool f16;               // fp16 data (else bf16)
+    bool f32 = false;       // fp32 data: fp32 contraction tile and fp32 matrix-core einsum
     const Item *items;      // forward plan items, grouped by ho
     const int32_t *block_ptr;  // [Ho + 1]
     const int32_t *ho_order;   // [Ho], heaviest latitude first
@@ -163,10 +164,10 @@ int fwd_mfma_channels(int kr);       // channels per forward workgroup for a psi
 size_t fused_mfma_reserved_bytes();  // LDS bytes besides the two piece stage buffers
 int fused_max_k();  // largest K the fused kernel accepts
 
-// C[m][n] = sum_k A[m][k] B[n][k] on bf16 matrix cores (operands contiguous along k; k ranges and
-// Kd multiples of 8; operand buffers below 2 GiB).  out_f32: fp32 partials [split][M][N], one per
-// k range of k_per_split (a multiple of 32); else bf16 C with row stride ldc (k_per_split = 0: one
-// range).
+// C[m][n] = sum_k A[m][k] B[n][k] on bf16 (or fp16) matrix cores (operands contiguous along k; k
+// ranges and Kd multiples of 8; operand buffers below 2 GiB).  out_f32: fp32 partials [split][M][N],
+// one per k range of k_per_split (a multiple of 32); else 16-bit C with row stride ldc
+// (k_per_split = 0: one range).
 struct GemmNtLaunch {
     const void *A;
     int64_t lda;
@@ -180,12 +181,13 @@ struct GemmNtLaunch {
     bool out_f32;
     void *C;
     int64_t ldc;
+    bool f16 = false;  // fp16 operands and output (else bf16)
 };
 hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream);
-// dst (Cn x R) = src (R x Cn)^T, bf16.
+// dst (Cn x R) = src (R x Cn)^T, 16-bit elements (bf16 or fp16: the bits are moved).
 hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream);
-// dW[o][col0 + m] = bf16(sum_{z < Z} P[z][o][m]), summed in increasing z.
-hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0,
+// dW[o][col0 + m] = 16-bit(sum_{z < Z} P[z][o][m]) (fp16 when f16, else bf16), summed in increasing z.
+hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0, bool f16,
                                   hipStream_t stream);
 
 }  // namespace disco

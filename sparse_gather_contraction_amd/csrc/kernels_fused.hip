@@ -11,7 +11,8 @@
 // the data type (bf16 or fp16) into LDS as a [pixel][c*K + k] tile, and then
 // multiplied on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16} with W as the
 // A operand (16 o x 32 rows) and the LDS tile as the B operand (32 rows x 16
-// pixels), fp32 accumulation in registers across all chunks.
+// pixels), fp32 accumulation in registers across all chunks.  fp32 data keeps
+// the chunk in fp32 and runs the einsum on v_mfma_f32_16x16x4_f32.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -52,6 +53,10 @@ template <> struct Elem<f16_t> {
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
+};
+
+template <> struct Elem<float> {  // fp32 data (the contraction's loads only; the einsum has its own kernel)
+    static __device__ __forceinline__ float to_f32(float v) { return v; }
 };
 
 template <int G, typename T>
@@ -188,6 +193,110 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
             }
 }
 
+// fp32 data: the same block structure with an fp32 contraction tile and the einsum on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32: A = W, 16 output channels x 4 rows; B = the tile, 4 rows x
+// 16 pixels), fp32 products and accumulation throughout.
+constexpr int kLdsStride32 = kR + 4;  // floats per pixel row (the 16 lanes of a row group hit distinct banks)
+
+__global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__restrict__ x, const float *__restrict__ W,
+                                                             float *__restrict__ y, const Item *__restrict__ items,
+                                                             const int32_t *__restrict__ block_ptr,
+                                                             const int32_t *__restrict__ ho_order,
+                                                             const Seg *__restrict__ segs,
+                                                             const float *__restrict__ vals, int B, int C, int Co,
+                                                             int K, int Ho, int Wo, int Hi, int Wi, int in_stride,
+                                                             int n_pt, int n_ob)
+{
+    __shared__ __attribute__((aligned(16))) float tile[kPx * kLdsStride32];
+
+    int bid = blockIdx.x;
+    const int pt = bid % n_pt;
+    bid /= n_pt;
+    const int ob = bid % n_ob;
+    bid /= n_ob;
+    const int b = bid % B;
+    const int ho = ho_order[bid / B];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wo0 = pt * kPx;
+    const int o_base = ob * kOBlk + wave * 64;
+    const int CC = kR / K;
+    const int64_t plane_sz = (int64_t)Hi * Wi;
+    const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
+    const int HoWo = Ho * Wo;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int npass = (CC * kPx + kThreads - 1) / kThreads;
+    for (int c0 = 0; c0 < C; c0 += CC) {
+        const int ccn = min(CC, C - c0);
+        __syncthreads();  // the previous chunk's MFMA reads of `tile` are done
+        for (int pass = 0; pass < npass; ++pass) {
+            const int pair = tid + kThreads * pass;
+            const int cl = pair / kPx;
+            const int px = pair - cl * kPx;
+            const int wo = wo0 + px;
+            const bool valid = (cl < ccn) && (wo < Wo);
+            const float *plane = x + ((int64_t)b * C + (c0 + (cl < ccn ? cl : 0))) * plane_sz;
+            for (int ii = it_begin; ii < it_end; ++ii) {
+                const Item it = items[ii];
+                float a[kMaxGroup];
+                switch (it.G) {
+                case 1: contract_item<1, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 2: contract_item<2, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                case 3: contract_item<3, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                default: contract_item<4, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+                }
+                if (cl < CC) {
+                    for (int g = 0; g < it.G; ++g) {
+                        const int k = it.out_off[g] / HoWo;
+                        tile[px * kLdsStride32 + cl * K + k] = valid ? a[g] : 0.0f;
+                    }
+                }
+            }
+        }
+        for (int e = tid; e < kPx * kR; e += kThreads) {
+            const int px = e / kR, r = e - px * kR;
+            if (r >= ccn * K) tile[px * kLdsStride32 + r] = 0.0f;
+        }
+        __syncthreads();
+        const int rvalid = ccn * K;
+        const int rl = lane >> 4;  // the lane's row within a 4-row step
+#pragma unroll 4
+        for (int ks = 0; ks < kR / 4; ++ks) {
+            const int rr = ks * 4 + rl;
+            float bop[4];
+#pragma unroll
+            for (int p4 = 0; p4 < 4; ++p4) bop[p4] = tile[(p4 * 16 + (lane & 15)) * kLdsStride32 + rr];
+#pragma unroll
+            for (int ot = 0; ot < 4; ++ot) {
+                const int o = o_base + ot * 16 + (lane & 15);
+                const float aop = (o < Co && rr < rvalid) ? W[((int64_t)o * C + c0) * K + rr] : 0.0f;
+#pragma unroll
+                for (int p4 = 0; p4 < 4; ++p4)
+                    acc[ot][p4] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop[p4], acc[ot][p4], 0, 0, 0);
+            }
+        }
+    }
+    // D[row = o][col = pixel]: lane holds col lane & 15, rows 4 (lane >> 4) + a
+#pragma unroll
+    for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+        for (int p4 = 0; p4 < 4; ++p4)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int o = o_base + ot * 16 + 4 * (lane >> 4) + a;
+                const int wo = wo0 + p4 * 16 + (lane & 15);
+                if (o < Co && wo < Wo) y[(((int64_t)b * Co + o) * Ho + ho) * Wo + wo] = acc[ot][p4][a];
+            }
+}
+
 }  // namespace
 
 hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
@@ -196,7 +305,11 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
     const int n_pt = (a.Wo + kPx - 1) / kPx;
     const int n_ob = (a.Co + kOBlk - 1) / kOBlk;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pt;
-    if (a.f16)
+    if (a.f32)
+        hipLaunchKernelGGL(fused_f32_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const float *)a.x,
+                           (const float *)a.W, (float *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
+                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    else if (a.f16)
         hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
                            (const f16_t *)a.W, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);

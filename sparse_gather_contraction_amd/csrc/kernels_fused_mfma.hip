@@ -394,7 +394,8 @@ __device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d
 // Fused op that keeps its contraction: chunk t's result (channels kCh t .. + 3), read back from the
 // einsum's operand exchange — the fp32 accumulators rounded to the data type, exactly the values
 // the einsum multiplied and the values the contraction-only mode writes — to save[b, c, k, ho, ...]
-// as 16-byte row segments.  Exchange unit (pp, h2, cl, ph), lane (r, hh) holds basis 8 hh .. + 7
+// as 16-byte row segments (by the first output-channel block only: the others hold the same values).
+// Exchange unit (pp, h2, cl, ph), lane (r, hh) holds basis 8 hh .. + 7
 // of longitude px0 + 8 r + 2 pp + ph, channel kCh t + 2 h2 + cl.  Called after the einsum (every
 // wave's operands are in the exchange); the exchange is overwritten only after the next step's
 // opening barrier.
@@ -449,7 +450,9 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // W slice visible; `cur` free for the exchange
             einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
-            if constexpr (SAVE) save_contraction(c, cur, t);
+            if constexpr (SAVE) {
+                if (c.o_base == 0) save_contraction(c, cur, t);  // one output-channel block writes it
+            }
         } else {
             store_contraction<F16>(c, d, t, pp, h2, wb);
         }
@@ -475,7 +478,9 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
         einsum<NOTH, F16>(cur, wb, c.lane, pp, h2, c.scale, d, yacc);
-        if constexpr (SAVE) save_contraction(c, cur, t);
+        if constexpr (SAVE) {
+            if (c.o_base == 0) save_contraction(c, cur, t);  // one output-channel block writes it
+        }
     } else {
         store_contraction<F16>(c, d, t, pp, h2, wb);
     }

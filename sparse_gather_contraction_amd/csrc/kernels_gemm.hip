@@ -1,4 +1,4 @@
-// kernels_gemm.hip — dense bf16 products on the gfx950 matrix cores for the backward of the fused
+// kernels_gemm.hip — dense bf16 / fp16 products on the gfx950 matrix cores for the backward of the fused
 // convolution (the gradients of <gy, y> for y = einsum(W, F x); torch-harmonics
 // "disco-kernel-dev" page, "Python dispatch layer": the fused autograd function pairs the fused
 // forward with the CSR transpose backward).
@@ -46,7 +46,29 @@ typedef GTile<128, 128, 2, 2> GSmall;
 typedef GTile<256, 256, 2, 4> GLarge;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One 32 x 32 x 16 product on the data type's matrix cores (operands travel as raw 16-bit patterns).
+template <bool F16>
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> the data type's 16-bit pattern, round to nearest even
+template <bool F16>
+__device__ __forceinline__ bf16_t to16(float v)
+{
+    if constexpr (F16)
+        return __builtin_bit_cast(bf16_t, (_Float16)v);
+    else
+        return f32_to_bf16(v);
+}
 typedef void __attribute__((address_space(3))) *lptr_t;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -89,8 +111,9 @@ __device__ __forceinline__ bf16x8 frag(const unsigned char *op, int row, int ks,
 }
 
 // C[m][n] = sum_{k in [k_begin, k_end)} A[m][k] B[n][k]; the tile index selects the k range (split).
-// OUT_F32: fp32 partial [z][M][N]; else bf16 C with row stride ldc.
-template <typename T, bool OUT_F32>
+// OUT_F32: fp32 partial [z][M][N]; else 16-bit C with row stride ldc.  F16: fp16 operands and
+// output (else bf16); the operands move as raw 16-bit patterns either way.
+template <typename T, bool OUT_F32, bool F16>
 __global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__restrict__ A, int64_t lda, int M,
                                                               uint32_t a_bytes, const bf16_t *__restrict__ Bm,
                                                               int64_t ldb, int N, uint32_t b_bytes, int Kd,
@@ -158,7 +181,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__re
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    d[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], d[i][j], 0, 0, 0);
+                    d[i][j] = mma<F16>(fa[i], fb[j], d[i][j]);
         }
     }
 
@@ -183,7 +206,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__re
 #pragma unroll
                         for (int a = 0; a < 16; ++a) {
                             const int ml = 32 * i + 8 * (a >> 2) + 4 * h + (a & 3);
-                            tile[ml * PITCH + (T::TN / T::WN) * wn + 32 * j + r] = f32_to_bf16(d[i][j][a]);
+                            tile[ml * PITCH + (T::TN / T::WN) * wn + 32 * j + r] = to16<F16>(d[i][j][a]);
                         }
             }
             __syncthreads();
@@ -215,7 +238,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_nt_kernel(const bf16_t *__re
                 if constexpr (OUT_F32)
                     reinterpret_cast<float *>(Cout)[((int64_t)z * M + m) * N + n] = d[i][j][a];
                 else
-                    reinterpret_cast<bf16_t *>(Cout)[(int64_t)m * ldc + n] = f32_to_bf16(d[i][j][a]);
+                    reinterpret_cast<bf16_t *>(Cout)[(int64_t)m * ldc + n] = to16<F16>(d[i][j][a]);
             }
         }
 }
@@ -239,7 +262,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16_t *__restrict
     }
 }
 
-// dW[o][col0 + m] = bf16(sum_{z < Z} P[z][o][m]) in increasing z.
+// dW[o][col0 + m] = 16-bit(sum_{z < Z} P[z][o][m]) in increasing z.
+template <bool F16>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ P, int Z, int Co, int Mc,
                                                               bf16_t *__restrict__ dW, int64_t ldw, int col0)
 {
@@ -248,10 +272,10 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
     const int o = (int)(i / Mc), m = (int)(i % Mc);
     float acc = 0.0f;
     for (int z = 0; z < Z; ++z) acc += P[((int64_t)z * Co + o) * Mc + m];
-    dW[(int64_t)o * ldw + col0 + m] = f32_to_bf16(acc);
+    dW[(int64_t)o * ldw + col0 + m] = to16<F16>(acc);
 }
 
-template <typename T>
+template <typename T, bool F16>
 hipError_t launch_gemm_tiles(const GemmNtLaunch &g, hipStream_t stream)
 {
     const int splits = (g.out_f32 && g.k_per_split > 0) ? (g.Kd + g.k_per_split - 1) / g.k_per_split : 1;
@@ -261,11 +285,11 @@ hipError_t launch_gemm_tiles(const GemmNtLaunch &g, hipStream_t stream)
     if (total >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));  // a multiple of the eight XCDs
     if (g.out_f32)
-        hipLaunchKernelGGL((gemm_nt_kernel<T, true>), grid, dim3(T::kThreads), 0, stream, (const bf16_t *)g.A, g.lda,
+        hipLaunchKernelGGL((gemm_nt_kernel<T, true, F16>), grid, dim3(T::kThreads), 0, stream, (const bf16_t *)g.A, g.lda,
                            g.M, g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m,
                            nt_n, (int)total);
     else
-        hipLaunchKernelGGL((gemm_nt_kernel<T, false>), grid, dim3(T::kThreads), 0, stream, (const bf16_t *)g.A, g.lda,
+        hipLaunchKernelGGL((gemm_nt_kernel<T, false, F16>), grid, dim3(T::kThreads), 0, stream, (const bf16_t *)g.A, g.lda,
                            g.M, g.a_bytes, (const bf16_t *)g.B, g.ldb, g.N, g.b_bytes, g.Kd, kps, g.C, g.ldc, nt_m,
                            nt_n, (int)total);
     return hipGetLastError();
@@ -277,8 +301,9 @@ hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     // the large tile when both output dimensions fill it
-    if (g.M >= 256 && g.N >= 256) return launch_gemm_tiles<GLarge>(g, stream);
-    return launch_gemm_tiles<GSmall>(g, stream);
+    const bool large = g.M >= 256 && g.N >= 256;
+    if (g.f16) return large ? launch_gemm_tiles<GLarge, true>(g, stream) : launch_gemm_tiles<GSmall, true>(g, stream);
+    return large ? launch_gemm_tiles<GLarge, false>(g, stream) : launch_gemm_tiles<GSmall, false>(g, stream);
 }
 
 hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream)
@@ -289,13 +314,17 @@ hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0,
+hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0, bool f16,
                                   hipStream_t stream)
 {
     const int64_t n = (int64_t)Co * Mc;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, P, Z, Co, Mc,
-                       (bf16_t *)dW, ldw, col0);
+    if (f16)
+        hipLaunchKernelGGL(reduce_partials_kernel<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, P, Z,
+                           Co, Mc, (bf16_t *)dW, ldw, col0);
+    else
+        hipLaunchKernelGGL(reduce_partials_kernel<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, P, Z,
+                           Co, Mc, (bf16_t *)dW, ldw, col0);
     return hipGetLastError();
 }
 

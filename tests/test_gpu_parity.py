@@ -294,7 +294,7 @@ def test_error_paths_leave_outputs_untouched():
     host = torch.full((1, 2, psi.K, psi.Ho, psi.Wo), sentinel)
     st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(host)), None)
     assert st == "DISCO_ERR_INVALID_ARGUMENT" and "device memory" in msg
-    Wf = torch.zeros((3, 2, psi.K), device=DEV)
+    Wf = torch.zeros((3, 2, psi.K), device=DEV, dtype=torch.bfloat16)  # dtypes of one call differ
     yf = torch.full((1, 3, psi.Ho, psi.Wo), sentinel, device=DEV)
     st, msg = _raw("disco_fused_conv", h.handle, ctypes.byref(sgc.tensor_desc(x)), ctypes.byref(sgc.tensor_desc(Wf)),
                    ctypes.byref(sgc.tensor_desc(yf)), None)
@@ -389,13 +389,14 @@ def test_bwd_bf16_both_kernels_agree_with_oracle(geom, mfma, monkeypatch):
 
 # ---------------------------------------------------------------- backward of the fused convolution
 
-def _fused_bwd_check(psi, B, C, Co, seed):
+def _fused_bwd_check(psi, B, C, Co, seed, dtype="bf16"):
     h = gpu_psi(psi)
-    x = randn((B, C, psi.Hi, psi.Wi), seed, "bf16")
-    W = randn((Co, C, psi.K), seed + 1, "bf16", std=1.0 / np.sqrt(C * psi.K))
-    gy = randn((B, Co, psi.Ho, psi.Wo), seed + 2, "bf16")
-    gx = nan_like((B, C, psi.Hi, psi.Wi), torch.bfloat16)
-    dW = nan_like((Co, C, psi.K), torch.bfloat16)
+    x = randn((B, C, psi.Hi, psi.Wi), seed, dtype)
+    W = randn((Co, C, psi.K), seed + 1, dtype, std=1.0 / np.sqrt(C * psi.K))
+    gy = randn((B, Co, psi.Ho, psi.Wo), seed + 2, dtype)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    gx = nan_like((B, C, psi.Hi, psi.Wi), tdt)
+    dW = nan_like((Co, C, psi.K), tdt)
     sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV), gx, dW)
     torch.cuda.synchronize()
     rgx, rdW = oracle.fused_bwd(psi, x, W, gy)
@@ -696,16 +697,23 @@ def test_one_handle_from_two_streams():
     x = randn((2, 8, 31, 64), 3600, "bf16").to(DEV)
     g = randn((2, 8, psi.K, 31, 64), 3601, "bf16").to(DEV)
     W = randn((16, 8, psi.K), 3602, "bf16", std=0.1).to(DEV)
-    ref = (sgc.disco_fwd(h, x), sgc.disco_bwd(h, g), sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g))
+    gy = randn((2, 16, 31, 64), 3603, "bf16").to(DEV)
+    _, kept = sgc.disco_fused_conv_save(h, x, W)
+    ref = (sgc.disco_fwd(h, x), sgc.disco_bwd(h, g), sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g),
+           *sgc.disco_fused_conv_bwd_saved(h, kept, W, gy))
     torch.cuda.synchronize()
     sa, sb = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)  # default priority
     outs = []
     for _ in range(3):
+        # the saved backward forks onto the library's side stream on both caller streams at once
         with torch.cuda.stream(sa):
             o, gx = sgc.disco_fwd(h, x), sgc.disco_bwd(h, g)
+            sgx_a, sdw_a = sgc.disco_fused_conv_bwd_saved(h, kept, W, gy)
         with torch.cuda.stream(sb):
             y, ye = sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g)
-        outs.append((o, gx, y, ye))
+            sgx_b, sdw_b = sgc.disco_fused_conv_bwd_saved(h, kept, W, gy)
+        outs.append((o, gx, y, ye, sgx_a, sdw_a))
+        outs.append((o, gx, y, ye, sgx_b, sdw_b))
     torch.cuda.synchronize()
     for got in outs:
         for a, b in zip(got, ref):
@@ -815,3 +823,175 @@ def test_fused_save_f16():
     torch.cuda.synchronize()
     assert torch.equal(y, y0)
     assert normalised_error(out.cpu(), oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL_F16
+
+
+# ---------------------------------------------------------------- fp32 fused convolution, fp16 fused backward
+# The fp32 fused convolution keeps every step in fp32 (fp32 psi, fp32 contraction chunk, fp32
+# matrix-core einsum): the fp32 variant each precision is compared with (bar 1e-5).  The fused
+# backward with fp16 data: g = W^T gy, the transpose contraction, the recomputed contraction and dW
+# all in fp16 data with fp32 accumulation (bar: the fp16 one).
+
+FUSED_F32_CFGS = [
+    # (Hi, Wi, Ho, Wo, theta_c, n_r, n_a, B, C, Co)
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 8, 32),      # K=16, p=1, two channel chunks of 4
+    (31, 60, 16, 30, 0.6, 3, 1, 1, 23, 20),     # K=3: chunks of 21 + 2 channels, ragged longitude tile
+    (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 300),    # K=8, p=2, Co above one block of 256
+    (31, 64, 31, 64, 1.5, 4, 4, 1, 6, 33),      # caps spanning whole rings
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED_F32_CFGS)
+def test_fused_f32_agrees_with_oracle(cfg):
+    Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
+    _log(f"fused fp32 {cfg}")
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
+    h = gpu_psi(psi)
+    x = randn((B, C, Hi, Wi), 4100 + C)
+    W = randn((Co, C, psi.K), 4101 + C, std=1.0 / np.sqrt(C * psi.K))
+    y = nan_like((B, Co, Ho, Wo), torch.float32)
+    sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV), y)
+    torch.cuda.synchronize()
+    ref = oracle.fused(psi, x, W)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)
+    assert normalised_error(y, ref, nrm) <= TOL["f32"]
+
+
+def test_fused_f32_721x1440_sampled():
+    """The 721x1440 K=16 filter of the fused workload with fp32 data (4 input, 8 output channels):
+    latitudes from pole to pole checked against the oracle."""
+    w = WORKLOADS["fused_bf16_721x1440"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = randn((1, 4, psi.Hi, psi.Wi), 4200)
+    W = randn((8, 4, psi.K), 4201, std=1.0 / np.sqrt(4 * psi.K))
+    _log("fused fp32 721x1440: GPU")
+    y = nan_like((1, 8, psi.Ho, psi.Wo), torch.float32)
+    sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV), y)
+    torch.cuda.synchronize()
+    hos = [0, 1, 2, 180, 360, 540, 718, 719, 720]
+    _log("fused fp32 721x1440: oracle")
+    ref = oracle.fused(psi, x, W, ho_list=hos)
+    nrm = oracle.fused(psi, x.abs(), W.abs(), ho_list=hos, abs_mode=True)
+    assert normalised_error(y[:, :, hos], ref, nrm) <= TOL["f32"]
+
+
+def test_fused_f32_save():
+    """fp32 data: the saving fused op's y equals the fused op's bitwise, and its kept contraction is
+    the fp32 forward (the fused kernel's contraction and the forward sum in different orders)."""
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    h = gpu_psi(psi)
+    x = randn((1, 5, psi.Hi, psi.Wi), 4300)
+    W = randn((7, 5, psi.K), 4301, std=0.1)
+    y0 = sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV))
+    y, out = sgc.disco_fused_conv_save(h, x.to(DEV), W.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("cfg", [
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 20, 24),     # K=16, s=1: two channel chunks (16 + 4)
+    (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 40),     # K=8, s=2
+    (16, 32, 16, 32, 2 * np.pi / 16, 3, 1, 3, 5, 136),  # K=3, B=3, Co above one tile
+])
+def test_fused_bwd_f16_small_ragged(cfg):
+    Hi, Wi, Ho, Wo, tc, nr, na, B, C, Co = cfg
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
+    _log(f"fused bwd fp16 {cfg}")
+    egx, edW, (gx, dW) = _fused_bwd_check(psi, B, C, Co, 4400 + C, "f16")
+    assert egx <= TOL_F16, egx
+    assert edW <= TOL_F16, edW
+    # the training path that keeps the contraction reproduces it bitwise
+    x = randn((B, C, psi.Hi, psi.Wi), 4400 + C, "f16").to(DEV)
+    W = randn((Co, C, psi.K), 4401 + C, "f16", std=1.0 / np.sqrt(C * psi.K)).to(DEV)
+    gy = randn((B, Co, psi.Ho, psi.Wo), 4402 + C, "f16").to(DEV)
+    h = gpu_psi(psi)
+    _, out = sgc.disco_fused_conv_save(h, x, W)
+    gxs, dWs = sgc.disco_fused_conv_bwd_saved(h, out, W, gy)
+    torch.cuda.synchronize()
+    assert torch.equal(gxs, gx) and torch.equal(dWs, dW)
+
+
+def test_fused_bwd_f16_721x1440_sampled():
+    """The fused workload's backward with fp16 data (B=2, C=Co=256 at 721x1440, K=16): one channel's
+    input-gradient planes and weight-gradient column against the oracle."""
+    w = WORKLOADS["fused_bf16_721x1440"]
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = randn((w.B, w.C, w.Hi, w.Wi), 4500, "f16")
+    W = randn((w.Co, w.C, w.K), 4501, "f16", std=1.0 / np.sqrt(w.C * w.K))
+    gy = randn((w.B, w.Co, psi.Ho, psi.Wo), 4502, "f16")
+    _log("fused bwd fp16 721x1440: GPU")
+    gx, dW = sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV))
+    torch.cuda.synchronize()
+    gx, dW = gx.cpu(), dW.cpu()
+    gy64 = gy.double().numpy().reshape(w.B, w.Co, -1)
+    W64 = W.double().numpy()
+    c = 77
+    _log(f"fused bwd fp16 721x1440: oracle channel {c}")
+    for b in range(w.B):
+        g = (W64[:, c, :].T @ gy64[b]).reshape(1, psi.K, psi.Ho, psi.Wo)
+        ga = (np.abs(W64[:, c, :]).T @ np.abs(gy64[b])).reshape(1, psi.K, psi.Ho, psi.Wo)
+        ref = oracle.bwd(psi, g.astype(np.float32))
+        nrm = oracle.bwd(psi, ga.astype(np.float32), abs_mode=True)
+        assert normalised_error(gx[b, c][None], ref, nrm) <= TOL_F16
+    out = np.stack([oracle.fwd(psi, x[b, c][None])[0].reshape(psi.K, -1) for b in range(w.B)])
+    outa = np.stack([oracle.fwd(psi, x[b, c][None].abs(), abs_mode=True)[0].reshape(psi.K, -1) for b in range(w.B)])
+    ref = sum(gy64[b] @ out[b].T for b in range(w.B))
+    nrm = sum(np.abs(gy64[b]) @ outa[b].T for b in range(w.B))
+    assert normalised_error(dW[:, c, :], ref, nrm) <= TOL_F16
+
+
+def test_fused_save_more_than_256_output_channels():
+    """Co = 512 (two output-channel blocks per latitude span, one of which writes the kept
+    contraction): y and the saved backward equal the plain and recomputing calls bitwise."""
+    psi = build_psi(24, 64, 24, 64, 0.4, 3, 3)  # K = 9, the page's stand-in basis shape
+    h = gpu_psi(psi)
+    x = randn((1, 16, psi.Hi, psi.Wi), 4600, "bf16").to(DEV)
+    W = randn((512, 16, psi.K), 4601, "bf16", std=1.0 / np.sqrt(16 * psi.K)).to(DEV)
+    gy = randn((1, 512, psi.Ho, psi.Wo), 4602, "bf16").to(DEV)
+    y0 = sgc.disco_fused_conv(h, x, W)
+    y, out = sgc.disco_fused_conv_save(h, x, W)
+    gx0, dW0 = sgc.disco_fused_conv_bwd(h, x, W, gy)
+    gx, dW = sgc.disco_fused_conv_bwd_saved(h, out, W, gy)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(gx, gx0) and torch.equal(dW, dW0)
+
+
+def test_outputs_overlapping_inputs_are_refused():
+    """Outputs that share bytes with an input are refused (DISCO_ERR_INVALID_ARGUMENT) before
+    anything is enqueued, and nothing is written."""
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    h = gpu_psi(psi)
+    nx = 2 * 4 * 31 * 64
+    buf = torch.full((4 * nx,), 5.0, dtype=torch.bfloat16, device=DEV)
+    x = buf[:nx].view(2, 4, 31, 64)
+    W = randn((8, 4, psi.K), 4700, "bf16", std=0.1).to(DEV)
+    big = torch.full((2 * 4 * psi.K * 31 * 64 + nx,), 5.0, dtype=torch.bfloat16, device=DEV)
+    xb = big[:nx].view(2, 4, 31, 64)
+    xb.copy_(x)
+    out_over_x = big[nx // 2: nx // 2 + 2 * 4 * psi.K * 31 * 64].view(2, 4, psi.K, 31, 64)
+    st, msg = _raw("disco_fwd", h.handle, ctypes.byref(sgc.tensor_desc(xb)), ctypes.byref(sgc.tensor_desc(out_over_x)),
+                   None)
+    assert st == "DISCO_ERR_INVALID_ARGUMENT" and "overlaps" in msg
+    # the saving fused op: out overlapping y
+    ybuf = torch.full((2 * 8 * 31 * 64 + 2 * 4 * psi.K * 31 * 64,), 5.0, dtype=torch.bfloat16, device=DEV)
+    y = ybuf[: 2 * 8 * 31 * 64].view(2, 8, 31, 64)
+    out_over_y = ybuf[8: 8 + 2 * 4 * psi.K * 31 * 64].view(2, 4, psi.K, 31, 64)
+    st, msg = _raw("disco_fused_conv_save", h.handle, ctypes.byref(sgc.tensor_desc(x)),
+                   ctypes.byref(sgc.tensor_desc(W)), ctypes.byref(sgc.tensor_desc(y)),
+                   ctypes.byref(sgc.tensor_desc(out_over_y)), None)
+    assert st == "DISCO_ERR_INVALID_ARGUMENT" and "overlaps" in msg
+    # the fused backward: gx overlapping gy
+    gbuf = torch.full((2 * 8 * 31 * 64 + nx,), 5.0, dtype=torch.bfloat16, device=DEV)
+    gy = gbuf[: 2 * 8 * 31 * 64].view(2, 8, 31, 64)
+    gx_over_gy = gbuf[64: 64 + nx].view(2, 4, 31, 64)
+    dW = torch.full((8, 4, psi.K), 5.0, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(sgc.disco_fused_conv_bwd_workspace(h, 2, 4, 8), dtype=torch.uint8, device=DEV)
+    lib = sgc.load_library()
+    stc = lib.disco_fused_conv_bwd(h.handle, *[ctypes.byref(sgc.tensor_desc(t)) for t in (x, W, gy, gx_over_gy, dW)],
+                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert sgc.STATUS_NAMES[stc] == "DISCO_ERR_INVALID_ARGUMENT" and "overlaps" in lib.disco_last_error().decode()
+    torch.cuda.synchronize()
+    assert bool((big[nx:] == 5.0).all()) and bool((ybuf == 5.0).all()) and bool((gbuf == 5.0).all())
+    assert bool((dW == 5.0).all())
