@@ -29,6 +29,11 @@
 // and x windows stream into LDS by direct global->LDS loads while the
 // current step is contracted; the chunk's W slice likewise.  No atomics;
 // every output is written once.
+#include <cstdlib>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan_fused.hpp"
@@ -789,6 +794,45 @@ int fused_mfma_channels_per_chunk() { return kCh; }
 
 int fwd_mfma_channels(int kr) { return kr == 8 ? 8 : 4; }
 
+namespace {
+
+// Allow kernel `fn` `lds` bytes of dynamic LDS on the current device.  The request is checked on the
+// host against the device's per-workgroup LDS (an oversized request returns hipErrorInvalidValue and
+// nothing is launched), and hipFuncSetAttribute runs only when a kernel needs more than it was last
+// given on that device (once per kernel and device in steady state).  DISCO_TEST_LDS_EXTRA (a test
+// knob) adds bytes to every request, so tests can make a launch exceed the device and see the refusal.
+hipError_t allow_lds(const void *fn, size_t lds)
+{
+    if (const char *x = getenv("DISCO_TEST_LDS_EXTRA")) lds += (size_t)std::max(0L, atol(x));
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::vector<int> dev_max(64, -1);
+    static std::vector<std::pair<std::pair<const void *, int>, size_t>> granted;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (dev_max[dev] < 0) {
+        int v = 0;
+        if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return e;
+        dev_max[dev] = v;
+    }
+    if (lds > (size_t)dev_max[dev]) return hipErrorInvalidValue;
+    for (auto &g : granted)
+        if (g.first.first == fn && g.first.second == dev) {
+            if (lds <= g.second) return hipSuccess;
+            if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+                return e;
+            g.second = lds;
+            return hipSuccess;
+        }
+    if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) return e;
+    granted.push_back({{fn, dev}, lds});
+    return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
 {
     if (a.B == 0 || a.C == 0) return hipSuccess;
@@ -799,7 +843,7 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
     const size_t lds = std::max<size_t>(2 * (size_t)buf_bytes, 32768);  // stage buffers; the epilogue's tile
     const void *fn = a.kr == 8 ? (a.f16 ? (const void *)fwd_mfma_kernel<8, true> : (const void *)fwd_mfma_kernel<8, false>)
                                : (a.f16 ? (const void *)fwd_mfma_kernel<16, true> : (const void *)fwd_mfma_kernel<16, false>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_lds(fn, lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_cb * n_pxb;
     const int64_t x_bs = a.x_bstride > 0 ? a.x_bstride : (int64_t)a.C * a.Hi * a.Wi;
@@ -832,7 +876,7 @@ hipError_t launch_fused_contract(const FusedContractLaunch &a, hipStream_t strea
     const int buf_bytes = std::max((a.max_piece_bytes + 15) & ~15, kXchBytes);
     const size_t lds = fused_mfma_lds_bytes(kMaxOt, a.max_piece_bytes, a.max_resident_bytes);  // 32 KiB output tile
     const void *fn = a.f16 ? (const void *)fused_mfma_kernel<2, true, false> : (const void *)fused_mfma_kernel<2, false, false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_lds(fn, lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_pxb;
     const int64_t x_bs = a.x_bstride > 0 ? a.x_bstride : (int64_t)a.C * a.Hi * a.Wi;
@@ -877,7 +921,7 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const void *fn = a.f16 ? (n_ot == 2 ? DISCO_FUSED_FN(2, true) : n_ot == 4 ? DISCO_FUSED_FN(4, true) : DISCO_FUSED_FN(8, true))
                            : (n_ot == 2 ? DISCO_FUSED_FN(2, false) : n_ot == 4 ? DISCO_FUSED_FN(4, false) : DISCO_FUSED_FN(8, false));
 #undef DISCO_FUSED_FN
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_lds(fn, lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pxb;
     // direct loads need 16-byte aligned runs and buffer offsets below 2^31
@@ -1175,7 +1219,7 @@ hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream)
                            : (n_ot == 2   ? (const void *)einsum_mfma_kernel<2, false>
                               : n_ot == 4 ? (const void *)einsum_mfma_kernel<4, false>
                                           : (const void *)einsum_mfma_kernel<8, false>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_lds(fn, lds);
     if (e != hipSuccess) return e;
     const int64_t nblk = (int64_t)a.B * n_ob * n_pt;
     // direct loads: 16-byte aligned runs, and one chunk's channels addressable with 32-bit offsets

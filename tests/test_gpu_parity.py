@@ -995,3 +995,31 @@ def test_outputs_overlapping_inputs_are_refused():
     torch.cuda.synchronize()
     assert bool((big[nx:] == 5.0).all()) and bool((ybuf == 5.0).all()) and bool((gbuf == 5.0).all())
     assert bool((dW == 5.0).all())
+
+
+def test_oversized_launch_is_refused_and_writes_nothing(monkeypatch):
+    """A launch whose LDS request exceeds the device's per-workgroup LDS is refused on the host
+    (DISCO_ERR_HIP) before anything is dispatched, and its output is untouched; the next call with a
+    fitting request runs normally.  DISCO_TEST_LDS_EXTRA inflates the request of the matrix-core
+    kernels by 1 MiB."""
+    psi = build_psi(19, 144, 19, 72, 0.7, 4, 2)  # a shape both matrix-core kernels cover
+    h = gpu_psi(psi)
+    x = randn((2, 5, 19, 144), 4800, "bf16").to(DEV)
+    W = randn((40, 5, psi.K), 4801, "bf16", std=0.2).to(DEV)
+    ref_y = sgc.disco_fused_conv(h, x, W)
+    ref_o = sgc.disco_fwd(h, x)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("DISCO_TEST_LDS_EXTRA", str(1 << 20))
+    y = nan_like((2, 40, 19, 72), torch.bfloat16)
+    o = nan_like((2, 5, psi.K, 19, 72), torch.bfloat16)
+    for call in (lambda: sgc.disco_fused_conv(h, x, W, y), lambda: sgc.disco_fwd(h, x, o)):
+        with pytest.raises(sgc.DiscoError) as ei:
+            call()
+        assert ei.value.status_name == "DISCO_ERR_HIP"
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(y).all()) and bool(torch.isnan(o).all())
+    monkeypatch.delenv("DISCO_TEST_LDS_EXTRA")
+    sgc.disco_fused_conv(h, x, W, y)
+    sgc.disco_fwd(h, x, o)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref_y) and torch.equal(o, ref_o)
