@@ -6,7 +6,12 @@
 //   * copy: the same stream written to a second buffer (read + write bytes);
 //   * fp32 FMA loop: eight independent v_fmac_f32 chains per lane (packed fp32 ops are disabled
 //     in this build, as in the library);
-//   * bf16 MFMA loop: four independent v_mfma_f32_32x32x16_bf16 accumulators per wave.
+//   * bf16 MFMA loop: four independent v_mfma_f32_32x32x16_bf16 accumulators per wave;
+//   * LDS read loop: 4-, 8- or 16-byte LDS reads per lane over a 64 KiB array, consecutive lanes
+//     on consecutive words (no bank conflicts), eight waves per workgroup, one workgroup per CU;
+//   * LDS-fed MFMA loop: per step two 16-byte reads and `nb32` 4-byte reads per lane feeding two
+//     v_mfma_f32_32x32x16_bf16 (the operand traffic of a contraction block of the fused kernel:
+//     one psi operand in 4-byte words, the x runs of two channels), loads issued one step ahead.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -15,6 +20,9 @@ hipError_t disco_probe_read(const void *buf, size_t bytes, float *out, int block
 hipError_t disco_probe_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream);
 hipError_t disco_probe_fma(int iters, float *out, int blocks, void *stream);
 hipError_t disco_probe_mfma(int iters, float *out, int blocks, void *stream);
+hipError_t disco_probe_lds(int iters, int width, float *out, int blocks, void *stream);
+hipError_t disco_probe_lds_mfma(int iters, int nb32, float *out, int blocks, void *stream);
+hipError_t disco_probe_lds_mfma_q(int iters, int p, int q, int depth, int threads, float *out, int blocks, void *stream);
 }
 
 namespace {
@@ -97,6 +105,136 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float *out)
     out[blockIdx.x * kThreads + threadIdx.x] = t;
 }
 
+constexpr int kLdsThreads = 512;
+constexpr int kLdsBytes = 65536;
+
+// Fills the array with lane-dependent words; every later read address is masked into it.
+__device__ __forceinline__ void fill_lds(uint32_t *lds)
+{
+    for (int i = threadIdx.x; i < kLdsBytes / 4; i += kLdsThreads) lds[i] = 0x9e3779b9u * (uint32_t)(i + 1);
+    __syncthreads();
+}
+
+template <int W>
+__global__ __launch_bounds__(kLdsThreads) void lds_kernel(int iters, float *out)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
+    fill_lds(lds);
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(lds);
+    const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) * W + (uint32_t)(threadIdx.x >> 6) * 4096u;
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t off = (lane_off + (uint32_t)(8 * it + u) * 64u * W) & (kLdsBytes - 1);
+            if constexpr (W == 16) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(base + off);
+                acc ^= v.x ^ v.y ^ v.z ^ v.w;
+            } else if constexpr (W == 8) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(base + off);
+                acc ^= v.x ^ v.y;
+            } else {
+                acc ^= *reinterpret_cast<const uint32_t *>(base + off);
+            }
+        }
+    }
+    out[blockIdx.x * kLdsThreads + threadIdx.x] = (float)acc;
+}
+
+template <int NB32>
+__global__ __launch_bounds__(kLdsThreads) void lds_mfma_kernel(int iters, float *out)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
+    fill_lds(lds);
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(lds);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // x runs: 16 bytes per lane, consecutive lanes 16 bytes apart; psi words: 4 bytes per lane,
+    // consecutive lanes 4 bytes apart, NB32 words 256 bytes apart
+    const uint32_t xo = (uint32_t)lane * 16u + (uint32_t)wave * 2048u, ao = 32768u + (uint32_t)lane * 4u + (uint32_t)wave * 1024u;
+    f32x16 d0 = {}, d1 = {};
+    auto ld = [&](int it, bf16x8 &b0, bf16x8 &b1, uint32_t (&a)[NB32]) {
+        const uint32_t step = (uint32_t)(it & 7) * 1024u;
+        b0 = *reinterpret_cast<const bf16x8 *>(base + ((xo + step) & 32767u));
+        b1 = *reinterpret_cast<const bf16x8 *>(base + ((xo + step + 16384u) & 32767u));
+#pragma unroll
+        for (int i = 0; i < NB32; ++i)
+            a[i] = *reinterpret_cast<const uint32_t *>(base + (32768u | ((ao + step + 256u * i) & 32767u)));
+    };
+    bf16x8 b0, b1, nb0, nb1;
+    uint32_t a[NB32], na[NB32];
+    ld(0, b0, b1, a);
+    for (int it = 0; it < iters; ++it) {
+        ld(it + 1, nb0, nb1, na);
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = NB32 > 4 ? __builtin_amdgcn_perm(a[(i + 1) % NB32], a[i], 0x05040302u) : a[i];
+        const bf16x8 av = __builtin_bit_cast(bf16x8, w);
+        d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, d1, 0, 0, 0);
+        b0 = nb0;
+        b1 = nb1;
+#pragma unroll
+        for (int i = 0; i < NB32; ++i) a[i] = na[i];
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += d0[k] + d1[k];
+    out[blockIdx.x * kLdsThreads + threadIdx.x] = t;
+}
+
+// P psi operands (phase pairs) x Q x operands (channels): per step 4P four-byte psi reads and Q
+// 16-byte x reads per lane feed P Q MFMAs; operands are loaded DEPTH steps ahead.  TH threads per
+// workgroup.
+template <int P, int Q, int DEPTH, int TH>
+__global__ __launch_bounds__(TH) void lds_mfma_q_kernel(int iters, float *out)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsBytes / 4];
+    for (int i = threadIdx.x; i < kLdsBytes / 4; i += TH) lds[i] = 0x9e3779b9u * (uint32_t)(i + 1);
+    __syncthreads();
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(lds);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t xo = (uint32_t)lane * 16u + (uint32_t)wave * 2048u, ao = (uint32_t)lane * 4u + (uint32_t)wave * 1024u;
+    f32x16 d[P][Q];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int c = 0; c < Q; ++c) d[p][c] = f32x16{};
+    bf16x8 b[DEPTH][Q];
+    uint32_t a[DEPTH][P][4];
+    auto ld = [&](int it, bf16x8 (&bb)[Q], uint32_t (&aa)[P][4]) {
+        const uint32_t step = (uint32_t)(it & 7) * 1024u;
+#pragma unroll
+        for (int c = 0; c < Q; ++c) bb[c] = *reinterpret_cast<const bf16x8 *>(base + ((xo + step + 4096u * c) & 32767u));
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                aa[p][i] = *reinterpret_cast<const uint32_t *>(base + (32768u | ((ao + step + 256u * i + 4096u * p) & 32767u)));
+    };
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) ld(j, b[j], a[j]);
+    for (int it = 0; it < iters; it += DEPTH) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a[j][p]);
+#pragma unroll
+                for (int c = 0; c < Q; ++c) d[p][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[j][c], d[p][c], 0, 0, 0);
+            }
+            ld(it + j + DEPTH, b[j], a[j]);
+        }
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int c = 0; c < Q; ++c)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) t += d[p][c][k];
+    out[blockIdx.x * TH + threadIdx.x] = t;
+}
+
 }  // namespace
 
 // bytes must be a multiple of 16 and the buffers 16-byte aligned (the caller passes torch tensors
@@ -130,4 +268,47 @@ hipError_t disco_probe_mfma(int iters, float *out, int blocks, void *stream)
     if (iters <= 0 || blocks <= 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, iters, out);
     return hipGetLastError();
+}
+
+// width: 4, 8 or 16 bytes per lane per read; out holds blocks * 512 floats.  Each workgroup
+// performs iters * 8 reads per lane.
+hipError_t disco_probe_lds(int iters, int width, float *out, int blocks, void *stream)
+{
+    if (iters <= 0 || blocks <= 0) return hipErrorInvalidValue;
+    const hipStream_t st = (hipStream_t)stream;
+    if (width == 4) hipLaunchKernelGGL(lds_kernel<4>, dim3(blocks), dim3(kLdsThreads), 0, st, iters, out);
+    else if (width == 8) hipLaunchKernelGGL(lds_kernel<8>, dim3(blocks), dim3(kLdsThreads), 0, st, iters, out);
+    else if (width == 16) hipLaunchKernelGGL(lds_kernel<16>, dim3(blocks), dim3(kLdsThreads), 0, st, iters, out);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// nb32: 4 (aligned psi words) or 5 (realigned); two MFMAs per iteration per wave; out holds
+// blocks * 512 floats.
+hipError_t disco_probe_lds_mfma(int iters, int nb32, float *out, int blocks, void *stream)
+{
+    if (iters <= 0 || blocks <= 0) return hipErrorInvalidValue;
+    const hipStream_t st = (hipStream_t)stream;
+    if (nb32 == 4) hipLaunchKernelGGL(lds_mfma_kernel<4>, dim3(blocks), dim3(kLdsThreads), 0, st, iters, out);
+    else if (nb32 == 5) hipLaunchKernelGGL(lds_mfma_kernel<5>, dim3(blocks), dim3(kLdsThreads), 0, st, iters, out);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// p psi operands x q channels per step (see the kernel), prefetch depth, threads 256 or 512; iters a
+// multiple of depth; p q MFMAs per iteration per wave; out holds blocks * threads floats.
+hipError_t disco_probe_lds_mfma_q(int iters, int p, int q, int depth, int threads, float *out, int blocks, void *stream)
+{
+    if (iters <= 0 || blocks <= 0 || depth <= 0 || iters % depth != 0) return hipErrorInvalidValue;
+    const hipStream_t st = (hipStream_t)stream;
+#define PROBE_Q(PP, QQ, DD, TT)                                                                                  \
+    if (p == PP && q == QQ && depth == DD && threads == TT) {                                                    \
+        hipLaunchKernelGGL((lds_mfma_q_kernel<PP, QQ, DD, TT>), dim3(blocks), dim3(TT), 0, st, iters, out);      \
+        return hipGetLastError();                                                                                \
+    }
+    PROBE_Q(1, 2, 2, 512) PROBE_Q(1, 4, 2, 512) PROBE_Q(2, 2, 2, 512) PROBE_Q(2, 1, 2, 512)
+    PROBE_Q(1, 4, 2, 256) PROBE_Q(2, 2, 2, 256) PROBE_Q(2, 4, 2, 256) PROBE_Q(4, 2, 2, 256) PROBE_Q(4, 4, 2, 256)
+    PROBE_Q(2, 4, 1, 256) PROBE_Q(4, 1, 2, 256) PROBE_Q(4, 1, 2, 512)
+#undef PROBE_Q
+    return hipErrorInvalidValue;
 }
