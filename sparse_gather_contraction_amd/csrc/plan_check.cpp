@@ -4,22 +4,29 @@
 // For one CSR read from a file it builds every plan disco_psi_create builds and checks
 //   * that every index a kernel derives from a plan stays inside the buffer it addresses
 //     (segments, records and stages of the plain, staged and tiled gathers, LDS reads and
-//     writes, output offsets), and
-//   * that the gather plans reproduce the contraction: each kernel's loop structure is
-//     replayed on the CPU in fp64 and compared with the CSR definition, and every
-//     destination element is written by exactly one item.
+//     writes, output offsets; descriptors, psi words and window runs of the phase-split
+//     matrix-core plans), and
+//   * that the plans reproduce the contraction: each kernel's loop structure is replayed on
+//     the CPU in fp64 and compared with the CSR definition (for the matrix-core plans: every
+//     lane's operands of every v_mfma_f32_32x32x16 block, summed as the instruction does, with
+//     psi rounded to bf16 as the plan stores it), every destination element of the gathers is
+//     written by exactly one item, and the row-inverted CSR of the matrix-core backward
+//     reproduces the backward.
 // Usage: plan_check <csr file>; exit status 0 when every check passes.
 // File layout (little endian): int32 K, Ho, Wo, Hi, Wi; int64 nnz; int64 row_ptr[K Ho + 1];
 // int32 col_hi[nnz]; int32 col_wi[nnz]; float val[nnz].
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <random>
 #include <string>
 #include <vector>
 
 #include "plan.hpp"
+#include "plan_fused.hpp"
 #include "plan_tile.hpp"
 
 using namespace disco;
@@ -349,6 +356,249 @@ void check_tile_grid(const TilePlan &tp, int BC)
     }
 }
 
+
+
+// ---- phase-split plans of the matrix-core kernels (kernels_fused_mfma.hip) -------------------
+
+float bf16_value(uint16_t h)
+{
+    const uint32_t u = (uint32_t)h << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// round to nearest even, written here from the bf16 format (8 exponent bits, 7 fraction bits)
+float round_bf16(float f)
+{
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return f;  // NaN stays NaN
+    const uint32_t lsb = (u >> 16) & 1u;
+    u = (u + 0x7fffu + lsb) & 0xffff0000u;
+    float r;
+    std::memcpy(&r, &u, 4);
+    return r;
+}
+
+// CSR definition at one output element with bf16 psi: sum over row (k, ho) of psi * src[hi, (wi + s wo) mod Wi]
+double ref_at(const CSRView &c, const std::vector<double> &src, int k, int ho, int wo)
+{
+    const int s = c.Wi / c.Wo;
+    const int64_t r = (int64_t)k * c.Ho + ho;
+    double acc = 0.0;
+    for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e)
+        acc += (double)round_bf16(c.val[e]) * src[(size_t)c.col_hi[e] * c.Wi + (c.col_wi[e] + (int64_t)s * wo) % c.Wi];
+    return acc;
+}
+
+struct PhaseBudget {
+    int kr, ch;
+    int64_t piece_budget;  // bytes of one streamed stage
+    bool resident;         // resident latitudes allowed
+    int xch_bytes;         // smallest window buffer of a resident latitude
+};
+
+// Replays the matrix-core contraction of plan p over CSR c (source plane src = c.Hi rows of c.Wi):
+// for every latitude and the checked longitude spans, the piece stages are built as the kernels
+// build them (descriptors and psi copied from the plan, window rows from the source plane, the
+// rest of the window area left as NaN), every lane of every block reads its psi words (four, or
+// five realigned) and its x runs with the kernels' lane offsets (A row r of phase group g:
+// phase q, basis k; B column n), and the 16-offset products are summed in fp64.  Rows k >= K and
+// longitudes past Wo are computed and must stay finite; the others must match the definition.
+void check_phase(const CSRView &c, const FusedPlan &p, const PhaseBudget &bu, const std::vector<double> &src,
+                 const std::string &what)
+{
+    if (!p.ok) return;
+    const int s = c.Wi / c.Wo, kr = bu.kr;
+    check(p.s == s && p.kr == kr && p.ch == bu.ch, what + ": plan parameters");
+    check((int)p.ho_piece.size() == c.Ho + 1 && p.ho_piece[0] == 0 && p.ho_piece.back() == (int32_t)p.pieces.size(),
+          what + ": latitude piece table");
+    if ((int)p.ho_piece.size() != c.Ho + 1) return;
+    std::vector<int> seen(c.Ho, 0);
+    check((int)p.ho_order.size() == c.Ho, what + ": latitude order size");
+    for (int32_t h : p.ho_order) {
+        check(h >= 0 && h < c.Ho, what + ": latitude order entry");
+        if (h >= 0 && h < c.Ho) ++seen[h];
+    }
+    for (int h = 0; h < c.Ho; ++h) check(seen[h] == 1, what + ": latitude order is not a permutation");
+    check(p.adata.size() == p.adata16.size(), what + ": fp16 psi size");
+    // structure of every piece
+    for (size_t i = 0; i < p.pieces.size(); ++i) {
+        const FPiece &pc = p.pieces[i];
+        const std::string pw = what + ": piece " + std::to_string(i);
+        check(pc.nblk >= 0 && pc.nblk % 2 == 0 && pc.desc_words == 2 * pc.nblk && pc.desc_words % 4 == 0,
+              pw + " block count / descriptor words");
+        check(pc.desc_begin >= 0 && 2 * ((int64_t)pc.desc_begin + pc.nblk) <= (int64_t)p.descs.size() &&
+                  (2 * (int64_t)pc.desc_begin) % 4 == 0,
+              pw + " descriptors outside the table or not 16-byte aligned");
+        check(pc.a_begin >= 0 && pc.a_begin % 8 == 0 && pc.a_elems >= 0 && pc.a_elems % 8 == 0 &&
+                  (int64_t)pc.a_begin + pc.a_elems <= (int64_t)p.adata.size(),
+              pw + " psi range outside the table or not 16-byte units");
+        check(pc.row_begin >= 0 && pc.row_begin <= pc.row_end && pc.row_end <= (int32_t)p.rows.size(), pw + " rows");
+        check(pc.win_elems >= 0 && pc.win_elems % 8 == 0 && pc.win_elems <= p.max_win, pw + " window area");
+        check(pc.a_copy_bytes == 0 || (pc.a_copy_bytes == pc.a_elems && pc.a_elems % 16 == 0), pw + " second psi copy");
+        check(!(pc.a_copy_bytes > 0 && pc.realign), pw + " two copies and realigned reads");
+        if (pc.row_begin < 0 || pc.row_end > (int32_t)p.rows.size() || pc.row_begin > pc.row_end) continue;
+        int64_t covered = 0;
+        for (int32_t j = pc.row_begin; j < pc.row_end; ++j) {
+            const FRow &fr = p.rows[j];
+            check(fr.sr >= 0 && fr.sr < c.Hi, pw + " source row outside the plane");
+            check(fr.len > 0 && fr.len % 8 == 0 && fr.start % 8 == 0 && fr.win_off == covered,
+                  pw + " window rows not contiguous 8-element runs");
+            covered += fr.len;
+        }
+        check(covered == pc.win_elems, pw + " window rows do not fill the window area");
+        const int64_t stage = 4 * (int64_t)pc.desc_words + 2 * (int64_t)pc.a_elems;
+        if (pc.resident > 0) {
+            check(bu.resident, pw + " resident piece in a streamed plan");
+            check(p.ho_piece.size() > 1, pw + " resident");
+            check(pc.resident % 16 == 0 && pc.resident >= 2 * (int64_t)bu.ch * pc.win_elems && pc.resident >= bu.xch_bytes,
+                  pw + " resident window buffer too small");
+            check(stage + 2 * (int64_t)pc.resident <= p.max_resident_bytes &&
+                      p.max_resident_bytes <= 2 * bu.piece_budget,
+                  pw + " resident layout exceeds its LDS");
+        } else {
+            check(fused_piece_bytes(pc.desc_words, pc.a_elems, bu.ch, pc.win_elems) <= p.max_piece_bytes &&
+                      p.max_piece_bytes <= bu.piece_budget,
+                  pw + " stage exceeds its LDS");
+        }
+    }
+    for (int h = 0; h < c.Ho; ++h) {
+        const int n = p.ho_piece[h + 1] - p.ho_piece[h];
+        check(n >= 0, what + ": latitude pieces");
+        for (int i = p.ho_piece[h]; i < p.ho_piece[h + 1]; ++i)
+            check(p.pieces[i].resident == 0 || n == 1, what + ": a resident latitude has one piece");
+    }
+    if (g_fail) return;
+
+    // the replay
+    const int PH = 32 / kr;  // phases per MFMA
+    const int n_spans = (c.Wo + kFusedSpan - 1) / kFusedSpan;
+    // columns: both ends of a span (the window's first and last runs) and a few inside; every span
+    // of a narrow grid, else the first and the last (ragged) one
+    std::vector<int> spans, cols = {0, 1, 2, 15, 16, 30, 31};
+    if (c.Wo <= 2 * kFusedSpan) {
+        for (int i = 0; i < n_spans; ++i) spans.push_back(i);
+    } else {
+        spans = {0, n_spans - 1};
+    }
+    double scale = 0.0, err = 0.0;
+    std::vector<double> win, acc;
+    for (int ho = 0; ho < c.Ho; ++ho) {
+        for (int sp : spans) {
+            const int px0 = sp * kFusedSpan;
+            acc.assign((size_t)8 * kr * cols.size(), 0.0);
+            for (int pi = p.ho_piece[ho]; pi < p.ho_piece[ho + 1]; ++pi) {
+                const FPiece &pc = p.pieces[pi];
+                win.assign(pc.win_elems, NAN);
+                for (int32_t j = pc.row_begin; j < pc.row_end; ++j) {
+                    const FRow &fr = p.rows[j];
+                    for (int i = 0; i < fr.len; ++i) {
+                        int64_t col = ((int64_t)s * px0 + fr.start + i) % c.Wi;
+                        if (col < 0) col += c.Wi;
+                        win[fr.win_off + i] = src[(size_t)fr.sr * c.Wi + col];
+                    }
+                }
+                const int64_t psi_bytes = 2 * (int64_t)pc.a_elems;
+                for (int blk = 0; blk < pc.nblk; ++blk) {
+                    const int32_t ax = p.descs[2 * ((size_t)pc.desc_begin + blk)];
+                    const int32_t xo = p.descs[2 * ((size_t)pc.desc_begin + blk) + 1];
+                    check(ax % 4 == 0 && xo % 16 == 0, what + ": block descriptor alignment");
+                    for (int q = 0; q < 8; ++q) {
+                        const int sq = s * q;
+                        const bool odd = (sq & 1) != 0;
+                        for (int k = 0; k < kr; ++k) {
+                            for (int hh = 0; hh < 2; ++hh) {
+                                // psi: the lane's words (A row = phase q, basis k; K half hh)
+                                const int64_t lane = 4 * (int64_t)kr * (4 * hh - (sq + 1) / 2) + 4 * k + ax +
+                                                     (odd && !pc.realign ? pc.a_copy_bytes : 0);
+                                const int nw = pc.realign ? 5 : 4;
+                                float h10[10];
+                                bool in = true;
+                                for (int w = 0; w < nw; ++w) {
+                                    const int64_t b = lane + 4 * (int64_t)kr * w;
+                                    in = in && b >= 0 && b + 4 <= psi_bytes;
+                                    if (b < 0 || b + 4 > psi_bytes) continue;
+                                    h10[2 * w] = bf16_value(p.adata[pc.a_begin + b / 2]);
+                                    h10[2 * w + 1] = bf16_value(p.adata[pc.a_begin + b / 2 + 1]);
+                                }
+                                check(in, what + ": psi word read outside the piece's psi");
+                                if (!in) return;
+                                const int sh = (pc.realign && odd) ? 1 : 0;
+                                for (size_t ci = 0; ci < cols.size(); ++ci) {
+                                    const int n = cols[ci];
+                                    const int64_t ex = xo / 2 + 8 * (int64_t)s * n + 8 * hh;  // B column n, K half hh
+                                    check(ex >= 0 && ex + 8 <= pc.win_elems, what + ": x run outside the window area");
+                                    if (ex < 0 || ex + 8 > pc.win_elems) return;
+                                    double sum = 0.0;
+                                    for (int i = 0; i < 8; ++i) {
+                                        const double a = h10[sh + i];
+                                        if (a != 0.0) sum += a * win[ex + i];
+                                    }
+                                    acc[((size_t)q * kr + k) * cols.size() + ci] += sum;
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+            for (int q = 0; q < 8; ++q)
+                for (int k = 0; k < kr; ++k)
+                    for (size_t ci = 0; ci < cols.size(); ++ci) {
+                        const double got = acc[((size_t)q * kr + k) * cols.size() + ci];
+                        const int wo = px0 + 8 * cols[ci] + q;
+                        if (k >= c.K || wo >= c.Wo) {
+                            check(std::isfinite(got), what + ": row past K or longitude past Wo reads unstaged LDS");
+                            continue;
+                        }
+                        const double want = ref_at(c, src, k, ho, wo);
+                        scale = std::max(scale, std::fabs(want));
+                        if (!(std::fabs(got - want) <= err)) err = std::isnan(got) ? INFINITY : std::fabs(got - want);
+                    }
+        }
+    }
+    check(err <= 1e-9 * std::max(scale, 1.0),
+          what + ": replay differs from the CSR definition (max error " + std::to_string(err) + ")");
+    (void)PH;
+}
+
+// The row-inverted CSR of the matrix-core backward: its forward over gout rows, row r = ho' g + k'
+// (= hi s + rho), column wo', must equal the backward gx[hi, rho + s wo'].
+void check_inverse(const CSRView &c, const InverseCSR &inv, int g, const std::vector<double> &gsrc,
+                   const std::vector<double> &want_b)
+{
+    const int s = c.Wi / c.Wo;
+    const CSRView &v = inv.view;
+    check(v.K == g && v.Ho == (c.Hi * s + g - 1) / g && v.Wo == c.Wo && v.Hi == c.K * c.Ho && v.Wi == c.Wo &&
+              v.nnz == c.nnz,
+          "inverse CSR shape");
+    int code = 0;
+    const std::string msg = validate_csr(v, &code);
+    check(code == 0, "inverse CSR rejected: " + msg);
+    if (code != 0) return;
+    double err = 0.0, scale = 0.0;
+    for (int ho = 0; ho < v.Ho; ++ho)
+        for (int k = 0; k < g; ++k) {
+            const int64_t r = (int64_t)ho * g + k;
+            const int64_t R = (int64_t)k * v.Ho + ho;
+            if (r >= (int64_t)c.Hi * s) {
+                check(v.row_ptr[R] == v.row_ptr[R + 1], "inverse CSR: a row past the gradient holds entries");
+                continue;
+            }
+            const int hi = (int)(r / s), rho = (int)(r % s);
+            for (int wo = 0; wo < c.Wo; ++wo) {
+                double acc = 0.0;
+                for (int64_t e = v.row_ptr[R]; e < v.row_ptr[R + 1]; ++e)
+                    acc += (double)v.val[e] * gsrc[(size_t)v.col_hi[e] * v.Wi + (v.col_wi[e] + wo) % v.Wi];
+                const double want = want_b[(size_t)hi * c.Wi + rho + (int64_t)s * wo];
+                scale = std::max(scale, std::fabs(want));
+                err = std::max(err, std::fabs(acc - want));
+            }
+        }
+    check(err <= 1e-9 * std::max(scale, 1.0), "inverse CSR: its forward differs from the backward");
+}
+
 }  // namespace
 
 int main(int argc, char **argv)
@@ -416,11 +666,40 @@ int main(int argc, char **argv)
         check_tile_grid(tf, BC);
         check_tile_grid(tb, BC);
     }
+    // matrix-core plans with the library's parameters (disco_api.hip, kernels_fused_mfma.hip): fused
+    // conv (basis rows 16, four channels per chunk, two 64 KiB stages beside the 32 KiB W slice,
+    // resident latitudes with 32 KiB operand exchange), forward (basis rows 8 or 16, 8 or 4 channels,
+    // 40 KiB stages), backward (8 gradient rows per group over the row-inverted CSR)
+    FusedPlan fup, fwp, bwp;
+    {
+        PhaseBudget bf{16, 4, ((160 * 1024 - 32 * 1024) / 2) & ~15, true, 32 * 1024};
+        PhasePlanParams prm;
+        prm.kr = bf.kr; prm.ch = bf.ch; prm.piece_budget = (int)bf.piece_budget; prm.xch_bytes = bf.xch_bytes;
+        build_phase_plan(c, prm, fup);
+        check_phase(c, fup, bf, x, "fused matrix-core plan");
+        const int fkr = c.K <= 8 ? 8 : 16;
+        PhaseBudget bw{fkr, fkr == 8 ? 8 : 4, 40 * 1024, false, 0};
+        PhasePlanParams fprm;
+        fprm.kr = bw.kr; fprm.ch = bw.ch; fprm.piece_budget = (int)bw.piece_budget; fprm.xch_bytes = 0;
+        fprm.allow_resident = false;
+        build_phase_plan(c, fprm, fwp);
+        check_phase(c, fwp, bw, x, "forward matrix-core plan");
+        const int g8 = 8;
+        InverseCSR inv;
+        build_inverse_csr(c, g8, inv);
+        check_inverse(c, inv, g8, g, want_b);
+        PhaseBudget bb{8, 8, 40 * 1024, false, 0};
+        PhasePlanParams bprm = fprm;
+        bprm.kr = 8; bprm.ch = 8;
+        build_phase_plan(inv.view, bprm, bwp);
+        check_phase(inv.view, bwp, bb, g, "backward matrix-core plan (row-inverted CSR)");
+    }
 
     printf("plan_check: K=%d Ho=%d Wo=%d Hi=%d Wi=%d nnz=%lld tiled fwd %s (NI=%d G=%d, %zu tasks, %d/%d split) "
-           "bwd %s (NI=%d, %zu tasks, %d/%d split)\n",
+           "bwd %s (NI=%d, %zu tasks, %d/%d split); matrix-core fused %s (%zu pieces), fwd %s (%zu), bwd %s (%zu)\n",
            c.K, c.Ho, c.Wo, c.Hi, c.Wi, (long long)c.nnz, tf.ok ? "on" : "off", tf.NI, tf.G, tf.tasks.size(), tf.n_ws4,
-           tf.n_ws2, tb.ok ? "on" : "off", tb.NI, tb.tasks.size(), tb.n_ws4, tb.n_ws2);
+           tf.n_ws2, tb.ok ? "on" : "off", tb.NI, tb.tasks.size(), tb.n_ws4, tb.n_ws2, fup.ok ? "on" : "off",
+           fup.pieces.size(), fwp.ok ? "on" : "off", fwp.pieces.size(), bwp.ok ? "on" : "off", bwp.pieces.size());
     if (g_fail) {
         fprintf(stderr, "plan_check: %d check(s) failed\n", g_fail);
         return 1;

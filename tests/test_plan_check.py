@@ -1,12 +1,17 @@
 """Host plan code under the address and undefined-behaviour sanitizers (CPU only).
 
-`sparse_gather_contraction_amd/csrc/plan_check.cpp` builds every gather plan that
-disco_psi_create builds (plain, LDS-staged for 4- and 2-byte elements, register-tiled),
-replays each kernel's indexing on the CPU and checks that every index stays inside the
-buffer it addresses, that every destination element is written exactly once, that the
-replay reproduces the CSR definition in fp64, and that the tiled kernel's workgroup
-decode serves every (task, plane) pair.  A plan bug would otherwise surface as a GPU
-memory fault.  The checker is compiled here with g++ and -fsanitize=address,undefined.
+`sparse_gather_contraction_amd/csrc/plan_check.cpp` builds every plan that
+disco_psi_create builds (plain, LDS-staged for 4- and 2-byte elements, register-tiled;
+the phase-split matrix-core plans of the fused conv, the forward and the backward over
+the row-inverted CSR), replays each kernel's indexing on the CPU and checks that every
+index stays inside the buffer it addresses (for the matrix-core plans: descriptors, every
+lane's psi words and x runs, stage sizes against the LDS budgets), that every destination
+element of the gathers is written exactly once, that the replay reproduces the CSR
+definition in fp64 (the matrix-core replay sums each block's 16 offsets per A row and B
+column as v_mfma_f32_32x32x16 does), that the row-inverted CSR reproduces the backward,
+and that the tiled kernel's workgroup decode serves every (task, plane) pair.  A plan bug
+would otherwise surface as a GPU memory fault.  The checker is compiled here with g++ and
+-fsanitize=address,undefined.
 """
 import os
 import subprocess
@@ -26,8 +31,8 @@ def checker(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("plan_check") / "plan_check")
     cmd = ["g++", "-O2", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-fno-omit-frame-pointer", "-I", CSRC,
-           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "plan_tile.cpp"), os.path.join(CSRC, "plan_check.cpp"),
-           "-o", out]
+           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "plan_fused.cpp"), os.path.join(CSRC, "plan_tile.cpp"),
+           os.path.join(CSRC, "plan_check.cpp"), "-o", out]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert r.returncode == 0, r.stdout
     return out
@@ -69,6 +74,10 @@ CASES = {
     "rand_L384": lambda: random_psi(2, 3, 384, 4, 768, 0.02, seed=7),
     "rand_L193": lambda: random_psi(2, 3, 193, 4, 386, 0.05, seed=8),
     "rand_L192": lambda: random_psi(3, 3, 192, 4, 384, 0.05, seed=9),
+    # matrix-core plans: K = 16 at s = 1 with resident latitudes (two psi copies) and streamed
+    # ones (rows cut into sub-rows, realigned psi reads); K = 8 at s = 2
+    "phase_k16_s1_resident_and_streamed": lambda: build_psi(33, 512, 33, 512, 0.5, 4, 4),
+    "phase_k8_s2": lambda: build_psi(25, 768, 25, 384, 0.5, 4, 2),
 }
 
 
@@ -116,11 +125,47 @@ def test_checker_catches_planted_plan_mistakes(name, tmp_path):
     mut = tmp_path / "plan_tile_mut.cpp"
     mut.write_text(src.replace(old, new))
     exe = str(tmp_path / "plan_check_mut")
-    cmd = ["g++", "-O1", "-std=c++17", "-I", CSRC, os.path.join(CSRC, "plan.cpp"), str(mut),
-           os.path.join(CSRC, "plan_check.cpp"), "-o", exe]
+    cmd = ["g++", "-O1", "-std=c++17", "-I", CSRC, os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "plan_fused.cpp"),
+           str(mut), os.path.join(CSRC, "plan_check.cpp"), "-o", exe]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert r.returncode == 0, r.stdout
     path = str(tmp_path / "psi.csr")
     _write_csr(workload_psi(WORKLOADS["fwdbwd_f32_181x360"]), path)
+    r = subprocess.run([exe, path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
+    assert r.returncode == 1 and "FAIL:" in r.stdout, r.stdout[-2000:]
+
+
+FUSED_MUTANTS = {
+    # each replaces one line of plan_fused.cpp with a plausible mistake the checker must catch
+    "psi offset drops the 8s lead": ("out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));",
+                                     "out.descs.push_back(2 * kr * (a_row_e + (t0 - first)));"),
+    "window offset one run late": ("out.descs.push_back(2 * (win_off + (t0 - first)));",
+                                   "out.descs.push_back(2 * (win_off + (t0 - first) + 8));"),
+    "second psi copy not shifted": ("if (copies == 2) put_pairs(copy1, copy1_16, m, first - 8 * s, ra, 1);",
+                                    "if (copies == 2) put_pairs(copy1, copy1_16, m, first - 8 * s, ra, 0);"),
+    "realigned psi tail too short": ("tail = realign ? 18 : 16;", "tail = 16;"),
+    "inverse CSR shift sign": ("out.col_wi[dst] = (c.Wo - (wi - rho) / s) % c.Wo;",
+                               "out.col_wi[dst] = (c.Wo + (wi - rho) / s) % c.Wo;"),
+    "last block of a row dropped": ("for (int32_t t0 = T0; t0 == T0 || t0 - 1 - smax < tmax; t0 += kBlkJ) {",
+                                    "for (int32_t t0 = T0; t0 == T0 || t0 + 15 - smax < tmax; t0 += kBlkJ) {"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_MUTANTS))
+def test_checker_catches_planted_matrix_core_plan_mistakes(name, tmp_path):
+    """Sensitivity of the matrix-core replay: a copy of plan_fused.cpp with one planted mistake must
+    fail the checker on a K = 16 psi with both resident and streamed latitudes."""
+    old, new = FUSED_MUTANTS[name]
+    src = open(os.path.join(CSRC, "plan_fused.cpp")).read()
+    assert src.count(old) == 1, name
+    mut = tmp_path / "plan_fused_mut.cpp"
+    mut.write_text(src.replace(old, new))
+    exe = str(tmp_path / "plan_check_mut")
+    cmd = ["g++", "-O1", "-std=c++17", "-I", CSRC, os.path.join(CSRC, "plan.cpp"), str(mut),
+           os.path.join(CSRC, "plan_tile.cpp"), os.path.join(CSRC, "plan_check.cpp"), "-o", exe]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    path = str(tmp_path / "psi.csr")
+    _write_csr(CASES["phase_k16_s1_resident_and_streamed"](), path)
     r = subprocess.run([exe, path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
     assert r.returncode == 1 and "FAIL:" in r.stdout, r.stdout[-2000:]
