@@ -78,6 +78,7 @@ struct Ctx {
     int64_t plane_sz;
     int64_t x_bstride;  // elements between batches of x (C planes when contiguous)
     bool vec_x, vec_w;
+    int x_half;  // s = 2: this lane reads the odd half of the split window area
     bool vec_out;  // contraction-only mode: output rows are 16-byte aligned (L, strides multiples of 8)
     float scale;  // contraction result scale: 2^-e for fp16 psi, 1 for bf16
     // contraction-only mode: out[b, c, k, ho, wo] at out + b * out_bstride
@@ -141,16 +142,24 @@ __device__ __forceinline__ void copy_units(const Ctx &c, __amdgpu_buffer_rsrc_t 
 // x windows of one piece for the chunk starting at channel c0: window of row r holds input
 // columns s px0 + start + i (mod Wi) of input latitude hi.  Rows go round the waves; a wave
 // handles all channels of its rows (row data is read once, no integer division).
+// With s = 2 a channel's window area keeps its 16-byte units split by parity: unit u (counted
+// from the area's start; rows start at even units) sits at unit (u % 2) * (win_elems / 16) + u / 2.
+// A lane's x runs are units 2 n + {0, 1} past the block's first, so the 64 lanes of a read then
+// touch consecutive units of one half instead of every other unit (no LDS bank conflicts).
+__device__ __forceinline__ int split_unit(int u, int half) { return (u & 1) * half + (u >> 1); }
+
 template <int NCH>
 __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, int c0, bf16_t *win)
 {
     const int nrows = pc.row_end - pc.row_begin;
     const int ccn = min(NCH, c.C - c0);
     const bf16_t *plane0 = c.x + (int64_t)c.b * c.x_bstride + (int64_t)c0 * c.plane_sz;
+    const bool split = c.s == 2;
+    const int half = pc.win_elems >> 4;  // units per half of a split area
     for (int r = c.wave; r < nrows; r += kWaves) {
         const FRow fr = c.rows[pc.row_begin + r];
-        bf16_t *dst = win + fr.win_off;
         const int nch = fr.len >> 3;
+        const int u_row = fr.win_off >> 3;  // the row's first unit (even when split)
         int g0 = c.s * c.px0 + fr.start;  // within a few Wi of [0, Wi)
         while (g0 < 0) g0 += c.Wi;
         while (g0 >= c.Wi) g0 -= c.Wi;
@@ -160,13 +169,19 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
             const uint32_t plane_bytes = 2u * (uint32_t)c.plane_sz;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(plane0, plane_bytes * (uint32_t)ccn);
             const uint32_t row0 = 2u * (uint32_t)(fr.sr * c.Wi);
-            for (int t = 0; t < nch; t += 64) {
-                const int e8 = t + c.lane;
-                int pos = g0 + 8 * e8;
-                while (pos >= c.Wi) pos -= c.Wi;
-                const uint32_t voff = row0 + 2u * (uint32_t)pos;
-                if (e8 < nch) {
-                    for (int cl = 0; cl < ccn; ++cl) dma16(rs, voff + plane_bytes * cl, dst + cl * pc.win_elems + 8 * t);
+            // units of one parity (split) or all units go to consecutive LDS units, one per lane
+            const int npar = split ? 2 : 1, nu = split ? nch >> 1 : nch;
+            for (int par = 0; par < npar; ++par) {
+                bf16_t *dst = win + 8 * (split ? par * half + (u_row >> 1) : u_row);
+                for (int t = 0; t < nu; t += 64) {
+                    const int i = t + c.lane;
+                    const int e8 = split ? 2 * i + par : i;  // unit of the row
+                    int pos = g0 + 8 * e8;
+                    while (pos >= c.Wi) pos -= c.Wi;
+                    const uint32_t voff = row0 + 2u * (uint32_t)pos;
+                    if (i < nu) {
+                        for (int cl = 0; cl < ccn; ++cl) dma16(rs, voff + plane_bytes * cl, dst + cl * pc.win_elems + 8 * t);
+                    }
                 }
             }
         } else {
@@ -174,12 +189,15 @@ __device__ __forceinline__ void stage_windows(const Ctx &c, const FPiece &pc, in
             for (int e = c.lane; e < fr.len; e += 64) {
                 int pos = g0 + e;
                 while (pos >= c.Wi) pos -= c.Wi;
-                for (int cl = 0; cl < ccn; ++cl) dst[cl * pc.win_elems + e] = xrow[cl * c.plane_sz + pos];
+                const int idx = split ? 8 * split_unit(u_row + (e >> 3), half) + (e & 7) : fr.win_off + e;
+                for (int cl = 0; cl < ccn; ++cl) win[cl * pc.win_elems + idx] = xrow[cl * c.plane_sz + pos];
             }
         }
         for (int cl = ccn; cl < NCH; ++cl)  // channels past C are zeros
-            for (int e8 = c.lane; e8 < nch; e8 += 64)
-                *reinterpret_cast<uint4 *>(dst + cl * pc.win_elems + 8 * e8) = make_uint4(0u, 0u, 0u, 0u);
+            for (int e8 = c.lane; e8 < nch; e8 += 64) {
+                const int u = split ? split_unit(u_row + e8, half) : u_row + e8;
+                *reinterpret_cast<uint4 *>(win + cl * pc.win_elems + 8 * u) = make_uint4(0u, 0u, 0u, 0u);
+            }
     }
 }
 
@@ -293,17 +311,18 @@ __device__ __forceinline__ void contract_pairs(const unsigned char *__restrict__
     }
 }
 
-// odd: the lane's phase shift is odd (second psi copy, or the realigning selector)
+// odd: the lane's phase shift is odd (second psi copy, or the realigning selector); x_half: the
+// lane reads the odd half of a split window area (s = 2)
 template <int KR, bool F16>
 __device__ __forceinline__ void contract(const unsigned char *__restrict__ stage, const unsigned char *__restrict__ win,
-                                         const FPiece &pc, int a_lane2, int x_lane2, bool odd, int ch0,
+                                         const FPiece &pc, int a_lane2, int x_lane2, int x_half, bool odd, int ch0,
                                          f32x16 (&d)[2])
 {
     const int npair = pc.nblk >> 1;
     if (npair <= 0) return;
     const unsigned char *a_base = stage + 4 * pc.desc_words + a_lane2;
     const int wel2 = 2 * pc.win_elems;
-    const unsigned char *x_base = win + ch0 * wel2 + x_lane2;
+    const unsigned char *x_base = win + ch0 * wel2 + x_lane2 + x_half * pc.win_elems;
     if (pc.realign)
         contract_pairs<KR, true, F16>(stage, a_base, x_base, wel2, npair, odd ? 0x05040302u : 0x03020100u, d);
     else
@@ -400,33 +419,45 @@ __device__ __forceinline__ void store_contraction(const Ctx &c, const f32x16 (&d
 // einsum's operand exchange — the fp32 accumulators rounded to the data type, exactly the values
 // the einsum multiplied and the values the contraction-only mode writes — to save[b, c, k, ho, ...]
 // as 16-byte row segments (by the first output-channel block only: the others hold the same values).
-// Exchange unit (pp, h2, cl, ph), lane (r, hh) holds basis 8 hh .. + 7
-// of longitude px0 + 8 r + 2 pp + ph, channel kCh t + 2 h2 + cl.  Called after the einsum (every
-// wave's operands are in the exchange); the exchange is overwritten only after the next step's
-// opening barrier.
+// Exchange unit (pp, h2, cl, ph), lane (r, hh) holds basis 8 hh .. + 7 of longitude px0 + 8 r + 2 pp + ph,
+// channel kCh t + 2 h2 + cl.  Thread (chl, hh, r, kh) reads the four bases 8 hh + 4 kh .. + 3 of its
+// eight units (one 8-byte read each; the 64 lanes of a wave read 512 contiguous bytes, free of bank
+// conflicts) and writes the four rows' eight longitudes px0 + 8 r .. + 7.  Called after the einsum
+// (every wave's operands are in the exchange); the exchange is overwritten only after the next
+// step's opening barrier.
 __device__ __forceinline__ void save_contraction(const Ctx &c, const unsigned char *__restrict__ xch, int t)
 {
-    const int64_t HoL = (int64_t)c.Ho * c.L;
-    for (int u = c.tid; u < kCh * 16 * 32; u += kThreads) {
-        const int r = u & 31, row = u >> 5, k = row & 15, chl = row >> 4;
-        const int ch = kCh * t + chl, wo = c.px0 + 8 * r;
-        if (k >= c.K || ch >= c.C || wo >= c.L) continue;
-        const int h2 = chl >> 1, cl = chl & 1;
-        const unsigned char *src = xch + 1024 * ((h2 * 2 + cl) * 2) + 16 * (r + 32 * (k >> 3)) + 2 * (k & 7);
-        uint16_t v[8];
+    static_assert(kThreads == kCh * 2 * 32 * 2, "one thread per (channel, basis half, column, basis quarter)");
+    const int kh = c.tid & 1, r = (c.tid >> 1) & 31, hh = (c.tid >> 6) & 1, chl = c.tid >> 7;
+    const int ch = kCh * t + chl, wo = c.px0 + 8 * r, k0 = 8 * hh + 4 * kh;
+    if (ch >= c.C || wo >= c.L || k0 >= c.K) return;
+    const int h2 = chl >> 1, cl = chl & 1;
+    const unsigned char *src = xch + 1024 * (h2 * 2 + cl) * 2 + 16 * (r + 32 * hh) + 8 * kh;
+    uint2 v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)  // q = 2 pp + ph: unit offset 1024 (8 pp + ph)
-            v[q] = *reinterpret_cast<const uint16_t *>(src + 1024 * (8 * (q >> 1) + (q & 1)));
-        bf16_t *dst = c.save + (int64_t)c.b * c.save_bstride + ((int64_t)ch * c.K + k) * HoL + (int64_t)c.ho * c.L + wo;
+    for (int q = 0; q < 8; ++q)  // q = 2 pp + ph: unit ((pp * 2 + h2) * 2 + cl) * 2 + ph
+        v[q] = *reinterpret_cast<const uint2 *>(src + 1024 * (8 * (q >> 1) + (q & 1)));
+    const int64_t HoL = (int64_t)c.Ho * c.L;
+    bf16_t *dst0 = c.save + (int64_t)c.b * c.save_bstride + ((int64_t)ch * c.K + k0) * HoL + (int64_t)c.ho * c.L + wo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (k0 + j >= c.K) break;
+        uint32_t h[8];  // basis k0 + j of the eight longitudes
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t w = (j < 2) ? v[q].x : v[q].y;
+            h[q] = (j & 1) ? (w >> 16) : (w & 0xffffu);
+        }
+        bf16_t *dst = dst0 + (int64_t)j * HoL;
         if (c.vec_save && wo + 8 <= c.L) {
-            uint4 w;
-            w.x = v[0] | ((uint32_t)v[1] << 16);
-            w.y = v[2] | ((uint32_t)v[3] << 16);
-            w.z = v[4] | ((uint32_t)v[5] << 16);
-            w.w = v[6] | ((uint32_t)v[7] << 16);
-            *reinterpret_cast<uint4 *>(dst) = w;
+            uint4 o;
+            o.x = h[0] | (h[1] << 16);
+            o.y = h[2] | (h[3] << 16);
+            o.z = h[4] | (h[5] << 16);
+            o.w = h[6] | (h[7] << 16);
+            *reinterpret_cast<uint4 *>(dst) = o;
         } else {
-            for (int e = 0; e < 8 && wo + e < c.L; ++e) dst[e] = v[e];
+            for (int e = 0; e < 8 && wo + e < c.L; ++e) dst[e] = (bf16_t)h[e];
         }
     }
 }
@@ -449,7 +480,7 @@ __device__ __forceinline__ void run_step(const Ctx &c, const FPiece *__restrict_
     }
     if (p == 0) zero(d);
     const FPiece pc = pieces[p_begin + p];
-    contract<16, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * h2, d);
+    contract<16, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, c.x_half, odd, 2 * h2, d);
     if (p + 1 == npieces) {
         if constexpr (EIN) {
             __builtin_amdgcn_s_waitcnt(0);
@@ -478,7 +509,7 @@ __device__ __forceinline__ void run_chunk_resident(const Ctx &c, const FPiece &p
     if (EIN && t > 0) stage_w(c, kCh * t, wb);
     if (t + 1 < nchunks) stage_windows<kCh>(c, pc, kCh * (t + 1), reinterpret_cast<bf16_t *>(nxt));
     zero(d);
-    contract<16, F16>(stage, cur, pc, a_lane2, x_lane2, odd, 2 * h2, d);
+    contract<16, F16>(stage, cur, pc, a_lane2, x_lane2, c.x_half, odd, 2 * h2, d);
     if constexpr (EIN) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // W slice visible; `cur` free for the exchange
@@ -551,7 +582,9 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
     const int q = 2 * pp + (r >> 4), sq = s * q;
     const int a_lane2 = 64 * (4 * hh - (sq + 1) / 2) + 4 * kb;  // bytes
     const bool odd = (sq & 1) != 0;  // reads the second psi copy
-    const int x_lane2 = 2 * (8 * s * r + 8 * hh);                // bytes
+    // x runs: units s n + hh past the block's first (bytes); with s = 2 the area is split by parity
+    const int x_lane2 = s == 2 ? 16 * r : 2 * (8 * s * r + 8 * hh);
+    c.x_half = s == 2 ? hh : 0;
 
     f32x16 yacc[2][NOTH];
 #pragma unroll
@@ -653,7 +686,7 @@ __device__ __forceinline__ void fwd_step(const Ctx &c, const FPiece *__restrict_
     __syncthreads();                // everyone's have; the previous step is done with `nxt`
     if (p + 1 < npieces) stage_step<FCH>(c, pieces[p_begin + p + 1], c0, nxt);
     const FPiece pc = pieces[p_begin + p];
-    contract<KR, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, odd, 2 * cp, d);
+    contract<KR, F16>(cur, cur + 4 * pc.desc_words + 2 * pc.a_elems, pc, a_lane2, x_lane2, c.x_half, odd, 2 * cp, d);
 }
 
 template <int KR, bool F16>
@@ -702,7 +735,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int q = PH * g + r / KR, sq = s * q;
     const int a_lane2 = 4 * KR * (4 * hh - (sq + 1) / 2) + 4 * (r % KR);  // bytes
     const bool odd = (sq & 1) != 0;  // reads the second psi copy
-    const int x_lane2 = 2 * (8 * s * r + 8 * hh);                        // bytes
+    // x runs: units s n + hh past the block's first (bytes); with s = 2 the area is split by parity
+    const int x_lane2 = s == 2 ? 16 * r : 2 * (8 * s * r + 8 * hh);
+    c.x_half = s == 2 ? hh : 0;
 
     f32x16 d[2];
     zero(d);

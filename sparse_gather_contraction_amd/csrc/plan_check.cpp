@@ -444,8 +444,8 @@ void check_phase(const CSRView &c, const FusedPlan &p, const PhaseBudget &bu, co
         for (int32_t j = pc.row_begin; j < pc.row_end; ++j) {
             const FRow &fr = p.rows[j];
             check(fr.sr >= 0 && fr.sr < c.Hi, pw + " source row outside the plane");
-            check(fr.len > 0 && fr.len % 8 == 0 && fr.start % 8 == 0 && fr.win_off == covered,
-                  pw + " window rows not contiguous 8-element runs");
+            check(fr.len > 0 && fr.len % (s == 2 ? 16 : 8) == 0 && fr.start % 8 == 0 && fr.win_off == covered,
+                  pw + " window rows not contiguous 8-element runs (16 when s = 2)");
             covered += fr.len;
         }
         check(covered == pc.win_elems, pw + " window rows do not fill the window area");
@@ -491,13 +491,24 @@ void check_phase(const CSRView &c, const FusedPlan &p, const PhaseBudget &bu, co
             acc.assign((size_t)8 * kr * cols.size(), 0.0);
             for (int pi = p.ho_piece[ho]; pi < p.ho_piece[ho + 1]; ++pi) {
                 const FPiece &pc = p.pieces[pi];
+                // a channel's window area as the kernels stage it: element e of the area at e, or with
+                // s = 2 split by unit parity, unit u at unit (u % 2) (win_elems / 16) + u / 2
+                const int half = pc.win_elems / 16;
+                auto phys = [&](int64_t e) {
+                    if (s != 2) return e;
+                    const int64_t u = e / 8;
+                    return 8 * ((u % 2) * half + u / 2) + e % 8;
+                };
                 win.assign(pc.win_elems, NAN);
                 for (int32_t j = pc.row_begin; j < pc.row_end; ++j) {
                     const FRow &fr = p.rows[j];
                     for (int i = 0; i < fr.len; ++i) {
                         int64_t col = ((int64_t)s * px0 + fr.start + i) % c.Wi;
                         if (col < 0) col += c.Wi;
-                        win[fr.win_off + i] = src[(size_t)fr.sr * c.Wi + col];
+                        const int64_t e = phys((int64_t)fr.win_off + i);
+                        check(e >= 0 && e < pc.win_elems, what + ": staged window element outside the area");
+                        if (e < 0 || e >= pc.win_elems) return;
+                        win[e] = src[(size_t)fr.sr * c.Wi + col];
                     }
                 }
                 const int64_t psi_bytes = 2 * (int64_t)pc.a_elems;
@@ -505,6 +516,7 @@ void check_phase(const CSRView &c, const FusedPlan &p, const PhaseBudget &bu, co
                     const int32_t ax = p.descs[2 * ((size_t)pc.desc_begin + blk)];
                     const int32_t xo = p.descs[2 * ((size_t)pc.desc_begin + blk) + 1];
                     check(ax % 4 == 0 && xo % 16 == 0, what + ": block descriptor alignment");
+                    check(s != 2 || pc.win_elems % 16 == 0, what + ": split window area of odd unit count");
                     for (int q = 0; q < 8; ++q) {
                         const int sq = s * q;
                         const bool odd = (sq & 1) != 0;
@@ -528,7 +540,12 @@ void check_phase(const CSRView &c, const FusedPlan &p, const PhaseBudget &bu, co
                                 const int sh = (pc.realign && odd) ? 1 : 0;
                                 for (size_t ci = 0; ci < cols.size(); ++ci) {
                                     const int n = cols[ci];
-                                    const int64_t ex = xo / 2 + 8 * (int64_t)s * n + 8 * hh;  // B column n, K half hh
+                                    // B column n, K half hh: the kernels' lane byte offset (x_lane2, and
+                                    // with s = 2 the odd half for hh = 1) plus the descriptor's
+                                    const int64_t xb = s == 2 ? xo + 16 * (int64_t)n + (int64_t)hh * pc.win_elems
+                                                              : xo + 2 * (8 * (int64_t)s * n + 8 * hh);
+                                    check(xb % 16 == 0, what + ": x run not 16-byte aligned");
+                                    const int64_t ex = xb / 2;
                                     check(ex >= 0 && ex + 8 <= pc.win_elems, what + ": x run outside the window area");
                                     if (ex < 0 || ex + 8 > pc.win_elems) return;
                                     double sum = 0.0;

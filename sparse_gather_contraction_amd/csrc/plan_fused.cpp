@@ -75,7 +75,9 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
     // fifth realigns an odd shift) from pair (base + 8 hh - s q) / 2
     int32_t tail = 16;
     auto ra_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 8 * s + tail; };
-    auto len_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 256 * s + 8; };  // window positions
+    // window positions; with s = 2 rows are whole pairs of 8-element units (the kernels split the area
+    // by unit parity, and a row then starts at an even unit)
+    auto len_of = [&](const SubRow &sb) { return sb.t0.back() - sb.first() + 256 * s + (s == 2 ? 16 : 8); };
     auto cost_of = [&](int64_t nblk, int64_t a_elems, int64_t win) {
         return fused_piece_bytes(2 * nblk, a_elems, ch, win);
     };
@@ -209,7 +211,9 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
                 out.rows.push_back(fr);
                 for (int32_t t0 : sb.t0) {
                     out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));
-                    out.descs.push_back(2 * (win_off + (t0 - first)));
+                    // window run: bytes into a channel's area; with s = 2 bytes into one parity half
+                    // (unit u of the area at 16 (u / 2): the run's first unit is even)
+                    out.descs.push_back((s == 2 ? 1 : 2) * (win_off + (t0 - first)));
                 }
                 put_pairs(out.adata, out.adata16, m, first - 8 * s, ra, 0);
                 if (copies == 2) put_pairs(copy1, copy1_16, m, first - 8 * s, ra, 1);

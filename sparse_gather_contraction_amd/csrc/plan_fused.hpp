@@ -23,8 +23,11 @@
 // of the one copy and realigns them (the plan picks per latitude, PhasePlanParams::
 // psi_copies); per block a descriptor (byte offsets of its psi rows and of its
 // window run in the piece stage); per row the window of input columns
-// s px0 + first + i, i < len = span of its blocks + 256 s + 8 (mod Wi).  Blocks
-// are contracted in pairs: a piece with an odd block count gets a zero block.
+// s px0 + first + i, i < len = span of its blocks + 256 s + 8 (mod Wi; + 16 when
+// s = 2, where the kernels keep a channel's window area split by the parity of its
+// 16-byte units, unit u at unit (u % 2) (area / 16) + u / 2, and the descriptor's
+// window offset counts bytes into one half).  Blocks are contracted in pairs: a
+// piece with an odd block count gets a zero block.
 //
 // Rows are cut into sub-rows and grouped into pieces; a piece's descriptors,
 // psi and windows (for one chunk of channels) fit one of two LDS stage
@@ -45,7 +48,7 @@ constexpr int kFusedSpan = 256;  // output longitudes per workgroup (8 phases x 
 struct FRow {          // one sub-row of a piece
     int32_t sr;        // source row = input latitude hi
     int32_t start;     // signed input-column offset of the window's first position (window = s px0 + start + i)
-    int32_t len;       // window length in positions (multiple of 8)
+    int32_t len;       // window length in positions (multiple of 8; of 16 when s = 2)
     int32_t win_off;   // element offset of this window inside one channel's window area
 };
 
@@ -56,7 +59,7 @@ struct FPiece {
     int32_t a_begin;     // first bf16 of the piece's psi in adata (multiple of 8)
     int32_t a_elems;     // bf16 count of the piece's psi (multiple of 8)
     int32_t row_begin, row_end;
-    int32_t win_elems;   // window elements per channel (multiple of 8)
+    int32_t win_elems;   // window elements per channel (multiple of 8; of 16 when s = 2)
     int32_t resident;    // > 0: the latitude's only piece, whose descriptors and psi stay in LDS for all
                          // chunks while the windows are double-buffered; the value is the window buffer
                          // size in bytes (at least the operand exchange)
