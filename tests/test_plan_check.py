@@ -139,8 +139,8 @@ FUSED_MUTANTS = {
     # each replaces one line of plan_fused.cpp with a plausible mistake the checker must catch
     "psi offset drops the 8s lead": ("out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));",
                                      "out.descs.push_back(2 * kr * (a_row_e + (t0 - first)));"),
-    "window offset one run late": ("out.descs.push_back(2 * (win_off + (t0 - first)));",
-                                   "out.descs.push_back(2 * (win_off + (t0 - first) + 8));"),
+    "window offset one run late": ("out.descs.push_back((s == 2 ? 1 : 2) * (win_off + (t0 - first)));",
+                                   "out.descs.push_back((s == 2 ? 1 : 2) * (win_off + (t0 - first) + 8));"),
     "second psi copy not shifted": ("if (copies == 2) put_pairs(copy1, copy1_16, m, first - 8 * s, ra, 1);",
                                     "if (copies == 2) put_pairs(copy1, copy1_16, m, first - 8 * s, ra, 0);"),
     "realigned psi tail too short": ("tail = realign ? 18 : 16;", "tail = 16;"),
