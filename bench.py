@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+CLOCK_HZ = 2.4e9  # peak engine clock (LDS bytes per clock are reported at it)
 # Published vector fp32 figure: 256 CUs x 4 SIMDs x 32 fp32 FMA per clock x 2 flops x 2.4 GHz.  The
 # library is built with packed fp32 ops disabled; the FMA-loop probe (plain v_fma_f32, no packed math)
 # reaches 112.7 TFLOP/s on the box, above what 16 lanes per SIMD per clock could give (78.6), so the
@@ -33,6 +34,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_FP32_FMA_TFLOPS = PEAK_FP32_VALU_TFLOPS
 PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_F16_MFMA_TFLOPS = 2500.0
+PEAK_FP32_MFMA_TFLOPS = 157.3  # dense fp32 matrix peak (v_mfma_f32_16x16x4_f32)
 
 
 def op_bytes(op, w, nnz, Co=0):
@@ -196,7 +199,9 @@ def main():
         nxt["fused_saved"] = time_fused_saved(sgc, torch, np, h_u, tensors, wu, dev, stream)
         nxt["fused_saved"]["recompute_step_ms"] = round(per["fused"]["ms"] + nxt["fused_bwd"]["ms"], 4)
         nxt["f16"] = time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream)
+        nxt["fp32_fused"] = time_fp32_fused(sgc, torch, np, dev, stream)
         nxt["page_shapes"] = time_page_shapes(sgc, torch, np, dev, stream)
+        nxt["valu_gathers_bf16"] = time_valu_gathers(sgc, torch, np, h_fb, tensors, wf, wb, psi_fb, dev, stream)
 
     ein = None
     if not args.no_einsum and "fused" in ops:
@@ -324,9 +329,12 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
     import ctypes
 
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_gather_contraction_amd", "libdisco_probes.so"))
-    for f in ("disco_probe_read", "disco_probe_copy", "disco_probe_fma", "disco_probe_mfma"):
+    for f in ("disco_probe_read", "disco_probe_copy", "disco_probe_fma", "disco_probe_mfma", "disco_probe_lds",
+              "disco_probe_lds_mfma"):
         getattr(lib, f).restype = ctypes.c_int
     P, S = ctypes.c_void_p, ctypes.c_size_t
+    lib.disco_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P]
+    lib.disco_probe_lds_mfma.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P]
     lib.disco_probe_read.argtypes = [P, S, P, ctypes.c_int, P]
     lib.disco_probe_copy.argtypes = [P, P, S, ctypes.c_int, P]
     lib.disco_probe_fma.argtypes = [ctypes.c_int, P, ctypes.c_int, P]
@@ -353,6 +361,17 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
     ms_f = _timed(torch, np, stream, lambda: ok(lib.disco_probe_fma(iters, out.data_ptr(), blocks, sp)), reps)
     miters = 2048
     ms_m = _timed(torch, np, stream, lambda: ok(lib.disco_probe_mfma(miters, out.data_ptr(), blocks, sp)), reps)
+    # LDS: 16- and 4-byte reads (512 threads, 8 reads per iteration), and the contraction's LDS-fed
+    # MFMA pattern (two 16-byte x runs + four or five 4-byte psi words per two MFMAs)
+    lblocks, liters = 1024, 4096
+    lout = torch.zeros(lblocks * 512, dtype=torch.float32, device=dev)
+    lds_ms = {w: _timed(torch, np, stream, lambda w=w: ok(lib.disco_probe_lds(liters, w, lout.data_ptr(), lblocks, sp)),
+                        reps)[0] for w in (4, 16)}
+    lm_iters = 8192
+    lm_ms = {nb: _timed(torch, np, stream,
+                        lambda nb=nb: ok(lib.disco_probe_lds_mfma(lm_iters, nb, lout.data_ptr(), lblocks, sp)), reps)[0]
+             for nb in (4, 5)}
+    del lout
     torch.cuda.empty_cache()
     read_gbs = nb / ms_r[0] / 1e6
     copy_gbs = 2 * copy_mib * (1 << 20) / ms_c[0] / 1e6
@@ -362,8 +381,13 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
            "copy_GBps": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
            "fp32_fma_TFLOPs": round(fma_tf, 2), "fp32_fma_frac_of_peak": round(fma_tf / PEAK_FP32_VALU_TFLOPS, 4),
            "bf16_mfma_TFLOPs": round(mfma_tf, 1), "bf16_mfma_frac_of_peak": round(mfma_tf / PEAK_BF16_MFMA_TFLOPS, 4),
+           "lds_b128_bytes_per_clk_per_cu": round(lblocks * 512 * liters * 8 * 16 / lds_ms[16] / 1e-3 / 256 / CLOCK_HZ, 1),
+           "lds_b32_bytes_per_clk_per_cu": round(lblocks * 512 * liters * 8 * 4 / lds_ms[4] / 1e-3 / 256 / CLOCK_HZ, 1),
+           "lds_fed_mfma_TFLOPs": {f"{nb}_psi_words": round(lblocks * 8 * lm_iters * 2 * 32768 / lm_ms[nb] / 1e9, 1)
+                                   for nb in (4, 5)},
            "note": f"HIP probes built here: read stream of {read_gib} GiB (16-byte loads), copy of {copy_mib} MiB "
-                   f"(read + write), fp32 FMA loop, bf16 MFMA loop; medians of {reps}"}
+                   f"(read + write), fp32 FMA loop, bf16 MFMA loop, LDS read loops (bytes per clock per CU at "
+                   f"{CLOCK_HZ / 1e9} GHz), the contraction's LDS-fed MFMA loop; medians of {reps}"}
     print(f"[bench] achievable: {res}", file=sys.stderr, flush=True)
     return res
 
@@ -424,7 +448,7 @@ def time_fp32_configs(sgc, torch, np, dev, stream, warm=10, reps=60):
     print(f"[bench] fp32 configs: { {k: v['ms_median'] for k, v in res.items()} }", file=sys.stderr, flush=True)
     return res
 
-def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=3):
+def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps=5):
     """Backward of the fused convolution on the fused workload (gradient gy ~ N(0,1), bf16), timed
     apart from the step (it is not part of `value`).  Algorithmic flops: the two dense products
     (W^T gy and the weight gradient, 2 per MAC each) plus the transpose contraction and the
@@ -435,24 +459,16 @@ def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps
     gx = torch.empty_like(tensors["x5"])
     dW = torch.empty_like(tensors["W5"])
     ws = torch.empty(sgc.disco_fused_conv_bwd_workspace(h, w.B, w.C, w.Co), dtype=torch.uint8, device=dev)
-    for _ in range(warm):
+    for _ in range(warm - 1):
         sgc.disco_fused_conv_bwd(h, tensors["x5"], tensors["W5"], gy, gx, dW, workspace=ws)
-    torch.cuda.synchronize()
-    ev = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        sgc.disco_fused_conv_bwd(h, tensors["x5"], tensors["W5"], gy, gx, dW, workspace=ws)
-        b.record(stream)
-        ev.append((a, b))
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms, p10, p90 = _timed(torch, np, stream,
+                          lambda: sgc.disco_fused_conv_bwd(h, tensors["x5"], tensors["W5"], gy, gx, dW, workspace=ws), reps)
     macs = w.B * w.Ho * w.Wo * w.Co * w.C * w.K
     upd = op_updates(w, psi.nnz)
     alg = 4 * macs + 4 * upd
     print(f"[bench] fused backward: {ms:.3f} ms", file=sys.stderr, flush=True)
-    return {"ms": round(ms, 4), "einsum_macs_x2": 2 * macs, "nnz_updates_x2": 2 * upd, "bound": "mfma",
+    return {"ms": round(ms, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+            "einsum_macs_x2": 2 * macs, "nnz_updates_x2": 2 * upd, "bound": "mfma",
             "mfma_tflops_algorithmic": round(alg / ms / 1e9, 3),
             "mfma_frac": round(alg / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
             "workspace_bytes": int(ws.numel()),
@@ -460,7 +476,7 @@ def time_fused_bwd(sgc, torch, np, h, tensors, w, psi, dev, stream, warm=2, reps
 
 
 
-def time_fused_saved(sgc, torch, np, h, tensors, w, dev, stream, warm=2, reps=3):
+def time_fused_saved(sgc, torch, np, h, tensors, w, dev, stream, warm=2, reps=5):
     """A training step of the fused convolution that keeps its contraction: disco_fused_conv_save
     (y and out = F x, 17 GB of bf16 written) then disco_fused_conv_bwd_saved (no recompute of F x),
     timed apart from the step; compare `recompute_step_ms` (fused op + the recomputing backward)."""
@@ -477,61 +493,118 @@ def time_fused_saved(sgc, torch, np, h, tensors, w, dev, stream, warm=2, reps=3)
            "bwd_saved": lambda: sgc.disco_fused_conv_bwd_saved(h, out, W, gy, gx, dW, workspace=ws)}
     res = {}
     for name, fn in fns.items():
-        for _ in range(warm):
+        for _ in range(warm - 1):
             fn()
-        torch.cuda.synchronize()
-        ev = []
-        for _ in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            ev.append((a, b))
-        torch.cuda.synchronize()
-        res[name + "_ms"] = round(float(np.mean([a.elapsed_time(b) for a, b in ev])), 4)
+        med, p10, p90 = _timed(torch, np, stream, fn, reps)
+        res[name + "_ms"] = round(med, 4)
+        res[name + "_ms_p10_p90"] = [round(p10, 4), round(p90, 4)]
     res["step_ms"] = round(res["fwd_save_ms"] + res["bwd_saved_ms"], 4)
     del out, ws
     torch.cuda.empty_cache()
     print(f"[bench] fused training step keeping the contraction: {res}", file=sys.stderr, flush=True)
     return res
 
-def time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream, warm=1, reps=3):
-    """The three ops of the step with fp16 data (same shapes and psi), timed apart from the step;
-    all three run on the fp16 matrix cores (psi as fp16 of psi * 2^e)."""
+def time_f16(sgc, torch, np, h_fb, h_u, wf, wb, wu, psi_fb, psi_u, dev, stream, reps=5):
+    """The three ops of the step and the fused op's backward with fp16 data (same shapes and psi),
+    timed apart from the step; all run on the fp16 matrix cores (psi as fp16 of psi * 2^e)."""
     from disco_inputs import randn
 
     x3 = randn((wf.B, wf.C, wf.Hi, wf.Wi), 3200, "f16").to(dev)
     g4 = randn((wb.B, wb.C, wb.K, wb.Ho, wb.Wo), 3201, "f16").to(dev)
     x5 = randn((wu.B, wu.C, wu.Hi, wu.Wi), 3202, "f16").to(dev)
     W5 = randn((wu.Co, wu.C, wu.K), 3203, "f16", std=1.0 / math.sqrt(wu.C * wu.K)).to(dev)
+    gy5 = randn((wu.B, wu.Co, wu.Ho, wu.Wo), 3204, "f16", std=0.1).to(dev)
+    gx5 = torch.empty_like(x5)
+    dW5 = torch.empty_like(W5)
+    ws = torch.empty(sgc.disco_fused_conv_bwd_workspace(h_u, wu.B, wu.C, wu.Co), dtype=torch.uint8, device=dev)
     calls = {"fwd": lambda: sgc.disco_fwd(h_fb, x3), "bwd": lambda: sgc.disco_bwd(h_fb, g4),
-             "fused": lambda: sgc.disco_fused_conv(h_u, x5, W5)}
+             "fused": lambda: sgc.disco_fused_conv(h_u, x5, W5),
+             "fused_bwd": lambda: sgc.disco_fused_conv_bwd(h_u, x5, W5, gy5, gx5, dW5, workspace=ws)}
     res = {}
     for op, fn in calls.items():
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        ev = []
-        for _ in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            ev.append((a, b))
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-        w, psi = {"fwd": (wf, psi_fb), "bwd": (wb, psi_fb), "fused": (wu, psi_u)}[op]
-        upd = op_updates(w, psi.nnz)
-        res[op] = {"ms": round(ms, 4), "Gnnz_updates_per_s": round(upd / ms / 1e6, 2)}
+        med, p10, p90 = _timed(torch, np, stream, fn, reps)
+        w, psi = {"fwd": (wf, psi_fb), "bwd": (wb, psi_fb), "fused": (wu, psi_u), "fused_bwd": (wu, psi_u)}[op]
+        upd = op_updates(w, psi.nnz) * (2 if op == "fused_bwd" else 1)
+        r = {"ms_median": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+             "Gnnz_updates_per_s": round(upd / med / 1e6, 2)}
+        if op in ("fused", "fused_bwd"):
+            macs = w.B * w.Ho * w.Wo * wu.Co * w.C * w.K * (2 if op == "fused_bwd" else 1)
+            alg = 2 * upd + 2 * macs
+            r["mfma_tflops_algorithmic"] = round(alg / med / 1e9, 3)
+            r["mfma_frac"] = round(alg / med / 1e9 / PEAK_F16_MFMA_TFLOPS, 4)
+        res[op] = r
+    del x3, g4, x5, W5, gy5, gx5, dW5, ws
+    torch.cuda.empty_cache()
     print(f"[bench] fp16: {res}", file=sys.stderr, flush=True)
     return res
 
 
-def time_page_shapes(sgc, torch, np, dev, stream, reps=3):
+def time_fp32_fused(sgc, torch, np, dev, stream, reps=5):
+    """The fused convolution in fp32 (fp32 contraction on the vector ALUs, einsum on
+    v_mfma_f32_16x16x4_f32) beside the same op in bf16, at the page's 256-channel self-convolution
+    shape: the page's "every precision against its fp32 variant" comparison."""
+    from disco_inputs import WORKLOADS, randn, workload_psi
+
+    w = WORKLOADS["page_self_256x360x720"]
+    psi = workload_psi(w)
+    h = sgc.disco_psi_create(psi, 0)
+    res = {"shape": {"B": w.B, "C": w.C, "Co": w.Co, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo],
+                     "nnz": psi.nnz}}
+    upd = op_updates(w, psi.nnz)
+    macs = w.B * w.Ho * w.Wo * w.Co * w.C * w.K
+    for dt, peak in (("f32", PEAK_FP32_MFMA_TFLOPS), ("bf16", PEAK_BF16_MFMA_TFLOPS)):
+        x = randn((w.B, w.C, w.Hi, w.Wi), 3400, dt).to(dev)
+        W = randn((w.Co, w.C, w.K), 3401, dt, std=1.0 / math.sqrt(w.C * w.K)).to(dev)
+        y = torch.empty((w.B, w.Co, w.Ho, w.Wo), dtype=x.dtype, device=dev)
+        med, p10, p90 = _timed(torch, np, stream, lambda: sgc.disco_fused_conv(h, x, W, y), reps)
+        alg = 2 * upd + 2 * macs
+        res[dt] = {"ms_median": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                   "tflops_algorithmic": round(alg / med / 1e9, 3), "peak_TFLOPs": peak,
+                   "frac": round(alg / med / 1e9 / peak, 4)}
+        del x, W, y
+    h.close()
+    torch.cuda.empty_cache()
+    res["note"] = "f32 against the fp32 matrix peak (the einsum's instruction), bf16 against the bf16 peak"
+    print(f"[bench] fp32 fused: {res}", file=sys.stderr, flush=True)
+    return res
+
+
+def time_valu_gathers(sgc, torch, np, h_fb, tensors, wf, wb, psi_fb, dev, stream, reps=5):
+    """The bf16 forward and backward at 721x1440 on the vector-ALU gathers (the matrix-core kernels
+    switched off with their knobs for these calls only): the LDS-staged gather path that 16-bit
+    data took before the matrix-core kernels, HBM-bound in design."""
+    res = {}
+    x3 = tensors.get("x3")
+    g4 = tensors.get("g4")
+    calls = {}
+    if x3 is not None:
+        calls["fwd"] = ("DISCO_FWD_MFMA", lambda: sgc.disco_fwd(h_fb, x3, tensors["out3"]), wf)
+    if g4 is not None:
+        calls["bwd"] = ("DISCO_BWD_MFMA", lambda: sgc.disco_bwd(h_fb, g4, tensors["gx4"]), wb)
+    for op, (knob, fn, w) in calls.items():
+        old = os.environ.get(knob)
+        os.environ[knob] = "0"
+        try:
+            med, p10, p90 = _timed(torch, np, stream, fn, reps)
+        finally:
+            if old is None:
+                del os.environ[knob]
+            else:
+                os.environ[knob] = old
+        byt = op_bytes(op, w, psi_fb.nnz)
+        upd = op_updates(w, psi_fb.nnz)
+        res[op] = {"ms_median": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                   "GBps": round(byt / med / 1e6, 2), "hbm_frac": round(byt / med / 1e6 / PEAK_HBM_GBS, 4),
+                   "Gnnz_updates_per_s": round(upd / med / 1e6, 2),
+                   "valu_frac": round(2 * upd / med / 1e9 / PEAK_FP32_VALU_TFLOPS, 4)}
+    print(f"[bench] bf16 vector-ALU gathers: {res}", file=sys.stderr, flush=True)
+    return res
+
+
+def time_page_shapes(sgc, torch, np, dev, stream, reps=5):
     """The DISCO page's own benchmark shapes (section "Serial Benchmarks": Gauss-Legendre grids,
-    theta_c = 0.017, K = 9 stand-in basis, batch 1), bf16: fused convolution and its backward."""
+    theta_c = 0.017, K = 9 stand-in basis, batch 1), bf16: fused convolution and its backward
+    (median of `reps`, p10 and p90)."""
     from disco_inputs import WORKLOADS, randn, workload_psi, workload_weight, workload_x
 
     res = {}
@@ -553,20 +626,10 @@ def time_page_shapes(sgc, torch, np, dev, stream, reps=3):
         r = {"shape": {"B": w.B, "C": w.C, "Co": w.Co, "K": w.K, "in": [w.Hi, w.Wi], "out": [w.Ho, w.Wo],
                        "nnz": psi.nnz, "grids": [w.grid_in, w.grid_out]}}
         for op, fn in fns.items():
-            fn()
-            torch.cuda.synchronize()
-            ev = []
-            for _ in range(reps):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                ev.append((a, b))
-            torch.cuda.synchronize()
-            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            ms, p10, p90 = _timed(torch, np, stream, fn, reps)
             alg = (2 * upd + 2 * macs) * (2 if op == "fused_bwd" else 1)
-            r[op] = {"ms": round(ms, 4), "mfma_tflops_algorithmic": round(alg / ms / 1e9, 3),
+            r[op] = {"ms": round(ms, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                     "mfma_tflops_algorithmic": round(alg / ms / 1e9, 3),
                      "mfma_frac": round(alg / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4)}
         res[name] = r
         h.close()
