@@ -330,9 +330,10 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
 
     lib = ctypes.CDLL(os.path.join(ROOT, "sparse_gather_contraction_amd", "libdisco_probes.so"))
     for f in ("disco_probe_read", "disco_probe_copy", "disco_probe_fma", "disco_probe_mfma", "disco_probe_lds",
-              "disco_probe_lds_mfma"):
+              "disco_probe_lds_mfma", "disco_probe_dma_read"):
         getattr(lib, f).restype = ctypes.c_int
     P, S = ctypes.c_void_p, ctypes.c_size_t
+    lib.disco_probe_dma_read.argtypes = [P, S, ctypes.c_int, ctypes.c_int, P]
     lib.disco_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P]
     lib.disco_probe_lds_mfma.argtypes = [ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P]
     lib.disco_probe_read.argtypes = [P, S, P, ctypes.c_int, P]
@@ -351,6 +352,10 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
     nb = buf.numel() * 4
     ms_r = _timed(torch, np, stream, lambda: ok(lib.disco_probe_read(buf.data_ptr(), nb, out.data_ptr(), blocks, sp)),
                   reps)
+    # the direct global -> LDS path (the library's stage loads): 3 GiB, one 4-wave workgroup per CU,
+    # four 1 KiB loads in flight per wave
+    nd = min(nb, 3 << 30)
+    ms_d = _timed(torch, np, stream, lambda: ok(lib.disco_probe_dma_read(buf.data_ptr(), nd, 4, 256, sp)), reps)
     del buf
     src = torch.ones(copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -377,7 +382,9 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
     copy_gbs = 2 * copy_mib * (1 << 20) / ms_c[0] / 1e6
     fma_tf = blocks * 256 * iters * 8 * 2 / ms_f[0] / 1e9
     mfma_tf = blocks * 4 * miters * 4 * (32 * 32 * 16 * 2) / ms_m[0] / 1e9
+    dma_gbs = nd / ms_d[0] / 1e6
     res = {"read_GBps": round(read_gbs, 1), "read_frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
+           "lds_dma_read_GBps": round(dma_gbs, 1), "lds_dma_read_frac_of_peak": round(dma_gbs / PEAK_HBM_GBS, 4),
            "copy_GBps": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
            "fp32_fma_TFLOPs": round(fma_tf, 2), "fp32_fma_frac_of_peak": round(fma_tf / PEAK_FP32_VALU_TFLOPS, 4),
            "bf16_mfma_TFLOPs": round(mfma_tf, 1), "bf16_mfma_frac_of_peak": round(mfma_tf / PEAK_BF16_MFMA_TFLOPS, 4),
@@ -386,7 +393,8 @@ def achievable(torch, np, dev, stream, read_gib=4, copy_mib=1024, reps=5):
            "lds_fed_mfma_TFLOPs": {f"{nb}_psi_words": round(lblocks * 8 * lm_iters * 2 * 32768 / lm_ms[nb] / 1e9, 1)
                                    for nb in (4, 5)},
            "note": f"HIP probes built here: read stream of {read_gib} GiB (16-byte loads), copy of {copy_mib} MiB "
-                   f"(read + write), fp32 FMA loop, bf16 MFMA loop, LDS read loops (bytes per clock per CU at "
+                   f"(read + write), a 3 GiB stream of direct global-to-LDS loads, fp32 FMA loop, bf16 MFMA loop, LDS "
+                   f"read loops (bytes per clock per CU at "
                    f"{CLOCK_HZ / 1e9} GHz), the contraction's LDS-fed MFMA loop; medians of {reps}"}
     print(f"[bench] achievable: {res}", file=sys.stderr, flush=True)
     return res

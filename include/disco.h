@@ -116,7 +116,11 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
  * fp32 accumulation (contraction chunks are rounded to the data type before the
  * MFMA).  F32: fp32 throughout (fp32 psi, an fp32 contraction chunk, the einsum
  * on the fp32 matrix cores) — the fp32 variant the 16-bit ones are compared
- * with (same page, "Test coverage requirements"). */
+ * with (same page, "Test coverage requirements").
+ * Memory: with BF16/F16 data and K < 16 the call takes a temporary of Co * C * 32 bytes from a
+ * memory pool the library keeps per device (stream-ordered: taken and returned on `stream`; the pool
+ * keeps freed memory for reuse until the process ends) to hold W in rows of 16 elements; if none can be
+ * had the kernel stages W element by element instead, with the same result. */
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
 
@@ -138,7 +142,8 @@ disco_status disco_fused_conv_save(disco_psi h, const disco_tensor *x, const dis
  * t: (B, C, K, Ho, Wo), W: (Co, C, K) -> y: (B, Co, Ho, Wo), on the current device (no psi).
  * BF16 and F16 only, K <= 16 (DISCO_ERR_SHAPE otherwise).  Runs the fused kernel's matrix-core
  * einsum tile with t streamed from device memory: fp32 accumulation in a fixed order, y rounded
- * once (RNE), bitwise reproducible run to run.  All tensors are caller-owned; y is overwritten. */
+ * once (RNE), bitwise reproducible run to run.  All tensors are caller-owned; y is overwritten.
+ * K < 16 takes the same stream-ordered W temporary as disco_fused_conv (same fallback). */
 disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_tensor *y, void *stream);
 
 /* Backward of the fused convolution: the gradients of <gy, y> for y = disco_fused_conv(x, W),

@@ -344,6 +344,51 @@ hipStream_t side_stream(int device)
     return streams[device];
 }
 
+// A memory pool per device for short-lived temporaries of one call (stream-ordered: hipMallocFromPoolAsync
+// and hipFreeAsync on the call's stream), created on first use and kept for the life of the process; it
+// keeps freed memory for reuse instead of returning it at each synchronization.  nullptr if it cannot be made.
+hipMemPool_t temp_pool(int device)
+{
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    if (device < 0 || device >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[device]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = device;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        (void)hipGetLastError();
+        pools[device] = pool;
+    }
+    return pools[device];
+}
+
+// W (Co, C, K) with K < 16 in rows of 16 (zeros past K) in a stream-ordered temporary of the device's pool,
+// for the matrix-core kernels' direct W-slice loads; nullptr (and no error left pending) when K is 16,
+// DISCO_PACK_W=0 (a test knob: keep the element-wise W staging) or the temporary cannot be had.  The
+// caller frees a non-null result with hipFreeAsync on the same stream after its launch.
+void *packed_w(int device, const void *W, int64_t Co, int64_t C, int K, hipStream_t stream, hipError_t *err)
+{
+    *err = hipSuccess;
+    if (K >= 16 || Co * C == 0 || getenv_is0("DISCO_PACK_W")) return nullptr;
+    hipMemPool_t pool = temp_pool(device);
+    void *wp = nullptr;
+    if (!pool || hipMallocFromPoolAsync(&wp, (size_t)(Co * C * 32), pool, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    *err = disco::launch_pack_w16(W, wp, (int)Co, (int)C, K, stream);
+    return wp;
+}
+
 bool staged_env_off()
 {
     const char *e = getenv("DISCO_STAGED");  // test knob: "0" forces the plain gather kernel
@@ -846,7 +891,21 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
         m.max_resident_bytes = h->fused.max_resident_bytes;
         m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
         m.save = save ? save->data : nullptr;
-        hipError_t e = disco::launch_fused_mfma(m, (hipStream_t)stream);
+        // K < 16: W's rows of K elements cannot be loaded as 16-byte runs, so a stream-ordered temporary
+        // holds W in rows of 16 (zeros past K) for the kernel's direct W-slice loads; without the
+        // temporary the kernel stages W element by element (same values, same result)
+        hipStream_t sm = (hipStream_t)stream;
+        hipError_t e = hipSuccess;
+        void *wp = packed_w(h->device, W->data, Co, C, h->K, sm, &e);
+        if (wp && e == hipSuccess) {
+            m.W = wp;
+            m.w16 = true;
+        }
+        if (e == hipSuccess) e = disco::launch_fused_mfma(m, sm);
+        if (wp) {
+            const hipError_t ef = hipFreeAsync(wp, sm);
+            if (e == hipSuccess) e = ef;
+        }
         if (e != hipSuccess)
             return fail(DISCO_ERR_HIP, std::string("fused launch failed: ") + hipGetErrorString(e));
         return DISCO_OK;
@@ -929,7 +988,18 @@ disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_te
     a.B = (int32_t)B; a.C = (int32_t)C; a.Co = (int32_t)Co; a.K = (int32_t)K;
     a.HW = HW;
     a.f16 = t->dtype == DISCO_F16;
-    hipError_t e = disco::launch_einsum_mfma(a, (hipStream_t)stream);
+    hipStream_t sm = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    void *wp = packed_w(dev, W->data, Co, C, (int)K, sm, &e);  // K < 16: W in rows of 16 (see packed_w)
+    if (wp && e == hipSuccess) {
+        a.W = wp;
+        a.w16 = true;
+    }
+    if (e == hipSuccess) e = disco::launch_einsum_mfma(a, sm);
+    if (wp) {
+        const hipError_t ef = hipFreeAsync(wp, sm);
+        if (e == hipSuccess) e = ef;
+    }
     if (e != hipSuccess) return fail(DISCO_ERR_HIP, std::string("einsum launch failed: ") + hipGetErrorString(e));
     return DISCO_OK;
 }

@@ -97,9 +97,14 @@ struct FusedMfmaLaunch {
     bool f16;     // fp16 data and psi (adata then holds fp16 psi * 2^e)
     float scale;  // 2^-e for fp16, 1 for bf16
     void *save = nullptr;  // non-null: also write the contraction (B, C, K, Ho, Wo), data type, contiguous
+    bool w16 = false;      // W holds rows of 16 elements (launch_pack_w16 output), not of K
 };
 
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream);
+
+// W (Co, C, K) with K <= 16 into rows of 16 elements (zeros past K), the layout the fused kernel's
+// direct W-slice loads read; Wp holds Co * C * 16 16-bit elements.
+hipError_t launch_pack_w16(const void *W, void *Wp, int Co, int C, int K, hipStream_t stream);
 
 // The fused kernel's contraction alone, out[b, c, k, ho, wo] (K <= 16), over the fused op's plan:
 // each block walks all channels with the latitude's psi resident where it fits.
@@ -127,6 +132,7 @@ struct EinsumLaunch {
     int32_t B, C, Co, K;
     int64_t HW;
     bool f16;
+    bool w16 = false;  // W holds rows of 16 elements (launch_pack_w16 output), not of K
 };
 hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream);
 size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_bytes);

@@ -942,6 +942,33 @@ size_t fused_mfma_lds_bytes(int n_ot, int max_piece_bytes, int max_resident_byte
     return (size_t)n_ot * kCh * 1024 + std::max<size_t>(2 * buf, (size_t)max_resident_bytes);
 }
 
+namespace {
+
+// Wp[(o C + c) 16 + k] = W[(o C + c) K + k] for k < K, else 0: W in the 16-element rows the fused
+// kernel's direct W-slice loads read (one thread per output element).
+__global__ __launch_bounds__(256) void pack_w16_kernel(const bf16_t *__restrict__ W, bf16_t *__restrict__ Wp,
+                                                       int64_t rows, int K)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * 16) return;
+    const int64_t r = i >> 4;
+    const int k = (int)(i & 15);
+    Wp[i] = k < K ? W[r * K + k] : (bf16_t)0;
+}
+
+}  // namespace
+
+hipError_t launch_pack_w16(const void *W, void *Wp, int Co, int C, int K, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)Co * C;
+    if (rows == 0) return hipSuccess;
+    if (K < 1 || K > 16) return hipErrorInvalidValue;
+    const int64_t n = rows * 16;
+    hipLaunchKernelGGL(pack_w16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, (const bf16_t *)W,
+                       (bf16_t *)Wp, rows, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
 {
     if (a.B == 0 || a.Co == 0) return hipSuccess;
@@ -963,7 +990,8 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
     const bool planes16 = ((int64_t)a.Hi * a.Wi) % 8 == 0 && a.Wi % 8 == 0 && ((uintptr_t)a.x % 16) == 0 &&
                           (int64_t)a.Hi * a.Wi * 2 * kCh < ((int64_t)1 << 31);
     const int vec_x = planes16 ? 1 : 0;
-    const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
+    // W rows of 16 elements (K = 16, or W packed by launch_pack_w16): the slice arrives by direct loads
+    const int vec_w = ((a.K == 16 || a.w16) && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
     const int vec_y = (a.Wo % 8 == 0 && ((uintptr_t)a.y % 16) == 0) ? 1 : 0;
     const int64_t x_bs = (int64_t)a.C * a.Hi * a.Wi;
     const int64_t save_bs = (int64_t)a.C * a.K * a.Ho * a.Wo;  // save is (B, C, K, Ho, Wo), contiguous
@@ -1260,7 +1288,8 @@ hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream)
     // direct loads: 16-byte aligned runs, and one chunk's channels addressable with 32-bit offsets
     const int vec_t = (a.HW % 8 == 0 && ((uintptr_t)a.t % 16) == 0 &&
                        (int64_t)2 * kEch * a.K * a.HW < ((int64_t)1 << 31)) ? 1 : 0;
-    const int vec_w = (a.K == 16 && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
+    // W rows of 16 elements (K = 16, or W packed by launch_pack_w16): the slice arrives by direct loads
+    const int vec_w = ((a.K == 16 || a.w16) && ((uintptr_t)a.W % 16) == 0 && (int64_t)a.Co * a.C * 32 < ((int64_t)1 << 31)) ? 1 : 0;
     const int vec_y = (a.HW % 8 == 0 && ((uintptr_t)a.y % 16) == 0) ? 1 : 0;
 #define DISCO_EINSUM_LAUNCH(N, F16)                                                                              \
     hipLaunchKernelGGL((einsum_mfma_kernel<N, F16>), dim3((unsigned)nblk), dim3(kThreads), lds, stream,           \

@@ -9,6 +9,9 @@
 //   * bf16 MFMA loop: four independent v_mfma_f32_32x32x16_bf16 accumulators per wave;
 //   * LDS read loop: 4-, 8- or 16-byte LDS reads per lane over a 64 KiB array, consecutive lanes
 //     on consecutive words (no bank conflicts), eight waves per workgroup, one workgroup per CU;
+//   * direct global -> LDS read stream: every 16-byte unit of a buffer loaded once with
+//     buffer_load_dwordx4 ... lds into a per-wave LDS ring, at most `inflight` loads in flight per
+//     wave (the path the library's stage loads take);
 //   * LDS-fed MFMA loop: per step two 16-byte reads and `nb32` 4-byte reads per lane feeding two
 //     v_mfma_f32_32x32x16_bf16 (the operand traffic of a contraction block of the fused kernel:
 //     one psi operand in 4-byte words, the x runs of two channels), loads issued one step ahead.
@@ -23,6 +26,7 @@ hipError_t disco_probe_mfma(int iters, float *out, int blocks, void *stream);
 hipError_t disco_probe_lds(int iters, int width, float *out, int blocks, void *stream);
 hipError_t disco_probe_lds_mfma(int iters, int nb32, float *out, int blocks, void *stream);
 hipError_t disco_probe_lds_mfma_q(int iters, int p, int q, int depth, int threads, float *out, int blocks, void *stream);
+hipError_t disco_probe_dma_read(const void *buf, size_t bytes, int inflight, int blocks, void *stream);
 }
 
 namespace {
@@ -235,6 +239,30 @@ __global__ __launch_bounds__(TH) void lds_mfma_q_kernel(int iters, float *out)
     out[blockIdx.x * TH + threadIdx.x] = t;
 }
 
+typedef void __attribute__((address_space(3))) *lds_ptr_t;
+
+// Wave w of a workgroup streams 1 KiB units u = (blockIdx * waves + w) + k * (gridDim * waves) of the
+// buffer into LDS slot k % RING of its own 16 KiB area; the wait before each load keeps at most
+// INFL - 1 older loads in flight.  The buffer resource bounds every read (units past the end read 0).
+template <int INFL>
+__global__ __launch_bounds__(256) void dma_read_kernel(const void *buf, uint32_t bytes, uint32_t n_units)
+{
+    constexpr int RING = 16;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * RING * 1024];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(buf), 0, (int)bytes, 0x00020000);
+    const uint32_t stride = gridDim.x * 4u;
+    uint32_t u = blockIdx.x * 4u + (uint32_t)wave;
+    unsigned char *area = lds + wave * RING * 1024;
+    for (int k = 0; u < n_units; ++k, u += stride) {
+        if constexpr (INFL == 4) __builtin_amdgcn_s_waitcnt(0x0f73);  // vmcnt <= 3
+        else if constexpr (INFL == 8) __builtin_amdgcn_s_waitcnt(0x0f77);  // vmcnt <= 7
+        else __builtin_amdgcn_s_waitcnt(0x0f7f);  // vmcnt <= 15
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(area + 1024 * (k % RING)), 16, u * 1024u + 16u * (uint32_t)lane, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 }  // namespace
 
 // bytes must be a multiple of 16 and the buffers 16-byte aligned (the caller passes torch tensors
@@ -311,4 +339,17 @@ hipError_t disco_probe_lds_mfma_q(int iters, int p, int q, int depth, int thread
     PROBE_Q(2, 4, 1, 256) PROBE_Q(4, 1, 2, 256) PROBE_Q(4, 1, 2, 512)
 #undef PROBE_Q
     return hipErrorInvalidValue;
+}
+
+// bytes: a multiple of 1024 below 2^32; inflight 4, 8 or 16; 256 threads per workgroup.
+hipError_t disco_probe_dma_read(const void *buf, size_t bytes, int inflight, int blocks, void *stream)
+{
+    if (bytes % 1024 != 0 || bytes >= ((size_t)1 << 32) || blocks <= 0 || (uintptr_t)buf % 16 != 0) return hipErrorInvalidValue;
+    const hipStream_t st = (hipStream_t)stream;
+    const uint32_t n = (uint32_t)(bytes / 1024);
+    if (inflight == 4) hipLaunchKernelGGL(dma_read_kernel<4>, dim3(blocks), dim3(256), 0, st, buf, (uint32_t)bytes, n);
+    else if (inflight == 8) hipLaunchKernelGGL(dma_read_kernel<8>, dim3(blocks), dim3(256), 0, st, buf, (uint32_t)bytes, n);
+    else if (inflight == 16) hipLaunchKernelGGL(dma_read_kernel<16>, dim3(blocks), dim3(256), 0, st, buf, (uint32_t)bytes, n);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }

@@ -1023,3 +1023,51 @@ def test_oversized_launch_is_refused_and_writes_nothing(monkeypatch):
     sgc.disco_fwd(h, x, o)
     torch.cuda.synchronize()
     assert torch.equal(y, ref_y) and torch.equal(o, ref_o)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fused_with_packed_w_equals_elementwise_w_staging(dtype, monkeypatch):
+    """K < 16: the fused op packs W into 16-element rows in a stream-ordered temporary and loads its W
+    slices as 16-byte runs; DISCO_PACK_W=0 keeps the element-wise staging.  Both multiply the same values
+    in the same order, so y (and the kept contraction) must be bitwise equal, and match the oracle; two
+    output-channel blocks (Co = 300) and a ragged channel count."""
+    psi = build_psi(19, 144, 19, 72, 0.7, 3, 3)  # K = 9
+    assert psi.K == 9
+    h = gpu_psi(psi)
+    td = torch.float16 if dtype == "f16" else torch.bfloat16
+    x = randn((2, 7, 19, 144), 4900, dtype).to(DEV)
+    W = randn((300, 7, 9), 4901, dtype, std=0.2).to(DEV)
+    y_pack, o_pack = sgc.disco_fused_conv_save(h, x, W)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("DISCO_PACK_W", "0")
+    y_elem, o_elem = sgc.disco_fused_conv_save(h, x, W)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("DISCO_PACK_W")
+    assert y_pack.dtype == td
+    assert torch.equal(y_pack, y_elem) and torch.equal(o_pack, o_elem)
+    xc, Wc = x.cpu(), W.cpu()
+    ref = oracle.fused(psi, xc, Wc)
+    nrm = oracle.fused(psi, xc.abs(), Wc.abs(), abs_mode=True)
+    assert normalised_error(y_pack, ref, nrm) <= (2e-3 if dtype == "f16" else TOL["bf16"])
+    y2 = sgc.disco_fused_conv(h, x, W)  # the plain op takes the same path
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y_pack)
+
+
+@pytest.mark.parametrize("cfg", [(2, 5, 40, 3, 7, 37, "bf16"), (2, 9, 300, 8, 5, 48, "bf16"), (1, 12, 256, 9, 4, 96, "f16")])
+def test_einsum_with_packed_w_equals_elementwise_w_staging(cfg, monkeypatch):
+    """K < 16: disco_einsum packs W into 16-element rows (stream-ordered temporary) and takes the direct
+    W-slice loads; DISCO_PACK_W=0 keeps the element-wise staging.  Same values, same order: bitwise equal."""
+    B, C, Co, K, Ho, Wo, dt = cfg
+    t = randn((B, C, K, Ho, Wo), 3300 + C, dt).to(DEV)
+    W = randn((Co, C, K), 3400 + C, dt, std=1.0 / np.sqrt(C * K)).to(DEV)
+    y_pack = sgc.disco_einsum(W, t)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("DISCO_PACK_W", "0")
+    y_elem = sgc.disco_einsum(W, t)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("DISCO_PACK_W")
+    assert torch.equal(y_pack, y_elem)
+    ref = oracle.einsum(W.cpu(), t.cpu())
+    nrm = oracle.einsum(W.cpu().abs(), t.cpu().abs(), abs_mode=True)
+    assert normalised_error(y_pack.cpu(), ref, nrm) <= TOL_EIN[dt]
