@@ -59,6 +59,27 @@ template <> struct Elem<float> {  // fp32 data (the contraction's loads only; th
     static __device__ __forceinline__ float to_f32(float v) { return v; }
 };
 
+// NB entries of a segment from entry t: the NB x loads go out together, then the multiply-adds in
+// entry order; base = (j0 + t + wo) mod Wo on entry, advanced past the NB entries.
+template <int NB, int G, typename T>
+__device__ __forceinline__ void contract_batch(const T *__restrict__ row, const float *__restrict__ v, int t, int &base,
+                                               int Wo, int in_stride, bool valid, float *acc)
+{
+    float xv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        int idx = base + u;
+        while (idx >= Wo) idx -= Wo;
+        xv[u] = valid ? Elem<T>::to_f32(row[(int64_t)in_stride * idx]) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = fmaf(v[(t + u) * G + g], xv[u], acc[g]);
+    base += NB;
+    while (base >= Wo) base -= Wo;
+}
+
 template <int G, typename T>
 __device__ __forceinline__ void contract_item(const T *__restrict__ plane, const Item &it,
                                               const Seg *__restrict__ segs, const float *__restrict__ vals,
@@ -70,15 +91,19 @@ __device__ __forceinline__ void contract_item(const T *__restrict__ plane, const
         const Seg sg = segs[q];
         const float *v = vals + sg.val_off;
         const T *row = plane + sg.in_off;
-        for (int t = 0; t < sg.m; ++t) {
-            int base = sg.j0 + t;
-            if (base >= Wo) base -= Wo;
-            int idx = base + wo;
-            if (idx >= Wo) idx -= Wo;
-            const float xv = valid ? Elem<T>::to_f32(row[(int64_t)in_stride * idx]) : 0.0f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = fmaf(v[t * G + g], xv, acc[g]);
+        int base = sg.j0 + wo;  // (j0 + t + wo) mod Wo at t = 0
+        while (base >= Wo) base -= Wo;
+        int t = 0;
+        for (; t + 8 <= sg.m; t += 8) contract_batch<8, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+        if (t + 4 <= sg.m) {
+            contract_batch<4, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+            t += 4;
         }
+        if (t + 2 <= sg.m) {
+            contract_batch<2, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+            t += 2;
+        }
+        if (t < sg.m) contract_batch<1, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
     }
 }
 
