@@ -55,55 +55,117 @@ template <> struct Elem<f16_t> {
     }
 };
 
-template <> struct Elem<float> {  // fp32 data (the contraction's loads only; the einsum has its own kernel)
+template <> struct Elem<float> {  // fp32 data (the contraction's loads and tile; the einsum has its own kernel)
     static __device__ __forceinline__ float to_f32(float v) { return v; }
+    static __device__ __forceinline__ float from_f32(float v) { return v; }
 };
 
-// NB entries of a segment from entry t: the NB x loads go out together, then the multiply-adds in
-// entry order; base = (j0 + t + wo) mod Wo on entry, advanced past the NB entries.
-template <int NB, int G, typename T>
-__device__ __forceinline__ void contract_batch(const T *__restrict__ row, const float *__restrict__ v, int t, int &base,
-                                               int Wo, int in_stride, bool valid, float *acc)
+// NB entries of a segment from entry t, for NP channel planes at once: the NB * NP x loads go out
+// together, then the multiply-adds in entry order; base = (j0 + t + wo) mod Wo on entry, advanced past
+// the NB entries.
+template <int NB, int NP, int G, typename T>
+__device__ __forceinline__ void contract_batch(const T *const (&row)[NP], const float *__restrict__ v, int t, int &base,
+                                               int Wo, int in_stride, const bool (&valid)[NP],
+                                               float (&acc)[NP][kMaxGroup])
 {
-    float xv[NB];
+    float xv[NP][NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
         int idx = base + u;
         while (idx >= Wo) idx -= Wo;
-        xv[u] = valid ? Elem<T>::to_f32(row[(int64_t)in_stride * idx]) : 0.0f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) xv[p][u] = valid[p] ? Elem<T>::to_f32(row[p][(int64_t)in_stride * idx]) : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[g] = fmaf(v[(t + u) * G + g], xv[u], acc[g]);
+        for (int g = 0; g < G; ++g) {
+            const float w = v[(t + u) * G + g];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) acc[p][g] = fmaf(w, xv[p][u], acc[p][g]);
+        }
     base += NB;
     while (base >= Wo) base -= Wo;
 }
 
-template <int G, typename T>
-__device__ __forceinline__ void contract_item(const T *__restrict__ plane, const Item &it,
-                                              const Seg *__restrict__ segs, const float *__restrict__ vals,
-                                              int Wo, int in_stride, int wo, bool valid, float *acc)
+// One item of the forward plan for NP channel planes at longitude wo: acc[p][g] = row g of the item,
+// summed over its segments' entries in order.
+template <int NP, int G, typename T>
+__device__ __forceinline__ void contract_item(const T *const (&plane)[NP], const Item &it,
+                                              const Seg *__restrict__ segs, const float *__restrict__ vals, int Wo,
+                                              int in_stride, int wo, const bool (&valid)[NP],
+                                              float (&acc)[NP][kMaxGroup])
 {
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[p][g] = 0.0f;
     for (int q = it.seg_begin; q < it.seg_end; ++q) {
         const Seg sg = segs[q];
         const float *v = vals + sg.val_off;
-        const T *row = plane + sg.in_off;
+        const T *row[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) row[p] = plane[p] + sg.in_off;
         int base = sg.j0 + wo;  // (j0 + t + wo) mod Wo at t = 0
         while (base >= Wo) base -= Wo;
         int t = 0;
-        for (; t + 8 <= sg.m; t += 8) contract_batch<8, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+        for (; t + 8 <= sg.m; t += 8) contract_batch<8, NP, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
         if (t + 4 <= sg.m) {
-            contract_batch<4, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+            contract_batch<4, NP, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
             t += 4;
         }
         if (t + 2 <= sg.m) {
-            contract_batch<2, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+            contract_batch<2, NP, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
             t += 2;
         }
-        if (t < sg.m) contract_batch<1, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+        if (t < sg.m) contract_batch<1, NP, G, T>(row, v, t, base, Wo, in_stride, valid, acc);
+    }
+}
+
+// The chunk's contraction (channels c0 .. c0 + ccn - 1) into the LDS tile [pixel][c K + k] (S: the
+// tile's element type, STRIDE its row length): per pass over eight of the chunk's channels, thread
+// (cl, px) handles channels cl and cl + 4 at longitude wo0 + px — two independent chains of loads in
+// flight — and writes the tile type's rounding of each sum.
+template <typename T, typename S, int STRIDE>
+__device__ __forceinline__ void contract_chunk(const T *__restrict__ xb, S *__restrict__ tile,
+                                               const Item *__restrict__ items, const Seg *__restrict__ segs,
+                                               const float *__restrict__ vals, int it_begin, int it_end,
+                                               int64_t plane_sz, int c0, int ccn, int CC, int K, int Wo, int HoWo,
+                                               int in_stride, int wo0, int tid)
+{
+    static_assert(kThreads == 4 * kPx, "four channels of kPx pixels per thread row");
+    constexpr int NP = 2;
+    const int cl0 = tid / kPx, px = tid - cl0 * kPx;
+    const int wo = wo0 + px;
+    for (int cb = 0; cb < CC; cb += 4 * NP) {
+        const T *plane[NP];
+        bool valid[NP];
+        int cl[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            cl[p] = cb + cl0 + 4 * p;
+            valid[p] = cl[p] < ccn && wo < Wo;
+            plane[p] = xb + (int64_t)(c0 + (cl[p] < ccn ? cl[p] : 0)) * plane_sz;
+        }
+        for (int ii = it_begin; ii < it_end; ++ii) {
+            const Item it = items[ii];
+            float a[NP][kMaxGroup];
+            switch (it.G) {
+            case 1: contract_item<NP, 1, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+            case 2: contract_item<NP, 2, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+            case 3: contract_item<NP, 3, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+            default: contract_item<NP, 4, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (cl[p] < CC) {
+                    for (int g = 0; g < it.G; ++g) {
+                        const int k = it.out_off[g] / HoWo;
+                        tile[px * STRIDE + cl[p] * K + k] = Elem<S>::from_f32(valid[p] ? a[p][g] : 0.0f);
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -143,35 +205,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int npass = (CC * kPx + kThreads - 1) / kThreads;
     for (int c0 = 0; c0 < C; c0 += CC) {
         const int ccn = min(CC, C - c0);
         __syncthreads();  // the previous chunk's MFMA reads of `tile` are done
         // ---- contraction of channels [c0, c0+ccn) into tile[px][cl*K + k] ----
-        for (int pass = 0; pass < npass; ++pass) {
-            const int pair = tid + kThreads * pass;
-            const int cl = pair / kPx;
-            const int px = pair - cl * kPx;
-            const int wo = wo0 + px;
-            const bool valid = (cl < ccn) && (wo < Wo);
-            const T *plane = x + ((int64_t)b * C + (c0 + (cl < ccn ? cl : 0))) * plane_sz;
-            for (int ii = it_begin; ii < it_end; ++ii) {
-                const Item it = items[ii];
-                float a[kMaxGroup];
-                switch (it.G) {
-                case 1: contract_item<1, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                case 2: contract_item<2, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                case 3: contract_item<3, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                default: contract_item<4, T>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                }
-                if (cl < CC) {
-                    for (int g = 0; g < it.G; ++g) {
-                        const int k = it.out_off[g] / HoWo;
-                        tile[px * kLdsStride + cl * K + k] = Elem<T>::from_f32(valid ? a[g] : 0.0f);
-                    }
-                }
-            }
-        }
+        contract_chunk<T, T, kLdsStride>(x + (int64_t)b * C * plane_sz, tile, items, segs, vals, it_begin, it_end,
+                                         plane_sz, c0, ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
         // rows past the chunk's (c, k) range are zero
         for (int e = tid; e < kPx * kR; e += kThreads) {
             const int px = e / kR, r = e - px * kR;
@@ -258,34 +297,11 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int npass = (CC * kPx + kThreads - 1) / kThreads;
     for (int c0 = 0; c0 < C; c0 += CC) {
         const int ccn = min(CC, C - c0);
         __syncthreads();  // the previous chunk's MFMA reads of `tile` are done
-        for (int pass = 0; pass < npass; ++pass) {
-            const int pair = tid + kThreads * pass;
-            const int cl = pair / kPx;
-            const int px = pair - cl * kPx;
-            const int wo = wo0 + px;
-            const bool valid = (cl < ccn) && (wo < Wo);
-            const float *plane = x + ((int64_t)b * C + (c0 + (cl < ccn ? cl : 0))) * plane_sz;
-            for (int ii = it_begin; ii < it_end; ++ii) {
-                const Item it = items[ii];
-                float a[kMaxGroup];
-                switch (it.G) {
-                case 1: contract_item<1, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                case 2: contract_item<2, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                case 3: contract_item<3, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                default: contract_item<4, float>(plane, it, segs, vals, Wo, in_stride, wo, valid, a); break;
-                }
-                if (cl < CC) {
-                    for (int g = 0; g < it.G; ++g) {
-                        const int k = it.out_off[g] / HoWo;
-                        tile[px * kLdsStride32 + cl * K + k] = valid ? a[g] : 0.0f;
-                    }
-                }
-            }
-        }
+        contract_chunk<float, float, kLdsStride32>(x + (int64_t)b * C * plane_sz, tile, items, segs, vals, it_begin,
+                                                   it_end, plane_sz, c0, ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
         for (int e = tid; e < kPx * kR; e += kThreads) {
             const int px = e / kR, r = e - px * kR;
             if (r >= ccn * K) tile[px * kLdsStride32 + r] = 0.0f;
