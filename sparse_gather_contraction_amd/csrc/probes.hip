@@ -12,6 +12,9 @@
 //   * direct global -> LDS read stream: every 16-byte unit of a buffer loaded once with
 //     buffer_load_dwordx4 ... lds into a per-wave LDS ring, at most `inflight` loads in flight per
 //     wave (the path the library's stage loads take);
+//   * direct global -> LDS row-piece stream: the buffer read as `rows` rows of equal length, each
+//     workgroup step taking one `piece`-byte piece of every row at the workgroup's column tile (the
+//     shape of a GEMM operand tile whose rows lie far apart), four waves, double-buffered steps;
 //   * LDS-fed MFMA loop: per step two 16-byte reads and `nb32` 4-byte reads per lane feeding two
 //     v_mfma_f32_32x32x16_bf16 (the operand traffic of a contraction block of the fused kernel:
 //     one psi operand in 4-byte words, the x runs of two channels), loads issued one step ahead.
@@ -27,6 +30,7 @@ hipError_t disco_probe_lds(int iters, int width, float *out, int blocks, void *s
 hipError_t disco_probe_lds_mfma(int iters, int nb32, float *out, int blocks, void *stream);
 hipError_t disco_probe_lds_mfma_q(int iters, int p, int q, int depth, int threads, float *out, int blocks, void *stream);
 hipError_t disco_probe_dma_read(const void *buf, size_t bytes, int inflight, int blocks, void *stream);
+hipError_t disco_probe_dma_rows(const void *buf, size_t bytes, int rows, int piece, int blocks, void *stream);
 }
 
 namespace {
@@ -263,6 +267,32 @@ __global__ __launch_bounds__(256) void dma_read_kernel(const void *buf, uint32_t
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Workgroup g walks column tiles g, g + gridDim, ... of a row-major buffer of `rows` rows of
+// `row_bytes` bytes: per tile it loads the `piece` bytes at column tile * piece of every row into its
+// LDS stage — the tile's pieces taken as one run of 16-byte lane units, 1 KiB per wave instruction,
+// waves in turn (with 512-byte pieces a wave instruction covers two rows) — keeping at most 15 loads
+// in flight per wave.  Every offset is below rows * row_bytes; LDS offsets wrap inside the stage.
+__global__ __launch_bounds__(256) void dma_rows_kernel(const void *buf, uint32_t bytes, int rows, uint32_t row_bytes,
+                                                       int piece, int n_tiles)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][32768];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(buf), 0, (int)bytes, 0x00020000);
+    const int n_inst = rows * piece / 1024;
+    int k = 0;
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x, ++k) {
+        unsigned char *stage = lds[k & 1];
+        for (int u = wave; u < n_inst; u += 4) {
+            __builtin_amdgcn_s_waitcnt(0x0f7f);  // vmcnt <= 15: bounded in flight
+            const uint32_t b = 1024u * (uint32_t)u + 16u * (uint32_t)lane;  // byte in the tile's run of pieces
+            const uint32_t r = b / (uint32_t)piece, w = b - r * (uint32_t)piece;
+            const uint32_t off = r * row_bytes + (uint32_t)tile * (uint32_t)piece + w;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + ((1024 * u) & 32767)), 16, off, 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 }  // namespace
 
 // bytes must be a multiple of 16 and the buffers 16-byte aligned (the caller passes torch tensors
@@ -351,5 +381,20 @@ hipError_t disco_probe_dma_read(const void *buf, size_t bytes, int inflight, int
     else if (inflight == 8) hipLaunchKernelGGL(dma_read_kernel<8>, dim3(blocks), dim3(256), 0, st, buf, (uint32_t)bytes, n);
     else if (inflight == 16) hipLaunchKernelGGL(dma_read_kernel<16>, dim3(blocks), dim3(256), 0, st, buf, (uint32_t)bytes, n);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// rows x (bytes / rows) buffer read in pieces of `piece` bytes (a multiple of 16 dividing the row
+// length, rows * piece a multiple of 1024); bytes below 2^32.
+hipError_t disco_probe_dma_rows(const void *buf, size_t bytes, int rows, int piece, int blocks, void *stream)
+{
+    if (rows <= 0 || piece <= 0 || piece % 16 != 0 || ((int64_t)rows * piece) % 1024 != 0 || bytes >= ((size_t)1 << 32) ||
+        bytes % rows != 0 || blocks <= 0)
+        return hipErrorInvalidValue;
+    const size_t row_bytes = bytes / rows;
+    if (row_bytes % piece != 0 || (uintptr_t)buf % 16 != 0) return hipErrorInvalidValue;
+    const int n_tiles = (int)(row_bytes / piece);
+    hipLaunchKernelGGL(dma_rows_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, buf, (uint32_t)bytes, rows,
+                       (uint32_t)row_bytes, piece, n_tiles);
     return hipGetLastError();
 }
