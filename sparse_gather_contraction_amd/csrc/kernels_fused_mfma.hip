@@ -1034,9 +1034,10 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
 // Workgroup = (b, 256 positions, up to 256 output channels), eight waves; wave w takes positions
 // p0 + 64 (w % 4) + 2n + ph (n < 32, ph = 0, 1: the two MFMA column sets) and output-channel tiles
 // h2 NOTH .. + NOTH - 1 (h2 = w / 4), fp32 accumulators in registers for all channels.  A step
-// covers kEch input channels; its stage holds the W slice (A operand order, as in the fused
-// kernel) and the t tile [channel][basis][256 positions], both brought in by direct global->LDS
-// loads through a ring of kEring stages issued kEring - 1 steps ahead.  A lane's B operand (basis
+// covers kEch input channels: the W slice (A operand order, as in the fused kernel) and the t tile
+// [channel][basis][256 positions] come in by direct global->LDS loads, the t tiles through a ring of
+// three stages issued two steps ahead (the t stream is the op's bound, and its rate follows the bytes
+// in flight) and the W slices through a ring of two issued one step ahead.  A lane's B operand (basis
 // 8 hh .. 8 hh + 7 at one position) is assembled from eight 4-byte LDS words, each holding the two
 // neighbouring positions of both column sets.  The 16-byte units of a tile row are XOR-swizzled by
 // 8 on rows whose basis index has bit 3 set, so the two lane halves (basis 0..7 and 8..15) read
@@ -1048,7 +1049,8 @@ hipError_t launch_fused_mfma(const FusedMfmaLaunch &a, hipStream_t stream)
 namespace {
 
 constexpr int kEch = 4;                                  // input channels per step
-constexpr int kEring = 2;                                // stages in the ring
+constexpr int kTring = 3;                                // t tile stages (issued two steps ahead)
+constexpr int kWring = 2;                                // W slice stages (issued one step ahead)
 constexpr int kTileBytes = kEch * 16 * kFusedSpan * 2;   // 32 KiB
 constexpr int kTileLoads = kTileBytes / 16 / kThreads;   // direct loads per thread per tile
 
@@ -1174,8 +1176,7 @@ __global__ __launch_bounds__(kThreads) void einsum_mfma_kernel(const bf16_t *__r
 {
     constexpr int NOTH = NOT / 2;
     constexpr int kW = NOT * kEch * 1024;
-    constexpr int kStage = kW + kTileBytes;
-    // LDS: ring of kEring stages [W slice][t tile]
+    // LDS: [W slice ring: kWring x kW][t tile ring: kTring x kTileBytes]
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     int bid = blockIdx.x;
@@ -1205,33 +1206,34 @@ __global__ __launch_bounds__(kThreads) void einsum_mfma_kernel(const bf16_t *__r
 #pragma unroll
             for (int a = 0; a < 16; ++a) yacc[ph][j][a] = 0.0f;
 
-    // Per step a thread issues exactly kLoads direct loads when both operands load directly and
-    // NOT = 8 (W: 8 kEch units over 8 waves; t: kTileLoads), so "at most kLoads * m in flight"
-    // means that every step but the next m has landed.  Otherwise wait for everything.
-    constexpr int kLoads = NOT * kEch / kWaves + kTileLoads;
-    static_assert(kEring <= 4, "the waits below cover up to two steps in flight");
+    // Step st's stage: W slice st (issued during step st - 1, or before the loop) and t tile st (issued
+    // during step st - 2).  Issue order is W slice st + 1, then t tile st + 2, so when step st begins
+    // only t tile st + 1 was issued after everything it needs; with direct loads for both operands and
+    // NOT = 8 a thread issues exactly kTileLoads loads per t tile, so "at most kTileLoads in flight"
+    // means step st's operands have landed.  Otherwise wait for everything.
     const bool ring = vec && c.vec_w && NOT == 8;
     const int nsteps = (C + kEch - 1) / kEch;
-    auto issue = [&](int st) {
-        unsigned char *dst = smem + (st % kEring) * kStage;
-        stage_w_ein(c, kEch * st, dst);
-        stage_tile(c, t, HW, p0, kEch * st, vec, dst + kW);
-    };
-    for (int st = 0; st < kEring - 1 && st < nsteps; ++st) issue(st);
+    unsigned char *const wring = smem;
+    unsigned char *const tring = smem + kWring * kW;
+    auto issue_w = [&](int st) { stage_w_ein(c, kEch * st, wring + (st % kWring) * kW); };
+    auto issue_t = [&](int st) { stage_tile(c, t, HW, p0, kEch * st, vec, tring + (st % kTring) * kTileBytes); };
+    if (nsteps > 0) {
+        issue_w(0);
+        issue_t(0);
+    }
+    if (nsteps > 1) issue_t(1);
     for (int st = 0; st < nsteps; ++st) {
         // A bare barrier: __syncthreads() would add a workgroup release fence, and the compiler makes
         // such a fence wait for every direct load into LDS still in flight (the later steps' too).
         // The compiler-level fences keep LDS accesses on their side of the barrier.
-        const int ahead = ring ? min(kEring - 2, nsteps - 1 - st) : 0;  // steps issued after this one
-        if (ahead == 2) wait_loads<2 * kLoads>();
-        else if (ahead == 1) wait_loads<kLoads>();
+        if (ring && st + 1 < nsteps) wait_loads<kTileLoads>();  // t tile st + 1 may stay in flight
         else __builtin_amdgcn_s_waitcnt(0);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // everyone's loads have landed; every wave is done with step st - 1
         asm volatile("" ::: "memory");
-        if (st + kEring - 1 < nsteps) issue(st + kEring - 1);  // into step st - 1's stage
-        const unsigned char *cur = smem + (st % kEring) * kStage;
-        einsum_chunk<NOTH, F16>(cur + kW, cur, c.lane, pp, h2, yacc);
+        if (st + 1 < nsteps) issue_w(st + 1);  // into step st - 1's W slot
+        if (st + 2 < nsteps) issue_t(st + 2);  // into step st - 1's t slot
+        einsum_chunk<NOTH, F16>(tring + (st % kTring) * kTileBytes, wring + (st % kWring) * kW, c.lane, pp, h2, yacc);
     }
     __builtin_amdgcn_s_waitcnt(0);  // nothing in flight before the ring's space is reused
 
@@ -1275,7 +1277,7 @@ hipError_t launch_einsum_mfma(const EinsumLaunch &a, hipStream_t stream)
     const int n_ob = (a.Co + kMaxOt * 32 - 1) / (kMaxOt * 32);
     const int n_ot1 = std::min(kMaxOt, (a.Co + 31) / 32);
     const int n_ot = n_ot1 <= 2 ? 2 : n_ot1 <= 4 ? 4 : 8;  // tiles past Co hold zero W
-    const size_t lds = (size_t)kEring * ((size_t)n_ot * kEch * 1024 + kTileBytes);  // 160 KiB at 256 channels
+    const size_t lds = (size_t)kWring * n_ot * kEch * 1024 + (size_t)kTring * kTileBytes;  // 160 KiB at 256 channels
     const void *fn = a.f16 ? (n_ot == 2   ? (const void *)einsum_mfma_kernel<2, true>
                               : n_ot == 4 ? (const void *)einsum_mfma_kernel<4, true>
                                           : (const void *)einsum_mfma_kernel<8, true>)
