@@ -289,6 +289,18 @@ def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
         ev.append((a, b))
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the same GEMM through the ROCm BLAS library behind torch.matmul (a reference point for this
+    # shape: bf16 in and out, one product per batch, contiguous operands)
+    W2 = W.reshape(w.Co, w.C * w.K)
+    tb = [t[b].reshape(w.C * w.K, w.Ho * w.Wo) for b in range(w.B)]
+    yb = [y[b].reshape(w.Co, w.Ho * w.Wo) for b in range(w.B)]
+
+    def lib_gemm():
+        for b in range(w.B):
+            torch.matmul(W2, tb[b], out=yb[b])
+
+    lib_ms, lib_p10, lib_p90 = _timed(torch, np, stream, lib_gemm, 5)
+    del tb, yb
     macs = w.B * w.Ho * w.Wo * w.Co * w.C * w.K
     byt = 2 * (t.numel() + W.numel() + y.numel())
     del t, y
@@ -298,8 +310,12 @@ def time_einsum(sgc, torch, np, w, tensors, dev, stream, warm=2, reps=10):
            "mfma_frac": round(2 * macs / ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
            "bytes": byt, "GBps": round(byt / ms / 1e6, 2), "hbm_frac": round(byt / ms / 1e6 / PEAK_HBM_GBS, 4),
            "gemm_mkn": [w.Co, w.C * w.K, w.B * w.Ho * w.Wo], "traffic": counter_traffic("einsum"),
-           "operand": "bf16 contraction (2,256,16,721,1440) in HBM, W (256,256,16), y (2,256,721,1440)"}
-    print(f"[bench] einsum alone: {ms:.3f} ms ({res['mfma_tflops']} TFLOP/s, {res['GBps']} GB/s)",
+           "operand": "bf16 contraction (2,256,16,721,1440) in HBM, W (256,256,16), y (2,256,721,1440)",
+           "library_gemm": {"ms_median": round(lib_ms, 4), "ms_p10_p90": [round(lib_p10, 4), round(lib_p90, 4)],
+                            "mfma_frac": round(2 * macs / lib_ms / 1e9 / PEAK_BF16_MFMA_TFLOPS, 4),
+                            "what": "torch.matmul (ROCm BLAS) on the same GEMM, one product per batch, bf16 in/out"}}
+    print(f"[bench] einsum alone: {ms:.3f} ms ({res['mfma_tflops']} TFLOP/s, {res['GBps']} GB/s); "
+          f"library GEMM {lib_ms:.3f} ms",
           file=sys.stderr, flush=True)
     return res
 
