@@ -155,9 +155,12 @@ disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_te
  * x: (B, C, Hi, Wi), W: (Co, C, K), gy: (B, Co, Ho, Wo) -> gx: (B, C, Hi, Wi), dW: (Co, C, K).
  * BF16 and F16; Co and Ho*Wo must be multiples of 8, K <= 256, and one batch of gy, of a channel
  * chunk of g, and W must each stay below 2 GiB (the matrix-core loads address 32-bit offsets).
- * Computed in channel chunks of g (the data type, on the matrix cores), the transpose contraction,
- * the forward contraction (the data type) and a split product for dW whose fp32 partials are summed
- * in a fixed order: results are bitwise reproducible run to run.  gx and dW must not overlap any
+ * gx: when Wi = Wo and K <= 16, gx[b,c] = sum_{o,k} W[o,c,k] (F_k^T gy[b,o]) is the fused convolution
+ * of gy over the per-basis transpose of psi (built by disco_psi_create) with W' = W permuted to
+ * (C, Co, K), its contraction rounded to the data type before the einsum as in disco_fused_conv;
+ * otherwise channel chunks of g (the data type, on the matrix cores) and the transpose contraction.
+ * dW: the forward contraction (the data type) per channel chunk and a split product whose fp32
+ * partials are summed in a fixed order.  Results are bitwise reproducible run to run.  gx and dW must not overlap any
  * input (DISCO_ERR_INVALID_ARGUMENT).  `workspace` is caller-owned device memory (256-byte aligned) of at
  * least the size disco_fused_conv_bwd_workspace reports for (B, C, Co); its contents on entry
  * are ignored and on return are unspecified.  Calls sharing one workspace must not overlap. */

@@ -302,6 +302,7 @@ struct disco_psi_s {
     DevFused fused;
     DevFused fwdm;  // phase-split plan of the matrix-core forward (bf16)
     DevFused bwdm;  // phase-split plan of the inverse CSR: the matrix-core backward (bf16)
+    DevFused fused_t;  // Wi = Wo: the fused op's plan of the per-basis transpose (the fused backward's gx)
     int32_t *ho_order = nullptr;
 };
 
@@ -589,7 +590,7 @@ FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int6
         L.kps = (int32_t)((per + 31) / 32 * 32);
         L.S = (int32_t)std::max<int64_t>(1, (L.N + L.kps - 1) / L.kps);
         size_t off = 0;
-        L.wt = off;   off = align256(off + (size_t)C * K * Co * 2);
+        L.wt = off;   off = align256(off + (size_t)C * std::max<int64_t>(K, 16) * Co * 2);  // W^T, or W' (C, Co, 16)
         L.gyt = off;  off = align256(off + (size_t)B * L.N * Co * 2);
         L.gbuf = off; off = align256(off + (size_t)B * L.Mc * L.N * 2);
         L.part = off; off = align256(off + (size_t)B * L.S * Co * L.Mc * 4);
@@ -676,7 +677,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the tiled plan");
     }
-    disco::FusedPlan fup, fwp, bwp;
+    disco::FusedPlan fup, fwp, bwp, fut;
     try {
         // two piece stage buffers share what the W slice leaves of the workgroup's LDS
         const int ch = disco::fused_mfma_channels_per_chunk();
@@ -689,6 +690,12 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         const char *pcp = getenv("DISCO_PSI_COPIES");  // tuning knob: psi copies for odd strides (1, 2 or 3)
         if (pcp && (pcp[0] == '1' || pcp[0] == '2' || pcp[0] == '3') && pcp[1] == 0) prm.psi_copies = pcp[0] - '0';
         disco::build_phase_plan(v, prm, fup);
+        if (fup.ok && csr->Wi == csr->Wo) {
+            // the fused backward's gx = the fused op over the per-basis transpose of psi (same grid both ways)
+            disco::TransposedCSR tr;
+            disco::build_transposed_csr(v, tr);
+            disco::build_phase_plan(tr.view, prm, fut);
+        }
         disco::PhasePlanParams fprm;
         fprm.kr = csr->K <= 8 ? 8 : 16;
         fprm.ch = disco::fwd_mfma_channels(fprm.kr);
@@ -744,6 +751,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     if (e == hipSuccess) e = upload_fused(h->fused, fup);
     if (e == hipSuccess) e = upload_fused(h->fwdm, fwp);
     if (e == hipSuccess) e = upload_fused(h->bwdm, bwp);
+    if (e == hipSuccess) e = upload_fused(h->fused_t, fut);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(h->fwd);
@@ -751,6 +759,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
         free_fused(h->fused);
         free_fused(h->fwdm);
         free_fused(h->bwdm);
+        free_fused(h->fused_t);
         free_tile(h->tfwd);
         free_tile(h->tbwd);
         for (int d = 0; d < 2; ++d) {
@@ -795,6 +804,7 @@ disco_status disco_psi_destroy(disco_psi h)
     free_fused(h->fused);
     free_fused(h->fwdm);
     free_fused(h->bwdm);
+    free_fused(h->fused_t);
     free_tile(h->tfwd);
     free_tile(h->tbwd);
     (void)hipFree(h->ho_order);
@@ -1089,11 +1099,22 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
     uint16_t *gxp = (uint16_t *)gx->data;
     const int64_t K = h->K, N = L.N, CK = C * K, plane_in = (int64_t)h->Hi * h->Wi;
     hipError_t e;
-    // W^T: rows (c, k), columns o
-    if ((e = disco::launch_transpose_bf16(W->data, wt, (int)Co, (int)CK, sm)) != hipSuccess) return hipfail(e, "W transpose");
-    for (int64_t b = 0; b < B; ++b)
-        if ((e = disco::launch_transpose_bf16(gyp + b * Co * N, gyt + b * N * Co, (int)Co, (int)N, sm)) != hipSuccess)
-            return hipfail(e, "gy transpose");
+    // gx: with Wi = Wo the fused op over the per-basis transpose of psi, with W'[c, o, k] = W[o, c, k]
+    // (gx[c] = sum_{o,k} W[o,c,k] F_k^T gy[o]); otherwise W^T gy per channel chunk, then the transpose
+    // contraction of that chunk
+    const bool gx_fused = h->fused_t.ok && h->Wi == h->Wo && !getenv_is0("DISCO_BWD_FUSED");  // test knob
+    if (gx_fused && B * h->Hi * ((C + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
+        return fail(DISCO_ERR_SHAPE, "fused backward grid exceeds 2^31 blocks");
+    if (gx_fused) {
+        if ((e = disco::launch_permute_w16(W->data, wt, (int)Co, (int)C, (int)K, sm)) != hipSuccess)
+            return hipfail(e, "W permutation");
+    } else {
+        // W^T: rows (c, k), columns o
+        if ((e = disco::launch_transpose_bf16(W->data, wt, (int)Co, (int)CK, sm)) != hipSuccess) return hipfail(e, "W transpose");
+        for (int64_t b = 0; b < B; ++b)
+            if ((e = disco::launch_transpose_bf16(gyp + b * Co * N, gyt + b * N * Co, (int)Co, (int)N, sm)) != hipSuccess)
+                return hipfail(e, "gy transpose");
+    }
     // dW partials of chunk c0 (gy times the contraction, over S position splits) and their fixed-order sum
     auto dw_chunk = [&](int64_t c0, int32_t Mc, const uint16_t *outp, int64_t ostride, hipStream_t sd) -> disco_status {
         for (int64_t b = 0; b < B; ++b) {
@@ -1153,13 +1174,30 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
             if ((st = dw_chunk(c0, Mc, svp + c0 * K * N, C * K * N, sd)) != DISCO_OK) return st;
         }
     }
+    if (gx_fused && C > 0) {
+        disco::FusedMfmaLaunch m;
+        m.x = gy->data; m.W = wt; m.y = gx->data;
+        m.pieces = h->fused_t.pieces; m.rows = h->fused_t.rows; m.descs = h->fused_t.descs;
+        m.f16 = f16;
+        m.adata = f16 ? h->fused_t.adata16 : h->fused_t.adata;
+        m.scale = f16 ? std::ldexp(1.0f, -h->fused_t.psi16_exp) : 1.0f;
+        m.ho_piece = h->fused_t.ho_piece; m.ho_order = h->fused_t.ho_order;
+        m.B = (int32_t)B; m.C = (int32_t)Co; m.Co = (int32_t)C; m.K = h->K;  // input channels o, output channels c
+        m.Ho = h->Hi; m.Wo = h->Wo; m.Hi = h->Ho; m.Wi = h->Wo; m.s = 1;
+        m.max_piece_bytes = h->fused_t.max_piece_bytes;
+        m.max_resident_bytes = h->fused_t.max_resident_bytes;
+        m.desc_bytes = h->fused_t.desc_bytes; m.adata_bytes = h->fused_t.adata_bytes;
+        m.w16 = true;  // W' in rows of 16
+        if ((e = disco::launch_fused_mfma(m, sm)) != hipSuccess) return hipfail(e, "gx fused");
+    }
     for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
         const int64_t cc = std::min<int64_t>(L.Cc, C - c0);
         const int32_t Mc = (int32_t)(cc * K);
         if (cc <= 0) break;
+        if (gx_fused && svp) break;  // gx done, dW on the side stream
         uint16_t *gb = gbuf;  // [b][c k][n] of this chunk
         const int64_t gstride = (int64_t)Mc * N;
-        for (int64_t b = 0; b < B; ++b) {
+        for (int64_t b = 0; b < B && !gx_fused; ++b) {
             // g[c k][n] = sum_o W[o, c0 + c, k] gy[b, o, n]
             disco::GemmNtLaunch g1;
             g1.A = wt + c0 * K * Co; g1.lda = Co; g1.M = Mc; g1.a_bytes = (uint32_t)((int64_t)Mc * Co * 2);
@@ -1169,7 +1207,7 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
             if ((e = disco::launch_gemm_nt(g1, sm)) != hipSuccess) return hipfail(e, "W^T gy product");
         }
         // gx[b, c0 + c] = F^T g, every batch in one launch
-        if ((st = enqueue_bwd(h, gb, gxp + c0 * plane_in, dt, B, cc, sm, gstride, C * plane_in)) != DISCO_OK)
+        if (!gx_fused && (st = enqueue_bwd(h, gb, gxp + c0 * plane_in, dt, B, cc, sm, gstride, C * plane_in)) != DISCO_OK)
             return st;
         // out[b][c k][n] = (F x)[b, c0 + c]: the fused kernel's contraction (psi resident across the
         // chunk's channels) where its plan exists, else the forward contraction; nothing to compute

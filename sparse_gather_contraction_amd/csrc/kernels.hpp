@@ -192,6 +192,8 @@ struct GemmNtLaunch {
 hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream);
 // dst (Cn x R) = src (R x Cn)^T, 16-bit elements (bf16 or fp16: the bits are moved).
 hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream);
+// W (Co, C, K) with K <= 16 into W' (C, Co, 16): W'[c, o, k] = W[o, c, k], zeros past K (16-bit elements).
+hipError_t launch_permute_w16(const void *W, void *Wt, int Co, int C, int K, hipStream_t stream);
 // dW[o][col0 + m] = 16-bit(sum_{z < Z} P[z][o][m]) (fp16 when f16, else bf16), summed in increasing z.
 hipError_t launch_reduce_partials(const float *P, int Z, int Co, int Mc, void *dW, int64_t ldw, int col0, bool f16,
                                   hipStream_t stream);

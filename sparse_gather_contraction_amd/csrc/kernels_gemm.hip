@@ -306,6 +306,32 @@ hipError_t launch_gemm_nt(const GemmNtLaunch &g, hipStream_t stream)
     return large ? launch_gemm_tiles<GLarge, false>(g, stream) : launch_gemm_tiles<GSmall, false>(g, stream);
 }
 
+namespace {
+
+// one thread per element of W' (C, Co, 16)
+__global__ __launch_bounds__(256) void permute_w16_kernel(const bf16_t *__restrict__ W, bf16_t *__restrict__ Wt, int Co,
+                                                         int C, int K)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)C * Co * 16) return;
+    const int k = (int)(i & 15);
+    const int64_t co = i >> 4;
+    const int o = (int)(co % Co), c = (int)(co / Co);
+    Wt[i] = k < K ? W[((int64_t)o * C + c) * K + k] : (bf16_t)0;
+}
+
+}  // namespace
+
+hipError_t launch_permute_w16(const void *W, void *Wt, int Co, int C, int K, hipStream_t stream)
+{
+    const int64_t n = (int64_t)C * Co * 16;
+    if (n == 0) return hipSuccess;
+    if (K < 1 || K > 16 || (n + 255) / 256 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(permute_w16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, (const bf16_t *)W,
+                       (bf16_t *)Wt, Co, C, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose_bf16(const void *src, void *dst, int R, int Cn, hipStream_t stream)
 {
     if (R <= 0 || Cn <= 0) return hipSuccess;

@@ -616,6 +616,38 @@ void check_inverse(const CSRView &c, const InverseCSR &inv, int g, const std::ve
     check(err <= 1e-9 * std::max(scale, 1.0), "inverse CSR: its forward differs from the backward");
 }
 
+// The per-basis transpose (Wi = Wo): its forward over gradient plane k must equal the backward of
+// basis k alone (the gradient with every other basis plane zero).
+void check_transposed(const CSRView &c, const TransposedCSR &tr, const std::vector<double> &g)
+{
+    const CSRView &v = tr.view;
+    check(v.K == c.K && v.Ho == c.Hi && v.Wo == c.Wo && v.Hi == c.Ho && v.Wi == c.Wo && v.nnz == c.nnz,
+          "transposed CSR shape");
+    int code = 0;
+    const std::string msg = validate_csr(v, &code);
+    check(code == 0, "transposed CSR rejected: " + msg);
+    if (code != 0) return;
+    const size_t plane = (size_t)c.Ho * c.Wo;
+    double err = 0.0, scale = 0.0;
+    for (int k = 0; k < c.K; ++k) {
+        std::vector<double> gk(g.size(), 0.0);
+        std::copy(g.begin() + k * plane, g.begin() + (k + 1) * plane, gk.begin() + k * plane);
+        const std::vector<double> want = ref_bwd(c, gk);
+        for (int hi = 0; hi < c.Hi; ++hi) {
+            const int64_t R = (int64_t)k * v.Ho + hi;
+            for (int j = 0; j < c.Wo; ++j) {
+                double acc = 0.0;
+                for (int64_t e = v.row_ptr[R]; e < v.row_ptr[R + 1]; ++e)
+                    acc += (double)v.val[e] * g[k * plane + (size_t)v.col_hi[e] * v.Wi + (v.col_wi[e] + j) % v.Wi];
+                const double w = want[(size_t)hi * c.Wi + j];
+                scale = std::max(scale, std::fabs(w));
+                err = std::max(err, std::fabs(acc - w));
+            }
+        }
+    }
+    check(err <= 1e-9 * std::max(scale, 1.0), "transposed CSR: its forward differs from the per-basis backward");
+}
+
 }  // namespace
 
 int main(int argc, char **argv)
@@ -710,6 +742,17 @@ int main(int argc, char **argv)
         bprm.kr = 8; bprm.ch = 8;
         build_phase_plan(inv.view, bprm, bwp);
         check_phase(inv.view, bwp, bb, g, "backward matrix-core plan (row-inverted CSR)");
+        if (fup.ok && c.Wi == c.Wo) {
+            // the fused backward's gx: the fused plan of the per-basis transpose, replayed over gradient plane 0
+            TransposedCSR tr;
+            build_transposed_csr(c, tr);
+            check_transposed(c, tr, g);
+            FusedPlan fut;
+            build_phase_plan(tr.view, prm, fut);
+            check(fut.ok, "fused plan of the per-basis transpose not built");
+            const std::vector<double> g0(g.begin(), g.begin() + (size_t)c.Ho * c.Wo);
+            if (fut.ok) check_phase(tr.view, fut, bf, g0, "fused matrix-core plan of the per-basis transpose");
+        }
     }
 
     printf("plan_check: K=%d Ho=%d Wo=%d Hi=%d Wi=%d nnz=%lld tiled fwd %s (NI=%d G=%d, %zu tasks, %d/%d split) "

@@ -305,4 +305,39 @@ void build_inverse_csr(const CSRView &c, int g, InverseCSR &out)
     out.view.val = out.val.data();
 }
 
+void build_transposed_csr(const CSRView &c, TransposedCSR &out)
+{
+    const int64_t nrow = (int64_t)c.K * c.Hi;
+    out.row_ptr.assign(nrow + 1, 0);
+    for (int32_t k = 0; k < c.K; ++k)
+        for (int64_t e = c.row_ptr[(int64_t)k * c.Ho]; e < c.row_ptr[(int64_t)(k + 1) * c.Ho]; ++e)
+            ++out.row_ptr[(int64_t)k * c.Hi + c.col_hi[e] + 1];
+    for (int64_t r = 0; r < nrow; ++r) out.row_ptr[r + 1] += out.row_ptr[r];
+    out.col_hi.resize(c.nnz);
+    out.col_wi.resize(c.nnz);
+    out.val.resize(c.nnz);
+    std::vector<int64_t> fill(out.row_ptr.begin(), out.row_ptr.end() - 1);
+    for (int32_t k = 0; k < c.K; ++k)
+        for (int32_t ho = 0; ho < c.Ho; ++ho) {
+            const int64_t r = (int64_t)k * c.Ho + ho;
+            for (int64_t e = c.row_ptr[r]; e < c.row_ptr[r + 1]; ++e) {
+                const int64_t dst = fill[(int64_t)k * c.Hi + c.col_hi[e]]++;
+                out.col_hi[dst] = ho;
+                out.col_wi[dst] = (c.Wo - c.col_wi[e]) % c.Wo;
+                out.val[dst] = c.val[e];
+            }
+        }
+    out.view = CSRView();
+    out.view.K = c.K;
+    out.view.Ho = c.Hi;
+    out.view.Wo = c.Wo;
+    out.view.Hi = c.Ho;
+    out.view.Wi = c.Wo;
+    out.view.nnz = c.nnz;
+    out.view.row_ptr = out.row_ptr.data();
+    out.view.col_hi = out.col_hi.data();
+    out.view.col_wi = out.col_wi.data();
+    out.view.val = out.val.data();
+}
+
 }  // namespace disco

@@ -119,6 +119,18 @@ struct InverseCSR {
 };
 void build_inverse_csr(const CSRView &c, int g, InverseCSR &out);
 
+// The per-basis transpose of psi when Wi = Wo (s = 1): row (k, hi) holds an entry (ho, (Wo - wi) mod Wo)
+// of value val for every entry (k, ho; hi, wi) of psi.  As a psi from the (Ho, Wo) grid to the (Hi, Wo)
+// grid it gives z[k, hi, j] = sum over those entries of val * g[ho, (j - wi) mod Wo], the adjoint of the
+// forward's basis-k contraction, so the fused convolution over it computes the fused op's input gradient.
+struct TransposedCSR {
+    std::vector<int64_t> row_ptr;
+    std::vector<int32_t> col_hi, col_wi;
+    std::vector<float> val;
+    CSRView view;
+};
+void build_transposed_csr(const CSRView &c, TransposedCSR &out);  // requires c.Wi == c.Wo
+
 // Bytes of one piece stage in LDS.
 inline int64_t fused_piece_bytes(int64_t desc_words, int64_t a_elems, int64_t ch, int64_t win_elems)
 {

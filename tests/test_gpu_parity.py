@@ -420,6 +420,29 @@ def test_fused_bwd_small_ragged(cfg):
     assert edW <= TOL["bf16"], edW
 
 
+@pytest.mark.parametrize("cfg", [
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 20, 24, "bf16"),   # K=16, s=1, Hi = Ho
+    (21, 48, 17, 48, 0.6, 3, 3, 1, 9, 264, "f16"),    # K=9 (W' in rows of 16), Hi != Ho, Co over one tile
+    (25, 48, 25, 48, 0.7, 4, 1, 2, 70, 8, "bf16"),    # K=4, two channel chunks
+])
+def test_fused_bwd_gx_through_the_transposed_psi(cfg, monkeypatch):
+    """With Wi = Wo the fused backward computes gx as a fused convolution over the per-basis transpose of
+    psi; DISCO_BWD_FUSED=0 keeps the W^T gy products and the transpose contraction.  Both against the
+    oracle; dW does not depend on the gx path (bitwise equal)."""
+    Hi, Wi, Ho, Wo, tc, nr, na, B, C, Co, dt = cfg
+    psi = build_psi(Hi, Wi, Ho, Wo, tc, nr, na)
+    _log(f"fused bwd gx paths {cfg}")
+    tol = TOL_F16 if dt == "f16" else TOL["bf16"]
+    egx, edW, (gx_t, dW_t) = _fused_bwd_check(psi, B, C, Co, 1500 + C, dt)
+    assert egx <= tol and edW <= tol, (egx, edW)
+    monkeypatch.setenv("DISCO_BWD_FUSED", "0")
+    egx0, edW0, (gx_0, dW_0) = _fused_bwd_check(psi, B, C, Co, 1500 + C, dt)
+    monkeypatch.delenv("DISCO_BWD_FUSED")
+    assert egx0 <= tol and edW0 <= tol, (egx0, edW0)
+    assert torch.equal(dW_t, dW_0)
+    assert not torch.equal(gx_t, gx_0)  # the two paths round differently: both really ran
+
+
 def test_fused_bwd_deterministic_and_workspace_reuse():
     psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
     h = gpu_psi(psi)

@@ -148,6 +148,9 @@ FUSED_MUTANTS = {
                                "out.col_wi[dst] = (c.Wo + (wi - rho) / s) % c.Wo;"),
     "last block of a row dropped": ("for (int32_t t0 = T0; t0 == T0 || t0 - 1 - smax < tmax; t0 += kBlkJ) {",
                                     "for (int32_t t0 = T0; t0 == T0 || t0 + 15 - smax < tmax; t0 += kBlkJ) {"),
+    "transposed CSR offset not negated": ("out.col_wi[dst] = (c.Wo - c.col_wi[e]) % c.Wo;",
+                                          "out.col_wi[dst] = c.col_wi[e];"),
+    "transposed CSR column keeps the input latitude": ("out.col_hi[dst] = ho;", "out.col_hi[dst] = c.col_hi[e];"),
 }
 
 
