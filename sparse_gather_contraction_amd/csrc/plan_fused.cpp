@@ -147,7 +147,10 @@ void build_phase_plan(const CSRView &c, const PhasePlanParams &prm, FusedPlan &o
                 for (int32_t t0 : sr.t0) {
                     SubRow trial = cur;
                     trial.t0.push_back(t0);
-                    if (!cur.t0.empty() && cost_of((int64_t)trial.t0.size(), (int64_t)copies * kr * ra_of(trial),
+                    // room for the zero block a piece with an odd block count gets, so that a piece of
+                    // one sub-row (never cut further) stays within the budget
+                    if (!cur.t0.empty() && cost_of((int64_t)trial.t0.size() + 1,
+                                                   (int64_t)copies * kr * (ra_of(trial) + 8 * s + tail),
                                                    len_of(trial)) > prm.piece_budget) {
                         subs.push_back(cur);
                         cur.t0.clear();
