@@ -188,8 +188,9 @@ disco_status disco_fused_conv_bwd_saved(disco_psi h, const disco_tensor *out, co
  * capture, tight serving loops, harnesses that forbid allocation.  It takes no workspace and calls
  * no allocating routine: its workspace is the library's own scratch array of 64 MiB per device
  * (held from the library's load until the process ends).  The channel chunks shrink until the
- * workspace fits; shapes whose workspace cannot fit 64 MiB (W^T and gy^T alone must: 2 (C K Co +
- * B Ho Wo Co) bytes) are refused with DISCO_ERR_SHAPE before anything is enqueued.  Every call on
+ * workspace fits; shapes whose workspace cannot fit 64 MiB are refused with DISCO_ERR_SHAPE before
+ * anything is enqueued (the fixed buffers alone must fit: 32 C Co bytes of permuted W where gx takes the
+ * fused launch over the transposed psi, else 2 (C K Co + B Ho Wo Co) bytes of W^T and gy^T).  Every call on
  * one device uses the same array: calls that overlap on one device (other streams, other threads)
  * race and must not be issued.  The array's contents on entry are ignored. */
 disco_status disco_fused_conv_bwd_noalloc(disco_psi h, const disco_tensor *x, const disco_tensor *W,

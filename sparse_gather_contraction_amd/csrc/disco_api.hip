@@ -571,9 +571,17 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // `cap`: the largest workspace the caller can give; channel chunks shrink (down to one channel) until
 // the layout fits, if it can.
+// The fused backward's gx takes one fused launch over the per-basis transpose of psi (Wi = Wo, plan built);
+// otherwise W^T gy per channel chunk and the transpose contraction.
+bool bwd_gx_fused(const disco_psi_s *h)
+{
+    return h->fused_t.ok && h->Wi == h->Wo && !getenv_is0("DISCO_BWD_FUSED");  // test knob: "0" keeps W^T gy
+}
+
 FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int64_t Co, size_t cap = SIZE_MAX)
 {
     const int64_t K = h->K;
+    const bool gx_fused = bwd_gx_fused(h);
     const int64_t N = (int64_t)h->Ho * h->Wo;
     // up to 1024 (c, k) rows per chunk (1024 measured 6 % faster than 512 at 721x1440: fewer launches,
     // gy^T read fewer times), and few enough that one batch's chunk stays below 2 GiB
@@ -590,8 +598,9 @@ FusedBwdLayout fused_bwd_layout(const disco_psi_s *h, int64_t B, int64_t C, int6
         L.kps = (int32_t)((per + 31) / 32 * 32);
         L.S = (int32_t)std::max<int64_t>(1, (L.N + L.kps - 1) / L.kps);
         size_t off = 0;
-        L.wt = off;   off = align256(off + (size_t)C * std::max<int64_t>(K, 16) * Co * 2);  // W^T, or W' (C, Co, 16)
-        L.gyt = off;  off = align256(off + (size_t)B * L.N * Co * 2);
+        // W^T (C K, Co), or W' (C, Co, 16) for the fused gx; gy^T only for the W^T gy products
+        L.wt = off;   off = align256(off + (size_t)C * (gx_fused ? 16 : K) * Co * 2);
+        L.gyt = off;  off = align256(off + (gx_fused ? 0 : (size_t)B * L.N * Co * 2));
         L.gbuf = off; off = align256(off + (size_t)B * L.Mc * L.N * 2);
         L.part = off; off = align256(off + (size_t)B * L.S * Co * L.Mc * 4);
         L.total = off;
@@ -1102,7 +1111,7 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
     // gx: with Wi = Wo the fused op over the per-basis transpose of psi, with W'[c, o, k] = W[o, c, k]
     // (gx[c] = sum_{o,k} W[o,c,k] F_k^T gy[o]); otherwise W^T gy per channel chunk, then the transpose
     // contraction of that chunk
-    const bool gx_fused = h->fused_t.ok && h->Wi == h->Wo && !getenv_is0("DISCO_BWD_FUSED");  // test knob
+    const bool gx_fused = bwd_gx_fused(h);
     if (gx_fused && B * h->Hi * ((C + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
         return fail(DISCO_ERR_SHAPE, "fused backward grid exceeds 2^31 blocks");
     if (gx_fused) {

@@ -462,6 +462,24 @@ __device__ __forceinline__ void save_contraction(const Ctx &c, const unsigned ch
     }
 }
 
+// Zero rows of a contraction (B, C, K, Ho, L) at dst for this workgroup's latitude and span: a latitude
+// without psi entries has no pieces, so no step writes its rows.
+__device__ __forceinline__ void zero_contraction(const Ctx &c, bf16_t *dst, int64_t bstride, bool vec)
+{
+    const int64_t HoL = (int64_t)c.Ho * c.L;
+    for (int u = c.tid; u < c.C * c.K * 32; u += kThreads) {
+        const int seg = u & 31, row = u >> 5, k = row % c.K, ch = row / c.K;
+        const int wo = c.px0 + 8 * seg;
+        if (wo >= c.L) continue;
+        bf16_t *p = dst + (int64_t)c.b * bstride + ((int64_t)ch * c.K + k) * HoL + (int64_t)c.ho * c.L + wo;
+        if (vec && wo + 8 <= c.L) {
+            *reinterpret_cast<uint4 *>(p) = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            for (int e = 0; e < 8 && wo + e < c.L; ++e) p[e] = 0;
+        }
+    }
+}
+
 // EIN: fused op (einsum into yacc); else contraction-only (the chunk's result is written out).
 // SAVE (with EIN): the fused op also writes each chunk's contraction to c.save.
 template <int NOTH, bool F16, bool EIN, bool SAVE = false>
@@ -631,6 +649,12 @@ __global__ __launch_bounds__(kThreads) void fused_mfma_kernel(
                                h2, d, yacc);
                 if (++p == npieces) { p = 0; ++t; }
             }
+        }
+    } else {
+        // no psi entries at this latitude: the contraction is zero (y gets zeros from the epilogue)
+        if constexpr (!EIN) zero_contraction(c, c.out, c.out_bstride, c.vec_out);
+        if constexpr (SAVE) {
+            if (c.o_base == 0) zero_contraction(c, c.save, c.save_bstride, c.vec_save);
         }
     }
 

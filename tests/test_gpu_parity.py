@@ -1094,3 +1094,30 @@ def test_einsum_with_packed_w_equals_elementwise_w_staging(cfg, monkeypatch):
     ref = oracle.einsum(W.cpu(), t.cpu())
     nrm = oracle.einsum(W.cpu().abs(), t.cpu().abs(), abs_mode=True)
     assert normalised_error(y_pack.cpu(), ref, nrm) <= TOL_EIN[dt]
+
+
+def test_latitudes_without_psi_entries_get_zero_contractions():
+    """An output latitude whose psi rows are all empty has no plan pieces: the fused op's saved contraction
+    and the fused backward's recomputed contraction are still written there (zeros), whatever the outputs
+    and the workspace held before (NaN fills)."""
+    K, Ho, Wo = 4, 12, 64
+    empty = [k * Ho + 5 for k in range(K)]  # latitude 5: no entries in any basis row
+    psi = random_psi(K, Ho, Wo, Ho, Wo, 0.004, seed=77, empty_rows=empty)
+    h = gpu_psi(psi)
+    B, C, Co = 1, 6, 16
+    x = randn((B, C, Ho, Wo), 1900, "bf16")
+    W = randn((Co, C, K), 1901, "bf16", std=0.3)
+    gy = randn((B, Co, Ho, Wo), 1902, "bf16")
+    y = nan_like((B, Co, Ho, Wo), torch.bfloat16)
+    out = nan_like((B, C, K, Ho, Wo), torch.bfloat16)
+    sgc.disco_fused_conv_save(h, x.to(DEV), W.to(DEV), y, out)
+    ws = torch.full((sgc.disco_fused_conv_bwd_workspace(h, B, C, Co),), 0xFF, dtype=torch.uint8, device=DEV)
+    gx, dW = sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((out[:, :, :, 5] == 0).all()) and bool((y[:, :, 5] == 0).all())
+    assert normalised_error(out.cpu(), oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL["bf16"]
+    assert normalised_error(y.cpu(), oracle.fused(psi, x, W), oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)) <= TOL["bf16"]
+    rgx, rdW = oracle.fused_bwd(psi, x, W, gy)
+    ngx, ndW = oracle.fused_bwd(psi, x, W, gy, abs_mode=True)
+    assert normalised_error(gx.cpu(), rgx, ngx) <= TOL["bf16"]
+    assert normalised_error(dW.cpu(), rdW, ndW) <= TOL["bf16"]

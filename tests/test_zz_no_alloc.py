@@ -58,8 +58,9 @@ def test_noalloc_backward_matches_the_workspace_entry_point_twice():
 
 
 def test_noalloc_backward_refuses_a_workspace_beyond_its_array():
-    # 256 x 512 output positions, 256 output channels: gy^T alone is 64 MiB, beyond the 64 MiB array
-    psi = random_psi(1, 256, 512, 256, 512, 2e-6, seed=31)
+    # 256 x 512 output positions, 256 output channels, Wi = 2 Wo (gx through W^T gy): gy^T alone is
+    # 64 MiB, beyond the 64 MiB array
+    psi = random_psi(1, 256, 512, 256, 1024, 2e-6, seed=31)
     h = sgc.disco_psi_create(psi, 0)
     x = torch.zeros((1, 2, psi.Hi, psi.Wi), dtype=torch.bfloat16, device=DEV)
     W = torch.zeros((256, 2, psi.K), dtype=torch.bfloat16, device=DEV)
@@ -70,4 +71,22 @@ def test_noalloc_backward_refuses_a_workspace_beyond_its_array():
     torch.cuda.synchronize()
     assert st == "DISCO_ERR_SHAPE" and "scratch" in msg, (st, msg)
     assert bool((gx == 3.0).all()) and bool((dW == 3.0).all())
+    h.close()
+
+
+def test_noalloc_backward_fits_where_gx_takes_the_transposed_psi():
+    # the same positions with Wi = Wo: gx is one fused launch over the transposed psi, no gy^T is kept,
+    # and the shape fits the array
+    psi = random_psi(1, 256, 512, 256, 512, 2e-6, seed=31)
+    h = sgc.disco_psi_create(psi, 0)
+    x = randn((1, 2, psi.Hi, psi.Wi), 3901, "bf16").to(DEV)
+    W = randn((256, 2, psi.K), 3902, "bf16", std=0.5).to(DEV)
+    gy = randn((1, 256, psi.Ho, psi.Wo), 3903, "bf16").to(DEV)
+    gx = torch.full_like(x, 3.0)
+    dW = torch.full_like(W, 3.0)
+    st, msg = _noalloc(h, x, W, gy, gx, dW)
+    assert st == "DISCO_OK", (st, msg)
+    rgx, rdW = sgc.disco_fused_conv_bwd(h, x, W, gy)
+    torch.cuda.synchronize()
+    assert torch.equal(gx, rgx) and torch.equal(dW, rdW)
     h.close()
