@@ -1096,10 +1096,12 @@ def test_einsum_with_packed_w_equals_elementwise_w_staging(cfg, monkeypatch):
     assert normalised_error(y_pack.cpu(), ref, nrm) <= TOL_EIN[dt]
 
 
-def test_latitudes_without_psi_entries_get_zero_contractions():
+@pytest.mark.parametrize("mfma", ["1", "0"])
+def test_latitudes_without_psi_entries_get_zero_contractions(mfma, monkeypatch):
     """An output latitude whose psi rows are all empty has no plan pieces: the fused op's saved contraction
     and the fused backward's recomputed contraction are still written there (zeros), whatever the outputs
-    and the workspace held before (NaN fills)."""
+    and the workspace held before (NaN fills); on the matrix-core kernels and with DISCO_FUSED_MFMA=0."""
+    monkeypatch.setenv("DISCO_FUSED_MFMA", mfma)
     K, Ho, Wo = 4, 12, 64
     empty = [k * Ho + 5 for k in range(K)]  # latitude 5: no entries in any basis row
     psi = random_psi(K, Ho, Wo, Ho, Wo, 0.004, seed=77, empty_rows=empty)
