@@ -42,6 +42,22 @@ def normalised_error(gpu, ref, nrm):
     return float(np.max(np.abs(g[~zero] - ref[~zero]) / nrm[~zero]))
 
 
+F16_SUBNORMAL_HALF_SPACING = 2.0 ** -25  # rounding a result below fp16's normal range errs by up to this
+
+
+def normalised_error_f16(gpu, ref, nrm):
+    """normalised_error for fp16 results, with the absolute rounding error of fp16 subnormals taken off
+    (a result below 2^-14 has an ulp of 2^-24, not a relative one)."""
+    g = gpu.detach().double().cpu().numpy() if hasattr(gpu, "detach") else np.asarray(gpu, np.float64)
+    assert g.shape == ref.shape == nrm.shape
+    assert np.all(np.isfinite(g)), "non-finite output (unwritten or NaN)"
+    zero = nrm == 0
+    assert np.all(g[zero] == 0.0), "elements with zero normaliser must be exactly 0"
+    if np.all(zero):
+        return 0.0
+    return float(np.max(np.maximum(np.abs(g[~zero] - ref[~zero]) - F16_SUBNORMAL_HALF_SPACING, 0.0) / nrm[~zero]))
+
+
 _PSI = {}
 
 
@@ -1123,3 +1139,67 @@ def test_latitudes_without_psi_entries_get_zero_contractions(mfma, monkeypatch):
     ngx, ndW = oracle.fused_bwd(psi, x, W, gy, abs_mode=True)
     assert normalised_error(gx.cpu(), rgx, ngx) <= TOL["bf16"]
     assert normalised_error(dW.cpu(), rdW, ndW) <= TOL["bf16"]
+
+
+def _random_case(seed):
+    """A random small problem: sparse random psi (some rows empty), s in {1, 2}, ragged sizes."""
+    rng = np.random.default_rng(seed)
+    K = int(rng.integers(1, 21))  # K > 16: the vector-ALU fused kernel
+    s = int(rng.integers(1, 3))
+    Ho = int(rng.integers(1, 10))
+    Wo = int(rng.choice([8, 16, 24, 40, 64, 72, 96, 264]))
+    Hi = int(rng.integers(1, 12))
+    Wi = s * Wo
+    empty = tuple(int(r) for r in rng.choice(K * Ho, size=min(K * Ho, int(rng.integers(0, 4))), replace=False))
+    psi = random_psi(K, Ho, Wo, Hi, Wi, float(rng.uniform(0.002, 0.05)), seed=seed, empty_rows=empty)
+    B = int(rng.integers(1, 3))
+    C = int(rng.integers(1, 11))
+    Co = 8 * int(rng.integers(1, 6))
+    dt = str(rng.choice(["bf16", "bf16", "f16", "f32"]))
+    return psi, B, C, Co, dt
+
+
+@pytest.mark.parametrize("seed", list(range(5000, 5100)))
+def test_random_problems_every_op_against_the_oracle(seed):
+    """Seeded random problems through fwd, bwd, the fused op (plain and saving), its backward (recomputing
+    and saved) and the einsum, each against the fp64 oracle, outputs NaN-filled beforehand (fp32 data: the
+    ops that take it)."""
+    psi, B, C, Co, dt = _random_case(seed)
+    _log(f"random problem seed={seed} K={psi.K} {psi.Ho}x{psi.Wo} <- {psi.Hi}x{psi.Wi} B={B} C={C} Co={Co} {dt}")
+    tol = {"f16": TOL_F16, "bf16": TOL["bf16"], "f32": TOL["f32"]}[dt]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
+    f32 = dt == "f32"
+    err = normalised_error_f16 if dt == "f16" else normalised_error  # random psi reaches fp16 subnormals
+    h = gpu_psi(psi)
+    x = randn((B, C, psi.Hi, psi.Wi), seed + 1, dt)
+    g = randn((B, C, psi.K, psi.Ho, psi.Wo), seed + 2, dt)
+    W = randn((Co, C, psi.K), seed + 3, dt, std=1.0 / np.sqrt(C * psi.K))
+    gy = randn((B, Co, psi.Ho, psi.Wo), seed + 4, dt)
+    out = nan_like((B, C, psi.K, psi.Ho, psi.Wo), tdt)
+    gx = nan_like((B, C, psi.Hi, psi.Wi), tdt)
+    y = nan_like((B, Co, psi.Ho, psi.Wo), tdt)
+    ys = nan_like((B, Co, psi.Ho, psi.Wo), tdt)
+    kept = nan_like((B, C, psi.K, psi.Ho, psi.Wo), tdt)
+    sgc.disco_fwd(h, x.to(DEV), out)
+    sgc.disco_bwd(h, g.to(DEV), gx)
+    sgc.disco_fused_conv(h, x.to(DEV), W.to(DEV), y)
+    sgc.disco_fused_conv_save(h, x.to(DEV), W.to(DEV), ys, kept)
+    if not f32:
+        fgx, fdW = sgc.disco_fused_conv_bwd(h, x.to(DEV), W.to(DEV), gy.to(DEV))
+        sgx, sdW = sgc.disco_fused_conv_bwd_saved(h, kept, W.to(DEV), gy.to(DEV))
+    ye = sgc.disco_einsum(W.to(DEV), g.to(DEV)) if psi.K <= 16 and not f32 else None
+    torch.cuda.synchronize()
+    assert err(out.cpu(), oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= tol
+    assert err(gx.cpu(), oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= tol
+    ry, ny = oracle.fused(psi, x, W), oracle.fused(psi, x.abs(), W.abs(), abs_mode=True)
+    assert err(y.cpu(), ry, ny) <= tol
+    assert torch.equal(ys, y)
+    assert err(kept.cpu(), oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= tol
+    if not f32:
+        rgx, rdW = oracle.fused_bwd(psi, x, W, gy)
+        ngx, ndW = oracle.fused_bwd(psi, x, W, gy, abs_mode=True)
+        for gxx, dww in ((fgx, fdW), (sgx, sdW)):
+            assert err(gxx.cpu(), rgx, ngx) <= tol
+            assert err(dww.cpu(), rdW, ndW) <= tol
+    if ye is not None:
+        assert err(ye.cpu(), oracle.einsum(W, g), oracle.einsum(W.abs(), g.abs(), abs_mode=True)) <= tol
