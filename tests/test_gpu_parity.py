@@ -1164,13 +1164,39 @@ def test_random_problems_every_op_against_the_oracle(seed):
     """Seeded random problems through fwd, bwd, the fused op (plain and saving), its backward (recomputing
     and saved) and the einsum, each against the fp64 oracle, outputs NaN-filled beforehand (fp32 data: the
     ops that take it)."""
+    _random_problem(seed)
+
+
+RANDOM_PATH_KNOBS = {
+    "vector-ALU fused": {"DISCO_FUSED_MFMA": "0"},
+    "vector-ALU fwd and bwd": {"DISCO_FWD_MFMA": "0", "DISCO_BWD_MFMA": "0"},
+    "staged fp32 gathers": {"DISCO_TILE": "0"},
+    "plain gathers": {"DISCO_TILE": "0", "DISCO_STAGED": "0", "DISCO_FWD_MFMA": "0", "DISCO_BWD_MFMA": "0"},
+    "gx through W^T gy": {"DISCO_BWD_FUSED": "0"},
+    "element-wise W staging": {"DISCO_PACK_W": "0"},
+    "one realigned psi copy": {"DISCO_PSI_COPIES": "1"},
+    "two psi copies": {"DISCO_PSI_COPIES": "2"},
+}
+
+
+@pytest.mark.parametrize("path", sorted(RANDOM_PATH_KNOBS))
+@pytest.mark.parametrize("seed", list(range(5100, 5125)))
+def test_random_problems_on_every_kernel_path(seed, path, monkeypatch):
+    """The random problems again with each kernel-path knob (a fresh psi handle, so that the knobs read
+    when the plans are built apply too)."""
+    for k, v in RANDOM_PATH_KNOBS[path].items():
+        monkeypatch.setenv(k, v)
+    _random_problem(seed, fresh=True)
+
+
+def _random_problem(seed, fresh=False):
     psi, B, C, Co, dt = _random_case(seed)
     _log(f"random problem seed={seed} K={psi.K} {psi.Ho}x{psi.Wo} <- {psi.Hi}x{psi.Wi} B={B} C={C} Co={Co} {dt}")
     tol = {"f16": TOL_F16, "bf16": TOL["bf16"], "f32": TOL["f32"]}[dt]
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
     f32 = dt == "f32"
     err = normalised_error_f16 if dt == "f16" else normalised_error  # random psi reaches fp16 subnormals
-    h = gpu_psi(psi)
+    h = sgc.disco_psi_create(psi, 0) if fresh else gpu_psi(psi)
     x = randn((B, C, psi.Hi, psi.Wi), seed + 1, dt)
     g = randn((B, C, psi.K, psi.Ho, psi.Wo), seed + 2, dt)
     W = randn((Co, C, psi.K), seed + 3, dt, std=1.0 / np.sqrt(C * psi.K))
@@ -1203,3 +1229,5 @@ def test_random_problems_every_op_against_the_oracle(seed):
             assert err(dww.cpu(), rdW, ndW) <= tol
     if ye is not None:
         assert err(ye.cpu(), oracle.einsum(W, g), oracle.einsum(W.abs(), g.abs(), abs_mode=True)) <= tol
+    if fresh:
+        h.close()
