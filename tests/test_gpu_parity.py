@@ -1141,10 +1141,10 @@ def test_latitudes_without_psi_entries_get_zero_contractions(mfma, monkeypatch):
     assert normalised_error(dW.cpu(), rdW, ndW) <= TOL["bf16"]
 
 
-def _random_case(seed):
+def _random_case(seed, k_range=None):
     """A random small problem: sparse random psi (some rows empty), s in {1, 2}, ragged sizes."""
     rng = np.random.default_rng(seed)
-    K = int(rng.integers(1, 21))  # K > 16: the vector-ALU fused kernel
+    K = int(rng.integers(*(k_range or (1, 21))))  # K > 16: the vector-ALU fused kernel
     s = int(rng.integers(1, 3))
     Ho = int(rng.integers(1, 10))
     Wo = int(rng.choice([8, 16, 24, 40, 64, 72, 96, 264]))
@@ -1189,8 +1189,18 @@ def test_random_problems_on_every_kernel_path(seed, path, monkeypatch):
     _random_problem(seed, fresh=True)
 
 
-def _random_problem(seed, fresh=False):
-    psi, B, C, Co, dt = _random_case(seed)
+@pytest.mark.parametrize("seed", list(range(5200, 5208)))
+def test_random_problems_with_many_channels(seed):
+    """The random problems with 60-200 input channels and K = 8..16: several channel chunks in the fused
+    kernel and in the fused backward's recomputed contraction (64-128 channels per chunk at these K)."""
+    rng = np.random.default_rng(seed)
+    _random_problem(seed, channels=int(rng.integers(60, 201)), k_range=(8, 17))
+
+
+def _random_problem(seed, fresh=False, channels=None, k_range=None):
+    psi, B, C, Co, dt = _random_case(seed, k_range)
+    if channels is not None:
+        C = channels
     _log(f"random problem seed={seed} K={psi.K} {psi.Ho}x{psi.Wo} <- {psi.Hi}x{psi.Wi} B={B} C={C} Co={Co} {dt}")
     tol = {"f16": TOL_F16, "bf16": TOL["bf16"], "f32": TOL["f32"]}[dt]
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
