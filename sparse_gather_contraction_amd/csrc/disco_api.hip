@@ -63,6 +63,7 @@ struct DevTile {
     int32_t n_tasks = 0;
     int32_t L = 0, row_len = 0, lrow = 0, deint = 1, rows_per_stage = 0, NI = 1, G = 1, PW = 1;
     int32_t n_ws4 = 0, n_ws2 = 0, max_recs = 0;
+    int32_t n_recs = 0;
 };
 
 constexpr int kLdsPerBlock = 160 * 1024;       // gfx950: a workgroup may allocate the whole 160 KiB
@@ -148,6 +149,8 @@ hipError_t upload_tile(DevTile &d, const disco::TilePlan &p)
 {
     d = DevTile();
     if (!p.ok || !disco::tile_supported(p.NI, p.G, p.PW)) return hipSuccess;
+    // the kernel addresses the records through one buffer resource (32-bit byte offsets)
+    if (p.recs.size() * sizeof(disco::TileRec) > (size_t)INT32_MAX) return hipSuccess;
     hipError_t e;
     if ((e = upload(&d.tasks, p.tasks)) != hipSuccess) return e;
     if ((e = upload(&d.stages, p.stages)) != hipSuccess) return e;
@@ -160,6 +163,7 @@ hipError_t upload_tile(DevTile &d, const disco::TilePlan &p)
     d.L = p.L; d.row_len = p.row_len; d.lrow = p.lrow; d.deint = p.deint; d.rows_per_stage = p.rows_per_stage;
     d.NI = p.NI; d.G = p.G; d.PW = p.PW;
     d.n_ws4 = p.n_ws4; d.n_ws2 = p.n_ws2; d.max_recs = p.max_recs;
+    d.n_recs = (int32_t)p.recs.size();
     return hipSuccess;
 }
 
@@ -403,8 +407,9 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const DevTile &tp
     if (BC == 0) return DISCO_OK;
     const size_t esz = dtype == DISCO_F32 ? 4 : 2;
     if (dtype == DISCO_F32 && tp.ok && !getenv_is0("DISCO_TILE")) {  // test knob: "0" turns the tiled gather off
+        // direct loads address a plane through one buffer resource (32-bit byte offsets)
         const bool vec = ((uintptr_t)src % 16 == 0) && (src_plane % 4 == 0) && (tp.row_len % 4 == 0) &&
-                         tp.L >= disco::kTileHalo;
+                         tp.L >= disco::kTileHalo && src_plane <= INT32_MAX / 4;
         // at most one workgroup per PW planes per task: keep the grid below 2^31 workgroups
         const int64_t n_pg_max = (((int64_t)1 << 31) - 1) / std::max<int32_t>(1, tp.n_tasks);
         const int64_t chunk = std::max<int64_t>(1, n_pg_max) * tp.PW;
@@ -416,7 +421,7 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const DevTile &tp
             a.recs = tp.recs; a.items = tp.items;
             a.n_tasks = tp.n_tasks;
             a.BC = (int32_t)std::min<int64_t>(chunk, BC - b0);
-            a.n_ws4 = tp.n_ws4; a.n_ws2 = tp.n_ws2; a.max_recs = tp.max_recs;
+            a.n_ws4 = tp.n_ws4; a.n_ws2 = tp.n_ws2; a.max_recs = tp.max_recs; a.n_recs = tp.n_recs;
             a.src_plane = src_plane; a.dst_plane = dst_plane;
             a.L = tp.L; a.row_len = tp.row_len; a.lrow = tp.lrow; a.deint = tp.deint;
             a.rows_per_stage = tp.rows_per_stage; a.NI = tp.NI; a.G = tp.G; a.PW = tp.PW;

@@ -59,8 +59,15 @@ struct TileLaunch {
     int64_t src_plane, dst_plane;
     int32_t L, row_len, lrow, deint, rows_per_stage, NI, G, PW;
     int32_t max_recs;           // records of the largest stage (LDS after the rows)
-    int32_t vec;                // source rows are 16-byte aligned (row_len and plane a multiple of 4), L >= halo
+    int32_t n_recs;             // records in all
+    int32_t vec;                // source rows are 16-byte aligned (row_len and plane a multiple of 4), L >= halo,
+                                // plane below 2 GiB: stages stream in by direct global -> LDS loads
 };
+// Allow kernel `fn` `lds` bytes of dynamic LDS on the current device: checked on the host against the
+// device's per-workgroup LDS (hipErrorInvalidValue, nothing launched, when it does not fit), the
+// function attribute raised only when a kernel needs more than it was last given on that device.
+hipError_t allow_lds(const void *fn, size_t lds);
+
 bool tile_supported(int NI, int G, int PW);
 hipError_t launch_tile(const TileLaunch &a, hipStream_t stream);
 

@@ -853,8 +853,6 @@ int fused_mfma_channels_per_chunk() { return kCh; }
 
 int fwd_mfma_channels(int kr) { return kr == 8 ? 8 : 4; }
 
-namespace {
-
 // Allow kernel `fn` `lds` bytes of dynamic LDS on the current device.  The request is checked on the
 // host against the device's per-workgroup LDS (an oversized request returns hipErrorInvalidValue and
 // nothing is launched), and hipFuncSetAttribute runs only when a kernel needs more than it was last
@@ -889,8 +887,6 @@ hipError_t allow_lds(const void *fn, size_t lds)
     granted.push_back({{fn, dev}, lds});
     return hipSuccess;
 }
-
-}  // namespace
 
 hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream)
 {

@@ -12,6 +12,8 @@
 //     longitude residue, s = 2: even and odd columns, so a segment reads consecutive words; every
 //     LDS row carries a wrap halo so no index needs a modulo inside a record), and so are the
 //     stage's records (64 bytes: window offset, wrap threshold, entry count c, values [c][G]).
+//     A stage's rows and records travel by direct global -> LDS loads, all issued before one wait
+//     (its metadata is read first, into registers, so no global load waits behind them).
 //   * Records are read as LDS broadcasts.  Per record a lane reads its c + kTileT - 1 window
 //     values once and issues c x G x kTileT multiply-adds (longitude-shift reuse); records of an
 //     item are grouped by c, one branch-free software-pipelined loop per c.
@@ -29,6 +31,25 @@ constexpr int kThreads = 256;
 constexpr int T = kTileT;
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// Raw buffer resource over `bytes` bytes at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct global -> LDS loads (buffer_load_dword / _dwordx4 ... lds): lane i of the instruction
+// writes LDS base `l` + 4 i (dma4) or + 16 i (dma16); lanes outside the exec mask write nothing.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *l)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)l, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *l)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)l, 16, voff, 0, 0, 0);
+}
 
 // One class of records (all with C entries) of one item: a branch-free loop, software-pipelined
 // and unrolled by two so that two sets of registers (window, values, header) alternate without
@@ -108,16 +129,20 @@ __device__ __forceinline__ void run_class(const TileRec *lrec, const char *lane,
 }
 
 // Records of item i in one stage: one loop per entry count; wave `wsi` of the WS waves sharing the
-// planes takes every WS-th record of each class.  ptr: the item's class bounds (global record
-// indices); rb: the stage's first record (LDS index 0).
+// planes takes every WS-th record of each class.  bounds (bounds_hi): lane q holds the stage's record
+// bound q (q + 64) (global record index; item-major, then by entry count), `base` = i kTileClasses; rb:
+// the stage's first record (LDS index 0).
 template <int G>
-__device__ __forceinline__ void run_item(const TileRec *lrec, const char *lane, int jlc, int wrap,
-                                         const int32_t *__restrict__ ptr, int rb, int wsi, int WS, float (&acc)[G][T])
+__device__ __forceinline__ void run_item(const TileRec *lrec, const char *lane, int jlc, int wrap, int bounds,
+                                         int bounds_hi, int base, int rb, int wsi, int WS, float (&acc)[G][T])
 {
     constexpr int CM = tile_piece_max(G);
     int p[kTileClasses + 1];
 #pragma unroll
-    for (int q = 0; q <= kTileClasses; ++q) p[q] = uni(ptr[q] - rb);
+    for (int q = 0; q <= kTileClasses; ++q) {
+        const int idx = base + q;  // a constant once the item loop is unrolled
+        p[q] = (idx < 64 ? __builtin_amdgcn_readlane(bounds, idx) : __builtin_amdgcn_readlane(bounds_hi, idx - 64)) - rb;
+    }
     run_class<1, G>(lrec, lane, jlc, wrap, p[0] + wsi, p[1], WS, acc);
     run_class<2, G>(lrec, lane, jlc, wrap, p[1] + wsi, p[2], WS, acc);
     run_class<3, G>(lrec, lane, jlc, wrap, p[2] + wsi, p[3], WS, acc);
@@ -126,6 +151,54 @@ __device__ __forceinline__ void run_item(const TileRec *lrec, const char *lane, 
     if constexpr (CM >= 6) run_class<6, G>(lrec, lane, jlc, wrap, p[5] + wsi, p[6], WS, acc);
     if constexpr (CM >= 7) run_class<7, G>(lrec, lane, jlc, wrap, p[6] + wsi, p[7], WS, acc);
     if constexpr (CM >= 8) run_class<8, G>(lrec, lane, jlc, wrap, p[7] + wsi, p[8], WS, acc);
+}
+
+// Queue records [rb, re) of the stage into LDS (16-byte direct loads spread over the workgroup).
+__device__ __forceinline__ void dma_recs(const TileLaunch &a, unsigned char *lrec, int rb, int re, int wave, int lane)
+{
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.recs, (uint32_t)a.n_recs * (uint32_t)sizeof(TileRec));
+    const int n = 4 * (re - rb);
+    for (int u0 = 64 * wave; u0 < n; u0 += 256) {
+        const int u = u0 + lane;
+        if (u < n) dma16(rs, (uint32_t)sizeof(TileRec) * (uint32_t)rb + 16u * (uint32_t)u, lrec + 16 * u0);
+    }
+}
+
+// Queue the stage's source rows of the workgroup's NPB planes into LDS by direct loads (source rows
+// 16-byte aligned, L >= kTileHalo).  LDS row positions 0 .. L + kTileHalo - 1 of a plane's row: with
+// deint = 1 position j holds row element j mod L (16-byte loads, one per four positions); with
+// deint = 2 the two residue rows rho = 0, 1 hold elements 2 (j mod L) + rho (4-byte loads, lane j of
+// an instruction writing position j, so the even/odd split costs no register traffic).  (Row, plane)
+// pairs go round the four waves.  rows_v: lane r holds the stage's source row r.
+__device__ __forceinline__ void dma_band(const TileLaunch &a, float *lds, int rows_v, int nrows, int plane0, int NPB,
+                                         int wave, int lane)
+{
+    const int stage_floats = a.rows_per_stage * a.deint * a.lrow;
+    const uint32_t plane_bytes = 4u * (uint32_t)a.src_plane;
+    const int lg = __builtin_ctz((unsigned)NPB);  // NPB = 4 PW / WS is a power of two
+    for (int rp = wave; rp < (nrows << lg); rp += 4) {  // (row, plane) pairs round the waves
+        const int r = rp >> lg, ps = rp & (NPB - 1);
+        if (plane0 + ps >= a.BC) continue;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.src + (int64_t)(plane0 + ps) * a.src_plane, plane_bytes);
+        const uint32_t row0 = 4u * (uint32_t)(__builtin_amdgcn_readlane(rows_v, r) * a.row_len);
+        float *drow = lds + ps * stage_floats + r * a.deint * a.lrow;
+        if (a.deint == 1) {
+            const int U = a.row_len >> 2, UH = U + kTileHalo / 4;
+            for (int u0 = 0; u0 < UH; u0 += 64) {
+                const int u = u0 + lane;
+                const int ug = u < U ? u : u - U;
+                if (u < UH) dma16(rs, row0 + 16u * (uint32_t)ug, drow + 4 * u0);
+            }
+        } else {
+            const int npos = a.L + kTileHalo;
+            for (int rho = 0; rho < 2; ++rho)
+                for (int j0 = 0; j0 < npos; j0 += 64) {
+                    const int j = j0 + lane;
+                    const int jg = j < a.L ? j : j - a.L;
+                    if (j < npos) dma4(rs, row0 + 4u * (uint32_t)(2 * jg + rho), drow + rho * a.lrow + j0);
+                }
+        }
+    }
 }
 
 // Copy records [rb, re) of the stage to LDS (16-byte units; the loads of a batch are issued
@@ -147,58 +220,13 @@ __device__ __forceinline__ void stage_recs(const TileLaunch &a, TileRec *lrec, i
     }
 }
 
-// Copy the stage's source rows of the workgroup's NPB planes into LDS (all four waves).  Vector
-// path (rows 16-byte aligned, L >= kTileHalo): a (row, plane) pair is row_len / 4 units of 16
-// bytes plus the halo units (the row's first kTileHalo positions again: 4 units, or 8 when a
-// forward row splits into two residue rows); a wave takes two pairs at a time and issues all
-// their loads before any LDS write, so the loads are in flight together.
+// Copy the stage's source rows of the workgroup's NPB planes into LDS with ordinary loads and
+// stores (source rows not 16-byte aligned, or L < kTileHalo).
 __device__ __forceinline__ void stage_band(const TileLaunch &a, float *lds, const int32_t *__restrict__ rows,
                                            int nrows, int plane0, int NPB, int wave, int lane)
 {
     const int stage_floats = a.rows_per_stage * a.deint * a.lrow;
     const int NRP = nrows * NPB;
-    if (a.vec) {
-        const int U = a.row_len >> 2;
-        const int UH = U + (a.deint == 1 ? kTileHalo / 4 : kTileHalo / 2);
-        for (int rp0 = wave; rp0 < NRP; rp0 += 8) {
-            float4 v[2][4];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int rp = rp0 + 4 * j;
-                const int r = rp / NPB, ps = rp - r * NPB;
-                const bool ok = rp < NRP && plane0 + ps < a.BC;
-                const float *srow = a.src + (int64_t)(plane0 + ps) * a.src_plane +
-                                    (int64_t)(ok ? rows[r] : 0) * a.row_len;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int u = lane + 64 * k;
-                    const int ug = u < U ? u : u - U;
-                    if (ok && u < UH) v[j][k] = *reinterpret_cast<const float4 *>(srow + 4 * ug);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int rp = rp0 + 4 * j;
-                const int r = rp / NPB, ps = rp - r * NPB;
-                if (!(rp < NRP && plane0 + ps < a.BC)) continue;
-                float *drow = lds + ps * stage_floats + r * a.deint * a.lrow;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int u = lane + 64 * k;
-                    if (u >= UH) continue;
-                    if (a.deint == 1) {
-                        const int d = u < U ? 4 * u : a.L + 4 * (u - U);
-                        *reinterpret_cast<float4 *>(drow + d) = v[j][k];
-                    } else {
-                        const int d = u < U ? 2 * u : a.L + 2 * (u - U);
-                        *reinterpret_cast<float2 *>(drow + d) = make_float2(v[j][k].x, v[j][k].z);
-                        *reinterpret_cast<float2 *>(drow + a.lrow + d) = make_float2(v[j][k].y, v[j][k].w);
-                    }
-                }
-            }
-        }
-        return;
-    }
     for (int rp = wave; rp < NRP; rp += 4) {
         const int r = rp / NPB, ps = rp - r * NPB;
         const int plane = plane0 + ps;
@@ -218,6 +246,68 @@ __device__ __forceinline__ void stage_band(const TileLaunch &a, float *lds, cons
             drow[rho * a.lrow + a.L + pos] = srow[rho + a.deint * jj];
         }
     }
+}
+
+// Per-workgroup constants of the stage loop.
+struct StageCtx {
+    int plane0, NPB, wave, lane;
+    int ps, jlc;      // the lane's plane within the workgroup, first position (clamped into the row)
+    int wsi, WS;      // the wave's share of the records, waves sharing the planes
+    int stage_floats; // floats of one plane's rows in a stage buffer
+};
+
+// A stage's metadata, one load per lane: lane q holds record bound q (bounds_hi: q + 64; there are
+// NI kTileClasses + 1 <= 65), lane r < nrows source row r (a stage has at most kTileMaxStageRows <= 64
+// rows).  It is read before the stage is queued, so no global load waits behind the direct loads.
+struct StageMeta {
+    int bounds_v, bounds_hi, rows_v;
+    int rb, re, nrows;
+    int row_begin;  // into stage_rows (the plain copy path reads them there)
+};
+
+template <int NI>
+__device__ __forceinline__ StageMeta load_meta(const TileLaunch &a, int st, int lane)
+{
+    const Stage sg = a.stages[uni(st)];
+    const int32_t *rp = a.stage_recptr + uni(sg.segptr);
+    StageMeta m;
+    m.row_begin = uni(sg.row_begin);
+    m.nrows = uni(sg.row_end) - m.row_begin;
+    m.bounds_v = lane <= NI * kTileClasses ? rp[lane] : 0;
+    m.bounds_hi = (NI * kTileClasses >= 64 && lane + 64 <= NI * kTileClasses) ? rp[lane + 64] : 0;
+    m.rows_v = lane < m.nrows ? a.stage_rows[m.row_begin + lane] : 0;
+    m.rb = __builtin_amdgcn_readlane(m.bounds_v, 0);
+    m.re = NI * kTileClasses < 64 ? __builtin_amdgcn_readlane(m.bounds_v, NI * kTileClasses)
+                                  : __builtin_amdgcn_readlane(m.bounds_hi, NI * kTileClasses - 64);
+    return m;
+}
+
+// Queue a stage into the stage buffer: direct loads for 16-byte aligned source rows, else ordinary
+// copies; either way the data is in place after the issuing threads' waits and the next barrier.
+template <int PW>
+__device__ __forceinline__ void queue_stage(const TileLaunch &a, const StageCtx &sc, const StageMeta &m, float *buf)
+{
+    float *lrec = buf + 4 * PW * sc.stage_floats;
+    if (a.vec) {
+        dma_band(a, buf, m.rows_v, m.nrows, sc.plane0, sc.NPB, sc.wave, sc.lane);
+        dma_recs(a, reinterpret_cast<unsigned char *>(lrec), m.rb, m.re, sc.wave, sc.lane);
+    } else {
+        stage_band(a, buf, a.stage_rows + m.row_begin, m.nrows, sc.plane0, sc.NPB, sc.wave, sc.lane);
+        stage_recs(a, reinterpret_cast<TileRec *>(lrec), m.rb, m.re, threadIdx.x);
+    }
+}
+
+// Contract the records of a stage in LDS (metadata m): LDS and registers only.
+template <int NI, int G, int PW>
+__device__ __forceinline__ void compute_stage(const TileLaunch &a, const StageCtx &sc, const StageMeta &m,
+                                              const float *cur, float (&acc)[NI][G][T])
+{
+    const TileRec *lrec = reinterpret_cast<const TileRec *>(cur + 4 * PW * sc.stage_floats);
+    const char *lane_base = reinterpret_cast<const char *>(cur + sc.ps * sc.stage_floats + sc.jlc);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        run_item<G>(lrec, lane_base, sc.jlc, 4 * a.L, m.bounds_v, m.bounds_hi, i * kTileClasses, m.rb, sc.wsi, sc.WS,
+                    acc[i]);
 }
 
 template <int NI, int G, int PW>
@@ -255,7 +345,6 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
     const int jl = ql * T;
     const int jlc = jl < a.L ? jl : 0;  // lanes past the row read valid LDS, results dropped
     const int stage_floats = a.rows_per_stage * a.deint * a.lrow;
-    const float *my = lds + ps * stage_floats;
 
     float acc[NI][G][T];
 #pragma unroll
@@ -265,19 +354,16 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
 #pragma unroll
             for (int t = 0; t < T; ++t) acc[i][g][t] = 0.0f;
 
-    TileRec *lrec = reinterpret_cast<TileRec *>(lds + 4 * PW * stage_floats);  // after the row area
-    const char *lane_base = reinterpret_cast<const char *>(my + jlc);
+    // stage buffer: [rows of the 4 PW planes][records]
+    float *buf = lds;
+    const StageCtx sc{plane0, NPB, wave, lane, ps, jlc, wsi, WS, stage_floats};
     for (int st = task.stage_begin; st < task.stage_end; ++st) {
-        const Stage sg = a.stages[uni(st)];
-        const int32_t *rp = a.stage_recptr + sg.segptr;
-        const int rb = uni(rp[0]), re = uni(rp[NI * kTileClasses]);
         __syncthreads();  // the previous stage is consumed
-        stage_band(a, lds, a.stage_rows + sg.row_begin, sg.row_end - sg.row_begin, plane0, NPB, wave, lane);
-        stage_recs(a, lrec, rb, re, threadIdx.x);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            run_item<G>(lrec, lane_base, jlc, 4 * a.L, rp + i * kTileClasses, rb, wsi, WS, acc[i]);
+        const StageMeta m = load_meta<NI>(a, st, lane);
+        queue_stage<PW>(a, sc, m, buf);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads have landed
+        __syncthreads();                // everyone's have
+        compute_stage<NI, G, PW>(a, sc, m, buf, acc);
     }
 
     if (WS > 1) {
@@ -324,6 +410,15 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
     }
 }
 
+template <int NI, int G, int PW>
+hipError_t launch_one(const TileLaunch &a, int64_t nblk, size_t lds, hipStream_t stream)
+{
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&tile_gather_kernel<NI, G, PW>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((tile_gather_kernel<NI, G, PW>), dim3((unsigned)nblk), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
 template <int NI, int G>
 hipError_t launch_pw(const TileLaunch &a, hipStream_t stream)
 {
@@ -335,11 +430,7 @@ hipError_t launch_pw(const TileLaunch &a, hipStream_t stream)
                          (size_t)a.max_recs * sizeof(TileRec);
     const size_t red = a.n_ws2 > 0 ? (size_t)3 * 64 * NI * G * T * sizeof(float) : 0;
     const size_t lds = stage > red ? stage : red;
-    if (a.PW == 2)
-        hipLaunchKernelGGL((tile_gather_kernel<NI, G, 2>), dim3((unsigned)nblk), dim3(kThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL((tile_gather_kernel<NI, G, 1>), dim3((unsigned)nblk), dim3(kThreads), lds, stream, a);
-    return hipGetLastError();
+    return a.PW == 2 ? launch_one<NI, G, 2>(a, nblk, lds, stream) : launch_one<NI, G, 1>(a, nblk, lds, stream);
 }
 
 }  // namespace

@@ -237,7 +237,7 @@ void check_tile(const CSRView &c, const TilePlan &tp, bool backward, int lds_bud
         for (int32_t st = task.stage_begin; st < task.stage_end; ++st) {
             const Stage &sg = tp.stages[st];
             const int nrows = sg.row_end - sg.row_begin;
-            check(nrows >= 1 && nrows <= tp.rows_per_stage, what + ": rows per stage");
+            check(nrows >= 1 && nrows <= tp.rows_per_stage && nrows <= kTileMaxStageRows, what + ": rows per stage");
             check(tp.stage_recptr[sg.segptr + tp.NI * kTileClasses] - tp.stage_recptr[sg.segptr] <= tp.max_recs,
                   what + ": stage holds more records than its LDS area");
             // LDS image as the staging loop writes it: residue rho of staged row r at (r deint + rho) lrow,

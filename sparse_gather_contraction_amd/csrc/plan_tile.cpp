@@ -32,7 +32,7 @@ void build_tile_plan(const CSRView &c, const GatherPlan &p, bool backward, int l
     out.NP = 4 * out.PW;
     out.lrow = (L + kTileHalo + 3) / 4 * 4;
     const int64_t row_bytes = (int64_t)out.NP * out.deint * out.lrow * 4;
-    int32_t rps = (int32_t)(lds_budget / row_bytes);
+    int32_t rps = (int32_t)std::min<int64_t>(kTileMaxStageRows, lds_budget / row_bytes);
     if (rps < 1) return;
 
     // rows per item: keep G when every item agrees, else split every item into single rows

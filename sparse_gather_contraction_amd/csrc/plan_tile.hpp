@@ -34,6 +34,7 @@ constexpr int kTileMaxRows = 8;    // accumulator rows per task (NI * G): 48 acc
 constexpr int kTileMaxL = 384;     // longest destination row the kernel covers (64 lanes x kTileT)
 constexpr int kTileRecVals = 12;   // value slots per record
 constexpr int kTileClasses = 8;    // records are grouped by entry count c = 1 .. 8
+constexpr int kTileMaxStageRows = 64;  // source rows per stage (one per lane of the kernel's row list)
 
 // entries per record for G rows sharing the segment
 constexpr int tile_piece_max(int G) { return G == 1 ? 8 : (G == 2 ? 6 : (G == 3 ? 4 : 3)); }
