@@ -19,6 +19,8 @@
 //     item are grouped by c, one branch-free software-pipelined loop per c.
 // Each output element is summed by one lane (or by WS lanes, added in a fixed order) in record
 // order and written once: no atomics, the result is bitwise reproducible.
+#include <cstddef>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan_tile.hpp"
@@ -357,13 +359,24 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
     // stage buffer: [rows of the 4 PW planes][records]
     float *buf = lds;
     const StageCtx sc{plane0, NPB, wave, lane, ps, jlc, wsi, WS, stage_floats};
+    // the task's items, read now so the epilogue waits on no load: lane q < 8 NI holds 32-bit word q of
+    // items [item_begin, item_begin + NI) (out_stride is word 3, out_off[g] word 4 + g of an item)
+    static_assert(sizeof(Item) == 32 && offsetof(Item, out_stride) == 12 && offsetof(Item, out_off) == 16,
+                  "item layout");
+    const int32_t *itw = reinterpret_cast<const int32_t *>(a.items + task.item_begin);
+    const int items_v = lane < 8 * NI ? itw[lane] : 0;
+    // Each stage's metadata is read while the previous stage's loads are in flight, so a stage costs one
+    // global round trip (its direct loads) before its contraction.
+    StageMeta m = {};
+    if (task.stage_begin < task.stage_end) m = load_meta<NI>(a, task.stage_begin, lane);
     for (int st = task.stage_begin; st < task.stage_end; ++st) {
         __syncthreads();  // the previous stage is consumed
-        const StageMeta m = load_meta<NI>(a, st, lane);
         queue_stage<PW>(a, sc, m, buf);
+        const StageMeta mn = st + 1 < task.stage_end ? load_meta<NI>(a, st + 1, lane) : m;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads have landed
         __syncthreads();                // everyone's have
         compute_stage<NI, G, PW>(a, sc, m, buf, acc);
+        m = mn;
     }
 
     if (WS > 1) {
@@ -397,15 +410,17 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
         float *dp = a.dst + (int64_t)plane * a.dst_plane;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const Item it = a.items[task.item_begin + i];
-            if (it.out_off[0] < 0) continue;  // padding item
+            const int out_stride = __builtin_amdgcn_readlane(items_v, 8 * i + 3);
+            if (__builtin_amdgcn_readlane(items_v, 8 * i + 4) < 0) continue;  // padding item
 #pragma unroll
-            for (int g = 0; g < G; ++g)
+            for (int g = 0; g < G; ++g) {
+                const int out_off = __builtin_amdgcn_readlane(items_v, 8 * i + 4 + g);
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const int j = jl + t;
-                    if (j < a.L) dp[(int64_t)it.out_off[g] + (int64_t)it.out_stride * j] = acc[i][g][t];
+                    if (j < a.L) dp[(int64_t)out_off + (int64_t)out_stride * j] = acc[i][g][t];
                 }
+            }
         }
     }
 }
