@@ -87,9 +87,13 @@ struct FusedLaunch {
     const Seg *segs;
     const float *vals;
     int32_t B, C, Co, K, Ho, Wo, Hi, Wi, in_stride;
+    const float *Wa = nullptr;  // fp32 data: W packed by launch_pack_wa_f32 (required)
 };
 
 hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream);
+// fp32 fused kernel: floats of W packed in its A-operand order (0 when K is outside 1 .. 64), and the packing
+int64_t fused_wa_f32_floats(int Co, int C, int K);
+hipError_t launch_pack_wa_f32(const float *W, float *Wa, int Co, int C, int K, hipStream_t stream);
 
 struct FusedMfmaLaunch {
     const void *x, *W;

@@ -259,10 +259,32 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
 
 // fp32 data: the same block structure with an fp32 contraction tile and the einsum on the fp32
 // matrix cores (v_mfma_f32_16x16x4_f32: A = W, 16 output channels x 4 rows; B = the tile, 4 rows x
-// 16 pixels), fp32 products and accumulation throughout.
+// 16 pixels), fp32 products and accumulation throughout.  W arrives packed in A-operand order
+// (launch_pack_wa_f32): an A operand spans 16 output channels whose W rows lie C K floats apart, so
+// loading it from W itself would touch 16 cache lines per 4-byte load.
+
+// Packed W for fused_f32_kernel: for chunk t (channels c0 = t CC .. + CC - 1, CC = kR / K), 16-channel
+// output tile o16, step quadruple kq and lane l, the float4 Wa[((t n_ot16 + o16) (kR / 16) + kq) 64 + l]
+// holds, for j = 0..3, W[o][c0 K + rr] with o = 16 o16 + l % 16 and rr = 4 (4 kq + j) + l / 16 — the A
+// operand of step 4 kq + j for that lane — and zero where o >= Co or rr reaches past the chunk's
+// channels.
+__global__ __launch_bounds__(256) void pack_wa_f32_kernel(const float *__restrict__ W, float *__restrict__ Wa, int Co,
+                                                          int C, int K, int64_t total)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int j = (int)(i & 3), l = (int)((i >> 2) & 63), kq = (int)((i >> 8) % (kR / 16));
+    const int64_t rest = (i >> 8) / (kR / 16);
+    const int n_ot16 = (Co + 15) / 16;
+    const int o16 = (int)(rest % n_ot16);
+    const int t = (int)(rest / n_ot16);
+    const int CC = kR / K, c0 = t * CC, ccn = min(CC, C - c0);
+    const int o = 16 * o16 + (l & 15), rr = 4 * (4 * kq + j) + (l >> 4);
+    Wa[i] = (o < Co && rr < ccn * K) ? W[((int64_t)o * C + c0) * K + rr] : 0.0f;
+}
 constexpr int kLdsStride32 = kR + 4;  // floats per pixel row (the 16 lanes of a row group hit distinct banks)
 
-__global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__restrict__ x, const float *__restrict__ W,
+__global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__restrict__ x, const float4 *__restrict__ Wa,
                                                              float *__restrict__ y, const Item *__restrict__ items,
                                                              const int32_t *__restrict__ block_ptr,
                                                              const int32_t *__restrict__ ho_order,
@@ -287,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
     const int wo0 = pt * kPx;
     const int o_base = ob * kOBlk + wave * 64;
     const int CC = kR / K;
+    const int n_ot16 = (Co + 15) / 16;
     const int64_t plane_sz = (int64_t)Hi * Wi;
     const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
     const int HoWo = Ho * Wo;
@@ -307,21 +330,31 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
             if (r >= ccn * K) tile[px * kLdsStride32 + r] = 0.0f;
         }
         __syncthreads();
-        const int rvalid = ccn * K;
         const int rl = lane >> 4;  // the lane's row within a 4-row step
-#pragma unroll 4
-        for (int ks = 0; ks < kR / 4; ++ks) {
-            const int rr = ks * 4 + rl;
-            float bop[4];
+        // A operands of the chunk's 16 steps: W packed by launch_pack_wa_f32, one 16-byte load per lane and
+        // output-channel tile for four steps (zeros past Co and past the chunk's ccn K rows)
+        const float4 *wq = Wa + (int64_t)(c0 / CC) * n_ot16 * (kR / 16) * 64 + lane;
 #pragma unroll
-            for (int p4 = 0; p4 < 4; ++p4) bop[p4] = tile[(p4 * 16 + (lane & 15)) * kLdsStride32 + rr];
+        for (int kq = 0; kq < kR / 16; ++kq) {
+            float4 aq[4];
 #pragma unroll
             for (int ot = 0; ot < 4; ++ot) {
-                const int o = o_base + ot * 16 + (lane & 15);
-                const float aop = (o < Co && rr < rvalid) ? W[((int64_t)o * C + c0) * K + rr] : 0.0f;
+                const int o16 = (o_base >> 4) + ot;
+                aq[ot] = o16 < n_ot16 ? wq[((int64_t)o16 * (kR / 16) + kq) * 64] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
 #pragma unroll
-                for (int p4 = 0; p4 < 4; ++p4)
-                    acc[ot][p4] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop[p4], acc[ot][p4], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const int rr = (4 * kq + j) * 4 + rl;
+                float bop[4];
+#pragma unroll
+                for (int p4 = 0; p4 < 4; ++p4) bop[p4] = tile[(p4 * 16 + (lane & 15)) * kLdsStride32 + rr];
+#pragma unroll
+                for (int ot = 0; ot < 4; ++ot) {
+                    const float aop = j == 0 ? aq[ot].x : j == 1 ? aq[ot].y : j == 2 ? aq[ot].z : aq[ot].w;
+#pragma unroll
+                    for (int p4 = 0; p4 < 4; ++p4)
+                        acc[ot][p4] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, bop[p4], acc[ot][p4], 0, 0, 0);
+                }
             }
         }
     }
@@ -346,11 +379,12 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
     const int n_pt = (a.Wo + kPx - 1) / kPx;
     const int n_ob = (a.Co + kOBlk - 1) / kOBlk;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pt;
-    if (a.f32)
+    if (a.f32) {
+        if (!a.Wa && a.C > 0) return hipErrorInvalidValue;  // the fp32 kernel takes W packed (launch_pack_wa_f32)
         hipLaunchKernelGGL(fused_f32_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const float *)a.x,
-                           (const float *)a.W, (float *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
+                           (const float4 *)a.Wa, (float *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
-    else if (a.f16)
+    } else if (a.f16)
         hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
                            (const f16_t *)a.W, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
@@ -358,6 +392,22 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
         hipLaunchKernelGGL(fused_kernel<bf16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const bf16_t *)a.x,
                            (const bf16_t *)a.W, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    return hipGetLastError();
+}
+
+int64_t fused_wa_f32_floats(int Co, int C, int K)
+{
+    if (K < 1 || K > kR) return 0;
+    const int64_t CC = kR / K, n_chunks = (C + CC - 1) / CC, n_ot16 = (Co + 15) / 16;
+    return n_chunks * n_ot16 * (kR / 16) * 64 * 4;
+}
+
+hipError_t launch_pack_wa_f32(const float *W, float *Wa, int Co, int C, int K, hipStream_t stream)
+{
+    const int64_t total = fused_wa_f32_floats(Co, C, K);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_wa_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, W, Wa, Co, C, K,
+                       total);
     return hipGetLastError();
 }
 

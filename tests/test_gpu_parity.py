@@ -879,6 +879,20 @@ FUSED_F32_CFGS = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_with_no_input_channels_writes_zeros(dtype):
+    """C = 0: y is an empty sum, so every output is written as zero (fp32 allocates no packed W then)."""
+    psi = build_psi(19, 144, 19, 72, 0.7, 4, 2)
+    h = gpu_psi(psi)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    x = torch.empty((2, 0, psi.Hi, psi.Wi), dtype=tdt, device=DEV)
+    W = torch.empty((40, 0, psi.K), dtype=tdt, device=DEV)
+    y = nan_like((2, 40, psi.Ho, psi.Wo), tdt)
+    sgc.disco_fused_conv(h, x, W, y)
+    torch.cuda.synchronize()
+    assert bool((y == 0).all())
+
+
 @pytest.mark.parametrize("cfg", FUSED_F32_CFGS)
 def test_fused_f32_agrees_with_oracle(cfg):
     Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
