@@ -32,6 +32,10 @@ struct DevPlan {
     int32_t *block_ptr = nullptr;
     int32_t n_items = 0;
     int32_t L = 0, in_stride = 1;
+    // the forward plan's source windows for the fp32 fused kernel (plan.hpp, FusedWindows)
+    disco::FWin *fw_rows = nullptr;
+    int32_t *fw_ho_ptr = nullptr, *fw_ho_len = nullptr, *fw_seg_off = nullptr;
+    int32_t fw_cap = 0;  // positions per channel of the kernel's LDS area (0: no windows)
 };
 
 constexpr int kStagedLdsBudget = 40 * 1024;  // bytes of LDS per block (four blocks per CU)
@@ -100,6 +104,10 @@ void free_plan(DevPlan &p)
     (void)hipFree(p.segs);
     (void)hipFree(p.vals);
     (void)hipFree(p.block_ptr);
+    (void)hipFree(p.fw_rows);
+    (void)hipFree(p.fw_ho_ptr);
+    (void)hipFree(p.fw_ho_len);
+    (void)hipFree(p.fw_seg_off);
     p = DevPlan();
 }
 
@@ -212,6 +220,18 @@ hipError_t upload_plan(DevPlan &d, const disco::GatherPlan &p)
     d.n_items = (int32_t)p.items.size();
     d.L = p.L;
     d.in_stride = p.in_stride;
+    return hipSuccess;
+}
+
+hipError_t upload_windows(DevPlan &d, const disco::FusedWindows &w, int K)
+{
+    hipError_t e;
+    if (w.rows.empty()) return hipSuccess;
+    if ((e = upload(&d.fw_rows, w.rows)) != hipSuccess) return e;
+    if ((e = upload(&d.fw_ho_ptr, w.ho_ptr)) != hipSuccess) return e;
+    if ((e = upload(&d.fw_ho_len, w.ho_len)) != hipSuccess) return e;
+    if ((e = upload(&d.fw_seg_off, w.seg_off)) != hipSuccess) return e;
+    d.fw_cap = disco::fused_win_cap_f32(K, w.ho_len.data(), (int)w.ho_len.size());
     return hipSuccess;
 }
 
@@ -687,9 +707,11 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     if (st != DISCO_OK) return st;
 
     disco::GatherPlan fp, bp;
+    disco::FusedWindows fw;
     try {
         disco::build_forward_plan(v, fp);
         disco::build_backward_plan(v, bp);
+        disco::build_fused_windows(fp, disco::fused_tile_px(), fw);
     } catch (const std::bad_alloc &) {
         return fail(DISCO_ERR_OOM, "host allocation failed while building the plan");
     }
@@ -776,6 +798,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     h->K = csr->K; h->Ho = csr->Ho; h->Wo = csr->Wo; h->Hi = csr->Hi; h->Wi = csr->Wi;
     h->nnz = csr->nnz;
     hipError_t e = upload_plan(h->fwd, fp);
+    if (e == hipSuccess) e = upload_windows(h->fwd, fw, csr->K);
     if (e == hipSuccess) e = upload_plan(h->bwd, bp);
     if (e == hipSuccess) e = upload(&h->ho_order, ho_order);
     for (int d = 0; d < 2 && e == hipSuccess; ++d) {
@@ -985,6 +1008,13 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
     a.Ho = h->Ho; a.Wo = h->Wo; a.Hi = h->Hi; a.Wi = h->Wi;
     a.in_stride = h->fwd.in_stride;
     a.Wa = wa;
+    if (!getenv_is0("DISCO_FUSED_WIN")) {  // test knob: "0" makes the fp32 fused kernel read x from global memory
+        a.fw_rows = h->fwd.fw_rows;
+        a.fw_ho_ptr = h->fwd.fw_ho_ptr;
+        a.fw_ho_len = h->fwd.fw_ho_len;
+        a.fw_seg_off = h->fwd.fw_seg_off;
+        a.fw_cap = h->fwd.fw_cap;
+    }
     hipError_t e = disco::launch_fused(a, (hipStream_t)stream);
     if (wa) {
         const hipError_t ef = hipFreeAsync(wa, (hipStream_t)stream);

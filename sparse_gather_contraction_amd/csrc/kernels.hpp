@@ -88,9 +88,17 @@ struct FusedLaunch {
     const float *vals;
     int32_t B, C, Co, K, Ho, Wo, Hi, Wi, in_stride;
     const float *Wa = nullptr;  // fp32 data: W packed by launch_pack_wa_f32 (required)
+    // fp32 data: the forward plan's source windows (plan.hpp, FusedWindows; null: global reads) and the
+    // positions per channel the kernel's LDS area holds (fused_win_cap_f32)
+    const FWin *fw_rows = nullptr;
+    const int32_t *fw_ho_ptr = nullptr, *fw_ho_len = nullptr, *fw_seg_off = nullptr;
+    int32_t fw_cap = 0;
 };
 
 hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream);
+// fp32 fused kernel: positions per channel of its LDS window area for this plan (latitudes with more
+// read their sources from global memory)
+int fused_win_cap_f32(int K, const int32_t *ho_len, int nho);
 // fp32 fused kernel: floats of W packed in its A-operand order (0 when K is outside 1 .. 64), and the packing
 int64_t fused_wa_f32_floats(int Co, int C, int K);
 hipError_t launch_pack_wa_f32(const float *W, float *Wa, int Co, int C, int K, hipStream_t stream);
@@ -180,6 +188,7 @@ hipError_t launch_fwd_mfma(const FwdMfmaLaunch &a, hipStream_t stream);
 int fwd_mfma_channels(int kr);       // channels per forward workgroup for a psi group of kr rows
 size_t fused_mfma_reserved_bytes();  // LDS bytes besides the two piece stage buffers
 int fused_max_k();  // largest K the fused kernel accepts
+int fused_tile_px();  // output longitudes per workgroup of the vector-ALU fused kernels
 
 // C[m][n] = sum_k A[m][k] B[n][k] on bf16 (or fp16) matrix cores (operands contiguous along k; k
 // ranges and Kd multiples of 8; operand buffers below 2 GiB).  out_f32: fp32 partials [split][M][N],

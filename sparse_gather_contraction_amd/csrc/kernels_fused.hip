@@ -13,6 +13,9 @@
 // A operand (16 o x 32 rows) and the LDS tile as the B operand (32 rows x 16
 // pixels), fp32 accumulation in registers across all chunks.  fp32 data keeps
 // the chunk in fp32 and runs the einsum on v_mfma_f32_16x16x4_f32.
+#include <algorithm>
+#include <climits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -26,6 +29,7 @@ constexpr int kPx = 64;        // output longitudes per block
 constexpr int kOBlk = 256;     // output channels per block (64 per wave)
 constexpr int kR = 64;         // reduction rows (c*K + k) per chunk: two MFMA k-steps
 constexpr int kLdsStride = kR + 8;  // 16-bit elements per pixel row in LDS (16-byte aligned rows)
+constexpr int kFusedWinBytes = 16 * 1024;  // fp32: LDS for a chunk's source windows
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -59,6 +63,84 @@ template <> struct Elem<float> {  // fp32 data (the contraction's loads and tile
     static __device__ __forceinline__ float to_f32(float v) { return v; }
     static __device__ __forceinline__ float from_f32(float v) { return v; }
 };
+
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// Raw buffer resource over `bytes` bytes at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// fp32 windows: the chunk's source windows (plan.hpp, FusedWindows) into LDS by direct global -> LDS
+// loads, one 4-byte load per staged position; (row, channel) pairs go round the four waves, lane l of an
+// instruction writing position q0 + l.  win: [channel][wl positions]; xb: the batch's channel planes.
+__device__ __forceinline__ void stage_fwin_f32(const float *__restrict__ xb, float *win, const FWin *__restrict__ rows,
+                                               int r0, int r1, int wl, int64_t plane_sz, int c0, int ccn, int Wo,
+                                               int in_stride, int wo0, int wave, int lane)
+{
+    const int nj = (r1 - r0) * ccn;
+    for (int job = wave; job < nj; job += kThreads / 64) {
+        const int r = r0 + job / ccn, cl = job - (job / ccn) * ccn;
+        const FWin w = rows[r];
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(xb + (int64_t)(c0 + cl) * plane_sz, 4u * (uint32_t)plane_sz);
+        for (int q0 = 0; q0 < w.len; q0 += 64) {
+            const int q = q0 + lane;
+            const int idx = (w.a + wo0 + q) % Wo;
+            if (q < w.len)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(win + cl * wl + w.base + q0), 4,
+                                                         4u * (uint32_t)(w.in_off + in_stride * idx), 0, 0, 0);
+        }
+    }
+}
+
+// The fp32 chunk's contraction from the staged windows: as contract_chunk, but a segment's entry t at
+// pixel px reads window position seg_off + t + px of its channel (no modulo, no global load).
+template <int NB, int NP, int G>
+__device__ __forceinline__ void contract_batch_win(const float *const (&lw)[NP], const float *__restrict__ v, int t,
+                                                   int pos, float (&acc)[NP][kMaxGroup])
+{
+    float xv[NP][NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) xv[p][u] = lw[p][pos + u];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float w = v[(t + u) * G + g];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) acc[p][g] = fmaf(w, xv[p][u], acc[p][g]);
+        }
+}
+
+template <int NP, int G>
+__device__ __forceinline__ void contract_item_win(const float *const (&lw)[NP], const Item &it,
+                                                  const Seg *__restrict__ segs, const int32_t *__restrict__ seg_off,
+                                                  const float *__restrict__ vals, int px, float (&acc)[NP][kMaxGroup])
+{
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[p][g] = 0.0f;
+    for (int q = it.seg_begin; q < it.seg_end; ++q) {
+        const Seg sg = segs[q];
+        const float *v = vals + sg.val_off;
+        const int pos = seg_off[q] + px;
+        int t = 0;
+        for (; t + 8 <= sg.m; t += 8) contract_batch_win<8, NP, G>(lw, v, t, pos + t, acc);
+        if (t + 4 <= sg.m) {
+            contract_batch_win<4, NP, G>(lw, v, t, pos + t, acc);
+            t += 4;
+        }
+        if (t + 2 <= sg.m) {
+            contract_batch_win<2, NP, G>(lw, v, t, pos + t, acc);
+            t += 2;
+        }
+        if (t < sg.m) contract_batch_win<1, NP, G>(lw, v, t, pos + t, acc);
+    }
+}
 
 // NB entries of a segment from entry t, for NP channel planes at once: the NB * NP x loads go out
 // together, then the multiply-adds in entry order; base = (j0 + t + wo) mod Wo on entry, advanced past
@@ -162,6 +244,50 @@ __device__ __forceinline__ void contract_chunk(const T *__restrict__ xb, S *__re
                     for (int g = 0; g < it.G; ++g) {
                         const int k = it.out_off[g] / HoWo;
                         tile[px * STRIDE + cl[p] * K + k] = Elem<S>::from_f32(valid[p] ? a[p][g] : 0.0f);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// contract_chunk for fp32 data from the chunk's staged windows (win: [channel][wl positions]); the same
+// multiply-adds in the same order, so the same sums.
+template <int STRIDE>
+__device__ __forceinline__ void contract_chunk_win(const float *win, int wl, float *__restrict__ tile,
+                                                   const Item *__restrict__ items, const Seg *__restrict__ segs,
+                                                   const int32_t *__restrict__ seg_off, const float *__restrict__ vals,
+                                                   int it_begin, int it_end, int ccn, int CC, int K, int Wo, int HoWo,
+                                                   int wo0, int tid)
+{
+    constexpr int NP = 2;
+    const int cl0 = tid / kPx, px = tid - cl0 * kPx;
+    const int wo = wo0 + px;
+    for (int cb = 0; cb < CC; cb += 4 * NP) {
+        const float *lw[NP];
+        bool valid[NP];
+        int cl[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            cl[p] = cb + cl0 + 4 * p;
+            valid[p] = cl[p] < ccn && wo < Wo;
+            lw[p] = win + (cl[p] < ccn ? cl[p] : 0) * wl;  // channels past the chunk read staged data, dropped
+        }
+        for (int ii = it_begin; ii < it_end; ++ii) {
+            const Item it = items[ii];
+            float a[NP][kMaxGroup];
+            switch (it.G) {
+            case 1: contract_item_win<NP, 1>(lw, it, segs, seg_off, vals, px, a); break;
+            case 2: contract_item_win<NP, 2>(lw, it, segs, seg_off, vals, px, a); break;
+            case 3: contract_item_win<NP, 3>(lw, it, segs, seg_off, vals, px, a); break;
+            default: contract_item_win<NP, 4>(lw, it, segs, seg_off, vals, px, a); break;
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (cl[p] < CC) {
+                    for (int g = 0; g < it.G; ++g) {
+                        const int k = it.out_off[g] / HoWo;
+                        tile[px * STRIDE + cl[p] * K + k] = valid[p] ? a[p][g] : 0.0f;
                     }
                 }
             }
@@ -291,9 +417,13 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
                                                              const Seg *__restrict__ segs,
                                                              const float *__restrict__ vals, int B, int C, int Co,
                                                              int K, int Ho, int Wo, int Hi, int Wi, int in_stride,
-                                                             int n_pt, int n_ob)
+                                                             int n_pt, int n_ob, const FWin *__restrict__ fw_rows,
+                                                             const int32_t *__restrict__ fw_ho_ptr,
+                                                             const int32_t *__restrict__ fw_ho_len,
+                                                             const int32_t *__restrict__ seg_off, int wcap)
 {
     __shared__ __attribute__((aligned(16))) float tile[kPx * kLdsStride32];
+    extern __shared__ __attribute__((aligned(16))) float win[];  // [CC][wl]: the chunk's source windows
 
     int bid = blockIdx.x;
     const int pt = bid % n_pt;
@@ -313,6 +443,12 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
     const int64_t plane_sz = (int64_t)Hi * Wi;
     const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
     const int HoWo = Ho * Wo;
+    // the latitude's windows when the launch has them (wcap > 0; else the tables are not passed) and they
+    // fit the LDS area (wcap positions per channel), else global reads
+    const int wl = wcap > 0 ? fw_ho_len[ho] : 0;
+    const bool use_win = wcap > 0 && wl <= wcap;
+    const int r0 = use_win ? fw_ho_ptr[ho] : 0, r1 = use_win ? fw_ho_ptr[ho + 1] : 0;
+    const float *xb = x + (int64_t)b * C * plane_sz;
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -322,9 +458,17 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
 
     for (int c0 = 0; c0 < C; c0 += CC) {
         const int ccn = min(CC, C - c0);
-        __syncthreads();  // the previous chunk's MFMA reads of `tile` are done
-        contract_chunk<float, float, kLdsStride32>(x + (int64_t)b * C * plane_sz, tile, items, segs, vals, it_begin,
-                                                   it_end, plane_sz, c0, ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
+        __syncthreads();  // the previous chunk's MFMA reads of `tile` and window reads are done
+        if (use_win) {
+            stage_fwin_f32(xb, win, fw_rows, r0, r1, wl, plane_sz, c0, ccn, Wo, in_stride, wo0, wave, lane);
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's window loads have landed
+            __syncthreads();                // everyone's have
+            contract_chunk_win<kLdsStride32>(win, wl, tile, items, segs, seg_off, vals, it_begin, it_end, ccn, CC, K,
+                                             Wo, HoWo, wo0, tid);
+        } else {
+            contract_chunk<float, float, kLdsStride32>(xb, tile, items, segs, vals, it_begin, it_end, plane_sz, c0,
+                                                       ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
+        }
         for (int e = tid; e < kPx * kR; e += kThreads) {
             const int px = e / kR, r = e - px * kR;
             if (r >= ccn * K) tile[px * kLdsStride32 + r] = 0.0f;
@@ -381,9 +525,17 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pt;
     if (a.f32) {
         if (!a.Wa && a.C > 0) return hipErrorInvalidValue;  // the fp32 kernel takes W packed (launch_pack_wa_f32)
-        hipLaunchKernelGGL(fused_f32_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const float *)a.x,
+        // windows in LDS where the plan has them and a channel plane is below 2 GiB (32-bit load offsets)
+        const bool win_ok = a.fw_rows && a.fw_ho_ptr && a.fw_ho_len && a.fw_seg_off && a.fw_cap > 0 &&
+                            (int64_t)a.Hi * a.Wi <= INT32_MAX / 4;
+        const int wcap = win_ok ? a.fw_cap : 0;
+        const size_t lds = (size_t)(kR / a.K) * wcap * sizeof(float);
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(&fused_f32_kernel), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fused_f32_kernel, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const float *)a.x,
                            (const float4 *)a.Wa, (float *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
-                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob, a.fw_rows, a.fw_ho_ptr,
+                           a.fw_ho_len, a.fw_seg_off, wcap);
     } else if (a.f16)
         hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
                            (const f16_t *)a.W, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
@@ -393,6 +545,17 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
                            (const bf16_t *)a.W, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
     return hipGetLastError();
+}
+
+int fused_win_cap_f32(int K, const int32_t *ho_len, int nho)
+{
+    // positions per channel of the largest latitude window set within kFusedWinBytes
+    if (K < 1 || K > kR) return 0;
+    const int64_t cc = kR / K;
+    int cap = 0;
+    for (int i = 0; i < nho; ++i)
+        if ((int64_t)ho_len[i] * cc * (int64_t)sizeof(float) <= kFusedWinBytes) cap = std::max(cap, ho_len[i]);
+    return cap;
 }
 
 int64_t fused_wa_f32_floats(int Co, int C, int K)
@@ -412,5 +575,7 @@ hipError_t launch_pack_wa_f32(const float *W, float *Wa, int Co, int C, int K, h
 }
 
 int fused_max_k() { return kR; }
+
+int fused_tile_px() { return kPx; }
 
 }  // namespace disco

@@ -396,4 +396,55 @@ void build_staged_plan(const CSRView &c, const GatherPlan &p, bool backward, int
     out.ok = true;
 }
 
+void build_fused_windows(const GatherPlan &p, int32_t px, FusedWindows &out)
+{
+    out = FusedWindows();
+    const int32_t L = p.L;
+    const int32_t nb = p.block_ptr.empty() ? 0 : (int32_t)p.block_ptr.size() - 1;
+    out.ho_ptr.assign(1, 0);
+    out.ho_len.assign(nb, 0);
+    out.seg_off.assign(p.segs.size(), 0);
+    for (int32_t b = 0; b < nb; ++b) {
+        // segments of the block by source row
+        std::vector<std::pair<int32_t, int32_t>> by_row;  // (in_off, segment)
+        for (int32_t i = p.block_ptr[b]; i < p.block_ptr[b + 1]; ++i)
+            for (int32_t q = p.items[i].seg_begin; q < p.items[i].seg_end; ++q) by_row.push_back({p.segs[q].in_off, q});
+        std::sort(by_row.begin(), by_row.end());
+        int32_t base = 0;
+        for (size_t r0 = 0; r0 < by_row.size();) {
+            size_t r1 = r0;
+            while (r1 < by_row.size() && by_row[r1].first == by_row[r0].first) ++r1;
+            // shortest arc: start at one segment's first shift, cover every segment's shifts (mod L)
+            int32_t best_a = 0, best_span = INT32_MAX;
+            for (size_t u = r0; u < r1; ++u) {
+                const int32_t a = p.segs[by_row[u].second].j0;
+                int32_t span = 0;
+                for (size_t v = r0; v < r1; ++v) {
+                    const Seg &sg = p.segs[by_row[v].second];
+                    span = std::max(span, (sg.j0 - a + L) % L + sg.m);
+                }
+                if (span < best_span) {
+                    best_span = span;
+                    best_a = a;
+                }
+            }
+            FWin w;
+            w.in_off = by_row[r0].first;
+            w.a = best_a;
+            w.len = best_span + px - 1;
+            w.base = base;
+            for (size_t v = r0; v < r1; ++v) {
+                const int32_t q = by_row[v].second;
+                out.seg_off[q] = base + (p.segs[q].j0 - best_a + L) % L;
+            }
+            out.rows.push_back(w);
+            base += w.len;
+            r0 = r1;
+        }
+        out.ho_len[b] = base;
+        out.max_len = std::max(out.max_len, base);
+        out.ho_ptr.push_back((int32_t)out.rows.size());
+    }
+}
+
 }  // namespace disco

@@ -117,4 +117,27 @@ std::string validate_csr(const CSRView &c, int *code);
 void build_forward_plan(const CSRView &c, GatherPlan &p);
 void build_backward_plan(const CSRView &c, GatherPlan &p);
 
+// ---------------------------------------------------------------------------
+// Source windows of the vector-ALU fused kernels (kernels_fused.hip): per output latitude (block b of
+// the forward plan), its distinct source rows, each with the shortest circular arc of shifts
+// [a, a + span) that its segments read.  A workgroup of `px` output longitudes from wo0 stages, per
+// channel, positions (a + wo0 + q) mod L, q < span + px - 1, of every such row back to back; segment q
+// of the plan then reads entry t at longitude wo0 + p from staged position seg_off[q] + t + p.
+struct FWin {           // 16 bytes
+    int32_t in_off;     // source row within a plane (in_stride apart positions)
+    int32_t a;          // first shift of the arc, in [0, L)
+    int32_t len;        // staged positions: span + px - 1
+    int32_t base;       // first staged position of the row within the latitude's area
+};
+
+struct FusedWindows {
+    std::vector<int32_t> ho_ptr;   // [blocks + 1]: rows of block b
+    std::vector<FWin> rows;
+    std::vector<int32_t> ho_len;   // [blocks]: staged positions per channel (sum of the rows' len)
+    std::vector<int32_t> seg_off;  // [segments]: base of its row + ((j0 - a) mod L)
+    int32_t max_len = 0;           // largest ho_len
+};
+
+void build_fused_windows(const GatherPlan &p, int32_t px, FusedWindows &out);
+
 }  // namespace disco

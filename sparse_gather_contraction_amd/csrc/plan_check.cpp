@@ -132,6 +132,75 @@ void check_gather(const CSRView &c, const GatherPlan &p, bool backward, const st
     compare(got, want, writes, what);
 }
 
+// ---- source windows of the vector-ALU fused kernels (plan.hpp, FusedWindows) -----------------------
+// Replays the fp32 fused kernel's contraction from staged windows: for every latitude and tile of px
+// output longitudes, the window image as the staging writes it, then every entry's read at
+// seg_off + t + (wo - wo0), which must stay inside its own row's staged positions.
+void check_windows(const CSRView &c, const GatherPlan &p, const FusedWindows &w, int px, const std::vector<double> &x,
+                   const std::vector<double> &want)
+{
+    const std::string what = "fused windows";
+    const int32_t L = p.L, nb = (int32_t)p.block_ptr.size() - 1;
+    check(w.ho_ptr.size() == (size_t)nb + 1 && w.ho_len.size() == (size_t)nb && w.seg_off.size() == p.segs.size(),
+          what + ": table sizes");
+    if (w.ho_ptr.size() != (size_t)nb + 1 || w.ho_len.size() != (size_t)nb || w.seg_off.size() != p.segs.size()) return;
+    const int64_t src_plane = (int64_t)c.Hi * c.Wi, dst_plane = (int64_t)c.K * c.Ho * c.Wo;
+    std::vector<double> got(dst_plane, 0.0);
+    std::vector<int> writes(dst_plane, 0);
+    for (int32_t b = 0; b < nb; ++b) {
+        const int32_t r0 = w.ho_ptr[b], r1 = w.ho_ptr[b + 1];
+        check(0 <= r0 && r0 <= r1 && r1 <= (int32_t)w.rows.size(), what + ": row range");
+        if (!(0 <= r0 && r0 <= r1 && r1 <= (int32_t)w.rows.size())) return;
+        int32_t base = 0;
+        for (int32_t r = r0; r < r1; ++r) {
+            const FWin &fr = w.rows[r];
+            check(fr.base == base && fr.len >= px && fr.a >= 0 && fr.a < L, what + ": row fields");
+            check(fr.in_off >= 0 && (int64_t)fr.in_off + (int64_t)p.in_stride * (L - 1) < src_plane,
+                  what + ": row out of the plane");
+            if ((int64_t)fr.in_off + (int64_t)p.in_stride * (L - 1) >= src_plane || fr.in_off < 0) return;
+            base += fr.len;
+        }
+        check(base == w.ho_len[b], what + ": latitude length");
+        for (int32_t wo0 = 0; wo0 < L; wo0 += px) {
+            std::vector<double> img((size_t)std::max(base, 0), NAN);
+            for (int32_t r = r0; r < r1; ++r) {
+                const FWin &fr = w.rows[r];
+                for (int32_t q = 0; q < fr.len; ++q)
+                    img[(size_t)fr.base + q] = x[(size_t)fr.in_off + (size_t)p.in_stride * ((fr.a + wo0 + q) % L)];
+            }
+            for (int32_t i = p.block_ptr[b]; i < p.block_ptr[b + 1]; ++i) {
+                const Item &it = p.items[i];
+                for (int32_t j = wo0; j < std::min(L, wo0 + px); ++j) {
+                    double acc[kMaxGroup] = {0.0, 0.0, 0.0, 0.0};
+                    for (int32_t q = it.seg_begin; q < it.seg_end; ++q) {
+                        const Seg &sg = p.segs[q];
+                        int32_t rr = -1;  // the segment's row
+                        for (int32_t r = r0; r < r1; ++r)
+                            if (w.rows[r].in_off == sg.in_off) rr = r;
+                        check(rr >= 0, what + ": segment without a row");
+                        if (rr < 0) return;
+                        const FWin &fr = w.rows[rr];
+                        for (int32_t t = 0; t < sg.m; ++t) {
+                            const int64_t pos = (int64_t)w.seg_off[q] + t + (j - wo0);
+                            check(pos >= fr.base && pos < (int64_t)fr.base + fr.len, what + ": read outside its row");
+                            if (pos < fr.base || pos >= (int64_t)fr.base + fr.len) return;
+                            for (int g = 0; g < it.G; ++g) acc[g] += (double)p.vals[sg.val_off + t * it.G + g] * img[pos];
+                        }
+                    }
+                    for (int g = 0; g < it.G; ++g) {
+                        const int64_t o = (int64_t)it.out_off[g] + (int64_t)it.out_stride * j;
+                        check(o >= 0 && o < dst_plane, what + ": store out of the plane");
+                        if (o < 0 || o >= dst_plane) return;
+                        got[o] = acc[g];
+                        writes[o]++;
+                    }
+                }
+            }
+        }
+    }
+    compare(got, want, writes, what.c_str());
+}
+
 // ---- LDS-staged gather (kernels_staged.hip) ----------------------------------------------------
 void check_staged(const CSRView &c, const StagedPlan &sp, bool backward, int elem_bytes, int lds_budget,
                   const std::vector<double> &src, const std::vector<double> &want)
@@ -697,6 +766,9 @@ int main(int argc, char **argv)
     build_backward_plan(c, bp);
     check_gather(c, fp, false, x, want_f);
     check_gather(c, bp, true, g, want_b);
+    FusedWindows fw;
+    build_fused_windows(fp, 64, fw);  // the vector-ALU fused kernels' 64-longitude tiles
+    check_windows(c, fp, fw, 64, x, want_f);
     // the library's budgets (disco_api.hip): 40 KiB per staged or tiled workgroup
     const int budget = 40 * 1024;
     for (int esz : {4, 2}) {

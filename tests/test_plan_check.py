@@ -135,6 +135,36 @@ def test_checker_catches_planted_plan_mistakes(name, tmp_path):
     assert r.returncode == 1 and "FAIL:" in r.stdout, r.stdout[-2000:]
 
 
+WINDOW_MUTANTS = {
+    # each replaces one line of plan.cpp's window builder with a plausible mistake the checker must catch
+    "window arc one shift short": ("span = std::max(span, (sg.j0 - a + L) % L + sg.m);",
+                                   "span = std::max(span, (sg.j0 - a + L) % L + sg.m - 1);"),
+    "window offset ignores the arc start": ("out.seg_off[q] = base + (p.segs[q].j0 - best_a + L) % L;",
+                                            "out.seg_off[q] = base + p.segs[q].j0 % L;"),
+    "window misses the tile's last longitude": ("w.len = best_span + px - 1;", "w.len = best_span + px - 2;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WINDOW_MUTANTS))
+def test_checker_catches_planted_window_mistakes(name, tmp_path):
+    """Sensitivity of the fused kernels' window replay: a copy of plan.cpp with one planted mistake in
+    the window builder must fail the checker on the 181x360 workload's psi."""
+    old, new = WINDOW_MUTANTS[name]
+    src = open(os.path.join(CSRC, "plan.cpp")).read()
+    assert src.count(old) == 1, name
+    mut = tmp_path / "plan_mut.cpp"
+    mut.write_text(src.replace(old, new))
+    exe = str(tmp_path / "plan_check_mut")
+    cmd = ["g++", "-O1", "-std=c++17", "-I", CSRC, str(mut), os.path.join(CSRC, "plan_fused.cpp"),
+           os.path.join(CSRC, "plan_tile.cpp"), os.path.join(CSRC, "plan_check.cpp"), "-o", exe]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    path = str(tmp_path / "psi.csr")
+    _write_csr(workload_psi(WORKLOADS["fwdbwd_f32_181x360"]), path)
+    r = subprocess.run([exe, path], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
+    assert r.returncode == 1 and "fused windows" in r.stdout, r.stdout[-2000:]
+
+
 FUSED_MUTANTS = {
     # each replaces one line of plan_fused.cpp with a plausible mistake the checker must catch
     "psi offset drops the 8s lead": ("out.descs.push_back(2 * kr * (a_row_e + (t0 - first) + 8 * s));",
