@@ -36,6 +36,8 @@ struct DevPlan {
     disco::FWin *fw_rows = nullptr;
     int32_t *fw_ho_ptr = nullptr, *fw_ho_len = nullptr, *fw_seg_off = nullptr;
     int32_t fw_cap = 0;  // positions per channel of the kernel's LDS area (0: no windows)
+    int32_t *fw_ho_psi = nullptr;  // per latitude: its segment and value runs (null: not contiguous)
+    int32_t fw_psi_bytes = 0;      // the largest latitude's psi as the kernel copies it to LDS
 };
 
 constexpr int kStagedLdsBudget = 40 * 1024;  // bytes of LDS per block (four blocks per CU)
@@ -108,6 +110,7 @@ void free_plan(DevPlan &p)
     (void)hipFree(p.fw_ho_ptr);
     (void)hipFree(p.fw_ho_len);
     (void)hipFree(p.fw_seg_off);
+    (void)hipFree(p.fw_ho_psi);
     p = DevPlan();
 }
 
@@ -223,14 +226,21 @@ hipError_t upload_plan(DevPlan &d, const disco::GatherPlan &p)
     return hipSuccess;
 }
 
-hipError_t upload_windows(DevPlan &d, const disco::FusedWindows &w, int K)
+hipError_t upload_windows(DevPlan &d, const disco::FusedWindows &w, const disco::GatherPlan &p, int K)
 {
     hipError_t e;
     if (w.rows.empty()) return hipSuccess;
+    for (size_t b = 0; w.psi_ok && b + 1 < p.block_ptr.size(); ++b) {  // items, segments (+ offsets), values
+        const int64_t bytes = (int64_t)(p.block_ptr[b + 1] - p.block_ptr[b]) * 32 +
+                              (int64_t)(w.ho_psi[4 * b + 1] - w.ho_psi[4 * b]) * 20 +
+                              (int64_t)(w.ho_psi[4 * b + 3] - w.ho_psi[4 * b + 2]) * 4;
+        d.fw_psi_bytes = (int32_t)std::min<int64_t>(std::max<int64_t>(d.fw_psi_bytes, bytes), INT32_MAX);
+    }
     if ((e = upload(&d.fw_rows, w.rows)) != hipSuccess) return e;
     if ((e = upload(&d.fw_ho_ptr, w.ho_ptr)) != hipSuccess) return e;
     if ((e = upload(&d.fw_ho_len, w.ho_len)) != hipSuccess) return e;
     if ((e = upload(&d.fw_seg_off, w.seg_off)) != hipSuccess) return e;
+    if (w.psi_ok && (e = upload(&d.fw_ho_psi, w.ho_psi)) != hipSuccess) return e;
     d.fw_cap = disco::fused_win_cap_f32(K, w.ho_len.data(), (int)w.ho_len.size());
     return hipSuccess;
 }
@@ -798,7 +808,7 @@ disco_status disco_psi_create(const disco_csr_desc *csr, int device, disco_psi *
     h->K = csr->K; h->Ho = csr->Ho; h->Wo = csr->Wo; h->Hi = csr->Hi; h->Wi = csr->Wi;
     h->nnz = csr->nnz;
     hipError_t e = upload_plan(h->fwd, fp);
-    if (e == hipSuccess) e = upload_windows(h->fwd, fw, csr->K);
+    if (e == hipSuccess) e = upload_windows(h->fwd, fw, fp, csr->K);
     if (e == hipSuccess) e = upload_plan(h->bwd, bp);
     if (e == hipSuccess) e = upload(&h->ho_order, ho_order);
     for (int d = 0; d < 2 && e == hipSuccess; ++d) {
@@ -1014,6 +1024,10 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
         a.fw_ho_len = h->fwd.fw_ho_len;
         a.fw_seg_off = h->fwd.fw_seg_off;
         a.fw_cap = h->fwd.fw_cap;
+        if (!getenv_is0("DISCO_FUSED_PSI_LDS")) {  // test knob: "0" reads psi from memory
+            a.fw_ho_psi = h->fwd.fw_ho_psi;
+            a.fw_psi_bytes = h->fwd.fw_psi_bytes;
+        }
     }
     hipError_t e = disco::launch_fused(a, (hipStream_t)stream);
     if (wa) {

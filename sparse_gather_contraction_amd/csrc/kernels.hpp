@@ -93,6 +93,8 @@ struct FusedLaunch {
     const FWin *fw_rows = nullptr;
     const int32_t *fw_ho_ptr = nullptr, *fw_ho_len = nullptr, *fw_seg_off = nullptr;
     int32_t fw_cap = 0;
+    const int32_t *fw_ho_psi = nullptr;  // [Ho][4]: the latitude's segment and value runs (null: not contiguous)
+    int32_t fw_psi_bytes = 0;            // largest latitude's psi in LDS (items, segments, values, offsets)
 };
 
 hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream);

@@ -29,7 +29,12 @@ constexpr int kPx = 64;        // output longitudes per block
 constexpr int kOBlk = 256;     // output channels per block (64 per wave)
 constexpr int kR = 64;         // reduction rows (c*K + k) per chunk: two MFMA k-steps
 constexpr int kLdsStride = kR + 8;  // 16-bit elements per pixel row in LDS (16-byte aligned rows)
-constexpr int kFusedWinBytes = 16 * 1024;  // fp32: LDS for a chunk's source windows
+// fp32: LDS for a chunk's source windows and for the latitude's psi (registers allow two workgroups of
+// this kernel per CU, so up to 75 KiB per workgroup cost no occupancy); these budgets hold whole-ring
+// windows of 360x720 grids, so no latitude falls back to per-entry global reads, which would leave a
+// tail of polar workgroups longer than the rest of the launch
+constexpr int kFusedWinBytes = 36 * 1024;
+constexpr int kFusedPsiBytes = 24 * 1024;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -115,18 +120,21 @@ __device__ __forceinline__ void contract_batch_win(const float *const (&lw)[NP],
         }
 }
 
+// segs, seg_off and vals hold the plan's segments from s_base and values from v_base (the whole plan, or
+// the latitude's runs copied to LDS).
 template <int NP, int G>
 __device__ __forceinline__ void contract_item_win(const float *const (&lw)[NP], const Item &it,
                                                   const Seg *__restrict__ segs, const int32_t *__restrict__ seg_off,
-                                                  const float *__restrict__ vals, int px, float (&acc)[NP][kMaxGroup])
+                                                  const float *__restrict__ vals, int s_base, int v_base, int px,
+                                                  float (&acc)[NP][kMaxGroup])
 {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int g = 0; g < G; ++g) acc[p][g] = 0.0f;
-    for (int q = it.seg_begin; q < it.seg_end; ++q) {
+    for (int q = it.seg_begin - s_base; q < it.seg_end - s_base; ++q) {
         const Seg sg = segs[q];
-        const float *v = vals + sg.val_off;
+        const float *v = vals + (sg.val_off - v_base);
         const int pos = seg_off[q] + px;
         int t = 0;
         for (; t + 8 <= sg.m; t += 8) contract_batch_win<8, NP, G>(lw, v, t, pos + t, acc);
@@ -257,8 +265,8 @@ template <int STRIDE>
 __device__ __forceinline__ void contract_chunk_win(const float *win, int wl, float *__restrict__ tile,
                                                    const Item *__restrict__ items, const Seg *__restrict__ segs,
                                                    const int32_t *__restrict__ seg_off, const float *__restrict__ vals,
-                                                   int it_begin, int it_end, int ccn, int CC, int K, int Wo, int HoWo,
-                                                   int wo0, int tid)
+                                                   int it_begin, int it_end, int s_base, int v_base, int ccn, int CC,
+                                                   int K, int Wo, int HoWo, int wo0, int tid)
 {
     constexpr int NP = 2;
     const int cl0 = tid / kPx, px = tid - cl0 * kPx;
@@ -277,10 +285,10 @@ __device__ __forceinline__ void contract_chunk_win(const float *win, int wl, flo
             const Item it = items[ii];
             float a[NP][kMaxGroup];
             switch (it.G) {
-            case 1: contract_item_win<NP, 1>(lw, it, segs, seg_off, vals, px, a); break;
-            case 2: contract_item_win<NP, 2>(lw, it, segs, seg_off, vals, px, a); break;
-            case 3: contract_item_win<NP, 3>(lw, it, segs, seg_off, vals, px, a); break;
-            default: contract_item_win<NP, 4>(lw, it, segs, seg_off, vals, px, a); break;
+            case 1: contract_item_win<NP, 1>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            case 2: contract_item_win<NP, 2>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            case 3: contract_item_win<NP, 3>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            default: contract_item_win<NP, 4>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
             }
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
@@ -420,10 +428,12 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
                                                              int n_pt, int n_ob, const FWin *__restrict__ fw_rows,
                                                              const int32_t *__restrict__ fw_ho_ptr,
                                                              const int32_t *__restrict__ fw_ho_len,
-                                                             const int32_t *__restrict__ seg_off, int wcap)
+                                                             const int32_t *__restrict__ seg_off, int wcap,
+                                                             const int4 *__restrict__ fw_ho_psi, int psi_cap)
 {
     __shared__ __attribute__((aligned(16))) float tile[kPx * kLdsStride32];
-    extern __shared__ __attribute__((aligned(16))) float win[];  // [CC][wl]: the chunk's source windows
+    // dynamic LDS: [CC][wcap] floats of source windows, then psi_cap bytes for the latitude's psi
+    extern __shared__ __attribute__((aligned(16))) float win[];
 
     int bid = blockIdx.x;
     const int pt = bid % n_pt;
@@ -449,6 +459,24 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
     const bool use_win = wcap > 0 && wl <= wcap;
     const int r0 = use_win ? fw_ho_ptr[ho] : 0, r1 = use_win ? fw_ho_ptr[ho + 1] : 0;
     const float *xb = x + (int64_t)b * C * plane_sz;
+    // with windows, the latitude's items, segments, values and window offsets are copied to LDS once
+    // (psi_cap bytes after the windows) when they fit, so the 37-odd chunks read no psi from memory
+    const int4 pr = use_win && psi_cap > 0 ? fw_ho_psi[ho] : make_int4(0, 0, 0, 0);  // s0, s1, v0, v1
+    const int n_it = it_end - it_begin, n_sg = pr.y - pr.x, n_v = pr.w - pr.z;
+    const bool use_psi = use_win && psi_cap > 0 && n_it * 32 + n_sg * 20 + n_v * 4 <= psi_cap;
+    unsigned char *lpsi = reinterpret_cast<unsigned char *>(win) + ((int64_t)CC * wcap * 4 + 15) / 16 * 16;
+    Item *l_items = reinterpret_cast<Item *>(lpsi);
+    Seg *l_segs = reinterpret_cast<Seg *>(lpsi + n_it * 32);
+    float *l_vals = reinterpret_cast<float *>(lpsi + n_it * 32 + n_sg * 16);
+    int32_t *l_off = reinterpret_cast<int32_t *>(lpsi + n_it * 32 + n_sg * 16 + n_v * 4);
+    if (use_psi) {
+        const int32_t *src_it = reinterpret_cast<const int32_t *>(items + it_begin);
+        const int32_t *src_sg = reinterpret_cast<const int32_t *>(segs + pr.x);
+        for (int e = tid; e < 8 * n_it; e += kThreads) reinterpret_cast<int32_t *>(l_items)[e] = src_it[e];
+        for (int e = tid; e < 4 * n_sg; e += kThreads) reinterpret_cast<int32_t *>(l_segs)[e] = src_sg[e];
+        for (int e = tid; e < n_v; e += kThreads) l_vals[e] = vals[pr.z + e];
+        for (int e = tid; e < n_sg; e += kThreads) l_off[e] = seg_off[pr.x + e];
+    }  // visible after the chunk loop's first barrier
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -463,8 +491,12 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
             stage_fwin_f32(xb, win, fw_rows, r0, r1, wl, plane_sz, c0, ccn, Wo, in_stride, wo0, wave, lane);
             __builtin_amdgcn_s_waitcnt(0);  // this thread's window loads have landed
             __syncthreads();                // everyone's have
-            contract_chunk_win<kLdsStride32>(win, wl, tile, items, segs, seg_off, vals, it_begin, it_end, ccn, CC, K,
-                                             Wo, HoWo, wo0, tid);
+            if (use_psi)
+                contract_chunk_win<kLdsStride32>(win, wl, tile, l_items, l_segs, l_off, l_vals, 0, n_it, pr.x, pr.z,
+                                                 ccn, CC, K, Wo, HoWo, wo0, tid);
+            else
+                contract_chunk_win<kLdsStride32>(win, wl, tile, items, segs, seg_off, vals, it_begin, it_end, 0, 0,
+                                                 ccn, CC, K, Wo, HoWo, wo0, tid);
         } else {
             contract_chunk<float, float, kLdsStride32>(xb, tile, items, segs, vals, it_begin, it_end, plane_sz, c0,
                                                        ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
@@ -529,13 +561,14 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
         const bool win_ok = a.fw_rows && a.fw_ho_ptr && a.fw_ho_len && a.fw_seg_off && a.fw_cap > 0 &&
                             (int64_t)a.Hi * a.Wi <= INT32_MAX / 4;
         const int wcap = win_ok ? a.fw_cap : 0;
-        const size_t lds = (size_t)(kR / a.K) * wcap * sizeof(float);
+        const int psi_cap = wcap > 0 && a.fw_ho_psi ? std::min(a.fw_psi_bytes, kFusedPsiBytes) : 0;
+        const size_t lds = ((size_t)(kR / a.K) * wcap * sizeof(float) + 15) / 16 * 16 + (size_t)psi_cap;
         hipError_t e = allow_lds(reinterpret_cast<const void *>(&fused_f32_kernel), lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fused_f32_kernel, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const float *)a.x,
                            (const float4 *)a.Wa, (float *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob, a.fw_rows, a.fw_ho_ptr,
-                           a.fw_ho_len, a.fw_seg_off, wcap);
+                           a.fw_ho_len, a.fw_seg_off, wcap, reinterpret_cast<const int4 *>(a.fw_ho_psi), psi_cap);
     } else if (a.f16)
         hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
                            (const f16_t *)a.W, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,

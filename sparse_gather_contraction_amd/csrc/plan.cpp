@@ -444,6 +444,23 @@ void build_fused_windows(const GatherPlan &p, int32_t px, FusedWindows &out)
         out.ho_len[b] = base;
         out.max_len = std::max(out.max_len, base);
         out.ho_ptr.push_back((int32_t)out.rows.size());
+        // the latitude's segments and values as contiguous runs (the plan appends them item by item)
+        int32_t s0 = INT32_MAX, s1 = 0, v0 = INT32_MAX, v1 = 0;
+        int64_t ns = 0, nv = 0;
+        for (int32_t i = p.block_ptr[b]; i < p.block_ptr[b + 1]; ++i) {
+            const Item &it = p.items[i];
+            s0 = std::min(s0, it.seg_begin);
+            s1 = std::max(s1, it.seg_end);
+            ns += it.seg_end - it.seg_begin;
+            for (int32_t q = it.seg_begin; q < it.seg_end; ++q) {
+                v0 = std::min(v0, p.segs[q].val_off);
+                v1 = std::max(v1, p.segs[q].val_off + p.segs[q].m * it.G);
+                nv += (int64_t)p.segs[q].m * it.G;
+            }
+        }
+        if (ns == 0) s0 = s1 = v0 = v1 = 0;
+        if (ns != s1 - s0 || nv != (int64_t)v1 - v0) out.psi_ok = false;
+        out.ho_psi.insert(out.ho_psi.end(), {s0, s1, v0, v1});
     }
 }
 

@@ -136,6 +136,10 @@ struct FusedWindows {
     std::vector<int32_t> ho_len;   // [blocks]: staged positions per channel (sum of the rows' len)
     std::vector<int32_t> seg_off;  // [segments]: base of its row + ((j0 - a) mod L)
     int32_t max_len = 0;           // largest ho_len
+    // the latitude's psi as one contiguous run of the plan: segments [s0, s1), values [v0, v1) (its items
+    // are [block_ptr[b], block_ptr[b + 1])); psi_ok false when some latitude's runs are not contiguous
+    std::vector<int32_t> ho_psi;   // [blocks][4]: s0, s1, v0, v1
+    bool psi_ok = true;
 };
 
 void build_fused_windows(const GatherPlan &p, int32_t px, FusedWindows &out);

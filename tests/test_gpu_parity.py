@@ -881,19 +881,22 @@ FUSED_F32_CFGS = [
 
 @pytest.mark.parametrize("cfg", FUSED_F32_CFGS)
 def test_fused_f32_windows_equal_global_reads(cfg, monkeypatch):
-    """The fp32 fused kernel reads its sources from windows staged in LDS where a latitude's windows fit
-    (DISCO_FUSED_WIN=0: from global memory); both multiply the same values in the same order, so y must
+    """The fp32 fused kernel reads its sources from windows staged in LDS where a latitude's windows fit,
+    and the latitude's psi from an LDS copy where it fits (DISCO_FUSED_PSI_LDS=0: psi from memory;
+    DISCO_FUSED_WIN=0: everything from memory); all multiply the same values in the same order, so y must
     be bitwise equal (the configurations include caps spanning whole rings, whose windows do not fit)."""
     Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
     psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
     h = gpu_psi(psi)
     x = randn((B, C, Hi, Wi), 4200 + C).to(DEV)
     W = randn((Co, C, psi.K), 4201 + C, std=1.0 / np.sqrt(C * psi.K)).to(DEV)
+    y_lds = sgc.disco_fused_conv(h, x, W)
+    monkeypatch.setenv("DISCO_FUSED_PSI_LDS", "0")
     y_win = sgc.disco_fused_conv(h, x, W)
     monkeypatch.setenv("DISCO_FUSED_WIN", "0")
     y_glob = sgc.disco_fused_conv(h, x, W)
     torch.cuda.synchronize()
-    assert torch.equal(y_win, y_glob)
+    assert torch.equal(y_lds, y_glob) and torch.equal(y_win, y_glob)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
