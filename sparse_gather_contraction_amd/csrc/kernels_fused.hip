@@ -12,7 +12,10 @@
 // multiplied on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16} with W as the
 // A operand (16 o x 32 rows) and the LDS tile as the B operand (32 rows x 16
 // pixels), fp32 accumulation in registers across all chunks.  fp32 data keeps
-// the chunk in fp32 and runs the einsum on v_mfma_f32_16x16x4_f32.
+// the chunk in fp32 and runs the einsum on v_mfma_f32_16x16x4_f32 with W packed
+// per call in A-operand order; its contraction reads x from per-latitude source
+// windows staged in LDS for each chunk, and the latitude's psi from an LDS copy
+// made once per block (plan.hpp, FusedWindows).
 #include <algorithm>
 #include <climits>
 
@@ -29,8 +32,8 @@ constexpr int kPx = 64;        // output longitudes per block
 constexpr int kOBlk = 256;     // output channels per block (64 per wave)
 constexpr int kR = 64;         // reduction rows (c*K + k) per chunk: two MFMA k-steps
 constexpr int kLdsStride = kR + 8;  // 16-bit elements per pixel row in LDS (16-byte aligned rows)
-// fp32: LDS for a chunk's source windows and for the latitude's psi (registers allow two workgroups of
-// this kernel per CU, so up to 75 KiB per workgroup cost no occupancy); these budgets hold whole-ring
+// fp32: LDS for a chunk's source windows and for the latitude's psi (the kernel's registers allow two
+// workgroups per CU, which up to 80 KiB of LDS per workgroup keeps); these budgets hold whole-ring
 // windows of 360x720 grids, so no latitude falls back to per-entry global reads, which would leave a
 // tail of polar workgroups longer than the rest of the launch
 constexpr int kFusedWinBytes = 36 * 1024;
