@@ -118,7 +118,7 @@ MUTANTS = {
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_checker_catches_planted_plan_mistakes(name, tmp_path):
     """Sensitivity: a copy of plan_tile.cpp with one planted mistake must fail the checker on the
-    181x360 workload's psi (built without sanitizers, only the verdict matters)."""
+    181x360 workload's psi (built without sanitizers, only the outcome matters)."""
     old, new = MUTANTS[name]
     src = open(os.path.join(CSRC, "plan_tile.cpp")).read()
     assert src.count(old) == 1, name
