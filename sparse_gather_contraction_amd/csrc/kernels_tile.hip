@@ -267,14 +267,14 @@ struct StageMeta {
     int row_begin;  // into stage_rows (the plain copy path reads them there)
 };
 
+// From the stage's descriptor fields (row range in stage_rows, record bounds at stage_recptr + segptr).
 template <int NI>
-__device__ __forceinline__ StageMeta load_meta(const TileLaunch &a, int st, int lane)
+__device__ __forceinline__ StageMeta load_meta(const TileLaunch &a, int row_begin, int row_end, int segptr, int lane)
 {
-    const Stage sg = a.stages[uni(st)];
-    const int32_t *rp = a.stage_recptr + uni(sg.segptr);
+    const int32_t *rp = a.stage_recptr + uni(segptr);
     StageMeta m;
-    m.row_begin = uni(sg.row_begin);
-    m.nrows = uni(sg.row_end) - m.row_begin;
+    m.row_begin = uni(row_begin);
+    m.nrows = uni(row_end) - m.row_begin;
     m.bounds_v = lane <= NI * kTileClasses ? rp[lane] : 0;
     m.bounds_hi = (NI * kTileClasses >= 64 && lane + 64 <= NI * kTileClasses) ? rp[lane + 64] : 0;
     m.rows_v = lane < m.nrows ? a.stage_rows[m.row_begin + lane] : 0;
@@ -365,14 +365,26 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
                   "item layout");
     const int32_t *itw = reinterpret_cast<const int32_t *>(a.items + task.item_begin);
     const int items_v = lane < 8 * NI ? itw[lane] : 0;
-    // Each stage's metadata is read while the previous stage's loads are in flight, so a stage costs one
-    // global round trip (its direct loads) before its contraction.
+    // The task's stage descriptors, read now (lane j: stage stage_begin + j), so that a stage's metadata
+    // loads depend on no other load; each stage's metadata is read while the previous stage's loads are
+    // in flight, so a stage costs one global round trip (its direct loads) before its contraction.
+    const int sb = uni(task.stage_begin), se = uni(task.stage_end);
+    const int4 sv = lane < se - sb ? reinterpret_cast<const int4 *>(a.stages + sb)[lane] : make_int4(0, 0, 0, 0);
+    auto meta_of = [&](int st) {
+        const int j = uni(st - sb);
+        if (j < 64)
+            return load_meta<NI>(a, __builtin_amdgcn_readlane(sv.x, j), __builtin_amdgcn_readlane(sv.y, j),
+                                 __builtin_amdgcn_readlane(sv.z, j), lane);
+        const Stage sg = a.stages[uni(st)];  // tasks of more than 64 stages
+        return load_meta<NI>(a, sg.row_begin, sg.row_end, sg.segptr, lane);
+    };
+    static_assert(sizeof(Stage) == 16, "stage layout: row_begin, row_end, segptr, pad");
     StageMeta m = {};
-    if (task.stage_begin < task.stage_end) m = load_meta<NI>(a, task.stage_begin, lane);
-    for (int st = task.stage_begin; st < task.stage_end; ++st) {
+    if (sb < se) m = meta_of(sb);
+    for (int st = sb; st < se; ++st) {
         __syncthreads();  // the previous stage is consumed
         queue_stage<PW>(a, sc, m, buf);
-        const StageMeta mn = st + 1 < task.stage_end ? load_meta<NI>(a, st + 1, lane) : m;
+        const StageMeta mn = st + 1 < se ? meta_of(st + 1) : m;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads have landed
         __syncthreads();                // everyone's have
         compute_stage<NI, G, PW>(a, sc, m, buf, acc);
