@@ -1074,33 +1074,38 @@ def test_oversized_launch_is_refused_and_writes_nothing(monkeypatch):
     """A launch whose LDS request exceeds the device's per-workgroup LDS is refused on the host
     (DISCO_ERR_HIP) before anything is dispatched, and its output is untouched; the next call with a
     fitting request runs normally.  DISCO_TEST_LDS_EXTRA inflates the request of every kernel that asks
-    for dynamic LDS (the matrix-core kernels and the fp32 tiled gather) by 1 MiB."""
-    psi = build_psi(19, 144, 19, 72, 0.7, 4, 2)  # a shape both matrix-core kernels and the tiled gather cover
+    for dynamic LDS (the matrix-core kernels, the fp32 tiled gather and the fp32 fused kernel) by 1 MiB."""
+    psi = build_psi(19, 144, 19, 72, 0.7, 4, 2)  # a shape the matrix-core kernels and the fp32 kernels cover
     h = gpu_psi(psi)
     x = randn((2, 5, 19, 144), 4800, "bf16").to(DEV)
     x32 = randn((2, 5, 19, 144), 4802, "f32").to(DEV)
     W = randn((40, 5, psi.K), 4801, "bf16", std=0.2).to(DEV)
+    W32 = randn((40, 5, psi.K), 4803, "f32", std=0.2).to(DEV)
     ref_y = sgc.disco_fused_conv(h, x, W)
     ref_o = sgc.disco_fwd(h, x)
     ref_o32 = sgc.disco_fwd(h, x32)
+    ref_y32 = sgc.disco_fused_conv(h, x32, W32)
     torch.cuda.synchronize()
     monkeypatch.setenv("DISCO_TEST_LDS_EXTRA", str(1 << 20))
     y = nan_like((2, 40, 19, 72), torch.bfloat16)
     o = nan_like((2, 5, psi.K, 19, 72), torch.bfloat16)
     o32 = nan_like((2, 5, psi.K, 19, 72), torch.float32)
+    y32 = nan_like((2, 40, 19, 72), torch.float32)
     for call in (lambda: sgc.disco_fused_conv(h, x, W, y), lambda: sgc.disco_fwd(h, x, o),
-                 lambda: sgc.disco_fwd(h, x32, o32)):
+                 lambda: sgc.disco_fwd(h, x32, o32), lambda: sgc.disco_fused_conv(h, x32, W32, y32)):
         with pytest.raises(sgc.DiscoError) as ei:
             call()
         assert ei.value.status_name == "DISCO_ERR_HIP"
     torch.cuda.synchronize()
-    assert bool(torch.isnan(y).all()) and bool(torch.isnan(o).all()) and bool(torch.isnan(o32).all())
+    for t in (y, o, o32, y32):
+        assert bool(torch.isnan(t).all())
     monkeypatch.delenv("DISCO_TEST_LDS_EXTRA")
     sgc.disco_fused_conv(h, x, W, y)
     sgc.disco_fwd(h, x, o)
     sgc.disco_fwd(h, x32, o32)
+    sgc.disco_fused_conv(h, x32, W32, y32)
     torch.cuda.synchronize()
-    assert torch.equal(y, ref_y) and torch.equal(o, ref_o) and torch.equal(o32, ref_o32)
+    assert torch.equal(y, ref_y) and torch.equal(o, ref_o) and torch.equal(o32, ref_o32) and torch.equal(y32, ref_y32)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
