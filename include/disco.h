@@ -120,10 +120,11 @@ disco_status disco_bwd(disco_psi h, const disco_tensor *gout, disco_tensor *gx, 
  * Memory: with BF16/F16 data and K < 16 the call takes a temporary of Co * C * 32 bytes from a
  * memory pool the library keeps per device (stream-ordered: taken and returned on `stream`; the pool
  * keeps freed memory for reuse until the process ends) to hold W in rows of 16 elements; if none can be
- * had the kernel stages W element by element instead, with the same result.  With F32 data the call
- * takes a temporary of the same pool holding W in the fp32 einsum's operand order (Co and C rounded up to
- * the kernel's 16-channel tiles and channel chunks, 64 floats per tile and chunk row group: about
- * 4 * Co * C * K bytes); if none can be had the call returns DISCO_ERR_OOM before anything is written. */
+ * had the kernel stages W element by element instead, with the same result.  With F32 data, and with
+ * 16-bit data on shapes outside the matrix-core kernel's plan (K > 16, Wi > 2 Wo, Wo not a multiple of 8),
+ * the call takes a temporary of the same pool holding W in the vector-ALU fused kernel's einsum operand
+ * order (Co and C rounded up to its 16-channel tiles and channel chunks: about Co * C * K elements); if
+ * none can be had the call returns DISCO_ERR_OOM before anything is written. */
 disco_status disco_fused_conv(disco_psi h, const disco_tensor *x, const disco_tensor *W,
                               disco_tensor *y, void *stream);
 

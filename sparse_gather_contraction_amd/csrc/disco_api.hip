@@ -410,13 +410,14 @@ hipMemPool_t temp_pool(int device)
 // for the matrix-core kernels' direct W-slice loads; nullptr (and no error left pending) when K is 16,
 // DISCO_PACK_W=0 (a test knob: keep the element-wise W staging) or the temporary cannot be had.  The
 // caller frees a non-null result with hipFreeAsync on the same stream after its launch.
-// fp32 fused op: W in the fp32 kernel's A-operand order (launch_pack_wa_f32) in a stream-ordered temporary of
-// the device's pool, packed on `stream`; nullptr when no floats are needed (C or Co zero) or, with *err set,
-// when the temporary cannot be had.  The caller frees a non-null result with hipFreeAsync on the same stream.
-float *packed_wa_f32(int device, const void *W, int64_t Co, int64_t C, int K, hipStream_t stream, hipError_t *err)
+// Vector-ALU fused kernels: W in the kernel's A-operand order (launch_pack_wa_f32 for fp32 data,
+// launch_pack_wa16 for 16-bit data) in a stream-ordered temporary of the device's pool, packed on `stream`;
+// nullptr when nothing is needed (C or Co zero) or, with *err set, when the temporary cannot be had.  The
+// caller frees a non-null result with hipFreeAsync on the same stream.
+void *packed_wa(int device, const void *W, int64_t Co, int64_t C, int K, bool f32, hipStream_t stream, hipError_t *err)
 {
     *err = hipSuccess;
-    const int64_t n = disco::fused_wa_f32_floats((int)Co, (int)C, K);
+    const int64_t n = f32 ? disco::fused_wa_f32_floats((int)Co, (int)C, K) : disco::fused_wa16_elems((int)Co, (int)C, K);
     if (n == 0) return nullptr;
     hipMemPool_t pool = temp_pool(device);
     if (!pool) {
@@ -424,12 +425,13 @@ float *packed_wa_f32(int device, const void *W, int64_t Co, int64_t C, int K, hi
         return nullptr;
     }
     void *wa = nullptr;
-    if ((*err = hipMallocFromPoolAsync(&wa, (size_t)n * sizeof(float), pool, stream)) != hipSuccess) {
+    if ((*err = hipMallocFromPoolAsync(&wa, (size_t)n * (f32 ? 4 : 2), pool, stream)) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
-    *err = disco::launch_pack_wa_f32((const float *)W, (float *)wa, (int)Co, (int)C, K, stream);
-    return (float *)wa;
+    *err = f32 ? disco::launch_pack_wa_f32((const float *)W, (float *)wa, (int)Co, (int)C, K, stream)
+               : disco::launch_pack_wa16(W, wa, (int)Co, (int)C, K, stream);
+    return wa;
 }
 
 void *packed_w(int device, const void *W, int64_t Co, int64_t C, int K, hipStream_t stream, hipError_t *err)
@@ -950,19 +952,20 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
     // every check before anything is enqueued (the fallback below writes `out` first)
     if (B * h->Ho * ((Co + 255) / 256) * ((h->Wo + 63) / 64) >= ((int64_t)1 << 31))
         return fail(DISCO_ERR_SHAPE, "fused grid exceeds 2^31 blocks");
-    // fp32: W packed for the kernel's einsum, before anything else is enqueued
-    float *wa = nullptr;
-    if (x->dtype == DISCO_F32 && B * Co * h->Ho > 0 && h->Wo > 0) {
+    // the vector-ALU fused kernels (fp32 data, or shapes outside the matrix-core plan) take W packed for
+    // their einsum: packed before anything else is enqueued
+    const bool valu = x->dtype == DISCO_F32 || !h->fused.ok || getenv_is0("DISCO_FUSED_MFMA");
+    void *wa = nullptr;
+    if (valu && B * Co * h->Ho > 0 && h->Wo > 0) {
         hipError_t e = hipSuccess;
-        wa = packed_wa_f32(h->device, W->data, Co, C, h->K, (hipStream_t)stream, &e);
+        wa = packed_wa(h->device, W->data, Co, C, h->K, x->dtype == DISCO_F32, (hipStream_t)stream, &e);
         if (e != hipSuccess) {
             if (wa) (void)hipFreeAsync(wa, (hipStream_t)stream);
             return fail(e == hipErrorOutOfMemory ? DISCO_ERR_OOM : DISCO_ERR_HIP,
-                        std::string("fp32 fused op: packing W failed: ") + hipGetErrorString(e));
+                        std::string("fused op: packing W failed: ") + hipGetErrorString(e));
         }
     }
-    if (save && B * C * h->Ho * h->Wo > 0 &&
-        (B * Co == 0 || x->dtype == DISCO_F32 || !h->fused.ok || getenv_is0("DISCO_FUSED_MFMA"))) {
+    if (save && B * C * h->Ho * h->Wo > 0 && (B * Co == 0 || valu)) {
         // no matrix-core fused kernel to keep the contraction from: the forward writes it
         if ((st = enqueue_fwd(h, x->data, save->data, x->dtype, B, C, (hipStream_t)stream)) != DISCO_OK) {
             if (wa) (void)hipFreeAsync(wa, (hipStream_t)stream);
@@ -970,7 +973,7 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
         }
     }
     if (B * Co * h->Ho == 0 || h->Wo == 0) return DISCO_OK;
-    if (x->dtype != DISCO_F32 && h->fused.ok && !getenv_is0("DISCO_FUSED_MFMA")) {  // test knob: "0" forces the VALU-contraction fused kernel
+    if (!valu) {  // DISCO_FUSED_MFMA=0 (test knob) forces the VALU-contraction fused kernel
         disco::FusedMfmaLaunch m;
         m.x = x->data; m.W = W->data; m.y = y->data;
         m.pieces = h->fused.pieces; m.rows = h->fused.rows; m.descs = h->fused.descs;
@@ -1017,7 +1020,8 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
     a.B = (int32_t)B; a.C = (int32_t)C; a.Co = (int32_t)Co; a.K = h->K;
     a.Ho = h->Ho; a.Wo = h->Wo; a.Hi = h->Hi; a.Wi = h->Wi;
     a.in_stride = h->fwd.in_stride;
-    a.Wa = wa;
+    if (x->dtype == DISCO_F32) a.Wa = (const float *)wa;
+    else a.Wa16 = wa;
     if (!getenv_is0("DISCO_FUSED_WIN")) {  // test knob: "0" makes the fp32 fused kernel read x from global memory
         a.fw_rows = h->fwd.fw_rows;
         a.fw_ho_ptr = h->fwd.fw_ho_ptr;

@@ -88,6 +88,7 @@ struct FusedLaunch {
     const float *vals;
     int32_t B, C, Co, K, Ho, Wo, Hi, Wi, in_stride;
     const float *Wa = nullptr;  // fp32 data: W packed by launch_pack_wa_f32 (required)
+    const void *Wa16 = nullptr; // 16-bit data: W packed by launch_pack_wa16 (required)
     // fp32 data: the forward plan's source windows (plan.hpp, FusedWindows; null: global reads) and the
     // positions per channel the kernel's LDS area holds (fused_win_cap_f32)
     const FWin *fw_rows = nullptr;
@@ -103,6 +104,9 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream);
 int fused_win_cap_f32(int K, const int32_t *ho_len, int nho);
 // fp32 fused kernel: floats of W packed in its A-operand order (0 when K is outside 1 .. 64), and the packing
 int64_t fused_wa_f32_floats(int Co, int C, int K);
+// 16-bit fused kernel: elements of W packed in its A-operand order (0 when K is outside 1 .. 64), and the packing
+int64_t fused_wa16_elems(int Co, int C, int K);
+hipError_t launch_pack_wa16(const void *W, void *Wa, int Co, int C, int K, hipStream_t stream);
 hipError_t launch_pack_wa_f32(const float *W, float *Wa, int Co, int C, int K, hipStream_t stream);
 
 struct FusedMfmaLaunch {

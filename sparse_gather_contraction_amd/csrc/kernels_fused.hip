@@ -307,7 +307,7 @@ __device__ __forceinline__ void contract_chunk_win(const float *win, int wl, flo
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x, const T *__restrict__ W,
+__global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x, const i16x8 *__restrict__ Wa,
                                                          T *__restrict__ y, const Item *__restrict__ items,
                                                          const int32_t *__restrict__ block_ptr,
                                                          const int32_t *__restrict__ ho_order,
@@ -332,6 +332,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
     const int wo0 = pt * kPx;
     const int o_base = ob * kOBlk + wave * 64;
     const int CC = kR / K;  // channels per chunk (host guarantees K <= kR)
+    const int n_ot16 = (Co + 15) / 16;
     const int64_t plane_sz = (int64_t)Hi * Wi;
     const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
     const int HoWo = Ho * Wo;
@@ -355,7 +356,9 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
         }
         __syncthreads();
         // ---- einsum on the matrix cores ----
-        const int rvalid = ccn * K;
+        // A operands: W packed by launch_pack_wa16 in operand order, one 16-byte load per lane, output-channel
+        // tile and k-step (zeros past Co and past the chunk's ccn K rows)
+        const i16x8 *wq = Wa + (int64_t)(c0 / CC) * n_ot16 * (kR / 32) * 64 + lane;
 #pragma unroll
         for (int ks = 0; ks < kR / 32; ++ks) {
             const int rr0 = ks * 32 + 8 * (lane >> 4);
@@ -367,13 +370,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
             }
 #pragma unroll
             for (int ot = 0; ot < 4; ++ot) {
-                const int o = o_base + ot * 16 + (lane & 15);
-                i16x8 av;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int rr = rr0 + i;
-                    av[i] = (o < Co && rr < rvalid) ? Elem<T>::bits(W[((int64_t)o * C + c0) * K + rr]) : (short)0;
-                }
+                const int o16 = (o_base >> 4) + ot;
+                const i16x8 av = o16 < n_ot16 ? wq[((int64_t)o16 * (kR / 32) + ks) * 64] : i16x8{0, 0, 0, 0, 0, 0, 0, 0};
                 const vec8 aop = __builtin_bit_cast(vec8, av);
 #pragma unroll
                 for (int p4 = 0; p4 < 4; ++p4)
@@ -399,6 +397,25 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
 // 16 pixels), fp32 products and accumulation throughout.  W arrives packed in A-operand order
 // (launch_pack_wa_f32): an A operand spans 16 output channels whose W rows lie C K floats apart, so
 // loading it from W itself would touch 16 cache lines per 4-byte load.
+
+// Packed W for fused_kernel (16-bit data): for chunk t (channels c0 = t CC .. + CC - 1), 16-channel output
+// tile o16, k-step ks (32 rows) and lane l, the eight 16-bit values at Wa[(((t n_ot16 + o16) (kR / 32) + ks)
+// 64 + l) 8 + e] are W[o][c0 K + rr] with o = 16 o16 + l % 16 and rr = 32 ks + 8 (l / 16) + e — the A
+// operand of that step for that lane — and zero where o >= Co or rr reaches past the chunk's channels.
+__global__ __launch_bounds__(256) void pack_wa16_kernel(const uint16_t *__restrict__ W, uint16_t *__restrict__ Wa,
+                                                        int Co, int C, int K, int64_t total)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int e = (int)(i & 7), l = (int)((i >> 3) & 63), ks = (int)((i >> 9) % (kR / 32));
+    const int64_t rest = (i >> 9) / (kR / 32);
+    const int n_ot16 = (Co + 15) / 16;
+    const int o16 = (int)(rest % n_ot16);
+    const int t = (int)(rest / n_ot16);
+    const int CC = kR / K, c0 = t * CC, ccn = min(CC, C - c0);
+    const int o = 16 * o16 + (l & 15), rr = 32 * ks + 8 * (l >> 4) + e;
+    Wa[i] = (o < Co && rr < ccn * K) ? W[((int64_t)o * C + c0) * K + rr] : (uint16_t)0;
+}
 
 // Packed W for fused_f32_kernel: for chunk t (channels c0 = t CC .. + CC - 1, CC = kR / K), 16-channel
 // output tile o16, step quadruple kq and lane l, the float4 Wa[((t n_ot16 + o16) (kR / 16) + kq) 64 + l]
@@ -572,14 +589,18 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
                            (const float4 *)a.Wa, (float *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
                            a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob, a.fw_rows, a.fw_ho_ptr,
                            a.fw_ho_len, a.fw_seg_off, wcap, reinterpret_cast<const int4 *>(a.fw_ho_psi), psi_cap);
-    } else if (a.f16)
-        hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
-                           (const f16_t *)a.W, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
-                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
-    else
-        hipLaunchKernelGGL(fused_kernel<bf16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const bf16_t *)a.x,
-                           (const bf16_t *)a.W, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B,
-                           a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    } else {
+        if (!a.Wa16 && a.C > 0) return hipErrorInvalidValue;  // the kernel takes W packed (launch_pack_wa16)
+        const i16x8 *wa = reinterpret_cast<const i16x8 *>(a.Wa16);
+        if (a.f16)
+            hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
+                               wa, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B, a.C, a.Co, a.K,
+                               a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+        else
+            hipLaunchKernelGGL(fused_kernel<bf16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream,
+                               (const bf16_t *)a.x, wa, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals,
+                               a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+    }
     return hipGetLastError();
 }
 
@@ -599,6 +620,22 @@ int64_t fused_wa_f32_floats(int Co, int C, int K)
     if (K < 1 || K > kR) return 0;
     const int64_t CC = kR / K, n_chunks = (C + CC - 1) / CC, n_ot16 = (Co + 15) / 16;
     return n_chunks * n_ot16 * (kR / 16) * 64 * 4;
+}
+
+int64_t fused_wa16_elems(int Co, int C, int K)
+{
+    if (K < 1 || K > kR) return 0;
+    const int64_t CC = kR / K, n_chunks = (C + CC - 1) / CC, n_ot16 = (Co + 15) / 16;
+    return n_chunks * n_ot16 * (kR / 32) * 64 * 8;
+}
+
+hipError_t launch_pack_wa16(const void *W, void *Wa, int Co, int C, int K, hipStream_t stream)
+{
+    const int64_t total = fused_wa16_elems(Co, C, K);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_wa16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       (const uint16_t *)W, (uint16_t *)Wa, Co, C, K, total);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_wa_f32(const float *W, float *Wa, int Co, int C, int K, hipStream_t stream)
