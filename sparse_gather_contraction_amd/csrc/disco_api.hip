@@ -1022,7 +1022,7 @@ disco_status fused_conv_impl(disco_psi h, const disco_tensor *x, const disco_ten
     a.in_stride = h->fwd.in_stride;
     if (x->dtype == DISCO_F32) a.Wa = (const float *)wa;
     else a.Wa16 = wa;
-    if (!getenv_is0("DISCO_FUSED_WIN")) {  // test knob: "0" makes the fp32 fused kernel read x from global memory
+    if (!getenv_is0("DISCO_FUSED_WIN")) {  // test knob: "0" makes the vector-ALU fused kernels read x from memory
         a.fw_rows = h->fwd.fw_rows;
         a.fw_ho_ptr = h->fwd.fw_ho_ptr;
         a.fw_ho_len = h->fwd.fw_ho_len;

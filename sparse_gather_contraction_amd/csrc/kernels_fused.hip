@@ -12,10 +12,10 @@
 // multiplied on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16} with W as the
 // A operand (16 o x 32 rows) and the LDS tile as the B operand (32 rows x 16
 // pixels), fp32 accumulation in registers across all chunks.  fp32 data keeps
-// the chunk in fp32 and runs the einsum on v_mfma_f32_16x16x4_f32 with W packed
-// per call in A-operand order; its contraction reads x from per-latitude source
-// windows staged in LDS for each chunk, and the latitude's psi from an LDS copy
-// made once per block (plan.hpp, FusedWindows).
+// the chunk in fp32 and runs the einsum on v_mfma_f32_16x16x4_f32.  Both take W
+// packed per call in their A-operand order, and their contraction reads x from
+// per-latitude source windows staged in LDS for each chunk and the latitude's psi
+// from an LDS copy made once per block (plan.hpp, FusedWindows).
 #include <algorithm>
 #include <climits>
 
@@ -80,39 +80,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-// fp32 windows: the chunk's source windows (plan.hpp, FusedWindows) into LDS by direct global -> LDS
-// loads, one 4-byte load per staged position; (row, channel) pairs go round the four waves, lane l of an
-// instruction writing position q0 + l.  win: [channel][wl positions]; xb: the batch's channel planes.
-__device__ __forceinline__ void stage_fwin_f32(const float *__restrict__ xb, float *win, const FWin *__restrict__ rows,
-                                               int r0, int r1, int wl, int64_t plane_sz, int c0, int ccn, int Wo,
-                                               int in_stride, int wo0, int wave, int lane)
+// The chunk's source windows (plan.hpp, FusedWindows) into LDS by direct global -> LDS loads, one load per
+// staged position into a 4-byte slot (4-byte loads for fp32 data, 2-byte loads for 16-bit data, whose value
+// is the slot's low half); (row, channel) pairs go round the four waves, lane l of an instruction writing
+// position q0 + l.  win: [channel][wl slots]; xb: the batch's channel planes.
+template <typename T>
+__device__ __forceinline__ void stage_fwin(const T *__restrict__ xb, uint32_t *win, const FWin *__restrict__ rows,
+                                           int r0, int r1, int wl, int64_t plane_sz, int c0, int ccn, int Wo,
+                                           int in_stride, int wo0, int wave, int lane)
 {
+    constexpr int E = sizeof(T);
     const int nj = (r1 - r0) * ccn;
     for (int job = wave; job < nj; job += kThreads / 64) {
         const int r = r0 + job / ccn, cl = job - (job / ccn) * ccn;
         const FWin w = rows[r];
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(xb + (int64_t)(c0 + cl) * plane_sz, 4u * (uint32_t)plane_sz);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(xb + (int64_t)(c0 + cl) * plane_sz, E * (uint32_t)plane_sz);
         for (int q0 = 0; q0 < w.len; q0 += 64) {
             const int q = q0 + lane;
             const int idx = (w.a + wo0 + q) % Wo;
-            if (q < w.len)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(win + cl * wl + w.base + q0), 4,
-                                                         4u * (uint32_t)(w.in_off + in_stride * idx), 0, 0, 0);
+            const uint32_t voff = E * (uint32_t)(w.in_off + in_stride * idx);
+            lptr_t dst = (lptr_t)(win + cl * wl + w.base + q0);
+            if (q < w.len) {
+                if constexpr (E == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff, 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 2, voff, 0, 0, 0);
+            }
         }
     }
 }
 
-// The fp32 chunk's contraction from the staged windows: as contract_chunk, but a segment's entry t at
-// pixel px reads window position seg_off + t + px of its channel (no modulo, no global load).
-template <int NB, int NP, int G>
-__device__ __forceinline__ void contract_batch_win(const float *const (&lw)[NP], const float *__restrict__ v, int t,
+// The value of a staged window slot (T: the data type).
+template <typename T>
+__device__ __forceinline__ float slot_val(uint32_t w)
+{
+    if constexpr (sizeof(T) == 4) return __uint_as_float(w);
+    else return Elem<T>::to_f32(__builtin_bit_cast(T, (unsigned short)w));
+}
+
+// The chunk's contraction from the staged windows: as contract_chunk, but a segment's entry t at pixel px
+// reads window position seg_off + t + px of its channel (no modulo, no global load).
+template <int NB, int NP, int G, typename T>
+__device__ __forceinline__ void contract_batch_win(const uint32_t *const (&lw)[NP], const float *__restrict__ v, int t,
                                                    int pos, float (&acc)[NP][kMaxGroup])
 {
     float xv[NP][NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
-        for (int p = 0; p < NP; ++p) xv[p][u] = lw[p][pos + u];
+        for (int p = 0; p < NP; ++p) xv[p][u] = slot_val<T>(lw[p][pos + u]);
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
@@ -125,8 +139,8 @@ __device__ __forceinline__ void contract_batch_win(const float *const (&lw)[NP],
 
 // segs, seg_off and vals hold the plan's segments from s_base and values from v_base (the whole plan, or
 // the latitude's runs copied to LDS).
-template <int NP, int G>
-__device__ __forceinline__ void contract_item_win(const float *const (&lw)[NP], const Item &it,
+template <int NP, int G, typename T>
+__device__ __forceinline__ void contract_item_win(const uint32_t *const (&lw)[NP], const Item &it,
                                                   const Seg *__restrict__ segs, const int32_t *__restrict__ seg_off,
                                                   const float *__restrict__ vals, int s_base, int v_base, int px,
                                                   float (&acc)[NP][kMaxGroup])
@@ -140,16 +154,16 @@ __device__ __forceinline__ void contract_item_win(const float *const (&lw)[NP], 
         const float *v = vals + (sg.val_off - v_base);
         const int pos = seg_off[q] + px;
         int t = 0;
-        for (; t + 8 <= sg.m; t += 8) contract_batch_win<8, NP, G>(lw, v, t, pos + t, acc);
+        for (; t + 8 <= sg.m; t += 8) contract_batch_win<8, NP, G, T>(lw, v, t, pos + t, acc);
         if (t + 4 <= sg.m) {
-            contract_batch_win<4, NP, G>(lw, v, t, pos + t, acc);
+            contract_batch_win<4, NP, G, T>(lw, v, t, pos + t, acc);
             t += 4;
         }
         if (t + 2 <= sg.m) {
-            contract_batch_win<2, NP, G>(lw, v, t, pos + t, acc);
+            contract_batch_win<2, NP, G, T>(lw, v, t, pos + t, acc);
             t += 2;
         }
-        if (t < sg.m) contract_batch_win<1, NP, G>(lw, v, t, pos + t, acc);
+        if (t < sg.m) contract_batch_win<1, NP, G, T>(lw, v, t, pos + t, acc);
     }
 }
 
@@ -262,10 +276,10 @@ __device__ __forceinline__ void contract_chunk(const T *__restrict__ xb, S *__re
     }
 }
 
-// contract_chunk for fp32 data from the chunk's staged windows (win: [channel][wl positions]); the same
-// multiply-adds in the same order, so the same sums.
-template <int STRIDE>
-__device__ __forceinline__ void contract_chunk_win(const float *win, int wl, float *__restrict__ tile,
+// contract_chunk from the chunk's staged windows (win: [channel][wl slots]); the same multiply-adds in the
+// same order, so the same sums.
+template <typename T, int STRIDE>
+__device__ __forceinline__ void contract_chunk_win(const uint32_t *win, int wl, T *__restrict__ tile,
                                                    const Item *__restrict__ items, const Seg *__restrict__ segs,
                                                    const int32_t *__restrict__ seg_off, const float *__restrict__ vals,
                                                    int it_begin, int it_end, int s_base, int v_base, int ccn, int CC,
@@ -275,7 +289,7 @@ __device__ __forceinline__ void contract_chunk_win(const float *win, int wl, flo
     const int cl0 = tid / kPx, px = tid - cl0 * kPx;
     const int wo = wo0 + px;
     for (int cb = 0; cb < CC; cb += 4 * NP) {
-        const float *lw[NP];
+        const uint32_t *lw[NP];
         bool valid[NP];
         int cl[NP];
 #pragma unroll
@@ -288,21 +302,105 @@ __device__ __forceinline__ void contract_chunk_win(const float *win, int wl, flo
             const Item it = items[ii];
             float a[NP][kMaxGroup];
             switch (it.G) {
-            case 1: contract_item_win<NP, 1>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
-            case 2: contract_item_win<NP, 2>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
-            case 3: contract_item_win<NP, 3>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
-            default: contract_item_win<NP, 4>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            case 1: contract_item_win<NP, 1, T>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            case 2: contract_item_win<NP, 2, T>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            case 3: contract_item_win<NP, 3, T>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
+            default: contract_item_win<NP, 4, T>(lw, it, segs, seg_off, vals, s_base, v_base, px, a); break;
             }
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 if (cl[p] < CC) {
                     for (int g = 0; g < it.G; ++g) {
                         const int k = it.out_off[g] / HoWo;
-                        tile[px * STRIDE + cl[p] * K + k] = valid[p] ? a[p][g] : 0.0f;
+                        tile[px * STRIDE + cl[p] * K + k] = Elem<T>::from_f32(valid[p] ? a[p][g] : 0.0f);
                     }
                 }
             }
         }
+    }
+}
+
+// The source windows and psi of one workgroup's latitude (plan.hpp, FusedWindows): windows when the
+// launch has them (wcap > 0; else the tables are not passed) and the latitude's fit the LDS area (wcap
+// slots per channel), else global reads; with windows, the latitude's items, segments, values and window
+// offsets are copied to LDS once (psi_cap bytes after the windows) when they fit, so the chunks read no
+// psi from memory.
+struct WinTables {
+    const FWin *rows;
+    const int32_t *ho_ptr, *ho_len, *seg_off;
+    const int4 *ho_psi;
+    int wcap, psi_cap;
+};
+
+struct LatWin {
+    bool use_win, use_psi;
+    int wl, r0, r1;
+    int n_it, s0, v0;
+    const Item *l_items;
+    const Seg *l_segs;
+    const float *l_vals;
+    const int32_t *l_off;
+};
+
+// The copies run on all threads; they are visible after the caller's next barrier.
+__device__ __forceinline__ LatWin setup_lat(const WinTables &wt, uint32_t *win, int CC, int ho, int it_begin,
+                                            int it_end, const Item *__restrict__ items, const Seg *__restrict__ segs,
+                                            const float *__restrict__ vals, int tid)
+{
+    LatWin L;
+    L.wl = wt.wcap > 0 ? wt.ho_len[ho] : 0;
+    L.use_win = wt.wcap > 0 && L.wl <= wt.wcap;
+    L.r0 = L.use_win ? wt.ho_ptr[ho] : 0;
+    L.r1 = L.use_win ? wt.ho_ptr[ho + 1] : 0;
+    const int4 pr = L.use_win && wt.psi_cap > 0 ? wt.ho_psi[ho] : make_int4(0, 0, 0, 0);  // s0, s1, v0, v1
+    const int n_it = it_end - it_begin, n_sg = pr.y - pr.x, n_v = pr.w - pr.z;
+    L.use_psi = L.use_win && wt.psi_cap > 0 && n_it * 32 + n_sg * 20 + n_v * 4 <= wt.psi_cap;
+    L.n_it = n_it;
+    L.s0 = pr.x;
+    L.v0 = pr.z;
+    unsigned char *lpsi = reinterpret_cast<unsigned char *>(win) + ((int64_t)CC * wt.wcap * 4 + 15) / 16 * 16;
+    Item *l_items = reinterpret_cast<Item *>(lpsi);
+    Seg *l_segs = reinterpret_cast<Seg *>(lpsi + n_it * 32);
+    float *l_vals = reinterpret_cast<float *>(lpsi + n_it * 32 + n_sg * 16);
+    int32_t *l_off = reinterpret_cast<int32_t *>(lpsi + n_it * 32 + n_sg * 16 + n_v * 4);
+    if (L.use_psi) {
+        const int32_t *src_it = reinterpret_cast<const int32_t *>(items + it_begin);
+        const int32_t *src_sg = reinterpret_cast<const int32_t *>(segs + pr.x);
+        for (int e = tid; e < 8 * n_it; e += kThreads) reinterpret_cast<int32_t *>(l_items)[e] = src_it[e];
+        for (int e = tid; e < 4 * n_sg; e += kThreads) reinterpret_cast<int32_t *>(l_segs)[e] = src_sg[e];
+        for (int e = tid; e < n_v; e += kThreads) l_vals[e] = vals[pr.z + e];
+        for (int e = tid; e < n_sg; e += kThreads) l_off[e] = wt.seg_off[pr.x + e];
+    }
+    L.l_items = l_items;
+    L.l_segs = l_segs;
+    L.l_vals = l_vals;
+    L.l_off = l_off;
+    return L;
+}
+
+// One chunk's contraction into the tile: from staged windows (staged here: one wait and a barrier) and
+// the LDS psi copy where the latitude has them, else from memory.  Caller: a barrier before (the previous
+// chunk is done with the tile and the windows).
+template <typename T, int STRIDE>
+__device__ __forceinline__ void contract_any(const LatWin &L, const WinTables &wt, uint32_t *win, const T *xb,
+                                             T *__restrict__ tile, const Item *__restrict__ items,
+                                             const Seg *__restrict__ segs, const float *__restrict__ vals,
+                                             int it_begin, int it_end, int64_t plane_sz, int c0, int ccn, int CC, int K,
+                                             int Wo, int HoWo, int in_stride, int wo0, int tid, int wave, int lane)
+{
+    if (L.use_win) {
+        stage_fwin<T>(xb, win, wt.rows, L.r0, L.r1, L.wl, plane_sz, c0, ccn, Wo, in_stride, wo0, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's window loads have landed
+        __syncthreads();                // everyone's have
+        if (L.use_psi)
+            contract_chunk_win<T, STRIDE>(win, L.wl, tile, L.l_items, L.l_segs, L.l_off, L.l_vals, 0, L.n_it, L.s0,
+                                          L.v0, ccn, CC, K, Wo, HoWo, wo0, tid);
+        else
+            contract_chunk_win<T, STRIDE>(win, L.wl, tile, items, segs, wt.seg_off, vals, it_begin, it_end, 0, 0, ccn,
+                                          CC, K, Wo, HoWo, wo0, tid);
+    } else {
+        contract_chunk<T, T, STRIDE>(xb, tile, items, segs, vals, it_begin, it_end, plane_sz, c0, ccn, CC, K, Wo,
+                                     HoWo, in_stride, wo0, tid);
     }
 }
 
@@ -313,10 +411,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
                                                          const int32_t *__restrict__ ho_order,
                                                          const Seg *__restrict__ segs, const float *__restrict__ vals,
                                                          int B, int C, int Co, int K, int Ho, int Wo, int Hi, int Wi,
-                                                         int in_stride, int n_pt, int n_ob)
+                                                         int in_stride, int n_pt, int n_ob, WinTables wt)
 {
     typedef typename Elem<T>::vec8 vec8;
     __shared__ __attribute__((aligned(16))) T tile[kPx * kLdsStride];
+    // dynamic LDS: [CC][wcap] 4-byte slots of source windows, then psi_cap bytes for the latitude's psi
+    extern __shared__ __attribute__((aligned(16))) uint32_t win[];
 
     int bid = blockIdx.x;
     const int pt = bid % n_pt;
@@ -336,6 +436,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
     const int64_t plane_sz = (int64_t)Hi * Wi;
     const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
     const int HoWo = Ho * Wo;
+    const T *xb = x + (int64_t)b * C * plane_sz;
+    const LatWin L = setup_lat(wt, win, CC, ho, it_begin, it_end, items, segs, vals, tid);
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -345,10 +447,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(const T *__restrict__ x
 
     for (int c0 = 0; c0 < C; c0 += CC) {
         const int ccn = min(CC, C - c0);
-        __syncthreads();  // the previous chunk's MFMA reads of `tile` are done
+        __syncthreads();  // the previous chunk's MFMA reads of `tile` and window reads are done
         // ---- contraction of channels [c0, c0+ccn) into tile[px][cl*K + k] ----
-        contract_chunk<T, T, kLdsStride>(x + (int64_t)b * C * plane_sz, tile, items, segs, vals, it_begin, it_end,
-                                         plane_sz, c0, ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
+        contract_any<T, kLdsStride>(L, wt, win, xb, tile, items, segs, vals, it_begin, it_end, plane_sz, c0, ccn, CC,
+                                    K, Wo, HoWo, in_stride, wo0, tid, wave, lane);
         // rows past the chunk's (c, k) range are zero
         for (int e = tid; e < kPx * kR; e += kThreads) {
             const int px = e / kR, r = e - px * kR;
@@ -452,8 +554,8 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
                                                              const int4 *__restrict__ fw_ho_psi, int psi_cap)
 {
     __shared__ __attribute__((aligned(16))) float tile[kPx * kLdsStride32];
-    // dynamic LDS: [CC][wcap] floats of source windows, then psi_cap bytes for the latitude's psi
-    extern __shared__ __attribute__((aligned(16))) float win[];
+    // dynamic LDS: [CC][wcap] 4-byte slots of source windows, then psi_cap bytes for the latitude's psi
+    extern __shared__ __attribute__((aligned(16))) uint32_t win[];
 
     int bid = blockIdx.x;
     const int pt = bid % n_pt;
@@ -473,30 +575,9 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
     const int64_t plane_sz = (int64_t)Hi * Wi;
     const int it_begin = block_ptr[ho], it_end = block_ptr[ho + 1];
     const int HoWo = Ho * Wo;
-    // the latitude's windows when the launch has them (wcap > 0; else the tables are not passed) and they
-    // fit the LDS area (wcap positions per channel), else global reads
-    const int wl = wcap > 0 ? fw_ho_len[ho] : 0;
-    const bool use_win = wcap > 0 && wl <= wcap;
-    const int r0 = use_win ? fw_ho_ptr[ho] : 0, r1 = use_win ? fw_ho_ptr[ho + 1] : 0;
     const float *xb = x + (int64_t)b * C * plane_sz;
-    // with windows, the latitude's items, segments, values and window offsets are copied to LDS once
-    // (psi_cap bytes after the windows) when they fit, so the 37-odd chunks read no psi from memory
-    const int4 pr = use_win && psi_cap > 0 ? fw_ho_psi[ho] : make_int4(0, 0, 0, 0);  // s0, s1, v0, v1
-    const int n_it = it_end - it_begin, n_sg = pr.y - pr.x, n_v = pr.w - pr.z;
-    const bool use_psi = use_win && psi_cap > 0 && n_it * 32 + n_sg * 20 + n_v * 4 <= psi_cap;
-    unsigned char *lpsi = reinterpret_cast<unsigned char *>(win) + ((int64_t)CC * wcap * 4 + 15) / 16 * 16;
-    Item *l_items = reinterpret_cast<Item *>(lpsi);
-    Seg *l_segs = reinterpret_cast<Seg *>(lpsi + n_it * 32);
-    float *l_vals = reinterpret_cast<float *>(lpsi + n_it * 32 + n_sg * 16);
-    int32_t *l_off = reinterpret_cast<int32_t *>(lpsi + n_it * 32 + n_sg * 16 + n_v * 4);
-    if (use_psi) {
-        const int32_t *src_it = reinterpret_cast<const int32_t *>(items + it_begin);
-        const int32_t *src_sg = reinterpret_cast<const int32_t *>(segs + pr.x);
-        for (int e = tid; e < 8 * n_it; e += kThreads) reinterpret_cast<int32_t *>(l_items)[e] = src_it[e];
-        for (int e = tid; e < 4 * n_sg; e += kThreads) reinterpret_cast<int32_t *>(l_segs)[e] = src_sg[e];
-        for (int e = tid; e < n_v; e += kThreads) l_vals[e] = vals[pr.z + e];
-        for (int e = tid; e < n_sg; e += kThreads) l_off[e] = seg_off[pr.x + e];
-    }  // visible after the chunk loop's first barrier
+    const WinTables wt{fw_rows, fw_ho_ptr, fw_ho_len, seg_off, fw_ho_psi, wcap, psi_cap};
+    const LatWin L = setup_lat(wt, win, CC, ho, it_begin, it_end, items, segs, vals, tid);
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -507,20 +588,8 @@ __global__ __launch_bounds__(kThreads) void fused_f32_kernel(const float *__rest
     for (int c0 = 0; c0 < C; c0 += CC) {
         const int ccn = min(CC, C - c0);
         __syncthreads();  // the previous chunk's MFMA reads of `tile` and window reads are done
-        if (use_win) {
-            stage_fwin_f32(xb, win, fw_rows, r0, r1, wl, plane_sz, c0, ccn, Wo, in_stride, wo0, wave, lane);
-            __builtin_amdgcn_s_waitcnt(0);  // this thread's window loads have landed
-            __syncthreads();                // everyone's have
-            if (use_psi)
-                contract_chunk_win<kLdsStride32>(win, wl, tile, l_items, l_segs, l_off, l_vals, 0, n_it, pr.x, pr.z,
-                                                 ccn, CC, K, Wo, HoWo, wo0, tid);
-            else
-                contract_chunk_win<kLdsStride32>(win, wl, tile, items, segs, seg_off, vals, it_begin, it_end, 0, 0,
-                                                 ccn, CC, K, Wo, HoWo, wo0, tid);
-        } else {
-            contract_chunk<float, float, kLdsStride32>(xb, tile, items, segs, vals, it_begin, it_end, plane_sz, c0,
-                                                       ccn, CC, K, Wo, HoWo, in_stride, wo0, tid);
-        }
+        contract_any<float, kLdsStride32>(L, wt, win, xb, tile, items, segs, vals, it_begin, it_end, plane_sz, c0, ccn,
+                                          CC, K, Wo, HoWo, in_stride, wo0, tid, wave, lane);
         for (int e = tid; e < kPx * kR; e += kThreads) {
             const int px = e / kR, r = e - px * kR;
             if (r >= ccn * K) tile[px * kLdsStride32 + r] = 0.0f;
@@ -575,14 +644,16 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
     const int n_pt = (a.Wo + kPx - 1) / kPx;
     const int n_ob = (a.Co + kOBlk - 1) / kOBlk;
     const int64_t nblk = (int64_t)a.B * a.Ho * n_ob * n_pt;
+    // windows in LDS where the plan has them and a channel plane is below 2 GiB (32-bit load offsets)
+    const bool win_ok = a.fw_rows && a.fw_ho_ptr && a.fw_ho_len && a.fw_seg_off && a.fw_cap > 0 &&
+                        (int64_t)a.Hi * a.Wi <= INT32_MAX / 4;
+    const int wcap = win_ok ? a.fw_cap : 0;
+    const int psi_cap = wcap > 0 && a.fw_ho_psi ? std::min(a.fw_psi_bytes, kFusedPsiBytes) : 0;
+    const size_t lds = ((size_t)(kR / a.K) * wcap * 4 + 15) / 16 * 16 + (size_t)psi_cap;  // 4-byte window slots
+    const WinTables wt{a.fw_rows, a.fw_ho_ptr, a.fw_ho_len, a.fw_seg_off, reinterpret_cast<const int4 *>(a.fw_ho_psi),
+                       wcap, psi_cap};
     if (a.f32) {
         if (!a.Wa && a.C > 0) return hipErrorInvalidValue;  // the fp32 kernel takes W packed (launch_pack_wa_f32)
-        // windows in LDS where the plan has them and a channel plane is below 2 GiB (32-bit load offsets)
-        const bool win_ok = a.fw_rows && a.fw_ho_ptr && a.fw_ho_len && a.fw_seg_off && a.fw_cap > 0 &&
-                            (int64_t)a.Hi * a.Wi <= INT32_MAX / 4;
-        const int wcap = win_ok ? a.fw_cap : 0;
-        const int psi_cap = wcap > 0 && a.fw_ho_psi ? std::min(a.fw_psi_bytes, kFusedPsiBytes) : 0;
-        const size_t lds = ((size_t)(kR / a.K) * wcap * sizeof(float) + 15) / 16 * 16 + (size_t)psi_cap;
         hipError_t e = allow_lds(reinterpret_cast<const void *>(&fused_f32_kernel), lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fused_f32_kernel, dim3((unsigned)nblk), dim3(kThreads), lds, stream, (const float *)a.x,
@@ -592,14 +663,18 @@ hipError_t launch_fused(const FusedLaunch &a, hipStream_t stream)
     } else {
         if (!a.Wa16 && a.C > 0) return hipErrorInvalidValue;  // the kernel takes W packed (launch_pack_wa16)
         const i16x8 *wa = reinterpret_cast<const i16x8 *>(a.Wa16);
+        const void *fn = a.f16 ? reinterpret_cast<const void *>(&fused_kernel<f16_t>)
+                               : reinterpret_cast<const void *>(&fused_kernel<bf16_t>);
+        hipError_t e = allow_lds(fn, lds);
+        if (e != hipSuccess) return e;
         if (a.f16)
-            hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream, (const f16_t *)a.x,
-                               wa, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals, a.B, a.C, a.Co, a.K,
-                               a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+            hipLaunchKernelGGL(fused_kernel<f16_t>, dim3((unsigned)nblk), dim3(kThreads), lds, stream,
+                               (const f16_t *)a.x, wa, (f16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals,
+                               a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob, wt);
         else
-            hipLaunchKernelGGL(fused_kernel<bf16_t>, dim3((unsigned)nblk), dim3(kThreads), 0, stream,
+            hipLaunchKernelGGL(fused_kernel<bf16_t>, dim3((unsigned)nblk), dim3(kThreads), lds, stream,
                                (const bf16_t *)a.x, wa, (bf16_t *)a.y, a.items, a.block_ptr, a.ho_order, a.segs, a.vals,
-                               a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob);
+                               a.B, a.C, a.Co, a.K, a.Ho, a.Wo, a.Hi, a.Wi, a.in_stride, n_pt, n_ob, wt);
     }
     return hipGetLastError();
 }

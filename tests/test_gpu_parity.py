@@ -879,17 +879,21 @@ FUSED_F32_CFGS = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("cfg", FUSED_F32_CFGS)
-def test_fused_f32_windows_equal_global_reads(cfg, monkeypatch):
-    """The fp32 fused kernel reads its sources from windows staged in LDS where a latitude's windows fit,
-    and the latitude's psi from an LDS copy where it fits (DISCO_FUSED_PSI_LDS=0: psi from memory;
-    DISCO_FUSED_WIN=0: everything from memory); all multiply the same values in the same order, so y must
-    be bitwise equal (the configurations include caps spanning whole rings, whose windows do not fit)."""
+def test_fused_f32_windows_equal_global_reads(cfg, dtype, monkeypatch):
+    """The vector-ALU fused kernels (fp32 data; 16-bit data with DISCO_FUSED_MFMA=0) read their sources from
+    windows staged in LDS where a latitude's windows fit, and the latitude's psi from an LDS copy where it
+    fits (DISCO_FUSED_PSI_LDS=0: psi from memory; DISCO_FUSED_WIN=0: everything from memory); all multiply
+    the same values in the same order, so y must be bitwise equal (the configurations include caps
+    spanning whole rings)."""
     Hi, Wi, Ho, Wo, tc, n_r, n_a, B, C, Co = cfg
     psi = build_psi(Hi, Wi, Ho, Wo, tc, n_r, n_a)
     h = gpu_psi(psi)
-    x = randn((B, C, Hi, Wi), 4200 + C).to(DEV)
-    W = randn((Co, C, psi.K), 4201 + C, std=1.0 / np.sqrt(C * psi.K)).to(DEV)
+    if dtype != "f32":
+        monkeypatch.setenv("DISCO_FUSED_MFMA", "0")
+    x = randn((B, C, Hi, Wi), 4200 + C, dtype).to(DEV)
+    W = randn((Co, C, psi.K), 4201 + C, dtype, std=1.0 / np.sqrt(C * psi.K)).to(DEV)
     y_lds = sgc.disco_fused_conv(h, x, W)
     monkeypatch.setenv("DISCO_FUSED_PSI_LDS", "0")
     y_win = sgc.disco_fused_conv(h, x, W)
