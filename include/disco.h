@@ -167,7 +167,10 @@ disco_status disco_einsum(const disco_tensor *W, const disco_tensor *t, disco_te
  * partials are summed in a fixed order.  Results are bitwise reproducible run to run.  gx and dW must not overlap any
  * input (DISCO_ERR_INVALID_ARGUMENT).  `workspace` is caller-owned device memory (256-byte aligned) of at
  * least the size disco_fused_conv_bwd_workspace reports for (B, C, Co); its contents on entry
- * are ignored and on return are unspecified.  Calls sharing one workspace must not overlap. */
+ * are ignored and on return are unspecified.  Calls sharing one workspace must not overlap.
+ * Where gx takes the fused launch, the recomputed contraction and the dW products run on the
+ * library's second stream beside it, with the same ordering guarantees as disco_fused_conv_bwd_saved
+ * (the call behaves as if everything ran on `stream`). */
 disco_status disco_fused_conv_bwd_workspace(disco_psi h, int64_t B, int64_t C, int64_t Co, size_t *bytes);
 disco_status disco_fused_conv_bwd(disco_psi h, const disco_tensor *x, const disco_tensor *W, const disco_tensor *gy,
                                   disco_tensor *gx, disco_tensor *dW, void *workspace, size_t workspace_bytes,

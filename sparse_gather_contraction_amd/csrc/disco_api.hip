@@ -1234,9 +1234,11 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
         return DISCO_OK;
     };
     // With the contraction kept, dW depends on the inputs only: it runs on a second stream, overlapping
-    // the chain W^T gy -> transpose contraction on the caller's stream (ordered by events at both ends).
-    // Once the side stream waits on the caller's, every exit joins it back (the guard's destructor on
-    // an early error return), so no side-stream work outlives the call unordered.
+    // gx on the caller's stream (ordered by events at both ends).  With gx one fused launch, the
+    // recomputed contraction and its dW products likewise run on the second stream beside it (they
+    // share no workspace region with it: gbuf and part against wt).  Once the side stream waits on the
+    // caller's, every exit joins it back (the guard's destructor on an early error return), so no
+    // side-stream work outlives the call unordered.
     struct Fork {
         hipEvent_t in = nullptr, done = nullptr;
         hipStream_t main = nullptr, side = nullptr;  // side set once it waits on `in`
@@ -1261,7 +1263,9 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
         }
     } fork;
     hipStream_t sd = sm;
-    if (svp && C > 0) {
+    // test knob: DISCO_BWD_OVERLAP=0 keeps the recomputing backward on the caller's stream
+    const bool overlap_recompute = gx_fused && !svp && !getenv_is0("DISCO_BWD_OVERLAP");
+    if ((svp || overlap_recompute) && C > 0) {
         hipStream_t side = side_stream(h->device);
         fork.main = sm;
         if (side && hipEventCreateWithFlags(&fork.in, hipEventDisableTiming) == hipSuccess &&
@@ -1272,11 +1276,13 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
         } else {
             (void)hipGetLastError();  // no second stream: everything on the caller's
         }
-        for (int64_t c0 = 0; c0 < C; c0 += L.Cc) {
+        for (int64_t c0 = 0; c0 < C && svp; c0 += L.Cc) {
             const int32_t Mc = (int32_t)(std::min<int64_t>(L.Cc, C - c0) * K);
             if ((st = dw_chunk(c0, Mc, svp + c0 * K * N, C * K * N, sd)) != DISCO_OK) return st;
         }
     }
+    // the stream of the recomputed contraction and its dW products
+    const hipStream_t sc = overlap_recompute ? sd : sm;
     if (gx_fused && C > 0) {
         disco::FusedMfmaLaunch m;
         m.x = gy->data; m.W = wt; m.y = gx->data;
@@ -1328,12 +1334,12 @@ disco_status fused_conv_bwd_impl(disco_psi h, const disco_tensor *x, const disco
             m.desc_bytes = h->fused.desc_bytes; m.adata_bytes = h->fused.adata_bytes;
             m.f16 = f16; m.scale = f16 ? std::ldexp(1.0f, -h->fused.psi16_exp) : 1.0f;
             m.x_bstride = C * plane_in; m.out_bstride = gstride;
-            if ((e = disco::launch_fused_contract(m, sm)) != hipSuccess) return hipfail(e, "contraction");
-        } else if ((st = enqueue_fwd(h, xp + c0 * plane_in, gb, dt, B, cc, sm, C * plane_in, gstride)) !=
+            if ((e = disco::launch_fused_contract(m, sc)) != hipSuccess) return hipfail(e, "contraction");
+        } else if ((st = enqueue_fwd(h, xp + c0 * plane_in, gb, dt, B, cc, sc, C * plane_in, gstride)) !=
                    DISCO_OK) {
             return st;
         }
-        if (!svp && (st = dw_chunk(c0, Mc, gb, gstride, sm)) != DISCO_OK) return st;
+        if (!svp && (st = dw_chunk(c0, Mc, gb, gstride, sc)) != DISCO_OK) return st;
     }
     if ((e = fork.join()) != hipSuccess) return hipfail(e, "side-stream join");
     return DISCO_OK;

@@ -421,9 +421,9 @@ def _fused_bwd_check(psi, B, C, Co, seed, dtype="bf16"):
 
 
 @pytest.mark.parametrize("cfg", [
-    (31, 64, 31, 64, 0.5, 4, 4, 2, 20, 24),     # K=16, s=1: two channel chunks (16 + 4), positions not a tile multiple
+    (31, 64, 31, 64, 0.5, 4, 4, 2, 20, 24),     # K=16, s=1: one chunk of 20 channels, positions not a tile multiple
     (19, 144, 19, 72, 0.7, 4, 2, 2, 9, 40),     # K=8, s=2: one chunk of 9 channels
-    (25, 48, 25, 48, 0.7, 4, 1, 1, 70, 8),      # K=4: chunks of 64 + 6 channels, Co = 8
+    (25, 48, 25, 48, 0.7, 4, 1, 1, 70, 8),      # K=4: 70 channels in one chunk (up to 256 at K=4), Co = 8
     (16, 32, 16, 32, 2 * np.pi / 16, 3, 1, 3, 5, 136),  # K=3, B=3, Co above one tile
 ])
 def test_fused_bwd_small_ragged(cfg):
@@ -439,7 +439,7 @@ def test_fused_bwd_small_ragged(cfg):
 @pytest.mark.parametrize("cfg", [
     (31, 64, 31, 64, 0.5, 4, 4, 2, 20, 24, "bf16"),   # K=16, s=1, Hi = Ho
     (21, 48, 17, 48, 0.6, 3, 3, 1, 9, 264, "f16"),    # K=9 (W' in rows of 16), Hi != Ho, Co over one tile
-    (25, 48, 25, 48, 0.7, 4, 1, 2, 70, 8, "bf16"),    # K=4, two channel chunks
+    (25, 48, 25, 48, 0.7, 4, 1, 2, 70, 8, "bf16"),    # K=4, B=2, 70 channels in one chunk
 ])
 def test_fused_bwd_gx_through_the_transposed_psi(cfg, monkeypatch):
     """With Wi = Wo the fused backward computes gx as a fused convolution over the per-basis transpose of
@@ -1207,6 +1207,30 @@ def _random_case(seed, k_range=None):
     return psi, B, C, Co, dt
 
 
+def test_fused_bwd_overlap_equals_one_stream(monkeypatch):
+    """The recomputing backward runs its contraction and dW products on a second stream beside the gx
+    launch; DISCO_BWD_OVERLAP=0 keeps them on the caller's stream.  Two channel chunks (K = 16, 70
+    channels), the workspace reused across calls: both orders give the same bits, and against the oracle."""
+    psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
+    assert psi.K == 16
+    _log("fused bwd overlap vs one stream")
+    egx, edW, (gx_a, dW_a) = _fused_bwd_check(psi, 2, 70, 24, 1700)
+    assert egx <= TOL["bf16"] and edW <= TOL["bf16"], (egx, edW)
+    monkeypatch.setenv("DISCO_BWD_OVERLAP", "0")
+    _, _, (gx_b, dW_b) = _fused_bwd_check(psi, 2, 70, 24, 1700)
+    monkeypatch.delenv("DISCO_BWD_OVERLAP")
+    assert torch.equal(gx_a, gx_b) and torch.equal(dW_a, dW_b)
+    h = gpu_psi(psi)
+    x = randn((2, 70, 31, 64), 1701, "bf16").to(DEV)
+    W = randn((24, 70, psi.K), 1702, "bf16", std=0.05).to(DEV)
+    gy = randn((2, 24, 31, 64), 1703, "bf16").to(DEV)
+    ws = torch.full((sgc.disco_fused_conv_bwd_workspace(h, 2, 70, 24),), 0x7f, dtype=torch.uint8, device=DEV)
+    runs = [sgc.disco_fused_conv_bwd(h, x, W, gy, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        assert torch.equal(r[0], runs[0][0]) and torch.equal(r[1], runs[0][1])
+
+
 @pytest.mark.parametrize("seed", list(range(5000, 5100)))
 def test_random_problems_every_op_against_the_oracle(seed):
     """Seeded random problems through fwd, bwd, the fused op (plain and saving), its backward (recomputing
@@ -1221,6 +1245,7 @@ RANDOM_PATH_KNOBS = {
     "staged fp32 gathers": {"DISCO_TILE": "0"},
     "plain gathers": {"DISCO_TILE": "0", "DISCO_STAGED": "0", "DISCO_FWD_MFMA": "0", "DISCO_BWD_MFMA": "0"},
     "gx through W^T gy": {"DISCO_BWD_FUSED": "0"},
+    "fused backward on one stream": {"DISCO_BWD_OVERLAP": "0"},
     "element-wise W staging": {"DISCO_PACK_W": "0"},
     "one realigned psi copy": {"DISCO_PSI_COPIES": "1"},
     "two psi copies": {"DISCO_PSI_COPIES": "2"},
