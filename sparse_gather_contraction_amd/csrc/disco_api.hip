@@ -62,11 +62,12 @@ struct DevTile {
     bool ok = false;
     disco::Task *tasks = nullptr;
     disco::Stage *stages = nullptr;
+    disco::Stage *task_first = nullptr;
     int32_t *stage_rows = nullptr;
     int32_t *stage_recptr = nullptr;
     disco::TileRec *recs = nullptr;
     disco::Item *items = nullptr;
-    int32_t n_tasks = 0;
+    int32_t n_tasks = 0, n_stages = 0;
     int32_t L = 0, row_len = 0, lrow = 0, deint = 1, rows_per_stage = 0, NI = 1, G = 1, PW = 1;
     int32_t n_ws4 = 0, n_ws2 = 0, max_recs = 0;
     int32_t n_recs = 0;
@@ -149,6 +150,7 @@ void free_tile(DevTile &d)
 {
     (void)hipFree(d.tasks);
     (void)hipFree(d.stages);
+    (void)hipFree(d.task_first);
     (void)hipFree(d.stage_rows);
     (void)hipFree(d.stage_recptr);
     (void)hipFree(d.recs);
@@ -165,12 +167,14 @@ hipError_t upload_tile(DevTile &d, const disco::TilePlan &p)
     hipError_t e;
     if ((e = upload(&d.tasks, p.tasks)) != hipSuccess) return e;
     if ((e = upload(&d.stages, p.stages)) != hipSuccess) return e;
+    if ((e = upload(&d.task_first, p.task_first)) != hipSuccess) return e;
     if ((e = upload(&d.stage_rows, p.stage_rows)) != hipSuccess) return e;
     if ((e = upload(&d.stage_recptr, p.stage_recptr)) != hipSuccess) return e;
     if ((e = upload(&d.recs, p.recs)) != hipSuccess) return e;
     if ((e = upload(&d.items, p.items)) != hipSuccess) return e;
     d.ok = true;
     d.n_tasks = (int32_t)p.tasks.size();
+    d.n_stages = (int32_t)p.stages.size();
     d.L = p.L; d.row_len = p.row_len; d.lrow = p.lrow; d.deint = p.deint; d.rows_per_stage = p.rows_per_stage;
     d.NI = p.NI; d.G = p.G; d.PW = p.PW;
     d.n_ws4 = p.n_ws4; d.n_ws2 = p.n_ws2; d.max_recs = p.max_recs;
@@ -472,6 +476,7 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const DevTile &tp
             a.src = (const float *)src + b0 * src_plane;
             a.dst = (float *)dst + b0 * dst_plane;
             a.tasks = tp.tasks; a.stages = tp.stages; a.stage_rows = tp.stage_rows; a.stage_recptr = tp.stage_recptr;
+            a.task_first = tp.task_first; a.n_stages = tp.n_stages;
             a.recs = tp.recs; a.items = tp.items;
             a.n_tasks = tp.n_tasks;
             a.BC = (int32_t)std::min<int64_t>(chunk, BC - b0);

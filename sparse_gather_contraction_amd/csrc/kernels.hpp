@@ -50,10 +50,12 @@ struct TileLaunch {
     float *dst;
     const Task *tasks;          // device, heaviest first
     const Stage *stages;
+    const Stage *task_first;    // per task: its first stage's descriptor (TilePlan::task_first)
     const int32_t *stage_rows;
     const int32_t *stage_recptr;
     const TileRec *recs;
     const Item *items;
+    int32_t n_stages;           // stages in all (0: task_first is not read)
     int32_t n_tasks, BC;        // tasks, planes
     int32_t n_ws4, n_ws2;       // task classes by wave split (see TilePlan)
     int64_t src_plane, dst_plane;

@@ -338,6 +338,10 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
     WS = uni(WS);
     const int NPB = 4 * PW / WS;  // planes of this workgroup
     const Task task = a.tasks[ti];
+    // the first stage's descriptor needs only the task number: read beside the task, so the first
+    // stage's metadata loads wait for one round trip instead of two (task, then its descriptors)
+    Stage f0 = {0, 0, 0, 0};
+    if (a.n_stages > 0) f0 = a.task_first[ti];
     const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wsi = wave % WS;    // this wave's share of the records
     const int ps = (wave / WS) * PW + (PW == 2 ? (lane >> 5) : 0);
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void tile_gather_kernel(TileLaunch a)
     };
     static_assert(sizeof(Stage) == 16, "stage layout: row_begin, row_end, segptr, pad");
     StageMeta m = {};
-    if (sb < se) m = meta_of(sb);
+    if (a.n_stages > 0) m = load_meta<NI>(a, f0.row_begin, f0.row_end, f0.segptr, lane);  // stage sb, if any
     for (int st = sb; st < se; ++st) {
         __syncthreads();  // the previous stage is consumed
         queue_stage<PW>(a, sc, m, buf);

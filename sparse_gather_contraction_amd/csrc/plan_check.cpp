@@ -298,6 +298,17 @@ void check_tile(const CSRView &c, const TilePlan &tp, bool backward, int lds_bud
     std::vector<int> writes(dst_plane, 0);
     const int lanes = 64 / tp.PW;  // lanes of one plane
     const int cmax = tile_piece_max(tp.G);
+    check(tp.task_first.size() == tp.tasks.size(), what + ": one first-stage descriptor per task");
+    for (size_t ti = 0; ti < tp.tasks.size(); ++ti) {
+        // the kernel reads task_first[ti] and that stage's metadata before it knows the task's stages
+        const Task &t = tp.tasks[ti];
+        const Stage &f = tp.task_first[ti];
+        if (tp.stages.empty()) continue;  // not read then
+        const Stage &want = t.stage_begin < t.stage_end && t.stage_begin >= 0 && t.stage_begin < (int32_t)tp.stages.size()
+                                ? tp.stages[t.stage_begin] : tp.stages[0];
+        check(f.row_begin == want.row_begin && f.row_end == want.row_end && f.segptr == want.segptr,
+              what + ": first-stage descriptor of a task");
+    }
     for (const Task &task : tp.tasks) {
         check(task.item_begin >= 0 && task.item_begin + tp.NI <= (int32_t)tp.items.size(), what + ": task items");
         check(task.stage_begin >= 0 && task.stage_begin <= task.stage_end && task.stage_end <= (int32_t)tp.stages.size(),

@@ -173,6 +173,10 @@ void build_tile_plan(const CSRView &c, const GatherPlan &p, bool backward, int l
         if (t.work > 2.0 * mean) ++out.n_ws2;
     }
     out.tasks = std::move(tasks);
+    out.task_first.clear();
+    for (const Task &t : out.tasks)
+        out.task_first.push_back(t.stage_begin < t.stage_end ? out.stages[t.stage_begin]
+                                                             : (out.stages.empty() ? Stage{0, 0, 0, 0} : out.stages[0]));
     out.ok = true;
 }
 

@@ -65,6 +65,9 @@ struct TilePlan {
     int32_t n_ws4 = 0, n_ws2 = 0;
     std::vector<Task> tasks;     // heaviest first
     std::vector<Stage> stages;   // Stage::segptr indexes stage_recptr
+    // per task (task order): its first stage's descriptor (stages[0] for a task without stages), so
+    // that a workgroup can read it knowing only its task number, beside the task itself
+    std::vector<Stage> task_first;
     std::vector<int32_t> stage_rows;    // source row index within a plane (hi, or k Ho + ho)
     // per stage NI * kTileClasses + 1 bounds into recs: item-major, then by entry count c = 1..8
     std::vector<int32_t> stage_recptr;

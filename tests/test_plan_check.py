@@ -112,6 +112,9 @@ MUTANTS = {
     "wrap threshold off by one": ("rec.w = L - rec.j0;", "rec.w = L - rec.j0 + 1;"),
     "halo too short for the longest record": ("out.lrow = (L + kTileHalo + 3) / 4 * 4;",
                                               "out.lrow = (L + 4 + 3) / 4 * 4;"),
+    "first-stage descriptor of the last stage": (
+        "out.task_first.push_back(t.stage_begin < t.stage_end ? out.stages[t.stage_begin]",
+        "out.task_first.push_back(t.stage_begin < t.stage_end ? out.stages[t.stage_end - 1]"),
 }
 
 
