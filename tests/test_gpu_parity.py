@@ -728,8 +728,9 @@ def test_einsum_721x1440_full_size_sampled():
 
 def test_one_handle_from_two_streams():
     """A psi handle is read-only after creation and may be used from several streams at once: the
-    forward and backward on one side stream, the fused op and the einsum on another, concurrently,
-    each equal bitwise to the same call on the default stream."""
+    forward and backward on one side stream, the fused op and the einsum on another, and both fused
+    backwards (which fork onto the library's own second stream) on both, concurrently, each equal
+    bitwise to the same call on the default stream."""
     _log("two streams")
     psi = build_psi(31, 64, 31, 64, 0.5, 4, 4)
     h = sgc.disco_psi_create(psi, 0)
@@ -739,20 +740,22 @@ def test_one_handle_from_two_streams():
     gy = randn((2, 16, 31, 64), 3603, "bf16").to(DEV)
     _, kept = sgc.disco_fused_conv_save(h, x, W)
     ref = (sgc.disco_fwd(h, x), sgc.disco_bwd(h, g), sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g),
-           *sgc.disco_fused_conv_bwd_saved(h, kept, W, gy))
+           *sgc.disco_fused_conv_bwd_saved(h, kept, W, gy), *sgc.disco_fused_conv_bwd(h, x, W, gy))
     torch.cuda.synchronize()
     sa, sb = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)  # default priority
     outs = []
     for _ in range(3):
-        # the saved backward forks onto the library's side stream on both caller streams at once
+        # both backwards fork onto the library's side stream, from both caller streams at once
         with torch.cuda.stream(sa):
             o, gx = sgc.disco_fwd(h, x), sgc.disco_bwd(h, g)
             sgx_a, sdw_a = sgc.disco_fused_conv_bwd_saved(h, kept, W, gy)
+            rgx_a, rdw_a = sgc.disco_fused_conv_bwd(h, x, W, gy)
         with torch.cuda.stream(sb):
             y, ye = sgc.disco_fused_conv(h, x, W), sgc.disco_einsum(W, g)
             sgx_b, sdw_b = sgc.disco_fused_conv_bwd_saved(h, kept, W, gy)
-        outs.append((o, gx, y, ye, sgx_a, sdw_a))
-        outs.append((o, gx, y, ye, sgx_b, sdw_b))
+            rgx_b, rdw_b = sgc.disco_fused_conv_bwd(h, x, W, gy)
+        outs.append((o, gx, y, ye, sgx_a, sdw_a, rgx_a, rdw_a))
+        outs.append((o, gx, y, ye, sgx_b, sdw_b, rgx_b, rdw_b))
     torch.cuda.synchronize()
     for got in outs:
         for a, b in zip(got, ref):
