@@ -133,7 +133,7 @@ void check_gather(const CSRView &c, const GatherPlan &p, bool backward, const st
 }
 
 // ---- source windows of the vector-ALU fused kernels (plan.hpp, FusedWindows) -----------------------
-// Replays the fp32 fused kernel's contraction from staged windows: for every latitude and tile of px
+// Replays the fused kernels' contraction from staged windows: for every latitude and tile of px
 // output longitudes, the window image as the staging writes it, then every entry's read at
 // seg_off + t + (wo - wo0), which must stay inside its own row's staged positions.
 void check_windows(const CSRView &c, const GatherPlan &p, const FusedWindows &w, int px, const std::vector<double> &x,
