@@ -480,7 +480,8 @@ disco_status run_gather(const DevPlan &p, const DevStaged &sp, const DevTile &tp
             a.recs = tp.recs; a.items = tp.items;
             a.n_tasks = tp.n_tasks;
             a.BC = (int32_t)std::min<int64_t>(chunk, BC - b0);
-            a.n_ws4 = tp.n_ws4; a.n_ws2 = tp.n_ws2; a.max_recs = tp.max_recs; a.n_recs = tp.n_recs;
+            disco::tile_wave_split(tp.n_tasks, tp.n_recs, tp.PW, tp.n_ws4, tp.n_ws2, a.BC, a.n_ws4, a.n_ws2);
+            a.max_recs = tp.max_recs; a.n_recs = tp.n_recs;
             a.src_plane = src_plane; a.dst_plane = dst_plane;
             a.L = tp.L; a.row_len = tp.row_len; a.lrow = tp.lrow; a.deint = tp.deint;
             a.rows_per_stage = tp.rows_per_stage; a.NI = tp.NI; a.G = tp.G; a.PW = tp.PW;

@@ -293,7 +293,8 @@ void check_tile(const CSRView &c, const TilePlan &tp, bool backward, int lds_bud
     check(tp.NP == 4 * tp.PW && (tp.PW == 1 || tp.PW == 2) && (64 / tp.PW) * T >= tp.L, what + ": lane layout");
     check(0 <= tp.n_ws4 && tp.n_ws4 <= tp.n_ws2 && tp.n_ws2 <= (int32_t)tp.tasks.size(), what + ": wave-split classes");
     check(tp.NI * tp.G <= kTileMaxRows, what + ": more accumulator rows than the kernel holds");
-    check(tp.n_ws2 == 0 || 3LL * 64 * tp.NI * tp.G * T * 4 <= lds_budget, what + ": wave-split sums exceed the LDS");
+    // any launch may split its tasks over waves (few planes: tile_wave_split), so the sums' area must fit
+    check(3LL * 64 * tp.NI * tp.G * T * 4 <= lds_budget, what + ": wave-split sums exceed the LDS");
     std::vector<double> got(dst_plane, 0.0);
     std::vector<int> writes(dst_plane, 0);
     const int lanes = 64 / tp.PW;  // lanes of one plane
@@ -401,20 +402,23 @@ void check_tile_grid(const TilePlan &tp, int BC)
     if (!tp.ok) return;
     const std::string what = "tiled grid (" + std::to_string(BC) + " planes)";
     const int PW = tp.PW, nt = (int)tp.tasks.size();
+    int32_t n_ws4 = 0, n_ws2 = 0;  // the classes the launch uses for BC planes
+    tile_wave_split(nt, (int64_t)tp.recs.size(), PW, tp.n_ws4, tp.n_ws2, BC, n_ws4, n_ws2);
+    check(0 <= n_ws4 && n_ws4 <= n_ws2 && n_ws2 <= nt, what + ": wave-split classes");
     const int npg4 = (BC + PW - 1) / PW, npg2 = (BC + 2 * PW - 1) / (2 * PW), npg1 = (BC + 4 * PW - 1) / (4 * PW);
-    const int64_t nblk = (int64_t)tp.n_ws4 * npg4 + (int64_t)(tp.n_ws2 - tp.n_ws4) * npg2 + (int64_t)(nt - tp.n_ws2) * npg1;
+    const int64_t nblk = (int64_t)n_ws4 * npg4 + (int64_t)(n_ws2 - n_ws4) * npg2 + (int64_t)(nt - n_ws2) * npg1;
     std::vector<int> seen((size_t)nt * BC, 0);
     for (int64_t b = 0; b < nblk; ++b) {
         int bid = (int)b, ti, pg, WS;
-        const int nb4 = tp.n_ws4 * npg4, nb2 = (tp.n_ws2 - tp.n_ws4) * npg2;
+        const int nb4 = n_ws4 * npg4, nb2 = (n_ws2 - n_ws4) * npg2;
         if (bid < nb4) {
             WS = 4; ti = bid / npg4; pg = bid - ti * npg4;
         } else if (bid < nb4 + nb2) {
             bid -= nb4;
-            WS = 2; ti = tp.n_ws4 + bid / npg2; pg = bid - (ti - tp.n_ws4) * npg2;
+            WS = 2; ti = n_ws4 + bid / npg2; pg = bid - (ti - n_ws4) * npg2;
         } else {
             bid -= nb4 + nb2;
-            WS = 1; ti = tp.n_ws2 + bid / npg1; pg = bid - (ti - tp.n_ws2) * npg1;
+            WS = 1; ti = n_ws2 + bid / npg1; pg = bid - (ti - n_ws2) * npg1;
         }
         check(ti >= 0 && ti < nt, what + ": task index out of range");
         if (ti < 0 || ti >= nt) return;
@@ -430,7 +434,7 @@ void check_tile_grid(const TilePlan &tp, int BC)
             }
     }
     for (int ti = 0; ti < nt; ++ti) {
-        const int WS = ti < tp.n_ws4 ? 4 : (ti < tp.n_ws2 ? 2 : 1);
+        const int WS = ti < n_ws4 ? 4 : (ti < n_ws2 ? 2 : 1);
         for (int pl = 0; pl < BC; ++pl)
             check(seen[(size_t)ti * BC + pl] == (1 << WS) - 1, what + ": a (task, plane) is not served by each share once");
     }

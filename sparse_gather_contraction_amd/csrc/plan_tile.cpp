@@ -180,4 +180,17 @@ void build_tile_plan(const CSRView &c, const GatherPlan &p, bool backward, int l
     out.ok = true;
 }
 
+void tile_wave_split(int32_t n_tasks, int64_t n_recs, int32_t PW, int32_t plan_ws4, int32_t plan_ws2, int64_t BC,
+                     int32_t &n_ws4, int32_t &n_ws2)
+{
+    n_ws4 = plan_ws4;
+    n_ws2 = plan_ws2;
+    if (n_recs < (int64_t)kTileSplitMinRecs * n_tasks) return;
+    if (BC <= 2 * (int64_t)PW) {
+        n_ws4 = n_ws2 = n_tasks;
+    } else if (BC < 4 * (int64_t)PW) {
+        n_ws2 = n_tasks;
+    }
+}
+
 }  // namespace disco

@@ -75,6 +75,16 @@ struct TilePlan {
     std::vector<Item> items;     // NI per task; out_off[0] < 0 marks padding
 };
 
+// Wave-split classes of a launch over BC planes: the plan's (n_ws4, n_ws2), except that with fewer
+// planes than a workgroup of one-wave tasks holds (4 PW) and tasks of kTileSplitMinRecs records or
+// more on average, the tasks split their records over more waves, so that no wave is left without a
+// plane: every task over 4 waves (PW planes per workgroup) when BC <= 2 PW, else at least over 2
+// (2 PW planes) when BC < 4 PW.  Smaller tasks keep the plan's classes: for them the partial sums'
+// pass through LDS costs more than the split saves.
+constexpr int kTileSplitMinRecs = 32;
+void tile_wave_split(int32_t n_tasks, int64_t n_recs, int32_t PW, int32_t plan_ws4, int32_t plan_ws2, int64_t BC,
+                     int32_t &n_ws4, int32_t &n_ws2);
+
 // `p` from build_forward_plan (backward = false) or build_backward_plan (backward = true);
 // `lds_budget` = bytes of LDS one workgroup may use.
 void build_tile_plan(const CSRView &c, const GatherPlan &p, bool backward, int lds_budget, TilePlan &out);

@@ -105,6 +105,26 @@ def test_bwd_full_parity_fp32():
     assert normalised_error(gx, ref, nrm) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("planes", [1, 3, 4, 6])
+def test_fp32_181x360_few_planes(planes):
+    """With few channel planes the tiled gather splits each task's records over more waves (2 or 4 waves
+    share a workgroup's planes and add their partial sums in wave order); the 181x360 forward's tasks are
+    large enough for that split.  Forward and backward against the oracle."""
+    w = WORKLOADS["fwdbwd_f32_181x360"]
+    _log(f"fp32 181x360 with {planes} planes")
+    psi = workload_psi(w)
+    h = gpu_psi(psi)
+    x = randn((1, planes, w.Hi, w.Wi), 3900 + planes, "f32")
+    out = nan_like((1, planes, w.K, w.Ho, w.Wo), torch.float32)
+    sgc.disco_fwd(h, x.to(DEV), out)
+    g = randn((1, planes, w.K, w.Ho, w.Wo), 3950 + planes, "f32")
+    gx = nan_like((1, planes, w.Hi, w.Wi), torch.float32)
+    sgc.disco_bwd(h, g.to(DEV), gx)
+    torch.cuda.synchronize()
+    assert normalised_error(out, oracle.fwd(psi, x), oracle.fwd(psi, x.abs(), abs_mode=True)) <= TOL["f32"]
+    assert normalised_error(gx, oracle.bwd(psi, g), oracle.bwd(psi, g.abs(), abs_mode=True)) <= TOL["f32"]
+
+
 PLANES_721 = [0, 21, 42, 63]
 
 
